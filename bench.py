@@ -1,0 +1,266 @@
+"""Benchmark of the MI355X factorized linear layer Y = (X.A).B.
+
+Default (one GPU): the Llama-3-8B-shaped q_proj at decode, X[8 x 4096],
+A[4096 x 1637], B[1637 x 4096] bf16 -- a misaligned rank -- through the
+fused decode kernel.  One step = one lr_linear_run (plan/dispatch, split-K
+GEMM1, rank padding and edge masking, T hand-off, GEMM2, deterministic
+reduction, bf16 epilogue).  The factors rotate over enough copies (>= 1 GiB)
+that every step streams them from HBM, not from the 256 MB last-level
+cache.  value = algorithmic bytes per step / time per step (TB/s).
+
+A second object reports the prefill workload (MLP up-projection,
+X[4096 x 4096], r = 2867, N = 14336) in TFLOP/s against the dense bf16
+MFMA peak.  The CPU oracle is timed on a bounded sample as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+                    [--calib-copy] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+METRIC = "low-rank linear: decode TB/s and prefill TFLOP/s vs roofline, across rank r"
+KERNEL_SOURCES = ["rank_linear_layer_amd/csrc/lr_decode.hip", "rank_linear_layer_amd/csrc/lr_prefill.hip",
+                  "rank_linear_layer_amd/csrc/lr_device.h", "rank_linear_layer_amd/csrc/lr_kernels.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def dev_bf16(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def time_steps(torch, fn, steps, warmup, stream):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per step
+
+
+def traffic_from_profile(name, launches_bytes):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if
+    they were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def bench_decode(torch, lrl, configs, datagen, metrics, steps, warmup):
+    c = configs.QPROJ_DECODE
+    M, K, r, N = c["M"], c["K"], c["r"], c["N"]
+    Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, configs.seed_base(c["index"]))
+    per = metrics.decode_bytes(M, K, r, N)
+    ncopies = max(2, int(np.ceil((1 << 30) / (2 * (K * r + r * N)))))
+    A0, B0 = dev_bf16(torch, Ab), dev_bf16(torch, Bb)
+    As = [A0] + [A0.clone() for _ in range(ncopies - 1)]
+    Bs = [B0] + [B0.clone() for _ in range(ncopies - 1)]
+    X = dev_bf16(torch, Xb)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    lins = [lrl.LowRankLinear(a, b, max_M=M) for a, b in zip(As, Bs)]
+    stream = torch.cuda.current_stream()
+    log("decode plan: %s; %d weight copies (%.0f MB)" % (lins[0].describe(), ncopies, ncopies * 2 * (K * r + r * N) / 1e6))
+
+    def step(i):
+        lins[i % ncopies](X, out=Y)
+
+    ms = time_steps(torch, step, steps, warmup, stream)
+    tbs = per / (ms * 1e-3) / 1e12
+    # warm-cache figure (same copy every step) for context
+    ms_warm = time_steps(torch, lambda i: lins[0](X, out=Y), max(50, steps // 4), 10, stream)
+    return dict(M=M, K=K, r=r, N=N, ms=ms, tbs=tbs, bytes=per, ncopies=ncopies,
+                warm_tbs=per / (ms_warm * 1e-3) / 1e12, plan=lins[0].describe())
+
+
+def bench_prefill(torch, lrl, configs, metrics, steps, warmup):
+    c = configs.MLP_UP_PREFILL
+    M, K, r, N = c["M"], c["K"], c["r"], c["N"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(configs.seed_base(c["index"]))
+    X = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    A = (torch.randn((K, r), generator=g, device="cuda", dtype=torch.float32) / np.sqrt(K)).to(torch.bfloat16)
+    B = (torch.randn((r, N), generator=g, device="cuda", dtype=torch.float32) / np.sqrt(r)).to(torch.bfloat16)
+    lin = lrl.LowRankLinear(A, B, max_M=M)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    ms = time_steps(torch, lambda i: lin(X, out=Y), steps, warmup, stream)
+    fl = metrics.lowrank_flops(M, K, r, N)
+    return dict(M=M, K=K, r=r, N=N, ms=ms, tflops=fl / (ms * 1e-3) / 1e12, flops=fl, plan=lin.describe())
+
+
+def cpu_baseline(configs, datagen, metrics, budget_s=12.0):
+    import oracle
+    c = configs.QPROJ_DECODE
+    M, K, r, N = c["M"], c["K"], c["r"], c["N"]
+    Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, configs.seed_base(c["index"]))
+    threads = oracle.default_threads()
+    oracle.lowrank_bf16(Xb[:1], Ab, Bb, nthreads=threads)  # load + warm
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.lowrank_bf16(Xb, Ab, Bb, nthreads=threads)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {"value": metrics.decode_bytes(M, K, r, N) / dt / 1e12, "unit": "TB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "q_proj decode M=8 K=4096 r=1637 N=4096, full output, %d oracle forwards in %.1f s "
+                      "(%.3f s each, float64, sequential sums)" % (n, n * dt, dt)}
+
+
+def calib_copy(torch):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters (run under --pmc)."""
+    nbytes = 256 << 20
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("calibration copy: 3 x %d bytes read and written" % nbytes)
+
+
+def run_sweep(torch, lrl, configs, metrics, steps):
+    """Throughput against rank (no-cliff check), printed as JSON lines on stderr."""
+    rows = []
+    for N in configs.SWEEP_N:
+        for r in configs.SWEEP_R:
+            K = configs.SWEEP_K
+            g = torch.Generator(device="cuda")
+            g.manual_seed(configs.sweep_seed(N, r))
+            ncop = max(2, int(np.ceil((1 << 30) / (2 * (K * r + r * N)))))
+            A = (torch.randn((K, r), generator=g, device="cuda") / np.sqrt(K)).to(torch.bfloat16)
+            B = (torch.randn((r, N), generator=g, device="cuda") / np.sqrt(r)).to(torch.bfloat16)
+            As = [A] + [A.clone() for _ in range(ncop - 1)]
+            Bs = [B] + [B.clone() for _ in range(ncop - 1)]
+            for M in configs.SWEEP_M:
+                X = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+                Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+                lins = [lrl.LowRankLinear(a, b, max_M=M) for a, b in zip(As, Bs)]
+                ms = time_steps(torch, lambda i: lins[i % ncop](X, out=Y), steps, 10, torch.cuda.current_stream())
+                row = dict(N=N, r=r, M=M, ms=ms, tbs=metrics.decode_bytes(M, K, r, N) / (ms * 1e-3) / 1e12,
+                           tflops=metrics.lowrank_flops(M, K, r, N) / (ms * 1e-3) / 1e12)
+                rows.append(row)
+                print(json.dumps({"sweep": row}), file=sys.stderr, flush=True)
+                del lins
+            del As, Bs
+    return rows
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep-steps", type=int, default=100)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer would shard along the rank with one all-reduce of Y; not built). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rank_linear_layer_amd as lrl
+    from rank_linear_layer_amd import configs, datagen, metrics
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lrl.load_library()
+    torch.cuda.set_device(0)
+
+    if args.calib_copy:
+        calib_copy(torch)
+
+    torch.cuda.synchronize()
+    d = bench_decode(torch, lrl, configs, datagen, metrics, args.steps, args.warmup)
+    log("decode: %.3f us/step, %.3f TB/s (warm-cache %.3f TB/s)" % (d["ms"] * 1e3, d["tbs"], d["warm_tbs"]))
+    result = {
+        "metric": METRIC,
+        "value": round(d["tbs"], 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) bf16 factors; %d rotating weight copies, "
+                "cold last-level cache)" % d["ncopies"],
+        "config": {"workload": "Llama-3-8B-shaped q_proj decode, misaligned rank", "M": d["M"], "K": d["K"],
+                   "r": d["r"], "N": d["N"], "path": "fused decode kernel", "weight_copies": d["ncopies"]},
+        "roofline": {"bound": "hbm", "achieved": round(d["bytes"] / (d["ms"] * 1e-3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(d["bytes"] / (d["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile("lr_decode_fused_qproj_decode_pmc.json", d["bytes"]),
+                     "kernel": "lr_decode_fused_kernel", "algorithmic_bytes_per_launch": d["bytes"]},
+        "warm_cache_tbs": round(d["warm_tbs"], 4),
+    }
+    if not args.no_prefill:
+        p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 50), 3)
+        log("prefill: %.3f ms/step, %.1f TFLOP/s" % (p["ms"], p["tflops"]))
+        result["prefill"] = {
+            "workload": "MLP up-projection prefill M=4096 K=4096 r=2867 N=14336",
+            "ms_per_step": round(p["ms"], 5), "value": round(p["tflops"], 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(p["tflops"], 2), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(p["tflops"] / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None, "kernel": "lr_prefill_gemm_kernel (2 launches)",
+                         "algorithmic_flops_per_step": p["flops"]},
+        }
+    if args.sweep:
+        result["sweep"] = run_sweep(torch, lrl, configs, metrics, args.sweep_steps)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(configs, datagen, metrics)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

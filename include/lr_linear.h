@@ -1,0 +1,148 @@
+/*
+ * lr_linear.h -- C ABI of the MI355X (gfx950) factorized linear layer.
+ *
+ * The operation
+ * -------------
+ * A linear layer Y = X.W whose weight has been replaced by two factors,
+ * W ~ A.B, with the rank r as the inner dimension of two smaller GEMMs
+ * ("Why Smaller Is Slower? Dimensional Misalignment in Compressed LLMs",
+ * section 1 and Figure 1).  The factor pair keeps the layer's input/output
+ * interface: y = Wx becomes y = A(Bx) in the column-vector orientation of
+ * "LowRankArena: What Happens When You Force SVD Compression Papers to Play
+ * by the Same Rules" (Prerequisites, Figure A).  Here, row-major:
+ *
+ *     X[M x K] . A[K x r] = T[M x r],     T . B[r x N] = Y[M x N]
+ *
+ * r and N may take any value >= 1 (r = 107, 1637, 2867, N = 3999 ...):
+ * the kernels pad the rank and mask the N edge on chip, so no shape falls
+ * back to a slower kernel tier (the tiers and penalties that the
+ * misalignment page measures in section 3.2 and Tables 3-4).
+ *
+ * Data types and layout
+ * ---------------------
+ * All matrices are bfloat16, row-major, dense (leading dimension = number
+ * of columns).  Base pointers must be 16-byte aligned (any allocation made
+ * by hipMalloc or torch is); rows may start at any 2-byte boundary.
+ * Arithmetic: bf16 inputs, fp32 accumulation, bf16 output rounded to
+ * nearest-even.  All pointers passed here are DEVICE pointers.
+ *
+ * Ownership
+ * ---------
+ * A and B are BORROWED by the handle: the caller keeps them alive and
+ * unchanged until lr_linear_destroy.  They are never copied, repacked or
+ * padded in device memory.  X and Y are borrowed for the duration of the
+ * enqueued work.  The handle OWNS a device workspace (allocated at create,
+ * sized for max_M) that holds split-K partial sums and, for M > 16, the
+ * bf16 intermediate T; lr_linear_destroy frees it.  Because the workspace
+ * is shared by every call on a handle, a handle must not be used by two
+ * streams at the same time.
+ *
+ * Semantics
+ * ---------
+ * Y is fully overwritten (no alpha/beta, no accumulation), exactly on its
+ * M x N extent; no byte outside it is written.  Calls are asynchronous on
+ * the given stream (a hipStream_t passed as void*; NULL = default stream):
+ * the status reflects argument validation and kernel launch only.  Faults
+ * inside kernels surface at the caller's next synchronization.
+ *
+ * Errors
+ * ------
+ * Functions return an lr_status and never abort, print or throw across the
+ * ABI.  lr_last_error() returns a thread-local detail string for the most
+ * recent failure on the calling thread.
+ */
+#ifndef LR_LINEAR_H
+#define LR_LINEAR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lr_status {
+    LR_OK = 0,
+    LR_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned base, overlap */
+    LR_ERR_UNSUPPORTED = 2,   /* no gfx950 device, or flags not understood */
+    LR_ERR_OUT_OF_MEMORY = 3, /* workspace allocation failed */
+    LR_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} lr_status;
+
+/* Opaque handle: one factorized projection (A, B) and its workspace. */
+typedef struct lr_linear lr_linear;
+
+/* Flags for lr_linear_create. */
+#define LR_FLAG_NONE          0u
+#define LR_FLAG_FORCE_DECODE  1u  /* use the fused decode kernel for every M (requires max_M <= 16) */
+#define LR_FLAG_FORCE_PREFILL 2u  /* use the MFMA prefill kernels for every M */
+
+/* Largest M that the fused decode kernel takes (more rows use prefill). */
+#define LR_DECODE_MAX_M 16
+
+/*
+ * lr_linear_create -- build a handle for one factor pair.
+ *   out    : receives the handle (set to NULL on failure).
+ *   K, r, N: X has K columns, A is K x r, B is r x N; each >= 1.
+ *   A, B   : device pointers to the bf16 factors (borrowed; 16-byte aligned).
+ *   max_M  : largest M that lr_linear_run will be called with (>= 0).
+ *   flags  : LR_FLAG_* bits.
+ * Chooses the kernels' partitioning for this shape and allocates the
+ * workspace on the current HIP device.  Launches no kernel.
+ * Errors: INVALID_ARG (null/size/alignment), UNSUPPORTED (no gfx950 device,
+ * unknown flags, FORCE_DECODE with max_M > 16), OUT_OF_MEMORY, HIP.
+ */
+lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N,
+                           const void* A, const void* B, int64_t max_M, uint32_t flags);
+
+/*
+ * lr_linear_run -- Y[M x N] = (X[M x K] . A) . B on `stream`.
+ *   M in [0, max_M]; M == 0 returns LR_OK and launches nothing.
+ * M <= 16: one fused launch (split-K GEMM1, on-chip T hand-off, GEMM2,
+ * deterministic reduction; T never round-trips through HBM).
+ * M > 16: MFMA GEMM1 into a bf16 T workspace, then MFMA GEMM2.
+ * Errors: INVALID_ARG (null handle/pointers, M out of range, misaligned
+ * base, Y overlapping X/A/B), HIP (launch failure).
+ */
+lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, void* stream);
+
+/*
+ * lr_mlp_packed_run -- a gate/up pair that shares its input X
+ * ("FlashSVD v1.5: Making Low-Rank Transformers Inference Actually Fast",
+ * abstract: packed MLP execution).  Computes
+ *     Y_gate = (X.A_gate).B_gate   and   Y_up = (X.A_up).B_up
+ * in the same launch(es), reading each tile of X once for both GEMM1s.
+ * gate and up must have equal K; their r and N may differ.  M must not
+ * exceed either handle's max_M.  Y_gate and Y_up must not overlap each
+ * other or any input.
+ * Errors: as lr_linear_run, plus INVALID_ARG for gate.K != up.K.
+ */
+lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const void* X,
+                            void* Y_gate, void* Y_up, int64_t M, void* stream);
+
+/* lr_linear_destroy -- free the workspace and the handle.  NULL is a no-op.
+ * The caller must ensure no enqueued work still uses the handle. */
+void lr_linear_destroy(lr_linear* h);
+
+/* Static, human-readable name of a status code. */
+const char* lr_status_str(lr_status s);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* lr_last_error(void);
+
+/*
+ * lr_linear_describe -- write a one-line description of the handle's plan
+ * (shape, padded rank, partition, workspace bytes) into buf (NUL-terminated,
+ * truncated to len).  Returns LR_ERR_INVALID_ARG for a NULL handle or buffer.
+ */
+lr_status lr_linear_describe(const lr_linear* h, char* buf, int64_t len);
+
+/*
+ * lr_linear_workspace_bytes -- device bytes the handle owns (0 for NULL).
+ */
+int64_t lr_linear_workspace_bytes(const lr_linear* h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LR_LINEAR_H */

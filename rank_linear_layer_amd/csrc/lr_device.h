@@ -1,0 +1,206 @@
+// Device-side building blocks shared by the decode and prefill kernels
+// (gfx950 / CDNA4, wave64).
+//
+// Misaligned rows.  A factor stored row-major with an odd leading dimension
+// (rank r = 1637, width N = 3999 ...) has rows that start at arbitrary
+// 2-byte boundaries.  The page on dimensional misalignment ("Why Smaller Is
+// Slower? ...", section 3.3 and Table 4) traces part of the slowdown to
+// exactly this: accesses that no longer fill whole memory sectors.  Here
+// every global load stays a naturally aligned 16-byte load.  A lane that
+// needs the 8 elements [j, j + 8) of a row loads the aligned 16-byte chunk
+// holding element j, takes the following chunk from its right-hand
+// neighbour lane through a DPP row shift, and funnel-shifts the pair by the
+// row's misalignment.  The 16 lanes of a DPP row load 16 consecutive chunks
+// and the first 15 of them produce output, so a wave row covers 120
+// columns.  Within the tiles used here all rows that one load
+// instruction touches have the same misalignment (they are congruent
+// mod 8), so the shift is wave-uniform and the selection below is a
+// uniform branch.
+//
+// MFMA operands.  v_mfma_f32_16x16x32_bf16 wants the reduction index
+// contiguous inside each lane (8 bf16 per lane).  Weights are stored with
+// the *output* index contiguous, so a lane that loaded rows k0..k0+7 at
+// columns j..j+7 transposes that 8 x 8 block in registers (v_perm) into
+// eight operands, one per column; MFMA e of a group then computes output
+// columns {8 * lane16 + e}.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lrk {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ u32x4_t zerou4() { return u32x4_t{0u, 0u, 0u, 0u}; }
+
+// bf16 bits -> fp32
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Loads the 16-byte chunk c (elements [8c, 8c + 8)) of a bf16 array of
+// `total` elements whose base is 16-byte aligned.  Elements at or beyond
+// `total` read as zero and are never fetched.
+__device__ __forceinline__ u32x4_t load_chunk(const uint16_t* __restrict__ base, int64_t c, int64_t total) {
+  const int64_t e0 = c * 8;
+  if (e0 + 8 <= total) return *reinterpret_cast<const u32x4_t*>(base + e0);
+  u32x4_t v = zerou4();
+  if (e0 < total) {
+    uint32_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = (e0 + i < total) ? (uint32_t)base[e0 + i] : 0u;
+    v[0] = t[0] | (t[1] << 16);
+    v[1] = t[2] | (t[3] << 16);
+    v[2] = t[4] | (t[5] << 16);
+    v[3] = t[6] | (t[7] << 16);
+  }
+  return v;
+}
+
+// Lane i of each 16-lane DPP row receives `src` of lane i + 1; lane 15 of
+// each row keeps `old`.
+__device__ __forceinline__ uint32_t dpp_row_shl1(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x101, 0xf, 0xf, false);
+}
+__device__ __forceinline__ u32x4_t dpp_row_shl1(const u32x4_t& old, const u32x4_t& src) {
+  u32x4_t r;
+  r[0] = dpp_row_shl1(old[0], src[0]);
+  r[1] = dpp_row_shl1(old[1], src[1]);
+  r[2] = dpp_row_shl1(old[2], src[2]);
+  r[3] = dpp_row_shl1(old[3], src[3]);
+  return r;
+}
+
+// Elements (2i+1, 2i+2) of the pair (y = dword i, x = dword i + 1).
+__device__ __forceinline__ uint32_t odd_pair(uint32_t x, uint32_t y) { return (y >> 16) | (x << 16); }
+
+// Elements [d, d + 8) of the 16-element window (lo, hi); d is wave-uniform.
+__device__ __forceinline__ u32x4_t realign(const u32x4_t& lo, const u32x4_t& hi, int d) {
+  u32x4_t o;
+  switch (d) {
+    default:
+    case 0: o = lo; break;
+    case 1: o[0] = odd_pair(lo[1], lo[0]); o[1] = odd_pair(lo[2], lo[1]); o[2] = odd_pair(lo[3], lo[2]); o[3] = odd_pair(hi[0], lo[3]); break;
+    case 2: o[0] = lo[1]; o[1] = lo[2]; o[2] = lo[3]; o[3] = hi[0]; break;
+    case 3: o[0] = odd_pair(lo[2], lo[1]); o[1] = odd_pair(lo[3], lo[2]); o[2] = odd_pair(hi[0], lo[3]); o[3] = odd_pair(hi[1], hi[0]); break;
+    case 4: o[0] = lo[2]; o[1] = lo[3]; o[2] = hi[0]; o[3] = hi[1]; break;
+    case 5: o[0] = odd_pair(lo[3], lo[2]); o[1] = odd_pair(hi[0], lo[3]); o[2] = odd_pair(hi[1], hi[0]); o[3] = odd_pair(hi[2], hi[1]); break;
+    case 6: o[0] = lo[3]; o[1] = hi[0]; o[2] = hi[1]; o[3] = hi[2]; break;
+    case 7: o[0] = odd_pair(hi[0], lo[3]); o[1] = odd_pair(hi[1], hi[0]); o[2] = odd_pair(hi[2], hi[1]); o[3] = odd_pair(hi[3], hi[2]); break;
+  }
+  return o;
+}
+
+// Zero the elements of an 8-element segment whose column col0 + e >= ncols.
+__device__ __forceinline__ u32x4_t mask_cols(const u32x4_t& v, int64_t col0, int64_t ncols) {
+  if (col0 + 8 <= ncols) return v;
+  u32x4_t o = zerou4();
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t w = v[p];
+    uint32_t keep = 0;
+    if (col0 + 2 * p < ncols) keep |= 0x0000FFFFu;
+    if (col0 + 2 * p + 1 < ncols) keep |= 0xFFFF0000u;
+    o[p] = w & keep;
+  }
+  return o;
+}
+
+// 8 x 8 bf16 transpose: seg[q] holds elements (row q, cols 0..7); returns in
+// op[e] the 8 rows of column e (row q at vector element q).
+__device__ __forceinline__ void transpose8x8(const u32x4_t seg[8], u32x4_t op[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      op[e][p] = __builtin_amdgcn_perm(seg[2 * p + 1][e >> 1], seg[2 * p][e >> 1], sel);
+    }
+  }
+}
+
+// Raw half of a realigned row-segment load: lane16 of a 16-lane DPP row
+// loads the aligned chunk that holds column colbase + 8*lane16 - d of row
+// `row` (d = misalignment, see realign_segment).  Lanes 0..14 produce the
+// 8 columns [colbase + 8*lane16, +8); lane 15 only supplies the high half
+// for lane 14, so one DPP row covers 120 columns.
+__device__ __forceinline__ u32x4_t load_row_raw(const uint16_t* __restrict__ base, int64_t row, int64_t nrows,
+                                                int64_t ld, int64_t colbase, int lane16, int64_t total) {
+  if (row >= nrows) return zerou4();
+  const int64_t c0 = (row * ld + colbase) >> 3;
+  return load_chunk(base, c0 + lane16, total);
+}
+
+// Second half: realign the raw chunk with the right-hand neighbour's chunk
+// and zero columns >= ncols.  `d` = (row * ld + colbase) mod 8 must be
+// uniform over the wave.  Lane 15's result is meaningless.
+__device__ __forceinline__ u32x4_t realign_segment(const u32x4_t& lo, int d, int64_t col0, int64_t ncols) {
+  const u32x4_t hi = dpp_row_shl1(zerou4(), lo);
+  return mask_cols(realign(lo, hi, d), col0, ncols);
+}
+
+// 8 consecutive elements [k0, k0 + 8) of row `row` of a row-major matrix
+// (leading dimension ld, valid columns < klen, valid rows < nrows).  When
+// `aligned` (ld and k0 multiples of 8) the load is one 16-byte access.
+__device__ __forceinline__ u32x4_t load_kvec(const uint16_t* __restrict__ base, int64_t row, int64_t nrows,
+                                             int64_t ld, int64_t k0, int64_t klen, bool aligned) {
+  if (row >= nrows || k0 >= klen) return zerou4();
+  const uint16_t* p = base + row * ld + k0;
+  if (aligned && k0 + 8 <= klen) return *reinterpret_cast<const u32x4_t*>(p);
+  uint32_t t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = (k0 + i < klen) ? (uint32_t)p[i] : 0u;
+  u32x4_t v;
+  v[0] = t[0] | (t[1] << 16);
+  v[1] = t[2] | (t[3] << 16);
+  v[2] = t[4] | (t[5] << 16);
+  v[3] = t[6] | (t[7] << 16);
+  return v;
+}
+
+// Device-coherent (agent scope) relaxed accesses used to exchange partial
+// sums between workgroups on different XCDs without L2 write-back or
+// invalidate fences: each access bypasses the non-coherent cache state.
+__device__ __forceinline__ void st_agent_f32(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent_f32(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void st_agent_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_agent_u32(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory operation of this wave has completed
+// (gfx9 encoding: vmcnt = 0, expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vmem_all() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+}  // namespace lrk

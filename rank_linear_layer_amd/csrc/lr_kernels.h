@@ -1,0 +1,75 @@
+// Internal interface between the C-ABI host library and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lrk {
+
+// ---------------------------------------------------------------- decode ---
+// Tile geometry of the fused decode kernel (M <= 16).
+constexpr int kDecThreads = 256;  // 4 waves
+constexpr int kDecWaves = 4;
+constexpr int kDecJS = 120;       // rank columns per j-slice (15 producing lanes x 8)
+constexpr int kDecKT = 32;        // K rows per k-tile (one MFMA K-step)
+constexpr int kDecNT = 120;       // output columns per n-tile
+constexpr int kDecMaxProj = 4;    // projections sharing X in one launch
+
+// One factorized projection inside a decode launch.  The launch's
+// workgroups [wg_begin, wg_begin + Jw*S) belong to it; workgroup
+// (js, s) = (local / S, local % S) computes the partial T of rank slice js
+// over K slice s, then the partial Y of rank slice js over N slice s.
+struct DecProj {
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* Y;
+  float* Tpart;     // [Jw*S][M][kDecJS]
+  float* Ypart;     // [S][Jw][ntps][M][kDecNT]
+  uint32_t* flags;  // [Jw*S] epoch stamps of finished T partials
+  uint32_t* ycnt;   // [S] arrival counters of Y partials (self-resetting)
+  uint32_t* ctrl;   // [0] generation, [1] finished n-slices, [2] spin-timeout flag
+  int r, N, Jw, S, ktps, ntps, wg_begin, pad_;
+};
+
+struct DecArgs {
+  const uint16_t* X;
+  int M, K, nproj, pad_;
+  DecProj p[kDecMaxProj];
+};
+
+hipError_t launch_decode(const DecArgs& args, int grid, hipStream_t stream);
+// Workgroups of the decode kernel that one compute unit holds at once (0 on error).
+int decode_blocks_per_cu();
+
+// --------------------------------------------------------------- prefill ---
+constexpr int kPreThreads = 256;  // 4 waves: 2 (M) x 2 (N)
+constexpr int kPreBM = 128;       // rows per workgroup tile
+constexpr int kPreBN = 240;       // columns per workgroup tile (2 waves x 120)
+constexpr int kPreKT = 32;
+
+// C[rows x out_cols] = P[rows x kd] . Q[kd x ldq] for one or two column
+// blocks in one launch.  P is k-contiguous (X or T); Q is row-major with
+// leading dimension ldq (= its column count) and qrows valid rows (rows
+// beyond qrows read as zero).  Output columns in [ldq, out_cols) are 0.
+struct PreOut {
+  const uint16_t* P;
+  const uint16_t* Q;
+  uint16_t* C;
+  int64_t ldp;      // leading dimension of P
+  int64_t kd;       // reduction length
+  int64_t ldq;      // = valid columns of Q
+  int64_t qrows;    // valid rows of Q
+  int64_t ldc;      // leading dimension of C
+  int64_t out_cols; // columns of C to write
+  int col_tiles;    // column tiles of this block
+  int pad_;
+};
+struct PreArgs {
+  int64_t rows;     // M
+  int nout;         // 1 or 2 column blocks
+  int row_tiles;
+  PreOut o[2];
+};
+hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream);
+
+}  // namespace lrk

@@ -1,0 +1,325 @@
+// C-ABI host library of the factorized linear layer (see include/lr_linear.h).
+//
+// Owns: argument validation (lr_validate.h), the per-shape partition chosen
+// at create time, the device workspace, and kernel launches on the caller's
+// stream.  Every step of Y = (X.A).B runs in the HIP kernels of
+// lr_decode.hip and lr_prefill.hip; nothing here computes on the host.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/lr_linear.h"
+#include "lr_kernels.h"
+#include "lr_validate.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lr_status fail(lr_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lr_status fail(lr_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+lr_status hip_fail(hipError_t e, const char* what) {
+  return fail(LR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+struct lr_linear {
+  int64_t K, r, N, max_M, r_pad;
+  uint32_t flags;
+  int device;
+  const uint16_t* A;
+  const uint16_t* B;
+  // workspace
+  void* ws;
+  size_t ws_bytes;
+  // decode partition and workspace views
+  bool has_decode;
+  lrv::DecPart dp;
+  int dec_max_M;
+  uint32_t* ctrl;
+  uint32_t* flags_buf;
+  uint32_t* ycnt;
+  float* Tpart;
+  float* Ypart;
+  // prefill workspace: T [max_M x r_pad] bf16
+  bool has_prefill;
+  uint16_t* Tbuf;
+};
+
+namespace {
+
+bool use_decode(const lr_linear* h, int64_t M) {
+  if (h->flags & LR_FLAG_FORCE_DECODE) return true;
+  if (h->flags & LR_FLAG_FORCE_PREFILL) return false;
+  return M <= LR_DECODE_MAX_M;
+}
+
+// Fill the kernel-side descriptor of one projection in a decode launch.
+lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
+  lrk::DecProj p;
+  p.A = h->A;
+  p.B = h->B;
+  p.Y = Y;
+  p.Tpart = h->Tpart;
+  p.Ypart = h->Ypart;
+  p.flags = h->flags_buf;
+  p.ycnt = h->ycnt;
+  p.ctrl = h->ctrl;
+  p.r = (int)h->r;
+  p.N = (int)h->N;
+  p.Jw = h->dp.Jw;
+  p.S = h->dp.S;
+  p.ktps = h->dp.ktps;
+  p.ntps = h->dp.ntps;
+  p.wg_begin = wg_begin;
+  p.pad_ = 0;
+  return p;
+}
+
+int num_cus(int device) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0) cus = 256;
+  return cus;
+}
+
+lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
+                     hipStream_t stream) {
+  lrk::DecArgs a;
+  memset(&a, 0, sizeof a);
+  a.X = (const uint16_t*)X;
+  a.M = (int)M;
+  a.K = (int)hs[0]->K;
+  a.nproj = n;
+  int wg = 0;
+  for (int i = 0; i < n; ++i) {
+    a.p[i] = dec_proj(hs[i], Ys[i], wg);
+    wg += hs[i]->dp.Jw * hs[i]->dp.S;
+  }
+  hipError_t e = lrk::launch_decode(a, wg, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return LR_OK;
+}
+
+lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
+                      hipStream_t stream) {
+  // phase 1: T_i = X . A_i (both projections in one launch)
+  lrk::PreArgs a1;
+  memset(&a1, 0, sizeof a1);
+  a1.rows = M;
+  a1.nout = n;
+  a1.row_tiles = (int)lrv::ceil_div(M, lrk::kPreBM);
+  for (int i = 0; i < n; ++i) {
+    const lr_linear* h = hs[i];
+    lrk::PreOut& o = a1.o[i];
+    o.P = (const uint16_t*)X;
+    o.ldp = h->K;
+    o.kd = h->K;
+    o.Q = h->A;
+    o.ldq = h->r;
+    o.qrows = h->K;
+    o.C = h->Tbuf;
+    o.ldc = h->r_pad;
+    o.out_cols = h->r_pad;
+    o.col_tiles = (int)lrv::ceil_div(h->r_pad, lrk::kPreBN);
+  }
+  hipError_t e = lrk::launch_prefill_gemm(a1, stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill phase-1 launch");
+  // phase 2: Y_i = T_i . B_i
+  lrk::PreArgs a2;
+  memset(&a2, 0, sizeof a2);
+  a2.rows = M;
+  a2.nout = n;
+  a2.row_tiles = a1.row_tiles;
+  for (int i = 0; i < n; ++i) {
+    const lr_linear* h = hs[i];
+    lrk::PreOut& o = a2.o[i];
+    o.P = h->Tbuf;
+    o.ldp = h->r_pad;
+    o.kd = h->r_pad;
+    o.Q = h->B;
+    o.ldq = h->N;
+    o.qrows = h->r;
+    o.C = Ys[i];
+    o.ldc = h->N;
+    o.out_cols = h->N;
+    o.col_tiles = (int)lrv::ceil_div(h->N, lrk::kPreBN);
+  }
+  e = lrk::launch_prefill_gemm(a2, stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill phase-2 launch");
+  return LR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lr_status_str(lr_status s) {
+  switch (s) {
+    case LR_OK: return "LR_OK";
+    case LR_ERR_INVALID_ARG: return "LR_ERR_INVALID_ARG";
+    case LR_ERR_UNSUPPORTED: return "LR_ERR_UNSUPPORTED";
+    case LR_ERR_OUT_OF_MEMORY: return "LR_ERR_OUT_OF_MEMORY";
+    case LR_ERR_HIP: return "LR_ERR_HIP";
+  }
+  return "LR_ERR_UNKNOWN";
+}
+
+const char* lr_last_error(void) { return g_err; }
+
+lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, const void* A, const void* B,
+                           int64_t max_M, uint32_t flags) {
+  if (!out) return fail(LR_ERR_INVALID_ARG, "out must be non-null");
+  *out = nullptr;
+  lr_status st = lrv::check_create(K, r, N, A, B, max_M, flags, g_err, sizeof g_err);
+  if (st != LR_OK) return st;
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(LR_ERR_UNSUPPORTED, "device %d is %s; these kernels are built for gfx950", dev, prop.gcnArchName);
+
+  lr_linear* h = new (std::nothrow) lr_linear;
+  if (!h) return fail(LR_ERR_OUT_OF_MEMORY, "host allocation failed");
+  memset(h, 0, sizeof *h);
+  h->K = K;
+  h->r = r;
+  h->N = N;
+  h->max_M = max_M;
+  h->r_pad = lrv::round_up(r, 32);
+  h->flags = flags;
+  h->device = dev;
+  h->A = (const uint16_t*)A;
+  h->B = (const uint16_t*)B;
+
+  h->has_decode = !(flags & LR_FLAG_FORCE_PREFILL) && max_M >= 1;
+  h->has_prefill = !(flags & LR_FLAG_FORCE_DECODE) && (max_M > LR_DECODE_MAX_M || (flags & LR_FLAG_FORCE_PREFILL));
+
+  size_t off = 0;
+  size_t o_ctrl = 0, o_flags = 0, o_ycnt = 0, o_tpart = 0, o_ypart = 0, o_tbuf = 0;
+  if (h->has_decode) {
+    h->dec_max_M = (int)(max_M < LR_DECODE_MAX_M ? max_M : LR_DECODE_MAX_M);
+    const int occ = lrk::decode_blocks_per_cu();
+    if (occ < 1) {
+      delete h;
+      return fail(LR_ERR_HIP, "decode kernel cannot be resident on this device");
+    }
+    h->dp = lrv::decode_partition(K, r, N, num_cus(dev));
+    const int64_t G = (int64_t)h->dp.Jw * h->dp.S;
+    o_ctrl = off;
+    off = align_up(off + 64);
+    o_flags = off;
+    off = align_up(off + (size_t)G * 4);
+    o_ycnt = off;
+    off = align_up(off + (size_t)h->dp.S * 4);
+    o_tpart = off;
+    off = align_up(off + (size_t)G * h->dec_max_M * lrk::kDecJS * 4);
+    o_ypart = off;
+    off = align_up(off + (size_t)G * h->dp.ntps * h->dec_max_M * lrk::kDecNT * 4);
+  }
+  if (h->has_prefill) {
+    o_tbuf = off;
+    off = align_up(off + (size_t)max_M * h->r_pad * 2);
+  }
+  h->ws_bytes = off;
+  if (off > 0) {
+    e = hipMalloc(&h->ws, off);
+    if (e != hipSuccess) {
+      delete h;
+      (void)hipGetLastError();
+      return fail(LR_ERR_OUT_OF_MEMORY, "workspace hipMalloc(%zu): %s", off, hipGetErrorString(e));
+    }
+    e = hipMemset(h->ws, 0, off);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      (void)hipFree(h->ws);
+      delete h;
+      return hip_fail(e, "workspace clear");
+    }
+  }
+  char* base = (char*)h->ws;
+  if (h->has_decode) {
+    h->ctrl = (uint32_t*)(base + o_ctrl);
+    h->flags_buf = (uint32_t*)(base + o_flags);
+    h->ycnt = (uint32_t*)(base + o_ycnt);
+    h->Tpart = (float*)(base + o_tpart);
+    h->Ypart = (float*)(base + o_ypart);
+  }
+  if (h->has_prefill) h->Tbuf = (uint16_t*)(base + o_tbuf);
+  *out = h;
+  return LR_OK;
+}
+
+lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, void* stream) {
+  if (!h) return fail(LR_ERR_INVALID_ARG, "handle is null");
+  lrv::Shape s{h->K, h->r, h->N, h->max_M, h->A, h->B};
+  lr_status st = lrv::check_run(s, X, Y, M, g_err, sizeof g_err);
+  if (st != LR_OK || M == 0) return st;
+  uint16_t* Ys[1] = {(uint16_t*)Y};
+  const lr_linear* hs[1] = {h};
+  if (use_decode(h, M)) return run_decode(hs, Ys, 1, X, M, (hipStream_t)stream);
+  return run_prefill(hs, Ys, 1, X, M, (hipStream_t)stream);
+}
+
+lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const void* X, void* Y_gate, void* Y_up,
+                            int64_t M, void* stream) {
+  if (!gate || !up) return fail(LR_ERR_INVALID_ARG, "gate and up handles must be non-null");
+  if (gate == up) return fail(LR_ERR_INVALID_ARG, "gate and up must be distinct handles (each owns a workspace)");
+  lrv::Shape sg{gate->K, gate->r, gate->N, gate->max_M, gate->A, gate->B};
+  lrv::Shape su{up->K, up->r, up->N, up->max_M, up->A, up->B};
+  lr_status st = lrv::check_packed(sg, su, X, Y_gate, Y_up, M, g_err, sizeof g_err);
+  if (st != LR_OK || M == 0) return st;
+  const bool dg = use_decode(gate, M), du = use_decode(up, M);
+  if (dg != du) return fail(LR_ERR_UNSUPPORTED, "gate and up handles choose different kernels for M=%lld", (long long)M);
+  uint16_t* Ys[2] = {(uint16_t*)Y_gate, (uint16_t*)Y_up};
+  const lr_linear* hs[2] = {gate, up};
+  if (dg) {
+    // One launch when both projections' workgroups fit on the device at
+    // once (every exchange group must be resident); else one per projection.
+    const int64_t G = (int64_t)gate->dp.Jw * gate->dp.S + (int64_t)up->dp.Jw * up->dp.S;
+    if (G <= (int64_t)num_cus(gate->device) * lrk::decode_blocks_per_cu()) return run_decode(hs, Ys, 2, X, M, (hipStream_t)stream);
+    st = run_decode(hs, Ys, 1, X, M, (hipStream_t)stream);
+    if (st != LR_OK) return st;
+    return run_decode(hs + 1, Ys + 1, 1, X, M, (hipStream_t)stream);
+  }
+  return run_prefill(hs, Ys, 2, X, M, (hipStream_t)stream);
+}
+
+void lr_linear_destroy(lr_linear* h) {
+  if (!h) return;
+  if (h->ws) (void)hipFree(h->ws);
+  delete h;
+}
+
+lr_status lr_linear_describe(const lr_linear* h, char* buf, int64_t len) {
+  if (!h || !buf || len <= 0) return fail(LR_ERR_INVALID_ARG, "null handle or buffer");
+  snprintf(buf, (size_t)len,
+           "K=%lld r=%lld N=%lld r_pad=%lld max_M=%lld decode=%d[Jw=%d S=%d ktps=%d ntps=%d grid=%d] "
+           "prefill=%d workspace=%zu",
+           (long long)h->K, (long long)h->r, (long long)h->N, (long long)h->r_pad, (long long)h->max_M,
+           (int)h->has_decode, h->dp.Jw, h->dp.S, h->dp.ktps, h->dp.ntps, h->dp.Jw * h->dp.S, (int)h->has_prefill,
+           h->ws_bytes);
+  return LR_OK;
+}
+
+int64_t lr_linear_workspace_bytes(const lr_linear* h) { return h ? (int64_t)h->ws_bytes : 0; }
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// Argument validation and work partitioning of the C ABI.  Pure host C++
+// with no HIP dependency, so it is unit-tested on the CPU (g++), and the
+// same code runs inside the library.
+#pragma once
+
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/lr_linear.h"
+
+namespace lrv {
+
+constexpr int kDecodeMaxM = LR_DECODE_MAX_M;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+inline Range span(const void* p, int64_t elems) {
+  uintptr_t a = (uintptr_t)p;
+  return Range{a, a + (uintptr_t)(elems > 0 ? elems : 0) * 2u};
+}
+inline bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest dimension accepted; keeps every flat index well inside int64 and
+// every per-row index inside int32.
+constexpr int64_t kMaxDim = (int64_t)1 << 24;
+
+inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, const void* B, int64_t max_M,
+                              uint32_t flags, char* err, size_t errlen) {
+  if (!A || !B) { snprintf(err, errlen, "A and B must be non-null device pointers"); return LR_ERR_INVALID_ARG; }
+  if (K < 1 || r < 1 || N < 1) {
+    snprintf(err, errlen, "K, r and N must be >= 1 (got K=%lld r=%lld N=%lld)", (long long)K, (long long)r, (long long)N);
+    return LR_ERR_INVALID_ARG;
+  }
+  if (K > kMaxDim || r > kMaxDim || N > kMaxDim || max_M > kMaxDim) {
+    snprintf(err, errlen, "dimension above the supported maximum %lld", (long long)kMaxDim);
+    return LR_ERR_INVALID_ARG;
+  }
+  if (max_M < 0) { snprintf(err, errlen, "max_M must be >= 0 (got %lld)", (long long)max_M); return LR_ERR_INVALID_ARG; }
+  if (!aligned16(A) || !aligned16(B)) { snprintf(err, errlen, "A and B must be 16-byte aligned"); return LR_ERR_INVALID_ARG; }
+  if (overlaps(span(A, K * r), span(B, r * N))) {
+    // Sharing storage between the factors is allowed (read-only); nothing to check.
+  }
+  const uint32_t known = LR_FLAG_FORCE_DECODE | LR_FLAG_FORCE_PREFILL;
+  if (flags & ~known) { snprintf(err, errlen, "unknown flag bits 0x%x", flags & ~known); return LR_ERR_UNSUPPORTED; }
+  if ((flags & LR_FLAG_FORCE_DECODE) && (flags & LR_FLAG_FORCE_PREFILL)) {
+    snprintf(err, errlen, "FORCE_DECODE and FORCE_PREFILL are exclusive");
+    return LR_ERR_INVALID_ARG;
+  }
+  if ((flags & LR_FLAG_FORCE_DECODE) && max_M > kDecodeMaxM) {
+    snprintf(err, errlen, "FORCE_DECODE needs max_M <= %d (got %lld)", kDecodeMaxM, (long long)max_M);
+    return LR_ERR_UNSUPPORTED;
+  }
+  return LR_OK;
+}
+
+struct Shape {
+  int64_t K, r, N, max_M;
+  const void* A;
+  const void* B;
+};
+
+inline lr_status check_run(const Shape& s, const void* X, const void* Y, int64_t M, char* err, size_t errlen) {
+  if (M < 0 || M > s.max_M) {
+    snprintf(err, errlen, "M=%lld outside [0, max_M=%lld]", (long long)M, (long long)s.max_M);
+    return LR_ERR_INVALID_ARG;
+  }
+  if (M == 0) return LR_OK;
+  if (!X || !Y) { snprintf(err, errlen, "X and Y must be non-null device pointers"); return LR_ERR_INVALID_ARG; }
+  if (!aligned16(X) || !aligned16(Y)) { snprintf(err, errlen, "X and Y must be 16-byte aligned"); return LR_ERR_INVALID_ARG; }
+  const Range ry = span(Y, M * s.N);
+  if (overlaps(ry, span(X, M * s.K)) || overlaps(ry, span(s.A, s.K * s.r)) || overlaps(ry, span(s.B, s.r * s.N))) {
+    snprintf(err, errlen, "Y overlaps an input (X, A or B)");
+    return LR_ERR_INVALID_ARG;
+  }
+  return LR_OK;
+}
+
+inline lr_status check_packed(const Shape& g, const Shape& u, const void* X, const void* Yg, const void* Yu, int64_t M,
+                              char* err, size_t errlen) {
+  if (g.K != u.K) {
+    snprintf(err, errlen, "gate.K=%lld differs from up.K=%lld", (long long)g.K, (long long)u.K);
+    return LR_ERR_INVALID_ARG;
+  }
+  lr_status st = check_run(g, X, Yg, M, err, errlen);
+  if (st != LR_OK) return st;
+  st = check_run(u, X, Yu, M, err, errlen);
+  if (st != LR_OK) return st;
+  if (M == 0) return LR_OK;
+  const Range rg = span(Yg, M * g.N), ru = span(Yu, M * u.N);
+  if (overlaps(rg, ru)) { snprintf(err, errlen, "Y_gate overlaps Y_up"); return LR_ERR_INVALID_ARG; }
+  if (overlaps(rg, span(u.A, u.K * u.r)) || overlaps(rg, span(u.B, u.r * u.N)) ||
+      overlaps(ru, span(g.A, g.K * g.r)) || overlaps(ru, span(g.B, g.r * g.N))) {
+    snprintf(err, errlen, "an output overlaps the other projection's factors");
+    return LR_ERR_INVALID_ARG;
+  }
+  return LR_OK;
+}
+
+// ------------------------------------------------------------ partition ---
+// Decode kernel: rank slices of 120 columns (Jw of them); K and N cut into S
+// slices.  S minimises the bytes streamed by the busiest workgroup, subject
+// to Jw * S <= budget (one workgroup per compute unit), ties to smaller S.
+struct DecPart {
+  int Jw, S, ktps, ntps;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget) {
+  const int64_t js_w = 120, kt = 32, nt = 120;
+  DecPart p;
+  p.Jw = (int)ceil_div(r, js_w);
+  const int64_t nk = ceil_div(K, kt), nn = ceil_div(N, nt);
+  int64_t smax = budget / p.Jw;
+  if (smax < 1) smax = 1;
+  const int64_t useful = nk > nn ? nk : nn;
+  if (smax > useful) smax = useful;
+  int64_t best_s = 1, best_cost = -1;
+  for (int64_t S = 1; S <= smax; ++S) {
+    const int64_t cost = ceil_div(nk, S) * kt * js_w + ceil_div(nn, S) * js_w * nt;  // elements per WG
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_s = S; }
+  }
+  p.S = (int)best_s;
+  p.ktps = (int)ceil_div(nk, best_s);
+  p.ntps = (int)ceil_div(nn, best_s);
+  return p;
+}
+
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+}  // namespace lrv

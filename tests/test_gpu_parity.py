@@ -1,0 +1,248 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 CPU
+oracle on the same seeded inputs.
+
+Bar (bf16 in, fp32 accumulate, bf16 out), per output tensor:
+    rel_fro = ||Y_gpu - Y_ref||_F / ||Y_ref||_F <= 5e-3
+    max_abs = max|Y_gpu - Y_ref| / max|Y_ref|   <= 2e-2
+Full-size workloads compare sampled outputs that the oracle computes one by
+one; smaller cases compare every element.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import rank_linear_layer_amd as lrl
+from rank_linear_layer_amd import configs, datagen
+from tests.gpu_util import assert_parity, banner, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lrl.load_library()  # raises loudly if the HIP library is missing
+    return torch
+
+
+def run_case(M, K, r, N, seed, flags=0, max_M=None, full=True, rows=None, cols=None):
+    banner("case M=%d K=%d r=%d N=%d flags=%d seed=%d" % (M, K, r, N, flags, seed))
+    Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, seed)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=max_M or M, flags=flags)
+    Y = lin(to_dev(Xb))
+    yb = to_bits(Y)
+    if full:
+        ref = oracle.lowrank_bf16(Xb, Ab, Bb)
+        p = assert_parity(yb, ref, "M=%d K=%d r=%d N=%d" % (M, K, r, N))
+    else:
+        ref = oracle.lowrank_bf16_sampled(Xb, Ab, Bb, rows, cols)
+        p = assert_parity(yb[np.ix_(rows, cols)], ref, "sampled M=%d K=%d r=%d N=%d" % (M, K, r, N))
+        assert np.all(np.isfinite(datagen.bf16_bits_to_f32(yb))), "non-finite output"
+    return p, lin, (Xb, Ab, Bb), yb
+
+
+# ------------------------------------------------------------ workloads ---
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_tiny_decode(M):
+    c = configs.TINY
+    run_case(M, c["K"], c["r"], c["N"], configs.seed_base(0))
+
+
+@pytest.mark.parametrize("M", [16, 17, 200])
+def test_tiny_prefill(M):
+    c = configs.TINY
+    run_case(M, c["K"], c["r"], c["N"], configs.seed_base(0) + 3, flags=lrl.LR_FLAG_FORCE_PREFILL)
+
+
+def test_eckart_young_factors_decode_and_prefill(gpu):
+    torch = gpu
+    c = configs.EY
+    W, A64, B64, Ab, Bb = datagen.svd_factor_inputs(c["K"], c["N"], c["k"], c["w_seed"])
+    # X random (decode) and X = I (prefill, Y = the rank-5 reconstruction)
+    Xb = datagen.normal_bf16((16, c["K"]), 1.0, c["x_seed"])
+    eye = datagen.bf16_bits_from_f32(np.eye(c["K"], dtype=np.float32))
+    for X_bits, flags in ((Xb, 0), (eye, 0), (eye[:16], lrl.LR_FLAG_FORCE_DECODE)):
+        M = X_bits.shape[0]
+        banner("eckart-young M=%d flags=%d" % (M, flags))
+        lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=flags)
+        yb = to_bits(lin(to_dev(X_bits)))
+        ref = oracle.lowrank_bf16(X_bits, Ab, Bb)
+        assert_parity(yb, ref, "EY M=%d" % M)
+    # X = I: the GPU reconstruction error is the tail energy of W's spectrum
+    # up to the bf16 rounding of factors and output.
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=c["K"])
+    Y = datagen.bf16_bits_to_f32(to_bits(lin(to_dev(eye)))).astype(np.float64)
+    S = np.linalg.svd(W, compute_uv=False)
+    tail = float(np.sum(S[c["k"]:] ** 2))
+    assert abs(float(np.sum((W - Y) ** 2)) - tail) <= 2e-3 * tail
+    del torch
+
+
+def test_qproj_decode_full():
+    c = configs.QPROJ_DECODE
+    p, lin, _, _ = run_case(c["M"], c["K"], c["r"], c["N"], configs.seed_base(c["index"]))
+    banner("q_proj decode parity %s plan %s" % (p, lin.describe()))
+
+
+def test_mlp_up_prefill_sampled():
+    c = configs.MLP_UP_PREFILL
+    rows = np.array([0, 1, 127, 128, 2047, 4094, 4095])
+    cols = np.unique(np.concatenate([np.arange(0, 20), np.arange(230, 250), np.arange(7000, 7010),
+                                     np.arange(14300, 14336)]))
+    p, lin, _, _ = run_case(c["M"], c["K"], c["r"], c["N"], configs.seed_base(c["index"]), full=False,
+                            rows=rows, cols=cols)
+    banner("mlp_up prefill sampled parity %s plan %s" % (p, lin.describe()))
+
+
+@pytest.mark.parametrize("name", ["q", "k", "down"])
+def test_layer_projections_decode_m1(name):
+    proj = {p.name: p for p in configs.LAYER_PROJS}[name]
+    idx = [p.name for p in configs.LAYER_PROJS].index(name)
+    run_case(1, proj.K, proj.r, proj.N, configs.seed_base(configs.LAYER_INDEX, idx))
+
+
+@pytest.mark.parametrize("N,r", [(4096, 1000), (3999, 1001), (3999, 1037), (4096, 1063), (3999, 1100)])
+def test_alignment_sweep_points(N, r):
+    seed = configs.sweep_seed(N, r)
+    run_case(1, configs.SWEEP_K, r, N, seed)
+    rows = np.array([0, 255, 511])
+    cols = np.array([0, 1, 2, 119, 120, 121, 2000, N - 2, N - 1])
+    run_case(512, configs.SWEEP_K, r, N, seed, full=False, rows=rows, cols=cols)
+
+
+# ----------------------------------------------------- adversarial grid ---
+
+GRID = []
+_r = [1, 2, 5, 7, 8, 15, 16, 17, 31, 32, 33, 119, 120, 121, 240, 241]
+_N = [1, 7, 48, 119, 120, 121, 239, 241, 3999]
+_M = [1, 2, 5, 15, 16, 17, 31, 64, 130]
+_K = [8, 31, 64, 100, 257, 33]
+for i, r in enumerate(_r):
+    for j in range(3):
+        GRID.append((_M[(i + 3 * j) % len(_M)], _K[(i + j) % len(_K)], r, _N[(2 * i + j) % len(_N)]))
+
+
+@pytest.mark.parametrize("M,K,r,N", GRID)
+def test_adversarial_shapes(M, K, r, N):
+    run_case(M, K, r, N, 9000 + 31 * r + N + M)
+
+
+@pytest.mark.parametrize("M,K,r,N,flags", [(3, 96, 13, 29, lrl.LR_FLAG_FORCE_PREFILL),
+                                           (40, 40, 9, 17, 0), (16, 2000, 300, 250, lrl.LR_FLAG_FORCE_PREFILL),
+                                           (2, 2000, 300, 250, 0)])
+def test_forced_paths(M, K, r, N, flags):
+    run_case(M, K, r, N, 4400 + M, flags=flags)
+
+
+# ---------------------------------------------------------------- packed ---
+
+@pytest.mark.parametrize("M", [1, 4, 64])
+def test_mlp_packed_matches_oracle_and_separate_runs(M):
+    K, r, N = 512, 67, 700
+    banner("packed M=%d" % M)
+    Xb = datagen.normal_bf16((M, K), 1.0, 31)
+    _, Agb, Bgb = datagen.factorized_inputs(1, K, r, N, 41)
+    _, Aub, Bub = datagen.factorized_inputs(1, K, r + 30, N - 100, 51)
+    gate = lrl.LowRankLinear(to_dev(Agb), to_dev(Bgb), max_M=M)
+    up = lrl.LowRankLinear(to_dev(Aub), to_dev(Bub), max_M=M)
+    X = to_dev(Xb)
+    Yg, Yu = lrl.mlp_packed(gate, up, X)
+    yg, yu = to_bits(Yg), to_bits(Yu)
+    assert_parity(yg, oracle.lowrank_bf16(Xb, Agb, Bgb), "packed gate")
+    assert_parity(yu, oracle.lowrank_bf16(Xb, Aub, Bub), "packed up")
+    assert np.array_equal(yg, to_bits(gate(X)))
+    assert np.array_equal(yu, to_bits(up(X)))
+
+
+# ----------------------------------------------------- invariants/edges ---
+
+@pytest.mark.parametrize("M,N,flags", [(3, 3999, 0), (33, 3999, 0), (5, 241, lrl.LR_FLAG_FORCE_PREFILL)])
+def test_canary_guards_and_poison(gpu, M, N, flags):
+    torch = gpu
+    K, r = 256, 37
+    banner("canary M=%d N=%d" % (M, N))
+    Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 77)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=flags)
+    G = 64  # guard elements on each side (128 bytes keeps Y 16-byte aligned)
+    poison = 0x7FC1
+    big = torch.full((M * N + 2 * G,), poison, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    Y = big[G:G + M * N].view(M, N)
+    lin(to_dev(Xb), out=Y)
+    allbits = to_bits(big)
+    assert np.all(allbits[:G] == poison) and np.all(allbits[G + M * N:] == poison), "guard zone written"
+    assert_parity(allbits[G:G + M * N].reshape(M, N), oracle.lowrank_bf16(Xb, Ab, Bb), "canary")
+
+
+@pytest.mark.parametrize("M,flags", [(8, 0), (48, 0)])
+def test_deterministic_bitwise(M, flags):
+    K, r, N = 1024, 333, 1500
+    Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 1234)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=flags)
+    X = to_dev(Xb)
+    outs = [to_bits(lin(X)) for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
+def test_repeated_calls_new_inputs_and_streams(gpu):
+    torch = gpu
+    K, r, N = 700, 150, 900
+    _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 555)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=16)
+    side = torch.cuda.Stream()
+    for i, M in enumerate([1, 16, 7, 16, 3, 1]):
+        Xb = datagen.normal_bf16((M, K), 1.0, 600 + i)
+        X = to_dev(Xb)
+        if i % 2:
+            with torch.cuda.stream(side):
+                Y = lin(X)
+            side.synchronize()
+        else:
+            Y = lin(X)
+        assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, Ab, Bb), "call %d M=%d" % (i, M))
+
+
+def test_zero_rank_padding_gpu(gpu):
+    torch = gpu
+    M, K, r, N = 8, 512, 107, 512
+    Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 808)
+    X = to_dev(Xb)
+    base = to_bits(lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M)(X))
+    for p in (1, 13, 21, 200):
+        Ap = np.concatenate([Ab, np.zeros((K, p), np.uint16)], axis=1)
+        Bp = np.concatenate([Bb, np.zeros((p, N), np.uint16)], axis=0)
+        yp = to_bits(lrl.LowRankLinear(to_dev(Ap), to_dev(Bp), max_M=M)(X))
+        if (r + p + 119) // 120 == (r + 119) // 120:
+            assert np.array_equal(yp, base), "padding by %d changed the result" % p
+        else:
+            assert_parity(yp, oracle.lowrank_bf16(Xb, Ab, Bb), "padded by %d" % p)
+    del torch
+
+
+def test_error_paths_on_device(gpu):
+    torch = gpu
+    K, r, N = 64, 5, 48
+    _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 3)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=4)
+    X = to_dev(datagen.normal_bf16((5, K), 1.0, 4))
+    with pytest.raises(lrl.LRError) as ei:
+        lin(X)  # M = 5 > max_M
+    assert ei.value.status == lrl.LR_ERR_INVALID_ARG
+    # M = 0 launches nothing and succeeds
+    Y0 = lin(X[:0])
+    assert Y0.shape == (0, N)
+    # Y overlapping X is rejected
+    buf = torch.zeros(4 * max(K, N) + 64, dtype=torch.bfloat16, device="cuda")
+    Xv = buf[:4 * K].view(4, K)
+    Yv = buf[:4 * N].view(4, N)
+    import ctypes
+    st = lrl.load_library().lr_linear_run(lin.handle, ctypes.c_void_p(Xv.data_ptr()), ctypes.c_void_p(Yv.data_ptr()),
+                                          4, None)
+    assert st == lrl.LR_ERR_INVALID_ARG
+    # gate and up with different K are rejected
+    _, A2, B2 = datagen.factorized_inputs(1, K + 8, r, N, 5)
+    other = lrl.LowRankLinear(to_dev(A2), to_dev(B2), max_M=4)
+    with pytest.raises(lrl.LRError):
+        lrl.mlp_packed(lin, other, X[:2])
