@@ -4,24 +4,24 @@
 // ...", "Why theoretical FLOPs saved does not equal faster inference" and
 // Q3: thin GEMMs, weight streaming and launch overhead dominate; a two-
 // kernel low-rank path adds a launch and intermediate-tensor traffic).  This
-// kernel therefore reads A and B exactly once, keeps T = X . A off HBM-bound
+// kernel therefore reads A and B exactly once, never sends T through HBM
 // round trips (partials live in a small L2/MALL-resident workspace), and
 // makes one launch.
 //
-// Work split (host plan in lr_linear.cpp): the rank is cut into Jw slices of
-// 120 columns, K and N into S slices.  Workgroup (js, s):
-//   1. GEMM1 partial: T_s[:, js] = X[:, Ks] . A[Ks, js]  (MFMA, split-K);
-//      the four waves take alternate 32-row k-tiles; the WG sums them in
-//      LDS and publishes the partial with device-coherent stores plus an
-//      epoch-stamped flag.
-//   2. Prefetch of its first two B tiles is issued before waiting, so the
-//      hand-off overlaps B streaming.
-//   3. Waits for the S partials of slice js, sums them in fixed order
-//      (deterministic), splits T into bf16 hi + lo halves (two MFMAs keep
-//      ~16 mantissa bits of T), and computes the partial
-//      Y_js[:, Ns] = T[:, js] . B[js, Ns] for its n-slice.
-//   4. The last of the Jw workgroups to publish a partial for n-slice s
-//      sums the Jw partials in fixed order and writes bf16 Y.
+// Work split (host plan in lr_validate.h): the rank is cut into Jw slices
+// of 120 columns, K and N into S slices.  Workgroup (js, s):
+//   1. issues the loads of its A tiles and of its first two B tiles at once,
+//      so all of its HBM traffic is in flight from the start;
+//   2. GEMM1 partial T_s[:, js] = X[:, Ks] . A[Ks, js] (MFMA); the four waves
+//      take alternate 32-row k-tiles and are summed in LDS;
+//   3. T hand-off: the partial is published with device-coherent stores; the
+//      last of the S workgroups of slice js to arrive sums the S partials in
+//      fixed order and publishes T_js with an epoch-stamped flag, which the
+//      others poll;
+//   4. GEMM2 partial Y_js[:, Ns] = T_js . B[js, Ns] with T split into bf16
+//      hi + lo halves (two MFMAs keep ~16 mantissa bits of T);
+//   5. the last of the Jw workgroups to publish a partial for n-slice s sums
+//      the Jw partials in fixed order and writes bf16 Y.
 // No floating-point atomics: results are bitwise reproducible.  Counters
 // reset themselves and a device-side generation number stamps each launch,
 // so no memset is needed between calls.
@@ -32,29 +32,69 @@ namespace lrk {
 
 constexpr uint32_t kSpinLimit = 1u << 22;
 
+// Optional phase timestamps (constant-rate device clock), compiled in only
+// with -DLR_DECODE_TRACE; used to see where a launch spends its time.
+#ifdef LR_DECODE_TRACE
+#define DEC_TRACE(i)                                                                              \
+  do {                                                                                            \
+    if (a.trace && tid == 0) a.trace[blockIdx.x * kDecTracePoints + (i)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define DEC_TRACE(i) \
+  do {               \
+  } while (0)
+#endif
+
 struct RawTile {
   u32x4_t c[8];
 };
 
 // Raw chunk loads of one 32-row x 120-column tile (rows rbase + 8g + q).
-__device__ __forceinline__ void load_tile_raw(RawTile& t, const uint16_t* __restrict__ base, int64_t rbase,
-                                              int64_t nrows, int64_t ld, int64_t colbase, int lane16, int g,
-                                              int64_t total) {
+__device__ __forceinline__ void load_tile_raw(RawTile& t, rsrc_t r, int64_t rbase, int64_t ld, int64_t colbase,
+                                              int lane16, int g) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) t.c[q] = load_row_raw(base, rbase + 8 * g + q, nrows, ld, colbase, lane16, total);
+  for (int q = 0; q < 8; ++q) t.c[q] = load_row_raw(r, rbase + 8 * g + q, ld, colbase, lane16);
 }
 
 // Realign + transpose a raw tile into 8 MFMA B-operands (one per column e).
-__device__ __forceinline__ void tile_operands(const RawTile& t, u32x4_t op[8], int64_t ld, int64_t colbase,
-                                              int lane16, int64_t ncols) {
+// Rows >= row_end are zeroed.
+__device__ __forceinline__ void tile_operands(const RawTile& t, u32x4_t op[8], int64_t rbase, int g,
+                                              int64_t row_end, int64_t ld, int64_t colbase, int lane16,
+                                              int64_t ncols) {
   u32x4_t seg[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    // rows rbase + 8g + q with rbase, 8g multiples of 8: misalignment (q*ld) mod 8
+    // rbase and 8g are multiples of 8, so the misalignment is (q * ld + colbase) mod 8
     const int d = (int)(((int64_t)q * ld + colbase) & 7);
-    seg[q] = realign_segment(t.c[q], d, colbase + 8 * lane16, ncols);
+    seg[q] = realign_segment(t.c[q], d, colbase + 8 * lane16, ncols, rbase + 8 * g + q < row_end);
   }
   transpose8x8(seg, op);
+}
+
+// out[v] = sum over p < npart (in order) of the float4 at
+// base + p * pstride + (tid + 256 v) * 16, for vector indices < nvec.
+template <int V>
+__device__ __forceinline__ void sum_partials(rsrc_t ws, uint32_t base, uint32_t pstride, int npart, int nvec,
+                                             int tid, f32x4_t out[V]) {
+#pragma unroll
+  for (int v = 0; v < V; ++v) out[v] = zero4();
+  for (int p0 = 0; p0 < npart; p0 += 8) {
+    f32x4_t t[8][V];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int vi = tid + kDecThreads * v;
+        const bool ok = (p0 + u < npart) && (vi < nvec);
+        const uint32_t off = ok ? base + (uint32_t)(p0 + u) * pstride + (uint32_t)vi * 16u : base;
+        const f32x4_t x = buf_load16_coherent(ws, off);
+        t[u][v] = ok ? x : zero4();
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int v = 0; v < V; ++v) out[v] += t[u][v];
+  }
 }
 
 __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecArgs a) {
@@ -73,116 +113,147 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   const int local = (int)blockIdx.x - P.wg_begin;
   const int js = local / P.S, s = local % P.S;
   const int M = a.M, K = a.K, r = P.r, N = P.N;
-  const int64_t totA = (int64_t)K * r, totB = (int64_t)r * N;
 
+  const rsrc_t rA = make_rsrc(P.A, (int64_t)K * r * 2);
+  const rsrc_t rB = make_rsrc(P.B, (int64_t)r * N * 2);
+  const rsrc_t rX = make_rsrc(a.X, (int64_t)M * K * 2);
+  const rsrc_t rW = make_rsrc(P.ws, P.ws_bytes);
+
+  DEC_TRACE(0);
   if (tid == 0) sh_epoch = ld_agent_u32(P.ctrl) + 1u;
 
-  // ---------------------------------------------------------- GEMM1 ------
+  // ------------------------------------------------ issue all loads -----
   const int j0 = js * kDecJS;
   const int nk = (K + kDecKT - 1) / kDecKT;
   const int kt_beg = s * P.ktps;
   const int kt_end = min(nk, kt_beg + P.ktps);
   const bool xal = (K & 7) == 0;
 
-  f32x4_t acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = zero4();
-
-  {
-    RawTile t0, t1;
-    u32x4_t x0 = zerou4(), x1 = zerou4();
-    int kt = kt_beg + w;
-    if (kt < kt_end) {
-      load_tile_raw(t0, P.A, (int64_t)kt * kDecKT, K, r, j0, np, g, totA);
-      x0 = (np < M) ? load_kvec(a.X, np, M, K, (int64_t)kt * kDecKT + 8 * g, K, xal) : zerou4();
-    }
-    while (kt < kt_end) {
-      const int kn = kt + kDecWaves;
-      if (kn < kt_end) {
-        load_tile_raw(t1, P.A, (int64_t)kn * kDecKT, K, r, j0, np, g, totA);
-        x1 = (np < M) ? load_kvec(a.X, np, M, K, (int64_t)kn * kDecKT + 8 * g, K, xal) : zerou4();
-      }
-      {
-        u32x4_t op[8];
-        tile_operands(t0, op, r, j0, np, r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = mfma_16x16x32(x0, op[e], acc[e]);
-      }
-      kt = kn;
-      if (kt >= kt_end) break;
-      const int kn2 = kt + kDecWaves;
-      if (kn2 < kt_end) {
-        load_tile_raw(t0, P.A, (int64_t)kn2 * kDecKT, K, r, j0, np, g, totA);
-        x0 = (np < M) ? load_kvec(a.X, np, M, K, (int64_t)kn2 * kDecKT + 8 * g, K, xal) : zerou4();
-      }
-      {
-        u32x4_t op[8];
-        tile_operands(t1, op, r, j0, np, r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = mfma_16x16x32(x1, op[e], acc[e]);
-      }
-      kt = kn2;
-    }
-  }
-
-  // Prefetch the first two B tiles of this workgroup's n-slice (rows of this
-  // wave's 32-row j-tile) before the hand-off.
   const int nn = (N + kDecNT - 1) / kDecNT;
   const int nt_beg = s * P.ntps;
   const int nt_end = min(nn, nt_beg + P.ntps);
   const int64_t jrow0 = (int64_t)j0 + 32 * w;
-  const bool wave_has_rows = jrow0 < r && jrow0 < (int64_t)j0 + kDecJS;
-  RawTile b0, b1;
-  if (wave_has_rows && nt_beg < nt_end)
-    load_tile_raw(b0, P.B, jrow0, min64(r, (int64_t)j0 + kDecJS), N, (int64_t)nt_beg * kDecNT, np, g, totB);
-  if (wave_has_rows && nt_beg + 1 < nt_end)
-    load_tile_raw(b1, P.B, jrow0, min64(r, (int64_t)j0 + kDecJS), N, (int64_t)(nt_beg + 1) * kDecNT, np, g, totB);
+  const int64_t jrow_end = min64(r, (int64_t)j0 + kDecJS);
 
-  // WG reduction of the four waves' partial T, then publish it.
+  RawTile t0, t1, b0, b1;
+  u32x4_t x0 = zerou4(), x1 = zerou4();
+  int kt = kt_beg + w;
+  if (kt < kt_end) {
+    load_tile_raw(t0, rA, (int64_t)kt * kDecKT, r, j0, np, g);
+    x0 = load_kvec(rX, np, K, (int64_t)kt * kDecKT + 8 * g, K, xal);
+  }
+  if (kt + kDecWaves < kt_end) {
+    load_tile_raw(t1, rA, (int64_t)(kt + kDecWaves) * kDecKT, r, j0, np, g);
+    x1 = load_kvec(rX, np, K, (int64_t)(kt + kDecWaves) * kDecKT + 8 * g, K, xal);
+  }
+  if (nt_beg < nt_end) load_tile_raw(b0, rB, jrow0, N, (int64_t)nt_beg * kDecNT, np, g);
+  if (nt_beg + 1 < nt_end) load_tile_raw(b1, rB, jrow0, N, (int64_t)(nt_beg + 1) * kDecNT, np, g);
+
+  // ---------------------------------------------------------- GEMM1 ------
+  f32x4_t acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = zero4();
+  while (kt < kt_end) {
+    {
+      u32x4_t op[8];
+      tile_operands(t0, op, (int64_t)kt * kDecKT, g, K, r, j0, np, r);
+      const u32x4_t xm = kvec_mask(x0, (int64_t)kt * kDecKT + 8 * g, K);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = mfma_16x16x32(xm, op[e], acc[e]);
+    }
+    kt += kDecWaves;
+    if (kt + kDecWaves < kt_end) {
+      load_tile_raw(t0, rA, (int64_t)(kt + kDecWaves) * kDecKT, r, j0, np, g);
+      x0 = load_kvec(rX, np, K, (int64_t)(kt + kDecWaves) * kDecKT + 8 * g, K, xal);
+    }
+    if (kt >= kt_end) break;
+    {
+      u32x4_t op[8];
+      tile_operands(t1, op, (int64_t)kt * kDecKT, g, K, r, j0, np, r);
+      const u32x4_t xm = kvec_mask(x1, (int64_t)kt * kDecKT + 8 * g, K);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = mfma_16x16x32(xm, op[e], acc[e]);
+    }
+    kt += kDecWaves;
+    if (kt + kDecWaves < kt_end) {
+      load_tile_raw(t1, rA, (int64_t)(kt + kDecWaves) * kDecKT, r, j0, np, g);
+      x1 = load_kvec(rX, np, K, (int64_t)(kt + kDecWaves) * kDecKT + 8 * g, K, xal);
+    }
+  }
+
+  // WG reduction of the four waves' partial T; publish it (float4 rows of
+  // kDecJS floats, M rows).
 #pragma unroll
   for (int e = 0; e < 8; ++e)
 #pragma unroll
     for (int t = 0; t < 4; ++t) red[w][4 * g + t][8 * np + e] = acc[e][t];
   __syncthreads();
-  {
-    float* tp = P.Tpart + (int64_t)(js * P.S + s) * M * kDecJS;
-    for (int idx = tid; idx < M * kDecJS; idx += kDecThreads) {
-      const int m = idx / kDecJS, jl = idx - m * kDecJS;
-      const float v = ((red[0][m][jl] + red[1][m][jl]) + red[2][m][jl]) + red[3][m][jl];
-      st_agent_f32(tp + idx, v);
-    }
+  DEC_TRACE(1);
+  constexpr int kV4 = kDecJS / 4;  // float4 per row of a slice
+  const int nvecT = M * kV4;
+  const uint32_t slice_bytes = (uint32_t)(M * kDecJS * 4);
+  for (int vi = tid; vi < nvecT; vi += kDecThreads) {
+    const int m = vi / kV4, c = (vi - m * kV4) * 4;
+    f32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ((red[0][m][c + i] + red[1][m][c + i]) + red[2][m][c + i]) + red[3][m][c + i];
+    buf_store16_coherent(rW, P.off_tpart + (uint32_t)(js * P.S + s) * slice_bytes + (uint32_t)vi * 16u, v);
   }
   wait_vmem_all();
   __syncthreads();
+  DEC_TRACE(2);
   const uint32_t epoch = sh_epoch;
-  if (tid == 0) st_agent_u32(P.flags + js * P.S + s, epoch);
+  if (tid == 0) sh_old = add_agent_u32(P.tcnt + js, 1u);
+  __syncthreads();
+  DEC_TRACE(3);
 
   // ----------------------------------------------------- T hand-off ------
-  if (w == 0) {
-    uint32_t spins = 0;
-    while (true) {
-      bool ok = true;
-      for (int i = l; i < P.S; i += 64) ok = ok && (ld_agent_u32(P.flags + js * P.S + i) == epoch);
-      if (__all(ok)) break;
-      if (++spins > kSpinLimit) {
-        if (l == 0) st_agent_u32(P.ctrl + 2, 1u);
-        break;
+  if (sh_old == (uint32_t)(P.S - 1)) {
+    // Last arriver: reduce the S partials of slice js in order, publish T_js.
+    if (tid == 0) st_agent_u32(P.tcnt + js, 0u);
+    f32x4_t sum[1];
+    for (int vbase = 0; vbase < nvecT; vbase += kDecThreads) {
+      sum_partials<1>(rW, P.off_tpart + (uint32_t)(js * P.S) * slice_bytes + (uint32_t)vbase * 16u, slice_bytes,
+                      P.S, nvecT - vbase, tid, sum);
+      const int vi = vbase + tid;
+      if (vi < nvecT) {
+        buf_store16_coherent(rW, P.off_tfin + (uint32_t)js * slice_bytes + (uint32_t)vi * 16u, sum[0]);
+        const int m = vi / kV4, c = (vi - m * kV4) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ts[m][c + i] = sum[0][i];
       }
-      __builtin_amdgcn_s_sleep(1);
+    }
+    wait_vmem_all();
+    __syncthreads();
+    if (tid == 0) st_agent_u32(P.tflag + js, epoch);
+  } else {
+    if (w == 0) {
+      uint32_t spins = 0;
+      while (true) {
+        const bool ok = ld_agent_u32(P.tflag + js) == epoch;
+        if (ok) break;
+        if (++spins > kSpinLimit) {
+          if (l == 0) st_agent_u32(P.ctrl + 2, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __syncthreads();
+    for (int vi = tid; vi < nvecT; vi += kDecThreads) {
+      const f32x4_t v = buf_load16_coherent(rW, P.off_tfin + (uint32_t)js * slice_bytes + (uint32_t)vi * 16u);
+      const int m = vi / kV4, c = (vi - m * kV4) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ts[m][c + i] = v[i];
     }
   }
-  __syncthreads();
-  // Columns kDecJS.. of Ts (read by wave 3's last k-slots) stay zero.
+  // rows >= M and columns >= kDecJS of Ts are zero (read as operands)
   for (int idx = tid; idx < 16 * (kDecJS + 8); idx += kDecThreads) {
     const int m = idx / (kDecJS + 8), jl = idx - m * (kDecJS + 8);
-    float v = 0.f;
-    if (m < M && jl < kDecJS) {
-      const float* src = P.Tpart + (int64_t)(js * P.S) * M * kDecJS + m * kDecJS + jl;
-      for (int ks = 0; ks < P.S; ++ks) v += ld_agent_f32(src + (int64_t)ks * M * kDecJS);
-    }
-    Ts[m][jl] = v;
+    if (m >= M || jl >= kDecJS) Ts[m][jl] = 0.f;
   }
   __syncthreads();
+  DEC_TRACE(4);
 
   // bf16 hi/lo split of this wave's 32 rank rows: lane (i = np, g) holds
   // T[i][32w + 8g + q], q = 0..7.
@@ -197,16 +268,15 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   }
 
   // ---------------------------------------------------------- GEMM2 ------
-  const int64_t jrows_end = min64(r, (int64_t)j0 + kDecJS);
-  float* yp_base = P.Ypart + ((int64_t)(s * P.Jw + js) * P.ntps) * M * kDecNT;
+  const uint32_t ypart_wg = P.off_ypart + (uint32_t)((s * P.Jw + js) * P.ntps) * (uint32_t)(M * kDecNT * 4);
   auto gemm2_tile = [&](const RawTile& bt, int nt) {
     const int64_t nb = (int64_t)nt * kDecNT;
     f32x4_t y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = zero4();
-    if (wave_has_rows) {
+    {
       u32x4_t op[8];
-      tile_operands(bt, op, N, nb, np, N);
+      tile_operands(bt, op, jrow0, g, jrow_end, N, nb, np, N);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         y[e] = mfma_16x16x32(thi, op[e], y[e]);
@@ -218,43 +288,52 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
 #pragma unroll
       for (int t = 0; t < 4; ++t) red[w][4 * g + t][8 * np + e] = y[e][t];
     __syncthreads();
-    float* yp = yp_base + (int64_t)(nt - nt_beg) * M * kDecNT;
-    for (int idx = tid; idx < M * kDecNT; idx += kDecThreads) {
-      const int m = idx / kDecNT, nl = idx - m * kDecNT;
-      const float v = ((red[0][m][nl] + red[1][m][nl]) + red[2][m][nl]) + red[3][m][nl];
-      st_agent_f32(yp + idx, v);
+    const uint32_t yp = ypart_wg + (uint32_t)(nt - nt_beg) * (uint32_t)(M * kDecNT * 4);
+    for (int vi = tid; vi < M * (kDecNT / 4); vi += kDecThreads) {
+      const int m = vi / (kDecNT / 4), c = (vi - m * (kDecNT / 4)) * 4;
+      f32x4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = ((red[0][m][c + i] + red[1][m][c + i]) + red[2][m][c + i]) + red[3][m][c + i];
+      buf_store16_coherent(rW, yp + (uint32_t)vi * 16u, v);
     }
     __syncthreads();
   };
   for (int nt = nt_beg; nt < nt_end; nt += 2) {
     gemm2_tile(b0, nt);
-    if (wave_has_rows && nt + 2 < nt_end)
-      load_tile_raw(b0, P.B, jrow0, jrows_end, N, (int64_t)(nt + 2) * kDecNT, np, g, totB);
+    if (nt + 2 < nt_end) load_tile_raw(b0, rB, jrow0, N, (int64_t)(nt + 2) * kDecNT, np, g);
     if (nt + 1 < nt_end) {
       gemm2_tile(b1, nt + 1);
-      if (wave_has_rows && nt + 3 < nt_end)
-        load_tile_raw(b1, P.B, jrow0, jrows_end, N, (int64_t)(nt + 3) * kDecNT, np, g, totB);
+      if (nt + 3 < nt_end) load_tile_raw(b1, rB, jrow0, N, (int64_t)(nt + 3) * kDecNT, np, g);
     }
   }
 
   // ------------------------------------------- final deterministic sum ---
+  DEC_TRACE(5);
   wait_vmem_all();
   __syncthreads();
   if (tid == 0) sh_old = add_agent_u32(P.ycnt + s, 1u);
   __syncthreads();
+  DEC_TRACE(6);
   if (sh_old == (uint32_t)(P.Jw - 1)) {
     if (tid == 0) st_agent_u32(P.ycnt + s, 0u);
-    const int64_t stride_js = (int64_t)P.ntps * M * kDecNT;
-    const float* ys = P.Ypart + (int64_t)s * P.Jw * stride_js;
-    const int cnt = (nt_end - nt_beg) * M * kDecNT;
-    for (int idx = tid; idx < cnt; idx += kDecThreads) {
-      const int ntl = idx / (M * kDecNT);
-      const int rem = idx - ntl * M * kDecNT;
-      const int m = rem / kDecNT, nl = rem - m * kDecNT;
-      const int64_t n = (int64_t)(nt_beg + ntl) * kDecNT + nl;
-      float v = 0.f;
-      for (int jj = 0; jj < P.Jw; ++jj) v += ld_agent_f32(ys + jj * stride_js + idx);
-      if (n < N) P.Y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
+    const uint32_t stride_js = (uint32_t)P.ntps * (uint32_t)(M * kDecNT * 4);
+    const uint32_t ys = P.off_ypart + (uint32_t)(s * P.Jw) * stride_js;
+    const int nvecY = (nt_end - nt_beg) * M * (kDecNT / 4);
+    f32x4_t sum[2];
+    for (int vbase = 0; vbase < nvecY; vbase += 2 * kDecThreads) {
+      sum_partials<2>(rW, ys + (uint32_t)vbase * 16u, stride_js, P.Jw, nvecY - vbase, tid, sum);
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const int vi = vbase + tid + kDecThreads * v;
+        if (vi >= nvecY) continue;
+        const int ntl = vi / (M * (kDecNT / 4));
+        const int rem = vi - ntl * M * (kDecNT / 4);
+        const int m = rem / (kDecNT / 4), c = (rem - m * (kDecNT / 4)) * 4;
+        const int64_t n0 = (int64_t)(nt_beg + ntl) * kDecNT + c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n0 + i < N) P.Y[(int64_t)m * N + n0 + i] = (uint16_t)f32_to_bf16_rne(sum[v][i]);
+      }
     }
     wait_vmem_all();
     __syncthreads();
@@ -266,6 +345,7 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
       }
     }
   }
+  DEC_TRACE(7);
 }
 
 hipError_t launch_decode(const DecArgs& args, int grid, hipStream_t stream) {

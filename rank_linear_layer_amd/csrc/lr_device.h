@@ -57,25 +57,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-// Loads the 16-byte chunk c (elements [8c, 8c + 8)) of a bf16 array of
-// `total` elements whose base is 16-byte aligned.  Elements at or beyond
-// `total` read as zero and are never fetched.
-__device__ __forceinline__ u32x4_t load_chunk(const uint16_t* __restrict__ base, int64_t c, int64_t total) {
-  const int64_t e0 = c * 8;
-  if (e0 + 8 <= total) return *reinterpret_cast<const u32x4_t*>(base + e0);
-  u32x4_t v = zerou4();
-  if (e0 < total) {
-    uint32_t t[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = (e0 + i < total) ? (uint32_t)base[e0 + i] : 0u;
-    v[0] = t[0] | (t[1] << 16);
-    v[1] = t[2] | (t[3] << 16);
-    v[2] = t[4] | (t[5] << 16);
-    v[3] = t[6] | (t[7] << 16);
-  }
-  return v;
-}
-
 // Lane i of each 16-lane DPP row receives `src` of lane i + 1; lane 15 of
 // each row keeps `old`.
 __device__ __forceinline__ uint32_t dpp_row_shl1(uint32_t old, uint32_t src) {
@@ -138,43 +119,82 @@ __device__ __forceinline__ void transpose8x8(const u32x4_t seg[8], u32x4_t op[8]
   }
 }
 
+// ------------------------------------------------------ buffer loads ---
+// All global reads go through buffer resources whose range is the
+// matrix itself (rounded up to whole dwords): the hardware returns zero for
+// any dword outside it, so tails and overhanging tiles need no branches
+// (a branch around a load would make the compiler wait for every load in
+// flight at the join).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kCoherent = 16;           // sc1: device-scope coherent access
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t rounded = (bytes + 3) & ~(int64_t)3;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)rounded, kRsrcFlags);
+}
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_u16(rsrc_t r, uint32_t byte_off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)byte_off, 0, 0);
+}
+__device__ __forceinline__ f32x4_t buf_load16_coherent(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCoherent));
+}
+__device__ __forceinline__ void buf_store16_coherent(rsrc_t r, uint32_t byte_off, const f32x4_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)byte_off, 0, kCoherent);
+}
+
 // Raw half of a realigned row-segment load: lane16 of a 16-lane DPP row
 // loads the aligned chunk that holds column colbase + 8*lane16 - d of row
 // `row` (d = misalignment, see realign_segment).  Lanes 0..14 produce the
 // 8 columns [colbase + 8*lane16, +8); lane 15 only supplies the high half
-// for lane 14, so one DPP row covers 120 columns.
-__device__ __forceinline__ u32x4_t load_row_raw(const uint16_t* __restrict__ base, int64_t row, int64_t nrows,
-                                                int64_t ld, int64_t colbase, int lane16, int64_t total) {
-  if (row >= nrows) return zerou4();
+// for lane 14, so one DPP row covers 120 columns.  Rows past the end of
+// the matrix read as zero.
+__device__ __forceinline__ u32x4_t load_row_raw(rsrc_t r, int64_t row, int64_t ld, int64_t colbase, int lane16) {
   const int64_t c0 = (row * ld + colbase) >> 3;
-  return load_chunk(base, c0 + lane16, total);
+  return buf_load16(r, (uint32_t)((c0 + lane16) * 16));
 }
 
-// Second half: realign the raw chunk with the right-hand neighbour's chunk
-// and zero columns >= ncols.  `d` = (row * ld + colbase) mod 8 must be
-// uniform over the wave.  Lane 15's result is meaningless.
-__device__ __forceinline__ u32x4_t realign_segment(const u32x4_t& lo, int d, int64_t col0, int64_t ncols) {
+// Second half: realign the raw chunk with the right-hand neighbour's chunk,
+// zero columns >= ncols, and zero the whole segment when !row_ok.  `d` =
+// (row * ld + colbase) mod 8 must be uniform over the wave.  Lane 15's
+// result is meaningless.
+__device__ __forceinline__ u32x4_t realign_segment(const u32x4_t& lo, int d, int64_t col0, int64_t ncols,
+                                                   bool row_ok) {
   const u32x4_t hi = dpp_row_shl1(zerou4(), lo);
-  return mask_cols(realign(lo, hi, d), col0, ncols);
+  const u32x4_t v = mask_cols(realign(lo, hi, d), col0, ncols);
+  return row_ok ? v : zerou4();
 }
 
 // 8 consecutive elements [k0, k0 + 8) of row `row` of a row-major matrix
-// (leading dimension ld, valid columns < klen, valid rows < nrows).  When
-// `aligned` (ld and k0 multiples of 8) the load is one 16-byte access.
-__device__ __forceinline__ u32x4_t load_kvec(const uint16_t* __restrict__ base, int64_t row, int64_t nrows,
-                                             int64_t ld, int64_t k0, int64_t klen, bool aligned) {
-  if (row >= nrows || k0 >= klen) return zerou4();
-  const uint16_t* p = base + row * ld + k0;
-  if (aligned && k0 + 8 <= klen) return *reinterpret_cast<const u32x4_t*>(p);
+// with leading dimension ld (the buffer covers the valid rows).  When ld is
+// a multiple of 8 (k0 always is) this is one 16-byte load and the result is
+// RAW: columns >= klen are cleared later by kvec_mask, at the point of use,
+// so that no instruction touches the destination registers while the load
+// is in flight.  Otherwise 8 two-byte loads, masked here (slow path).
+__device__ __forceinline__ u32x4_t load_kvec(rsrc_t r, int64_t row, int64_t ld, int64_t k0, int64_t klen,
+                                             bool aligned) {
+  const int64_t e0 = row * ld + k0;
+  if (aligned) return buf_load16(r, (uint32_t)(e0 * 2));
   uint32_t t[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) t[i] = (k0 + i < klen) ? (uint32_t)p[i] : 0u;
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t x = buf_load_u16(r, (uint32_t)((e0 + i) * 2));
+    t[i] = (k0 + i < klen) ? x : 0u;
+  }
   u32x4_t v;
   v[0] = t[0] | (t[1] << 16);
   v[1] = t[2] | (t[3] << 16);
   v[2] = t[4] | (t[5] << 16);
   v[3] = t[6] | (t[7] << 16);
   return v;
+}
+// Completes load_kvec: with ld and k0 multiples of 8 the segment is either
+// entirely inside the row (k0 < klen) or entirely past it.
+__device__ __forceinline__ u32x4_t kvec_mask(const u32x4_t& v, int64_t k0, int64_t klen) {
+  return (k0 < klen) ? v : zerou4();
 }
 
 // Device-coherent (agent scope) relaxed accesses used to exchange partial

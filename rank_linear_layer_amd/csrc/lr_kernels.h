@@ -19,23 +19,31 @@ constexpr int kDecMaxProj = 4;    // projections sharing X in one launch
 // workgroups [wg_begin, wg_begin + Jw*S) belong to it; workgroup
 // (js, s) = (local / S, local % S) computes the partial T of rank slice js
 // over K slice s, then the partial Y of rank slice js over N slice s.
+// Workspace regions are byte offsets from `ws` (one buffer resource):
+//   off_tpart  [Jw*S][M][kDecJS] fp32   GEMM1 partials
+//   off_tfin   [Jw][M][kDecJS]   fp32   reduced T slices
+//   off_ypart  [S][Jw][ntps][M][kDecNT] fp32 GEMM2 partials
 struct DecProj {
   const uint16_t* A;
   const uint16_t* B;
   uint16_t* Y;
-  float* Tpart;     // [Jw*S][M][kDecJS]
-  float* Ypart;     // [S][Jw][ntps][M][kDecNT]
-  uint32_t* flags;  // [Jw*S] epoch stamps of finished T partials
-  uint32_t* ycnt;   // [S] arrival counters of Y partials (self-resetting)
+  const void* ws;
   uint32_t* ctrl;   // [0] generation, [1] finished n-slices, [2] spin-timeout flag
-  int r, N, Jw, S, ktps, ntps, wg_begin, pad_;
+  uint32_t* tcnt;   // [Jw] arrivals of T partials (self-resetting)
+  uint32_t* tflag;  // [Jw] epoch stamp of a published T slice
+  uint32_t* ycnt;   // [S] arrivals of Y partials (self-resetting)
+  int64_t ws_bytes;
+  uint32_t off_tpart, off_tfin, off_ypart;
+  int r, N, Jw, S, ktps, ntps, wg_begin;
 };
 
 struct DecArgs {
   const uint16_t* X;
+  uint64_t* trace;  // per-workgroup phase timestamps (builds with LR_DECODE_TRACE only)
   int M, K, nproj, pad_;
   DecProj p[kDecMaxProj];
 };
+constexpr int kDecTracePoints = 8;
 
 hipError_t launch_decode(const DecArgs& args, int grid, hipStream_t stream);
 // Workgroups of the decode kernel that one compute unit holds at once (0 on error).

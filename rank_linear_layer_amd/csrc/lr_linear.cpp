@@ -51,11 +51,13 @@ struct lr_linear {
   bool has_decode;
   lrv::DecPart dp;
   int dec_max_M;
+  char* dws;          // decode workspace base
+  int64_t dws_bytes;
   uint32_t* ctrl;
-  uint32_t* flags_buf;
+  uint32_t* tcnt;
+  uint32_t* tflag;
   uint32_t* ycnt;
-  float* Tpart;
-  float* Ypart;
+  uint32_t off_tpart, off_tfin, off_ypart;
   // prefill workspace: T [max_M x r_pad] bf16
   bool has_prefill;
   uint16_t* Tbuf;
@@ -75,11 +77,15 @@ lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
   p.A = h->A;
   p.B = h->B;
   p.Y = Y;
-  p.Tpart = h->Tpart;
-  p.Ypart = h->Ypart;
-  p.flags = h->flags_buf;
-  p.ycnt = h->ycnt;
+  p.ws = h->dws;
+  p.ws_bytes = h->dws_bytes;
   p.ctrl = h->ctrl;
+  p.tcnt = h->tcnt;
+  p.tflag = h->tflag;
+  p.ycnt = h->ycnt;
+  p.off_tpart = h->off_tpart;
+  p.off_tfin = h->off_tfin;
+  p.off_ypart = h->off_ypart;
   p.r = (int)h->r;
   p.N = (int)h->N;
   p.Jw = h->dp.Jw;
@@ -87,7 +93,6 @@ lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
   p.ktps = h->dp.ktps;
   p.ntps = h->dp.ntps;
   p.wg_begin = wg_begin;
-  p.pad_ = 0;
   return p;
 }
 
@@ -97,11 +102,18 @@ int num_cus(int device) {
   return cus;
 }
 
+#ifdef LR_DECODE_TRACE
+uint64_t* g_trace = nullptr;
+#endif
+
 lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                      hipStream_t stream) {
   lrk::DecArgs a;
   memset(&a, 0, sizeof a);
   a.X = (const uint16_t*)X;
+#ifdef LR_DECODE_TRACE
+  a.trace = g_trace;
+#endif
   a.M = (int)M;
   a.K = (int)hs[0]->K;
   a.nproj = n;
@@ -214,7 +226,7 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
   h->has_prefill = !(flags & LR_FLAG_FORCE_DECODE) && (max_M > LR_DECODE_MAX_M || (flags & LR_FLAG_FORCE_PREFILL));
 
   size_t off = 0;
-  size_t o_ctrl = 0, o_flags = 0, o_ycnt = 0, o_tpart = 0, o_ypart = 0, o_tbuf = 0;
+  size_t o_ctrl = 0, o_tcnt = 0, o_tflag = 0, o_ycnt = 0, o_tpart = 0, o_tfin = 0, o_ypart = 0, o_tbuf = 0;
   if (h->has_decode) {
     h->dec_max_M = (int)(max_M < LR_DECODE_MAX_M ? max_M : LR_DECODE_MAX_M);
     const int occ = lrk::decode_blocks_per_cu();
@@ -226,14 +238,23 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     const int64_t G = (int64_t)h->dp.Jw * h->dp.S;
     o_ctrl = off;
     off = align_up(off + 64);
-    o_flags = off;
-    off = align_up(off + (size_t)G * 4);
+    o_tcnt = off;
+    off = align_up(off + (size_t)h->dp.Jw * 4);
+    o_tflag = off;
+    off = align_up(off + (size_t)h->dp.Jw * 4);
     o_ycnt = off;
     off = align_up(off + (size_t)h->dp.S * 4);
     o_tpart = off;
     off = align_up(off + (size_t)G * h->dec_max_M * lrk::kDecJS * 4);
+    o_tfin = off;
+    off = align_up(off + (size_t)h->dp.Jw * h->dec_max_M * lrk::kDecJS * 4);
     o_ypart = off;
     off = align_up(off + (size_t)G * h->dp.ntps * h->dec_max_M * lrk::kDecNT * 4);
+    if (off >= ((size_t)1 << 31)) {
+      delete h;
+      return fail(LR_ERR_UNSUPPORTED, "decode workspace of %zu bytes exceeds 2 GiB", off);
+    }
+    h->dws_bytes = (int64_t)off;
   }
   if (h->has_prefill) {
     o_tbuf = off;
@@ -257,11 +278,14 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
   }
   char* base = (char*)h->ws;
   if (h->has_decode) {
+    h->dws = base;  // the decode regions start the workspace
     h->ctrl = (uint32_t*)(base + o_ctrl);
-    h->flags_buf = (uint32_t*)(base + o_flags);
+    h->tcnt = (uint32_t*)(base + o_tcnt);
+    h->tflag = (uint32_t*)(base + o_tflag);
     h->ycnt = (uint32_t*)(base + o_ycnt);
-    h->Tpart = (float*)(base + o_tpart);
-    h->Ypart = (float*)(base + o_ypart);
+    h->off_tpart = (uint32_t)o_tpart;
+    h->off_tfin = (uint32_t)o_tfin;
+    h->off_ypart = (uint32_t)o_ypart;
   }
   if (h->has_prefill) h->Tbuf = (uint16_t*)(base + o_tbuf);
   *out = h;
@@ -321,5 +345,10 @@ lr_status lr_linear_describe(const lr_linear* h, char* buf, int64_t len) {
 }
 
 int64_t lr_linear_workspace_bytes(const lr_linear* h) { return h ? (int64_t)h->ws_bytes : 0; }
+
+#ifdef LR_DECODE_TRACE
+// Trace builds only: device buffer of grid * 8 uint64 phase timestamps.
+void lr_debug_set_trace(void* device_buf) { g_trace = (uint64_t*)device_buf; }
+#endif
 
 }  // extern "C"

@@ -24,19 +24,21 @@ struct PreRaw {
   u32x4_t c[8];
 };
 
-__device__ __forceinline__ void pre_load_raw(PreRaw& t, const uint16_t* __restrict__ Q, int64_t kb, int64_t qrows,
-                                             int64_t ldq, int64_t colbase, int lane16, int g, int64_t total) {
+__device__ __forceinline__ void pre_load_raw(PreRaw& t, rsrc_t rQ, int64_t kb, int64_t ldq, int64_t colbase,
+                                             int lane16, int g) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) t.c[q] = load_row_raw(Q, kb + 8 * g + q, qrows, ldq, colbase, lane16, total);
+  for (int q = 0; q < 8; ++q) t.c[q] = load_row_raw(rQ, kb + 8 * g + q, ldq, colbase, lane16);
 }
 
+// Rows past the end of Q already read as zero (buffer range), so every row
+// of the tile is kept.
 __device__ __forceinline__ void pre_operands(const PreRaw& t, u32x4_t op[8], int64_t ldq, int64_t colbase,
                                              int lane16) {
   u32x4_t seg[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int d = (int)(((int64_t)q * ldq + colbase) & 7);
-    seg[q] = realign_segment(t.c[q], d, colbase + 8 * lane16, ldq);
+    seg[q] = realign_segment(t.c[q], d, colbase + 8 * lane16, ldq, true);
   }
   transpose8x8(seg, op);
 }
@@ -55,7 +57,8 @@ __global__ __launch_bounds__(kPreThreads) void lr_prefill_gemm_kernel(const PreA
   const PreOut O = a.o[bi];
   const int64_t mb = (int64_t)blockIdx.y * kPreBM + 64 * wm;
   const int64_t colbase = (int64_t)ct * kPreBN + 120 * wn;
-  const int64_t totQ = O.qrows * O.ldq;
+  const rsrc_t rQ = make_rsrc(O.Q, O.qrows * O.ldq * 2);
+  const rsrc_t rP = make_rsrc(O.P, a.rows * O.ldp * 2);
   const bool pal = (O.ldp & 7) == 0;
 
   f32x4_t acc[4][8];
@@ -69,26 +72,29 @@ __global__ __launch_bounds__(kPreThreads) void lr_prefill_gemm_kernel(const PreA
   u32x4_t x0[4], x1[4];
   auto load_step = [&](PreRaw& rr, u32x4_t* xx, int ks) {
     const int64_t kb = (int64_t)ks * kPreKT;
-    pre_load_raw(rr, O.Q, kb, O.qrows, O.ldq, colbase, np, g, totQ);
+    pre_load_raw(rr, rQ, kb, O.ldq, colbase, np, g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xx[i] = load_kvec(O.P, mb + 16 * i + np, a.rows, O.ldp, kb + 8 * g, O.kd, pal);
+    for (int i = 0; i < 4; ++i) xx[i] = load_kvec(rP, mb + 16 * i + np, O.ldp, kb + 8 * g, O.kd, pal);
   };
-  auto compute_step = [&](const PreRaw& rr, const u32x4_t* xx) {
+  auto compute_step = [&](const PreRaw& rr, const u32x4_t* xx, int ks) {
     u32x4_t op[8];
     pre_operands(rr, op, O.ldq, colbase, np);
+    const int64_t k0 = (int64_t)ks * kPreKT + 8 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const u32x4_t xm = kvec_mask(xx[i], k0, O.kd);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[i][e] = mfma_16x16x32(xx[i], op[e], acc[i][e]);
+      for (int e = 0; e < 8; ++e) acc[i][e] = mfma_16x16x32(xm, op[e], acc[i][e]);
+    }
   };
 
   if (nks > 0) load_step(r0, x0, 0);
   for (int ks = 0; ks < nks; ks += 2) {
     if (ks + 1 < nks) load_step(r1, x1, ks + 1);
-    compute_step(r0, x0);
+    compute_step(r0, x0, ks);
     if (ks + 1 >= nks) break;
     if (ks + 2 < nks) load_step(r0, x0, ks + 2);
-    compute_step(r1, x1);
+    compute_step(r1, x1, ks + 1);
   }
 
   // Epilogue: lane (np, g) of MFMA (i, e) holds rows mb + 16i + 4g + t,

@@ -26,6 +26,8 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Largest dimension accepted; keeps every flat index well inside int64 and
 // every per-row index inside int32.
 constexpr int64_t kMaxDim = (int64_t)1 << 24;
+// Kernels address each matrix through a 32-bit buffer range.
+constexpr int64_t kMaxMatrixBytes = ((int64_t)1 << 31) - 64;
 
 inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, const void* B, int64_t max_M,
                               uint32_t flags, char* err, size_t errlen) {
@@ -40,8 +42,10 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
   }
   if (max_M < 0) { snprintf(err, errlen, "max_M must be >= 0 (got %lld)", (long long)max_M); return LR_ERR_INVALID_ARG; }
   if (!aligned16(A) || !aligned16(B)) { snprintf(err, errlen, "A and B must be 16-byte aligned"); return LR_ERR_INVALID_ARG; }
-  if (overlaps(span(A, K * r), span(B, r * N))) {
-    // Sharing storage between the factors is allowed (read-only); nothing to check.
+  if (K * r * 2 > kMaxMatrixBytes || r * N * 2 > kMaxMatrixBytes || max_M * K * 2 > kMaxMatrixBytes ||
+      max_M * N * 2 > kMaxMatrixBytes || max_M * ((r + 31) / 32 * 32) * 2 > kMaxMatrixBytes) {
+    snprintf(err, errlen, "a matrix would exceed 2 GiB (32-bit buffer addressing)");
+    return LR_ERR_UNSUPPORTED;
   }
   const uint32_t known = LR_FLAG_FORCE_DECODE | LR_FLAG_FORCE_PREFILL;
   if (flags & ~known) { snprintf(err, errlen, "unknown flag bits 0x%x", flags & ~known); return LR_ERR_UNSUPPORTED; }
