@@ -75,6 +75,8 @@ typedef struct lr_linear lr_linear;
 #define LR_FLAG_NONE          0u
 #define LR_FLAG_FORCE_DECODE  1u  /* use the fused decode kernel for every M (requires max_M <= 16) */
 #define LR_FLAG_FORCE_PREFILL 2u  /* use the MFMA prefill kernels for every M */
+#define LR_FLAG_DECODE_STREAMING 4u  /* decode with the register-streaming kernel even where the
+                                        LDS-resident one applies (both compute the same result) */
 
 /* Largest M that the fused decode kernel takes (more rows use prefill). */
 #define LR_DECODE_MAX_M 16

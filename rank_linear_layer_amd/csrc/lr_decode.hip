@@ -35,11 +35,15 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 // Optional phase timestamps (constant-rate device clock), compiled in only
 // with -DLR_DECODE_TRACE; used to see where a launch spends its time.
 #ifdef LR_DECODE_TRACE
+#define DEC_TRACE_ENTRY() const uint64_t trace_entry_ = __builtin_amdgcn_s_memrealtime()
+#define DEC_TRACE_ENTRY_STORE() do { if (a.trace && tid == 0) a.trace[blockIdx.x * kDecTracePoints + 15] = trace_entry_; } while (0)
 #define DEC_TRACE(i)                                                                              \
   do {                                                                                            \
     if (a.trace && tid == 0) a.trace[blockIdx.x * kDecTracePoints + (i)] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
 #else
+#define DEC_TRACE_ENTRY() do { } while (0)
+#define DEC_TRACE_ENTRY_STORE() do { } while (0)
 #define DEC_TRACE(i) \
   do {               \
   } while (0)
@@ -98,6 +102,7 @@ __device__ __forceinline__ void sum_partials(rsrc_t ws, uint32_t base, uint32_t 
 }
 
 __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecArgs a) {
+  DEC_TRACE_ENTRY();
   __shared__ float red[kDecWaves][16][kDecJS + 8];
   __shared__ float Ts[16][kDecJS + 8];
   __shared__ uint32_t sh_epoch, sh_old;
@@ -120,6 +125,7 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   const rsrc_t rW = make_rsrc(P.ws, P.ws_bytes);
 
   DEC_TRACE(0);
+  DEC_TRACE_ENTRY_STORE();
   if (tid == 0) sh_epoch = ld_agent_u32(P.ctrl) + 1u;
 
   // ------------------------------------------------ issue all loads -----
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   for (int e = 0; e < 8; ++e)
 #pragma unroll
     for (int t = 0; t < 4; ++t) red[w][4 * g + t][8 * np + e] = acc[e][t];
-  __syncthreads();
+  barrier_lds();
   DEC_TRACE(1);
   constexpr int kV4 = kDecJS / 4;  // float4 per row of a slice
   const int nvecT = M * kV4;
@@ -200,11 +206,11 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
     buf_store16_coherent(rW, P.off_tpart + (uint32_t)(js * P.S + s) * slice_bytes + (uint32_t)vi * 16u, v);
   }
   wait_vmem_all();
-  __syncthreads();
+  barrier_lds();
   DEC_TRACE(2);
   const uint32_t epoch = sh_epoch;
   if (tid == 0) sh_old = add_agent_u32(P.tcnt + js, 1u);
-  __syncthreads();
+  barrier_lds();
   DEC_TRACE(3);
 
   // ----------------------------------------------------- T hand-off ------
@@ -224,7 +230,7 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
       }
     }
     wait_vmem_all();
-    __syncthreads();
+    barrier_lds();
     if (tid == 0) st_agent_u32(P.tflag + js, epoch);
   } else {
     if (w == 0) {
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
         __builtin_amdgcn_s_sleep(1);
       }
     }
-    __syncthreads();
+    barrier_lds();
     for (int vi = tid; vi < nvecT; vi += kDecThreads) {
       const f32x4_t v = buf_load16_coherent(rW, P.off_tfin + (uint32_t)js * slice_bytes + (uint32_t)vi * 16u);
       const int m = vi / kV4, c = (vi - m * kV4) * 4;
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
     const int m = idx / (kDecJS + 8), jl = idx - m * (kDecJS + 8);
     if (m >= M || jl >= kDecJS) Ts[m][jl] = 0.f;
   }
-  __syncthreads();
+  barrier_lds();
   DEC_TRACE(4);
 
   // bf16 hi/lo split of this wave's 32 rank rows: lane (i = np, g) holds
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
     for (int e = 0; e < 8; ++e)
 #pragma unroll
       for (int t = 0; t < 4; ++t) red[w][4 * g + t][8 * np + e] = y[e][t];
-    __syncthreads();
+    barrier_lds();
     const uint32_t yp = ypart_wg + (uint32_t)(nt - nt_beg) * (uint32_t)(M * kDecNT * 4);
     for (int vi = tid; vi < M * (kDecNT / 4); vi += kDecThreads) {
       const int m = vi / (kDecNT / 4), c = (vi - m * (kDecNT / 4)) * 4;
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
       for (int i = 0; i < 4; ++i) v[i] = ((red[0][m][c + i] + red[1][m][c + i]) + red[2][m][c + i]) + red[3][m][c + i];
       buf_store16_coherent(rW, yp + (uint32_t)vi * 16u, v);
     }
-    __syncthreads();
+    barrier_lds();
   };
   for (int nt = nt_beg; nt < nt_end; nt += 2) {
     gemm2_tile(b0, nt);
@@ -310,9 +316,9 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   // ------------------------------------------- final deterministic sum ---
   DEC_TRACE(5);
   wait_vmem_all();
-  __syncthreads();
+  barrier_lds();
   if (tid == 0) sh_old = add_agent_u32(P.ycnt + s, 1u);
-  __syncthreads();
+  barrier_lds();
   DEC_TRACE(6);
   if (sh_old == (uint32_t)(P.Jw - 1)) {
     if (tid == 0) st_agent_u32(P.ycnt + s, 0u);
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
       }
     }
     wait_vmem_all();
-    __syncthreads();
+    barrier_lds();
     if (tid == 0) {
       const uint32_t old2 = add_agent_u32(P.ctrl + 1, 1u);
       if (old2 == (uint32_t)(P.S - 1)) {

@@ -1,0 +1,483 @@
+// LDS-resident fused decode kernel (M <= 16): Y = (X . A) . B, one launch.
+//
+// Same method as lr_decode.hip, for shapes whose per-workgroup slabs fit in
+// LDS (the plan checks this; every other shape takes lr_decode.hip).
+// Decode is bound by reading A and B from HBM once ("LowRankArena ...",
+// "Why theoretical FLOPs saved does not equal faster inference"), so every
+// byte a workgroup needs is requested in the first instructions of the
+// kernel, straight into LDS (buffer_load ... lds): no VGPRs are tied up by
+// loads in flight and each compute unit keeps its whole share outstanding.
+//
+// Wave roles keep the in-order vector-memory counter from coupling phases:
+// waves 0-1 load X and A, waves 2-3 load B.  GEMM1 starts once A is in LDS
+// while B is still arriving.
+//
+// Work split: the rank is cut into Jw slices of JS <= 128 columns (Jw a
+// multiple of 8), K and N into S slices.  Workgroup (js, s):
+//   GEMM1  T_s[:, js] = X[:, Ks] . A[Ks, js]            (MFMA)
+//   T hand-off within the XCD: the S workgroups of slice js run on one XCD
+//          (workgroups are dealt to XCDs round-robin, which the host checks
+//          at start-up); each publishes its partial through that XCD's L2
+//          with an epoch flag, and every member sums the S partials in
+//          order s = 0..S-1 (bitwise identical in every member).  Without a
+//          verified XCD map the same exchange runs device-coherent.
+//   GEMM2  Y_js[:, Ns] = T_js . B[js, Ns]               (T as bf16 hi + lo)
+//   Y reduce-scatter across XCDs: partials published device-coherent with
+//          epoch flags; member js of n-slice s sums its 1/Jw share of the
+//          n-slice over the Jw partials in order and writes bf16 Y.
+// No atomics and no floating-point reordering: results are bitwise
+// reproducible.  The epoch comes from the host (one per call of a handle),
+// so no counter is reset between calls.
+//
+// The misalignment of the rows (ld mod 8) selects one of eight compile-time
+// shift patterns for a whole GEMM loop (one uniform switch per phase); the
+// eight variants are the same code with different constants.
+#include "lr_device.h"
+#include "lr_kernels.h"
+
+namespace lrk {
+
+namespace {
+
+constexpr uint32_t kResSpinLimit = 1u << 22;
+// Byte offset past the end of every buffer range used here: the load
+// returns zeros (and writes them to LDS) without any branch.
+constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void lds_load16(rsrc_t r, void* lds_base_wave, uint32_t gbyte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base_wave, 16, (int)gbyte_off, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4_t lds_read16(const char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+// 8 rows held as chunk runs in LDS (row q at rows + q * pitch) -> 8 MFMA
+// B-operands.  lane16 reads chunks c_off + lane16 and c_off + lane16 + 1 of
+// each run; LD8 = (leading dimension mod 8) fixes every row's shift.
+template <int LD8>
+__device__ __forceinline__ void lds_tile_ops(const char* rows, int pitch, int c_off, int lane16, int64_t col0,
+                                             int64_t ncols, int64_t row0, int64_t row_end, u32x4_t op[8]) {
+  u32x4_t lo[8], hi[8], seg[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const char* p = rows + q * pitch + (c_off + lane16) * 16;
+    lo[q] = lds_read16(p);
+    hi[q] = lds_read16(p + 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const u32x4_t v = mask_cols(realign(lo[q], hi[q], (q * LD8) & 7), col0, ncols);
+    seg[q] = (row0 + q < row_end) ? v : zerou4();
+  }
+  transpose8x8(seg, op);
+}
+
+struct ResCtx {
+  const char* sA;
+  const char* sB;
+  const char* sX;
+  int w, g, np;
+  int kt_cnt, CB;
+  int64_t kbase, j0, jend, K, r, N, nb0;
+};
+
+// GEMM1 partial over this wave's k-tiles (t = w, w + 4, ...).
+template <int LD8>
+__device__ __forceinline__ void gemm1_wave(const ResCtx& c, f32x4_t acc[8]) {
+  for (int t = c.w; t < c.kt_cnt; t += 4) {
+    const int64_t krow0 = c.kbase + (int64_t)t * kResKT + 8 * c.g;
+    u32x4_t op[8];
+    lds_tile_ops<LD8>(c.sA + (size_t)(t * kResKT + 8 * c.g) * (kResCA * 16), kResCA * 16, 0, c.np,
+                      c.j0 + 8 * c.np, c.jend, krow0, c.K, op);
+    const u32x4_t x = kvec_mask(lds_read16(c.sX + c.np * (kResXK * 2) + (t * kResKT + 8 * c.g) * 2), krow0, c.K);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = mfma_16x16x32(x, op[e], acc[e]);
+  }
+}
+
+// GEMM2 partial of one 128-column n-tile for this wave's 32 rank rows.
+template <int LD8>
+__device__ __forceinline__ void gemm2_wave(const ResCtx& c, int ntl, const u32x4_t& thi, const u32x4_t& tlo,
+                                           f32x4_t y[8]) {
+  const int64_t jrow0 = c.j0 + 32 * c.w + 8 * c.g;
+  const int64_t nb = c.nb0 + (int64_t)ntl * kResNT;
+  u32x4_t op[8];
+  lds_tile_ops<LD8>(c.sB + (size_t)(32 * c.w + 8 * c.g) * (c.CB * 16), c.CB * 16, 16 * ntl, c.np, nb + 8 * c.np,
+                    c.N, jrow0, c.jend, op);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    y[e] = mfma_16x16x32(thi, op[e], y[e]);
+    y[e] = mfma_16x16x32(tlo, op[e], y[e]);
+  }
+}
+
+}  // namespace
+
+// Optional phase timestamps (constant-rate device clock), compiled in only
+// with -DLR_DECODE_TRACE.
+#ifdef LR_DECODE_TRACE
+#define RES_TRACE_ENTRY() const uint64_t trace_entry_ = __builtin_amdgcn_s_memrealtime()
+#define RES_TRACE_ENTRY_STORE() do { if (a.trace && tid == 0) a.trace[blockIdx.x * kDecTracePoints + 15] = trace_entry_; } while (0)
+#define RES_TRACE(i)                                                                                         \
+  do {                                                                                                       \
+    if (a.trace && tid == 0) a.trace[blockIdx.x * kDecTracePoints + (i)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define RES_TRACE_ENTRY() do { } while (0)
+#define RES_TRACE_ENTRY_STORE() do { } while (0)
+#define RES_TRACE(i) \
+  do {               \
+  } while (0)
+#endif
+
+#define LR_LD8_SWITCH(v, CALL) \
+  switch ((v) & 7) {           \
+    case 0: CALL(0); break;    \
+    case 1: CALL(1); break;    \
+    case 2: CALL(2); break;    \
+    case 3: CALL(3); break;    \
+    case 4: CALL(4); break;    \
+    case 5: CALL(5); break;    \
+    case 6: CALL(6); break;    \
+    default: CALL(7); break;   \
+  }
+
+__global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArgs a) {
+  RES_TRACE_ENTRY();
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, np = l & 15, g = l >> 4;
+
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kDecMaxProj; ++i)
+    if (i < a.nproj && (int)blockIdx.x >= a.p[i].wg_begin) pi = i;
+  const DecProj P = a.p[pi];
+  const int local = (int)blockIdx.x - P.wg_begin;
+  // Workgroup -> (rank slice, K/N slice).  With the XCD map, the S members of
+  // a rank slice share local % 8 and so run on one XCD.
+  int js, s;
+  if (P.xcd_local) {
+    const int x = local & 7, slot = local >> 3;
+    js = x + 8 * (slot / P.S);
+    s = slot - (slot / P.S) * P.S;
+  } else {
+    js = local / P.S;
+    s = local - js * P.S;
+  }
+  const int M = a.M, K = a.K, r = P.r, N = P.N;
+  const int JS = P.js_w;
+  const int ntps = P.ntps;
+  const int CB = kResNT / 8 * ntps + 1;  // chunks per B row run
+  const uint32_t epoch = P.epoch;
+
+  const rsrc_t rA = make_rsrc(P.A, (int64_t)K * r * 2);
+  const rsrc_t rB = make_rsrc(P.B, (int64_t)r * N * 2);
+  const rsrc_t rX = make_rsrc(a.X, (int64_t)M * K * 2);
+  const rsrc_t rW = make_rsrc(P.ws, P.ws_bytes);
+
+  char* const sX = smem;               // [16][kResXK] bf16, row pitch kResXK*2
+  char* const sA = smem + kResXBytes;  // [ktps*32][kResCA] chunks
+  char* const sB = sA + kResABytes;    // [128][CB] chunks
+  float* const red = reinterpret_cast<float*>(sA);                 // after GEMM1: [4][16][128]
+  float* const Ts = reinterpret_cast<float*>(sA + kResRedBytes);  // [16][136]
+
+  const int64_t j0 = (int64_t)js * JS;
+  const int64_t jend = min64(r, j0 + JS);
+  const int nk = (K + kResKT - 1) / kResKT;
+  const int kt_beg = s * P.ktps;
+  const int kt_cnt = max(0, min(nk, kt_beg + P.ktps) - kt_beg);
+  const int64_t kbase = (int64_t)kt_beg * kResKT;
+  const int nn = (N + kResNT - 1) / kResNT;
+  const int nt_beg = s * ntps;
+  const int nt_cnt = max(0, min(nn, nt_beg + ntps) - nt_beg);
+  const int64_t nb0 = (int64_t)nt_beg * kResNT;
+
+  RES_TRACE(0);
+  RES_TRACE_ENTRY_STORE();
+
+  // ------------------------------------------ issue every load up front --
+  if (w < 2) {
+    // X: 16 rows x kResXK columns starting at kbase (rows >= M read as zero)
+    constexpr int nxi = 16 * (kResXK / 8) / 64;
+    for (int i = w; i < nxi; i += 2) {
+      const int c = i * 64 + l;
+      const int m = c / (kResXK / 8), cc = c - m * (kResXK / 8);
+      const uint32_t off = (uint32_t)(((int64_t)m * K + kbase) * 2 + (int64_t)cc * 16);
+      lds_load16(rX, sX + i * 1024, off);
+    }
+    // A: kt_cnt*32 rows, each a run of kResCA chunks starting at the chunk
+    // that holds column j0 of the row
+    const int nachunks = kt_cnt * kResKT * kResCA;
+    const int nai = (nachunks + 63) / 64;
+    for (int i = w; i < nai; i += 2) {
+      const int c = i * 64 + l;
+      const int row = c / kResCA, cc = c - row * kResCA;
+      const int64_t grow = kbase + row;
+      const int64_t chunk = ((grow * r + j0) >> 3) + cc;
+      const uint32_t off = (c < nachunks && grow < K) ? (uint32_t)(chunk * 16) : kOutOfRange;
+      lds_load16(rA, sA + i * 1024, off);
+    }
+  } else {
+    // B: the slice's rows (up to 128), each a run of CB chunks starting at
+    // the chunk that holds column nb0 of the row; rows past the slice read 0
+    const int nbchunks = 128 * CB;
+    const int nbi = (nbchunks + 63) / 64;
+    for (int i = w - 2; i < nbi; i += 2) {
+      const int c = i * 64 + l;
+      const int row = c / CB, cc = c - row * CB;
+      const int64_t grow = j0 + row;
+      const int64_t chunk = ((grow * N + nb0) >> 3) + cc;
+      const uint32_t off = (c < nbchunks && grow < jend && nt_cnt > 0) ? (uint32_t)(chunk * 16) : kOutOfRange;
+      lds_load16(rB, sB + i * 1024, off);
+    }
+  }
+  if (w < 2) wait_vmem_all();
+  barrier_lds();  // X and A are in LDS (B may still be arriving)
+  RES_TRACE(1);
+
+  ResCtx ctx;
+  ctx.sA = sA;
+  ctx.sB = sB;
+  ctx.sX = sX;
+  ctx.w = w;
+  ctx.g = g;
+  ctx.np = np;
+  ctx.kt_cnt = kt_cnt;
+  ctx.CB = CB;
+  ctx.kbase = kbase;
+  ctx.j0 = j0;
+  ctx.jend = jend;
+  ctx.K = K;
+  ctx.r = r;
+  ctx.N = N;
+  ctx.nb0 = nb0;
+
+  // ---------------------------------------------------------- GEMM1 ------
+  f32x4_t acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = zero4();
+#define LR_G1(D) gemm1_wave<D>(ctx, acc)
+  LR_LD8_SWITCH(r, LR_G1)
+#undef LR_G1
+  RES_TRACE(2);
+  barrier_lds();  // every wave is done reading A: the A region is free
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) red[(w * 16 + 4 * g + t) * 128 + 8 * np + e] = acc[e][t];
+  barrier_lds();
+
+  // ------------------------------------------- publish the T partial -----
+  // slice layout: [M][128] fp32 (columns >= JS unused)
+  const int v4row = JS / 4;
+  const int nvecT = M * v4row;
+  const uint32_t slice_bytes = (uint32_t)(M * 128 * 4);
+  const uint32_t grp_base = P.off_tpart + (uint32_t)(js * P.S) * slice_bytes;
+  if (w < 2) {
+    for (int vi = tid; vi < nvecT; vi += 128) {
+      const int m = vi / v4row, c = (vi - m * v4row) * 4;
+      f32x4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = m * 128 + c + i;
+        v[i] = ((red[o] + red[16 * 128 + o]) + red[32 * 128 + o]) + red[48 * 128 + o];
+      }
+      const uint32_t off = grp_base + (uint32_t)s * slice_bytes + (uint32_t)(m * 128 + c) * 4u;
+      if (P.xcd_local)
+        buf_store16(rW, off, v);
+      else
+        buf_store16_coherent(rW, off, v);
+    }
+    wait_vmem_all();  // the partial is visible before the flag
+  }
+  barrier_lds();
+  const uint32_t tflag_grp = P.off_tflag + (uint32_t)(js * P.S) * 4u;
+  if (tid == 0) {
+    if (P.xcd_local)
+      buf_store_u32(rW, tflag_grp + (uint32_t)s * 4u, epoch);
+    else
+      buf_store_u32_coherent(rW, tflag_grp + (uint32_t)s * 4u, epoch);
+  }
+  RES_TRACE(3);
+
+  // ------------------------------------ T hand-off: all S partials -------
+  if (w == 0) {
+    uint32_t spins = 0;
+    while (true) {
+      bool ok = true;
+      for (int i = l; i < P.S; i += 64) {
+        const uint32_t f = P.xcd_local ? buf_load_u32_l2(rW, tflag_grp + (uint32_t)i * 4u)
+                                       : buf_load_u32_coherent(rW, tflag_grp + (uint32_t)i * 4u);
+        ok = ok && (f == epoch);
+      }
+      if (__all(ok)) break;
+      if (++spins > kResSpinLimit) {
+        if (l == 0) st_agent_u32(P.ctrl + 2, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  barrier_lds();
+  RES_TRACE(4);
+  // thread -> float4 element of the slice; all S partials of it in flight,
+  // summed in order s = 0..S-1
+  for (int vi = tid; vi < 16 * 32; vi += kResThreads) {
+    const int m = vi >> 5, c = (vi & 31) * 4;
+    const bool ok = m < M && c < JS;
+    const uint32_t voff = ok ? (uint32_t)(m * 128 + c) * 4u : 0u;
+    f32x4_t sum = zero4();
+    for (int p0 = 0; p0 < P.S; p0 += 32) {
+      f32x4_t t[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const uint32_t off = grp_base + (uint32_t)min(p0 + u, P.S - 1) * slice_bytes + voff;
+        t[u] = P.xcd_local ? buf_load16_l2(rW, off) : buf_load16_coherent(rW, off);
+      }
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (p0 + u < P.S) sum += t[u];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ts[m * 136 + c + i] = ok ? sum[i] : 0.f;
+  }
+  for (int idx = tid; idx < 16 * 8; idx += kResThreads) Ts[(idx >> 3) * 136 + 128 + (idx & 7)] = 0.f;
+  wait_vmem_all();  // B (loaded by waves 2-3) is in LDS
+  barrier_lds();
+  RES_TRACE(5);
+
+  // bf16 hi/lo split of this wave's 32 rank rows: lane (i = np, g) holds
+  // T[i][32w + 8g + q], q = 0..7.
+  u32x4_t thi, tlo;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float t0v = Ts[np * 136 + 32 * w + 8 * g + 2 * p];
+    const float t1v = Ts[np * 136 + 32 * w + 8 * g + 2 * p + 1];
+    const uint32_t h0 = f32_to_bf16_rne(t0v), h1 = f32_to_bf16_rne(t1v);
+    thi[p] = h0 | (h1 << 16);
+    tlo[p] = pack_bf16x2(t0v - __uint_as_float(h0 << 16), t1v - __uint_as_float(h1 << 16));
+  }
+
+  // ---------------------------------------------------------- GEMM2 ------
+  // Y partial layout per (s, js): [nt][M][128] fp32 = ntps*M*32 float4
+  const int vmax = ntps * M * 32;
+  const uint32_t ypart_wg = P.off_ypart + (uint32_t)(s * P.Jw + js) * (uint32_t)vmax * 16u;
+  for (int ntl = 0; ntl < nt_cnt; ++ntl) {
+    f32x4_t y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = zero4();
+#define LR_G2(D) gemm2_wave<D>(ctx, ntl, thi, tlo, y)
+    LR_LD8_SWITCH(N, LR_G2)
+#undef LR_G2
+    barrier_lds();  // previous tile's red reads (and the Ts reads) are done
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) red[(w * 16 + 4 * g + t) * 128 + 8 * np + e] = y[e][t];
+    barrier_lds();
+    for (int vi = tid; vi < M * 32; vi += kResThreads) {
+      const int m = vi >> 5, c = (vi & 31) * 4;
+      f32x4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = m * 128 + c + i;
+        v[i] = ((red[o] + red[16 * 128 + o]) + red[32 * 128 + o]) + red[48 * 128 + o];
+      }
+      buf_store16_coherent(rW, ypart_wg + (uint32_t)(ntl * M * 32 + vi) * 16u, v);
+    }
+  }
+  RES_TRACE(6);
+
+  // -------------------------------- Y reduce-scatter over the Jw slices --
+  if (nt_cnt > 0) {
+    wait_vmem_all();
+    barrier_lds();
+    const uint32_t yflag_grp = P.off_yflag + (uint32_t)(s * P.Jw) * 4u;
+    if (tid == 0) buf_store_u32_coherent(rW, yflag_grp + (uint32_t)js * 4u, epoch);
+    if (w == 0) {
+      uint32_t spins = 0;
+      while (true) {
+        bool ok = true;
+        for (int i = l; i < P.Jw; i += 64) ok = ok && (buf_load_u32_coherent(rW, yflag_grp + (uint32_t)i * 4u) == epoch);
+        if (__all(ok)) break;
+        if (++spins > kResSpinLimit) {
+          if (l == 0) st_agent_u32(P.ctrl + 2, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    barrier_lds();
+    RES_TRACE(7);
+    // my share of the n-slice: float4 indices [v_lo, v_hi) of nt_cnt*M*32
+    const int vtot = nt_cnt * M * 32;
+    const int share = (vtot + P.Jw - 1) / P.Jw;
+    const int v_lo = js * share;
+    const int v_hi = min(vtot, v_lo + share);
+    const uint32_t grp_y = P.off_ypart + (uint32_t)(s * P.Jw) * (uint32_t)vmax * 16u;
+    for (int vi = v_lo + tid; vi < v_hi; vi += kResThreads) {
+      f32x4_t sum = zero4();
+      for (int p0 = 0; p0 < P.Jw; p0 += 32) {
+        f32x4_t t[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+          t[u] = buf_load16_coherent(rW, grp_y + ((uint32_t)min(p0 + u, P.Jw - 1) * (uint32_t)vmax + (uint32_t)vi) * 16u);
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+          if (p0 + u < P.Jw) sum += t[u];
+      }
+      const int ntl = vi / (M * 32);
+      const int rem = vi - ntl * M * 32;
+      const int m = rem >> 5, c = (rem & 31) * 4;
+      const int64_t n0 = nb0 + (int64_t)ntl * kResNT + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n0 + i < N) P.Y[(int64_t)m * N + n0 + i] = (uint16_t)f32_to_bf16_rne(sum[i]);
+    }
+  }
+  RES_TRACE(8);
+}
+
+hipError_t launch_decode_res(const DecArgs& args, int grid, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)lr_decode_res_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kResLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(lr_decode_res_kernel, dim3(grid), dim3(kResThreads), kResLdsBytes, stream, args);
+  return hipGetLastError();
+}
+
+bool decode_res_available() {
+  int dev = 0, lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return false;
+  return lds >= kResLdsBytes;
+}
+
+// Records HW_REG_XCC_ID of each workgroup of a grid.
+__global__ void xcc_map_kernel(uint32_t* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
+}
+
+bool xcd_round_robin(int grid) {
+  uint32_t* d = nullptr;
+  if (hipMalloc(&d, (size_t)grid * 4) != hipSuccess) return false;
+  bool ok = false;
+  hipLaunchKernelGGL(xcc_map_kernel, dim3(grid), dim3(64), 0, 0, d);
+  uint32_t* h = new uint32_t[grid];
+  if (hipGetLastError() == hipSuccess && hipMemcpy(h, d, (size_t)grid * 4, hipMemcpyDeviceToHost) == hipSuccess) {
+    ok = true;
+    for (int i = 0; i < grid; ++i) ok = ok && (h[i] == (uint32_t)(i & 7));
+  }
+  delete[] h;
+  (void)hipFree(d);
+  return ok;
+}
+
+}  // namespace lrk

@@ -145,6 +145,45 @@ __device__ __forceinline__ f32x4_t buf_load16_coherent(rsrc_t r, uint32_t byte_o
 __device__ __forceinline__ void buf_store16_coherent(rsrc_t r, uint32_t byte_off, const f32x4_t& v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)byte_off, 0, kCoherent);
 }
+// Loads that skip the compute unit's L1 but may hit the XCD's L2: data
+// written by other compute units of the same XCD through that L2.  This is
+// the non-temporal bit (nt).  sc0 alone is work-group scope, which may be
+// served from a stale L1 line: a poll loop on such a load can spin on the
+// old value until the line happens to be evicted.
+constexpr int kSkipL1 = 2;
+__device__ __forceinline__ f32x4_t buf_load16_l2(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kSkipL1));
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t byte_off, const f32x4_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)byte_off, 0, 0);
+}
+// Flag reads for poll loops.  The compiler fences around each load keep it
+// inside the loop (a plain buffer load with nothing else touching memory in
+// the loop could legally be hoisted out of it).
+__device__ __forceinline__ uint32_t buf_load_u32_l2(rsrc_t r, uint32_t byte_off) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kSkipL1);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return v;
+}
+__device__ __forceinline__ uint32_t buf_load_u32_coherent(rsrc_t r, uint32_t byte_off) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kCoherent);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return v;
+}
+__device__ __forceinline__ void buf_store_u32(rsrc_t r, uint32_t byte_off, uint32_t v) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)byte_off, 0, 0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ void buf_store_u32_coherent(rsrc_t r, uint32_t byte_off, uint32_t v) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)byte_off, 0, kCoherent);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Id of the XCD (accelerator complex die) this wave runs on (HW_REG_XCC_ID).
+__device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xFu; }
 
 // Raw half of a realigned row-segment load: lane16 of a 16-lane DPP row
 // loads the aligned chunk that holds column colbase + 8*lane16 - d of row
@@ -215,6 +254,20 @@ __device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
 __device__ __forceinline__ uint32_t add_agent_u32(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// accesses (lgkmcnt = 0) and meets the other waves, without waiting for
+// global loads or stores still in flight.  (__syncthreads() also drains the
+// vector-memory counter, which would stall every barrier behind loads that
+// are deliberately kept in flight and behind write-through stores.)  Code
+// that needs global stores or LDS-DMA loads complete calls wait_vmem_all()
+// first.
+__device__ __forceinline__ void barrier_lds() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Wait until every vector memory operation of this wave has completed
 // (gfx9 encoding: vmcnt = 0, expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem_all() {

@@ -30,11 +30,15 @@ struct DecProj {
   const void* ws;
   uint32_t* ctrl;   // [0] generation, [1] finished n-slices, [2] spin-timeout flag
   uint32_t* tcnt;   // [Jw] arrivals of T partials (self-resetting)
-  uint32_t* tflag;  // [Jw] epoch stamp of a published T slice
+  uint32_t* tflag;  // epoch stamps: [Jw] published T slices (streaming), [Jw*S] partials (resident)
   uint32_t* ycnt;   // [S] arrivals of Y partials (self-resetting)
   int64_t ws_bytes;
   uint32_t off_tpart, off_tfin, off_ypart;
+  uint32_t off_tflag, off_yflag;  // resident kernel: [Jw*S] flag words each
+  uint32_t epoch;                  // resident kernel: stamp of this call (host counter, never 0)
   int r, N, Jw, S, ktps, ntps, wg_begin;
+  int js_w;       // rank columns per slice
+  int xcd_local;  // resident kernel: rank-slice groups share an XCD (verified map)
 };
 
 struct DecArgs {
@@ -43,17 +47,41 @@ struct DecArgs {
   int M, K, nproj, pad_;
   DecProj p[kDecMaxProj];
 };
-constexpr int kDecTracePoints = 8;
+constexpr int kDecTracePoints = 16;
 
 hipError_t launch_decode(const DecArgs& args, int grid, hipStream_t stream);
+
+// LDS-resident decode kernel (lr_decode_res.hip): 128-column rank slices,
+// every slab of a workgroup held in LDS at once.
+constexpr int kResThreads = 256;
+constexpr int kResJS = 128;
+constexpr int kResKT = 32;
+constexpr int kResNT = 128;
+constexpr int kResMaxKt = 8;   // k-tiles per workgroup
+constexpr int kResMaxNt = 2;   // n-tiles per workgroup
+constexpr int kResCA = kResJS / 8 + 1;                 // chunks per A row run
+constexpr int kResXK = kResMaxKt * kResKT;             // X columns staged
+constexpr int kResXBytes = 16 * kResXK * 2;
+constexpr int kResABytes = kResMaxKt * kResKT * kResCA * 16;
+constexpr int kResBBytes = kResJS * (kResNT / 8 * kResMaxNt + 1) * 16;
+constexpr int kResRedBytes = 4 * 16 * kResJS * 4;
+constexpr int kResLdsBytes = kResXBytes + kResABytes + kResBBytes;
+static_assert(kResRedBytes + 16 * (kResJS + 8) * 4 <= kResABytes, "reduction buffers must fit the A region");
+hipError_t launch_decode_res(const DecArgs& args, int grid, hipStream_t stream);
+// True when the device accepts kResLdsBytes of LDS per workgroup.
+bool decode_res_available();
+// True when workgroup i of a `grid`-sized launch runs on XCD i % 8 for every i
+// (checked with HW_REG_XCC_ID).
+bool xcd_round_robin(int grid);
 // Workgroups of the decode kernel that one compute unit holds at once (0 on error).
 int decode_blocks_per_cu();
 
 // --------------------------------------------------------------- prefill ---
-constexpr int kPreThreads = 256;  // 4 waves: 2 (M) x 2 (N)
-constexpr int kPreBM = 128;       // rows per workgroup tile
-constexpr int kPreBN = 240;       // columns per workgroup tile (2 waves x 120)
-constexpr int kPreKT = 32;
+constexpr int kPreThreads = 256;  // 4 waves, each 64 rows x all columns of the tile
+constexpr int kPreBM = 256;       // rows per workgroup tile
+constexpr int kPreBN = 240;       // columns per workgroup tile (15 MFMA column tiles)
+constexpr int kPreKT = 64;        // k per LDS stage
+constexpr int kPreLdsBytes = 2 * (15 + 16) * 2080;  // two stages of Q (240 cols) + P (256 rows) tiles
 
 // C[rows x out_cols] = P[rows x kd] . Q[kd x ldq] for one or two column
 // blocks in one launch.  P is k-contiguous (X or T); Q is row-major with
@@ -79,5 +107,7 @@ struct PreArgs {
   PreOut o[2];
 };
 hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream);
+// True when the device accepts kPreLdsBytes of LDS per workgroup.
+bool prefill_available();
 
 }  // namespace lrk

@@ -10,6 +10,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "../../include/lr_linear.h"
@@ -57,7 +59,9 @@ struct lr_linear {
   uint32_t* tcnt;
   uint32_t* tflag;
   uint32_t* ycnt;
-  uint32_t off_tpart, off_tfin, off_ypart;
+  uint32_t off_tpart, off_tfin, off_ypart, off_tflag, off_yflag;
+  bool xcd_local;
+  mutable std::atomic<uint32_t> epoch;  // stamp of the last call (resident decode kernel)
   // prefill workspace: T [max_M x r_pad] bf16
   bool has_prefill;
   uint16_t* Tbuf;
@@ -86,6 +90,13 @@ lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
   p.off_tpart = h->off_tpart;
   p.off_tfin = h->off_tfin;
   p.off_ypart = h->off_ypart;
+  p.off_tflag = h->off_tflag;
+  p.off_yflag = h->off_yflag;
+  uint32_t ep = h->epoch.fetch_add(1u) + 1u;
+  if (ep == 0u) ep = h->epoch.fetch_add(1u) + 1u;  // 0 is the value of a fresh flag
+  p.epoch = ep;
+  p.js_w = h->dp.js_w;
+  p.xcd_local = h->xcd_local ? 1 : 0;
   p.r = (int)h->r;
   p.N = (int)h->N;
   p.Jw = h->dp.Jw;
@@ -94,6 +105,21 @@ lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
   p.ntps = h->dp.ntps;
   p.wg_begin = wg_begin;
   return p;
+}
+
+// Whether workgroups are dealt to XCDs round-robin (checked once per device).
+bool xcd_map_ok(int device) {
+  static std::mutex mu;
+  static int cached[64];
+  static bool init = false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!init) {
+    for (int& c : cached) c = -1;
+    init = true;
+  }
+  if (device < 0 || device >= 64) return false;
+  if (cached[device] < 0) cached[device] = lrk::xcd_round_robin(1024) ? 1 : 0;
+  return cached[device] == 1;
 }
 
 int num_cus(int device) {
@@ -122,7 +148,7 @@ lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, con
     a.p[i] = dec_proj(hs[i], Ys[i], wg);
     wg += hs[i]->dp.Jw * hs[i]->dp.S;
   }
-  hipError_t e = lrk::launch_decode(a, wg, stream);
+  hipError_t e = hs[0]->dp.kind == 1 ? lrk::launch_decode_res(a, wg, stream) : lrk::launch_decode(a, wg, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return LR_OK;
 }
@@ -211,7 +237,8 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
 
   lr_linear* h = new (std::nothrow) lr_linear;
   if (!h) return fail(LR_ERR_OUT_OF_MEMORY, "host allocation failed");
-  memset(h, 0, sizeof *h);
+  memset((void*)h, 0, sizeof *h);
+  h->epoch.store(0u);
   h->K = K;
   h->r = r;
   h->N = N;
@@ -234,27 +261,36 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
       delete h;
       return fail(LR_ERR_HIP, "decode kernel cannot be resident on this device");
     }
-    h->dp = lrv::decode_partition(K, r, N, num_cus(dev));
+    h->dp = lrv::decode_partition(K, r, N, num_cus(dev),
+                                  !(flags & LR_FLAG_DECODE_STREAMING) && lrk::decode_res_available());
     const int64_t G = (int64_t)h->dp.Jw * h->dp.S;
     o_ctrl = off;
     off = align_up(off + 64);
     o_tcnt = off;
     off = align_up(off + (size_t)h->dp.Jw * 4);
     o_tflag = off;
-    off = align_up(off + (size_t)h->dp.Jw * 4);
+    off = align_up(off + (size_t)G * 4);  // one flag per workgroup (resident kernel) or per slice
+    h->off_yflag = (uint32_t)off;
+    off = align_up(off + (size_t)G * 4);
     o_ycnt = off;
     off = align_up(off + (size_t)h->dp.S * 4);
     o_tpart = off;
-    off = align_up(off + (size_t)G * h->dec_max_M * lrk::kDecJS * 4);
+    off = align_up(off + (size_t)G * h->dec_max_M * (h->dp.kind == 1 ? 128 : h->dp.js_w) * 4);
     o_tfin = off;
-    off = align_up(off + (size_t)h->dp.Jw * h->dec_max_M * lrk::kDecJS * 4);
+    off = align_up(off + (size_t)h->dp.Jw * h->dec_max_M * h->dp.js_w * 4);
     o_ypart = off;
-    off = align_up(off + (size_t)G * h->dp.ntps * h->dec_max_M * lrk::kDecNT * 4);
+    off = align_up(off + (size_t)G * h->dp.ntps * h->dec_max_M * h->dp.nt_w * 4);
+    h->xcd_local = h->dp.kind == 1 && (h->dp.Jw % 8 == 0) && xcd_map_ok(dev);
     if (off >= ((size_t)1 << 31)) {
       delete h;
       return fail(LR_ERR_UNSUPPORTED, "decode workspace of %zu bytes exceeds 2 GiB", off);
     }
     h->dws_bytes = (int64_t)off;
+  }
+  if (h->has_prefill && !lrk::prefill_available()) {
+    delete h;
+    return fail(LR_ERR_UNSUPPORTED, "device %d cannot give a workgroup %d bytes of LDS (prefill kernel)", dev,
+                lrk::kPreLdsBytes);
   }
   if (h->has_prefill) {
     o_tbuf = off;
@@ -286,6 +322,7 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     h->off_tpart = (uint32_t)o_tpart;
     h->off_tfin = (uint32_t)o_tfin;
     h->off_ypart = (uint32_t)o_ypart;
+    h->off_tflag = (uint32_t)o_tflag;
   }
   if (h->has_prefill) h->Tbuf = (uint16_t*)(base + o_tbuf);
   *out = h;
@@ -319,7 +356,9 @@ lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const vo
     // One launch when both projections' workgroups fit on the device at
     // once (every exchange group must be resident); else one per projection.
     const int64_t G = (int64_t)gate->dp.Jw * gate->dp.S + (int64_t)up->dp.Jw * up->dp.S;
-    if (G <= (int64_t)num_cus(gate->device) * lrk::decode_blocks_per_cu()) return run_decode(hs, Ys, 2, X, M, (hipStream_t)stream);
+    const int per_cu = gate->dp.kind == 1 ? 1 : lrk::decode_blocks_per_cu();
+    if (gate->dp.kind == up->dp.kind && G <= (int64_t)num_cus(gate->device) * per_cu)
+      return run_decode(hs, Ys, 2, X, M, (hipStream_t)stream);
     st = run_decode(hs, Ys, 1, X, M, (hipStream_t)stream);
     if (st != LR_OK) return st;
     return run_decode(hs + 1, Ys + 1, 1, X, M, (hipStream_t)stream);
@@ -336,10 +375,10 @@ void lr_linear_destroy(lr_linear* h) {
 lr_status lr_linear_describe(const lr_linear* h, char* buf, int64_t len) {
   if (!h || !buf || len <= 0) return fail(LR_ERR_INVALID_ARG, "null handle or buffer");
   snprintf(buf, (size_t)len,
-           "K=%lld r=%lld N=%lld r_pad=%lld max_M=%lld decode=%d[Jw=%d S=%d ktps=%d ntps=%d grid=%d] "
-           "prefill=%d workspace=%zu",
+           "K=%lld r=%lld N=%lld r_pad=%lld max_M=%lld decode=%d[kind=%s Jw=%d JS=%d S=%d ktps=%d ntps=%d grid=%d] "
+           "xcd_local=%d prefill=%d workspace=%zu",
            (long long)h->K, (long long)h->r, (long long)h->N, (long long)h->r_pad, (long long)h->max_M,
-           (int)h->has_decode, h->dp.Jw, h->dp.S, h->dp.ktps, h->dp.ntps, h->dp.Jw * h->dp.S, (int)h->has_prefill,
+           (int)h->has_decode, h->dp.kind == 1 ? "resident" : "streaming", h->dp.Jw, h->dp.js_w, h->dp.S, h->dp.ktps, h->dp.ntps, h->dp.Jw * h->dp.S, (int)h->xcd_local, (int)h->has_prefill,
            h->ws_bytes);
   return LR_OK;
 }

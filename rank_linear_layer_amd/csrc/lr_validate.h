@@ -47,7 +47,7 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
     snprintf(err, errlen, "a matrix would exceed 2 GiB (32-bit buffer addressing)");
     return LR_ERR_UNSUPPORTED;
   }
-  const uint32_t known = LR_FLAG_FORCE_DECODE | LR_FLAG_FORCE_PREFILL;
+  const uint32_t known = LR_FLAG_FORCE_DECODE | LR_FLAG_FORCE_PREFILL | LR_FLAG_DECODE_STREAMING;
   if (flags & ~known) { snprintf(err, errlen, "unknown flag bits 0x%x", flags & ~known); return LR_ERR_UNSUPPORTED; }
   if ((flags & LR_FLAG_FORCE_DECODE) && (flags & LR_FLAG_FORCE_PREFILL)) {
     snprintf(err, errlen, "FORCE_DECODE and FORCE_PREFILL are exclusive");
@@ -104,18 +104,57 @@ inline lr_status check_packed(const Shape& g, const Shape& u, const void* X, con
 }
 
 // ------------------------------------------------------------ partition ---
-// Decode kernel: rank slices of 120 columns (Jw of them); K and N cut into S
-// slices.  S minimises the bytes streamed by the busiest workgroup, subject
-// to Jw * S <= budget (one workgroup per compute unit), ties to smaller S.
+// Decode kernels cut the rank into Jw slices and K and N into S slices;
+// workgroup (js, s) owns rank slice js, K slice s and N slice s.
+//  kind 1 (LDS-resident): Jw is a multiple of 8 and slices are at most 128
+//    columns wide (a multiple of 8); every slab of a workgroup fits in LDS at
+//    once: at most 8 k-tiles of 32 rows and 2 n-tiles of 128 columns; one
+//    workgroup per CU, so Jw * S <= CUs.  Requires K % 8 == 0 (rows of X are
+//    staged as aligned 16-byte chunks).
+//  kind 0 (streaming, 120-wide slices): any shape; tiles stream through
+//    registers.
+// S minimises the elements streamed by the busiest workgroup (ties to the
+// smaller S), subject to Jw * S <= budget.
 struct DecPart {
-  int Jw, S, ktps, ntps;
+  int kind, Jw, S, ktps, ntps, js_w, nt_w;
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget) {
+inline int64_t round_up8(int64_t a) { return (a + 7) / 8 * 8; }
+
+inline bool decode_resident_partition(int64_t K, int64_t r, int64_t N, int budget, DecPart* out) {
+  if (K % 8 != 0) return false;
+  const int64_t kt = 32, nt = 128;
+  // Jw a multiple of 8 (one rank-slice group per XCD slot), slices <= 128 wide
+  const int64_t Jw = 8 * ceil_div(ceil_div(r, 128), 8);
+  const int64_t js_w = round_up8(ceil_div(r, Jw));
+  const int64_t nk = ceil_div(K, kt), nn = ceil_div(N, nt);
+  int64_t best_s = -1, best_cost = -1;
+  for (int64_t S = 1; S * Jw <= budget; ++S) {
+    const int64_t ktps = ceil_div(nk, S), ntps = ceil_div(nn, S);
+    if (ktps > 8 || ntps > 2) continue;
+    if ((S - 1) * ktps >= nk && (S - 1) * ntps >= nn) continue;  // a fully idle slice
+    const int64_t cost = ktps * kt * js_w + ntps * js_w * nt;
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_s = S; }
+  }
+  if (best_s < 0) return false;
+  out->kind = 1;
+  out->Jw = (int)Jw;
+  out->S = (int)best_s;
+  out->ktps = (int)ceil_div(nk, best_s);
+  out->ntps = (int)ceil_div(nn, best_s);
+  out->js_w = (int)js_w;
+  out->nt_w = (int)nt;
+  return true;
+}
+
+inline DecPart decode_streaming_partition(int64_t K, int64_t r, int64_t N, int budget) {
   const int64_t js_w = 120, kt = 32, nt = 120;
   DecPart p;
+  p.kind = 0;
+  p.js_w = (int)js_w;
+  p.nt_w = (int)nt;
   p.Jw = (int)ceil_div(r, js_w);
   const int64_t nk = ceil_div(K, kt), nn = ceil_div(N, nt);
   int64_t smax = budget / p.Jw;
@@ -131,6 +170,12 @@ inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget) {
   p.ktps = (int)ceil_div(nk, best_s);
   p.ntps = (int)ceil_div(nn, best_s);
   return p;
+}
+
+inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget, bool allow_resident = true) {
+  DecPart p;
+  if (allow_resident && decode_resident_partition(K, r, N, budget, &p)) return p;
+  return decode_streaming_partition(K, r, N, budget);
 }
 
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }

@@ -45,10 +45,14 @@ def run_case(M, K, r, N, seed, flags=0, max_M=None, full=True, rows=None, cols=N
 
 # ------------------------------------------------------------ workloads ---
 
+DECODE_KERNELS = [0, lrl.LR_FLAG_DECODE_STREAMING]
+
+
 @pytest.mark.parametrize("M", [1, 8, 16])
-def test_tiny_decode(M):
+@pytest.mark.parametrize("dflag", DECODE_KERNELS)
+def test_tiny_decode(M, dflag):
     c = configs.TINY
-    run_case(M, c["K"], c["r"], c["N"], configs.seed_base(0))
+    run_case(M, c["K"], c["r"], c["N"], configs.seed_base(0), flags=dflag)
 
 
 @pytest.mark.parametrize("M", [16, 17, 200])
@@ -81,9 +85,10 @@ def test_eckart_young_factors_decode_and_prefill(gpu):
     del torch
 
 
-def test_qproj_decode_full():
+@pytest.mark.parametrize("dflag", DECODE_KERNELS)
+def test_qproj_decode_full(dflag):
     c = configs.QPROJ_DECODE
-    p, lin, _, _ = run_case(c["M"], c["K"], c["r"], c["N"], configs.seed_base(c["index"]))
+    p, lin, _, _ = run_case(c["M"], c["K"], c["r"], c["N"], configs.seed_base(c["index"]), flags=dflag)
     banner("q_proj decode parity %s plan %s" % (p, lin.describe()))
 
 
@@ -97,7 +102,7 @@ def test_mlp_up_prefill_sampled():
     banner("mlp_up prefill sampled parity %s plan %s" % (p, lin.describe()))
 
 
-@pytest.mark.parametrize("name", ["q", "k", "down"])
+@pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
 def test_layer_projections_decode_m1(name):
     proj = {p.name: p for p in configs.LAYER_PROJS}[name]
     idx = [p.name for p in configs.LAYER_PROJS].index(name)
@@ -130,6 +135,17 @@ def test_adversarial_shapes(M, K, r, N):
     run_case(M, K, r, N, 9000 + 31 * r + N + M)
 
 
+# decode shapes that fit the LDS-resident kernel (K % 8 == 0), both kernels
+RES_GRID = [(1, 8, 1, 1), (3, 64, 5, 48), (16, 256, 129, 257), (7, 2048, 255, 300), (2, 512, 128, 128),
+            (5, 512, 383, 3999), (16, 8192, 64, 64), (1, 4096, 1100, 3999)]
+
+
+@pytest.mark.parametrize("M,K,r,N", RES_GRID)
+@pytest.mark.parametrize("dflag", DECODE_KERNELS)
+def test_decode_kernels_resident_shapes(M, K, r, N, dflag):
+    run_case(M, K, r, N, 7100 + r + N + M, flags=dflag)
+
+
 @pytest.mark.parametrize("M,K,r,N,flags", [(3, 96, 13, 29, lrl.LR_FLAG_FORCE_PREFILL),
                                            (40, 40, 9, 17, 0), (16, 2000, 300, 250, lrl.LR_FLAG_FORCE_PREFILL),
                                            (2, 2000, 300, 250, 0)])
@@ -140,7 +156,7 @@ def test_forced_paths(M, K, r, N, flags):
 # ---------------------------------------------------------------- packed ---
 
 @pytest.mark.parametrize("M", [1, 4, 64])
-def test_mlp_packed_matches_oracle_and_separate_runs(M):
+def test_mlp_packed_matches_oracle_and_separate_runs(M):  # noqa: C901
     K, r, N = 512, 67, 700
     banner("packed M=%d" % M)
     Xb = datagen.normal_bf16((M, K), 1.0, 31)
@@ -176,7 +192,7 @@ def test_canary_guards_and_poison(gpu, M, N, flags):
     assert_parity(allbits[G:G + M * N].reshape(M, N), oracle.lowrank_bf16(Xb, Ab, Bb), "canary")
 
 
-@pytest.mark.parametrize("M,flags", [(8, 0), (48, 0)])
+@pytest.mark.parametrize("M,flags", [(8, 0), (8, lrl.LR_FLAG_DECODE_STREAMING), (48, 0)])
 def test_deterministic_bitwise(M, flags):
     K, r, N = 1024, 333, 1500
     Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 1234)

@@ -32,9 +32,10 @@ int t_check_packed(long long Kg, long long Ku, long long r, long long N, unsigne
   lrv::Shape u{Ku, r, N, 64, (const void*)Au, (const void*)Bu};
   return lrv::check_packed(g, u, (const void*)X, (const void*)Yg, (const void*)Yu, M, err, sizeof err);
 }
-void t_partition(long long K, long long r, long long N, int budget, int* out) {
-  lrv::DecPart p = lrv::decode_partition(K, r, N, budget);
+void t_partition(long long K, long long r, long long N, int budget, int allow_res, int* out) {
+  lrv::DecPart p = lrv::decode_partition(K, r, N, budget, allow_res != 0);
   out[0] = p.Jw; out[1] = p.S; out[2] = p.ktps; out[3] = p.ntps;
+  out[4] = p.kind; out[5] = p.js_w; out[6] = p.nt_w;
 }
 }
 """
@@ -53,7 +54,7 @@ def shim(tmp_path_factory):
     lib.t_check_create.argtypes = [ll, ll, ll, ull, ull, ll, ctypes.c_uint]
     lib.t_check_run.argtypes = [ll, ll, ll, ll, ull, ull, ull, ull, ll]
     lib.t_check_packed.argtypes = [ll, ll, ll, ll, ull, ull, ull, ull, ull, ull, ull, ll]
-    lib.t_partition.argtypes = [ll, ll, ll, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.t_partition.argtypes = [ll, ll, ll, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     return lib
 
 
@@ -66,7 +67,8 @@ def test_create_validation(shim):
     assert shim.t_check_create(4096, 1637, 4096, 0, 0x2000000, 16, 0) == INVALID
     assert shim.t_check_create(4096, 0, 4096, 0x100000, 0x2000000, 16, 0) == INVALID
     assert shim.t_check_create(4096, 1637, 4096, 0x100008, 0x2000000, 16, 0) == INVALID  # 8B aligned only
-    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 4) == UNSUPPORTED
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 8) == UNSUPPORTED
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 4) == OK
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 17, 1) == UNSUPPORTED
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 17, 2) == OK
     assert shim.t_check_create(1 << 25, 8, 8, 0x100000, 0x2000000, 1, 0) == INVALID
@@ -101,27 +103,48 @@ def test_packed_validation(shim):
     assert shim.t_check_packed(64, 64, 5, 48, Ag, Bg, Au, Bu, X, Au, Yu, 4) == INVALID
 
 
-def _part(shim, K, r, N, budget=256):
-    out = (ctypes.c_int * 4)()
-    shim.t_partition(K, r, N, budget, out)
+def _part(shim, K, r, N, budget=256, allow_res=True):
+    out = (ctypes.c_int * 7)()
+    shim.t_partition(K, r, N, budget, 1 if allow_res else 0, out)
     return list(out)
 
 
-@pytest.mark.parametrize("K,r,N", [(4096, 1637, 4096), (512, 107, 512), (64, 5, 48), (4096, 817, 1024),
-                                   (4096, 2867, 14336), (14336, 2867, 4096), (4096, 1000, 3999),
-                                   (7, 1, 1), (4096, 5000, 4096)])
-def test_decode_partition_covers_and_fits(shim, K, r, N):
-    Jw, S, ktps, ntps = _part(shim, K, r, N)
-    assert Jw == -(-r // 120)
-    assert Jw * S <= max(256, Jw)            # one workgroup per CU (or one slice row if r is huge)
-    nk, nn = -(-K // 32), -(-N // 120)
+SHAPES = [(4096, 1637, 4096), (512, 107, 512), (64, 5, 48), (4096, 817, 1024), (4096, 2867, 14336),
+          (14336, 2867, 4096), (4096, 1000, 3999), (7, 1, 1), (4096, 5000, 4096), (4096, 1100, 3999), (12, 3, 7)]
+
+
+@pytest.mark.parametrize("K,r,N", SHAPES)
+@pytest.mark.parametrize("allow_res", [True, False])
+def test_decode_partition_covers_and_fits(shim, K, r, N, allow_res):
+    Jw, S, ktps, ntps, kind, js_w, nt_w = _part(shim, K, r, N, allow_res=allow_res)
+    assert Jw == -(-r // js_w) or (kind == 1 and Jw * js_w >= r)
+    nk, nn = -(-K // 32), -(-N // nt_w)
     assert S * ktps >= nk and S * ntps >= nn   # every tile is owned
     assert (S - 1) * ktps < nk or (S - 1) * ntps < nn  # no fully idle slice
     assert S >= 1 and ktps >= 1 and ntps >= 1
+    if kind == 1:
+        # resident kernel: one workgroup per CU, slabs fit the LDS plan
+        assert allow_res and K % 8 == 0 and nt_w == 128
+        assert js_w % 8 == 0 and 8 <= js_w <= 128 and Jw % 8 == 0 and Jw * js_w >= r
+        assert Jw * S <= 256 and ktps <= 8 and ntps <= 2
+    else:
+        assert (js_w, nt_w) == (120, 120)
+        assert Jw * S <= max(256, Jw)
+
+
+def test_resident_partition_chosen_for_decode_workloads(shim):
+    # q_proj, k/v projections and the alignment sweep fit the resident kernel
+    for K, r, N in [(4096, 1637, 4096), (4096, 817, 1024), (4096, 1000, 4096), (4096, 1100, 3999)]:
+        assert _part(shim, K, r, N)[4] == 1, (K, r, N)
+    # MLP projections are too large per workgroup: streaming kernel
+    for K, r, N in [(4096, 2867, 14336), (14336, 2867, 4096)]:
+        assert _part(shim, K, r, N)[4] == 0, (K, r, N)
+    # K not a multiple of 8: streaming kernel
+    assert _part(shim, 4100, 100, 512)[4] == 0
 
 
 def test_decode_partition_balances_q_proj(shim):
-    Jw, S, ktps, ntps = _part(shim, 4096, 1637, 4096)
+    Jw, S, ktps, ntps, kind, js_w, nt_w = _part(shim, 4096, 1637, 4096, allow_res=False)
     assert Jw == 14
     # per-workgroup element count is within 25% of the ideal even split
     per_wg = ktps * 32 * 120 + ntps * 120 * 120
