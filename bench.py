@@ -32,8 +32,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "low-rank linear: decode TB/s and prefill TFLOP/s vs roofline, across rank r"
-KERNEL_SOURCES = ["rank_linear_layer_amd/csrc/lr_decode.hip", "rank_linear_layer_amd/csrc/lr_prefill.hip",
-                  "rank_linear_layer_amd/csrc/lr_device.h", "rank_linear_layer_amd/csrc/lr_kernels.h"]
+KERNEL_SOURCES = ["rank_linear_layer_amd/csrc/lr_decode.hip", "rank_linear_layer_amd/csrc/lr_decode_res.hip",
+                  "rank_linear_layer_amd/csrc/lr_prefill.hip", "rank_linear_layer_amd/csrc/lr_device.h",
+                  "rank_linear_layer_amd/csrc/lr_kernels.h"]
 
 
 def kernel_source_hash() -> str:
@@ -64,6 +65,24 @@ def time_steps(torch, fn, steps, warmup, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps  # ms per step
+
+
+def time_launches(torch, fn, n, stream):
+    """Average duration of one launch: an event pair around each of n
+    launches on the launch stream (the GPU-side time of that launch alone,
+    without the gaps between steps)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / n  # ms
+
+
+def decode_kernel_name(plan):
+    return "lr_decode_res_kernel" if "kind=resident" in plan else "lr_decode_fused_kernel"
 
 
 def traffic_from_profile(name, launches_bytes):
@@ -102,9 +121,10 @@ def bench_decode(torch, lrl, configs, datagen, metrics, steps, warmup):
 
     ms = time_steps(torch, step, steps, warmup, stream)
     tbs = per / (ms * 1e-3) / 1e12
+    ms_launch = time_launches(torch, step, steps, stream)
     # warm-cache figure (same copy every step) for context
     ms_warm = time_steps(torch, lambda i: lins[0](X, out=Y), max(50, steps // 4), 10, stream)
-    return dict(M=M, K=K, r=r, N=N, ms=ms, tbs=tbs, bytes=per, ncopies=ncopies,
+    return dict(M=M, K=K, r=r, N=N, ms=ms, tbs=tbs, bytes=per, ncopies=ncopies, ms_launch=ms_launch,
                 warm_tbs=per / (ms_warm * 1e-3) / 1e12, plan=lins[0].describe())
 
 
@@ -218,7 +238,10 @@ def main():
 
     torch.cuda.synchronize()
     d = bench_decode(torch, lrl, configs, datagen, metrics, args.steps, args.warmup)
-    log("decode: %.3f us/step, %.3f TB/s (warm-cache %.3f TB/s)" % (d["ms"] * 1e3, d["tbs"], d["warm_tbs"]))
+    log("decode: %.3f us/step, %.3f TB/s (warm-cache %.3f TB/s); %.3f us per launch alone"
+        % (d["ms"] * 1e3, d["tbs"], d["warm_tbs"], d["ms_launch"] * 1e3))
+    kname = decode_kernel_name(d["plan"])
+    ach = d["bytes"] / (d["ms_launch"] * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(d["tbs"], 4),
@@ -234,12 +257,12 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) bf16 factors; %d rotating weight copies, "
                 "cold last-level cache)" % d["ncopies"],
         "config": {"workload": "Llama-3-8B-shaped q_proj decode, misaligned rank", "M": d["M"], "K": d["K"],
-                   "r": d["r"], "N": d["N"], "path": "fused decode kernel", "weight_copies": d["ncopies"]},
-        "roofline": {"bound": "hbm", "achieved": round(d["bytes"] / (d["ms"] * 1e-3) / 1e9, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(d["bytes"] / (d["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile("lr_decode_fused_qproj_decode_pmc.json", d["bytes"]),
-                     "kernel": "lr_decode_fused_kernel", "algorithmic_bytes_per_launch": d["bytes"]},
+                   "r": d["r"], "N": d["N"], "path": kname, "weight_copies": d["ncopies"]},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile("%s_qproj_decode_pmc.json" % kname, d["bytes"]),
+                     "kernel": kname, "algorithmic_bytes_per_launch": d["bytes"],
+                     "us_per_launch": round(d["ms_launch"] * 1e3, 3)},
         "warm_cache_tbs": round(d["warm_tbs"], 4),
     }
     if not args.no_prefill:

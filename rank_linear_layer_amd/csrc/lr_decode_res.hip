@@ -51,25 +51,32 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, void* lds_base_wave, uint32
 }
 
 __device__ __forceinline__ u32x4_t lds_read16(const char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void lds_write16(char* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 
 // 8 rows held as chunk runs in LDS (row q at rows + q * pitch) -> 8 MFMA
-// B-operands.  lane16 reads chunks c_off + lane16 and c_off + lane16 + 1 of
-// each run; LD8 = (leading dimension mod 8) fixes every row's shift.
+// B-operands, in two steps so that the LDS reads of the next tile can be in
+// flight while this one is transposed.  lane16 reads chunks c_off + lane16
+// and c_off + lane16 + 1 of each run; LD8 = (leading dimension mod 8) fixes
+// every row's shift.  No masking here: rows past the matrix are zero in
+// LDS, and output columns past the slice or the matrix are dropped by the
+// callers.
+struct TileRaw {
+  u32x4_t lo[8], hi[8];
+};
 template <int LD8>
-__device__ __forceinline__ void lds_tile_ops(const char* rows, int pitch, int c_off, int lane16, int64_t col0,
-                                             int64_t ncols, int64_t row0, int64_t row_end, u32x4_t op[8]) {
-  u32x4_t lo[8], hi[8], seg[8];
+__device__ __forceinline__ void tile_read(const char* rows, int pitch, int c_off, int lane16, TileRaw& t) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const char* p = rows + q * pitch + (c_off + lane16) * 16;
-    lo[q] = lds_read16(p);
-    hi[q] = lds_read16(p + 16);
+    t.lo[q] = lds_read16(p);
+    if (((q * LD8) & 7) != 0) t.hi[q] = lds_read16(p + 16);
   }
+}
+template <int LD8>
+__device__ __forceinline__ void tile_ops(const TileRaw& t, u32x4_t op[8]) {
+  u32x4_t seg[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const u32x4_t v = mask_cols(realign(lo[q], hi[q], (q * LD8) & 7), col0, ncols);
-    seg[q] = (row0 + q < row_end) ? v : zerou4();
-  }
+  for (int q = 0; q < 8; ++q) seg[q] = ((q * LD8) & 7) != 0 ? realign(t.lo[q], t.hi[q], (q * LD8) & 7) : t.lo[q];
   transpose8x8(seg, op);
 }
 
@@ -82,33 +89,56 @@ struct ResCtx {
   int64_t kbase, j0, jend, K, r, N, nb0;
 };
 
-// GEMM1 partial over this wave's k-tiles (t = w, w + 4, ...).
+// GEMM1 partial over this wave's k-tiles t = w and w + 4 (a workgroup holds
+// at most 8 k-tiles).  Both tiles are always computed: the LDS rows of tiles
+// past kt_cnt are zero and their X operand is cleared, so they add exact
+// zeros.  (Straight-line MFMA code keeps the accumulators in place; a
+// conditional block around the MFMAs made the compiler shuffle them right
+// behind each MFMA.)
 template <int LD8>
 __device__ __forceinline__ void gemm1_wave(const ResCtx& c, f32x4_t acc[8]) {
-  for (int t = c.w; t < c.kt_cnt; t += 4) {
-    const int64_t krow0 = c.kbase + (int64_t)t * kResKT + 8 * c.g;
+  const int pitch = kResCA * 16;
+  TileRaw rt[2];
+  u32x4_t xt[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = c.w + 4 * h;
+    tile_read<LD8>(c.sA + (size_t)(t * kResKT + 8 * c.g) * pitch, pitch, 0, c.np, rt[h]);
+    xt[h] = lds_read16(c.sX + c.np * (kResXK * 2) + (t * kResKT + 8 * c.g) * 2);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = c.w + 4 * h;
     u32x4_t op[8];
-    lds_tile_ops<LD8>(c.sA + (size_t)(t * kResKT + 8 * c.g) * (kResCA * 16), kResCA * 16, 0, c.np,
-                      c.j0 + 8 * c.np, c.jend, krow0, c.K, op);
-    const u32x4_t x = kvec_mask(lds_read16(c.sX + c.np * (kResXK * 2) + (t * kResKT + 8 * c.g) * 2), krow0, c.K);
+    tile_ops<LD8>(rt[h], op);
+    // X columns >= K (and tiles past kt_cnt) contribute zero
+    const int64_t k0 = c.kbase + (int64_t)t * kResKT + 8 * c.g;
+    const u32x4_t x = (t < c.kt_cnt && k0 < c.K) ? xt[h] : zerou4();
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = mfma_16x16x32(x, op[e], acc[e]);
   }
 }
 
-// GEMM2 partial of one 128-column n-tile for this wave's 32 rank rows.
+// GEMM2 partials of this workgroup's two 128-column n-tiles for this wave's
+// 32 rank rows (the second is computed even when the workgroup has one
+// n-tile and is then never stored).
 template <int LD8>
-__device__ __forceinline__ void gemm2_wave(const ResCtx& c, int ntl, const u32x4_t& thi, const u32x4_t& tlo,
-                                           f32x4_t y[8]) {
-  const int64_t jrow0 = c.j0 + 32 * c.w + 8 * c.g;
-  const int64_t nb = c.nb0 + (int64_t)ntl * kResNT;
-  u32x4_t op[8];
-  lds_tile_ops<LD8>(c.sB + (size_t)(32 * c.w + 8 * c.g) * (c.CB * 16), c.CB * 16, 16 * ntl, c.np, nb + 8 * c.np,
-                    c.N, jrow0, c.jend, op);
+__device__ __forceinline__ void gemm2_wave(const ResCtx& c, const u32x4_t& thi, const u32x4_t& tlo, f32x4_t y0[8],
+                                           f32x4_t y1[8]) {
+  const char* rows = c.sB + (size_t)(32 * c.w + 8 * c.g) * (c.CB * 16);
+  TileRaw b[2];
+  tile_read<LD8>(rows, c.CB * 16, 0, c.np, b[0]);
+  tile_read<LD8>(rows, c.CB * 16, 16, c.np, b[1]);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    y[e] = mfma_16x16x32(thi, op[e], y[e]);
-    y[e] = mfma_16x16x32(tlo, op[e], y[e]);
+  for (int h = 0; h < 2; ++h) {
+    u32x4_t op[8];
+    tile_ops<LD8>(b[h], op);
+    f32x4_t* y = h == 0 ? y0 : y1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y[e] = mfma_16x16x32(thi, op[e], y[e]);
+      y[e] = mfma_16x16x32(tlo, op[e], y[e]);
+    }
   }
 }
 
@@ -198,6 +228,20 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   RES_TRACE(0);
   RES_TRACE_ENTRY_STORE();
 
+  // LDS rows of the B slab past the slice are never loaded.  GEMM2 multiplies
+  // them by T columns that are exactly zero, so they are cleared here: bits
+  // left by an earlier kernel could be NaN or Inf.  (The B loads below write
+  // only zeros there, so the order of the two does not matter.)
+  {
+    const int r0 = (int)(jend - j0);
+    const int nz = (kResJS - r0) * CB;
+    for (int i = tid; i < nz; i += kResThreads) lds_write16(sB + ((size_t)r0 * CB + i) * 16, zerou4());
+    // likewise the A rows of k-tiles past kt_cnt (GEMM1 always runs 8 tiles)
+    const int az = (kResMaxKt - kt_cnt) * kResKT * kResCA;
+    for (int i = tid; i < az; i += kResThreads)
+      lds_write16(sA + ((size_t)kt_cnt * kResKT * kResCA + i) * 16, zerou4());
+  }
+
   // ------------------------------------------ issue every load up front --
   if (w < 2) {
     // X: 16 rows x kResXK columns starting at kbase (rows >= M read as zero)
@@ -216,21 +260,26 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
       const int c = i * 64 + l;
       const int row = c / kResCA, cc = c - row * kResCA;
       const int64_t grow = kbase + row;
-      const int64_t chunk = ((grow * r + j0) >> 3) + cc;
-      const uint32_t off = (c < nachunks && grow < K) ? (uint32_t)(chunk * 16) : kOutOfRange;
+      const int64_t e0 = grow * r + j0;
+      // only the chunks that hold columns [j0, jend) of the row are fetched
+      const int need = (int)(((e0 & 7) + (jend - j0) + 7) >> 3);
+      const uint32_t off = (c < nachunks && grow < K && cc < need) ? (uint32_t)(((e0 >> 3) + cc) * 16) : kOutOfRange;
       lds_load16(rA, sA + i * 1024, off);
     }
   } else {
-    // B: the slice's rows (up to 128), each a run of CB chunks starting at
-    // the chunk that holds column nb0 of the row; rows past the slice read 0
-    const int nbchunks = 128 * CB;
+    // B: the slice's rows, each a run of CB chunks starting at the chunk
+    // that holds column nb0 of the row (LDS rows past the slice are never
+    // read: GEMM2 zeroes rank rows >= jend)
+    const int nbchunks = (int)(jend - j0) * CB;
     const int nbi = (nbchunks + 63) / 64;
     for (int i = w - 2; i < nbi; i += 2) {
       const int c = i * 64 + l;
       const int row = c / CB, cc = c - row * CB;
       const int64_t grow = j0 + row;
-      const int64_t chunk = ((grow * N + nb0) >> 3) + cc;
-      const uint32_t off = (c < nbchunks && grow < jend && nt_cnt > 0) ? (uint32_t)(chunk * 16) : kOutOfRange;
+      const int64_t e0 = grow * N + nb0;
+      const int need = (int)(((e0 & 7) + min64((int64_t)nt_cnt * kResNT, N - nb0) + 7) >> 3);
+      const uint32_t off =
+          (c < nbchunks && grow < jend && nt_cnt > 0 && cc < need) ? (uint32_t)(((e0 >> 3) + cc) * 16) : kOutOfRange;
       lds_load16(rB, sB + i * 1024, off);
     }
   }
@@ -283,7 +332,8 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int o = m * 128 + c + i;
-        v[i] = ((red[o] + red[16 * 128 + o]) + red[32 * 128 + o]) + red[48 * 128 + o];
+        const float t = ((red[o] + red[16 * 128 + o]) + red[32 * 128 + o]) + red[48 * 128 + o];
+        v[i] = c + i < jend - j0 ? t : 0.f;  // columns past the slice (or r) are exactly zero
       }
       const uint32_t off = grp_base + (uint32_t)s * slice_bytes + (uint32_t)(m * 128 + c) * 4u;
       if (P.xcd_local)
@@ -323,28 +373,35 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   }
   barrier_lds();
   RES_TRACE(4);
-  // thread -> float4 element of the slice; all S partials of it in flight,
-  // summed in order s = 0..S-1
-  for (int vi = tid; vi < 16 * 32; vi += kResThreads) {
-    const int m = vi >> 5, c = (vi & 31) * 4;
-    const bool ok = m < M && c < JS;
-    const uint32_t voff = ok ? (uint32_t)(m * 128 + c) * 4u : 0u;
-    f32x4_t sum = zero4();
-    for (int p0 = 0; p0 < P.S; p0 += 32) {
-      f32x4_t t[32];
+  // thread -> float4 element of the slice (M x JS valid floats); all S
+  // partials of it in flight, summed in order s = 0..S-1.  Ts is cleared
+  // first: rows >= M and columns >= JS are zero for GEMM2.
+  for (int idx = tid; idx < 16 * 136; idx += kResThreads) Ts[idx] = 0.f;
+  barrier_lds();
+  {
+    const int v4row = JS / 4;
+    for (int vi = tid; vi < M * v4row; vi += kResThreads) {
+      const int m = vi / v4row, c = (vi - m * v4row) * 4;
+      const uint32_t voff = (uint32_t)(m * 128 + c) * 4u;
+      f32x4_t sum = zero4();
+      for (int p0 = 0; p0 < P.S; p0 += 16) {
+        const int np0 = min(16, P.S - p0);
+        f32x4_t t[16];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const uint32_t off = grp_base + (uint32_t)min(p0 + u, P.S - 1) * slice_bytes + voff;
-        t[u] = P.xcd_local ? buf_load16_l2(rW, off) : buf_load16_coherent(rW, off);
+        for (int u = 0; u < 16; ++u) {
+          const uint32_t off = grp_base + (uint32_t)(p0 + min(u, np0 - 1)) * slice_bytes + voff;
+          if (u < np0) t[u] = P.xcd_local ? buf_load16_l2(rW, off) : buf_load16_coherent(rW, off);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (u < np0) sum += t[u];
       }
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        if (p0 + u < P.S) sum += t[u];
+      for (int i = 0; i < 4; ++i)
+        if (c + i < JS) Ts[m * 136 + c + i] = sum[i];
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Ts[m * 136 + c + i] = ok ? sum[i] : 0.f;
   }
-  for (int idx = tid; idx < 16 * 8; idx += kResThreads) Ts[(idx >> 3) * 136 + 128 + (idx & 7)] = 0.f;
+  RES_TRACE(9);
   wait_vmem_all();  // B (loaded by waves 2-3) is in LDS
   barrier_lds();
   RES_TRACE(5);
@@ -365,18 +422,21 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   // Y partial layout per (s, js): [nt][M][128] fp32 = ntps*M*32 float4
   const int vmax = ntps * M * 32;
   const uint32_t ypart_wg = P.off_ypart + (uint32_t)(s * P.Jw + js) * (uint32_t)vmax * 16u;
-  for (int ntl = 0; ntl < nt_cnt; ++ntl) {
-    f32x4_t y[8];
+  f32x4_t y0[8], y1[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = zero4();
-#define LR_G2(D) gemm2_wave<D>(ctx, ntl, thi, tlo, y)
-    LR_LD8_SWITCH(N, LR_G2)
+  for (int e = 0; e < 8; ++e) {
+    y0[e] = zero4();
+    y1[e] = zero4();
+  }
+#define LR_G2(D) gemm2_wave<D>(ctx, thi, tlo, y0, y1)
+  LR_LD8_SWITCH(N, LR_G2)
 #undef LR_G2
+  for (int ntl = 0; ntl < nt_cnt; ++ntl) {
     barrier_lds();  // previous tile's red reads (and the Ts reads) are done
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) red[(w * 16 + 4 * g + t) * 128 + 8 * np + e] = y[e][t];
+      for (int t = 0; t < 4; ++t) red[(w * 16 + 4 * g + t) * 128 + 8 * np + e] = ntl == 0 ? y0[e][t] : y1[e][t];
     barrier_lds();
     for (int vi = tid; vi < M * 32; vi += kResThreads) {
       const int m = vi >> 5, c = (vi & 31) * 4;
