@@ -108,7 +108,8 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   __shared__ uint32_t sh_epoch, sh_old;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, np = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int l = tid & 63, np = l & 15, g = l >> 4;
 
   int pi = 0;
 #pragma unroll

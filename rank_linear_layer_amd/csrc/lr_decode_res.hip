@@ -3,14 +3,17 @@
 // Same method as lr_decode.hip, for shapes whose per-workgroup slabs fit in
 // LDS (the plan checks this; every other shape takes lr_decode.hip).
 // Decode is bound by reading A and B from HBM once ("LowRankArena ...",
-// "Why theoretical FLOPs saved does not equal faster inference"), so every
-// byte a workgroup needs is requested in the first instructions of the
-// kernel, straight into LDS (buffer_load ... lds): no VGPRs are tied up by
-// loads in flight and each compute unit keeps its whole share outstanding.
+// "Why theoretical FLOPs saved does not equal faster inference").  Every
+// byte a workgroup needs goes straight into LDS (buffer_load ... lds): no
+// VGPRs are tied up by loads in flight.  A (with X) is requested first and
+// alone, so that GEMM1 and the T hand-off can start as early as possible;
+// B is requested once the T partial is published and streams in during the
+// hand-off.  Adjacent rank slices sit on one XCD, so the 128-byte lines that
+// straddle two slices of a misaligned A row are fetched once into that
+// XCD's L2.
 //
 // Wave roles keep the in-order vector-memory counter from coupling phases:
-// waves 0-1 load X and A, waves 2-3 load B.  GEMM1 starts once A is in LDS
-// while B is still arriving.
+// waves 0-1 load X and A and publish the T partial, waves 2-3 load B.
 //
 // Work split: the rank is cut into Jw slices of JS <= 128 columns (Jw a
 // multiple of 8), K and N into S slices.  Workgroup (js, s):
@@ -48,6 +51,38 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ void lds_load16(rsrc_t r, void* lds_base_wave, uint32_t gbyte_off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base_wave, 16, (int)gbyte_off, 0, 0, 0);
+}
+
+// Direct loads of `rows` runs of `cpr` 16-byte chunks into LDS slots
+// [0, rows * cpr) of `lds` (run q at slot q * cpr).  Run q starts at the
+// aligned chunk that holds element e_first + q * ld; of each run only the
+// chunks that hold its `ncols` elements are fetched, and runs q >= valid
+// rows read as zero.  This wave issues load instructions first, first +
+// step, ... (64 slots each).  The slot -> (run, chunk) map advances by a
+// constant per instruction, so no division is done per load; element
+// offsets fit 32 bits (matrices are below 2 GiB).
+__device__ __forceinline__ void dma_runs(rsrc_t r, char* lds, uint32_t e_first, uint32_t ld, int rows, int valid,
+                                         int cpr, int ncols, int first, int step, int lane) {
+  const int ninst = (rows * cpr + 63) / 64;
+  const int s0 = 64 * first + lane;
+  int row = s0 / cpr, cc = s0 - row * cpr;
+  const int adv = 64 * step;
+  const int drow = adv / cpr, dcc = adv - drow * cpr;
+  uint32_t e0 = e_first + (uint32_t)row * ld;
+  const uint32_t dld = (uint32_t)drow * ld;
+  for (int i = first; i < ninst; i += step) {
+    const int need = (int)(((e0 & 7u) + (uint32_t)max(ncols, 0) + 7u) >> 3);
+    const bool ok = row < valid && cc < need;
+    lds_load16(r, lds + i * 1024, ok ? ((e0 >> 3) + (uint32_t)cc) * 16u : kOutOfRange);
+    row += drow;
+    cc += dcc;
+    e0 += dld;
+    if (cc >= cpr) {
+      cc -= cpr;
+      row += 1;
+      e0 += ld;
+    }
+  }
 }
 
 __device__ __forceinline__ u32x4_t lds_read16(const char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
@@ -178,7 +213,8 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, np = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int l = tid & 63, np = l & 15, g = l >> 4;
 
   int pi = 0;
 #pragma unroll
@@ -191,7 +227,7 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   int js, s;
   if (P.xcd_local) {
     const int x = local & 7, slot = local >> 3;
-    js = x + 8 * (slot / P.S);
+    js = x * (P.Jw >> 3) + slot / P.S;  // each XCD holds adjacent rank slices (shared A lines)
     s = slot - (slot / P.S) * P.S;
   } else {
     js = local / P.S;
@@ -242,51 +278,18 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
       lds_write16(sA + ((size_t)kt_cnt * kResKT * kResCA + i) * 16, zerou4());
   }
 
-  // ------------------------------------------ issue every load up front --
+  // ------------------------------------------- X and A straight to LDS --
   if (w < 2) {
     // X: 16 rows x kResXK columns starting at kbase (rows >= M read as zero)
-    constexpr int nxi = 16 * (kResXK / 8) / 64;
-    for (int i = w; i < nxi; i += 2) {
-      const int c = i * 64 + l;
-      const int m = c / (kResXK / 8), cc = c - m * (kResXK / 8);
-      const uint32_t off = (uint32_t)(((int64_t)m * K + kbase) * 2 + (int64_t)cc * 16);
-      lds_load16(rX, sX + i * 1024, off);
-    }
+    dma_runs(rX, sX, (uint32_t)kbase, (uint32_t)K, 16, M, kResXK / 8, kResXK, w, 2, l);
     // A: kt_cnt*32 rows, each a run of kResCA chunks starting at the chunk
-    // that holds column j0 of the row
-    const int nachunks = kt_cnt * kResKT * kResCA;
-    const int nai = (nachunks + 63) / 64;
-    for (int i = w; i < nai; i += 2) {
-      const int c = i * 64 + l;
-      const int row = c / kResCA, cc = c - row * kResCA;
-      const int64_t grow = kbase + row;
-      const int64_t e0 = grow * r + j0;
-      // only the chunks that hold columns [j0, jend) of the row are fetched
-      const int need = (int)(((e0 & 7) + (jend - j0) + 7) >> 3);
-      const uint32_t off = (c < nachunks && grow < K && cc < need) ? (uint32_t)(((e0 >> 3) + cc) * 16) : kOutOfRange;
-      lds_load16(rA, sA + i * 1024, off);
-    }
-  } else {
-    // B: the slice's rows, each a run of CB chunks starting at the chunk
-    // that holds column nb0 of the row (LDS rows past the slice are never
-    // read: GEMM2 zeroes rank rows >= jend)
-    const int nbchunks = (int)(jend - j0) * CB;
-    const int nbi = (nbchunks + 63) / 64;
-    for (int i = w - 2; i < nbi; i += 2) {
-      const int c = i * 64 + l;
-      const int row = c / CB, cc = c - row * CB;
-      const int64_t grow = j0 + row;
-      const int64_t e0 = grow * N + nb0;
-      const int need = (int)(((e0 & 7) + min64((int64_t)nt_cnt * kResNT, N - nb0) + 7) >> 3);
-      const uint32_t off =
-          (c < nbchunks && grow < jend && nt_cnt > 0 && cc < need) ? (uint32_t)(((e0 >> 3) + cc) * 16) : kOutOfRange;
-      lds_load16(rB, sB + i * 1024, off);
-    }
+    // that holds column j0 of the row; rows >= K read as zero
+    dma_runs(rA, sA, (uint32_t)(kbase * r + j0), (uint32_t)r, kt_cnt * kResKT, (int)min64(kt_cnt * kResKT, K - kbase),
+             kResCA, (int)(jend - j0), w, 2, l);
   }
-  if (w < 2) wait_vmem_all();
-  barrier_lds();  // X and A are in LDS (B may still be arriving)
+  wait_vmem_all();
+  barrier_lds();  // X and A are in LDS
   RES_TRACE(1);
-
   ResCtx ctx;
   ctx.sA = sA;
   ctx.sB = sB;
@@ -352,6 +355,17 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
       buf_store_u32_coherent(rW, tflag_grp + (uint32_t)s * 4u, epoch);
   }
   RES_TRACE(3);
+  // B is requested only now: A had the memory system to itself, and the T
+  // partial stores above did not queue behind B's requests.  B is needed
+  // only at GEMM2 and streams in during the T hand-off.
+  if (w >= 2) {
+    // B: the slice's rows, each a run of CB chunks starting at the chunk
+    // that holds column nb0 of the row (LDS rows past the slice are cleared
+    // above)
+    dma_runs(rB, sB, (uint32_t)(j0 * N + nb0), (uint32_t)N, (int)(jend - j0), (int)(jend - j0), CB,
+             (int)min64((int64_t)nt_cnt * kResNT, N - nb0), w - 2, 2, l);
+  }
+
 
   // ------------------------------------ T hand-off: all S partials -------
   if (w == 0) {
@@ -390,7 +404,7 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const uint32_t off = grp_base + (uint32_t)(p0 + min(u, np0 - 1)) * slice_bytes + voff;
-          if (u < np0) t[u] = P.xcd_local ? buf_load16_l2(rW, off) : buf_load16_coherent(rW, off);
+          if (u < np0) t[u] = P.xcd_local ? buf_load16_fresh(rW, off) : buf_load16_coherent(rW, off);
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u)

@@ -154,6 +154,13 @@ constexpr int kSkipL1 = 2;
 __device__ __forceinline__ f32x4_t buf_load16_l2(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kSkipL1));
 }
+// Data written by other compute units of this XCD during this kernel, read
+// once: a plain load misses the (kernel-start invalidated) L1 and is served
+// by the shared L2.  Only for addresses this compute unit has not read
+// before in the kernel.
+__device__ __forceinline__ f32x4_t buf_load16_fresh(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
 __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t byte_off, const f32x4_t& v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)byte_off, 0, 0);
 }

@@ -77,11 +77,13 @@ bool xcd_round_robin(int grid);
 int decode_blocks_per_cu();
 
 // --------------------------------------------------------------- prefill ---
-constexpr int kPreThreads = 256;  // 4 waves, each 64 rows x all columns of the tile
+constexpr int kPreThreads = 512;  // 8 waves (two per SIMD)
 constexpr int kPreBM = 256;       // rows per workgroup tile
-constexpr int kPreBN = 240;       // columns per workgroup tile (15 MFMA column tiles)
-constexpr int kPreKT = 64;        // k per LDS stage
-constexpr int kPreLdsBytes = 2 * (15 + 16) * 2080;  // two stages of Q (240 cols) + P (256 rows) tiles
+constexpr int kPreKT = 32;        // k per LDS stage (one MFMA k-step)
+// columns per workgroup tile = 32 * nb, nb in [kPreMinNB, kPreMaxNB]
+constexpr int kPreMinNB = 6;
+constexpr int kPreMaxNB = 8;
+constexpr int kPreLdsBytes = 256 * 33 * 16;  // max(3 raw slots + 2 gathered tiles, epilogue staging)
 
 // C[rows x out_cols] = P[rows x kd] . Q[kd x ldq] for one or two column
 // blocks in one launch.  P is k-contiguous (X or T); Q is row-major with
@@ -104,6 +106,8 @@ struct PreArgs {
   int64_t rows;     // M
   int nout;         // 1 or 2 column blocks
   int row_tiles;
+  int nb;           // MFMA column blocks per wave: the tile is 32 * nb columns wide
+  int pad_;
   PreOut o[2];
 };
 hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream);

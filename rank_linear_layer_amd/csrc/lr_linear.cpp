@@ -96,7 +96,8 @@ lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
   if (ep == 0u) ep = h->epoch.fetch_add(1u) + 1u;  // 0 is the value of a fresh flag
   p.epoch = ep;
   p.js_w = h->dp.js_w;
-  p.xcd_local = h->xcd_local ? 1 : 0;
+  // the XCD-local exchange needs workgroup (local id) on XCD local % 8
+  p.xcd_local = (h->xcd_local && wg_begin % 8 == 0) ? 1 : 0;
   p.r = (int)h->r;
   p.N = (int)h->N;
   p.Jw = h->dp.Jw;
@@ -155,12 +156,19 @@ lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, con
 
 lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                       hipStream_t stream) {
+  const int cus = num_cus(hs[0]->device);
   // phase 1: T_i = X . A_i (both projections in one launch)
   lrk::PreArgs a1;
   memset(&a1, 0, sizeof a1);
   a1.rows = M;
   a1.nout = n;
   a1.row_tiles = (int)lrv::ceil_div(M, lrk::kPreBM);
+  int64_t cols1[2] = {0, 0}, cols2[2] = {0, 0};
+  for (int i = 0; i < n; ++i) {
+    cols1[i] = hs[i]->r_pad;
+    cols2[i] = hs[i]->N;
+  }
+  a1.nb = lrv::prefill_pick_nb(M, cols1, n, cus);
   for (int i = 0; i < n; ++i) {
     const lr_linear* h = hs[i];
     lrk::PreOut& o = a1.o[i];
@@ -173,7 +181,7 @@ lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, co
     o.C = h->Tbuf;
     o.ldc = h->r_pad;
     o.out_cols = h->r_pad;
-    o.col_tiles = (int)lrv::ceil_div(h->r_pad, lrk::kPreBN);
+    o.col_tiles = (int)lrv::ceil_div(h->r_pad, 32 * a1.nb);
   }
   hipError_t e = lrk::launch_prefill_gemm(a1, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill phase-1 launch");
@@ -183,6 +191,7 @@ lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, co
   a2.rows = M;
   a2.nout = n;
   a2.row_tiles = a1.row_tiles;
+  a2.nb = lrv::prefill_pick_nb(M, cols2, n, cus);
   for (int i = 0; i < n; ++i) {
     const lr_linear* h = hs[i];
     lrk::PreOut& o = a2.o[i];
@@ -195,7 +204,7 @@ lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, co
     o.C = Ys[i];
     o.ldc = h->N;
     o.out_cols = h->N;
-    o.col_tiles = (int)lrv::ceil_div(h->N, lrk::kPreBN);
+    o.col_tiles = (int)lrv::ceil_div(h->N, 32 * a2.nb);
   }
   e = lrk::launch_prefill_gemm(a2, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill phase-2 launch");

@@ -9,30 +9,33 @@
 //   phase 2  Y[M x N]     = T . B      (reduction over r_pad; B rows >= r
 //                                       read as 0, never fetched)
 // The rank is padded to the 32-wide MFMA K-step on chip only; A and B keep
-// their public shapes.  Any r mod 8 and N mod 8 is handled by the same
-// kernel: misaligned weight rows are realigned in registers (see
-// lr_device.h), misaligned output rows are written through an LDS staging
-// tile that mirrors each row's alignment.
+// their public shapes.  Any r mod 8 and N mod 8 runs through the same code
+// (the page on dimensional misalignment, "Why Smaller Is Slower? ...",
+// section 3.3, traces part of the slowdown of odd ranks to misaligned
+// rows; here a misaligned row costs nothing extra on the compute path).
 //
-// Workgroup tile: 256 rows x 240 columns, 64-deep k-steps, 4 waves, one
-// workgroup per compute unit.  Wave w owns rows [64w, 64w + 64) and all 240
-// columns: 4 x 15 MFMA 16x16x32 tiles, 240 fp32 accumulators per lane.
+// Workgroup: 8 waves (two per SIMD), tile 256 rows x 32*NB columns, 32-deep
+// k-steps.  Wave (wm, wn) = (w % 4, w / 4) owns rows [64 wm, +64) and NB
+// MFMA column blocks of 16: 4 x NB tiles of v_mfma_f32_16x16x32_bf16.  The
+// two waves of a SIMD interleave: while one waits on LDS or a barrier the
+// other keeps the matrix core busy.
 //
-// Per k-step the workgroup stages two operand tiles in LDS (double
-// buffered, 2 x 63 KB):
-//   P tile  256 rows x 64 k   (X or T; k-contiguous, copied as is)
-//   Q tile  240 cols x 64 k   (A or B transposed: each lane loads 8 rows x
-//                              8 columns, realigns and transposes them in
-//                              registers, and writes 8 k-contiguous column
-//                              segments)
-// Both tiles use one layout, built from blocks of 16 rows (or columns) x 8
-// chunks of 16 bytes: chunk c of line L of block b sits at
-//   b * 2080 + 256 c + 16 sigma(L),   sigma(L) = ((L & 7) << 1) | (L >> 3).
-// An MFMA operand read (16 consecutive lines, one chunk) and a transposing
-// write (lines 8j + e for 16 lanes j) both touch 16 distinct 16-byte bank
-// groups, and the operand address is one per-lane base plus a compile-time
-// offset.  With an aligned P the P tile is filled by direct-to-LDS buffer
-// loads (no registers), in the same layout.
+// Every global read is a direct-to-LDS buffer load (no registers), issued
+// three k-steps ahead into a ring of three raw slots:
+//   P slot  256 rows x 32 k, already in MFMA operand order
+//           (16-row block b, chunk c, row L at b*1024 + c*256 + L*16: one
+//           operand read is 256 contiguous bytes per 16 lanes)
+//   Q slot  32 rows x 33 raw 16-byte chunks of A or B, each row starting at
+//           the aligned chunk that holds the tile's first column
+// The MFMA B operand wants 8 consecutive k of one output column per lane,
+// while A and B store the output index contiguously.  One k-step ahead of
+// the MFMAs the waves gather the Q slot into Qt (same layout as the P slot,
+// 16 output columns per block) with 2-byte LDS reads: element (k, n) sits at
+// byte 2 (d_k + n) of raw row k, d_k = the row's misalignment, so an odd
+// leading dimension needs no shifting in registers at all.
+//
+// An aligned P (X with K mod 8 = 0, and always T) is loaded straight into its
+// slot; a misaligned X goes through registers one step ahead (2-byte loads).
 //
 // Grid: tiles are dealt so that each XCD (workgroup id mod 8) gets one
 // contiguous run of the tile order, and the order walks groups of four row
@@ -45,26 +48,31 @@ namespace lrk {
 
 namespace {
 
-constexpr int kBM = kPreBM;          // 256
-constexpr int kBN = kPreBN;          // 240
-constexpr int kBK = kPreKT;          // 64
-constexpr int kBlk = 2080;           // one 16-line block: 16 x 8 chunks + 32 bytes of skew
-constexpr int kStageQ = 15 * kBlk;   // Q tile bytes (240 columns)
-constexpr int kStageP = 16 * kBlk;   // P tile bytes (256 rows)
-constexpr int kStage = kStageQ + kStageP;
-constexpr int kEpiRS = 496;          // epilogue staging row pitch (31 chunks)
-constexpr int kGroupRows = 4;        // row tiles per group in the tile order
+constexpr int kThreads = kPreThreads;  // 512
+constexpr int kBM = kPreBM;            // 256
+constexpr int kBK = kPreKT;            // 32
+constexpr int kSlotP = 16 * 1024;      // P slot: 16 blocks of 16 rows x 4 chunks
+constexpr int kQChunks = 33;           // raw chunks per Q row (256 columns + realign)
+constexpr int kQRowBytes = kQChunks * 16;
+constexpr int kQInst = 17;             // direct loads per Q slot (1088 >= 32 * 33 chunks)
+constexpr int kSlotQ = kQInst * 1024;
+constexpr int kSlot = kSlotP + kSlotQ;
+constexpr int kQt = 16 * 1024;         // gathered Q: up to 16 column blocks
+constexpr int kQtBase = 3 * kSlot;
+constexpr int kEpiPitch = kQRowBytes;  // epilogue staging row pitch (33 chunks)
+constexpr int kGroupRows = 4;          // row tiles per group in the tile order
 constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
-static_assert(kPreLdsBytes == 2 * kStage, "LDS size");
-static_assert(kBM * kEpiRS <= 2 * kStage, "epilogue staging must fit the stage buffers");
+static_assert(kQtBase + 2 * kQt <= kPreLdsBytes, "LDS layout");
+static_assert(kBM * kEpiPitch <= kPreLdsBytes, "epilogue staging");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ int sigma(int L) { return ((L & 7) << 1) | (L >> 3); }
-__device__ __forceinline__ int sigma_inv(int s) { return ((s & 1) << 3) | (s >> 1); }
-
 __device__ __forceinline__ u32x4_t lds_read16(const char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void lds_write16(char* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+__device__ __forceinline__ uint32_t lds_read_u16(const char* p) { return *reinterpret_cast<const uint16_t*>(p); }
+__device__ __forceinline__ void dma16(rsrc_t r, char* lds_wave_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 16, (int)off, 0, 0, 0);
+}
 
 struct Tile {
   int bi;      // output block (0 or 1)
@@ -75,7 +83,7 @@ struct Tile {
 // Workgroup id -> tile.  XCD x (= id mod 8) receives the contiguous run
 // [x*q + min(x, rem), ...) of the tile order; the order is row-tile groups of
 // kGroupRows, walked column tile by column tile across both outputs.
-__device__ __forceinline__ Tile map_tile(const PreArgs& a) {
+__device__ __forceinline__ Tile map_tile(const PreArgs& a, int bn) {
   const int ct_total = a.o[0].col_tiles + (a.nout > 1 ? a.o[1].col_tiles : 0);
   const int total = a.row_tiles * ct_total;
   const int q = total >> 3, rem = total & 7;
@@ -96,195 +104,214 @@ __device__ __forceinline__ Tile map_tile(const PreArgs& a) {
     ct -= a.o[0].col_tiles;
   }
   T.mb = (int64_t)rt * kBM;
-  T.nb = (int64_t)ct * kBN;
+  T.nb = (int64_t)ct * bn;
   return T;
 }
 
-// ------------------------------------------------------------- Q tile ---
-// Thread (dr = tid / 16, j = tid % 16): k-group g = dr / 2 (rows kb + 8g ..
-// + 7), column half hc = dr % 2 (columns nb + 120 hc + 8j .. + 7; lane 15 of
-// the DPP row only lends its chunk to lane 14).
-struct QRaw {
-  u32x4_t c[8];
+struct Ctx {
+  rsrc_t rP, rQ;
+  int64_t ldp, kd, ldq, qrows, mb, nb;
+  int qcols;  // columns of Q inside this tile (<= BN; past them the rows hold other data)
+  int w, l;
 };
 
-__device__ __forceinline__ void q_load(QRaw& t, rsrc_t rQ, int64_t ldq, int64_t kb, int64_t col, int g, int j) {
+// -------------------------------------------------------------- loads ---
+// P slot, aligned P: wave w loads 16-row blocks w and w + 8.  Lane l of a
+// block fills chunk l / 16 of row l % 16; chunks at or past kd read zero.
+__device__ __forceinline__ void p_dma(const Ctx& c, char* slotP, int64_t kb) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) t.c[q] = load_row_raw(rQ, kb + 8 * g + q, ldq, col, j);
-}
-
-// Realign (row q of the group is misaligned by (q * LD8) mod 8: the group's
-// first row index is a multiple of 8 and the column a multiple of 8),
-// transpose and write the 8 column segments of lane j.
-template <int LD8>
-__device__ __forceinline__ void q_store(const QRaw& t, char* stageQ, int64_t ldq, int64_t col, int g, int j,
-                                        int J) {
-  u32x4_t seg[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) seg[q] = realign_segment(t.c[q], (q * LD8) & 7, col + 8 * j, ldq, true);
-  u32x4_t op[8];
-  transpose8x8(seg, op);
-  if (j < 15) {
-    char* base = stageQ + (J >> 1) * kBlk + 256 * g + 16 * (J & 1);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lds_write16(base + 32 * e, op[e]);
+  for (int h = 0; h < 2; ++h) {
+    const int b = c.w + 8 * h;
+    const int64_t row = c.mb + 16 * b + (c.l & 15);
+    const int64_t k0 = kb + 8 * (c.l >> 4);
+    const uint32_t off = k0 < c.kd ? (uint32_t)((row * c.ldp + k0) * 2) : kOutOfRange;
+    dma16(c.rP, slotP + b * 1024, off);
   }
 }
 
-// ------------------------------------------------------------- P tile ---
-// Unit u = 8w + i (i = 0..7) of wave w covers block u / 2, chunks 4 (u % 2)
-// .. + 3; lane l fills slot l of the unit: chunk 4 (u % 2) + l / 16 of line
-// sigma_inv(l % 16).
-__device__ __forceinline__ void p_unit(int u, int l, int& line, int& chunk) {
-  line = 16 * (u >> 1) + sigma_inv(l & 15);
-  chunk = 4 * (u & 1) + (l >> 4);
-}
-
-// Aligned P: direct-to-LDS loads; chunks at or past kd read as zero.
-__device__ __forceinline__ void p_load_direct(rsrc_t rP, int64_t ldp, int64_t kd, int64_t mb, int64_t kb,
-                                              char* stageP, int w, int l) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int u = 8 * w + i;
-    int line, chunk;
-    p_unit(u, l, line, chunk);
-    const int64_t k0 = kb + 8 * chunk;
-    const uint32_t off = k0 < kd ? (uint32_t)(((mb + line) * ldp + k0) * 2) : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(stageP + (u >> 1) * kBlk + 1024 * (u & 1)), 16,
-                                             (int)off, 0, 0, 0);
-  }
-}
-
-// Misaligned P (ldp mod 8 != 0): 2-byte loads into registers.
-struct PRaw {
-  u32x4_t c[8];
+// P slot, misaligned P: the same two chunks per lane through registers.
+struct PRegs {
+  u32x4_t v[2];
 };
-__device__ __forceinline__ void p_load_regs(PRaw& t, rsrc_t rP, int64_t ldp, int64_t kd, int64_t mb, int64_t kb,
-                                            int w, int l) {
+__device__ __forceinline__ void p_regs_load(const Ctx& c, PRegs& p, int64_t kb) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int line, chunk;
-    p_unit(8 * w + i, l, line, chunk);
-    t.c[i] = load_kvec(rP, mb + line, ldp, kb + 8 * chunk, kd, false);
+  for (int h = 0; h < 2; ++h) {
+    const int b = c.w + 8 * h;
+    p.v[h] = load_kvec(c.rP, c.mb + 16 * b + (c.l & 15), c.ldp, kb + 8 * (c.l >> 4), c.kd, false);
   }
 }
-__device__ __forceinline__ void p_store_regs(const PRaw& t, char* stageP, int w, int l) {
+__device__ __forceinline__ void p_regs_store(const Ctx& c, const PRegs& p, char* slotP) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int u = 8 * w + i;
-    lds_write16(stageP + (u >> 1) * kBlk + 1024 * (u & 1) + 16 * l, t.c[i]);
+  for (int h = 0; h < 2; ++h) lds_write16(slotP + (c.w + 8 * h) * 1024 + c.l * 16, p.v[h]);
+}
+
+// Q slot: 32 raw rows x 33 chunks = 1056 chunks in 17 loads of 64 chunks;
+// wave w issues loads w and w + 8, wave 0 also load 16.  Only the chunks
+// that hold the tile's qcols columns of a row are fetched.
+__device__ __forceinline__ void q_dma_one(const Ctx& c, char* slotQ, int64_t kb, int i) {
+  const int s = 64 * i + c.l;
+  const int row = s / kQChunks, ch = s - row * kQChunks;
+  const int64_t krow = kb + row;
+  const int64_t e0 = krow * c.ldq + c.nb;
+  const int need = (int)(((e0 & 7) + c.qcols + 7) >> 3);
+  const bool ok = row < kBK && krow < c.qrows && ch < need;
+  dma16(c.rQ, slotQ + i * 1024, ok ? (uint32_t)(((e0 >> 3) + ch) * 16) : kOutOfRange);
+}
+__device__ __forceinline__ void q_dma(const Ctx& c, char* slotQ, int64_t kb) {
+  q_dma_one(c, slotQ, kb, c.w);
+  q_dma_one(c, slotQ, kb, c.w + 8);
+  if (c.w == 0) q_dma_one(c, slotQ, kb, 16);
+}
+
+// --------------------------------------------------------------- gather ---
+// Qt block cb, chunk g, lane L holds the 8 k of k-group g for output column
+// 16 cb + L.  Item = (g, n) for n < BN; consecutive lanes take consecutive
+// columns, so each 2-byte read instruction touches one contiguous run of a
+// raw row.  Columns at or past qcols are written as zero.
+template <int NB>
+__device__ __forceinline__ void gather(const Ctx& c, const char* slotQ, char* qt, int64_t kb) {
+  constexpr int BN = 32 * NB;
+  constexpr int items = 4 * BN;
+  // misalignment of raw row 8g + q: ((kb + 8g + q) * ldq + nb) mod 8 = (q * ldq) mod 8
+  int dq[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dq[q] = (int)((q * c.ldq) & 7);
+  (void)kb;
+  const int tid = 64 * c.w + c.l;
+#pragma unroll
+  for (int it = 0; it < (items + kThreads - 1) / kThreads; ++it) {
+    const int item = tid + kThreads * it;
+    if ((items % kThreads) != 0 && item >= items) break;
+    const int g = item / BN, n = item - g * BN;
+    const char* rows = slotQ + (8 * g) * kQRowBytes + 2 * n;
+    uint32_t e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e[q] = lds_read_u16(rows + q * kQRowBytes + 2 * dq[q]);
+    u32x4_t v;
+    v[0] = e[0] | (e[1] << 16);
+    v[1] = e[2] | (e[3] << 16);
+    v[2] = e[4] | (e[5] << 16);
+    v[3] = e[6] | (e[7] << 16);
+    if (n >= c.qcols) v = zerou4();
+    lds_write16(qt + (n >> 4) * 1024 + g * 256 + (n & 15) * 16, v);
   }
 }
 
 // -------------------------------------------------------------- compute ---
-// One 64-deep k-step from a stage: 2 MFMA k-steps of 4 x 15 tiles.
-__device__ __forceinline__ void compute_stage(const char* stage, int lane_off, int w, f32x4_t (&acc)[4][15]) {
-  const char* pq = stage + lane_off;
-  const char* pp = stage + kStageQ + 4 * w * kBlk + lane_off;
+template <int NB>
+__device__ __forceinline__ void compute(const char* slotP, const char* qt, int wm, int wn, int lane_off,
+                                        f32x4_t (&acc)[4][NB]) {
+  u32x4_t a[4], b[NB];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    u32x4_t a[4], b[15];
+  for (int i = 0; i < 4; ++i) a[i] = lds_read16(slotP + (4 * wm + i) * 1024 + lane_off);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = lds_read16(pp + i * kBlk + 1024 * kk);
-#pragma unroll
-    for (int cb = 0; cb < 15; ++cb) b[cb] = lds_read16(pq + cb * kBlk + 1024 * kk);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int cb = 0; cb < 15; ++cb) acc[i][cb] = mfma_16x16x32(a[i], b[cb], acc[i][cb]);
-  }
-}
-
-template <int LD8, bool PAL>
-__device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, char* smem) {
-  const PreOut& O = a.o[T.bi];
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63;
-  const int dr = tid >> 4, j = tid & 15;
-  const int g = dr >> 1, hc = dr & 1;
-  const int J = 15 * hc + j;
-  const int64_t qcol = T.nb + 120 * hc;
-
-  const rsrc_t rQ = make_rsrc(O.Q, O.qrows * O.ldq * 2);
-  const rsrc_t rP = make_rsrc(O.P, a.rows * O.ldp * 2);
-  const int lane_off = 256 * (l >> 4) + 16 * sigma(l & 15);
-
-  f32x4_t acc[4][15];
+  for (int j = 0; j < NB; ++j) b[j] = lds_read16(qt + (NB * wn + j) * 1024 + lane_off);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int cb = 0; cb < 15; ++cb) acc[i][cb] = zero4();
+    for (int j = 0; j < NB; ++j) acc[i][j] = mfma_16x16x32(a[i], b[j], acc[i][j]);
+}
+
+template <int NB, bool PAL>
+__device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, char* smem) {
+  constexpr int BN = 32 * NB;
+  const PreOut& O = a.o[T.bi];
+  Ctx c;
+  c.rP = make_rsrc(O.P, a.rows * O.ldp * 2);
+  c.rQ = make_rsrc(O.Q, O.qrows * O.ldq * 2);
+  c.ldp = O.ldp;
+  c.kd = O.kd;
+  c.ldq = O.ldq;
+  c.qrows = O.qrows;
+  c.mb = T.mb;
+  c.nb = T.nb;
+  c.qcols = (int)min64((int64_t)BN, O.ldq - T.nb);
+  c.w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform: scalar branches
+  c.l = threadIdx.x & 63;
+  const int wm = c.w & 3, wn = c.w >> 2;
+  const int lane_off = (c.l >> 4) * 256 + (c.l & 15) * 16;
+
+  f32x4_t acc[4][NB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
 
   const int nks = (int)((O.kd + kBK - 1) / kBK);
-  QRaw qr;
-  PRaw pr;
+  auto slot = [&](int s) { return smem + (s % 3) * kSlot; };
+  auto qtb = [&](int s) { return smem + kQtBase + (s & 1) * kQt; };
 
-  // prologue: stage 0
-  if (PAL)
-    p_load_direct(rP, O.ldp, O.kd, T.mb, 0, smem + kStageQ, w, l);
-  else
-    p_load_regs(pr, rP, O.ldp, O.kd, T.mb, 0, w, l);
-  q_load(qr, rQ, O.ldq, 0, qcol, g, j);
+  // prologue: stages 0 and 1 in flight, stage 0 gathered, stage 2 in flight
+  PRegs pr;
+  if (nks > 0) {
+    if (PAL) p_dma(c, slot(0), 0); else p_regs_load(c, pr, 0);
+    q_dma(c, slot(0) + kSlotP, 0);
+  }
+  if (nks > 1) {
+    if (PAL) p_dma(c, slot(1), kBK);
+    q_dma(c, slot(1) + kSlotP, kBK);
+  }
   wait_vmem_all();
-  q_store<LD8>(qr, smem, O.ldq, qcol, g, j, J);
-  if (!PAL) p_store_regs(pr, smem + kStageQ, w, l);
+  if (!PAL && nks > 0) p_regs_store(c, pr, slot(0));
+  barrier_lds();
+  if (nks > 0) gather<NB>(c, slot(0) + kSlotP, qtb(0), 0);
+  if (!PAL && nks > 1) p_regs_load(c, pr, kBK);
+  if (nks > 2) {
+    if (PAL) p_dma(c, slot(2), 2 * kBK);
+    q_dma(c, slot(2) + kSlotP, 2 * kBK);
+  }
+  if (!PAL && nks > 1) {
+    wait_vmem_all();
+    p_regs_store(c, pr, slot(1));
+  }
   barrier_lds();
 
-  for (int ks = 0; ks < nks; ++ks) {
-    char* cur = smem + (ks & 1) * kStage;
-    char* nxt = smem + ((ks + 1) & 1) * kStage;
-    const bool more = ks + 1 < nks;  // uniform
-    const int64_t kb = (int64_t)(ks + 1) * kBK;
-    if (more) {
-      if (PAL)
-        p_load_direct(rP, O.ldp, O.kd, T.mb, kb, nxt + kStageQ, w, l);
-      else
-        p_load_regs(pr, rP, O.ldp, O.kd, T.mb, kb, w, l);
-      q_load(qr, rQ, O.ldq, kb, qcol, g, j);
-    }
-    compute_stage(cur, lane_off, w, acc);
-    if (more) {
-      wait_vmem_all();
-      q_store<LD8>(qr, nxt, O.ldq, qcol, g, j, J);
-      if (!PAL) p_store_regs(pr, nxt + kStageQ, w, l);
-      barrier_lds();
+  for (int s = 0; s < nks; ++s) {
+    // misaligned P: stage s + 2 travels through registers during this step
+    if (!PAL && s + 2 < nks) p_regs_load(c, pr, (int64_t)(s + 2) * kBK);
+    compute<NB>(slot(s), qtb(s), wm, wn, lane_off, acc);
+    if (s + 1 < nks) gather<NB>(c, slot(s + 1) + kSlotP, qtb(s + 1), (int64_t)(s + 1) * kBK);
+    wait_vmem_all();  // stage s + 2 has landed (and the registers of a misaligned P)
+    if (!PAL && s + 2 < nks) p_regs_store(c, pr, slot(s + 2));
+    barrier_lds();
+    // slot s % 3 is free: every wave is past compute(s) and gathered s earlier
+    if (s + 3 < nks) {
+      if (PAL) p_dma(c, slot(s + 3), (int64_t)(s + 3) * kBK);
+      q_dma(c, slot(s + 3) + kSlotP, (int64_t)(s + 3) * kBK);
     }
   }
 
   // ------------------------------------------------------------ epilogue --
-  // Stage the wave's 64 x 240 bf16 block in LDS with every row shifted by
-  // its misalignment d = (row * ldc + nb) mod 8, so that LDS chunk k of a
-  // row is global 16-byte chunk k of that row's segment.  Lane (L, G) of
-  // tile (i, cb) holds rows 16i + 4G + t, column 16cb + L.
-  barrier_lds();  // every wave is done with the stage buffers
-  const int L = l & 15, G = l >> 4;
+  // Stage the 256 x BN bf16 tile in LDS with every row shifted by its
+  // misalignment d = (row * ldc + nb) mod 8, so that LDS chunk k of a row is
+  // global 16-byte chunk k of that row's segment.  Lane (L, G) of tile
+  // (i, j) holds rows 64 wm + 16 i + 4 G + t, column 16 (NB wn + j) + L.
+  const int L = c.l & 15, G = c.l >> 4;
   const int64_t ldc = O.ldc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int m = 64 * w + 16 * i + 4 * G + t;
+      const int m = 64 * wm + 16 * i + 4 * G + t;
       const int d = (int)(((T.mb + m) * ldc + T.nb) & 7);
-      uint16_t* row = reinterpret_cast<uint16_t*>(smem + m * kEpiRS) + d + L;
+      uint16_t* row = reinterpret_cast<uint16_t*>(smem + m * kEpiPitch) + d + 16 * NB * wn + L;
 #pragma unroll
-      for (int cb = 0; cb < 15; ++cb) row[16 * cb] = (uint16_t)f32_to_bf16_rne(acc[i][cb][t]);
+      for (int j = 0; j < NB; ++j) row[16 * j] = (uint16_t)f32_to_bf16_rne(acc[i][j][t]);
     }
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (rows are wave-private)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  barrier_lds();
 
   const rsrc_t rC = make_rsrc(O.C, a.rows * ldc * 2);
-  const int64_t ncols = min64((int64_t)kBN, O.out_cols - T.nb);
-  const int k = l & 31;
-  for (int it = 0; it < 32; ++it) {
-    const int m = 64 * w + 2 * it + (l >> 5);
+  const int ncols = (int)min64((int64_t)BN, O.out_cols - T.nb);
+  constexpr int nitems = kBM * kQChunks;
+  for (int item = threadIdx.x; item < nitems; item += kThreads) {
+    const int m = item / kQChunks, k = item - m * kQChunks;
     const int64_t R = T.mb + m;
-    if (R >= a.rows || k > 30) continue;
+    if (R >= a.rows) continue;
     const int d = (int)((R * ldc + T.nb) & 7);
     const int n0 = 8 * k - d;  // tile column of the chunk's first element
     if (n0 >= ncols) continue;
-    const u32x4_t v = lds_read16(smem + m * kEpiRS + 16 * k);
+    const u32x4_t v = lds_read16(smem + m * kEpiPitch + 16 * k);
     const int64_t e0 = R * ldc + T.nb + n0;  // multiple of 8
     if (n0 >= 0 && n0 + 8 <= ncols) {
       __builtin_amdgcn_raw_buffer_store_b128(v, rC, (int)(e0 * 2), 0, 0);
@@ -300,33 +327,23 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, char*
   }
 }
 
-template <bool PAL>
-__global__ __launch_bounds__(kPreThreads, 1) void lr_prefill_gemm_kernel(const PreArgs a) {
+template <int NB, bool PAL>
+__global__ __launch_bounds__(kThreads, 1) void lr_prefill_gemm_kernel(const PreArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const Tile T = map_tile(a);
-  const int64_t ld8 = a.o[T.bi].ldq & 7;
-  switch (ld8) {
-    case 0: gemm_tile<0, PAL>(a, T, smem); break;
-    case 1: gemm_tile<1, PAL>(a, T, smem); break;
-    case 2: gemm_tile<2, PAL>(a, T, smem); break;
-    case 3: gemm_tile<3, PAL>(a, T, smem); break;
-    case 4: gemm_tile<4, PAL>(a, T, smem); break;
-    case 5: gemm_tile<5, PAL>(a, T, smem); break;
-    case 6: gemm_tile<6, PAL>(a, T, smem); break;
-    default: gemm_tile<7, PAL>(a, T, smem); break;
-  }
+  const Tile T = map_tile(a, 32 * NB);
+  gemm_tile<NB, PAL>(a, T, smem);
 }
 
-template <bool PAL>
+template <int NB, bool PAL>
 hipError_t launch_one(const PreArgs& args, int grid, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lr_prefill_gemm_kernel<PAL>,
+    hipError_t e = hipFuncSetAttribute((const void*)lr_prefill_gemm_kernel<NB, PAL>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kPreLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(lr_prefill_gemm_kernel<PAL>, dim3(grid), dim3(kPreThreads), kPreLdsBytes, stream, args);
+  hipLaunchKernelGGL((lr_prefill_gemm_kernel<NB, PAL>), dim3(grid), dim3(kThreads), kPreLdsBytes, stream, args);
   return hipGetLastError();
 }
 
@@ -338,7 +355,12 @@ hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   bool pal = true;
   for (int i = 0; i < args.nout; ++i) pal = pal && (args.o[i].ldp & 7) == 0;
-  return pal ? launch_one<true>(args, grid, stream) : launch_one<false>(args, grid, stream);
+  switch (args.nb) {
+    case 6: return pal ? launch_one<6, true>(args, grid, stream) : launch_one<6, false>(args, grid, stream);
+    case 7: return pal ? launch_one<7, true>(args, grid, stream) : launch_one<7, false>(args, grid, stream);
+    case 8: return pal ? launch_one<8, true>(args, grid, stream) : launch_one<8, false>(args, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 bool prefill_available() {

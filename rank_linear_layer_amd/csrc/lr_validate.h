@@ -180,4 +180,27 @@ inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget, boo
 
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+// Prefill tile width: 32 * nb columns, nb in [6, 8].  A workgroup's time
+// grows with nb (4 * nb MFMAs per k-step plus a fixed share for loads and
+// the barrier, about two column blocks' worth); the launch takes as many
+// rounds as it has workgroups per compute unit.  The cheapest nb wins (the
+// wider one on a tie).  out_cols holds the output columns of the nout
+// outputs of one launch.
+inline int prefill_pick_nb(int64_t rows, const int64_t* out_cols, int nout, int num_cus) {
+  const int64_t row_tiles = ceil_div(rows, 256);
+  int best = 8;
+  int64_t best_cost = -1;
+  for (int nb = 8; nb >= 6; --nb) {
+    int64_t tiles = 0;
+    for (int i = 0; i < nout; ++i) tiles += row_tiles * ceil_div(out_cols[i], 32 * nb);
+    const int64_t rounds = ceil_div(tiles, num_cus > 0 ? num_cus : 1);
+    const int64_t cost = rounds * (nb + 2);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = nb;
+    }
+  }
+  return best;
+}
+
 }  // namespace lrv
