@@ -165,24 +165,23 @@ __device__ __forceinline__ void q_dma(const Ctx& c, char* slotQ, int64_t kb) {
 
 // --------------------------------------------------------------- gather ---
 // Qt block cb, chunk g, lane L holds the 8 k of k-group g for output column
-// 16 cb + L.  Item = (g, n) for n < BN; consecutive lanes take consecutive
-// columns, so each 2-byte read instruction touches one contiguous run of a
-// raw row.  Columns at or past qcols are written as zero.
-template <int NB>
-__device__ __forceinline__ void gather(const Ctx& c, const char* slotQ, char* qt, int64_t kb) {
-  constexpr int BN = 32 * NB;
-  constexpr int items = 4 * BN;
+// 16 cb + L.  Item = (g, n) for all 256 columns of the slot (columns past
+// the tile width land in Qt blocks that no MFMA reads), two per thread, so
+// the gather is straight-line code that the compiler can interleave with the
+// MFMAs of the current step.  Consecutive lanes take consecutive columns:
+// each 2-byte read instruction touches one contiguous run of a raw row.
+// Columns at or past qcols are written as zero.
+__device__ __forceinline__ void gather(const Ctx& c, const char* slotQ, char* qt) {
   // misalignment of raw row 8g + q: ((kb + 8g + q) * ldq + nb) mod 8 = (q * ldq) mod 8
+  // (kb and nb are multiples of 8)
   int dq[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) dq[q] = (int)((q * c.ldq) & 7);
-  (void)kb;
   const int tid = 64 * c.w + c.l;
 #pragma unroll
-  for (int it = 0; it < (items + kThreads - 1) / kThreads; ++it) {
+  for (int it = 0; it < 2; ++it) {
     const int item = tid + kThreads * it;
-    if ((items % kThreads) != 0 && item >= items) break;
-    const int g = item / BN, n = item - g * BN;
+    const int g = item >> 8, n = item & 255;
     const char* rows = slotQ + (8 * g) * kQRowBytes + 2 * n;
     uint32_t e[8];
 #pragma unroll
@@ -254,7 +253,7 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, char*
   wait_vmem_all();
   if (!PAL && nks > 0) p_regs_store(c, pr, slot(0));
   barrier_lds();
-  if (nks > 0) gather<NB>(c, slot(0) + kSlotP, qtb(0), 0);
+  if (nks > 0) gather(c, slot(0) + kSlotP, qtb(0));
   if (!PAL && nks > 1) p_regs_load(c, pr, kBK);
   if (nks > 2) {
     if (PAL) p_dma(c, slot(2), 2 * kBK);
@@ -270,7 +269,9 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, char*
     // misaligned P: stage s + 2 travels through registers during this step
     if (!PAL && s + 2 < nks) p_regs_load(c, pr, (int64_t)(s + 2) * kBK);
     compute<NB>(slot(s), qtb(s), wm, wn, lane_off, acc);
-    if (s + 1 < nks) gather<NB>(c, slot(s + 1) + kSlotP, qtb(s + 1), (int64_t)(s + 1) * kBK);
+    // next stage's operand (past the last stage this reads a consumed slot
+    // and fills a Qt buffer nothing reads again)
+    gather(c, slot(s + 1) + kSlotP, qtb(s + 1));
     wait_vmem_all();  // stage s + 2 has landed (and the registers of a misaligned P)
     if (!PAL && s + 2 < nks) p_regs_store(c, pr, slot(s + 2));
     barrier_lds();
