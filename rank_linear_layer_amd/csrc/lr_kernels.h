@@ -99,6 +99,8 @@ struct PreOut {
   int64_t qrows;    // valid rows of Q
   int64_t ldc;      // leading dimension of C
   int64_t out_cols; // columns of C to write
+  float* part;      // k-split fp32 partials [splits][rows][ldpart] (splits > 1)
+  int64_t ldpart;   // >= out_cols, multiple of 4
   int col_tiles;    // column tiles of this block
   int pad_;
 };
@@ -107,10 +109,15 @@ struct PreArgs {
   int nout;         // 1 or 2 column blocks
   int row_tiles;
   int nb;           // MFMA column blocks per wave: the tile is 32 * nb columns wide
+  int splits;       // k-splits per tile (1: the GEMM writes bf16 C itself)
+  int split_steps;  // 32-deep k-steps per split
   int pad_;
   PreOut o[2];
 };
 hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream);
+// C[rows x cols] = bf16(sum of `splits` fp32 partials, in split order).
+hipError_t launch_prefill_reduce(const float* part, int splits, int64_t rows, int64_t cols, int64_t ldpart,
+                                 uint16_t* C, int64_t ldc, hipStream_t stream);
 // True when the device accepts kPreLdsBytes of LDS per workgroup.
 bool prefill_available();
 

@@ -62,9 +62,11 @@ struct lr_linear {
   uint32_t off_tpart, off_tfin, off_ypart, off_tflag, off_yflag;
   bool xcd_local;
   mutable std::atomic<uint32_t> epoch;  // stamp of the last call (resident decode kernel)
-  // prefill workspace: T [max_M x r_pad] bf16
+  // prefill workspace: T [max_M x r_pad] bf16, and fp32 k-split partials
   bool has_prefill;
   uint16_t* Tbuf;
+  float* part;
+  int64_t part_bytes;
 };
 
 namespace {
@@ -154,21 +156,46 @@ lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, con
   return LR_OK;
 }
 
+// One prefill phase: C_i = P_i . Q_i for the n outputs, then the k-split
+// reduction if the plan splits k.
+lr_status prefill_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, int64_t kd, hipStream_t stream,
+                        const char* what) {
+  const int cus = num_cus(hs[0]->device);
+  int64_t cols[2] = {0, 0};
+  for (int i = 0; i < n; ++i) cols[i] = a.o[i].out_cols;
+  lrv::PrePlan pl = lrv::prefill_plan(a.rows, cols, n, kd, cus);
+  for (int i = 0; i < n && pl.splits > 1; ++i) {
+    const int64_t need = (int64_t)pl.splits * a.rows * lrv::round_up(cols[i], 4) * 4;
+    if (need > hs[i]->part_bytes) pl = lrv::prefill_plan(a.rows, cols, n, kd, cus, 1);
+  }
+  a.nb = pl.nb;
+  a.splits = pl.splits;
+  a.split_steps = pl.split_steps;
+  for (int i = 0; i < n; ++i) {
+    a.o[i].col_tiles = (int)lrv::ceil_div(cols[i], 32 * pl.nb);
+    a.o[i].part = hs[i]->part;
+    a.o[i].ldpart = lrv::round_up(cols[i], 4);
+  }
+  hipError_t e = lrk::launch_prefill_gemm(a, stream);
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (pl.splits > 1) {
+    for (int i = 0; i < n; ++i) {
+      e = lrk::launch_prefill_reduce(a.o[i].part, pl.splits, a.rows, cols[i], a.o[i].ldpart, a.o[i].C, a.o[i].ldc,
+                                     stream);
+      if (e != hipSuccess) return hip_fail(e, "prefill k-split reduction launch");
+    }
+  }
+  return LR_OK;
+}
+
 lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                       hipStream_t stream) {
-  const int cus = num_cus(hs[0]->device);
   // phase 1: T_i = X . A_i (both projections in one launch)
   lrk::PreArgs a1;
   memset(&a1, 0, sizeof a1);
   a1.rows = M;
   a1.nout = n;
   a1.row_tiles = (int)lrv::ceil_div(M, lrk::kPreBM);
-  int64_t cols1[2] = {0, 0}, cols2[2] = {0, 0};
-  for (int i = 0; i < n; ++i) {
-    cols1[i] = hs[i]->r_pad;
-    cols2[i] = hs[i]->N;
-  }
-  a1.nb = lrv::prefill_pick_nb(M, cols1, n, cus);
   for (int i = 0; i < n; ++i) {
     const lr_linear* h = hs[i];
     lrk::PreOut& o = a1.o[i];
@@ -181,17 +208,16 @@ lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, co
     o.C = h->Tbuf;
     o.ldc = h->r_pad;
     o.out_cols = h->r_pad;
-    o.col_tiles = (int)lrv::ceil_div(h->r_pad, 32 * a1.nb);
   }
-  hipError_t e = lrk::launch_prefill_gemm(a1, stream);
-  if (e != hipSuccess) return hip_fail(e, "prefill phase-1 launch");
+  lr_status st = prefill_phase(hs, a1, n, hs[0]->K, stream, "prefill phase-1 launch");
+  if (st != LR_OK) return st;
   // phase 2: Y_i = T_i . B_i
   lrk::PreArgs a2;
   memset(&a2, 0, sizeof a2);
   a2.rows = M;
   a2.nout = n;
   a2.row_tiles = a1.row_tiles;
-  a2.nb = lrv::prefill_pick_nb(M, cols2, n, cus);
+  int64_t kd2 = 0;
   for (int i = 0; i < n; ++i) {
     const lr_linear* h = hs[i];
     lrk::PreOut& o = a2.o[i];
@@ -204,11 +230,9 @@ lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, co
     o.C = Ys[i];
     o.ldc = h->N;
     o.out_cols = h->N;
-    o.col_tiles = (int)lrv::ceil_div(h->N, 32 * a2.nb);
+    kd2 = kd2 > h->r_pad ? kd2 : h->r_pad;
   }
-  e = lrk::launch_prefill_gemm(a2, stream);
-  if (e != hipSuccess) return hip_fail(e, "prefill phase-2 launch");
-  return LR_OK;
+  return prefill_phase(hs, a2, n, kd2, stream, "prefill phase-2 launch");
 }
 
 }  // namespace
@@ -301,9 +325,13 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     return fail(LR_ERR_UNSUPPORTED, "device %d cannot give a workgroup %d bytes of LDS (prefill kernel)", dev,
                 lrk::kPreLdsBytes);
   }
+  size_t o_part = 0;
   if (h->has_prefill) {
     o_tbuf = off;
     off = align_up(off + (size_t)max_M * h->r_pad * 2);
+    h->part_bytes = lrv::prefill_partial_bytes(max_M, K, h->r_pad, N, num_cus(dev));
+    o_part = off;
+    off = align_up(off + (size_t)h->part_bytes);
   }
   h->ws_bytes = off;
   if (off > 0) {
@@ -333,7 +361,10 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     h->off_ypart = (uint32_t)o_ypart;
     h->off_tflag = (uint32_t)o_tflag;
   }
-  if (h->has_prefill) h->Tbuf = (uint16_t*)(base + o_tbuf);
+  if (h->has_prefill) {
+    h->Tbuf = (uint16_t*)(base + o_tbuf);
+    h->part = h->part_bytes > 0 ? (float*)(base + o_part) : nullptr;
+  }
   *out = h;
   return LR_OK;
 }

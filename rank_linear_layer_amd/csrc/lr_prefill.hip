@@ -83,11 +83,10 @@ struct Tile {
 // Workgroup id -> tile.  XCD x (= id mod 8) receives the contiguous run
 // [x*q + min(x, rem), ...) of the tile order; the order is row-tile groups of
 // kGroupRows, walked column tile by column tile across both outputs.
-__device__ __forceinline__ Tile map_tile(const PreArgs& a, int bn) {
+__device__ __forceinline__ Tile map_tile(const PreArgs& a, int bn, int bid) {
   const int ct_total = a.o[0].col_tiles + (a.nout > 1 ? a.o[1].col_tiles : 0);
   const int total = a.row_tiles * ct_total;
   const int q = total >> 3, rem = total & 7;
-  const int bid = (int)blockIdx.x;
   const int x = bid & 7, j = bid >> 3;
   const int t = x * q + min(x, rem) + j;
   const int per_group = kGroupRows * ct_total;
@@ -212,7 +211,7 @@ __device__ __forceinline__ void compute(const char* slotP, const char* qt, int w
 }
 
 template <int NB, bool PAL>
-__device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, char* smem) {
+__device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int ks, char* smem) {
   constexpr int BN = 32 * NB;
   const PreOut& O = a.o[T.bi];
   Ctx c;
@@ -236,28 +235,32 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, char*
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
 
-  const int nks = (int)((O.kd + kBK - 1) / kBK);
+  // this workgroup's k-steps: [s0, s0 + nks) of the ceil(kd / 32) steps
+  const int nks_all = (int)((O.kd + kBK - 1) / kBK);
+  const int s0 = ks * a.split_steps;
+  const int nks = max(0, min(nks_all - s0, a.split_steps));
+  const int64_t k0 = (int64_t)s0 * kBK;
   auto slot = [&](int s) { return smem + (s % 3) * kSlot; };
   auto qtb = [&](int s) { return smem + kQtBase + (s & 1) * kQt; };
 
   // prologue: stages 0 and 1 in flight, stage 0 gathered, stage 2 in flight
   PRegs pr;
   if (nks > 0) {
-    if (PAL) p_dma(c, slot(0), 0); else p_regs_load(c, pr, 0);
-    q_dma(c, slot(0) + kSlotP, 0);
+    if (PAL) p_dma(c, slot(0), k0); else p_regs_load(c, pr, k0);
+    q_dma(c, slot(0) + kSlotP, k0);
   }
   if (nks > 1) {
-    if (PAL) p_dma(c, slot(1), kBK);
-    q_dma(c, slot(1) + kSlotP, kBK);
+    if (PAL) p_dma(c, slot(1), k0 + kBK);
+    q_dma(c, slot(1) + kSlotP, k0 + kBK);
   }
   wait_vmem_all();
   if (!PAL && nks > 0) p_regs_store(c, pr, slot(0));
   barrier_lds();
   if (nks > 0) gather(c, slot(0) + kSlotP, qtb(0));
-  if (!PAL && nks > 1) p_regs_load(c, pr, kBK);
+  if (!PAL && nks > 1) p_regs_load(c, pr, k0 + kBK);
   if (nks > 2) {
-    if (PAL) p_dma(c, slot(2), 2 * kBK);
-    q_dma(c, slot(2) + kSlotP, 2 * kBK);
+    if (PAL) p_dma(c, slot(2), k0 + 2 * kBK);
+    q_dma(c, slot(2) + kSlotP, k0 + 2 * kBK);
   }
   if (!PAL && nks > 1) {
     wait_vmem_all();
@@ -267,7 +270,7 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, char*
 
   for (int s = 0; s < nks; ++s) {
     // misaligned P: stage s + 2 travels through registers during this step
-    if (!PAL && s + 2 < nks) p_regs_load(c, pr, (int64_t)(s + 2) * kBK);
+    if (!PAL && s + 2 < nks) p_regs_load(c, pr, k0 + (int64_t)(s + 2) * kBK);
     compute<NB>(slot(s), qtb(s), wm, wn, lane_off, acc);
     // next stage's operand (past the last stage this reads a consumed slot
     // and fills a Qt buffer nothing reads again)
@@ -277,12 +280,31 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, char*
     barrier_lds();
     // slot s % 3 is free: every wave is past compute(s) and gathered s earlier
     if (s + 3 < nks) {
-      if (PAL) p_dma(c, slot(s + 3), (int64_t)(s + 3) * kBK);
-      q_dma(c, slot(s + 3) + kSlotP, (int64_t)(s + 3) * kBK);
+      if (PAL) p_dma(c, slot(s + 3), k0 + (int64_t)(s + 3) * kBK);
+      q_dma(c, slot(s + 3) + kSlotP, k0 + (int64_t)(s + 3) * kBK);
     }
   }
 
   // ------------------------------------------------------------ epilogue --
+  if (a.splits > 1) {
+    // fp32 partial of this k-split: [ks][rows][ldpart], summed in split order
+    // and rounded by lr_prefill_reduce_kernel.  Lane (L, G) of tile (i, j)
+    // holds rows 64 wm + 16 i + 4 G + t, column 16 (NB wn + j) + L.
+    const int L = c.l & 15, G = c.l >> 4;
+    float* part = O.part + (int64_t)ks * a.rows * O.ldpart;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t m = T.mb + 64 * wm + 16 * i + 4 * G + t;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int64_t n = T.nb + 16 * (NB * wn + j) + L;
+          if (m < a.rows && n < O.out_cols) part[m * O.ldpart + n] = acc[i][j][t];
+        }
+      }
+    return;
+  }
   // Stage the 256 x BN bf16 tile in LDS with every row shifted by its
   // misalignment d = (row * ldc + nb) mod 8, so that LDS chunk k of a row is
   // global 16-byte chunk k of that row's segment.  Lane (L, G) of tile
@@ -331,8 +353,37 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, char*
 template <int NB, bool PAL>
 __global__ __launch_bounds__(kThreads, 1) void lr_prefill_gemm_kernel(const PreArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const Tile T = map_tile(a, 32 * NB);
-  gemm_tile<NB, PAL>(a, T, smem);
+  // workgroup -> (tile, k-split): consecutive ids are different tiles of one
+  // split, so the XCD dealing of tiles is the same for every split
+  const int tiles = a.row_tiles * (a.o[0].col_tiles + (a.nout > 1 ? a.o[1].col_tiles : 0));
+  const int ks = (int)blockIdx.x / tiles;
+  const Tile T = map_tile(a, 32 * NB, (int)blockIdx.x - ks * tiles);
+  gemm_tile<NB, PAL>(a, T, ks, smem);
+}
+
+// Y (or T) = bf16(sum over k-splits of the fp32 partials, in split order).
+// Thread -> 4 consecutive columns of one row.
+__global__ __launch_bounds__(256) void lr_prefill_reduce_kernel(const float* part, int splits, int64_t rows,
+                                                               int64_t cols, int64_t ldpart, uint16_t* C,
+                                                               int64_t ldc) {
+  const int64_t q = (cols + 3) / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * q) return;
+  const int64_t m = idx / q, n = (idx - m * q) * 4;
+  const float* p = part + m * ldpart + n;
+  f32x4_t sum = *reinterpret_cast<const f32x4_t*>(p);
+  for (int s = 1; s < splits; ++s) sum += *reinterpret_cast<const f32x4_t*>(p + (int64_t)s * rows * ldpart);
+  uint16_t* c = C + m * ldc + n;
+  if (n + 4 <= cols && ((m * ldc + n) & 3) == 0) {
+    uint2 v;
+    v.x = pack_bf16x2(sum[0], sum[1]);
+    v.y = pack_bf16x2(sum[2], sum[3]);
+    *reinterpret_cast<uint2*>(c) = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < cols) c[e] = (uint16_t)f32_to_bf16_rne(sum[e]);
+  }
 }
 
 template <int NB, bool PAL>
@@ -352,7 +403,7 @@ hipError_t launch_one(const PreArgs& args, int grid, hipStream_t stream) {
 
 hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream) {
   const int ct = args.o[0].col_tiles + (args.nout > 1 ? args.o[1].col_tiles : 0);
-  const int grid = ct * args.row_tiles;
+  const int grid = ct * args.row_tiles * args.splits;
   if (grid <= 0) return hipSuccess;
   bool pal = true;
   for (int i = 0; i < args.nout; ++i) pal = pal && (args.o[i].ldp & 7) == 0;
@@ -362,6 +413,15 @@ hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream) {
     case 8: return pal ? launch_one<8, true>(args, grid, stream) : launch_one<8, false>(args, grid, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_prefill_reduce(const float* part, int splits, int64_t rows, int64_t cols, int64_t ldpart,
+                                 uint16_t* C, int64_t ldc, hipStream_t stream) {
+  const int64_t items = rows * ((cols + 3) / 4);
+  if (items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lr_prefill_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, part,
+                     splits, rows, cols, ldpart, C, ldc);
+  return hipGetLastError();
 }
 
 bool prefill_available() {

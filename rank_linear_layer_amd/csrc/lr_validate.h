@@ -180,27 +180,59 @@ inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget, boo
 
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-// Prefill tile width: 32 * nb columns, nb in [6, 8].  A workgroup's time
-// grows with nb (4 * nb MFMAs per k-step plus a fixed share for loads and
-// the barrier, about two column blocks' worth); the launch takes as many
-// rounds as it has workgroups per compute unit.  The cheapest nb wins (the
-// wider one on a tie).  out_cols holds the output columns of the nout
-// outputs of one launch.
-inline int prefill_pick_nb(int64_t rows, const int64_t* out_cols, int nout, int num_cus) {
+// Prefill launch plan: tile width 32 * nb columns (nb in [6, 8]) and a
+// k-split.  Cost unit: one 32-deep k-step of one workgroup with one MFMA
+// column block per wave (a step costs about nb + 2 units: nb column blocks
+// plus a fixed share for loads and the barrier; one unit is about 0.14 us).
+// A launch takes as many rounds as it has workgroups per compute unit.  A
+// k-split (splits > 1) adds a reduction kernel: one launch (about 14 units)
+// plus writing and reading the fp32 partials (about 700 KB per unit).  The
+// cheapest plan wins (fewer splits, then the wider tile, on a tie).
+struct PrePlan {
+  int nb, splits, split_steps;
+};
+inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int64_t kd, int num_cus,
+                            int max_splits = 32) {
   const int64_t row_tiles = ceil_div(rows, 256);
-  int best = 8;
-  int64_t best_cost = -1;
+  const int64_t nks = ceil_div(kd, 32);
+  const int cus = num_cus > 0 ? num_cus : 1;
+  int64_t cols = 0;
+  for (int i = 0; i < nout; ++i) cols += out_cols[i];
+  PrePlan best{8, 1, (int)nks};
+  double best_cost = -1;
   for (int nb = 8; nb >= 6; --nb) {
     int64_t tiles = 0;
     for (int i = 0; i < nout; ++i) tiles += row_tiles * ceil_div(out_cols[i], 32 * nb);
-    const int64_t rounds = ceil_div(tiles, num_cus > 0 ? num_cus : 1);
-    const int64_t cost = rounds * (nb + 2);
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best = nb;
+    for (int64_t want = 1; want <= max_splits && want <= nks; ++want) {
+      const int64_t steps = ceil_div(nks, want);
+      const int64_t splits = ceil_div(nks, steps);  // no empty split
+      if (splits != want) continue;
+      const int64_t rounds = ceil_div(tiles * splits, cus);
+      double cost = (double)(rounds * steps * (nb + 2));
+      if (splits > 1) cost += 14.0 + (double)(2 * splits * rows * cols * 4 + rows * cols * 2) / 700e3;
+      if (best_cost < 0 || cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = PrePlan{nb, (int)splits, (int)steps};
+      }
     }
   }
   return best;
+}
+
+// fp32 partial bytes a handle needs for its own output over every M <= max_M
+// (both phases share the region; M steps of 256 change the tiling).
+inline int64_t prefill_partial_bytes(int64_t max_M, int64_t K, int64_t r_pad, int64_t N, int num_cus) {
+  int64_t need = 0;
+  for (int64_t m = 256;; m += 256) {
+    const int64_t M = m < max_M ? m : max_M;
+    const int64_t c1 = r_pad, c2 = N;
+    const PrePlan p1 = prefill_plan(M, &c1, 1, K, num_cus);
+    const PrePlan p2 = prefill_plan(M, &c2, 1, r_pad, num_cus);
+    if (p1.splits > 1) need = need > p1.splits * M * round_up(c1, 4) * 4 ? need : p1.splits * M * round_up(c1, 4) * 4;
+    if (p2.splits > 1) need = need > p2.splits * M * round_up(c2, 4) * 4 ? need : p2.splits * M * round_up(c2, 4) * 4;
+    if (M == max_M) break;
+  }
+  return need;
 }
 
 }  // namespace lrv

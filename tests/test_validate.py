@@ -37,6 +37,14 @@ void t_partition(long long K, long long r, long long N, int budget, int allow_re
   out[0] = p.Jw; out[1] = p.S; out[2] = p.ktps; out[3] = p.ntps;
   out[4] = p.kind; out[5] = p.js_w; out[6] = p.nt_w;
 }
+void t_prefill_plan(long long rows, long long c0, long long c1, int nout, long long kd, int cus, int* out) {
+  const int64_t cols[2] = {c0, c1};
+  lrv::PrePlan p = lrv::prefill_plan(rows, cols, nout, kd, cus);
+  out[0] = p.nb; out[1] = p.splits; out[2] = p.split_steps;
+}
+long long t_partial_bytes(long long max_M, long long K, long long r_pad, long long N, int cus) {
+  return lrv::prefill_partial_bytes(max_M, K, r_pad, N, cus);
+}
 }
 """
 
@@ -55,6 +63,9 @@ def shim(tmp_path_factory):
     lib.t_check_run.argtypes = [ll, ll, ll, ll, ull, ull, ull, ull, ll]
     lib.t_check_packed.argtypes = [ll, ll, ll, ll, ull, ull, ull, ull, ull, ull, ull, ll]
     lib.t_partition.argtypes = [ll, ll, ll, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.t_prefill_plan.argtypes = [ll, ll, ll, ctypes.c_int, ll, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.t_partial_bytes.argtypes = [ll, ll, ll, ll, ctypes.c_int]
+    lib.t_partial_bytes.restype = ll
     return lib
 
 
@@ -150,3 +161,46 @@ def test_decode_partition_balances_q_proj(shim):
     per_wg = ktps * 32 * 120 + ntps * 120 * 120
     ideal = (128 * 32 * 120 + 35 * 120 * 120) / S
     assert per_wg <= 1.25 * ideal
+
+
+def _plan(shim, rows, cols, kd, cus=256):
+    out = (ctypes.c_int * 3)()
+    c = list(cols) + [0]
+    shim.t_prefill_plan(rows, c[0], c[1], len(cols), kd, cus, out)
+    return tuple(out)
+
+
+@pytest.mark.parametrize("rows,cols,kd", [
+    (4096, (2880,), 4096), (4096, (14336,), 2880),          # MLP up-projection, both phases
+    (2048, (1664,), 4096), (2048, (4096,), 1664),           # q_proj at M = 2048
+    (2048, (2880, 2880), 4096), (2048, (14336, 14336), 2880),  # packed gate/up
+    (512, (1056,), 4096), (512, (3999,), 1056),             # alignment sweep at M = 512
+    (17, (128,), 512), (40, (512,), 128), (300, (33,), 7),  # small and ragged
+])
+def test_prefill_plan_covers_k_and_fits(shim, rows, cols, kd):
+    nb, splits, steps = _plan(shim, rows, cols, kd)
+    nks = -(-kd // 32)
+    assert 6 <= nb <= 8
+    assert splits >= 1 and steps >= 1
+    # every k-step is in exactly one split and no split is empty
+    assert splits * steps >= nks and (splits - 1) * steps < nks
+
+
+def test_prefill_plan_fills_the_machine_for_small_m(shim):
+    # MLP up at M = 4096: enough tiles, no split
+    assert _plan(shim, 4096, (14336,), 2880)[1] == 1
+    # the M = 512 sweep shape has 12 tiles of 256 x 192: it splits k
+    nb, splits, steps = _plan(shim, 512, (1056,), 4096)
+    tiles = 2 * -(-1056 // (32 * nb))
+    assert splits > 1 and tiles * splits >= 64
+
+
+def test_prefill_partial_bytes_cover_every_plan(shim):
+    for max_M, K, r_pad, N in [(4096, 4096, 2880, 14336), (2048, 4096, 1664, 4096), (512, 4096, 1056, 3999),
+                               (600, 14336, 2880, 4096)]:
+        have = shim.t_partial_bytes(max_M, K, r_pad, N, 256)
+        for M in list(range(17, max_M + 1, 97)) + [max_M]:
+            for cols, kd in (((r_pad,), K), ((N,), r_pad)):
+                nb, splits, steps = _plan(shim, M, cols, kd)
+                if splits > 1:
+                    assert splits * M * (-(-cols[0] // 4) * 4) * 4 <= have, (max_M, M, cols, kd, splits)
