@@ -82,8 +82,8 @@ constexpr int kPreBM = 256;       // rows per workgroup tile
 constexpr int kPreKT = 32;        // k per LDS stage (one MFMA k-step)
 // columns per workgroup tile = 32 * nb, nb in [kPreMinNB, kPreMaxNB]
 constexpr int kPreMinNB = 6;
-constexpr int kPreMaxNB = 8;
-constexpr int kPreLdsBytes = 256 * 33 * 16;  // max(3 raw slots + 2 gathered tiles, epilogue staging)
+constexpr int kPreMaxNB = 7;
+constexpr int kPreLdsBytes = 4 * (16 + 15) * 1024 + 2 * 16 * 1024;  // 4 raw slots + 2 gathered tiles
 
 // C[rows x out_cols] = P[rows x kd] . Q[kd x ldq] for one or two column
 // blocks in one launch.  P is k-contiguous (X or T); Q is row-major with

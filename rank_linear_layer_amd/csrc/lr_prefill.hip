@@ -52,18 +52,28 @@ constexpr int kThreads = kPreThreads;  // 512
 constexpr int kBM = kPreBM;            // 256
 constexpr int kBK = kPreKT;            // 32
 constexpr int kSlotP = 16 * 1024;      // P slot: 16 blocks of 16 rows x 4 chunks
-constexpr int kQChunks = 33;           // raw chunks per Q row (256 columns + realign)
-constexpr int kQRowBytes = kQChunks * 16;
-constexpr int kQInst = 17;             // direct loads per Q slot (1088 >= 32 * 33 chunks)
-constexpr int kSlotQ = kQInst * 1024;
+constexpr int kSlotQ = 15 * 1024;      // Q slot: 32 raw rows of up to 29 chunks (nb <= 7)
 constexpr int kSlot = kSlotP + kSlotQ;
-constexpr int kQt = 16 * 1024;         // gathered Q: up to 16 column blocks
-constexpr int kQtBase = 3 * kSlot;
-constexpr int kEpiPitch = kQRowBytes;  // epilogue staging row pitch (33 chunks)
+constexpr int kSlots = 4;              // ring depth: loads run three k-steps ahead
+constexpr int kQt = 16 * 1024;         // gathered Q: 16 column blocks (the gather covers 256 columns)
+constexpr int kQtBase = kSlots * kSlot;
 constexpr int kGroupRows = 4;          // row tiles per group in the tile order
 constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
 static_assert(kQtBase + 2 * kQt <= kPreLdsBytes, "LDS layout");
-static_assert(kBM * kEpiPitch <= kPreLdsBytes, "epilogue staging");
+
+// Geometry that depends on the tile width 32 * NB.
+template <int NB>
+struct Geo {
+  static constexpr int kQChunks = 4 * NB + 1;  // raw chunks per Q row: 32 NB columns + one for misalignment
+  static constexpr int kQRowBytes = kQChunks * 16;
+  static constexpr int kQInst = (32 * kQChunks + 63) / 64;  // direct loads per Q slot
+  static constexpr int kEpiPitch = kQRowBytes;               // epilogue staging row pitch
+  static_assert(kQInst * 1024 <= kSlotQ, "Q slot");
+  static_assert(kQInst <= 16, "two direct loads per wave cover the Q slot");
+  // the gather reads columns up to 255 (+ 7 of misalignment) of the last raw row
+  static_assert(31 * kQRowBytes + 2 * (255 + 7) + 2 <= kSlotQ, "gather stays inside the Q slot");
+  static_assert(kBM * kEpiPitch <= kPreLdsBytes, "epilogue staging");
+};
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -115,17 +125,29 @@ struct Ctx {
 };
 
 // -------------------------------------------------------------- loads ---
+// Every direct load's byte offset is computed once per workgroup and then
+// advanced by a uniform stride per k-step: P moves 32 columns (64 bytes) and
+// Q moves 32 rows (64 * ldq bytes) per step, which keeps each row's
+// misalignment, so the chunk selection of a lane never changes.
+
 // P slot, aligned P: wave w loads 16-row blocks w and w + 8.  Lane l of a
 // block fills chunk l / 16 of row l % 16; chunks at or past kd read zero.
-__device__ __forceinline__ void p_dma(const Ctx& c, char* slotP, int64_t kb) {
+struct PDma {
+  uint32_t off0[2];  // byte offset at k-step 0 of this split
+  int kcol;          // lane's first column at k-step 0
+};
+__device__ __forceinline__ void p_dma_init(const Ctx& c, int64_t k0, PDma& d) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int b = c.w + 8 * h;
-    const int64_t row = c.mb + 16 * b + (c.l & 15);
-    const int64_t k0 = kb + 8 * (c.l >> 4);
-    const uint32_t off = k0 < c.kd ? (uint32_t)((row * c.ldp + k0) * 2) : kOutOfRange;
-    dma16(c.rP, slotP + b * 1024, off);
+    const int64_t row = c.mb + 16 * (c.w + 8 * h) + (c.l & 15);
+    d.off0[h] = (uint32_t)((row * c.ldp + k0 + 8 * (c.l >> 4)) * 2);
   }
+  d.kcol = (int)(k0 + 8 * (c.l >> 4));
+}
+__device__ __forceinline__ void p_dma(const Ctx& c, const PDma& d, char* slotP, int t) {
+  const bool ok = (int64_t)d.kcol + 32 * t < c.kd;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) dma16(c.rP, slotP + (c.w + 8 * h) * 1024, ok ? d.off0[h] + 64u * t : kOutOfRange);
 }
 
 // P slot, misaligned P: the same two chunks per lane through registers.
@@ -144,22 +166,56 @@ __device__ __forceinline__ void p_regs_store(const Ctx& c, const PRegs& p, char*
   for (int h = 0; h < 2; ++h) lds_write16(slotP + (c.w + 8 * h) * 1024 + c.l * 16, p.v[h]);
 }
 
-// Q slot: 32 raw rows x 33 chunks = 1056 chunks in 17 loads of 64 chunks;
-// wave w issues loads w and w + 8, wave 0 also load 16.  Only the chunks
-// that hold the tile's qcols columns of a row are fetched.
-__device__ __forceinline__ void q_dma_one(const Ctx& c, char* slotQ, int64_t kb, int i) {
-  const int s = 64 * i + c.l;
-  const int row = s / kQChunks, ch = s - row * kQChunks;
-  const int64_t krow = kb + row;
-  const int64_t e0 = krow * c.ldq + c.nb;
-  const int need = (int)(((e0 & 7) + c.qcols + 7) >> 3);
-  const bool ok = row < kBK && krow < c.qrows && ch < need;
-  dma16(c.rQ, slotQ + i * 1024, ok ? (uint32_t)(((e0 >> 3) + ch) * 16) : kOutOfRange);
+// Q slot: 32 raw rows x (4 NB + 1) chunks in Geo::kQInst loads of 64
+// chunks; wave w issues loads w and w + 8 (when they exist).  Only the
+// chunks that hold the tile's qcols columns of a row are fetched.
+struct QDma {
+  uint32_t off0[2];  // byte offset at k-step 0 of this split
+  int krow[2];       // lane's raw row at k-step 0 (k index)
+  bool ok[2];        // lane fills a real chunk of a real row of the slot
+};
+template <int NB>
+__device__ __forceinline__ void q_dma_init(const Ctx& c, int64_t k0, QDma& d) {
+  constexpr int QC = Geo<NB>::kQChunks;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = c.w + 8 * h;
+    const int s = 64 * i + c.l;
+    const int row = s / QC, ch = s - row * QC;
+    const int64_t e0 = (k0 + row) * c.ldq + c.nb;
+    const int need = (int)(((e0 & 7) + c.qcols + 7) >> 3);
+    d.ok[h] = i < Geo<NB>::kQInst && row < kBK && ch < need;
+    d.off0[h] = d.ok[h] ? (uint32_t)(((e0 >> 3) + ch) * 16) : 0u;
+    d.krow[h] = (int)(k0 + row);
+  }
 }
-__device__ __forceinline__ void q_dma(const Ctx& c, char* slotQ, int64_t kb) {
-  q_dma_one(c, slotQ, kb, c.w);
-  q_dma_one(c, slotQ, kb, c.w + 8);
-  if (c.w == 0) q_dma_one(c, slotQ, kb, 16);
+template <int NB>
+__device__ __forceinline__ void q_dma(const Ctx& c, const QDma& d, char* slotQ, int t) {
+  const uint32_t stride = (uint32_t)(64 * c.ldq);  // 32 rows of bf16
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (c.w + 8 * h < Geo<NB>::kQInst) {  // uniform
+      const bool ok = d.ok[h] && (int64_t)d.krow[h] + 32 * t < c.qrows;
+      dma16(c.rQ, slotQ + (c.w + 8 * h) * 1024, ok ? d.off0[h] + stride * (uint32_t)t : kOutOfRange);
+    }
+  }
+}
+// Direct loads one stage costs wave w (P: 2, Q: its share of kQInst).
+template <int NB, bool PAL>
+__device__ __forceinline__ int dma_per_stage(int w) {
+  return (PAL ? 2 : 0) + (w < Geo<NB>::kQInst ? (Geo<NB>::kQInst - 1 - w) / 8 + 1 : 0);
+}
+// s_waitcnt vmcnt(n), n in [0, 4] (gfx9 encoding: expcnt and lgkmcnt left at max).
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // --------------------------------------------------------------- gather ---
@@ -170,7 +226,9 @@ __device__ __forceinline__ void q_dma(const Ctx& c, char* slotQ, int64_t kb) {
 // MFMAs of the current step.  Consecutive lanes take consecutive columns:
 // each 2-byte read instruction touches one contiguous run of a raw row.
 // Columns at or past qcols are written as zero.
+template <int NB>
 __device__ __forceinline__ void gather(const Ctx& c, const char* slotQ, char* qt) {
+  constexpr int kQRowBytes = Geo<NB>::kQRowBytes;
   // misalignment of raw row 8g + q: ((kb + 8g + q) * ldq + nb) mod 8 = (q * ldq) mod 8
   // (kb and nb are multiples of 8)
   int dq[8];
@@ -240,28 +298,32 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   const int s0 = ks * a.split_steps;
   const int nks = max(0, min(nks_all - s0, a.split_steps));
   const int64_t k0 = (int64_t)s0 * kBK;
-  auto slot = [&](int s) { return smem + (s % 3) * kSlot; };
+  auto slot = [&](int s) { return smem + (s & (kSlots - 1)) * kSlot; };
   auto qtb = [&](int s) { return smem + kQtBase + (s & 1) * kQt; };
+  PDma pd;
+  QDma qd;
+  if (PAL) p_dma_init(c, k0, pd);
+  q_dma_init<NB>(c, k0, qd);
+  auto stage_dma = [&](int s) {
+    if (PAL) p_dma(c, pd, slot(s), s);
+    q_dma<NB>(c, qd, slot(s) + kSlotP, s);
+  };
+  const int dma_w = dma_per_stage<NB, PAL>(c.w);
 
-  // prologue: stages 0 and 1 in flight, stage 0 gathered, stage 2 in flight
+  // prologue: stages 0 and 1 landed, stage 0 gathered, stages 2 and 3 in flight
   PRegs pr;
   if (nks > 0) {
-    if (PAL) p_dma(c, slot(0), k0); else p_regs_load(c, pr, k0);
-    q_dma(c, slot(0) + kSlotP, k0);
+    if (!PAL) p_regs_load(c, pr, k0);
+    stage_dma(0);
   }
-  if (nks > 1) {
-    if (PAL) p_dma(c, slot(1), k0 + kBK);
-    q_dma(c, slot(1) + kSlotP, k0 + kBK);
-  }
+  if (nks > 1) stage_dma(1);
   wait_vmem_all();
   if (!PAL && nks > 0) p_regs_store(c, pr, slot(0));
   barrier_lds();
-  if (nks > 0) gather(c, slot(0) + kSlotP, qtb(0));
+  if (nks > 0) gather<NB>(c, slot(0) + kSlotP, qtb(0));
   if (!PAL && nks > 1) p_regs_load(c, pr, k0 + kBK);
-  if (nks > 2) {
-    if (PAL) p_dma(c, slot(2), k0 + 2 * kBK);
-    q_dma(c, slot(2) + kSlotP, k0 + 2 * kBK);
-  }
+  if (nks > 2) stage_dma(2);
+  if (nks > 3) stage_dma(3);
   if (!PAL && nks > 1) {
     wait_vmem_all();
     p_regs_store(c, pr, slot(1));
@@ -274,15 +336,17 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
     compute<NB>(slot(s), qtb(s), wm, wn, lane_off, acc);
     // next stage's operand (past the last stage this reads a consumed slot
     // and fills a Qt buffer nothing reads again)
-    gather(c, slot(s + 1) + kSlotP, qtb(s + 1));
-    wait_vmem_all();  // stage s + 2 has landed (and the registers of a misaligned P)
+    gather<NB>(c, slot(s + 1) + kSlotP, qtb(s + 1));
+    // stage s + 2 has landed; stage s + 3 (issued one step later) may still
+    // be in flight.  The misaligned P path drains everything.
+    if (PAL && s + 3 < nks)
+      wait_vmem_upto(dma_w);
+    else
+      wait_vmem_all();
     if (!PAL && s + 2 < nks) p_regs_store(c, pr, slot(s + 2));
     barrier_lds();
-    // slot s % 3 is free: every wave is past compute(s) and gathered s earlier
-    if (s + 3 < nks) {
-      if (PAL) p_dma(c, slot(s + 3), k0 + (int64_t)(s + 3) * kBK);
-      q_dma(c, slot(s + 3) + kSlotP, k0 + (int64_t)(s + 3) * kBK);
-    }
+    // slot s is free: every wave is past compute(s) and gathered s earlier
+    if (s + 4 < nks) stage_dma(s + 4);
   }
 
   // ------------------------------------------------------------ epilogue --
@@ -317,7 +381,7 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
     for (int t = 0; t < 4; ++t) {
       const int m = 64 * wm + 16 * i + 4 * G + t;
       const int d = (int)(((T.mb + m) * ldc + T.nb) & 7);
-      uint16_t* row = reinterpret_cast<uint16_t*>(smem + m * kEpiPitch) + d + 16 * NB * wn + L;
+      uint16_t* row = reinterpret_cast<uint16_t*>(smem + m * Geo<NB>::kEpiPitch) + d + 16 * NB * wn + L;
 #pragma unroll
       for (int j = 0; j < NB; ++j) row[16 * j] = (uint16_t)f32_to_bf16_rne(acc[i][j][t]);
     }
@@ -326,6 +390,7 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
 
   const rsrc_t rC = make_rsrc(O.C, a.rows * ldc * 2);
   const int ncols = (int)min64((int64_t)BN, O.out_cols - T.nb);
+  constexpr int kQChunks = Geo<NB>::kQChunks;
   constexpr int nitems = kBM * kQChunks;
   for (int item = threadIdx.x; item < nitems; item += kThreads) {
     const int m = item / kQChunks, k = item - m * kQChunks;
@@ -334,7 +399,7 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
     const int d = (int)((R * ldc + T.nb) & 7);
     const int n0 = 8 * k - d;  // tile column of the chunk's first element
     if (n0 >= ncols) continue;
-    const u32x4_t v = lds_read16(smem + m * kEpiPitch + 16 * k);
+    const u32x4_t v = lds_read16(smem + m * Geo<NB>::kEpiPitch + 16 * k);
     const int64_t e0 = R * ldc + T.nb + n0;  // multiple of 8
     if (n0 >= 0 && n0 + 8 <= ncols) {
       __builtin_amdgcn_raw_buffer_store_b128(v, rC, (int)(e0 * 2), 0, 0);
@@ -410,7 +475,6 @@ hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream) {
   switch (args.nb) {
     case 6: return pal ? launch_one<6, true>(args, grid, stream) : launch_one<6, false>(args, grid, stream);
     case 7: return pal ? launch_one<7, true>(args, grid, stream) : launch_one<7, false>(args, grid, stream);
-    case 8: return pal ? launch_one<8, true>(args, grid, stream) : launch_one<8, false>(args, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -180,7 +180,7 @@ inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget, boo
 
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-// Prefill launch plan: tile width 32 * nb columns (nb in [6, 8]) and a
+// Prefill launch plan: tile width 32 * nb columns (nb in [6, 7]) and a
 // k-split.  Cost unit: one 32-deep k-step of one workgroup with one MFMA
 // column block per wave (a step costs about nb + 2 units: nb column blocks
 // plus a fixed share for loads and the barrier; one unit is about 0.14 us).
@@ -198,9 +198,9 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
   const int cus = num_cus > 0 ? num_cus : 1;
   int64_t cols = 0;
   for (int i = 0; i < nout; ++i) cols += out_cols[i];
-  PrePlan best{8, 1, (int)nks};
+  PrePlan best{7, 1, (int)nks};
   double best_cost = -1;
-  for (int nb = 8; nb >= 6; --nb) {
+  for (int nb = 7; nb >= 6; --nb) {
     int64_t tiles = 0;
     for (int i = 0; i < nout; ++i) tiles += row_tiles * ceil_div(out_cols[i], 32 * nb);
     for (int64_t want = 1; want <= max_splits && want <= nks; ++want) {

@@ -180,7 +180,7 @@ def _plan(shim, rows, cols, kd, cus=256):
 def test_prefill_plan_covers_k_and_fits(shim, rows, cols, kd):
     nb, splits, steps = _plan(shim, rows, cols, kd)
     nks = -(-kd // 32)
-    assert 6 <= nb <= 8
+    assert 6 <= nb <= 7
     assert splits >= 1 and steps >= 1
     # every k-step is in exactly one split and no split is empty
     assert splits * steps >= nks and (splits - 1) * steps < nks
