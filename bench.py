@@ -10,10 +10,12 @@ cache.  value = algorithmic bytes per step / time per step (TB/s).
 
 A second object reports the prefill workload (MLP up-projection,
 X[4096 x 4096], r = 2867, N = 14336) in TFLOP/s against the dense bf16
-MFMA peak.  The CPU oracle is timed on a bounded sample as a baseline.
+MFMA peak, and a third one a whole decoder layer of factorized projections
+at M = 1 (TB/s) and M = 2048 (TFLOP/s).  The CPU oracle is timed on a
+bounded sample as a baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
-                    [--calib-copy] [--sweep]
+                    [--no-layer] [--calib-copy] [--sweep]
 """
 from __future__ import annotations
 
@@ -129,6 +131,41 @@ def bench_prefill(torch, lrl, configs, metrics, steps, warmup):
     return dict(M=M, K=K, r=r, N=N, ms=ms, tflops=fl / (ms * 1e-3) / 1e12, flops=fl, plan=lin.describe())
 
 
+def bench_layer(torch, lrl, configs, metrics, M, steps, warmup):
+    """One decoder layer of factorized projections (q, k, v, o, packed
+    gate/up, down) at M rows: the layer's span per step.  Weights rotate over
+    enough copies (>= 1 GiB) that every step streams them from HBM."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(configs.seed_base(configs.LAYER_INDEX))
+    projs = {p.name: p for p in configs.LAYER_PROJS}
+    wbytes = sum(2 * (p.K * p.r + p.r * p.N) for p in configs.LAYER_PROJS)
+    ncop = max(1, int(np.ceil((1 << 30) / wbytes))) if M <= 16 else 1
+    sets = []
+    for _ in range(ncop):
+        lins = {}
+        for name, p in projs.items():
+            A = (torch.randn((p.K, p.r), generator=g, device="cuda") / np.sqrt(p.K)).to(torch.bfloat16)
+            B = (torch.randn((p.r, p.N), generator=g, device="cuda") / np.sqrt(p.r)).to(torch.bfloat16)
+            lins[name] = lrl.LowRankLinear(A, B, max_M=M)
+        sets.append(lins)
+    X = torch.randn((M, 4096), generator=g, device="cuda").to(torch.bfloat16)
+    H = torch.randn((M, 14336), generator=g, device="cuda").to(torch.bfloat16)
+    outs = {name: torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for name, p in projs.items()}
+
+    def step(i):
+        L = sets[i % ncop]
+        for name in ("q", "k", "v", "o"):
+            L[name](X, out=outs[name])
+        lrl.mlp_packed(L["gate"], L["up"], X, out_gate=outs["gate"], out_up=outs["up"])
+        L["down"](H, out=outs["down"])
+
+    ms = time_steps(torch, step, steps, warmup, torch.cuda.current_stream())
+    byts = sum(metrics.decode_bytes(M, p.K, p.r, p.N) for p in configs.LAYER_PROJS)
+    fl = sum(metrics.lowrank_flops(M, p.K, p.r, p.N) for p in configs.LAYER_PROJS)
+    return dict(M=M, ms=ms, tbs=byts / (ms * 1e-3) / 1e12, tflops=fl / (ms * 1e-3) / 1e12, bytes=byts, flops=fl,
+                launches=6, copies=ncop)
+
+
 def cpu_baseline(configs, datagen, metrics, budget_s=12.0):
     import oracle
     c = configs.QPROJ_DECODE
@@ -197,6 +234,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=100)
@@ -262,6 +300,23 @@ def main():
                          "traffic": None, "kernel": "lr_prefill_gemm_kernel (2 launches)",
                          "algorithmic_flops_per_step": p["flops"]},
         }
+    if not args.no_layer:
+        lay = {}
+        for M in configs.LAYER_M:
+            d_ = bench_layer(torch, lrl, configs, metrics, M, 200 if M <= 16 else 10, 20 if M <= 16 else 2)
+            log("layer M=%d: %.1f us/layer, %.3f TB/s, %.1f TFLOP/s (%d launches, %d weight copies)"
+                % (M, d_["ms"] * 1e3, d_["tbs"], d_["tflops"], d_["launches"], d_["copies"]))
+            if M <= 16:
+                lay["M%d" % M] = {"us_per_layer": round(d_["ms"] * 1e3, 2), "value": round(d_["tbs"], 4),
+                                  "unit": "TB/s", "roofline_frac_hbm": round(d_["tbs"] * 1e3 / HBM_PEAK_GBS, 4),
+                                  "algorithmic_bytes": d_["bytes"], "launches": d_["launches"],
+                                  "weight_copies": d_["copies"]}
+            else:
+                lay["M%d" % M] = {"us_per_layer": round(d_["ms"] * 1e3, 2), "value": round(d_["tflops"], 2),
+                                  "unit": "TFLOP/s", "roofline_frac_mfma": round(d_["tflops"] / BF16_PEAK_TFLOPS, 4),
+                                  "algorithmic_flops": d_["flops"], "launches": d_["launches"]}
+        result["layer"] = {"workload": "Llama-3-8B-shaped decoder layer: q,o 4096->4096 r1637; k,v 4096->1024 "
+                                       "r817; gate,up 4096->14336 r2867 (packed); down 14336->4096 r2867", **lay}
     if args.sweep:
         result["sweep"] = run_sweep(torch, lrl, configs, metrics, args.sweep_steps)
     if not args.no_cpu:
