@@ -200,31 +200,52 @@ def calib_copy(torch):
     log("calibration copy: 3 x %d bytes read and written" % nbytes)
 
 
-def run_sweep(torch, lrl, configs, metrics, steps):
-    """Throughput against rank (no-cliff check), printed as JSON lines on stderr."""
+def run_sweep(torch, lrl, configs, metrics, steps, stride=1):
+    """Throughput against rank at K = 4096 for both widths N and both M of
+    the alignment sweep (the no-cliff check).  Every point is printed as a
+    JSON line on stderr; the summary per (N, M) series goes into the result:
+    min / median / max, and the ranks whose throughput falls more than 10%
+    below the median of their +-8 neighbours (a cliff)."""
     rows = []
+    K = configs.SWEEP_K
     for N in configs.SWEEP_N:
-        for r in configs.SWEEP_R:
-            K = configs.SWEEP_K
+        for r in configs.SWEEP_R[::stride]:
             g = torch.Generator(device="cuda")
             g.manual_seed(configs.sweep_seed(N, r))
-            ncop = max(2, int(np.ceil((1 << 30) / (2 * (K * r + r * N)))))
+            wb = 2 * (K * r + r * N)
             A = (torch.randn((K, r), generator=g, device="cuda") / np.sqrt(K)).to(torch.bfloat16)
             B = (torch.randn((r, N), generator=g, device="cuda") / np.sqrt(r)).to(torch.bfloat16)
-            As = [A] + [A.clone() for _ in range(ncop - 1)]
-            Bs = [B] + [B.clone() for _ in range(ncop - 1)]
             for M in configs.SWEEP_M:
+                # decode streams >= 1 GiB of weight copies; prefill >= 256 MB
+                ncop = max(2, int(np.ceil(((1 << 30) if M <= 16 else (256 << 20)) / wb)))
+                As = [A] + [A.clone() for _ in range(ncop - 1)]
+                Bs = [B] + [B.clone() for _ in range(ncop - 1)]
                 X = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
                 Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
                 lins = [lrl.LowRankLinear(a, b, max_M=M) for a, b in zip(As, Bs)]
                 ms = time_steps(torch, lambda i: lins[i % ncop](X, out=Y), steps, 10, torch.cuda.current_stream())
-                row = dict(N=N, r=r, M=M, ms=ms, tbs=metrics.decode_bytes(M, K, r, N) / (ms * 1e-3) / 1e12,
-                           tflops=metrics.lowrank_flops(M, K, r, N) / (ms * 1e-3) / 1e12)
+                row = dict(N=N, r=r, M=M, us=round(ms * 1e3, 3),
+                           tbs=round(metrics.decode_bytes(M, K, r, N) / (ms * 1e-3) / 1e12, 4),
+                           tflops=round(metrics.lowrank_flops(M, K, r, N) / (ms * 1e-3) / 1e12, 2))
                 rows.append(row)
                 print(json.dumps({"sweep": row}), file=sys.stderr, flush=True)
-                del lins
-            del As, Bs
-    return rows
+                del lins, As, Bs
+            del A, B
+    summary = {}
+    for N in configs.SWEEP_N:
+        for M in configs.SWEEP_M:
+            ser = [x for x in rows if x["N"] == N and x["M"] == M]
+            key = "tbs" if M <= 16 else "tflops"
+            v = np.array([x[key] for x in ser])
+            cliffs = []
+            for i, x in enumerate(ser):
+                nb = np.concatenate([v[max(0, i - 8):i], v[i + 1:i + 9]])
+                if len(nb) and x[key] < 0.9 * np.median(nb):
+                    cliffs.append(x["r"])
+            summary["N%d_M%d" % (N, M)] = {"unit": "TB/s" if M <= 16 else "TFLOP/s", "points": len(ser),
+                                           "min": float(v.min()), "median": float(np.median(v)),
+                                           "max": float(v.max()), "cliff_ranks": cliffs}
+    return summary
 
 
 def main():
@@ -238,6 +259,7 @@ def main():
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=100)
+    ap.add_argument("--sweep-stride", type=int, default=1)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -318,7 +340,7 @@ def main():
         result["layer"] = {"workload": "Llama-3-8B-shaped decoder layer: q,o 4096->4096 r1637; k,v 4096->1024 "
                                        "r817; gate,up 4096->14336 r2867 (packed); down 14336->4096 r2867", **lay}
     if args.sweep:
-        result["sweep"] = run_sweep(torch, lrl, configs, metrics, args.sweep_steps)
+        result["sweep"] = run_sweep(torch, lrl, configs, metrics, args.sweep_steps, args.sweep_stride)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(configs, datagen, metrics)
     else:
