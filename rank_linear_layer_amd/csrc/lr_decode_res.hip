@@ -49,8 +49,11 @@ constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Weight and activation slabs are read once: non-temporal (streaming) loads,
+// so that the XCD's L2 keeps the small T partials the group exchanges
+// instead of the 4 MB per XCD of A and B passing through it.
 __device__ __forceinline__ void lds_load16(rsrc_t r, void* lds_base_wave, uint32_t gbyte_off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base_wave, 16, (int)gbyte_off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base_wave, 16, (int)gbyte_off, 0, 0, kSkipL1);
 }
 
 // Direct loads of `rows` runs of `cpr` 16-byte chunks into LDS slots
@@ -445,6 +448,7 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
 #define LR_G2(D) gemm2_wave<D>(ctx, thi, tlo, y0, y1)
   LR_LD8_SWITCH(N, LR_G2)
 #undef LR_G2
+  RES_TRACE(10);
   for (int ntl = 0; ntl < nt_cnt; ++ntl) {
     barrier_lds();  // previous tile's red reads (and the Ts reads) are done
 #pragma unroll
@@ -468,6 +472,7 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   // -------------------------------- Y reduce-scatter over the Jw slices --
   if (nt_cnt > 0) {
     wait_vmem_all();
+    RES_TRACE(11);
     barrier_lds();
     const uint32_t yflag_grp = P.off_yflag + (uint32_t)(s * P.Jw) * 4u;
     if (tid == 0) buf_store_u32_coherent(rW, yflag_grp + (uint32_t)js * 4u, epoch);
