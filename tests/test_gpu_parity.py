@@ -167,6 +167,29 @@ def test_forced_paths(M, K, r, N, flags):
     run_case(M, K, r, N, 4400 + M, flags=flags)
 
 
+# k-split prefill plans (fp32 partials + reduction kernel), including the
+# misaligned-X path (K mod 8 != 0), a ragged M and both tile widths
+@pytest.mark.parametrize("M,K,r,N", [(300, 4100, 100, 200), (257, 4096, 131, 999), (600, 2050, 77, 3001),
+                                     (33, 8192, 40, 64), (512, 1030, 250, 4100)])
+def test_prefill_k_split_plans(M, K, r, N):
+    p, lin, _, _ = run_case(M, K, r, N, 5100 + M + r)
+    banner("k-split case M=%d K=%d r=%d N=%d parity %s plan %s" % (M, K, r, N, p, lin.describe()))
+
+
+@pytest.mark.parametrize("M", [300])
+def test_mlp_packed_prefill_k_split(M):
+    # packed gate/up at a small M: the shared plan splits k for both outputs
+    K = 2048
+    Xb = datagen.normal_bf16((M, K), 1.0, 61)
+    _, Agb, Bgb = datagen.factorized_inputs(1, K, 203, 900, 71)
+    _, Aub, Bub = datagen.factorized_inputs(1, K, 150, 1300, 81)
+    gate = lrl.LowRankLinear(to_dev(Agb), to_dev(Bgb), max_M=M)
+    up = lrl.LowRankLinear(to_dev(Aub), to_dev(Bub), max_M=M)
+    Yg, Yu = lrl.mlp_packed(gate, up, to_dev(Xb))
+    assert_parity(to_bits(Yg), oracle.lowrank_bf16(Xb, Agb, Bgb), "packed k-split gate")
+    assert_parity(to_bits(Yu), oracle.lowrank_bf16(Xb, Aub, Bub), "packed k-split up")
+
+
 # ---------------------------------------------------------------- packed ---
 
 @pytest.mark.parametrize("M", [1, 4, 64])
