@@ -77,6 +77,11 @@ typedef struct lr_linear lr_linear;
 #define LR_FLAG_FORCE_PREFILL 2u  /* use the MFMA prefill kernels for every M */
 #define LR_FLAG_DECODE_STREAMING 4u  /* decode with the register-streaming kernel even where the
                                         LDS-resident one applies (both compute the same result) */
+#define LR_FLAG_PREFILL_TWO_WAVE 8u  /* prefill only with the two-waves-per-SIMD kernel (tiles of
+                                        256 x 192 or 224) instead of the cost model's choice */
+#define LR_FLAG_PREFILL_ONE_WAVE 16u /* prefill with the one-wave-per-SIMD kernel (256 x 256 tiles)
+                                        wherever it applies: X, or T, rows 16-byte aligned, and the
+                                        same leading dimension mod 8 for both factors of a pair */
 
 /* Largest M that the fused decode kernel takes (more rows use prefill). */
 #define LR_DECODE_MAX_M 16

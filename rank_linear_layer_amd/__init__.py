@@ -29,6 +29,8 @@ LR_FLAG_NONE = 0
 LR_FLAG_FORCE_DECODE = 1
 LR_FLAG_FORCE_PREFILL = 2
 LR_FLAG_DECODE_STREAMING = 4
+LR_FLAG_PREFILL_TWO_WAVE = 8
+LR_FLAG_PREFILL_ONE_WAVE = 16
 LR_DECODE_MAX_M = 16
 
 EXPORTED_SYMBOLS = (

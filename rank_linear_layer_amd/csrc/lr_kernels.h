@@ -115,6 +115,9 @@ struct PreArgs {
   PreOut o[2];
 };
 hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream);
+// One wave per SIMD, 256 x 256 tiles, for a 16-byte aligned P (nb = 8, even
+// split_steps, equal weight leading dimensions mod 8 across outputs).
+hipError_t launch_prefill_w4(const PreArgs& args, hipStream_t stream);
 // C[rows x cols] = bf16(sum of `splits` fp32 partials, in split order).
 hipError_t launch_prefill_reduce(const float* part, int splits, int64_t rows, int64_t cols, int64_t ldpart,
                                  uint16_t* C, int64_t ldc, hipStream_t stream);

@@ -67,6 +67,8 @@ struct lr_linear {
   uint16_t* Tbuf;
   float* part;
   int64_t part_bytes;
+  // plan of the last prefill call per phase: kernel kind, nb, splits (reported by describe)
+  mutable std::atomic<int> last_plan[2][3];
 };
 
 namespace {
@@ -158,15 +160,31 @@ lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, con
 
 // One prefill phase: C_i = P_i . Q_i for the n outputs, then the k-split
 // reduction if the plan splits k.
-lr_status prefill_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, int64_t kd, hipStream_t stream,
-                        const char* what) {
+lr_status prefill_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, int64_t kd, int phase,
+                        hipStream_t stream, const char* what) {
   const int cus = num_cus(hs[0]->device);
   int64_t cols[2] = {0, 0};
   for (int i = 0; i < n; ++i) cols[i] = a.o[i].out_cols;
-  lrv::PrePlan pl = lrv::prefill_plan(a.rows, cols, n, kd, cus);
+  // the one-wave-per-SIMD kernel loads P straight into LDS (16-byte aligned
+  // rows only) and is specialised on the weight leading dimension mod 8
+  bool w4 = true;
+  for (int i = 0; i < n; ++i)
+    w4 = w4 && a.o[i].ldp % 8 == 0 && reinterpret_cast<uintptr_t>(a.o[i].P) % 16 == 0 &&
+         a.o[i].ldq % 8 == a.o[0].ldq % 8;
+  const uint32_t fl = hs[0]->flags;
+  int kinds = lrv::kPlanTwoWave | (w4 ? lrv::kPlanOneWave : 0);
+  if (fl & LR_FLAG_PREFILL_TWO_WAVE) kinds = lrv::kPlanTwoWave;
+  if ((fl & LR_FLAG_PREFILL_ONE_WAVE) && w4) kinds = lrv::kPlanOneWave;
+  const bool q_aligned = a.o[0].ldq % 8 == 0;
+  lrv::PrePlan pl = lrv::prefill_plan(a.rows, cols, n, kd, cus, 32, kinds, q_aligned);
   for (int i = 0; i < n && pl.splits > 1; ++i) {
     const int64_t need = (int64_t)pl.splits * a.rows * lrv::round_up(cols[i], 4) * 4;
-    if (need > hs[i]->part_bytes) pl = lrv::prefill_plan(a.rows, cols, n, kd, cus, 1);
+    if (need > hs[i]->part_bytes) pl = lrv::prefill_plan(a.rows, cols, n, kd, cus, 1, kinds, q_aligned);
+  }
+  for (int i = 0; i < n; ++i) {
+    hs[i]->last_plan[phase][0] = pl.kind;
+    hs[i]->last_plan[phase][1] = pl.nb;
+    hs[i]->last_plan[phase][2] = pl.splits;
   }
   a.nb = pl.nb;
   a.splits = pl.splits;
@@ -176,7 +194,7 @@ lr_status prefill_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, int6
     a.o[i].part = hs[i]->part;
     a.o[i].ldpart = lrv::round_up(cols[i], 4);
   }
-  hipError_t e = lrk::launch_prefill_gemm(a, stream);
+  hipError_t e = pl.kind == 1 ? lrk::launch_prefill_w4(a, stream) : lrk::launch_prefill_gemm(a, stream);
   if (e != hipSuccess) return hip_fail(e, what);
   if (pl.splits > 1) {
     for (int i = 0; i < n; ++i) {
@@ -209,7 +227,7 @@ lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, co
     o.ldc = h->r_pad;
     o.out_cols = h->r_pad;
   }
-  lr_status st = prefill_phase(hs, a1, n, hs[0]->K, stream, "prefill phase-1 launch");
+  lr_status st = prefill_phase(hs, a1, n, hs[0]->K, 0, stream, "prefill phase-1 launch");
   if (st != LR_OK) return st;
   // phase 2: Y_i = T_i . B_i
   lrk::PreArgs a2;
@@ -232,7 +250,7 @@ lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, co
     o.out_cols = h->N;
     kd2 = kd2 > h->r_pad ? kd2 : h->r_pad;
   }
-  return prefill_phase(hs, a2, n, kd2, stream, "prefill phase-2 launch");
+  return prefill_phase(hs, a2, n, kd2, 1, stream, "prefill phase-2 launch");
 }
 
 }  // namespace
@@ -272,6 +290,8 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
   if (!h) return fail(LR_ERR_OUT_OF_MEMORY, "host allocation failed");
   memset((void*)h, 0, sizeof *h);
   h->epoch.store(0u);
+  for (auto& ph : h->last_plan)
+    for (auto& v : ph) v.store(-1);
   h->K = K;
   h->r = r;
   h->N = N;
@@ -416,10 +436,12 @@ lr_status lr_linear_describe(const lr_linear* h, char* buf, int64_t len) {
   if (!h || !buf || len <= 0) return fail(LR_ERR_INVALID_ARG, "null handle or buffer");
   snprintf(buf, (size_t)len,
            "K=%lld r=%lld N=%lld r_pad=%lld max_M=%lld decode=%d[kind=%s Jw=%d JS=%d S=%d ktps=%d ntps=%d grid=%d] "
-           "xcd_local=%d prefill=%d workspace=%zu",
+           "xcd_local=%d prefill=%d[last phase1 kind=%d nb=%d splits=%d, phase2 kind=%d nb=%d splits=%d] "
+           "workspace=%zu",
            (long long)h->K, (long long)h->r, (long long)h->N, (long long)h->r_pad, (long long)h->max_M,
            (int)h->has_decode, h->dp.kind == 1 ? "resident" : "streaming", h->dp.Jw, h->dp.js_w, h->dp.S, h->dp.ktps, h->dp.ntps, h->dp.Jw * h->dp.S, (int)h->xcd_local, (int)h->has_prefill,
-           h->ws_bytes);
+           h->last_plan[0][0].load(), h->last_plan[0][1].load(), h->last_plan[0][2].load(), h->last_plan[1][0].load(),
+           h->last_plan[1][1].load(), h->last_plan[1][2].load(), h->ws_bytes);
   return LR_OK;
 }
 

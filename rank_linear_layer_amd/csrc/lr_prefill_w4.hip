@@ -1,0 +1,488 @@
+// Prefill GEMM with one wave per SIMD and 128 x 128 wave tiles (M > 16,
+// 16-byte aligned P).
+//
+// Same product, phases and tile walk as lr_prefill.hip (phase 1 T = X . A
+// with the rank padded on chip, phase 2 Y = T . B; k-split partials), laid
+// out for the way gfx950 moves data:
+//  * L2 -> LDS loads run at full rate only when each instruction covers
+//    whole 128-byte lines.  A k-stage is therefore 64 deep, so one row of P
+//    is exactly one line; a direct-to-LDS load of 8 rows x 128 B fills the
+//    P slot with an XOR swizzle (chunk c of row R at position
+//    8 R + (c ^ ((R / 2) mod 8))) that keeps the MFMA operand reads free of
+//    bank conflicts.
+//  * The weight operand (A or B, output index contiguous) is read with
+//    aligned 16-byte loads into registers: lanes 0-31 take 32 consecutive
+//    chunks of one row, lanes 32-63 the same chunks 8 rows further.  A row
+//    that starts d elements past a 16-byte boundary (odd rank or width) is
+//    realigned in registers with the neighbouring lane's chunk (DPP wave
+//    shift) and a byte funnel shift; d depends only on the row modulo 8 and
+//    on the leading dimension modulo 8, which is a template argument.  Each
+//    lane then transposes its 8 rows x 8 columns block with v_perm_b32 and
+//    writes 8 operand vectors (8 k of one column) into the Qt slot, whose
+//    16-column groups are XOR-permuted so that both these writes and the
+//    MFMA reads are conflict free.
+//  * Four waves, one per SIMD, each own a 128 x 128 quarter of the 256 x 256
+//    tile: 16 v_mfma_f32_32x32x16_bf16 accumulators (256 AGPRs), the largest
+//    wave tile the register file holds, which minimises LDS operand traffic
+//    per flop.
+//
+// LDS holds three P slots and two Qt slots (160 KB).  P of stage s + 3 is
+// requested after the barrier of stage s (two stages to arrive), the weight
+// rows of stage s + 2 at the start of stage s into one of two register sets
+// (a little over one stage).  The cost per 64-deep stage measured on MI355X
+// is about 3600 cycles for 64 MFMAs of 32 cycles each; the plan picks this
+// kernel where its 256-wide tiles make that cheaper than the two-wave one.
+#include "lr_device.h"
+#include "lr_kernels.h"
+
+namespace lrk {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBM = 256;
+constexpr int kBN = 256;
+constexpr int kPSlot = kBM * 64 * 2;   // 32 KB: 256 rows x 64 k
+constexpr int kQtSlot = kBN * 64 * 2;  // 32 KB: 256 columns x 64 k
+constexpr int kStageChunks = kBN / 8 + 1;  // staged output row: 256 columns + room for misalignment
+constexpr int kStageRowBytes = kStageChunks * 16;
+constexpr int kGroupRows = 4;
+constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
+
+constexpr int kPSlots = 3;
+constexpr int kQtBase = kPSlots * kPSlot;
+// three P slots and two Qt slots (160 KB); the epilogue stages the bf16 tile in the same memory
+constexpr int kLdsBytes = kQtBase + 2 * kQtSlot > kBM * kStageRowBytes ? kQtBase + 2 * kQtSlot : kBM * kStageRowBytes;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ u32x4_t lds_read16(const char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void lds_write16(char* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Misalignment (elements) of weight row i of an 8-row group when the leading
+// dimension is QMOD modulo 8 (the group's first row and the tile's first
+// column are multiples of 8).
+__host__ __device__ constexpr int row_shift(int qmod, int i) { return (i * qmod) & 7; }
+template <int QMOD>
+__host__ __device__ constexpr int extra_loads() {
+  int n = 0;
+  for (int i = 0; i < 8; ++i) n += row_shift(QMOD, i) != 0;
+  return n;
+}
+
+// 16-column groups of Qt are permuted: column n sits at entry pos(n).
+__device__ __forceinline__ int qt_pos(int n) { return (n & ~15) | ((n & 15) ^ ((n >> 4) & 15)); }
+
+struct Tile {
+  int bi;
+  int64_t mb, nb;
+};
+
+// Tiles are dealt so that each XCD (workgroup id mod 8) gets one contiguous
+// run of the tile order, which walks groups of four row tiles column by
+// column: the workgroups on one XCD share P and weight panels in its L2.
+__device__ __forceinline__ Tile map_tile(const PreArgs& a, int bid) {
+  const int ct_total = a.o[0].col_tiles + (a.nout > 1 ? a.o[1].col_tiles : 0);
+  const int total = a.row_tiles * ct_total;
+  const int q = total >> 3, rem = total & 7;
+  const int x = bid & 7, j = bid >> 3;
+  const int t = x * q + min(x, rem) + j;
+  const int per_group = kGroupRows * ct_total;
+  const int grp = t / per_group;
+  const int first = grp * kGroupRows;
+  const int gs = min(kGroupRows, a.row_tiles - first);
+  const int within = t - grp * per_group;
+  const int rt = first + within % gs;
+  int ct = within / gs;
+  Tile T;
+  T.bi = 0;
+  if (a.nout > 1 && ct >= a.o[0].col_tiles) {
+    T.bi = 1;
+    ct -= a.o[0].col_tiles;
+  }
+  T.mb = (int64_t)rt * kBM;
+  T.nb = (int64_t)ct * kBN;
+  return T;
+}
+
+// Chunk j of a weight row and the following chunk (the next lane's, or `x`
+// for the last lane of each half), shifted down by d elements (d is a
+// constant after unrolling).
+__device__ __forceinline__ u32x4_t realign(const u32x4_t& lo, const u32x4_t& x, bool last, int d) {
+  if (d == 0) return lo;
+  const int q = d >> 1;
+  uint32_t cat[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    cat[t] = lo[t];
+    if (t <= q) {
+      const uint32_t nx = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo[t], 0x130, 0xf, 0xf, false);  // wave_shl:1
+      cat[4 + t] = last ? x[t] : nx;
+    } else {
+      cat[4 + t] = 0u;
+    }
+  }
+  u32x4_t o;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) o[t] = (d & 1) ? __builtin_amdgcn_alignbyte(cat[t + q + 1], cat[t + q], 2) : cat[t + q];
+  return o;
+}
+
+template <int QMOD, bool MASK>
+__device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks, char* smem) {
+  constexpr int NX = extra_loads<QMOD>();
+  constexpr int NQ = 8 + NX;  // register loads per stage
+  const PreOut& O = a.o[T.bi];
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  const int wm = w & 1, wn = w >> 1;
+  const int L = l & 31, gL = l >> 5;
+  const rsrc_t rP = make_rsrc(O.P, a.rows * O.ldp * 2);
+  const rsrc_t rQ = make_rsrc(O.Q, O.qrows * O.ldq * 2);
+  const int qcols = (int)min64((int64_t)kBN, O.ldq - T.nb);
+
+  const int nks_all = (int)((O.kd + 31) / 32);
+  const int s0 = ks * a.split_steps;  // even: splits start on a 64-deep stage
+  const int nk = max(0, min(nks_all - s0, a.split_steps));
+  const int nst = (nk + 1) >> 1;
+  const int64_t k0 = (int64_t)s0 * 32;
+
+  // ---- P direct loads: instruction i of wave w fills tile rows 8 (8w + i) .. +7;
+  // lane l takes row R = 8 (8w + i) + l / 8, chunk (l % 8) ^ ((R / 2) % 8), which
+  // depends on i only through i % 2
+  int p_c[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) p_c[h] = (l & 7) ^ ((4 * h + (l >> 4)) & 7);
+  const uint32_t p_base = (uint32_t)(((T.mb + 64 * w + (l >> 3)) * O.ldp + k0) * 2);
+  const uint32_t p_rows8 = (uint32_t)(16 * O.ldp);  // 8 rows
+  // instruction i of this wave's eight for stage st into P slot `slot`
+  auto p_issue_one = [&](char* slot, int st, int i) {
+    const bool ok = k0 + 8 * p_c[i & 1] + 64 * (int64_t)st < O.kd;
+    const uint32_t off = p_base + p_rows8 * (uint32_t)i + 16u * (uint32_t)p_c[i & 1] + 128u * (uint32_t)st;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(slot + (8 * w + i) * 1024), 16,
+                                             (int)(ok ? off : kOutOfRange), 0, 0, 0);
+  };
+  auto p_issue = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p_issue_one(smem + (st % kPSlots) * kPSlot, st, i);
+  };
+
+  // ---- weight rows: lane (L, gL) loads chunk L of rows row0 + i (i < 8),
+  // row0 = k0 + 16w + 8gL; row0 * ldq + nb is a multiple of 8, so row i's
+  // first chunk is that of row 0 plus floor(i * ldq / 8)
+  const int64_t row0 = k0 + 16 * w + 8 * gL;
+  const uint32_t q_base = (uint32_t)(2 * (row0 * O.ldq + T.nb) + 16 * L);
+  const uint32_t q_stride = (uint32_t)(128 * O.ldq);  // 64 rows
+  // Two register sets for the weight rows alternate between stages (rows of
+  // stage s + 1 are realigned from one while the rows of stage s + 2 arrive
+  // in the other), so no loaded register is ever copied or reused while its
+  // load is in flight.  The chunk after a misaligned row is fetched with only
+  // the dwords the funnel shift reads.
+  struct QRegs {
+    u32x4_t v[8], x[8];
+  };
+  QRegs qa, qb;
+  auto q_row_off = [&](int i, int st, bool& ok) {
+    ok = row0 + 64 * (int64_t)st + i < O.qrows;
+    return q_base + q_stride * (uint32_t)st + 16u * (uint32_t)((i * O.ldq) >> 3);
+  };
+  auto q_issue_row_main = [&](QRegs& q, int i, int st) {
+    bool ok;
+    const uint32_t off = q_row_off(i, st, ok);
+    q.v[i] = buf_load16(rQ, ok ? off : kOutOfRange);
+  };
+  auto q_issue_row_extra = [&](QRegs& q, int i, int st) {
+    const int d = row_shift(QMOD, i);
+    if (d == 0) return;
+    bool ok;
+    const uint32_t xo = q_row_off(i, st, ok) + 16u;
+    const uint32_t xoff = ok && L == 31 ? xo : kOutOfRange;
+    const int n = (d >> 1) + 1;  // dwords of the next chunk the shift reads
+    u32x4_t x = zerou4();
+    if (n == 1) {
+      x[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rQ, (int)xoff, 0, 0);
+    } else if (n == 2) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(rQ, (int)xoff, 0, 0);
+      x[0] = t[0];
+      x[1] = t[1];
+    } else if (n == 3) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b96(rQ, (int)xoff, 0, 0);
+      x[0] = t[0];
+      x[1] = t[1];
+      x[2] = t[2];
+    } else {
+      x = buf_load16(rQ, xoff);
+    }
+    q.x[i] = x;
+  };
+  auto q_issue_row = [&](QRegs& q, int i, int st) {
+    q_issue_row_main(q, i, st);
+    q_issue_row_extra(q, i, st);
+  };
+  auto q_issue = [&](QRegs& q, int st) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q_issue_row(q, i, st);
+  };
+  // write offsets into Qt for this lane's 8 columns 8L + e
+  const int qt_c = 2 * w + gL;
+  const int m7 = (L >> 1) & 7;
+  const int qt_w0 = qt_c * 4096 + 16 * (16 * (L >> 1) + ((8 * (L & 1)) ^ (((L >> 1) & 15) & 8)));
+  u32x4_t r[8];
+  auto q_realign_row = [&](const QRegs& q, int i) { r[i] = realign(q.v[i], q.x[i], L == 31, row_shift(QMOD, i)); };
+  // column e of the lane's block: 8 k of column 8L + e, into Qt slot `qt`
+  auto q_store_col = [&](int e, char* qt) {
+    const int t = e >> 1;
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    u32x4_t o;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = __builtin_amdgcn_perm(r[2 * u + 1][t], r[2 * u][t], sel);
+    if (MASK && 8 * L + e >= qcols) o = zerou4();  // last column tile: columns past the matrix read as zero
+    lds_write16(qt + qt_w0 + 16 * (e ^ m7), o);
+  };
+  auto q_store = [&](const QRegs& q, int st) {
+    char* qt = smem + kQtBase + (st & 1) * kQtSlot;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q_realign_row(q, i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q_store_col(e, qt);
+  };
+
+  // ---- MFMA operand addresses
+  const int xr = (L >> 1) & 7;
+  const int y = gL ^ xr;
+  const int a_base = 128 * (128 * wm + L);  // + rb * 4096 + 16 (2kk ^ y)
+  int b_base[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) b_base[cb] = gL * 4096 + 16 * qt_pos(128 * wn + 32 * cb + L);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  auto rd = [&](const char* ps, const char* qs, int kk, u32x4_t(&A)[4], u32x4_t(&B)[4]) {
+    const int ao = a_base + 16 * ((2 * kk) ^ y);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) A[rb] = lds_read16(ps + ao + rb * 4096);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) B[cb] = lds_read16(qs + b_base[cb] + kk * 8192);
+  };
+  // MFMAs 2j and 2j + 1 of a k16 block (row block j / 2, column blocks 2 (j % 2) + 0, 1)
+  // MFMA i of a k16 block: row block i / 4, column block i % 4
+  auto mf1 = [&](const u32x4_t(&A)[4], const u32x4_t(&B)[4], int i) {
+    acc[i >> 2][i & 3] = mfma32(A[i >> 2], B[i & 3], acc[i >> 2][i & 3]);
+  };
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto pslot = [&](int st) { return smem + (st % kPSlots) * kPSlot; };
+  auto qtslot = [&](int st) { return smem + kQtBase + (st & 1) * kQtSlot; };
+
+  // ---- prologue: P of stages 0-2 requested, the weight rows of stage 0 in
+  // Qt, the rows of stage 1 requested, P of stage 0 landed, the operands of
+  // the first k16 block of stage 0 read
+  u32x4_t A0[4], B0[4], A1[4], B1[4];
+  q_issue(qb, 0);
+  p_issue(0);
+  p_issue(1);
+  p_issue(2);
+  q_store(qb, 0);
+  q_issue(qa, 1);
+  wait_vm<16 + NQ>();
+  barrier_lds();
+  rd(pslot(0), qtslot(0), 0, A0, B0);
+
+  // Stage s multiplies four k16 blocks (M0..M3, 16 MFMAs each) from two
+  // operand register sets: the operands of a block are read while the block
+  // before it runs, and the first block's operands are read at the end of the
+  // previous stage, so no stage starts by waiting for LDS.  The other work
+  // is placed after single MFMAs (each keeps the matrix core busy for about
+  // 32 cycles): during M0 the weight rows of stage s + 2 are requested into
+  // the register set stage s - 1 emptied; during M1 the rows of stage s + 1
+  // (requested during stage s - 1) are realigned and transposed into Qt of
+  // s + 1; the one barrier of the
+  // stage sits four MFMAs into M2, after the last LDS read of the stage's P
+  // slot, and is followed by the request of P for stage s + 3 into that
+  // slot.  sched_barrier fences keep this order: on each SIMD this one wave
+  // is all there is to keep the matrix core busy.  Requests past the last
+  // stage land in slots no later stage reads.
+  auto stage = [&](int s, const QRegs& qin, QRegs& qout) {
+    const char* ps = pslot(s);
+    const char* qs = qtslot(s);
+    char* qt_next = smem + kQtBase + ((s + 1) & 1) * kQtSlot;
+    rd(ps, qs, 1, A1, B1);
+    fence();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mf1(A0, B0, i);
+      fence();
+      if ((i & 1) == 0)
+        q_issue_row_main(qout, i >> 1, s + 2);
+      else
+        q_issue_row_extra(qout, i >> 1, s + 2);
+      fence();
+    }
+    rd(ps, qs, 2, A0, B0);
+    fence();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mf1(A1, B1, i);
+      fence();
+      if (i < 8)
+        q_realign_row(qin, i);
+      else
+        q_store_col(i - 8, qt_next);
+      fence();
+    }
+    rd(ps, qs, 3, A1, B1);
+    fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mf1(A0, B0, i);
+      fence();
+    }
+    // P of stage s + 1 must have landed (P of s + 2 and the weight rows of
+    // s + 2 may stay in flight); after the barrier every wave has read this
+    // stage's P slot and written Qt of s + 1
+    wait_vm<8 + NQ>();
+    barrier_lds();
+    char* pnext = smem + (s % kPSlots) * kPSlot;  // slot of stage s + 3
+    const int st3 = s + 3;
+#pragma unroll
+    for (int i = 4; i < 16; ++i) {
+      mf1(A0, B0, i);
+      fence();
+      if (i >= 8) p_issue_one(pnext, st3, i - 8);
+      fence();
+    }
+    rd(pslot(s + 1), qt_next, 0, A0, B0);
+    fence();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mf1(A1, B1, i);
+      fence();
+    }
+  };
+  for (int s = 0; s < nst; s += 2) {
+    stage(s, qa, qb);
+    if (s + 1 < nst) stage(s + 1, qb, qa);
+  }
+  wait_vm<0>();
+  barrier_lds();
+
+  // ------------------------------------------------------------ epilogue --
+  // acc[rb][cb] lane l, register 4b + t: row 8b + 4 gL + t of 32-row block
+  // 4 wm + rb, column L of 32-column block 4 wn + cb.
+  if (a.splits > 1) {
+    float* part = O.part + (int64_t)ks * a.rows * O.ldpart;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t m = T.mb + 128 * wm + 32 * rb + 8 * (e >> 2) + 4 * gL + (e & 3);
+          const int64_t n = T.nb + 128 * wn + 32 * cb + L;
+          if (m < a.rows && n < O.out_cols) part[m * O.ldpart + n] = acc[rb][cb][e];
+        }
+    return;
+  }
+  const int64_t ldc = O.ldc;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = 128 * wm + 32 * rb + 8 * (e >> 2) + 4 * gL + (e & 3);
+      const int d = (int)(((T.mb + m) * ldc + T.nb) & 7);
+      uint16_t* row = reinterpret_cast<uint16_t*>(smem + m * kStageRowBytes) + d + 128 * wn + L;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) row[32 * cb] = (uint16_t)f32_to_bf16_rne(acc[rb][cb][e]);
+    }
+  barrier_lds();
+  const rsrc_t rC = make_rsrc(O.C, a.rows * ldc * 2);
+  const int ncols = (int)min64((int64_t)kBN, O.out_cols - T.nb);
+  constexpr int nitems = kBM * kStageChunks;
+  for (int item = threadIdx.x; item < nitems; item += kThreads) {
+    const int m = item / kStageChunks, k = item - m * kStageChunks;
+    const int64_t R = T.mb + m;
+    if (R >= a.rows) continue;
+    const int d = (int)((R * ldc + T.nb) & 7);
+    const int n0 = 8 * k - d;
+    if (n0 >= ncols) continue;
+    const u32x4_t v = lds_read16(smem + m * kStageRowBytes + 16 * k);
+    const int64_t e0 = R * ldc + T.nb + n0;
+    if (n0 >= 0 && n0 + 8 <= ncols) {
+      __builtin_amdgcn_raw_buffer_store_b128(v, rC, (int)(e0 * 2), 0, 0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int n = n0 + e;
+        if (n >= 0 && n < ncols)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(v[e >> 1] >> (16 * (e & 1))), rC, (int)((e0 + e) * 2), 0,
+                                                0);
+      }
+    }
+  }
+}
+
+template <int QMOD>
+__global__ __launch_bounds__(kThreads, 1) void lr_prefill_w4_kernel(const PreArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tiles = a.row_tiles * (a.o[0].col_tiles + (a.nout > 1 ? a.o[1].col_tiles : 0));
+  const int ks = (int)blockIdx.x / tiles;
+  const Tile T = map_tile(a, (int)blockIdx.x - ks * tiles);
+  if (a.o[T.bi].ldq - T.nb < kBN)
+    w4_tile<QMOD, true>(a, T, ks, smem);
+  else
+    w4_tile<QMOD, false>(a, T, ks, smem);
+}
+
+template <int QMOD>
+hipError_t launch_w4(const PreArgs& args, int grid, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)lr_prefill_w4_kernel<QMOD>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((lr_prefill_w4_kernel<QMOD>), dim3(grid), dim3(kThreads), kLdsBytes, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_w4(const PreArgs& args, hipStream_t stream) {
+  const int ct = args.o[0].col_tiles + (args.nout > 1 ? args.o[1].col_tiles : 0);
+  const int grid = ct * args.row_tiles * args.splits;
+  if (grid <= 0) return hipSuccess;
+  if (args.nb != 8 || args.split_steps % 2 != 0) return hipErrorInvalidValue;
+  const int qmod = (int)(args.o[0].ldq & 7);
+  if (args.nout > 1 && (int)(args.o[1].ldq & 7) != qmod) return hipErrorInvalidValue;
+  switch (qmod) {
+    case 0: return launch_w4<0>(args, grid, stream);
+    case 1: return launch_w4<1>(args, grid, stream);
+    case 2: return launch_w4<2>(args, grid, stream);
+    case 3: return launch_w4<3>(args, grid, stream);
+    case 4: return launch_w4<4>(args, grid, stream);
+    case 5: return launch_w4<5>(args, grid, stream);
+    case 6: return launch_w4<6>(args, grid, stream);
+    default: return launch_w4<7>(args, grid, stream);
+  }
+}
+
+}  // namespace lrk

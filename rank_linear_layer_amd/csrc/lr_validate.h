@@ -47,10 +47,15 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
     snprintf(err, errlen, "a matrix would exceed 2 GiB (32-bit buffer addressing)");
     return LR_ERR_UNSUPPORTED;
   }
-  const uint32_t known = LR_FLAG_FORCE_DECODE | LR_FLAG_FORCE_PREFILL | LR_FLAG_DECODE_STREAMING;
+  const uint32_t known = LR_FLAG_FORCE_DECODE | LR_FLAG_FORCE_PREFILL | LR_FLAG_DECODE_STREAMING |
+                         LR_FLAG_PREFILL_TWO_WAVE | LR_FLAG_PREFILL_ONE_WAVE;
   if (flags & ~known) { snprintf(err, errlen, "unknown flag bits 0x%x", flags & ~known); return LR_ERR_UNSUPPORTED; }
   if ((flags & LR_FLAG_FORCE_DECODE) && (flags & LR_FLAG_FORCE_PREFILL)) {
     snprintf(err, errlen, "FORCE_DECODE and FORCE_PREFILL are exclusive");
+    return LR_ERR_INVALID_ARG;
+  }
+  if ((flags & LR_FLAG_PREFILL_TWO_WAVE) && (flags & LR_FLAG_PREFILL_ONE_WAVE)) {
+    snprintf(err, errlen, "PREFILL_TWO_WAVE and PREFILL_ONE_WAVE are exclusive");
     return LR_ERR_INVALID_ARG;
   }
   if ((flags & LR_FLAG_FORCE_DECODE) && max_M > kDecodeMaxM) {
@@ -190,29 +195,49 @@ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // cheapest plan wins (fewer splits, then the wider tile, on a tie).
 struct PrePlan {
   int nb, splits, split_steps;
+  int kind;  // 0: two waves per SIMD, tile 256 x 32 nb; 1: one wave per SIMD, tile 256 x 256
 };
+// Kernel, tile width and k-split for one prefill phase, from a cost model in
+// units of one 32-deep k-step of one tile (about 0.14 us on MI355X): rounds
+// of the 256-CU machine times steps per tile times the per-step cost of the
+// kernel, plus the partial write/read and reduction launch when k is split.
+// Measured per-step costs: two-wave kernel nb + 2 (nb = 6, 7); one-wave
+// kernel (256 x 256) 7.6 when the weight leading dimension is a multiple of
+// 8, 9.0 otherwise (the rows are realigned in registers); its k-splits start
+// on 64-deep stages.  `kinds`: bit 0 allows the two-wave kernel, bit 1 the
+// one-wave kernel (which needs a 16-byte aligned P).
+constexpr int kPlanTwoWave = 1;
+constexpr int kPlanOneWave = 2;
 inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int64_t kd, int num_cus,
-                            int max_splits = 32) {
+                            int max_splits = 32, int kinds_allowed = kPlanTwoWave, bool q_aligned = false) {
   const int64_t row_tiles = ceil_div(rows, 256);
   const int64_t nks = ceil_div(kd, 32);
   const int cus = num_cus > 0 ? num_cus : 1;
   int64_t cols = 0;
   for (int i = 0; i < nout; ++i) cols += out_cols[i];
-  PrePlan best{7, 1, (int)nks};
+  PrePlan best{7, 1, (int)nks, 0};
   double best_cost = -1;
-  for (int nb = 7; nb >= 6; --nb) {
+  const struct {
+    int nb, kind;
+    double per_step;
+  } kinds[3] = {{8, 1, q_aligned ? 7.6 : 9.0}, {7, 0, 9.0}, {6, 0, 8.0}};
+  for (const auto& kn : kinds) {
+    if (!(kinds_allowed & (kn.kind == 1 ? kPlanOneWave : kPlanTwoWave))) continue;
+    const int gran = kn.kind == 1 ? 2 : 1;
+    const int64_t units = ceil_div(nks, gran);
     int64_t tiles = 0;
-    for (int i = 0; i < nout; ++i) tiles += row_tiles * ceil_div(out_cols[i], 32 * nb);
-    for (int64_t want = 1; want <= max_splits && want <= nks; ++want) {
-      const int64_t steps = ceil_div(nks, want);
-      const int64_t splits = ceil_div(nks, steps);  // no empty split
+    for (int i = 0; i < nout; ++i) tiles += row_tiles * ceil_div(out_cols[i], 32 * kn.nb);
+    for (int64_t want = 1; want <= max_splits && want <= units; ++want) {
+      const int64_t per = ceil_div(units, want);
+      const int64_t splits = ceil_div(units, per);  // no empty split
       if (splits != want) continue;
+      const int64_t steps = per * gran;
       const int64_t rounds = ceil_div(tiles * splits, cus);
-      double cost = (double)(rounds * steps * (nb + 2));
+      double cost = (double)(rounds * steps) * kn.per_step;
       if (splits > 1) cost += 14.0 + (double)(2 * splits * rows * cols * 4 + rows * cols * 2) / 700e3;
       if (best_cost < 0 || cost < best_cost - 1e-9) {
         best_cost = cost;
-        best = PrePlan{nb, (int)splits, (int)steps};
+        best = PrePlan{kn.nb, (int)splits, (int)steps, kn.kind};
       }
     }
   }
@@ -222,15 +247,25 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
 // fp32 partial bytes a handle needs for its own output over every M <= max_M
 // (both phases share the region; M steps of 256 change the tiling).
 inline int64_t prefill_partial_bytes(int64_t max_M, int64_t K, int64_t r_pad, int64_t N, int num_cus) {
+  // Within one 256-row bucket the tiling is fixed and larger M only makes
+  // splitting costlier, so the split count at the bucket's smallest M times
+  // its largest M bounds every M in the bucket.
   int64_t need = 0;
   for (int64_t m = 256;; m += 256) {
-    const int64_t M = m < max_M ? m : max_M;
+    const int64_t hi = m < max_M ? m : max_M;
+    const int64_t lo = m - 255 < hi ? m - 255 : hi;
     const int64_t c1 = r_pad, c2 = N;
-    const PrePlan p1 = prefill_plan(M, &c1, 1, K, num_cus);
-    const PrePlan p2 = prefill_plan(M, &c2, 1, r_pad, num_cus);
-    if (p1.splits > 1) need = need > p1.splits * M * round_up(c1, 4) * 4 ? need : p1.splits * M * round_up(c1, 4) * 4;
-    if (p2.splits > 1) need = need > p2.splits * M * round_up(c2, 4) * 4 ? need : p2.splits * M * round_up(c2, 4) * 4;
-    if (M == max_M) break;
+    for (int kinds = 1; kinds <= 3; ++kinds) {
+      for (int qa = 0; qa < 2; ++qa) {
+        const PrePlan p1 = prefill_plan(lo, &c1, 1, K, num_cus, 32, kinds, qa != 0);
+        const PrePlan p2 = prefill_plan(lo, &c2, 1, r_pad, num_cus, 32, kinds, qa != 0);
+        const int64_t n1 = p1.splits > 1 ? p1.splits * hi * round_up(c1, 4) * 4 : 0;
+        const int64_t n2 = p2.splits > 1 ? p2.splits * hi * round_up(c2, 4) * 4 : 0;
+        need = need > n1 ? need : n1;
+        need = need > n2 ? need : n2;
+      }
+    }
+    if (hi == max_M) break;
   }
   return need;
 }

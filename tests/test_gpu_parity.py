@@ -190,6 +190,54 @@ def test_mlp_packed_prefill_k_split(M):
     assert_parity(to_bits(Yu), oracle.lowrank_bf16(Xb, Aub, Bub), "packed k-split up")
 
 
+# ------------------------------------------------- prefill kernel kinds ---
+# Each prefill kernel forced on its own: the two-wave kernel (256 x 192 or
+# 224 tiles, 2-byte LDS gather) and the one-wave kernel (256 x 256 tiles,
+# weight rows realigned in registers, specialised on the weight leading
+# dimension mod 8).  Phase 1 reads A (leading dimension r) and phase 2 reads
+# B (leading dimension N), so the first eight shapes cover every r mod 8 and
+# N mod 8; the rest add ragged M, partial column tiles, rank padding,
+# k-splits and a misaligned X (K mod 8 != 0: phase 1 falls back to the
+# two-wave kernel).
+KIND_SHAPES = [(300, 512, 256 + q, 512 + (3 * q) % 8) for q in range(8)] + [
+    (513, 1024, 645, 2056), (257, 2048, 817, 1024), (40, 4096, 333, 999), (1000, 520, 77, 300),
+    (333, 1001, 100, 300)]
+
+
+def _plan_kinds(lin):
+    """(phase-1 kind, phase-2 kind) of the last prefill call, from describe()."""
+    import re
+    m = re.search(r"phase1 kind=(-?\d+) nb=\d+ splits=\d+, phase2 kind=(-?\d+)", lin.describe())
+    return int(m.group(1)), int(m.group(2))
+
+
+@pytest.mark.parametrize("flags", [lrl.LR_FLAG_PREFILL_TWO_WAVE, lrl.LR_FLAG_PREFILL_ONE_WAVE])
+@pytest.mark.parametrize("M,K,r,N", KIND_SHAPES)
+def test_prefill_kernel_kinds(M, K, r, N, flags):
+    p, lin, _, _ = run_case(M, K, r, N, 6100 + M + r + N, flags=flags)
+    k1, k2 = _plan_kinds(lin)
+    banner("kinds M=%d K=%d r=%d N=%d flags=%d: phase kinds %d %d parity %s" % (M, K, r, N, flags, k1, k2, p))
+    if flags == lrl.LR_FLAG_PREFILL_TWO_WAVE:
+        assert (k1, k2) == (0, 0)
+    else:
+        assert k1 == (1 if K % 8 == 0 else 0) and k2 == 1
+
+
+def test_mlp_packed_one_wave():
+    # packed gate/up through the one-wave kernel (both factors r = 203)
+    M, K = 300, 1024
+    Xb = datagen.normal_bf16((M, K), 1.0, 63)
+    _, Agb, Bgb = datagen.factorized_inputs(1, K, 203, 900, 73)
+    _, Aub, Bub = datagen.factorized_inputs(1, K, 203, 1300, 83)
+    f = lrl.LR_FLAG_PREFILL_ONE_WAVE
+    gate = lrl.LowRankLinear(to_dev(Agb), to_dev(Bgb), max_M=M, flags=f)
+    up = lrl.LowRankLinear(to_dev(Aub), to_dev(Bub), max_M=M, flags=f)
+    Yg, Yu = lrl.mlp_packed(gate, up, to_dev(Xb))
+    assert _plan_kinds(gate) == (1, 1)
+    assert_parity(to_bits(Yg), oracle.lowrank_bf16(Xb, Agb, Bgb), "packed one-wave gate")
+    assert_parity(to_bits(Yu), oracle.lowrank_bf16(Xb, Aub, Bub), "packed one-wave up")
+
+
 # ---------------------------------------------------------------- packed ---
 
 @pytest.mark.parametrize("M", [1, 4, 64])

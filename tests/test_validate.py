@@ -37,10 +37,11 @@ void t_partition(long long K, long long r, long long N, int budget, int allow_re
   out[0] = p.Jw; out[1] = p.S; out[2] = p.ktps; out[3] = p.ntps;
   out[4] = p.kind; out[5] = p.js_w; out[6] = p.nt_w;
 }
-void t_prefill_plan(long long rows, long long c0, long long c1, int nout, long long kd, int cus, int* out) {
+void t_prefill_plan(long long rows, long long c0, long long c1, int nout, long long kd, int cus, int kinds,
+                    int q_aligned, int* out) {
   const int64_t cols[2] = {c0, c1};
-  lrv::PrePlan p = lrv::prefill_plan(rows, cols, nout, kd, cus);
-  out[0] = p.nb; out[1] = p.splits; out[2] = p.split_steps;
+  lrv::PrePlan p = lrv::prefill_plan(rows, cols, nout, kd, cus, 32, kinds, q_aligned != 0);
+  out[0] = p.nb; out[1] = p.splits; out[2] = p.split_steps; out[3] = p.kind;
 }
 long long t_partial_bytes(long long max_M, long long K, long long r_pad, long long N, int cus) {
   return lrv::prefill_partial_bytes(max_M, K, r_pad, N, cus);
@@ -63,7 +64,8 @@ def shim(tmp_path_factory):
     lib.t_check_run.argtypes = [ll, ll, ll, ll, ull, ull, ull, ull, ll]
     lib.t_check_packed.argtypes = [ll, ll, ll, ll, ull, ull, ull, ull, ull, ull, ull, ll]
     lib.t_partition.argtypes = [ll, ll, ll, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
-    lib.t_prefill_plan.argtypes = [ll, ll, ll, ctypes.c_int, ll, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.t_prefill_plan.argtypes = [ll, ll, ll, ctypes.c_int, ll, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_int)]
     lib.t_partial_bytes.argtypes = [ll, ll, ll, ll, ctypes.c_int]
     lib.t_partial_bytes.restype = ll
     return lib
@@ -78,7 +80,10 @@ def test_create_validation(shim):
     assert shim.t_check_create(4096, 1637, 4096, 0, 0x2000000, 16, 0) == INVALID
     assert shim.t_check_create(4096, 0, 4096, 0x100000, 0x2000000, 16, 0) == INVALID
     assert shim.t_check_create(4096, 1637, 4096, 0x100008, 0x2000000, 16, 0) == INVALID  # 8B aligned only
-    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 8) == UNSUPPORTED
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 32) == UNSUPPORTED  # unknown flag
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 4096, 8) == OK      # PREFILL_TWO_WAVE
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 4096, 16) == OK     # PREFILL_ONE_WAVE
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 4096, 24) == INVALID  # both
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 4) == OK
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 17, 1) == UNSUPPORTED
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 17, 2) == OK
@@ -163,34 +168,58 @@ def test_decode_partition_balances_q_proj(shim):
     assert per_wg <= 1.25 * ideal
 
 
-def _plan(shim, rows, cols, kd, cus=256):
-    out = (ctypes.c_int * 3)()
+TWO_WAVE, ONE_WAVE = 1, 2
+
+
+def _plan(shim, rows, cols, kd, cus=256, kinds=TWO_WAVE, q_aligned=False):
+    out = (ctypes.c_int * 4)()
     c = list(cols) + [0]
-    shim.t_prefill_plan(rows, c[0], c[1], len(cols), kd, cus, out)
+    shim.t_prefill_plan(rows, c[0], c[1], len(cols), kd, cus, kinds, int(q_aligned), out)
     return tuple(out)
 
 
-@pytest.mark.parametrize("rows,cols,kd", [
+PLAN_SHAPES = [
     (4096, (2880,), 4096), (4096, (14336,), 2880),          # MLP up-projection, both phases
     (2048, (1664,), 4096), (2048, (4096,), 1664),           # q_proj at M = 2048
     (2048, (2880, 2880), 4096), (2048, (14336, 14336), 2880),  # packed gate/up
     (512, (1056,), 4096), (512, (3999,), 1056),             # alignment sweep at M = 512
     (17, (128,), 512), (40, (512,), 128), (300, (33,), 7),  # small and ragged
-])
-def test_prefill_plan_covers_k_and_fits(shim, rows, cols, kd):
-    nb, splits, steps = _plan(shim, rows, cols, kd)
+]
+
+
+@pytest.mark.parametrize("kinds", [TWO_WAVE, ONE_WAVE, TWO_WAVE | ONE_WAVE])
+@pytest.mark.parametrize("q_aligned", [False, True])
+@pytest.mark.parametrize("rows,cols,kd", PLAN_SHAPES)
+def test_prefill_plan_covers_k_and_fits(shim, rows, cols, kd, kinds, q_aligned):
+    nb, splits, steps, kind = _plan(shim, rows, cols, kd, kinds=kinds, q_aligned=q_aligned)
     nks = -(-kd // 32)
-    assert 6 <= nb <= 7
+    assert kind in (0, 1) and (kinds >> kind) & 1
+    if kind == 0:
+        assert 6 <= nb <= 7
+    else:
+        # the one-wave kernel: 256-wide tiles, splits on 64-deep stages
+        assert nb == 8 and steps % 2 == 0
     assert splits >= 1 and steps >= 1
     # every k-step is in exactly one split and no split is empty
     assert splits * steps >= nks and (splits - 1) * steps < nks
+
+
+def test_prefill_plan_picks_by_cost(shim):
+    both = TWO_WAVE | ONE_WAVE
+    # MLP up phase 2 (B rows aligned, 14336 wide): the one-wave kernel
+    assert _plan(shim, 4096, (14336,), 2880, kinds=both, q_aligned=True)[3] == 1
+    # MLP up phase 1 (A rows 2867 wide, misaligned): the two-wave kernel
+    assert _plan(shim, 4096, (2880,), 4096, kinds=both, q_aligned=False)[3] == 0
+    # only one kind allowed: that kind
+    assert _plan(shim, 4096, (14336,), 2880, kinds=TWO_WAVE, q_aligned=True)[3] == 0
+    assert _plan(shim, 4096, (2880,), 4096, kinds=ONE_WAVE, q_aligned=False)[3] == 1
 
 
 def test_prefill_plan_fills_the_machine_for_small_m(shim):
     # MLP up at M = 4096: enough tiles, no split
     assert _plan(shim, 4096, (14336,), 2880)[1] == 1
     # the M = 512 sweep shape has 12 tiles of 256 x 192: it splits k
-    nb, splits, steps = _plan(shim, 512, (1056,), 4096)
+    nb, splits, steps, kind = _plan(shim, 512, (1056,), 4096)
     tiles = 2 * -(-1056 // (32 * nb))
     assert splits > 1 and tiles * splits >= 64
 
@@ -201,6 +230,8 @@ def test_prefill_partial_bytes_cover_every_plan(shim):
         have = shim.t_partial_bytes(max_M, K, r_pad, N, 256)
         for M in list(range(17, max_M + 1, 97)) + [max_M]:
             for cols, kd in (((r_pad,), K), ((N,), r_pad)):
-                nb, splits, steps = _plan(shim, M, cols, kd)
-                if splits > 1:
-                    assert splits * M * (-(-cols[0] // 4) * 4) * 4 <= have, (max_M, M, cols, kd, splits)
+                for kinds in (TWO_WAVE, ONE_WAVE, TWO_WAVE | ONE_WAVE):
+                    for qa in (False, True):
+                        nb, splits, steps, kind = _plan(shim, M, cols, kd, kinds=kinds, q_aligned=qa)
+                        if splits > 1:
+                            assert splits * M * (-(-cols[0] // 4) * 4) * 4 <= have, (max_M, M, cols, kd, splits)
