@@ -35,6 +35,27 @@
 #include "lr_device.h"
 #include "lr_kernels.h"
 
+// Optional per-stage timestamps (shader clock) of the first eight workgroups
+// of launches with LR_PREFILL_TRACE workgroups, compiled in only with
+// -DLR_PREFILL_TRACE=<grid>; lr_prefill_trace_read() copies them out.
+#ifdef LR_PREFILL_TRACE
+__device__ uint64_t g_w4trace[8 * 4 * 64 * 8];
+extern "C" int lr_prefill_trace_read(void* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_w4trace), sizeof(g_w4trace));
+}
+#define W4_TRACE(k)                                                                            \
+  do {                                                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    if (gridDim.x == LR_PREFILL_TRACE && blockIdx.x < 8 && s < 64 && (threadIdx.x & 63) == 0)  \
+      g_w4trace[((blockIdx.x * 4 + w) * 64 + s) * 8 + (k)] = __builtin_amdgcn_s_memtime();      \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+  } while (0)
+#else
+#define W4_TRACE(k) \
+  do {              \
+  } while (0)
+#endif
+
 namespace lrk {
 
 namespace {
@@ -284,6 +305,13 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
     for (int cb = 0; cb < 4; ++cb) B[cb] = lds_read16(qs + b_base[cb] + kk * 8192);
   };
   // MFMAs 2j and 2j + 1 of a k16 block (row block j / 2, column blocks 2 (j % 2) + 0, 1)
+  // one of the eight operand reads of k16 block kk: A[i] for i < 4, else B[i - 4]
+  auto rd1 = [&](const char* ps, const char* qs, int kk, u32x4_t(&A)[4], u32x4_t(&B)[4], int i) {
+    if (i < 4)
+      A[i] = lds_read16(ps + a_base + 16 * ((2 * kk) ^ y) + i * 4096);
+    else
+      B[i - 4] = lds_read16(qs + b_base[i - 4] + kk * 8192);
+  };
   // MFMA i of a k16 block: row block i / 4, column block i % 4
   auto mf1 = [&](const u32x4_t(&A)[4], const u32x4_t(&B)[4], int i) {
     acc[i >> 2][i & 3] = mfma32(A[i >> 2], B[i & 3], acc[i >> 2][i & 3]);
@@ -307,75 +335,77 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
   rd(pslot(0), qtslot(0), 0, A0, B0);
 
   // Stage s multiplies four k16 blocks (M0..M3, 16 MFMAs each) from two
-  // operand register sets: the operands of a block are read while the block
-  // before it runs, and the first block's operands are read at the end of the
-  // previous stage, so no stage starts by waiting for LDS.  The other work
-  // is placed after single MFMAs (each keeps the matrix core busy for about
-  // 32 cycles): during M0 the weight rows of stage s + 2 are requested into
-  // the register set stage s - 1 emptied; during M1 the rows of stage s + 1
-  // (requested during stage s - 1) are realigned and transposed into Qt of
-  // s + 1; the one barrier of the
-  // stage sits four MFMAs into M2, after the last LDS read of the stage's P
-  // slot, and is followed by the request of P for stage s + 3 into that
-  // slot.  sched_barrier fences keep this order: on each SIMD this one wave
-  // is all there is to keep the matrix core busy.  Requests past the last
-  // stage land in slots no later stage reads.
+  // operand register sets; the eight operand reads of block kk + 1 are
+  // spread over the first eight MFMAs of block kk, and the other work sits
+  // after single MFMAs too (each keeps the matrix core busy for about 32
+  // cycles), so the one wave on each SIMD never leaves it idle for long:
+  //   M0: the weight rows of stage s + 2 are requested into the register set
+  //       stage s - 1 emptied;
+  //   M1: the rows of stage s + 1 (requested during stage s - 1) are
+  //       realigned and transposed into Qt of s + 1;
+  //   M2: the last reads of this stage's P slot and Qt;
+  //   then P of s + 1 is awaited and the stage's one barrier met;
+  //   M3: the first operands of stage s + 1 are read and P of stage s + 3 is
+  //       requested into this stage's P slot.
+  // sched_barrier fences keep this order.  Requests past the last stage land
+  // in slots no later stage reads.  (Spreading the memory requests four to a
+  // block instead measured slightly slower.)
   auto stage = [&](int s, const QRegs& qin, QRegs& qout) {
     const char* ps = pslot(s);
     const char* qs = qtslot(s);
     char* qt_next = smem + kQtBase + ((s + 1) & 1) * kQtSlot;
-    rd(ps, qs, 1, A1, B1);
-    fence();
+    W4_TRACE(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       mf1(A0, B0, i);
       fence();
+      if (i < 8) rd1(ps, qs, 1, A1, B1, i);
       if ((i & 1) == 0)
         q_issue_row_main(qout, i >> 1, s + 2);
       else
         q_issue_row_extra(qout, i >> 1, s + 2);
       fence();
     }
-    rd(ps, qs, 2, A0, B0);
-    fence();
+    W4_TRACE(1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       mf1(A1, B1, i);
       fence();
+      if (i < 8) rd1(ps, qs, 2, A0, B0, i);
       if (i < 8)
         q_realign_row(qin, i);
       else
         q_store_col(i - 8, qt_next);
       fence();
     }
-    rd(ps, qs, 3, A1, B1);
-    fence();
+    W4_TRACE(2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 16; ++i) {
       mf1(A0, B0, i);
+      fence();
+      if (i < 8) rd1(ps, qs, 3, A1, B1, i);
       fence();
     }
     // P of stage s + 1 must have landed (P of s + 2 and the weight rows of
     // s + 2 may stay in flight); after the barrier every wave has read this
-    // stage's P slot and written Qt of s + 1
+    // stage's P slot and Qt and written Qt of s + 1
+    W4_TRACE(3);
     wait_vm<8 + NQ>();
     barrier_lds();
-    char* pnext = smem + (s % kPSlots) * kPSlot;  // slot of stage s + 3
-    const int st3 = s + 3;
-#pragma unroll
-    for (int i = 4; i < 16; ++i) {
-      mf1(A0, B0, i);
-      fence();
-      if (i >= 8) p_issue_one(pnext, st3, i - 8);
-      fence();
-    }
-    rd(pslot(s + 1), qt_next, 0, A0, B0);
-    fence();
+    W4_TRACE(4);
+    char* p3 = smem + (s % kPSlots) * kPSlot;  // slot of stage s + 3
+    const char* ps1 = pslot(s + 1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       mf1(A1, B1, i);
       fence();
+      if (i < 8)
+        rd1(ps1, qt_next, 0, A0, B0, i);
+      else
+        p_issue_one(p3, s + 3, i - 8);
+      fence();
     }
+    W4_TRACE(5);
   };
   for (int s = 0; s < nst; s += 2) {
     stage(s, qa, qb);

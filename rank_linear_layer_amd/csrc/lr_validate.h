@@ -202,8 +202,8 @@ struct PrePlan {
 // of the 256-CU machine times steps per tile times the per-step cost of the
 // kernel, plus the partial write/read and reduction launch when k is split.
 // Measured per-step costs: two-wave kernel nb + 2 (nb = 6, 7); one-wave
-// kernel (256 x 256) 7.6 when the weight leading dimension is a multiple of
-// 8, 9.0 otherwise (the rows are realigned in registers); its k-splits start
+// kernel (256 x 256) 7.0 when the weight leading dimension is a multiple of
+// 8, 9.1 otherwise (the rows are realigned in registers); its k-splits start
 // on 64-deep stages.  `kinds`: bit 0 allows the two-wave kernel, bit 1 the
 // one-wave kernel (which needs a 16-byte aligned P).
 constexpr int kPlanTwoWave = 1;
@@ -220,7 +220,7 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
   const struct {
     int nb, kind;
     double per_step;
-  } kinds[3] = {{8, 1, q_aligned ? 7.6 : 9.0}, {7, 0, 9.0}, {6, 0, 8.0}};
+  } kinds[3] = {{8, 1, q_aligned ? 7.0 : 9.1}, {7, 0, 9.0}, {6, 0, 8.0}};
   for (const auto& kn : kinds) {
     if (!(kinds_allowed & (kn.kind == 1 ? kPlanOneWave : kPlanTwoWave))) continue;
     const int gran = kn.kind == 1 ? 2 : 1;
