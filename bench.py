@@ -34,17 +34,33 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "low-rank linear: decode TB/s and prefill TFLOP/s vs roofline, across rank r"
-KERNEL_SOURCES = ["rank_linear_layer_amd/csrc/lr_decode.hip", "rank_linear_layer_amd/csrc/lr_decode_res.hip",
-                  "rank_linear_layer_amd/csrc/lr_prefill.hip", "rank_linear_layer_amd/csrc/lr_device.h",
-                  "rank_linear_layer_amd/csrc/lr_kernels.h"]
+_CSRC = "rank_linear_layer_amd/csrc/"
+DECODE_SOURCES = [_CSRC + f for f in ("lr_decode.hip", "lr_decode_res.hip", "lr_device.h", "lr_kernels.h")]
+PREFILL_SOURCES = [_CSRC + f for f in ("lr_prefill.hip", "lr_prefill_w4.hip", "lr_device.h", "lr_kernels.h",
+                                       "lr_validate.h", "lr_linear.cpp")]
+PREFILL_KERNELS = {0: "lr_prefill_gemm_kernel", 1: "lr_prefill_w4_kernel"}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
+    """Hash of the kernel sources a counter summary was taken on (decode
+    sources by default)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or DECODE_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def prefill_kernels(plan):
+    """Kernel names of the two prefill phases from a describe() string."""
+    import re
+    m = re.search(r"phase1 kind=(-?\d+) nb=\d+ splits=(\d+), phase2 kind=(-?\d+) nb=\d+ splits=(\d+)", plan)
+    if not m:
+        return None
+    names = []
+    for kind, splits in ((int(m.group(1)), int(m.group(2))), (int(m.group(3)), int(m.group(4)))):
+        names.append(PREFILL_KERNELS.get(kind, "?") + (" + lr_prefill_reduce_kernel" if splits > 1 else ""))
+    return names
 
 
 def log(msg):
@@ -73,9 +89,9 @@ def decode_kernel_name(plan):
     return "lr_decode_res_kernel" if "kind=resident" in plan else "lr_decode_fused_kernel"
 
 
-def traffic_from_profile(name, launches_bytes):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if
-    they were taken on the current kernel sources (else None)."""
+def traffic_from_profile(name, sources=None, key="hbm_bytes_per_launch"):
+    """HBM bytes from a committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
@@ -84,9 +100,9 @@ def traffic_from_profile(name, launches_bytes):
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get(key)
 
 
 def bench_decode(torch, lrl, configs, datagen, metrics, steps, warmup):
@@ -306,7 +322,7 @@ def main():
                    "r": d["r"], "N": d["N"], "path": kname, "weight_copies": d["ncopies"]},
         "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile("%s_qproj_decode_pmc.json" % kname, d["bytes"]),
+                     "traffic": traffic_from_profile("%s_qproj_decode_pmc.json" % kname),
                      "kernel": kname, "algorithmic_bytes_per_launch": d["bytes"],
                      "us_per_launch": round(d["ms"] * 1e3, 3)},
         "warm_cache_tbs": round(d["warm_tbs"], 4),
@@ -314,12 +330,15 @@ def main():
     if not args.no_prefill:
         p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 50), 3)
         log("prefill: %.3f ms/step, %.1f TFLOP/s" % (p["ms"], p["tflops"]))
+        kn = prefill_kernels(p["plan"])
         result["prefill"] = {
             "workload": "MLP up-projection prefill M=4096 K=4096 r=2867 N=14336",
             "ms_per_step": round(p["ms"], 5), "value": round(p["tflops"], 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(p["tflops"], 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(p["tflops"] / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel": "lr_prefill_gemm_kernel (2 launches)",
+                         "traffic": traffic_from_profile("prefill_mlp_up_pmc.json", PREFILL_SOURCES,
+                                                         "hbm_bytes_per_step"),
+                         "kernel": "phase 1 %s, phase 2 %s" % tuple(kn) if kn else "prefill (2 launches)",
                          "algorithmic_flops_per_step": p["flops"]},
         }
     if not args.no_layer:
