@@ -50,9 +50,20 @@ extern "C" int lr_prefill_trace_read(void* host) {
       g_w4trace[((blockIdx.x * 4 + w) * 64 + s) * 8 + (k)] = __builtin_amdgcn_s_memtime();      \
     __builtin_amdgcn_sched_barrier(0);                                                         \
   } while (0)
+// tile-level points (start, after the prologue, after the stages, end) go to stage slot 63
+#define W4_TRACE_TILE(k)                                                                      \
+  do {                                                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    if (gridDim.x == LR_PREFILL_TRACE && blockIdx.x < 8 && (threadIdx.x & 63) == 0)           \
+      g_w4trace[((blockIdx.x * 4 + w) * 64 + 63) * 8 + (k)] = __builtin_amdgcn_s_memtime();   \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+  } while (0)
 #else
 #define W4_TRACE(k) \
   do {              \
+  } while (0)
+#define W4_TRACE_TILE(k) \
+  do {                   \
   } while (0)
 #endif
 
@@ -175,6 +186,7 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
   const rsrc_t rQ = make_rsrc(O.Q, O.qrows * O.ldq * 2);
   const int qcols = (int)min64((int64_t)kBN, O.ldq - T.nb);
 
+  W4_TRACE_TILE(0);
   const int nks_all = (int)((O.kd + 31) / 32);
   const int s0 = ks * a.split_steps;  // even: splits start on a 64-deep stage
   const int nk = max(0, min(nks_all - s0, a.split_steps));
@@ -332,6 +344,7 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
   q_issue(qa, 1);
   wait_vm<16 + NQ>();
   barrier_lds();
+  W4_TRACE_TILE(1);
   rd(pslot(0), qtslot(0), 0, A0, B0);
 
   // Stage s multiplies four k16 blocks (M0..M3, 16 MFMAs each) from two
@@ -411,8 +424,10 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
     stage(s, qa, qb);
     if (s + 1 < nst) stage(s + 1, qb, qa);
   }
+  W4_TRACE_TILE(2);
   wait_vm<0>();
   barrier_lds();
+  W4_TRACE_TILE(4);
 
   // ------------------------------------------------------------ epilogue --
   // acc[rb][cb] lane l, register 4b + t: row 8b + 4 gL + t of 32-row block
@@ -429,44 +444,81 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
           const int64_t n = T.nb + 128 * wn + 32 * cb + L;
           if (m < a.rows && n < O.out_cols) part[m * O.ldpart + n] = acc[rb][cb][e];
         }
+    W4_TRACE_TILE(3);
     return;
   }
   const int64_t ldc = O.ldc;
+  // Staging: row m of the tile sits at m * kStageRowBytes, shifted by the
+  // misalignment d of the output row, which depends only on (T.mb + m) mod 8
+  // = (T.mb + 4 gL + e % 4) mod 8 for this lane's registers.
+  int sbase[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = (int)(((T.mb + 4 * gL + j) * ldc + T.nb) & 7);
+    sbase[j] = (128 * wm + 4 * gL + j) * kStageRowBytes + 2 * (d + 128 * wn + L);
+  }
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int m = 128 * wm + 32 * rb + 8 * (e >> 2) + 4 * gL + (e & 3);
-      const int d = (int)(((T.mb + m) * ldc + T.nb) & 7);
-      uint16_t* row = reinterpret_cast<uint16_t*>(smem + m * kStageRowBytes) + d + 128 * wn + L;
+      uint16_t* row = reinterpret_cast<uint16_t*>(smem + sbase[e & 3] + (32 * rb + 8 * (e >> 2)) * kStageRowBytes);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) row[32 * cb] = (uint16_t)f32_to_bf16_rne(acc[rb][cb][e]);
     }
   barrier_lds();
+  W4_TRACE_TILE(5);
+  // Copy-out: item i = (row i / 33, chunk i % 33), thread t takes items
+  // t, t + 256, ... (256 = 7 rows + 25 chunks), so consecutive threads
+  // store consecutive 16-byte chunks of a row.  All 33 chunks of a thread
+  // are read from LDS first (the accumulators are dead by now), then stored.
   const rsrc_t rC = make_rsrc(O.C, a.rows * ldc * 2);
   const int ncols = (int)min64((int64_t)kBN, O.out_cols - T.nb);
-  constexpr int nitems = kBM * kStageChunks;
-  for (int item = threadIdx.x; item < nitems; item += kThreads) {
-    const int m = item / kStageChunks, k = item - m * kStageChunks;
-    const int64_t R = T.mb + m;
-    if (R >= a.rows) continue;
-    const int d = (int)((R * ldc + T.nb) & 7);
-    const int n0 = 8 * k - d;
-    if (n0 >= ncols) continue;
-    const u32x4_t v = lds_read16(smem + m * kStageRowBytes + 16 * k);
-    const int64_t e0 = R * ldc + T.nb + n0;
-    if (n0 >= 0 && n0 + 8 <= ncols) {
-      __builtin_amdgcn_raw_buffer_store_b128(v, rC, (int)(e0 * 2), 0, 0);
-    } else {
+  const int m_first = (int)threadIdx.x / kStageChunks, k_first = (int)threadIdx.x - m_first * kStageChunks;
+  u32x4_t chunk[kStageChunks];
+  {
+    int m = m_first, k = k_first;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int n = n0 + e;
-        if (n >= 0 && n < ncols)
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(v[e >> 1] >> (16 * (e & 1))), rC, (int)((e0 + e) * 2), 0,
-                                                0);
+    for (int it = 0; it < kStageChunks; ++it) {
+      chunk[it] = lds_read16(smem + m * kStageRowBytes + 16 * k);
+      m += 7;
+      k += 25;
+      if (k >= kStageChunks) {
+        k -= kStageChunks;
+        m += 1;
       }
     }
   }
+  int m = m_first, k = k_first;
+  int64_t rowoff = (T.mb + m) * ldc + T.nb;  // element index of (row, first tile column)
+#pragma unroll
+  for (int it = 0; it < kStageChunks; ++it) {
+    const int d = (int)(rowoff & 7);
+    const int n0 = 8 * k - d;
+    if (T.mb + m < a.rows && n0 < ncols) {
+      const u32x4_t v = chunk[it];
+      const int64_t e0 = rowoff + n0;
+      if (n0 >= 0 && n0 + 8 <= ncols) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, rC, (int)(e0 * 2), 0, 0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int n = n0 + e;
+          if (n >= 0 && n < ncols)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(v[e >> 1] >> (16 * (e & 1))), rC, (int)((e0 + e) * 2), 0,
+                                                  0);
+        }
+      }
+    }
+    m += 7;
+    k += 25;
+    rowoff += 7 * ldc;
+    if (k >= kStageChunks) {
+      k -= kStageChunks;
+      m += 1;
+      rowoff += ldc;
+    }
+  }
+  W4_TRACE_TILE(3);
 }
 
 template <int QMOD>
