@@ -198,14 +198,16 @@ struct PrePlan {
   int kind;  // 0: two waves per SIMD, tile 256 x 32 nb; 1: one wave per SIMD, tile 256 x 256
 };
 // Kernel, tile width and k-split for one prefill phase, from a cost model in
-// units of one 32-deep k-step of one tile (about 0.14 us on MI355X): rounds
-// of the 256-CU machine times steps per tile times the per-step cost of the
-// kernel, plus the partial write/read and reduction launch when k is split.
-// Measured per-step costs: two-wave kernel nb + 2 (nb = 6, 7); one-wave
-// kernel (256 x 256) 7.0 when the weight leading dimension is a multiple of
-// 8, 9.1 otherwise (the rows are realigned in registers); its k-splits start
-// on 64-deep stages.  `kinds`: bit 0 allows the two-wave kernel, bit 1 the
-// one-wave kernel (which needs a 16-byte aligned P).
+// units of about 0.14 us (one 32-deep k-step of the two-wave kernel at nb = 7
+// is 8.55): rounds of the 256-CU machine times (k-steps per split x the
+// kernel's per-step cost + its per-tile cost: start-up, epilogue), plus the
+// partial write/read and reduction launch when k is split.  Measured on
+// MI355X: two-wave kernel nb = 6 7.9 and nb = 7 8.55 per step, 40 per tile
+// (80 with fp32 partials); one-wave kernel 5.9 per step when the weight
+// leading dimension is a multiple of 8 and 8.45 otherwise (rows realigned in
+// registers), 85 per tile (200 with fp32 partials), k-splits on 64-deep
+// stages.  `kinds`: bit 0 allows the two-wave kernel, bit 1 the one-wave
+// kernel (which needs a 16-byte aligned P).
 constexpr int kPlanTwoWave = 1;
 constexpr int kPlanOneWave = 2;
 inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int64_t kd, int num_cus,
@@ -219,8 +221,8 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
   double best_cost = -1;
   const struct {
     int nb, kind;
-    double per_step;
-  } kinds[3] = {{8, 1, q_aligned ? 7.0 : 9.1}, {7, 0, 9.0}, {6, 0, 8.0}};
+    double per_step, per_tile, per_tile_split;
+  } kinds[3] = {{8, 1, q_aligned ? 5.9 : 8.45, 85.0, 200.0}, {7, 0, 8.55, 40.0, 80.0}, {6, 0, 7.9, 40.0, 80.0}};
   for (const auto& kn : kinds) {
     if (!(kinds_allowed & (kn.kind == 1 ? kPlanOneWave : kPlanTwoWave))) continue;
     const int gran = kn.kind == 1 ? 2 : 1;
@@ -233,7 +235,7 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
       if (splits != want) continue;
       const int64_t steps = per * gran;
       const int64_t rounds = ceil_div(tiles * splits, cus);
-      double cost = (double)(rounds * steps) * kn.per_step;
+      double cost = (double)rounds * ((double)steps * kn.per_step + (splits > 1 ? kn.per_tile_split : kn.per_tile));
       if (splits > 1) cost += 14.0 + (double)(2 * splits * rows * cols * 4 + rows * cols * 2) / 700e3;
       if (best_cost < 0 || cost < best_cost - 1e-9) {
         best_cost = cost;
