@@ -147,10 +147,12 @@ def bench_prefill(torch, lrl, configs, metrics, steps, warmup):
     return dict(M=M, K=K, r=r, N=N, ms=ms, tflops=fl / (ms * 1e-3) / 1e12, flops=fl, plan=lin.describe())
 
 
-def bench_layer(torch, lrl, configs, metrics, M, steps, warmup):
+def bench_layer(torch, lrl, configs, metrics, M, steps, warmup, grouped=True):
     """One decoder layer of factorized projections (q, k, v, o, packed
-    gate/up, down) at M rows: the layer's span per step.  Weights rotate over
-    enough copies (>= 1 GiB) that every step streams them from HBM."""
+    gate/up, down) at M rows: the layer's span per step.  q, k and v share X
+    in one group call (or three separate calls with grouped=False).  Weights
+    rotate over enough copies (>= 1 GiB) that every step streams them from
+    HBM."""
     g = torch.Generator(device="cuda")
     g.manual_seed(configs.seed_base(configs.LAYER_INDEX))
     projs = {p.name: p for p in configs.LAYER_PROJS}
@@ -170,8 +172,12 @@ def bench_layer(torch, lrl, configs, metrics, M, steps, warmup):
 
     def step(i):
         L = sets[i % ncop]
-        for name in ("q", "k", "v", "o"):
-            L[name](X, out=outs[name])
+        if grouped:
+            lrl.group_run([L["q"], L["k"], L["v"]], X, outs=[outs["q"], outs["k"], outs["v"]])
+        else:
+            for name in ("q", "k", "v"):
+                L[name](X, out=outs[name])
+        L["o"](X, out=outs["o"])
         lrl.mlp_packed(L["gate"], L["up"], X, out_gate=outs["gate"], out_up=outs["up"])
         L["down"](H, out=outs["down"])
 
@@ -179,7 +185,7 @@ def bench_layer(torch, lrl, configs, metrics, M, steps, warmup):
     byts = sum(metrics.decode_bytes(M, p.K, p.r, p.N) for p in configs.LAYER_PROJS)
     fl = sum(metrics.lowrank_flops(M, p.K, p.r, p.N) for p in configs.LAYER_PROJS)
     return dict(M=M, ms=ms, tbs=byts / (ms * 1e-3) / 1e12, tflops=fl / (ms * 1e-3) / 1e12, bytes=byts, flops=fl,
-                launches=6, copies=ncop)
+                calls=4 if grouped else 6, copies=ncop)
 
 
 def cpu_baseline(configs, datagen, metrics, budget_s=12.0):
@@ -344,20 +350,26 @@ def main():
     if not args.no_layer:
         lay = {}
         for M in configs.LAYER_M:
-            d_ = bench_layer(torch, lrl, configs, metrics, M, 200 if M <= 16 else 10, 20 if M <= 16 else 2)
-            log("layer M=%d: %.1f us/layer, %.3f TB/s, %.1f TFLOP/s (%d launches, %d weight copies)"
-                % (M, d_["ms"] * 1e3, d_["tbs"], d_["tflops"], d_["launches"], d_["copies"]))
+            steps_, warm_ = (200, 20) if M <= 16 else (10, 2)
+            d_ = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_)
+            sep = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_, grouped=False)
+            log("layer M=%d: %.1f us/layer, %.3f TB/s, %.1f TFLOP/s (%d library calls, %d weight copies); "
+                "q, k, v as separate calls: %.1f us/layer"
+                % (M, d_["ms"] * 1e3, d_["tbs"], d_["tflops"], d_["calls"], d_["copies"], sep["ms"] * 1e3))
             if M <= 16:
                 lay["M%d" % M] = {"us_per_layer": round(d_["ms"] * 1e3, 2), "value": round(d_["tbs"], 4),
                                   "unit": "TB/s", "roofline_frac_hbm": round(d_["tbs"] * 1e3 / HBM_PEAK_GBS, 4),
-                                  "algorithmic_bytes": d_["bytes"], "launches": d_["launches"],
-                                  "weight_copies": d_["copies"]}
+                                  "algorithmic_bytes": d_["bytes"], "library_calls": d_["calls"],
+                                  "weight_copies": d_["copies"],
+                                  "us_per_layer_qkv_separate": round(sep["ms"] * 1e3, 2)}
             else:
                 lay["M%d" % M] = {"us_per_layer": round(d_["ms"] * 1e3, 2), "value": round(d_["tflops"], 2),
                                   "unit": "TFLOP/s", "roofline_frac_mfma": round(d_["tflops"] / BF16_PEAK_TFLOPS, 4),
-                                  "algorithmic_flops": d_["flops"], "launches": d_["launches"]}
+                                  "algorithmic_flops": d_["flops"], "library_calls": d_["calls"],
+                                  "us_per_layer_qkv_separate": round(sep["ms"] * 1e3, 2)}
         result["layer"] = {"workload": "Llama-3-8B-shaped decoder layer: q,o 4096->4096 r1637; k,v 4096->1024 "
-                                       "r817; gate,up 4096->14336 r2867 (packed); down 14336->4096 r2867", **lay}
+                                       "r817 (q, k, v grouped on a shared X); gate,up 4096->14336 r2867 (packed); "
+                                       "down 14336->4096 r2867", **lay}
     if args.sweep:
         result["sweep"] = run_sweep(torch, lrl, configs, metrics, args.sweep_steps, args.sweep_stride)
     if not args.no_cpu:

@@ -118,13 +118,44 @@ lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, v
  * abstract: packed MLP execution).  Computes
  *     Y_gate = (X.A_gate).B_gate   and   Y_up = (X.A_up).B_up
  * in the same launch(es), reading each tile of X once for both GEMM1s.
- * gate and up must have equal K; their r and N may differ.  M must not
- * exceed either handle's max_M.  Y_gate and Y_up must not overlap each
- * other or any input.
- * Errors: as lr_linear_run, plus INVALID_ARG for gate.K != up.K.
+ * Same as lr_group_run with n = 2 and handles {gate, up}.
+ * gate and up must be distinct handles with equal K; their r and N may
+ * differ.  M must not exceed either handle's max_M.  Y_gate and Y_up must
+ * not overlap each other or any input.
+ * Errors: as lr_linear_run, plus INVALID_ARG for gate.K != up.K or
+ * gate == up.
  */
 lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const void* X,
                             void* Y_gate, void* Y_up, int64_t M, void* stream);
+
+/* Most projections one lr_group_run call takes. */
+#define LR_GROUP_MAX 4
+
+/*
+ * lr_group_run -- n projections that share their input X, such as the
+ * q, k and v projections of an attention block (the packed execution of
+ * "FlashSVD v1.5: Making Low-Rank Transformers Inference Actually Fast",
+ * abstract, widened from the gate/up pair to any n <= LR_GROUP_MAX).
+ * Computes Ys[i][M x N_i] = (X[M x K] . A_i) . B_i for i < n.
+ *   hs : n distinct handles (host array of handle pointers) with equal K;
+ *        r and N may differ.  Each owns its workspace, so no handle may
+ *        appear twice.  The prefill kernel flags of hs[0] govern the call.
+ *   X  : device pointer, bf16 [M x K] row-major, shared by every projection.
+ *   Ys : host array of n device pointers, bf16 [M x N_i] row-major; no
+ *        output may overlap X, another output or any handle's factors.
+ *   M  : rows, in [0, min max_M]; M == 0 returns LR_OK and launches nothing.
+ * Projections that take the decode kernel at this M share decode launches
+ * (as many as fit on the device at once); the others share one launch per
+ * prefill GEMM, in which every output's tiles are dealt over the CUs
+ * together (one launch per weight leading dimension mod 8 where the
+ * one-wave kernel is cheaper that way).  Results equal n lr_linear_run
+ * calls up to the order of fp32 additions.
+ * Errors: INVALID_ARG (null array, handle or pointer, n outside
+ * [1, LR_GROUP_MAX], repeated handle, unequal K, M out of range,
+ * misaligned base, overlapping output), HIP (launch failure).
+ */
+lr_status lr_group_run(const lr_linear* const* hs, int n, const void* X, void* const* Ys,
+                       int64_t M, void* stream);
 
 /* lr_linear_destroy -- free the workspace and the handle.  NULL is a no-op.
  * The caller must ensure no enqueued work still uses the handle. */

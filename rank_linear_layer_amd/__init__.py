@@ -9,6 +9,7 @@ raise.
     lin = LowRankLinear(A, B, max_M=16)     # A [K x r], B [r x N] bf16 cuda
     Y = lin(X)                               # X [M x K] bf16 cuda -> Y [M x N]
     Yg, Yu = mlp_packed(gate, up, X)         # gate/up pair sharing X
+    Yq, Yk, Yv = group_run([q, k, v], X)     # up to four projections sharing X
 """
 from __future__ import annotations
 
@@ -32,11 +33,13 @@ LR_FLAG_DECODE_STREAMING = 4
 LR_FLAG_PREFILL_TWO_WAVE = 8
 LR_FLAG_PREFILL_ONE_WAVE = 16
 LR_DECODE_MAX_M = 16
+LR_GROUP_MAX = 4
 
 EXPORTED_SYMBOLS = (
     "lr_linear_create",
     "lr_linear_run",
     "lr_mlp_packed_run",
+    "lr_group_run",
     "lr_linear_destroy",
     "lr_status_str",
     "lr_last_error",
@@ -76,6 +79,8 @@ def load_library(path: str | None = None):
         lib.lr_linear_run.restype = ctypes.c_int
         lib.lr_mlp_packed_run.argtypes = [vp, vp, vp, vp, vp, i64, vp]
         lib.lr_mlp_packed_run.restype = ctypes.c_int
+        lib.lr_group_run.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.POINTER(vp), i64, vp]
+        lib.lr_group_run.restype = ctypes.c_int
         lib.lr_linear_destroy.argtypes = [vp]
         lib.lr_linear_destroy.restype = None
         lib.lr_status_str.argtypes = [ctypes.c_int]
@@ -189,20 +194,48 @@ class LowRankLinear:
             pass
 
 
+def _outputs(projs, X, outs):
+    import torch
+    M = X.shape[0]
+    if outs is None:
+        outs = [None] * len(projs)
+    if len(outs) != len(projs):
+        raise ValueError("%d outputs for %d projections" % (len(outs), len(projs)))
+    res = []
+    for p, o in zip(projs, outs):
+        if o is None:
+            o = torch.empty((M, p.N), dtype=torch.bfloat16, device=X.device)
+        else:
+            _require_bf16_cuda(o, "out")
+            if tuple(o.shape) != (M, p.N):
+                raise ValueError("out must be [%d x %d]" % (M, p.N))
+        res.append(o)
+    return res
+
+
 def mlp_packed(gate: LowRankLinear, up: LowRankLinear, X, out_gate=None, out_up=None, stream=None):
     """Y_gate = (X.A_g).B_g and Y_up = (X.A_u).B_u in one pass over X."""
-    import torch
     _require_bf16_cuda(X, "X")
-    M = X.shape[0]
-    if out_gate is None:
-        out_gate = torch.empty((M, gate.N), dtype=torch.bfloat16, device=X.device)
-    if out_up is None:
-        out_up = torch.empty((M, up.N), dtype=torch.bfloat16, device=X.device)
+    out_gate, out_up = _outputs([gate, up], X, [out_gate, out_up])
     st = load_library().lr_mlp_packed_run(gate.handle, up.handle, ctypes.c_void_p(X.data_ptr()),
                                           ctypes.c_void_p(out_gate.data_ptr()), ctypes.c_void_p(out_up.data_ptr()),
-                                          M, _stream_ptr(stream))
+                                          X.shape[0], _stream_ptr(stream))
     _check(st, "lr_mlp_packed_run")
     return out_gate, out_up
+
+
+def group_run(projs, X, outs=None, stream=None):
+    """Ys[i] = (X.A_i).B_i for up to LR_GROUP_MAX projections sharing X,
+    in shared launches (lr_group_run)."""
+    _require_bf16_cuda(X, "X")
+    projs = list(projs)
+    outs = _outputs(projs, X, outs)
+    n = len(projs)
+    hs = (ctypes.c_void_p * max(n, 1))(*[p.handle.value for p in projs])
+    ys = (ctypes.c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
+    st = load_library().lr_group_run(hs, n, ctypes.c_void_p(X.data_ptr()), ys, X.shape[0], _stream_ptr(stream))
+    _check(st, "lr_group_run")
+    return outs
 
 
 def status_name(status: int) -> str:

@@ -77,6 +77,7 @@ bool xcd_round_robin(int grid);
 int decode_blocks_per_cu();
 
 // --------------------------------------------------------------- prefill ---
+constexpr int kPreMaxOut = 4;   // projections sharing X in one prefill launch
 constexpr int kPreThreads = 512;  // 8 waves (two per SIMD)
 constexpr int kPreBM = 256;       // rows per workgroup tile
 constexpr int kPreKT = 32;        // k per LDS stage (one MFMA k-step)
@@ -106,13 +107,13 @@ struct PreOut {
 };
 struct PreArgs {
   int64_t rows;     // M
-  int nout;         // 1 or 2 column blocks
+  int nout;         // 1 .. kPreMaxOut column blocks (projections sharing P's rows)
   int row_tiles;
   int nb;           // MFMA column blocks per wave: the tile is 32 * nb columns wide
   int splits;       // k-splits per tile (1: the GEMM writes bf16 C itself)
   int split_steps;  // 32-deep k-steps per split
   int pad_;
-  PreOut o[2];
+  PreOut o[kPreMaxOut];
 };
 hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream);
 // One wave per SIMD, 256 x 256 tiles, for a 16-byte aligned P (nb = 8, even

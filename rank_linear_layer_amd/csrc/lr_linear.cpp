@@ -160,27 +160,93 @@ lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, con
 
 // One prefill phase: C_i = P_i . Q_i for the n outputs, then the k-split
 // reduction if the plan splits k.
-lr_status prefill_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, int64_t kd, int phase,
-                        hipStream_t stream, const char* what) {
-  const int cus = num_cus(hs[0]->device);
-  int64_t cols[2] = {0, 0};
-  for (int i = 0; i < n; ++i) cols[i] = a.o[i].out_cols;
-  // the one-wave-per-SIMD kernel loads P straight into LDS (16-byte aligned
-  // rows only) and is specialised on the weight leading dimension mod 8
-  bool w4 = true;
-  for (int i = 0; i < n; ++i)
-    w4 = w4 && a.o[i].ldp % 8 == 0 && reinterpret_cast<uintptr_t>(a.o[i].P) % 16 == 0 &&
-         a.o[i].ldq % 8 == a.o[0].ldq % 8;
-  const uint32_t fl = hs[0]->flags;
+// The one-wave-per-SIMD kernel loads P straight into LDS (16-byte aligned
+// rows only) and is specialised on the weight leading dimension mod 8.
+bool w4_operands(const lrk::PreOut& o) {
+  return o.ldp % 8 == 0 && reinterpret_cast<uintptr_t>(o.P) % 16 == 0;
+}
+
+// Kernel kinds the handles' flags allow for outputs whose operands do (w4)
+// or do not suit the one-wave kernel.
+int allowed_kinds(const lr_linear* h, bool w4) {
   int kinds = lrv::kPlanTwoWave | (w4 ? lrv::kPlanOneWave : 0);
-  if (fl & LR_FLAG_PREFILL_TWO_WAVE) kinds = lrv::kPlanTwoWave;
-  if ((fl & LR_FLAG_PREFILL_ONE_WAVE) && w4) kinds = lrv::kPlanOneWave;
+  if (h->flags & LR_FLAG_PREFILL_TWO_WAVE) kinds = lrv::kPlanTwoWave;
+  if ((h->flags & LR_FLAG_PREFILL_ONE_WAVE) && w4) kinds = lrv::kPlanOneWave;
+  return kinds;
+}
+
+// Plan of one launch over outputs o[0..n), shrunk to one split when a
+// handle's partial buffer cannot hold the planned split count.
+lrv::PrePlan plan_launch(const lr_linear* const* hs, const lrk::PreArgs& a, int n, int64_t kd, int kinds) {
+  const int cus = num_cus(hs[0]->device);
+  int64_t cols[lrk::kPreMaxOut] = {};
+  for (int i = 0; i < n; ++i) cols[i] = a.o[i].out_cols;
   const bool q_aligned = a.o[0].ldq % 8 == 0;
   lrv::PrePlan pl = lrv::prefill_plan(a.rows, cols, n, kd, cus, 32, kinds, q_aligned);
   for (int i = 0; i < n && pl.splits > 1; ++i) {
     const int64_t need = (int64_t)pl.splits * a.rows * lrv::round_up(cols[i], 4) * 4;
     if (need > hs[i]->part_bytes) pl = lrv::prefill_plan(a.rows, cols, n, kd, cus, 1, kinds, q_aligned);
   }
+  return pl;
+}
+
+lr_status launch_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, const lrv::PrePlan& pl, int phase,
+                       hipStream_t stream, const char* what);
+
+// One prefill phase: C_i = P_i . Q_i for the n outputs, then the k-split
+// reduction if the plan splits k.  Outputs whose weights differ in leading
+// dimension mod 8 cannot share a one-wave launch; they run as one two-wave
+// launch or as one launch per residue class, whichever the cost model
+// prefers.
+lr_status prefill_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, int64_t kd, int phase,
+                        hipStream_t stream, const char* what) {
+  bool w4 = true, same_mod = true;
+  for (int i = 0; i < n; ++i) {
+    w4 = w4 && w4_operands(a.o[i]);
+    same_mod = same_mod && a.o[i].ldq % 8 == a.o[0].ldq % 8;
+  }
+  const int kinds_all = allowed_kinds(hs[0], w4);
+  const lrv::PrePlan joint = plan_launch(hs, a, n, kd, same_mod ? kinds_all : lrv::kPlanTwoWave);
+  if (same_mod || !(kinds_all & lrv::kPlanOneWave) || (hs[0]->flags & LR_FLAG_PREFILL_TWO_WAVE))
+    return launch_phase(hs, a, n, joint, phase, stream, what);
+  // residue classes of the weight leading dimension, in first-seen order
+  lrk::PreArgs sub[lrk::kPreMaxOut];
+  const lr_linear* sub_hs[lrk::kPreMaxOut][lrk::kPreMaxOut];
+  int64_t sub_kd[lrk::kPreMaxOut] = {};
+  int64_t mods[lrk::kPreMaxOut];
+  int ng = 0;
+  for (int i = 0; i < n; ++i) {
+    int g = 0;
+    while (g < ng && mods[g] != a.o[i].ldq % 8) ++g;
+    if (g == ng) {
+      mods[ng] = a.o[i].ldq % 8;
+      sub[ng] = a;
+      sub[ng].nout = 0;
+      ++ng;
+    }
+    sub_hs[g][sub[g].nout] = hs[i];
+    sub[g].o[sub[g].nout++] = a.o[i];
+    sub_kd[g] = sub_kd[g] > a.o[i].kd ? sub_kd[g] : a.o[i].kd;
+  }
+  lrv::PrePlan plans[lrk::kPreMaxOut];
+  double split_cost = 0;
+  for (int g = 0; g < ng; ++g) {
+    plans[g] = plan_launch(sub_hs[g], sub[g], sub[g].nout, sub_kd[g], kinds_all);
+    split_cost += plans[g].cost;
+  }
+  if (!(hs[0]->flags & LR_FLAG_PREFILL_ONE_WAVE) && joint.cost <= split_cost)
+    return launch_phase(hs, a, n, joint, phase, stream, what);
+  for (int g = 0; g < ng; ++g) {
+    const lr_status st = launch_phase(sub_hs[g], sub[g], sub[g].nout, plans[g], phase, stream, what);
+    if (st != LR_OK) return st;
+  }
+  return LR_OK;
+}
+
+lr_status launch_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, const lrv::PrePlan& pl, int phase,
+                       hipStream_t stream, const char* what) {
+  int64_t cols[lrk::kPreMaxOut] = {};
+  for (int i = 0; i < n; ++i) cols[i] = a.o[i].out_cols;
   for (int i = 0; i < n; ++i) {
     hs[i]->last_plan[phase][0] = pl.kind;
     hs[i]->last_plan[phase][1] = pl.nb;
@@ -208,7 +274,7 @@ lr_status prefill_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, int6
 
 lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                       hipStream_t stream) {
-  // phase 1: T_i = X . A_i (both projections in one launch)
+  // phase 1: T_i = X . A_i (the projections share X in one launch)
   lrk::PreArgs a1;
   memset(&a1, 0, sizeof a1);
   a1.rows = M;
@@ -251,6 +317,44 @@ lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, co
     kd2 = kd2 > h->r_pad ? kd2 : h->r_pad;
   }
   return prefill_phase(hs, a2, n, kd2, 1, stream, "prefill phase-2 launch");
+}
+
+// n projections sharing X.  Those that take the decode kernel at this M
+// share decode launches, packed greedily in order while every workgroup of a
+// launch can be resident at once (the exchange groups need that) and the
+// kernel kind agrees; the rest share one prefill launch per phase.
+static_assert(lrk::kDecMaxProj >= lrv::kMaxGroup && lrk::kPreMaxOut >= lrv::kMaxGroup, "group size");
+lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
+                    hipStream_t stream) {
+  const lr_linear* dh[lrk::kDecMaxProj];
+  uint16_t* dy[lrk::kDecMaxProj];
+  const lr_linear* ph[lrk::kPreMaxOut];
+  uint16_t* py[lrk::kPreMaxOut];
+  int nd = 0, np = 0;
+  for (int i = 0; i < n; ++i) {
+    if (use_decode(hs[i], M)) {
+      dh[nd] = hs[i];
+      dy[nd++] = Ys[i];
+    } else {
+      ph[np] = hs[i];
+      py[np++] = Ys[i];
+    }
+  }
+  for (int b = 0; b < nd;) {
+    const int per_cu = dh[b]->dp.kind == 1 ? 1 : lrk::decode_blocks_per_cu();
+    const int64_t cap = (int64_t)num_cus(dh[b]->device) * per_cu;
+    int64_t wgs = (int64_t)dh[b]->dp.Jw * dh[b]->dp.S;
+    int e = b + 1;
+    while (e < nd && dh[e]->dp.kind == dh[b]->dp.kind && wgs + (int64_t)dh[e]->dp.Jw * dh[e]->dp.S <= cap) {
+      wgs += (int64_t)dh[e]->dp.Jw * dh[e]->dp.S;
+      ++e;
+    }
+    const lr_status st = run_decode(dh + b, dy + b, e - b, X, M, stream);
+    if (st != LR_OK) return st;
+    b = e;
+  }
+  if (np > 0) return run_prefill(ph, py, np, X, M, stream);
+  return LR_OK;
 }
 
 }  // namespace
@@ -400,30 +504,32 @@ lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, v
   return run_prefill(hs, Ys, 1, X, M, (hipStream_t)stream);
 }
 
+lr_status lr_group_run(const lr_linear* const* hs, int n, const void* X, void* const* Ys, int64_t M, void* stream) {
+  if (!hs || !Ys) return fail(LR_ERR_INVALID_ARG, "handle and output arrays must be non-null");
+  if (n < 1 || n > lrv::kMaxGroup) return fail(LR_ERR_INVALID_ARG, "n=%d projections; 1 to %d share X", n, lrv::kMaxGroup);
+  lrv::Shape s[lrv::kMaxGroup];
+  const void* yv[lrv::kMaxGroup];
+  uint16_t* ys[lrv::kMaxGroup];
+  for (int i = 0; i < n; ++i) {
+    if (!hs[i]) return fail(LR_ERR_INVALID_ARG, "handle %d is null", i);
+    for (int j = 0; j < i; ++j)
+      if (hs[j] == hs[i])
+        return fail(LR_ERR_INVALID_ARG, "handles %d and %d are the same (each owns a workspace)", j, i);
+    s[i] = lrv::Shape{hs[i]->K, hs[i]->r, hs[i]->N, hs[i]->max_M, hs[i]->A, hs[i]->B};
+    yv[i] = Ys[i];
+    ys[i] = (uint16_t*)Ys[i];
+  }
+  const lr_status st = lrv::check_group(s, n, X, yv, M, g_err, sizeof g_err);
+  if (st != LR_OK || M == 0) return st;
+  return run_group(hs, ys, n, X, M, (hipStream_t)stream);
+}
+
 lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const void* X, void* Y_gate, void* Y_up,
                             int64_t M, void* stream) {
   if (!gate || !up) return fail(LR_ERR_INVALID_ARG, "gate and up handles must be non-null");
-  if (gate == up) return fail(LR_ERR_INVALID_ARG, "gate and up must be distinct handles (each owns a workspace)");
-  lrv::Shape sg{gate->K, gate->r, gate->N, gate->max_M, gate->A, gate->B};
-  lrv::Shape su{up->K, up->r, up->N, up->max_M, up->A, up->B};
-  lr_status st = lrv::check_packed(sg, su, X, Y_gate, Y_up, M, g_err, sizeof g_err);
-  if (st != LR_OK || M == 0) return st;
-  const bool dg = use_decode(gate, M), du = use_decode(up, M);
-  if (dg != du) return fail(LR_ERR_UNSUPPORTED, "gate and up handles choose different kernels for M=%lld", (long long)M);
-  uint16_t* Ys[2] = {(uint16_t*)Y_gate, (uint16_t*)Y_up};
   const lr_linear* hs[2] = {gate, up};
-  if (dg) {
-    // One launch when both projections' workgroups fit on the device at
-    // once (every exchange group must be resident); else one per projection.
-    const int64_t G = (int64_t)gate->dp.Jw * gate->dp.S + (int64_t)up->dp.Jw * up->dp.S;
-    const int per_cu = gate->dp.kind == 1 ? 1 : lrk::decode_blocks_per_cu();
-    if (gate->dp.kind == up->dp.kind && G <= (int64_t)num_cus(gate->device) * per_cu)
-      return run_decode(hs, Ys, 2, X, M, (hipStream_t)stream);
-    st = run_decode(hs, Ys, 1, X, M, (hipStream_t)stream);
-    if (st != LR_OK) return st;
-    return run_decode(hs + 1, Ys + 1, 1, X, M, (hipStream_t)stream);
-  }
-  return run_prefill(hs, Ys, 2, X, M, (hipStream_t)stream);
+  void* Ys[2] = {Y_gate, Y_up};
+  return lr_group_run(hs, 2, X, Ys, M, stream);
 }
 
 void lr_linear_destroy(lr_linear* h) {

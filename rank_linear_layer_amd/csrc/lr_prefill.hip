@@ -84,6 +84,16 @@ __device__ __forceinline__ void dma16(rsrc_t r, char* lds_wave_base, uint32_t of
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 16, (int)off, 0, 0, 0);
 }
 
+// Column tiles of all the outputs of a launch (outputs follow one another
+// in the tile order).
+__host__ __device__ __forceinline__ int total_col_tiles(const PreArgs& a) {
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < kPreMaxOut; ++i)
+    if (i < a.nout) n += a.o[i].col_tiles;
+  return n;
+}
+
 struct Tile {
   int bi;      // output block (0 or 1)
   int64_t mb;  // first row
@@ -94,7 +104,7 @@ struct Tile {
 // [x*q + min(x, rem), ...) of the tile order; the order is row-tile groups of
 // kGroupRows, walked column tile by column tile across both outputs.
 __device__ __forceinline__ Tile map_tile(const PreArgs& a, int bn, int bid) {
-  const int ct_total = a.o[0].col_tiles + (a.nout > 1 ? a.o[1].col_tiles : 0);
+  const int ct_total = total_col_tiles(a);
   const int total = a.row_tiles * ct_total;
   const int q = total >> 3, rem = total & 7;
   const int x = bid & 7, j = bid >> 3;
@@ -108,10 +118,12 @@ __device__ __forceinline__ Tile map_tile(const PreArgs& a, int bn, int bid) {
   int ct = within / gs;
   Tile T;
   T.bi = 0;
-  if (a.nout > 1 && ct >= a.o[0].col_tiles) {
-    T.bi = 1;
-    ct -= a.o[0].col_tiles;
-  }
+#pragma unroll
+  for (int i = 0; i + 1 < kPreMaxOut; ++i)
+    if (i + 1 < a.nout && T.bi == i && ct >= a.o[i].col_tiles) {
+      ct -= a.o[i].col_tiles;
+      T.bi = i + 1;
+    }
   T.mb = (int64_t)rt * kBM;
   T.nb = (int64_t)ct * bn;
   return T;
@@ -420,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 1) void lr_prefill_gemm_kernel(const PreA
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // workgroup -> (tile, k-split): consecutive ids are different tiles of one
   // split, so the XCD dealing of tiles is the same for every split
-  const int tiles = a.row_tiles * (a.o[0].col_tiles + (a.nout > 1 ? a.o[1].col_tiles : 0));
+  const int tiles = a.row_tiles * total_col_tiles(a);
   const int ks = (int)blockIdx.x / tiles;
   const Tile T = map_tile(a, 32 * NB, (int)blockIdx.x - ks * tiles);
   gemm_tile<NB, PAL>(a, T, ks, smem);
@@ -467,7 +479,7 @@ hipError_t launch_one(const PreArgs& args, int grid, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream) {
-  const int ct = args.o[0].col_tiles + (args.nout > 1 ? args.o[1].col_tiles : 0);
+  const int ct = total_col_tiles(args);
   const int grid = ct * args.row_tiles * args.splits;
   if (grid <= 0) return hipSuccess;
   bool pal = true;

@@ -118,6 +118,16 @@ __host__ __device__ constexpr int extra_loads() {
 // 16-column groups of Qt are permuted: column n sits at entry pos(n).
 __device__ __forceinline__ int qt_pos(int n) { return (n & ~15) | ((n & 15) ^ ((n >> 4) & 15)); }
 
+// Column tiles of all the outputs of a launch (outputs follow one another
+// in the tile order).
+__host__ __device__ __forceinline__ int total_col_tiles(const PreArgs& a) {
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < kPreMaxOut; ++i)
+    if (i < a.nout) n += a.o[i].col_tiles;
+  return n;
+}
+
 struct Tile {
   int bi;
   int64_t mb, nb;
@@ -127,7 +137,7 @@ struct Tile {
 // run of the tile order, which walks groups of four row tiles column by
 // column: the workgroups on one XCD share P and weight panels in its L2.
 __device__ __forceinline__ Tile map_tile(const PreArgs& a, int bid) {
-  const int ct_total = a.o[0].col_tiles + (a.nout > 1 ? a.o[1].col_tiles : 0);
+  const int ct_total = total_col_tiles(a);
   const int total = a.row_tiles * ct_total;
   const int q = total >> 3, rem = total & 7;
   const int x = bid & 7, j = bid >> 3;
@@ -141,10 +151,12 @@ __device__ __forceinline__ Tile map_tile(const PreArgs& a, int bid) {
   int ct = within / gs;
   Tile T;
   T.bi = 0;
-  if (a.nout > 1 && ct >= a.o[0].col_tiles) {
-    T.bi = 1;
-    ct -= a.o[0].col_tiles;
-  }
+#pragma unroll
+  for (int i = 0; i + 1 < kPreMaxOut; ++i)
+    if (i + 1 < a.nout && T.bi == i && ct >= a.o[i].col_tiles) {
+      ct -= a.o[i].col_tiles;
+      T.bi = i + 1;
+    }
   T.mb = (int64_t)rt * kBM;
   T.nb = (int64_t)ct * kBN;
   return T;
@@ -524,7 +536,7 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
 template <int QMOD>
 __global__ __launch_bounds__(kThreads, 1) void lr_prefill_w4_kernel(const PreArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int tiles = a.row_tiles * (a.o[0].col_tiles + (a.nout > 1 ? a.o[1].col_tiles : 0));
+  const int tiles = a.row_tiles * total_col_tiles(a);
   const int ks = (int)blockIdx.x / tiles;
   const Tile T = map_tile(a, (int)blockIdx.x - ks * tiles);
   if (a.o[T.bi].ldq - T.nb < kBN)
@@ -549,12 +561,13 @@ hipError_t launch_w4(const PreArgs& args, int grid, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill_w4(const PreArgs& args, hipStream_t stream) {
-  const int ct = args.o[0].col_tiles + (args.nout > 1 ? args.o[1].col_tiles : 0);
+  const int ct = total_col_tiles(args);
   const int grid = ct * args.row_tiles * args.splits;
   if (grid <= 0) return hipSuccess;
   if (args.nb != 8 || args.split_steps % 2 != 0) return hipErrorInvalidValue;
   const int qmod = (int)(args.o[0].ldq & 7);
-  if (args.nout > 1 && (int)(args.o[1].ldq & 7) != qmod) return hipErrorInvalidValue;
+  for (int i = 1; i < args.nout; ++i)
+    if ((int)(args.o[i].ldq & 7) != qmod) return hipErrorInvalidValue;
   switch (qmod) {
     case 0: return launch_w4<0>(args, grid, stream);
     case 1: return launch_w4<1>(args, grid, stream);

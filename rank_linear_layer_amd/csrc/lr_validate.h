@@ -87,25 +87,49 @@ inline lr_status check_run(const Shape& s, const void* X, const void* Y, int64_t
   return LR_OK;
 }
 
-inline lr_status check_packed(const Shape& g, const Shape& u, const void* X, const void* Yg, const void* Yu, int64_t M,
-                              char* err, size_t errlen) {
-  if (g.K != u.K) {
-    snprintf(err, errlen, "gate.K=%lld differs from up.K=%lld", (long long)g.K, (long long)u.K);
+// Projections sharing X in one call: 1..kMaxGroup handles of equal K, each
+// run checked as lr_linear_run would check it, no output overlapping another
+// output or another projection's factors.
+constexpr int kMaxGroup = LR_GROUP_MAX;
+inline lr_status check_group(const Shape* s, int n, const void* X, const void* const* Ys, int64_t M, char* err,
+                             size_t errlen) {
+  if (n < 1 || n > kMaxGroup) {
+    snprintf(err, errlen, "n=%d projections; 1 to %d share X in one call", n, kMaxGroup);
     return LR_ERR_INVALID_ARG;
   }
-  lr_status st = check_run(g, X, Yg, M, err, errlen);
-  if (st != LR_OK) return st;
-  st = check_run(u, X, Yu, M, err, errlen);
-  if (st != LR_OK) return st;
+  for (int i = 1; i < n; ++i)
+    if (s[i].K != s[0].K) {
+      snprintf(err, errlen, "projection %d has K=%lld, projection 0 has K=%lld", i, (long long)s[i].K,
+               (long long)s[0].K);
+      return LR_ERR_INVALID_ARG;
+    }
+  for (int i = 0; i < n; ++i) {
+    const lr_status st = check_run(s[i], X, Ys[i], M, err, errlen);
+    if (st != LR_OK) return st;
+  }
   if (M == 0) return LR_OK;
-  const Range rg = span(Yg, M * g.N), ru = span(Yu, M * u.N);
-  if (overlaps(rg, ru)) { snprintf(err, errlen, "Y_gate overlaps Y_up"); return LR_ERR_INVALID_ARG; }
-  if (overlaps(rg, span(u.A, u.K * u.r)) || overlaps(rg, span(u.B, u.r * u.N)) ||
-      overlaps(ru, span(g.A, g.K * g.r)) || overlaps(ru, span(g.B, g.r * g.N))) {
-    snprintf(err, errlen, "an output overlaps the other projection's factors");
-    return LR_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) {
+    const Range ri = span(Ys[i], M * s[i].N);
+    for (int j = 0; j < n; ++j) {
+      if (j == i) continue;
+      if (j > i && overlaps(ri, span(Ys[j], M * s[j].N))) {
+        snprintf(err, errlen, "outputs %d and %d overlap", i, j);
+        return LR_ERR_INVALID_ARG;
+      }
+      if (overlaps(ri, span(s[j].A, s[j].K * s[j].r)) || overlaps(ri, span(s[j].B, s[j].r * s[j].N))) {
+        snprintf(err, errlen, "output %d overlaps the factors of projection %d", i, j);
+        return LR_ERR_INVALID_ARG;
+      }
+    }
   }
   return LR_OK;
+}
+
+inline lr_status check_packed(const Shape& g, const Shape& u, const void* X, const void* Yg, const void* Yu, int64_t M,
+                              char* err, size_t errlen) {
+  const Shape s[2] = {g, u};
+  const void* Ys[2] = {Yg, Yu};
+  return check_group(s, 2, X, Ys, M, err, errlen);
 }
 
 // ------------------------------------------------------------ partition ---
@@ -195,7 +219,8 @@ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // cheapest plan wins (fewer splits, then the wider tile, on a tie).
 struct PrePlan {
   int nb, splits, split_steps;
-  int kind;  // 0: two waves per SIMD, tile 256 x 32 nb; 1: one wave per SIMD, tile 256 x 256
+  int kind;     // 0: two waves per SIMD, tile 256 x 32 nb; 1: one wave per SIMD, tile 256 x 256
+  double cost;  // the model's cost of the plan
 };
 // Kernel, tile width and k-split for one prefill phase, from a cost model in
 // units of about 0.14 us (one 32-deep k-step of the two-wave kernel at nb = 7
@@ -217,7 +242,7 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
   const int cus = num_cus > 0 ? num_cus : 1;
   int64_t cols = 0;
   for (int i = 0; i < nout; ++i) cols += out_cols[i];
-  PrePlan best{7, 1, (int)nks, 0};
+  PrePlan best{7, 1, (int)nks, 0, 0.0};
   double best_cost = -1;
   const struct {
     int nb, kind;
@@ -239,7 +264,7 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
       if (splits > 1) cost += 14.0 + (double)(2 * splits * rows * cols * 4 + rows * cols * 2) / 700e3;
       if (best_cost < 0 || cost < best_cost - 1e-9) {
         best_cost = cost;
-        best = PrePlan{kn.nb, (int)splits, (int)steps, kn.kind};
+        best = PrePlan{kn.nb, (int)splits, (int)steps, kn.kind, cost};
       }
     }
   }

@@ -28,7 +28,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("lr_linear_create", "lr_linear_run", "lr_mlp_packed_run", "lr_linear_destroy",
+    for n in ("lr_linear_create", "lr_linear_run", "lr_mlp_packed_run", "lr_group_run", "lr_linear_destroy",
               "lr_status_str", "lr_last_error"):
         assert n in names
     assert set(names) == set(lrl.EXPORTED_SYMBOLS)
@@ -69,6 +69,17 @@ def test_create_rejects_bad_arguments_before_any_hip_call(lib):
 def test_run_and_packed_reject_null_handles(lib):
     assert lib.lr_linear_run(None, None, None, 1, None) == lrl.LR_ERR_INVALID_ARG
     assert lib.lr_mlp_packed_run(None, None, None, None, None, 1, None) == lrl.LR_ERR_INVALID_ARG
+    # group: null arrays, null handle, n out of range, a repeated handle --
+    # all rejected before the handles are read or any HIP call is made
+    assert lib.lr_group_run(None, 1, None, None, 1, None) == lrl.LR_ERR_INVALID_ARG
+    vp = ctypes.c_void_p
+    ys = (vp * 4)(0x1000, 0x2000, 0x3000, 0x4000)
+    assert lib.lr_group_run((vp * 1)(None), 1, vp(0x1000), ys, 1, None) == lrl.LR_ERR_INVALID_ARG
+    assert b"handle 0 is null" in lib.lr_last_error()
+    fake_h = (vp * 5)(0x10, 0x20, 0x30, 0x40, 0x50)
+    assert lib.lr_group_run(fake_h, 0, vp(0x1000), ys, 1, None) == lrl.LR_ERR_INVALID_ARG
+    assert lib.lr_group_run(fake_h, 5, vp(0x1000), ys, 1, None) == lrl.LR_ERR_INVALID_ARG
+    assert b"1 to 4" in lib.lr_last_error()
     lib.lr_linear_destroy(None)  # no-op
     buf = ctypes.create_string_buffer(16)
     assert lib.lr_linear_describe(None, buf, 16) == lrl.LR_ERR_INVALID_ARG

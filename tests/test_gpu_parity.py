@@ -238,6 +238,118 @@ def test_mlp_packed_one_wave():
     assert_parity(to_bits(Yu), oracle.lowrank_bf16(Xb, Aub, Bub), "packed one-wave up")
 
 
+# ----------------------------------------------------------------- group ---
+# n projections sharing X in shared launches (lr_group_run): the q, k and v
+# projections of the decoder layer, and smaller groups that reach the
+# per-residue launch split, the mixed decode/prefill split and the limits.
+
+def _layer_group(names, M):
+    projs = {p.name: (i, p) for i, p in enumerate(configs.LAYER_PROJS)}
+    Xb = datagen.normal_bf16((M, 4096), 1.0, configs.seed_base(configs.LAYER_INDEX))
+    fac = []
+    for nm in names:
+        i, p = projs[nm]
+        _, Ab, Bb = datagen.factorized_inputs(1, p.K, p.r, p.N, configs.seed_base(configs.LAYER_INDEX, i))
+        fac.append((Ab, Bb))
+    return Xb, fac
+
+
+@pytest.mark.parametrize("M", [1, 8, 64, 300])
+def test_group_qkv_matches_oracle(M):
+    banner("group qkv M=%d" % M)
+    Xb, fac = _layer_group(["q", "k", "v"], M)
+    lins = [lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M) for A, B in fac]
+    X = to_dev(Xb)
+    Ys = lrl.group_run(lins, X)
+    ys = [to_bits(Y) for Y in Ys]
+    for nm, y, (A, B) in zip("qkv", ys, fac):
+        assert_parity(y, oracle.lowrank_bf16(Xb, A, B), "group %s M=%d" % (nm, M))
+    # a repeated group call is bitwise equal; separate runs agree to the bar
+    Ys2 = lrl.group_run(lins, X)
+    assert all(np.array_equal(y, to_bits(Y2)) for y, Y2 in zip(ys, Ys2))
+    for nm, y, lin in zip("qkv", ys, lins):
+        assert_parity(y, datagen.bf16_bits_to_f32(to_bits(lin(X))).astype(np.float64), "group vs separate " + nm)
+    if M > lrl.LR_DECODE_MAX_M:
+        banner("group qkv M=%d plans: %s" % (M, " | ".join(lin.describe().split("xcd_local")[1] for lin in lins)))
+
+
+def test_group_qkv_m2048_sampled():
+    M = 2048
+    Xb, fac = _layer_group(["q", "k", "v"], M)
+    lins = [lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M) for A, B in fac]
+    Ys = lrl.group_run(lins, to_dev(Xb))
+    rows = np.array([0, 1, 255, 256, 777, 1023, 1024, 2046, 2047])
+    for nm, Y, (A, B), lin in zip("qkv", Ys, fac, lins):
+        N = B.shape[1]
+        cols = np.unique(np.concatenate([np.arange(0, 9), np.arange(250, 260), np.array([N // 2]),
+                                         np.arange(N - 9, N)]))
+        y = to_bits(Y)
+        p = assert_parity(y[np.ix_(rows, cols)], oracle.lowrank_bf16_sampled(Xb, A, B, rows, cols),
+                          "group %s M=2048 sampled" % nm)
+        assert np.all(np.isfinite(datagen.bf16_bits_to_f32(y)))
+        banner("group %s M=2048 sampled parity %s plan %s" % (nm, p, lin.describe()))
+
+
+# four projections whose A leading dimensions (r) differ mod 8 while the B
+# leading dimensions (N) agree: phase 1 runs as one two-wave launch or one
+# one-wave launch per residue class, phase 2 as one launch
+GROUP4 = [(203, 900), (150, 1300), (99, 517), (211, 260)]
+
+
+@pytest.mark.parametrize("flags", [0, lrl.LR_FLAG_PREFILL_TWO_WAVE, lrl.LR_FLAG_PREFILL_ONE_WAVE])
+@pytest.mark.parametrize("M", [40, 300])
+def test_group_four_projections_mixed_residues(M, flags):
+    K = 1024
+    banner("group4 M=%d flags=%d" % (M, flags))
+    Xb = datagen.normal_bf16((M, K), 1.0, 91)
+    fac = [datagen.factorized_inputs(1, K, r, N, 101 + 10 * i)[1:] for i, (r, N) in enumerate(GROUP4)]
+    lins = [lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M, flags=flags) for A, B in fac]
+    Ys = lrl.group_run(lins, to_dev(Xb))
+    for i, (Y, (A, B)) in enumerate(zip(Ys, fac)):
+        assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, A, B), "group4 output %d M=%d flags=%d" % (i, M, flags))
+    kinds = [_plan_kinds(lin) for lin in lins]
+    banner("group4 M=%d flags=%d kinds %s" % (M, flags, kinds))
+    if flags == lrl.LR_FLAG_PREFILL_TWO_WAVE:
+        assert all(k == (0, 0) for k in kinds)
+    if flags == lrl.LR_FLAG_PREFILL_ONE_WAVE:
+        assert all(k == (1, 1) for k in kinds)
+
+
+def test_group_mixed_decode_and_prefill():
+    # at M = 4 a FORCE_PREFILL handle takes the prefill kernels while the
+    # others share a decode launch
+    M, K = 4, 512
+    Xb = datagen.normal_bf16((M, K), 1.0, 93)
+    shapes = [(67, 700, 0), (97, 600, lrl.LR_FLAG_FORCE_PREFILL), (33, 128, 0)]
+    fac = [datagen.factorized_inputs(1, K, r, N, 201 + 10 * i)[1:] for i, (r, N, _) in enumerate(shapes)]
+    lins = [lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M, flags=f) for (A, B), (_, _, f) in zip(fac, shapes)]
+    Ys = lrl.group_run(lins, to_dev(Xb))
+    for i, (Y, (A, B)) in enumerate(zip(Ys, fac)):
+        assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, A, B), "mixed group output %d" % i)
+    assert _plan_kinds(lins[1])[0] >= 0
+
+
+def test_group_errors_on_device():
+    K = 256
+    fac = [datagen.factorized_inputs(1, K, 17, 64, 301 + i)[1:] for i in range(2)]
+    a, b = [lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=8) for A, B in fac]
+    _, A2, B2 = datagen.factorized_inputs(1, 128, 17, 64, 311)
+    c = lrl.LowRankLinear(to_dev(A2), to_dev(B2), max_M=8)
+    X = to_dev(datagen.normal_bf16((4, K), 1.0, 5))
+    with pytest.raises(lrl.LRError) as e:
+        lrl.group_run([a, a], X)
+    assert e.value.status == lrl.LR_ERR_INVALID_ARG and "same" in str(e.value)
+    with pytest.raises(lrl.LRError) as e:
+        lrl.group_run([a, c], X)
+    assert e.value.status == lrl.LR_ERR_INVALID_ARG and "K=" in str(e.value)
+    with pytest.raises(lrl.LRError) as e:
+        lrl.group_run([a, b], to_dev(datagen.normal_bf16((9, K), 1.0, 5)))  # M above max_M
+    assert e.value.status == lrl.LR_ERR_INVALID_ARG
+    Ya, Yb = lrl.group_run([a, b], X)
+    with pytest.raises(lrl.LRError):  # outputs overlap
+        lrl.group_run([a, b], X, outs=[Ya, Ya])
+
+
 # ---------------------------------------------------------------- packed ---
 
 @pytest.mark.parametrize("M", [1, 4, 64])

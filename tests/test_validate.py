@@ -32,6 +32,17 @@ int t_check_packed(long long Kg, long long Ku, long long r, long long N, unsigne
   lrv::Shape u{Ku, r, N, 64, (const void*)Au, (const void*)Bu};
   return lrv::check_packed(g, u, (const void*)X, (const void*)Yg, (const void*)Yu, M, err, sizeof err);
 }
+int t_check_group(int n, const long long* K, const long long* r, const long long* N, const unsigned long long* A,
+                  const unsigned long long* B, unsigned long long X, const unsigned long long* Y, long long M) {
+  char err[256];
+  lrv::Shape s[8];
+  const void* ys[8];
+  for (int i = 0; i < n && i < 8; ++i) {
+    s[i] = lrv::Shape{K[i], r[i], N[i], 64, (const void*)A[i], (const void*)B[i]};
+    ys[i] = (const void*)Y[i];
+  }
+  return lrv::check_group(s, n, (const void*)X, ys, M, err, sizeof err);
+}
 void t_partition(long long K, long long r, long long N, int budget, int allow_res, int* out) {
   lrv::DecPart p = lrv::decode_partition(K, r, N, budget, allow_res != 0);
   out[0] = p.Jw; out[1] = p.S; out[2] = p.ktps; out[3] = p.ntps;
@@ -63,6 +74,8 @@ def shim(tmp_path_factory):
     lib.t_check_create.argtypes = [ll, ll, ll, ull, ull, ll, ctypes.c_uint]
     lib.t_check_run.argtypes = [ll, ll, ll, ll, ull, ull, ull, ull, ll]
     lib.t_check_packed.argtypes = [ll, ll, ll, ll, ull, ull, ull, ull, ull, ull, ull, ll]
+    P = ctypes.POINTER
+    lib.t_check_group.argtypes = [ctypes.c_int, P(ll), P(ll), P(ll), P(ull), P(ull), ull, P(ull), ll]
     lib.t_partition.argtypes = [ll, ll, ll, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.t_prefill_plan.argtypes = [ll, ll, ll, ctypes.c_int, ll, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.POINTER(ctypes.c_int)]
@@ -73,6 +86,38 @@ def shim(tmp_path_factory):
 
 OK, INVALID, UNSUPPORTED = 0, 1, 2
 MB = 1 << 20
+
+
+def _group(shim, K, r, N, A, B, X, Y, M=4):
+    n = len(K)
+    ll, ull = ctypes.c_longlong, ctypes.c_ulonglong
+    arr = lambda t, v: (t * 8)(*v)
+    return shim.t_check_group(n, arr(ll, K), arr(ll, r), arr(ll, N), arr(ull, A), arr(ull, B), X, arr(ull, Y), M)
+
+
+def test_group_validation(shim):
+    # q, k, v: equal K, different r and N
+    K, r, N = [64, 64, 64], [13, 7, 7], [64, 16, 16]
+    A = [10 * MB, 11 * MB, 12 * MB]
+    B = [13 * MB, 14 * MB, 15 * MB]
+    X, Y = 20 * MB, [30 * MB, 40 * MB, 50 * MB]
+    assert _group(shim, K, r, N, A, B, X, Y) == OK
+    assert _group(shim, K[:1], r[:1], N[:1], A, B, X, Y) == OK
+    assert _group(shim, K + [64], r + [5], N + [8], A + [16 * MB], B + [17 * MB], X, Y + [60 * MB]) == OK
+    # n outside 1..4
+    assert _group(shim, [], [], [], [], [], X, []) == INVALID
+    assert _group(shim, K + K[:2], r + r[:2], N + N[:2], A + A[:2], B + B[:2], X, Y + Y[:2]) == INVALID
+    # unequal K
+    assert _group(shim, [64, 64, 32], r, N, A, B, X, Y) == INVALID
+    # output 2 overlaps output 0 (q writes 4 x 64 bf16 = 512 bytes from Y[0])
+    assert _group(shim, K, r, N, A, B, X, [Y[0], Y[1], Y[0] + 256]) == INVALID
+    assert _group(shim, K, r, N, A, B, X, [Y[0], Y[1], Y[0] + 512]) == OK
+    # an output overlaps another projection's factor, or X
+    assert _group(shim, K, r, N, A, B, X, [Y[0], B[2] + 2, Y[2]]) == INVALID
+    assert _group(shim, K, r, N, A, B, X, [Y[0], Y[1], X + 16]) == INVALID
+    # bad M for every projection; M == 0 skips the overlap checks
+    assert _group(shim, K, r, N, A, B, X, Y, M=65) == INVALID
+    assert _group(shim, K, r, N, A, B, X, [Y[0], Y[0], Y[0]], M=0) == OK
 
 
 def test_create_validation(shim):
