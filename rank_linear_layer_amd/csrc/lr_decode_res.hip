@@ -183,20 +183,32 @@ __device__ __forceinline__ void gemm2_wave(const ResCtx& c, const u32x4_t& thi, 
 }  // namespace
 
 // Optional phase timestamps (constant-rate device clock), compiled in only
-// with -DLR_DECODE_TRACE.
+// with -DLR_DECODE_TRACE.  They are held in scalar registers and stored at
+// the end of the kernel, so that no trace store sits in the vector-memory
+// counter that the phases wait on.
 #ifdef LR_DECODE_TRACE
-#define RES_TRACE_ENTRY() const uint64_t trace_entry_ = __builtin_amdgcn_s_memrealtime()
-#define RES_TRACE_ENTRY_STORE() do { if (a.trace && tid == 0) a.trace[blockIdx.x * kDecTracePoints + 15] = trace_entry_; } while (0)
-#define RES_TRACE(i)                                                                                         \
-  do {                                                                                                       \
-    if (a.trace && tid == 0) a.trace[blockIdx.x * kDecTracePoints + (i)] = __builtin_amdgcn_s_memrealtime(); \
+#define RES_TRACE_ENTRY()          \
+  uint64_t trace_t_[16] = {};      \
+  trace_t_[15] = res_trace_now()
+#define RES_TRACE_ENTRY_STORE() do { } while (0)
+#define RES_TRACE(i) trace_t_[i] = res_trace_now()
+#define RES_TRACE_FLUSH()                                                                    \
+  do {                                                                                       \
+    if (a.trace && tid == 0)                                                                 \
+      for (int i_ = 0; i_ < 16; ++i_) a.trace[blockIdx.x * kDecTracePoints + i_] = trace_t_[i_]; \
   } while (0)
+__device__ __forceinline__ uint64_t res_trace_now() {
+  uint64_t t;
+  asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t) : : "memory");
+  return t;
+}
 #else
 #define RES_TRACE_ENTRY() do { } while (0)
 #define RES_TRACE_ENTRY_STORE() do { } while (0)
 #define RES_TRACE(i) \
   do {               \
   } while (0)
+#define RES_TRACE_FLUSH() do { } while (0)
 #endif
 
 #define LR_LD8_SWITCH(v, CALL) \
@@ -518,6 +530,7 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
     }
   }
   RES_TRACE(8);
+  RES_TRACE_FLUSH();
 }
 
 hipError_t launch_decode_res(const DecArgs& args, int grid, hipStream_t stream) {
