@@ -82,6 +82,8 @@ typedef struct lr_linear lr_linear;
 #define LR_FLAG_PREFILL_ONE_WAVE 16u /* prefill with the one-wave-per-SIMD kernel (256 x 256 tiles)
                                         wherever it applies: X, or T, rows 16-byte aligned, and the
                                         same leading dimension mod 8 for both factors of a pair */
+#define LR_FLAG_DENSE    32u  /* dense fallback: form W = A.B (bf16) at create and run Y = X.W */
+#define LR_FLAG_FACTORED 64u  /* never take the dense fallback */
 
 /* Largest M that the fused decode kernel takes (more rows use prefill). */
 #define LR_DECODE_MAX_M 16
@@ -94,9 +96,21 @@ typedef struct lr_linear lr_linear;
  *   max_M  : largest M that lr_linear_run will be called with (>= 0).
  *   flags  : LR_FLAG_* bits.
  * Chooses the kernels' partitioning for this shape and allocates the
- * workspace on the current HIP device.  Launches no kernel.
- * Errors: INVALID_ARG (null/size/alignment), UNSUPPORTED (no gfx950 device,
- * unknown flags, FORCE_DECODE with max_M > 16), OUT_OF_MEMORY, HIP.
+ * workspace on the current HIP device.  Launches no kernel, except for the
+ * dense fallback: when LR_FLAG_DENSE is set, or (without LR_FLAG_FACTORED)
+ * when the factors hold at least 95% of the bytes of the K x N matrix they
+ * replace, i.e. 100 r (K + N) >= 95 K N ("LowRankArena: What Happens When
+ * You Force SVD Compression Papers to Play by the Same Rules", Q3: a dense
+ * GEMM where the retained rank saves no memory bandwidth), create forms
+ * W = A.B in bf16 (fp32 accumulation) with the prefill GEMM on the null
+ * stream, plus W in the decode kernel's operand layout, and waits for them.
+ * Runs then compute Y = X.W: decode with one workgroup per 16 columns and
+ * no exchange between workgroups, prefill with one GEMM.  W is a snapshot:
+ * A and B are not read again.  The workspace then holds W (K x N bf16) when
+ * max_M > 16 and its decode layout when decode applies.
+ * Errors: INVALID_ARG (null/size/alignment, exclusive flags together),
+ * UNSUPPORTED (no gfx950 device, unknown flags, FORCE_DECODE with
+ * max_M > 16, DENSE with a W above 2 GiB), OUT_OF_MEMORY, HIP.
  */
 lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N,
                            const void* A, const void* B, int64_t max_M, uint32_t flags);

@@ -32,6 +32,8 @@ LR_FLAG_FORCE_PREFILL = 2
 LR_FLAG_DECODE_STREAMING = 4
 LR_FLAG_PREFILL_TWO_WAVE = 8
 LR_FLAG_PREFILL_ONE_WAVE = 16
+LR_FLAG_DENSE = 32
+LR_FLAG_FACTORED = 64
 LR_DECODE_MAX_M = 16
 LR_GROUP_MAX = 4
 

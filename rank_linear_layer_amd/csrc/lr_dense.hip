@@ -1,0 +1,153 @@
+// Dense fallback: Y = X . W with W = A . B formed once when the handle is
+// created, for shapes where the factorization saves (almost) no weight bytes
+// ("LowRankArena: What Happens When You Force SVD Compression Papers to Play
+// by the Same Rules", Q3: The FLOP-savings-to-latency gap, on a method that
+// runs a layer as one dense GEMM when its retained rank saves no memory
+// bandwidth).  The k/v projections of the Llama-3-8B-shaped layer at
+// r = 817 hold 99.7% of the dense bytes.
+//
+// W itself is computed by the prefill GEMM (P = A, Q = B).  This file holds
+// the two pieces that are specific to the dense path:
+//
+//  * lr_dense_swizzle_kernel: W (row-major K x N) -> Wsw, the decode layout.
+//    Column group g (16 columns) and k-step s (32 rows) form one 1 KB block,
+//    blocks of a group stored consecutively; inside a block lane l holds the
+//    16 bytes W[32 s + 8 (l / 16) + 0..7][16 g + l % 16], which is exactly
+//    the B operand of a 16x16x32 bf16 MFMA.  Rows >= K and columns >= N are
+//    zero.
+//
+//  * lr_dense_decode_kernel (M <= 16, HBM-bound): one workgroup per column
+//    group reads that group's K x 16 slab of Wsw as whole 1 KB blocks (each
+//    wave instruction is one contiguous kilobyte) and multiplies it by X.
+//    The eight waves split K; their 16 x 16 partials are summed in LDS in
+//    wave order and written as bf16.  No workgroup exchanges anything with
+//    another, so the kernel is one HBM stream plus one LDS reduction.
+#include "lr_device.h"
+#include "lr_kernels.h"
+
+namespace lrk {
+
+namespace {
+
+constexpr int kDnThreads = 512;  // 8 waves
+constexpr int kDnWaves = kDnThreads / 64;
+constexpr int kDnChunk = 16;     // k-steps whose operands are in flight at once per wave
+
+// Elements [d, d + 8) of the 16-element window (lo, hi), d in 0..7 per lane.
+__device__ __forceinline__ u32x4_t realign_lane(const u32x4_t& lo, const u32x4_t& hi, int d) {
+  const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  const int q = d >> 1;
+  const uint32_t sh = (uint32_t)(d & 1) * 16u;
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = q == 0 ? w[i] : q == 1 ? w[i + 1] : q == 2 ? w[i + 2] : w[i + 3];
+    const uint32_t b = q == 0 ? w[i + 1] : q == 1 ? w[i + 2] : q == 2 ? w[i + 3] : w[i + 4];
+    o[i] = __builtin_amdgcn_alignbit(b, a, sh);
+  }
+  return o;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void lr_dense_swizzle_kernel(const uint16_t* W, uint16_t* Wsw, int64_t K, int64_t N,
+                                                               int64_t nk, int64_t nblocks) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (block, lane)
+  const int64_t blk = t >> 6;
+  if (blk >= nblocks) return;
+  const int l = (int)(t & 63);
+  const int64_t g = blk / nk, s = blk - g * nk;
+  const int64_t col = 16 * g + (l & 15);
+  const int64_t row0 = 32 * s + 8 * (l >> 4);
+  uint32_t e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t row = row0 + j;
+    e[j] = (row < K && col < N) ? (uint32_t)W[row * N + col] : 0u;
+  }
+  u32x4_t v;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) v[p] = e[2 * p] | (e[2 * p + 1] << 16);
+  *reinterpret_cast<u32x4_t*>(Wsw + t * 8) = v;
+}
+
+__global__ __launch_bounds__(kDnThreads) void lr_dense_decode_kernel(const DenseArgs a) {
+  __shared__ float red[kDnWaves][256];
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int64_t g = blockIdx.x;  // column group
+  const int64_t nk = a.nk;
+  // this wave's k-steps [s0, s1)
+  const int64_t per = (nk + kDnWaves - 1) / kDnWaves;
+  const int64_t s0 = min64(nk, (int64_t)w * per), s1 = min64(nk, s0 + per);
+
+  const rsrc_t rW = make_rsrc(a.Wsw + g * nk * 512, nk * 1024);
+  const rsrc_t rX = make_rsrc(a.X, (int64_t)a.M * a.K * 2);
+  // A operand of lane l: row m = l % 16 of X (rows >= M read as zero),
+  // columns 32 s + 8 (l / 16) .. + 7.  With K a multiple of 8 that is one
+  // aligned 16-byte load; otherwise the two aligned chunks around it are
+  // loaded and the lane realigns them by its row's offset.
+  const int m = l & 15;
+  const bool xal = (a.K & 7) == 0;
+  const int64_t xrow = (int64_t)m * a.K;
+  const int d = (int)(xrow & 7);
+
+  f32x4_t acc = zero4();
+  for (int64_t c0 = s0; c0 < s1; c0 += kDnChunk) {
+    u32x4_t wv[kDnChunk], xl[kDnChunk], xh[kDnChunk];
+#pragma unroll
+    for (int i = 0; i < kDnChunk; ++i) {
+      // steps past s1 read block offsets past this group's range: zeros
+      const int64_t s = c0 + i;
+      wv[i] = buf_load16(rW, (uint32_t)(s < s1 ? (s * 1024 + l * 16) : nk * 1024));
+      const int64_t e = xrow + 32 * s + 8 * (l >> 4);
+      if (xal) {
+        xl[i] = buf_load16(rX, (uint32_t)(e * 2));
+      } else {
+        xl[i] = buf_load16(rX, (uint32_t)((e >> 3) * 16));
+        xh[i] = buf_load16(rX, (uint32_t)((e >> 3) * 16 + 16));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kDnChunk; ++i) {
+      // columns >= K (the next row's elements, or bytes past X) and rows
+      // >= M are cleared: rows of W past K are zero, but 0 * NaN is not
+      const u32x4_t x = mask_cols(xal ? xl[i] : realign_lane(xl[i], xh[i], d), 32 * (c0 + i) + 8 * (l >> 4), a.K);
+      acc = mfma_16x16x32(m < a.M ? x : zerou4(), wv[i], acc);
+    }
+  }
+  // acc lane l, register t: row 4 (l / 16) + t, column l % 16
+#pragma unroll
+  for (int t = 0; t < 4; ++t) red[w][(4 * (l >> 4) + t) * 16 + (l & 15)] = acc[t];
+  __syncthreads();
+  if (tid < 256) {
+    const int row = tid >> 4, col = tid & 15;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kDnWaves; ++i) s += red[i][tid];
+    const int64_t n = 16 * g + col;
+    if (row < a.M && n < a.N) a.Y[(int64_t)row * a.N + n] = (uint16_t)f32_to_bf16_rne(s);
+  }
+}
+
+hipError_t launch_dense_swizzle(const uint16_t* W, uint16_t* Wsw, int64_t K, int64_t N, hipStream_t stream) {
+  const int64_t nk = (K + 31) / 32, ng = (N + 15) / 16;
+  const int64_t nblocks = nk * ng;
+  const int64_t threads = nblocks * 64;
+  const int64_t grid = (threads + 255) / 256;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lr_dense_swizzle_kernel, dim3((unsigned)grid), dim3(256), 0, stream, W, Wsw, K, N, nk, nblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_decode(const DenseArgs& args, hipStream_t stream) {
+  const int64_t ng = (args.N + 15) / 16;
+  if (ng <= 0 || args.M <= 0) return hipSuccess;
+  if (args.M > 16 || args.nk != (args.K + 31) / 32 || ng > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lr_dense_decode_kernel, dim3((unsigned)ng), dim3(kDnThreads), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace lrk

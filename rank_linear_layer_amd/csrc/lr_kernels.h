@@ -76,6 +76,22 @@ bool xcd_round_robin(int grid);
 // Workgroups of the decode kernel that one compute unit holds at once (0 on error).
 int decode_blocks_per_cu();
 
+// ----------------------------------------------------------------- dense ---
+// Dense fallback (W = A . B precomputed).  Wsw is W in the decode layout:
+// ceil(N/16) column groups x ceil(K/32) k-steps of 1 KB blocks, each block
+// the 16x16x32 MFMA B operand of that group and step (zero past K and N).
+struct DenseArgs {
+  const uint16_t* X;    // [M x K] bf16
+  const uint16_t* Wsw;  // decode layout of W
+  uint16_t* Y;          // [M x N] bf16
+  int64_t M, K, N;
+  int64_t nk;           // ceil(K / 32)
+};
+// Wsw from W (row-major [K x N]); Wsw holds ceil(N/16)*ceil(K/32)*512 bf16.
+hipError_t launch_dense_swizzle(const uint16_t* W, uint16_t* Wsw, int64_t K, int64_t N, hipStream_t stream);
+// Y = X . W for M <= 16: one workgroup per 16-column group, no exchange.
+hipError_t launch_dense_decode(const DenseArgs& args, hipStream_t stream);
+
 // --------------------------------------------------------------- prefill ---
 constexpr int kPreMaxOut = 4;   // projections sharing X in one prefill launch
 constexpr int kPreThreads = 512;  // 8 waves (two per SIMD)

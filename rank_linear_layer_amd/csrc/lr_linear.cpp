@@ -69,6 +69,11 @@ struct lr_linear {
   int64_t part_bytes;
   // plan of the last prefill call per phase: kernel kind, nb, splits (reported by describe)
   mutable std::atomic<int> last_plan[2][3];
+  // dense fallback: W = A.B row-major [K x N] (prefill) and in the decode
+  // layout (decode), both formed at create
+  bool dense;
+  uint16_t* W;
+  uint16_t* Wsw;
 };
 
 namespace {
@@ -136,6 +141,20 @@ int num_cus(int device) {
 #ifdef LR_DECODE_TRACE
 uint64_t* g_trace = nullptr;
 #endif
+
+lr_status run_dense_decode(const lr_linear* h, uint16_t* Y, const void* X, int64_t M, hipStream_t stream) {
+  lrk::DenseArgs a;
+  a.X = (const uint16_t*)X;
+  a.Wsw = h->Wsw;
+  a.Y = Y;
+  a.M = M;
+  a.K = h->K;
+  a.N = h->N;
+  a.nk = lrv::ceil_div(h->K, 32);
+  const hipError_t e = lrk::launch_dense_decode(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "dense decode launch");
+  return LR_OK;
+}
 
 lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                      hipStream_t stream) {
@@ -274,7 +293,8 @@ lr_status launch_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, const
 
 lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                       hipStream_t stream) {
-  // phase 1: T_i = X . A_i (the projections share X in one launch)
+  // phase 1: T_i = X . A_i, or Y_i = X . W_i for dense-fallback handles
+  // (the projections share X in one launch)
   lrk::PreArgs a1;
   memset(&a1, 0, sizeof a1);
   a1.rows = M;
@@ -286,25 +306,37 @@ lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, co
     o.P = (const uint16_t*)X;
     o.ldp = h->K;
     o.kd = h->K;
-    o.Q = h->A;
-    o.ldq = h->r;
-    o.qrows = h->K;
-    o.C = h->Tbuf;
-    o.ldc = h->r_pad;
-    o.out_cols = h->r_pad;
+    if (h->dense) {
+      o.Q = h->W;
+      o.ldq = h->N;
+      o.qrows = h->K;
+      o.C = Ys[i];
+      o.ldc = h->N;
+      o.out_cols = h->N;
+    } else {
+      o.Q = h->A;
+      o.ldq = h->r;
+      o.qrows = h->K;
+      o.C = h->Tbuf;
+      o.ldc = h->r_pad;
+      o.out_cols = h->r_pad;
+    }
   }
   lr_status st = prefill_phase(hs, a1, n, hs[0]->K, 0, stream, "prefill phase-1 launch");
   if (st != LR_OK) return st;
-  // phase 2: Y_i = T_i . B_i
+  // phase 2: Y_i = T_i . B_i for the factorized handles
   lrk::PreArgs a2;
   memset(&a2, 0, sizeof a2);
   a2.rows = M;
-  a2.nout = n;
   a2.row_tiles = a1.row_tiles;
+  const lr_linear* h2[lrk::kPreMaxOut];
+  int n2 = 0;
   int64_t kd2 = 0;
   for (int i = 0; i < n; ++i) {
     const lr_linear* h = hs[i];
-    lrk::PreOut& o = a2.o[i];
+    if (h->dense) continue;
+    lrk::PreOut& o = a2.o[n2];
+    h2[n2++] = h;
     o.P = h->Tbuf;
     o.ldp = h->r_pad;
     o.kd = h->r_pad;
@@ -316,13 +348,49 @@ lr_status run_prefill(const lr_linear* const* hs, uint16_t* const* Ys, int n, co
     o.out_cols = h->N;
     kd2 = kd2 > h->r_pad ? kd2 : h->r_pad;
   }
-  return prefill_phase(hs, a2, n, kd2, 1, stream, "prefill phase-2 launch");
+  a2.nout = n2;
+  if (n2 == 0) return LR_OK;
+  return prefill_phase(h2, a2, n2, kd2, 1, stream, "prefill phase-2 launch");
 }
 
-// n projections sharing X.  Those that take the decode kernel at this M
-// share decode launches, packed greedily in order while every workgroup of a
-// launch can be resident at once (the exchange groups need that) and the
-// kernel kind agrees; the rest share one prefill launch per phase.
+// W = A . B (bf16, row-major [K x N]) with the prefill GEMM (P = A, Q = B,
+// one split), then its decode layout when the handle decodes.
+lr_status form_dense(lr_linear* h, uint16_t* W) {
+  lrk::PreArgs a;
+  memset(&a, 0, sizeof a);
+  a.rows = h->K;
+  a.nout = 1;
+  a.row_tiles = (int)lrv::ceil_div(h->K, lrk::kPreBM);
+  lrk::PreOut& o = a.o[0];
+  o.P = h->A;
+  o.ldp = h->r;
+  o.kd = h->r;
+  o.Q = h->B;
+  o.ldq = h->N;
+  o.qrows = h->r;
+  o.C = W;
+  o.ldc = h->N;
+  o.out_cols = h->N;
+  const bool w4 = w4_operands(o);
+  const int kinds = lrv::kPlanTwoWave | (w4 ? lrv::kPlanOneWave : 0);
+  const int64_t cols = h->N;
+  const lrv::PrePlan pl = lrv::prefill_plan(h->K, &cols, 1, h->r, num_cus(h->device), 1, kinds, h->N % 8 == 0);
+  a.nb = pl.nb;
+  a.splits = 1;
+  a.split_steps = pl.split_steps;
+  o.col_tiles = (int)lrv::ceil_div(cols, 32 * pl.nb);
+  o.ldpart = lrv::round_up(cols, 4);
+  hipError_t e = pl.kind == 1 ? lrk::launch_prefill_w4(a, nullptr) : lrk::launch_prefill_gemm(a, nullptr);
+  if (e != hipSuccess) return hip_fail(e, "dense fallback: W = A.B launch");
+  if (h->Wsw) {
+    e = lrk::launch_dense_swizzle(W, h->Wsw, h->K, h->N, nullptr);
+    if (e != hipSuccess) return hip_fail(e, "dense fallback: decode layout launch");
+  }
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "dense fallback: forming W");
+  return LR_OK;
+}
+
 static_assert(lrk::kDecMaxProj >= lrv::kMaxGroup && lrk::kPreMaxOut >= lrv::kMaxGroup, "group size");
 lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                     hipStream_t stream) {
@@ -332,7 +400,10 @@ lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, cons
   uint16_t* py[lrk::kPreMaxOut];
   int nd = 0, np = 0;
   for (int i = 0; i < n; ++i) {
-    if (use_decode(hs[i], M)) {
+    if (use_decode(hs[i], M) && hs[i]->dense) {
+      const lr_status st = run_dense_decode(hs[i], Ys[i], X, M, stream);
+      if (st != LR_OK) return st;
+    } else if (use_decode(hs[i], M)) {
       dh[nd] = hs[i];
       dy[nd++] = Ys[i];
     } else {
@@ -408,11 +479,12 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
 
   h->has_decode = !(flags & LR_FLAG_FORCE_PREFILL) && max_M >= 1;
   h->has_prefill = !(flags & LR_FLAG_FORCE_DECODE) && (max_M > LR_DECODE_MAX_M || (flags & LR_FLAG_FORCE_PREFILL));
+  h->dense = lrv::choose_dense(K, r, N, flags);
 
   size_t off = 0;
   size_t o_ctrl = 0, o_tcnt = 0, o_tflag = 0, o_ycnt = 0, o_tpart = 0, o_tfin = 0, o_ypart = 0, o_tbuf = 0;
-  if (h->has_decode) {
-    h->dec_max_M = (int)(max_M < LR_DECODE_MAX_M ? max_M : LR_DECODE_MAX_M);
+  if (h->has_decode) h->dec_max_M = (int)(max_M < LR_DECODE_MAX_M ? max_M : LR_DECODE_MAX_M);
+  if (h->has_decode && !h->dense) {
     const int occ = lrk::decode_blocks_per_cu();
     if (occ < 1) {
       delete h;
@@ -444,18 +516,29 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     }
     h->dws_bytes = (int64_t)off;
   }
-  if (h->has_prefill && !lrk::prefill_available()) {
+  // the prefill kernels also form W for the dense fallback
+  if ((h->has_prefill || (h->dense && h->has_decode)) && !lrk::prefill_available()) {
     delete h;
     return fail(LR_ERR_UNSUPPORTED, "device %d cannot give a workgroup %d bytes of LDS (prefill kernel)", dev,
                 lrk::kPreLdsBytes);
   }
-  size_t o_part = 0;
+  size_t o_part = 0, o_w = 0, o_wsw = 0;
   if (h->has_prefill) {
-    o_tbuf = off;
-    off = align_up(off + (size_t)max_M * h->r_pad * 2);
-    h->part_bytes = lrv::prefill_partial_bytes(max_M, K, h->r_pad, N, num_cus(dev));
+    if (!h->dense) {
+      o_tbuf = off;
+      off = align_up(off + (size_t)max_M * h->r_pad * 2);
+    }
+    h->part_bytes = lrv::prefill_partial_bytes(max_M, K, h->r_pad, N, num_cus(dev), h->dense);
     o_part = off;
     off = align_up(off + (size_t)h->part_bytes);
+  }
+  if (h->dense && h->has_prefill) {
+    o_w = off;
+    off = align_up(off + (size_t)K * N * 2);
+  }
+  if (h->dense && h->has_decode) {
+    o_wsw = off;
+    off = align_up(off + (size_t)lrv::ceil_div(N, 16) * lrv::ceil_div(K, 32) * 1024);
   }
   h->ws_bytes = off;
   if (off > 0) {
@@ -474,7 +557,7 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     }
   }
   char* base = (char*)h->ws;
-  if (h->has_decode) {
+  if (h->has_decode && !h->dense) {
     h->dws = base;  // the decode regions start the workspace
     h->ctrl = (uint32_t*)(base + o_ctrl);
     h->tcnt = (uint32_t*)(base + o_tcnt);
@@ -486,8 +569,32 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     h->off_tflag = (uint32_t)o_tflag;
   }
   if (h->has_prefill) {
-    h->Tbuf = (uint16_t*)(base + o_tbuf);
+    h->Tbuf = h->dense ? nullptr : (uint16_t*)(base + o_tbuf);
     h->part = h->part_bytes > 0 ? (float*)(base + o_part) : nullptr;
+  }
+  if (h->dense && (h->has_decode || h->has_prefill)) {
+    // W lives in the workspace when prefill reads it; a decode-only handle
+    // keeps just the decode layout and forms W in a temporary buffer
+    void* tmp = nullptr;
+    if (h->has_prefill) {
+      h->W = (uint16_t*)(base + o_w);
+    } else {
+      e = hipMalloc(&tmp, (size_t)K * N * 2);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(h->ws);
+        delete h;
+        return fail(LR_ERR_OUT_OF_MEMORY, "dense fallback: hipMalloc(%lld) for W", (long long)(K * N * 2));
+      }
+    }
+    if (h->has_decode) h->Wsw = (uint16_t*)(base + o_wsw);
+    st = form_dense(h, h->W ? h->W : (uint16_t*)tmp);
+    if (tmp) (void)hipFree(tmp);
+    if (st != LR_OK) {
+      (void)hipFree(h->ws);
+      delete h;
+      return st;
+    }
   }
   *out = h;
   return LR_OK;
@@ -500,6 +607,7 @@ lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, v
   if (st != LR_OK || M == 0) return st;
   uint16_t* Ys[1] = {(uint16_t*)Y};
   const lr_linear* hs[1] = {h};
+  if (use_decode(h, M) && h->dense) return run_dense_decode(h, Ys[0], X, M, (hipStream_t)stream);
   if (use_decode(h, M)) return run_decode(hs, Ys, 1, X, M, (hipStream_t)stream);
   return run_prefill(hs, Ys, 1, X, M, (hipStream_t)stream);
 }
@@ -541,11 +649,11 @@ void lr_linear_destroy(lr_linear* h) {
 lr_status lr_linear_describe(const lr_linear* h, char* buf, int64_t len) {
   if (!h || !buf || len <= 0) return fail(LR_ERR_INVALID_ARG, "null handle or buffer");
   snprintf(buf, (size_t)len,
-           "K=%lld r=%lld N=%lld r_pad=%lld max_M=%lld decode=%d[kind=%s Jw=%d JS=%d S=%d ktps=%d ntps=%d grid=%d] "
+           "K=%lld r=%lld N=%lld r_pad=%lld max_M=%lld dense=%d decode=%d[kind=%s Jw=%d JS=%d S=%d ktps=%d ntps=%d grid=%d] "
            "xcd_local=%d prefill=%d[last phase1 kind=%d nb=%d splits=%d, phase2 kind=%d nb=%d splits=%d] "
            "workspace=%zu",
            (long long)h->K, (long long)h->r, (long long)h->N, (long long)h->r_pad, (long long)h->max_M,
-           (int)h->has_decode, h->dp.kind == 1 ? "resident" : "streaming", h->dp.Jw, h->dp.js_w, h->dp.S, h->dp.ktps, h->dp.ntps, h->dp.Jw * h->dp.S, (int)h->xcd_local, (int)h->has_prefill,
+           (int)h->dense, (int)h->has_decode, h->dp.kind == 1 ? "resident" : "streaming", h->dp.Jw, h->dp.js_w, h->dp.S, h->dp.ktps, h->dp.ntps, h->dp.Jw * h->dp.S, (int)h->xcd_local, (int)h->has_prefill,
            h->last_plan[0][0].load(), h->last_plan[0][1].load(), h->last_plan[0][2].load(), h->last_plan[1][0].load(),
            h->last_plan[1][1].load(), h->last_plan[1][2].load(), h->ws_bytes);
   return LR_OK;

@@ -48,7 +48,7 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
     return LR_ERR_UNSUPPORTED;
   }
   const uint32_t known = LR_FLAG_FORCE_DECODE | LR_FLAG_FORCE_PREFILL | LR_FLAG_DECODE_STREAMING |
-                         LR_FLAG_PREFILL_TWO_WAVE | LR_FLAG_PREFILL_ONE_WAVE;
+                         LR_FLAG_PREFILL_TWO_WAVE | LR_FLAG_PREFILL_ONE_WAVE | LR_FLAG_DENSE | LR_FLAG_FACTORED;
   if (flags & ~known) { snprintf(err, errlen, "unknown flag bits 0x%x", flags & ~known); return LR_ERR_UNSUPPORTED; }
   if ((flags & LR_FLAG_FORCE_DECODE) && (flags & LR_FLAG_FORCE_PREFILL)) {
     snprintf(err, errlen, "FORCE_DECODE and FORCE_PREFILL are exclusive");
@@ -58,11 +58,31 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
     snprintf(err, errlen, "PREFILL_TWO_WAVE and PREFILL_ONE_WAVE are exclusive");
     return LR_ERR_INVALID_ARG;
   }
+  if ((flags & LR_FLAG_DENSE) && (flags & LR_FLAG_FACTORED)) {
+    snprintf(err, errlen, "DENSE and FACTORED are exclusive");
+    return LR_ERR_INVALID_ARG;
+  }
+  if ((flags & LR_FLAG_DENSE) && K * N * 2 > kMaxMatrixBytes) {
+    snprintf(err, errlen, "DENSE: W = A.B (%lld x %lld) would exceed 2 GiB", (long long)K, (long long)N);
+    return LR_ERR_UNSUPPORTED;
+  }
   if ((flags & LR_FLAG_FORCE_DECODE) && max_M > kDecodeMaxM) {
     snprintf(err, errlen, "FORCE_DECODE needs max_M <= %d (got %lld)", kDecodeMaxM, (long long)max_M);
     return LR_ERR_UNSUPPORTED;
   }
   return LR_OK;
+}
+
+// Dense fallback choice: forced by a flag, else taken when the factors hold
+// at least 95% of the bytes of the K x N matrix they replace (the
+// factorization then saves almost no HBM traffic, and one GEMM without a T
+// hand-off is faster) and W is addressable through a 32-bit range.
+constexpr int64_t kDensePercent = 95;
+inline bool choose_dense(int64_t K, int64_t r, int64_t N, uint32_t flags) {
+  if (flags & LR_FLAG_FACTORED) return false;
+  if (flags & LR_FLAG_DENSE) return true;
+  if (K * N * 2 > kMaxMatrixBytes) return false;
+  return 100 * r * (K + N) >= kDensePercent * K * N;
 }
 
 struct Shape {
@@ -273,7 +293,9 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
 
 // fp32 partial bytes a handle needs for its own output over every M <= max_M
 // (both phases share the region; M steps of 256 change the tiling).
-inline int64_t prefill_partial_bytes(int64_t max_M, int64_t K, int64_t r_pad, int64_t N, int num_cus) {
+// For a dense-fallback handle the one GEMM is X . W (N columns, depth K).
+inline int64_t prefill_partial_bytes(int64_t max_M, int64_t K, int64_t r_pad, int64_t N, int num_cus,
+                                     bool dense = false) {
   // Within one 256-row bucket the tiling is fixed and larger M only makes
   // splitting costlier, so the split count at the bucket's smallest M times
   // its largest M bounds every M in the bucket.
@@ -284,9 +306,10 @@ inline int64_t prefill_partial_bytes(int64_t max_M, int64_t K, int64_t r_pad, in
     const int64_t c1 = r_pad, c2 = N;
     for (int kinds = 1; kinds <= 3; ++kinds) {
       for (int qa = 0; qa < 2; ++qa) {
-        const PrePlan p1 = prefill_plan(lo, &c1, 1, K, num_cus, 32, kinds, qa != 0);
-        const PrePlan p2 = prefill_plan(lo, &c2, 1, r_pad, num_cus, 32, kinds, qa != 0);
-        const int64_t n1 = p1.splits > 1 ? p1.splits * hi * round_up(c1, 4) * 4 : 0;
+        const int64_t cd = dense ? c2 : c1;
+        const PrePlan p1 = prefill_plan(lo, &cd, 1, K, num_cus, 32, kinds, qa != 0);
+        const PrePlan p2 = prefill_plan(lo, &c2, 1, dense ? K : r_pad, num_cus, 32, kinds, qa != 0);
+        const int64_t n1 = p1.splits > 1 ? p1.splits * hi * round_up(cd, 4) * 4 : 0;
         const int64_t n2 = p2.splits > 1 ? p2.splits * hi * round_up(c2, 4) * 4 : 0;
         need = need > n1 ? need : n1;
         need = need > n2 ? need : n2;

@@ -27,7 +27,11 @@ def gpu():
     return torch
 
 
-def run_case(M, K, r, N, seed, flags=0, max_M=None, full=True, rows=None, cols=None):
+def run_case(M, K, r, N, seed, flags=0, max_M=None, full=True, rows=None, cols=None, auto=False):
+    # the factorized kernels unless a case asks for the dense fallback or
+    # for the library's own choice (auto)
+    if not auto and not flags & lrl.LR_FLAG_DENSE:
+        flags |= lrl.LR_FLAG_FACTORED
     banner("case M=%d K=%d r=%d N=%d flags=%d seed=%d" % (M, K, r, N, flags, seed))
     Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, seed)
     lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=max_M or M, flags=flags)
@@ -303,7 +307,9 @@ def test_group_four_projections_mixed_residues(M, flags):
     banner("group4 M=%d flags=%d" % (M, flags))
     Xb = datagen.normal_bf16((M, K), 1.0, 91)
     fac = [datagen.factorized_inputs(1, K, r, N, 101 + 10 * i)[1:] for i, (r, N) in enumerate(GROUP4)]
-    lins = [lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M, flags=flags) for A, B in fac]
+    # (211, 260) would take the dense fallback by itself: kept factorized here
+    f = flags | lrl.LR_FLAG_FACTORED
+    lins = [lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M, flags=f) for A, B in fac]
     Ys = lrl.group_run(lins, to_dev(Xb))
     for i, (Y, (A, B)) in enumerate(zip(Ys, fac)):
         assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, A, B), "group4 output %d M=%d flags=%d" % (i, M, flags))
@@ -374,13 +380,76 @@ def test_mlp_packed_matches_oracle_and_separate_runs(M):  # noqa: C901
     assert np.array_equal(yg, to_bits(Yg2)) and np.array_equal(yu, to_bits(Yu2))
 
 
+# ----------------------------------------------------------- dense fallback ---
+# W = A.B formed at create; decode reads its MFMA-operand layout with no
+# exchange between workgroups, prefill runs X.W through the prefill GEMM.
+# Cases: the k/v layer shape (auto: its factors hold 99.7% of the dense
+# bytes), forced on the q shape, misaligned K (X rows realigned per lane),
+# N past a 16-column group, ragged M, tiny shapes.
+DENSE_CASES = [(1, 4096, 817, 1024, 0), (8, 4096, 817, 1024, 0), (16, 4096, 817, 1024, 0),
+               (8, 4096, 1637, 4096, lrl.LR_FLAG_DENSE), (5, 1001, 700, 300, lrl.LR_FLAG_DENSE),
+               (16, 4096, 1063, 3999, lrl.LR_FLAG_DENSE), (1, 8, 3, 1, 0), (3, 33, 40, 17, 0),
+               (300, 1024, 645, 1000, lrl.LR_FLAG_DENSE), (40, 520, 400, 300, lrl.LR_FLAG_DENSE),
+               (513, 1001, 900, 700, 0), (4, 64, 5, 48, lrl.LR_FLAG_DENSE | lrl.LR_FLAG_FORCE_PREFILL)]
+
+
+def _expect_dense(K, r, N, flags):
+    """The library's rule: forced, or the factors hold >= 95% of K x N."""
+    if flags & lrl.LR_FLAG_DENSE:
+        return True
+    return 100 * r * (K + N) >= 95 * K * N
+
+
+@pytest.mark.parametrize("M,K,r,N,flags", DENSE_CASES)
+def test_dense_fallback(M, K, r, N, flags):
+    assert _expect_dense(K, r, N, flags)
+    p, lin, _, _ = run_case(M, K, r, N, 9100 + M + K + r + N, flags=flags, auto=True)
+    assert "dense=1" in lin.describe()
+    banner("dense M=%d K=%d r=%d N=%d flags=%d parity %s" % (M, K, r, N, flags, p))
+
+
+def test_dense_fallback_m2048_sampled():
+    # the k/v projection at M = 2048: one GEMM X.W instead of two
+    proj = {p.name: p for p in configs.LAYER_PROJS}["k"]
+    rows = np.array([0, 1, 255, 256, 1500, 2047])
+    cols = np.unique(np.concatenate([np.arange(0, 9), np.arange(500, 520), np.arange(proj.N - 9, proj.N)]))
+    p, lin, _, _ = run_case(2048, proj.K, proj.r, proj.N, 9300, flags=lrl.LR_FLAG_DENSE, full=False,
+                            rows=rows, cols=cols)
+    assert "dense=1" in lin.describe()
+    banner("dense k M=2048 sampled parity %s plan %s" % (p, lin.describe()))
+
+
+def test_dense_choice_follows_the_rule():
+    K = 512
+    for r, N, flags in [(107, 512, 0), (250, 512, 0), (240, 512, 0), (250, 512, lrl.LR_FLAG_FACTORED),
+                        (20, 512, lrl.LR_FLAG_DENSE)]:
+        _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 17)
+        lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=4, flags=flags)
+        want = _expect_dense(K, r, N, flags) and not flags & lrl.LR_FLAG_FACTORED
+        assert ("dense=1" in lin.describe()) == want, (r, N, flags, lin.describe())
+
+
+def test_group_mixed_dense_and_factored():
+    # q factorized, k and v dense (auto) in one group: decode and prefill
+    for M in (4, 300):
+        Xb, fac = _layer_group(["q", "k", "v"], M)
+        lins = [lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M) for A, B in fac]
+        assert [("dense=1" in lin.describe()) for lin in lins] == [False, True, True]
+        Ys = lrl.group_run(lins, to_dev(Xb))
+        for nm, Y, (A, B) in zip("qkv", Ys, fac):
+            assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, A, B), "mixed group %s M=%d" % (nm, M))
+
+
 # ----------------------------------------------------- invariants/edges ---
 
-@pytest.mark.parametrize("M,N,flags", [(3, 3999, 0), (33, 3999, 0), (5, 241, lrl.LR_FLAG_FORCE_PREFILL)])
+@pytest.mark.parametrize("M,N,flags", [(3, 3999, 0), (33, 3999, 0), (5, 241, lrl.LR_FLAG_FORCE_PREFILL),
+                                       (3, 241, lrl.LR_FLAG_DENSE), (33, 3999, lrl.LR_FLAG_DENSE)])
 def test_canary_guards_and_poison(gpu, M, N, flags):
     torch = gpu
     K, r = 256, 37
-    banner("canary M=%d N=%d" % (M, N))
+    if not flags & lrl.LR_FLAG_DENSE:
+        flags |= lrl.LR_FLAG_FACTORED
+    banner("canary M=%d N=%d flags=%d" % (M, N, flags))
     Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 77)
     lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=flags)
     G = 64  # guard elements on each side (128 bytes keeps Y 16-byte aligned)

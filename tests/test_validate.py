@@ -43,6 +43,9 @@ int t_check_group(int n, const long long* K, const long long* r, const long long
   }
   return lrv::check_group(s, n, (const void*)X, ys, M, err, sizeof err);
 }
+int t_choose_dense(long long K, long long r, long long N, unsigned flags) {
+  return lrv::choose_dense(K, r, N, flags) ? 1 : 0;
+}
 void t_partition(long long K, long long r, long long N, int budget, int allow_res, int* out) {
   lrv::DecPart p = lrv::decode_partition(K, r, N, budget, allow_res != 0);
   out[0] = p.Jw; out[1] = p.S; out[2] = p.ktps; out[3] = p.ntps;
@@ -76,6 +79,7 @@ def shim(tmp_path_factory):
     lib.t_check_packed.argtypes = [ll, ll, ll, ll, ull, ull, ull, ull, ull, ull, ull, ll]
     P = ctypes.POINTER
     lib.t_check_group.argtypes = [ctypes.c_int, P(ll), P(ll), P(ll), P(ull), P(ull), ull, P(ull), ll]
+    lib.t_choose_dense.argtypes = [ll, ll, ll, ctypes.c_uint]
     lib.t_partition.argtypes = [ll, ll, ll, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.t_prefill_plan.argtypes = [ll, ll, ll, ctypes.c_int, ll, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.POINTER(ctypes.c_int)]
@@ -125,7 +129,13 @@ def test_create_validation(shim):
     assert shim.t_check_create(4096, 1637, 4096, 0, 0x2000000, 16, 0) == INVALID
     assert shim.t_check_create(4096, 0, 4096, 0x100000, 0x2000000, 16, 0) == INVALID
     assert shim.t_check_create(4096, 1637, 4096, 0x100008, 0x2000000, 16, 0) == INVALID  # 8B aligned only
-    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 32) == UNSUPPORTED  # unknown flag
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 128) == UNSUPPORTED  # unknown flag
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 32) == OK  # DENSE
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 64) == OK  # FACTORED
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 96) == INVALID  # both
+    # DENSE needs W = A.B (K x N bf16) inside a 32-bit range; the factors alone fit
+    assert shim.t_check_create(40000, 8, 40000, 0x100000, 0x2000000, 16, 32) == UNSUPPORTED
+    assert shim.t_check_create(40000, 8, 40000, 0x100000, 0x2000000, 16, 0) == OK
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 4096, 8) == OK      # PREFILL_TWO_WAVE
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 4096, 16) == OK     # PREFILL_ONE_WAVE
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 4096, 24) == INVALID  # both
@@ -133,6 +143,26 @@ def test_create_validation(shim):
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 17, 1) == UNSUPPORTED
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 17, 2) == OK
     assert shim.t_check_create(1 << 25, 8, 8, 0x100000, 0x2000000, 1, 0) == INVALID
+
+
+def test_dense_fallback_choice(shim):
+    # taken when the factors hold >= 95% of the dense matrix's bytes:
+    # r (K + N) >= 0.95 K N, or when forced; never with FACTORED
+    assert shim.t_choose_dense(4096, 817, 1024, 0) == 1     # k/v: 99.7%
+    assert shim.t_choose_dense(4096, 1637, 4096, 0) == 0    # q/o: 80%
+    assert shim.t_choose_dense(4096, 2867, 14336, 0) == 0   # gate/up: 90%
+    assert shim.t_choose_dense(14336, 2867, 4096, 0) == 0   # down: 90%
+    assert shim.t_choose_dense(4096, 1100, 3999, 0) == 0    # sweep
+    assert shim.t_choose_dense(512, 107, 512, 0) == 0       # tiny config
+    assert shim.t_choose_dense(512, 250, 512, 0) == 1       # 97.7%
+    assert shim.t_choose_dense(512, 243, 512, 0) == 0       # 94.9%
+    assert shim.t_choose_dense(512, 244, 512, 0) == 1       # 95.3%
+    assert shim.t_choose_dense(4096, 1637, 4096, 32) == 1   # forced
+    assert shim.t_choose_dense(4096, 817, 1024, 64) == 0    # FACTORED
+    assert shim.t_choose_dense(40000, 39999, 40000, 0) == 0  # W past a 32-bit range
+    # the rule against exact integers
+    for K, r, N in [(7, 3, 5), (100, 49, 100), (100, 48, 100), (33, 40, 17)]:
+        assert shim.t_choose_dense(K, r, N, 0) == int(100 * r * (K + N) >= 95 * K * N)
 
 
 def test_run_validation_overlap_and_range(shim):
