@@ -147,7 +147,7 @@ def bench_prefill(torch, lrl, configs, metrics, steps, warmup):
     return dict(M=M, K=K, r=r, N=N, ms=ms, tflops=fl / (ms * 1e-3) / 1e12, flops=fl, plan=lin.describe())
 
 
-def bench_layer(torch, lrl, configs, metrics, M, steps, warmup, grouped=True):
+def bench_layer(torch, lrl, configs, metrics, M, steps, warmup, grouped=True, graph=False):
     """One decoder layer of factorized projections (q, k, v, o, packed
     gate/up, down) at M rows: the layer's span per step.  q, k and v share X
     in one group call (or three separate calls with grouped=False).  Weights
@@ -181,11 +181,26 @@ def bench_layer(torch, lrl, configs, metrics, M, steps, warmup, grouped=True):
         lrl.mlp_packed(L["gate"], L["up"], X, out_gate=outs["gate"], out_up=outs["up"])
         L["down"](H, out=outs["down"])
 
-    ms = time_steps(torch, step, steps, warmup, torch.cuda.current_stream())
+    if graph:
+        # one captured graph holds a layer step per weight copy; a replay is
+        # ncop layers with no host launch work between the kernels
+        for i in range(ncop):
+            step(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(ncop):
+                step(i)
+        reps = max(1, steps // ncop)
+        ms = time_steps(torch, lambda i: g.replay(), reps, max(1, warmup // ncop), torch.cuda.current_stream()) / ncop
+        del g
+    else:
+        ms = time_steps(torch, step, steps, warmup, torch.cuda.current_stream())
     byts = sum(metrics.decode_bytes(M, p.K, p.r, p.N) for p in configs.LAYER_PROJS)
     fl = sum(metrics.lowrank_flops(M, p.K, p.r, p.N) for p in configs.LAYER_PROJS)
+    dense = [nm for nm, lin in sets[0].items() if "dense=1" in lin.describe()]
     return dict(M=M, ms=ms, tbs=byts / (ms * 1e-3) / 1e12, tflops=fl / (ms * 1e-3) / 1e12, bytes=byts, flops=fl,
-                calls=4 if grouped else 6, copies=ncop)
+                calls=4 if grouped else 6, copies=ncop, dense=dense)
 
 
 def cpu_baseline(configs, datagen, metrics, budget_s=12.0):
@@ -353,20 +368,27 @@ def main():
             steps_, warm_ = (200, 20) if M <= 16 else (10, 2)
             d_ = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_)
             sep = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_, grouped=False)
+            gr = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_, graph=True)
             log("layer M=%d: %.1f us/layer, %.3f TB/s, %.1f TFLOP/s (%d library calls, %d weight copies); "
-                "q, k, v as separate calls: %.1f us/layer"
-                % (M, d_["ms"] * 1e3, d_["tbs"], d_["tflops"], d_["calls"], d_["copies"], sep["ms"] * 1e3))
+                "q, k, v as separate calls: %.1f us/layer; replayed as a HIP graph: %.1f us/layer"
+                % (M, d_["ms"] * 1e3, d_["tbs"], d_["tflops"], d_["calls"], d_["copies"], sep["ms"] * 1e3,
+                   gr["ms"] * 1e3))
             if M <= 16:
                 lay["M%d" % M] = {"us_per_layer": round(d_["ms"] * 1e3, 2), "value": round(d_["tbs"], 4),
                                   "unit": "TB/s", "roofline_frac_hbm": round(d_["tbs"] * 1e3 / HBM_PEAK_GBS, 4),
                                   "algorithmic_bytes": d_["bytes"], "library_calls": d_["calls"],
                                   "weight_copies": d_["copies"],
-                                  "us_per_layer_qkv_separate": round(sep["ms"] * 1e3, 2)}
+                                  "us_per_layer_qkv_separate": round(sep["ms"] * 1e3, 2),
+                                  "us_per_layer_graph": round(gr["ms"] * 1e3, 2),
+                                  "value_graph": round(gr["tbs"], 4)}
             else:
                 lay["M%d" % M] = {"us_per_layer": round(d_["ms"] * 1e3, 2), "value": round(d_["tflops"], 2),
                                   "unit": "TFLOP/s", "roofline_frac_mfma": round(d_["tflops"] / BF16_PEAK_TFLOPS, 4),
                                   "algorithmic_flops": d_["flops"], "library_calls": d_["calls"],
-                                  "us_per_layer_qkv_separate": round(sep["ms"] * 1e3, 2)}
+                                  "us_per_layer_qkv_separate": round(sep["ms"] * 1e3, 2),
+                                  "us_per_layer_graph": round(gr["ms"] * 1e3, 2),
+                                  "value_graph": round(gr["tflops"], 2)}
+        lay["dense_fallback"] = d_["dense"]
         result["layer"] = {"workload": "Llama-3-8B-shaped decoder layer: q,o 4096->4096 r1637; k,v 4096->1024 "
                                        "r817 (q, k, v grouped on a shared X); gate,up 4096->14336 r2867 (packed); "
                                        "down 14336->4096 r2867", **lay}

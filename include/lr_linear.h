@@ -121,6 +121,14 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N,
  * M <= 16: one fused launch (split-K GEMM1, on-chip T hand-off, GEMM2,
  * deterministic reduction; T never round-trips through HBM).
  * M > 16: MFMA GEMM1 into a bf16 T workspace, then MFMA GEMM2.
+ * Graph capture: a run only enqueues kernels, and its launch arguments do
+ * not change from call to call (the decode kernels stamp their exchanges
+ * with a generation word kept in the workspace), so runs, group runs and
+ * packed runs may be captured into a HIP graph on `stream` and replayed
+ * ("FlashSVD v1.5: Making Low-Rank Transformers Inference Actually Fast",
+ * abstract: per-layer graph replay).  Make one call per handle before
+ * capturing (the first call sets kernel attributes), and do not replay a
+ * graph while another call on the same handle is in flight.
  * Errors: INVALID_ARG (null handle/pointers, M out of range, misaligned
  * base, Y overlapping X/A/B), HIP (launch failure).
  */

@@ -29,8 +29,14 @@
 //          epoch flags; member js of n-slice s sums its 1/Jw share of the
 //          n-slice over the Jw partials in order and writes bf16 Y.
 // No atomics and no floating-point reordering: results are bitwise
-// reproducible.  The epoch comes from the host (one per call of a handle),
-// so no counter is reset between calls.
+// reproducible.  The epoch of a launch is the handle's generation word
+// (ctrl[0]) plus one, read by every workgroup at entry; workgroup 0 stores
+// it back at its end.  Workgroup 0 finishes only after the Y flags of all
+// rank slices of its n-slice, each of which followed the T flags of every
+// K slice of that rank slice, so by then every workgroup of the launch has
+// read the word.  No counter is reset between calls and no argument
+// changes from one launch to the next, so a captured graph can replay the
+// launch.
 //
 // The misalignment of the rows (ld mod 8) selects one of eight compile-time
 // shift patterns for a whole GEMM loop (one uniform switch per phase); the
@@ -252,7 +258,8 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   const int JS = P.js_w;
   const int ntps = P.ntps;
   const int CB = kResNT / 8 * ntps + 1;  // chunks per B row run
-  const uint32_t epoch = P.epoch;
+  // the generation word is requested here and first used after A has landed
+  const uint32_t gen_v = ld_agent_u32(P.ctrl);
 
   const rsrc_t rA = make_rsrc(P.A, (int64_t)K * r * 2);
   const rsrc_t rB = make_rsrc(P.B, (int64_t)r * N * 2);
@@ -304,6 +311,8 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   }
   wait_vmem_all();
   barrier_lds();  // X and A are in LDS
+  const uint32_t gen = __builtin_amdgcn_readfirstlane(gen_v);
+  const uint32_t epoch = gen + 1u == 0u ? 1u : gen + 1u;  // 0 is the value of a fresh flag
   RES_TRACE(1);
   ResCtx ctx;
   ctx.sA = sA;
@@ -530,6 +539,7 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
     }
   }
   RES_TRACE(8);
+  if (local == 0 && tid == 0) st_agent_u32(P.ctrl, epoch);  // the next launch's generation
   RES_TRACE_FLUSH();
 }
 

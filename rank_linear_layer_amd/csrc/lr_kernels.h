@@ -28,14 +28,13 @@ struct DecProj {
   const uint16_t* B;
   uint16_t* Y;
   const void* ws;
-  uint32_t* ctrl;   // [0] generation, [1] finished n-slices, [2] spin-timeout flag
+  uint32_t* ctrl;   // [0] generation (launch stamp - 1), [1] finished n-slices, [2] spin-timeout flag
   uint32_t* tcnt;   // [Jw] arrivals of T partials (self-resetting)
   uint32_t* tflag;  // epoch stamps: [Jw] published T slices (streaming), [Jw*S] partials (resident)
   uint32_t* ycnt;   // [S] arrivals of Y partials (self-resetting)
   int64_t ws_bytes;
   uint32_t off_tpart, off_tfin, off_ypart;
   uint32_t off_tflag, off_yflag;  // resident kernel: [Jw*S] flag words each
-  uint32_t epoch;                  // resident kernel: stamp of this call (host counter, never 0)
   int r, N, Jw, S, ktps, ntps, wg_begin;
   int js_w;       // rank columns per slice
   int xcd_local;  // resident kernel: rank-slice groups share an XCD (verified map)

@@ -61,7 +61,6 @@ struct lr_linear {
   uint32_t* ycnt;
   uint32_t off_tpart, off_tfin, off_ypart, off_tflag, off_yflag;
   bool xcd_local;
-  mutable std::atomic<uint32_t> epoch;  // stamp of the last call (resident decode kernel)
   // prefill workspace: T [max_M x r_pad] bf16, and fp32 k-split partials
   bool has_prefill;
   uint16_t* Tbuf;
@@ -101,9 +100,6 @@ lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
   p.off_ypart = h->off_ypart;
   p.off_tflag = h->off_tflag;
   p.off_yflag = h->off_yflag;
-  uint32_t ep = h->epoch.fetch_add(1u) + 1u;
-  if (ep == 0u) ep = h->epoch.fetch_add(1u) + 1u;  // 0 is the value of a fresh flag
-  p.epoch = ep;
   p.js_w = h->dp.js_w;
   // the XCD-local exchange needs workgroup (local id) on XCD local % 8
   p.xcd_local = (h->xcd_local && wg_begin % 8 == 0) ? 1 : 0;
@@ -464,7 +460,6 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
   lr_linear* h = new (std::nothrow) lr_linear;
   if (!h) return fail(LR_ERR_OUT_OF_MEMORY, "host allocation failed");
   memset((void*)h, 0, sizeof *h);
-  h->epoch.store(0u);
   for (auto& ph : h->last_plan)
     for (auto& v : ph) v.store(-1);
   h->K = K;

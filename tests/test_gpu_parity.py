@@ -532,3 +532,67 @@ def test_error_paths_on_device(gpu):
     other = lrl.LowRankLinear(to_dev(A2), to_dev(B2), max_M=4)
     with pytest.raises(lrl.LRError):
         lrl.mlp_packed(lin, other, X[:2])
+
+
+# ------------------------------------------------------------- graph replay ---
+# A whole layer (q, k, v grouped; o; gate/up packed; down) captured once in a
+# HIP graph and replayed: no launch argument changes between replays (the
+# decode kernels stamp their exchanges with a device-side generation).  Each
+# replay follows eager work on the same handles and new contents of the
+# captured input, and must equal the eager result for those contents.
+
+@pytest.mark.parametrize("M,flags", [(1, 0), (5, lrl.LR_FLAG_DECODE_STREAMING), (64, 0)])
+def test_layer_graph_replay(gpu, M, flags):
+    torch = gpu
+    banner("graph replay M=%d flags=%d" % (M, flags))
+    scale = 4  # a quarter-width layer keeps the test short
+    projs = [(p.name, p.K // scale, p.r // scale, p.N // scale) for p in configs.LAYER_PROJS]
+    lins, fac = {}, {}
+    for i, (nm, K, r, N) in enumerate(projs):
+        _, A, B = datagen.factorized_inputs(1, K, r, N, 7000 + 10 * i)
+        fac[nm] = (A, B)
+        lins[nm] = lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M, flags=flags)
+    K0, H = projs[0][1], projs[-1][1]
+    X = torch.empty((M, K0), dtype=torch.bfloat16, device="cuda")
+    Hin = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    outs = {nm: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for nm, _, _, N in projs}
+
+    def step():
+        lrl.group_run([lins["q"], lins["k"], lins["v"]], X, outs=[outs["q"], outs["k"], outs["v"]])
+        lins["o"](X, out=outs["o"])
+        lrl.mlp_packed(lins["gate"], lins["up"], X, out_gate=outs["gate"], out_up=outs["up"])
+        lins["down"](Hin, out=outs["down"])
+
+    def load_inputs(seed):
+        X.copy_(torch.from_numpy(datagen.normal_bf16((M, K0), 1.0, seed).view(np.int16)).view(torch.bfloat16))
+        Hin.copy_(torch.from_numpy(datagen.normal_bf16((M, H), 1.0, seed + 1).view(np.int16)).view(torch.bfloat16))
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return {nm: to_bits(t).copy() for nm, t in outs.items()}
+
+    load_inputs(11)
+    step()
+    step()  # warm: kernel attributes set outside capture
+    eager11 = snapshot()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep, seed in enumerate([11, 23, 11, 37]):
+        load_inputs(seed)
+        step()  # eager work on the same handles between replays
+        ref = snapshot()
+        if seed == 11:
+            assert all(np.array_equal(ref[nm], eager11[nm]) for nm in outs)
+        g.replay()
+        got = snapshot()
+        for nm in outs:
+            assert np.array_equal(got[nm], ref[nm]), "replay %d (%s) differs from eager" % (rep, nm)
+    # the last replay against the oracle
+    Xb = datagen.normal_bf16((M, K0), 1.0, 37)
+    Hb = datagen.normal_bf16((M, H), 1.0, 38)
+    for nm, K, r, N in projs:
+        A, B = fac[nm]
+        src = Hb if nm == "down" else Xb
+        assert_parity(got[nm], oracle.lowrank_bf16(src, A, B), "graph %s M=%d" % (nm, M))
+    del g
