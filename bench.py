@@ -282,7 +282,49 @@ def run_sweep(torch, lrl, configs, metrics, steps, stride=1):
             summary["N%d_M%d" % (N, M)] = {"unit": "TB/s" if M <= 16 else "TFLOP/s", "points": len(ser),
                                            "min": float(v.min()), "median": float(np.median(v)),
                                            "max": float(v.max()), "cliff_ranks": cliffs}
-    return summary
+    return summary, rows
+
+
+def gac_from_sweep(rows, configs):
+    """GAC's rank re-selection ("Why Smaller Is Slower?", section 4) driven
+    by the measured sweep: a synthetic compressed model of 16 weights of the
+    sweep shape (K = 4096, N = 4096 / 3999 alternating) with continuous ranks
+    d* in (1030, 1070) and random importance scores; candidates are the
+    multiples of 8 within 4% below / 6% above d* that the measured latency
+    table does not mark as a cliff; the budget is the misaligned model's
+    parameter count.  Reports, per M, how many aligned candidates the table
+    rejected and the summed latency of the misaligned ranks against the
+    selected aligned ones."""
+    from rank_linear_layer_amd import gac
+    rng = np.random.default_rng(2026)
+    K = configs.SWEEP_K
+    n = 16
+    Ns = [configs.SWEEP_N[i % len(configs.SWEEP_N)] for i in range(n)]
+    dstar = rng.uniform(1030, 1070, n)
+    scores = rng.uniform(0.5, 2.0, n)
+    costs = [K + N for N in Ns]
+    budget = int(sum(c * d for c, d in zip(costs, dstar)))
+    out = {"weights": n, "d_star_range": [1030, 1070], "budget_params": budget}
+    for M in configs.SWEEP_M:
+        lat = {(x["N"], x["r"]): x["us"] for x in rows if x["M"] == M}
+        cands, rejected, total = [], 0, 0
+        for d, N in zip(dstar, Ns):
+            table = {r: lat.get((N, r)) for r in range(900, 1200)}
+            c_all = gac.candidates(d, table, window=(0.96, 1.06))
+            c_aligned = [r for r in range(8 * int(np.ceil(0.96 * d / 8)), int(1.06 * d) + 1, 8) if table.get(r)]
+            rejected += len(c_aligned) - len(c_all)
+            total += len(c_aligned)
+            cands.append(c_all)
+        dims, obj = gac.select(list(scores), costs, list(dstar), cands, budget)
+        def nearest(N, d):
+            return lat[min((k for k in lat if k[0] == N), key=lambda k: abs(k[1] - d))]
+        t_mis = sum(nearest(N, d) for d, N in zip(dstar, Ns))
+        t_gac = sum(lat[(N, d)] for d, N in zip(dims, Ns))
+        out["M%d" % M] = {"aligned_candidates": total, "rejected_as_cliffs": rejected,
+                          "us_misaligned_ranks": round(t_mis, 2), "us_gac_ranks": round(t_gac, 2),
+                          "gac_speedup": round(t_mis / t_gac, 4),
+                          "params_misaligned": budget, "params_gac": int(sum(c * d for c, d in zip(costs, dims)))}
+    return out
 
 
 def main():
@@ -297,6 +339,7 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--sweep-stride", type=int, default=1)
+    ap.add_argument("--gac", action="store_true", help="with --sweep: GAC rank re-selection on the measured table")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -393,7 +436,10 @@ def main():
                                        "r817 (q, k, v grouped on a shared X); gate,up 4096->14336 r2867 (packed); "
                                        "down 14336->4096 r2867", **lay}
     if args.sweep:
-        result["sweep"] = run_sweep(torch, lrl, configs, metrics, args.sweep_steps, args.sweep_stride)
+        result["sweep"], sweep_rows = run_sweep(torch, lrl, configs, metrics, args.sweep_steps, args.sweep_stride)
+        if args.gac:
+            result["gac"] = gac_from_sweep(sweep_rows, configs)
+            log("gac: %s" % json.dumps(result["gac"]))
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(configs, datagen, metrics)
     else:

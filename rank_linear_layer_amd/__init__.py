@@ -47,6 +47,7 @@ EXPORTED_SYMBOLS = (
     "lr_last_error",
     "lr_linear_describe",
     "lr_linear_workspace_bytes",
+    "lr_gac_select",
 )
 
 
@@ -93,6 +94,10 @@ def load_library(path: str | None = None):
         lib.lr_linear_describe.restype = ctypes.c_int
         lib.lr_linear_workspace_bytes.argtypes = [vp]
         lib.lr_linear_workspace_bytes.restype = i64
+        P = ctypes.POINTER
+        lib.lr_gac_select.argtypes = [ctypes.c_int, P(ctypes.c_double), P(i64), P(ctypes.c_double),
+                                      P(ctypes.c_int), P(i64), i64, i64, P(i64), P(ctypes.c_double)]
+        lib.lr_gac_select.restype = ctypes.c_int
         _lib = lib
         return lib
 

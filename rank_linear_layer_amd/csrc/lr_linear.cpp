@@ -35,6 +35,16 @@ lr_status hip_fail(hipError_t e, const char* what) {
   return fail(LR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+// The library's other translation units report through the same
+// thread-local detail string (not exported).
+__attribute__((visibility("hidden"))) lr_status lr_internal_fail(lr_status st, const char* msg) {
+  return fail(st, "%s", msg);
+}
+
+namespace {
+
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 

@@ -1,6 +1,6 @@
 """CPU tests of the C-ABI library: it loads, exports every symbol that
-include/lr_linear.h declares, and rejects bad arguments before touching the
-GPU (validation runs first; no compute call is made here)."""
+include/*.h declares, and rejects bad arguments before touching the GPU
+(validation runs first; no GPU compute call is made here)."""
 import ctypes
 import os
 import re
@@ -10,13 +10,16 @@ import pytest
 import rank_linear_layer_amd as lrl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "lr_linear.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lr_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(lr_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
