@@ -19,6 +19,7 @@ from . import _check, load_library
 
 ALIGN = 8                # the heuristic filter: d mod 8 == 0 (the pages' minimum requirement)
 WINDOW = (0.85, 1.20)    # candidates between 0.85 d* and 1.2 d*
+TOL = 0.05               # a larger dimension must be over 5% faster to mark d as a cliff (timing noise)
 
 
 def quantization_unit(unit_costs, align: int = ALIGN) -> int:
@@ -26,7 +27,7 @@ def quantization_unit(unit_costs, align: int = ALIGN) -> int:
     return align * min(int(c) for c in unit_costs)
 
 
-def candidates(d_star: float, latency, align: int = ALIGN, window=WINDOW, tol: float = 0.0):
+def candidates(d_star: float, latency, align: int = ALIGN, window=WINDOW, tol: float = TOL):
     """Candidate dimensions for a continuous allocation d_star.
 
     Multiples of `align` in [window[0] d*, window[1] d*] (at least one
