@@ -71,6 +71,10 @@ __global__ __launch_bounds__(256) void lr_dense_swizzle_kernel(const uint16_t* W
   *reinterpret_cast<u32x4_t*>(Wsw + t * 8) = v;
 }
 
+// XAL: K is a multiple of 8 (X rows are 16-byte aligned).  A compile-time
+// choice: a branch around the loads would make the compiler wait for every
+// load in flight where the branches join.
+template <bool XAL>
 __global__ __launch_bounds__(kDnThreads) void lr_dense_decode_kernel(const DenseArgs a) {
   __shared__ float red[kDnWaves][256];
   const int tid = threadIdx.x;
@@ -89,7 +93,6 @@ __global__ __launch_bounds__(kDnThreads) void lr_dense_decode_kernel(const Dense
   // aligned 16-byte load; otherwise the two aligned chunks around it are
   // loaded and the lane realigns them by its row's offset.
   const int m = l & 15;
-  const bool xal = (a.K & 7) == 0;
   const int64_t xrow = (int64_t)m * a.K;
   const int d = (int)(xrow & 7);
 
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(kDnThreads) void lr_dense_decode_kernel(const Dense
       const int64_t s = c0 + i;
       wv[i] = buf_load16(rW, (uint32_t)(s < s1 ? (s * 1024 + l * 16) : nk * 1024));
       const int64_t e = xrow + 32 * s + 8 * (l >> 4);
-      if (xal) {
+      if (XAL) {
         xl[i] = buf_load16(rX, (uint32_t)(e * 2));
       } else {
         xl[i] = buf_load16(rX, (uint32_t)((e >> 3) * 16));
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kDnThreads) void lr_dense_decode_kernel(const Dense
     for (int i = 0; i < kDnChunk; ++i) {
       // columns >= K (the next row's elements, or bytes past X) and rows
       // >= M are cleared: rows of W past K are zero, but 0 * NaN is not
-      const u32x4_t x = mask_cols(xal ? xl[i] : realign_lane(xl[i], xh[i], d), 32 * (c0 + i) + 8 * (l >> 4), a.K);
+      const u32x4_t x = mask_cols(XAL ? xl[i] : realign_lane(xl[i], xh[i], d), 32 * (c0 + i) + 8 * (l >> 4), a.K);
       acc = mfma_16x16x32(m < a.M ? x : zerou4(), wv[i], acc);
     }
   }
@@ -146,7 +149,10 @@ hipError_t launch_dense_decode(const DenseArgs& args, hipStream_t stream) {
   const int64_t ng = (args.N + 15) / 16;
   if (ng <= 0 || args.M <= 0) return hipSuccess;
   if (args.M > 16 || args.nk != (args.K + 31) / 32 || ng > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lr_dense_decode_kernel, dim3((unsigned)ng), dim3(kDnThreads), 0, stream, args);
+  if ((args.K & 7) == 0)
+    hipLaunchKernelGGL(lr_dense_decode_kernel<true>, dim3((unsigned)ng), dim3(kDnThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL(lr_dense_decode_kernel<false>, dim3((unsigned)ng), dim3(kDnThreads), 0, stream, args);
   return hipGetLastError();
 }
 
