@@ -33,13 +33,24 @@ namespace lrk {
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 // Optional phase timestamps (constant-rate device clock), compiled in only
-// with -DLR_DECODE_TRACE; used to see where a launch spends its time.
+// with -DLR_DECODE_TRACE; used to see where a launch spends its time.  They
+// are held in scalar registers and stored when the kernel ends, so that no
+// trace store sits in the vector-memory counter that the phases wait on.
 #ifdef LR_DECODE_TRACE
-#define DEC_TRACE_ENTRY() const uint64_t trace_entry_ = __builtin_amdgcn_s_memrealtime()
-#define DEC_TRACE_ENTRY_STORE() do { if (a.trace && tid == 0) a.trace[blockIdx.x * kDecTracePoints + 15] = trace_entry_; } while (0)
-#define DEC_TRACE(i)                                                                              \
-  do {                                                                                            \
-    if (a.trace && tid == 0) a.trace[blockIdx.x * kDecTracePoints + (i)] = __builtin_amdgcn_s_memrealtime(); \
+__device__ __forceinline__ uint64_t dec_trace_now() {
+  uint64_t t;
+  asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t) : : "memory");
+  return t;
+}
+#define DEC_TRACE_ENTRY()     \
+  uint64_t trace_t_[16] = {}; \
+  trace_t_[15] = dec_trace_now()
+#define DEC_TRACE_ENTRY_STORE() do { } while (0)
+#define DEC_TRACE(i) trace_t_[i] = dec_trace_now()
+#define DEC_TRACE_FLUSH()                                                                        \
+  do {                                                                                           \
+    if (a.trace && tid == 0)                                                                     \
+      for (int i_ = 0; i_ < 16; ++i_) a.trace[blockIdx.x * kDecTracePoints + i_] = trace_t_[i_]; \
   } while (0)
 #else
 #define DEC_TRACE_ENTRY() do { } while (0)
@@ -47,11 +58,29 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 #define DEC_TRACE(i) \
   do {               \
   } while (0)
+#define DEC_TRACE_FLUSH() do { } while (0)
 #endif
 
 struct RawTile {
   u32x4_t c[8];
 };
+
+// Offsets with bit 31 set lie past the end of every buffer range (matrices
+// and the workspace are below 2 GiB): such a load returns zeros and such a
+// store is dropped, without touching memory.  Loads and stores that depend
+// on a condition use this instead of a branch: at the join of a branch
+// around memory instructions the compiler must assume the shorter queue and
+// waits for every request in flight, which collapses double buffering.
+__device__ __forceinline__ uint32_t off_if(uint32_t off, bool ok) { return off | ((uint32_t)!ok << 31); }
+
+__device__ __forceinline__ void load_tile_raw_if(RawTile& t, rsrc_t r, int64_t rbase, int64_t ld, int64_t colbase,
+                                                 int lane16, int g, bool ok) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t c0 = ((rbase + 8 * g + q) * ld + colbase) >> 3;
+    t.c[q] = buf_load16(r, off_if((uint32_t)((c0 + lane16) * 16), ok));
+  }
+}
 
 // Raw chunk loads of one 32-row x 120-column tile (rows rbase + 8g + q).
 __device__ __forceinline__ void load_tile_raw(RawTile& t, rsrc_t r, int64_t rbase, int64_t ld, int64_t colbase,
@@ -117,7 +146,22 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
     if (i < a.nproj && (int)blockIdx.x >= a.p[i].wg_begin) pi = i;
   const DecProj P = a.p[pi];
   const int local = (int)blockIdx.x - P.wg_begin;
-  const int js = local / P.S, s = local % P.S;
+  // Workgroup -> (rank slice, K/N slice).  With a verified round-robin XCD
+  // dispatch, each XCD takes a contiguous run of the rank-slice-major order,
+  // so adjacent rank slices (which share the 128-byte lines around their
+  // boundaries in A) are fetched into the same L2.  Any bijection is
+  // correct; this one only saves HBM traffic.
+  int js, s;
+  if (P.xcd_local) {
+    const int G = P.Jw * P.S;
+    const int x = local & 7, slot = local >> 3;
+    const int p = x * (G >> 3) + min(x, G & 7) + slot;
+    js = p / P.S;
+    s = p - js * P.S;
+  } else {
+    js = local / P.S;
+    s = local - js * P.S;
+  }
   const int M = a.M, K = a.K, r = P.r, N = P.N;
 
   const rsrc_t rA = make_rsrc(P.A, (int64_t)K * r * 2);
@@ -276,7 +320,9 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
 
   // ---------------------------------------------------------- GEMM2 ------
   const uint32_t ypart_wg = P.off_ypart + (uint32_t)((s * P.Jw + js) * P.ntps) * (uint32_t)(M * kDecNT * 4);
-  auto gemm2_tile = [&](const RawTile& bt, int nt) {
+  // One n-tile: its partial is stored only when `ok` (a tile past the end of
+  // the slice is computed on zeros and its stores are dropped).
+  auto gemm2_tile = [&](const RawTile& bt, int nt, bool ok) {
     const int64_t nb = (int64_t)nt * kDecNT;
     f32x4_t y[8];
 #pragma unroll
@@ -301,17 +347,17 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
       f32x4_t v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = ((red[0][m][c + i] + red[1][m][c + i]) + red[2][m][c + i]) + red[3][m][c + i];
-      buf_store16_coherent(rW, yp + (uint32_t)vi * 16u, v);
+      buf_store16_coherent(rW, off_if(yp + (uint32_t)vi * 16u, ok), v);
     }
     barrier_lds();
   };
+  // Tiles in pairs with no branch around a load or store: the next tile of
+  // each buffer is requested (or replaced by zeros) right after its use.
   for (int nt = nt_beg; nt < nt_end; nt += 2) {
-    gemm2_tile(b0, nt);
-    if (nt + 2 < nt_end) load_tile_raw(b0, rB, jrow0, N, (int64_t)(nt + 2) * kDecNT, np, g);
-    if (nt + 1 < nt_end) {
-      gemm2_tile(b1, nt + 1);
-      if (nt + 3 < nt_end) load_tile_raw(b1, rB, jrow0, N, (int64_t)(nt + 3) * kDecNT, np, g);
-    }
+    gemm2_tile(b0, nt, true);
+    load_tile_raw_if(b0, rB, jrow0, N, (int64_t)(nt + 2) * kDecNT, np, g, nt + 2 < nt_end);
+    gemm2_tile(b1, nt + 1, nt + 1 < nt_end);
+    load_tile_raw_if(b1, rB, jrow0, N, (int64_t)(nt + 3) * kDecNT, np, g, nt + 3 < nt_end);
   }
 
   // ------------------------------------------- final deterministic sum ---
@@ -353,6 +399,7 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
     }
   }
   DEC_TRACE(7);
+  DEC_TRACE_FLUSH();
 }
 
 hipError_t launch_decode(const DecArgs& args, int grid, hipStream_t stream) {

@@ -37,7 +37,8 @@ struct DecProj {
   uint32_t off_tflag, off_yflag;  // resident kernel: [Jw*S] flag words each
   int r, N, Jw, S, ktps, ntps, wg_begin;
   int js_w;       // rank columns per slice
-  int xcd_local;  // resident kernel: rank-slice groups share an XCD (verified map)
+  int xcd_local;  // workgroups are dealt to XCDs round-robin (verified) and wg_begin % 8 == 0:
+                  // resident kernel: rank-slice groups share an XCD; streaming: adjacent slices do
 };
 
 struct DecArgs {

@@ -514,7 +514,10 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     off = align_up(off + (size_t)h->dp.Jw * h->dec_max_M * h->dp.js_w * 4);
     o_ypart = off;
     off = align_up(off + (size_t)G * h->dp.ntps * h->dec_max_M * h->dp.nt_w * 4);
-    h->xcd_local = h->dp.kind == 1 && (h->dp.Jw % 8 == 0) && xcd_map_ok(dev);
+    // resident kernel: its T exchange runs through one XCD's L2, so every
+    // rank-slice group must sit on one XCD (Jw a multiple of 8); streaming
+    // kernel: only a traffic-saving placement of adjacent rank slices
+    h->xcd_local = (h->dp.kind == 1 ? h->dp.Jw % 8 == 0 : true) && xcd_map_ok(dev);
     if (off >= ((size_t)1 << 31)) {
       delete h;
       return fail(LR_ERR_UNSUPPORTED, "decode workspace of %zu bytes exceeds 2 GiB", off);
@@ -647,7 +650,17 @@ lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const vo
 
 void lr_linear_destroy(lr_linear* h) {
   if (!h) return;
-  if (h->ws) (void)hipFree(h->ws);
+  if (h->ws) {
+    // A handle may be released (e.g. by a garbage collector) while another
+    // stream captures a graph.  hipFree is not allowed under a global-mode
+    // capture and would invalidate it; in relaxed mode this thread's free
+    // leaves other captures alone.  (The caller must not free a handle that
+    // a graph being captured or replayed still uses.)
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    const bool swapped = hipThreadExchangeStreamCaptureMode(&mode) == hipSuccess;
+    (void)hipFree(h->ws);
+    if (swapped) (void)hipThreadExchangeStreamCaptureMode(&mode);
+  }
   delete h;
 }
 

@@ -596,3 +596,26 @@ def test_layer_graph_replay(gpu, M, flags):
         src = Hb if nm == "down" else Xb
         assert_parity(got[nm], oracle.lowrank_bf16(src, A, B), "graph %s M=%d" % (nm, M))
     del g
+
+
+def test_handle_released_during_capture(gpu):
+    # a handle freed while a graph is being captured (a garbage-collected
+    # handle of earlier work) must not invalidate that capture
+    torch = gpu
+    K, r, N, M = 256, 40, 128, 2
+    _, A, B = datagen.factorized_inputs(1, K, r, N, 21)
+    keep = lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M)
+    spare = lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M)
+    Xb = datagen.normal_bf16((M, K), 1.0, 22)
+    X = to_dev(Xb)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    keep(X, out=Y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        spare.close()
+        keep(X, out=Y)
+    Y.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, A, B), "after a release during capture")
