@@ -86,6 +86,8 @@ def time_steps(torch, fn, steps, warmup, stream):
 
 
 def decode_kernel_name(plan):
+    if "kind=split" in plan:
+        return "lr_decode_split_kernel"
     return "lr_decode_res_kernel" if "kind=resident" in plan else "lr_decode_fused_kernel"
 
 
@@ -129,6 +131,36 @@ def bench_decode(torch, lrl, configs, datagen, metrics, steps, warmup):
     ms_warm = time_steps(torch, lambda i: lins[0](X, out=Y), max(50, steps // 4), 10, stream)
     return dict(M=M, K=K, r=r, N=N, ms=ms, tbs=tbs, bytes=per, ncopies=ncopies,
                 warm_tbs=per / (ms_warm * 1e-3) / 1e12, plan=lins[0].describe())
+
+
+def bench_dense_decode(torch, lrl, configs, steps, warmup):
+    """Dense fallback decode (W = A.B formed at create): the k/v layer shape,
+    where the library takes it by itself, and the q_proj shape with
+    LR_FLAG_DENSE.  Bytes per launch are what the kernel reads and writes,
+    2 (MK + KN + MN); W copies rotate over >= 1 GiB."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(configs.seed_base(configs.LAYER_INDEX, 1))
+    out = {}
+    for name, (M, K, r, N, flags) in (("kv_auto", (8, 4096, 817, 1024, 0)),
+                                      ("qproj_forced", (8, 4096, 1637, 4096, lrl.LR_FLAG_DENSE))):
+        A = (torch.randn((K, r), generator=g, device="cuda") / np.sqrt(K)).to(torch.bfloat16)
+        B = (torch.randn((r, N), generator=g, device="cuda") / np.sqrt(r)).to(torch.bfloat16)
+        X = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ncop = max(2, int(np.ceil((1 << 30) / (2 * K * N))))
+        lins = [lrl.LowRankLinear(A, B, max_M=M, flags=flags) for _ in range(ncop)]
+        assert "dense=1" in lins[0].describe()
+        ms = time_steps(torch, lambda i: lins[i % ncop](X, out=Y), steps, warmup, torch.cuda.current_stream())
+        byts = 2 * (M * K + K * N + M * N)
+        out[name] = {"M": M, "K": K, "r": r, "N": N, "us_per_launch": round(ms * 1e3, 3),
+                     "hbm_bytes_per_launch": byts, "tbs": round(byts / (ms * 1e-3) / 1e12, 4),
+                     "roofline_frac_hbm": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "kernel": "lr_dense_decode_kernel", "w_copies": ncop}
+        log("dense decode %s: %.2f us/launch, %.3f TB/s of W bytes (%d copies)" % (name, ms * 1e3,
+                                                                                  out[name]["tbs"], ncop))
+        del lins
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_prefill(torch, lrl, configs, metrics, steps, warmup):
@@ -406,6 +438,7 @@ def main():
                          "algorithmic_flops_per_step": p["flops"]},
         }
     if not args.no_layer:
+        result["dense_decode"] = bench_dense_decode(torch, lrl, configs, min(args.steps, 400), 20)
         lay = {}
         for M in configs.LAYER_M:
             steps_, warm_ = (200, 20) if M <= 16 else (10, 2)

@@ -76,7 +76,8 @@ typedef struct lr_linear lr_linear;
 #define LR_FLAG_FORCE_DECODE  1u  /* use the fused decode kernel for every M (requires max_M <= 16) */
 #define LR_FLAG_FORCE_PREFILL 2u  /* use the MFMA prefill kernels for every M */
 #define LR_FLAG_DECODE_STREAMING 4u  /* decode with the register-streaming kernel even where the
-                                        LDS-resident one applies (both compute the same result) */
+                                        role-split or LDS-resident one applies (all compute the
+                                        same result) */
 #define LR_FLAG_PREFILL_TWO_WAVE 8u  /* prefill only with the two-waves-per-SIMD kernel (tiles of
                                         256 x 192 or 224) instead of the cost model's choice */
 #define LR_FLAG_PREFILL_ONE_WAVE 16u /* prefill with the one-wave-per-SIMD kernel (256 x 256 tiles)
@@ -84,6 +85,10 @@ typedef struct lr_linear lr_linear;
                                         same leading dimension mod 8 for both factors of a pair */
 #define LR_FLAG_DENSE    32u  /* dense fallback: form W = A.B (bf16) at create and run Y = X.W */
 #define LR_FLAG_FACTORED 64u  /* never take the dense fallback */
+#define LR_FLAG_DECODE_SPLIT 128u  /* decode with the role-split kernel where its plan fits (the
+                                      default already; kept for callers that name it) */
+#define LR_FLAG_DECODE_RESIDENT 256u  /* never the role-split kernel: the LDS-resident kernel where
+                                         it applies, else the register-streaming one */
 
 /* Largest M that the fused decode kernel takes (more rows use prefill). */
 #define LR_DECODE_MAX_M 16

@@ -34,6 +34,8 @@ LR_FLAG_PREFILL_TWO_WAVE = 8
 LR_FLAG_PREFILL_ONE_WAVE = 16
 LR_FLAG_DENSE = 32
 LR_FLAG_FACTORED = 64
+LR_FLAG_DECODE_SPLIT = 128
+LR_FLAG_DECODE_RESIDENT = 256
 LR_DECODE_MAX_M = 16
 LR_GROUP_MAX = 4
 

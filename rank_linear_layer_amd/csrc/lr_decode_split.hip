@@ -1,0 +1,361 @@
+// Role-split fused decode kernel (M <= 16): Y = (X . A) . B in one launch,
+// with the compute units divided between the two products instead of every
+// workgroup taking a share of both.
+//
+// Decode reads each weight byte once and is bound by HBM ("LowRankArena
+// ...", "Why theoretical FLOPs saved does not equal faster inference").  A
+// single launch pays its start-up and its end once, but the second product
+// needs all of T = X . A: in the kernels that give every workgroup a rank
+// slice of both factors, the T hand-off sits between the A stream and the
+// B stream's use, and the partial Y sums of the rank slices need a second
+// hand-off.  Here:
+//
+//  * workgroups [0, GA) produce T: producer j owns rank columns
+//    [16 j, 16 j + 16) and computes T[:, those] = X . A[:, those] over all
+//    of K, so a T slice is final where it is computed.  It is published
+//    device-coherent (fp32) with an epoch flag;
+//  * workgroups [GA, GA + GB) produce Y: each owns gpw 16-column groups of N
+//    and computes Y[:, those] = T . B[:, those] over the whole rank, so no
+//    partial Y ever leaves a workgroup.  A Y producer requests its whole B
+//    slab into registers at entry, while the T producers stream A, so both
+//    factors are in flight from the start; it then waits for the GA flags,
+//    reads T and finishes with MFMAs on operands it already holds (T as
+//    bf16 hi + lo: two MFMAs per step, about fp32 accuracy).
+//
+// Both factors are kept in the MFMA operand block layout of the dense path
+// (copied at create): 16 columns x 32 rows per 1 KB block, lane l holding
+// rows 32 s + 8 (l / 16) .. + 7 of column l % 16, rows and columns past the
+// matrix zero.  Every weight load is one contiguous kilobyte per wave and
+// no row alignment reaches the kernel: a misaligned rank or width costs
+// only its zero padding.
+//
+// T producers have lower workgroup ids and never wait, so the launch
+// completes even when not every workgroup is resident at once.  The epoch
+// of a launch is the generation word ctrl[0] plus one, read by every
+// workgroup at entry.  Each Y producer counts itself in ctrl[1] once it has
+// read the generation; Y producer 0 waits for that count as well as for the
+// T flags (each stored after its producer read the generation), then
+// clears the count and stores the epoch as the next generation.  No
+// argument changes between launches and nothing is cleared from the host,
+// so a captured graph can replay it.
+#include "lr_device.h"
+#include "lr_kernels.h"
+
+namespace lrk {
+
+namespace {
+
+constexpr int kSpThreads = 512;  // 8 waves
+constexpr int kSpWaves = kSpThreads / 64;
+constexpr int kSpChunk = 16;     // A blocks in flight per wave at once
+constexpr uint32_t kSpSpinLimit = 1u << 22;
+constexpr uint32_t kSpOut = 0x7FFFFF00u;  // past every buffer range: loads read 0, stores are dropped
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void buf_store8_coherent(rsrc_t r, uint32_t byte_off, uint32_t v0, uint32_t v1) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = {v0, v1};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)byte_off, 0, kCoherent);
+}
+
+// Optional phase timestamps (constant-rate device clock), compiled in only
+// with -DLR_DECODE_TRACE: held in scalar registers, stored at the end.
+#ifdef LR_DECODE_TRACE
+#define SP_TRACE(i) tr[i] = sp_trace_now()
+__device__ __forceinline__ uint64_t sp_trace_now() {
+  uint64_t t;
+  asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t) : : "memory");
+  return t;
+}
+#else
+#define SP_TRACE(i) \
+  do {              \
+  } while (0)
+#endif
+
+// T producer: rank columns [16 j, 16 j + 16) over all of K, eight waves
+// splitting the k-steps, then the slice published and flagged.
+template <bool XAL>
+__device__ __forceinline__ void t_producer(const SplitArgs& a, int j, uint32_t epoch, float (*red)[256], uint64_t* tr) {
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int nk = a.nkA;
+  const int per = (nk + kSpWaves - 1) / kSpWaves;
+  const int s0 = min(nk, w * per), s1 = min(nk, s0 + per);
+  const rsrc_t rA = make_rsrc(a.Asw + (int64_t)j * nk * 512, (int64_t)nk * 1024);
+  const rsrc_t rX = make_rsrc(a.X, (int64_t)a.M * a.K * 2);
+  // MFMA A operand of lane l: X row m = l % 16 (rows >= M read as zero),
+  // columns 32 s + 8 (l / 16) .. + 7; unaligned rows are loaded as the two
+  // aligned chunks around them and shifted per lane
+  const int m = l & 15;
+  const int64_t xrow = (int64_t)m * a.K;
+  const int d = (int)(xrow & 7);
+  f32x4_t acc = zero4();
+  for (int c0 = s0; c0 < s1; c0 += kSpChunk) {
+    u32x4_t wv[kSpChunk], xl[kSpChunk], xh[kSpChunk];
+#pragma unroll
+    for (int i = 0; i < kSpChunk; ++i) {
+      const int s = c0 + i;
+      wv[i] = buf_load16(rA, s < s1 ? (uint32_t)(s * 1024 + l * 16) : kSpOut);
+      const int64_t e = xrow + 32 * s + 8 * (l >> 4);
+      if (XAL) {
+        xl[i] = buf_load16(rX, (uint32_t)(e * 2));
+      } else {
+        xl[i] = buf_load16(rX, (uint32_t)((e >> 3) * 16));
+        xh[i] = buf_load16(rX, (uint32_t)((e >> 3) * 16 + 16));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kSpChunk; ++i) {
+      // columns >= K are cleared (they hold the next row, and 0 * NaN is not 0)
+      const u32x4_t x = mask_cols(XAL ? xl[i] : realign_lane(xl[i], xh[i], d), 32 * (c0 + i) + 8 * (l >> 4), a.K);
+      acc = mfma_16x16x32(m < a.M ? x : zerou4(), wv[i], acc);
+    }
+  }
+  SP_TRACE(1);
+  // acc lane l, register t: row 4 (l / 16) + t, column l % 16
+#pragma unroll
+  for (int t = 0; t < 4; ++t) red[w][(4 * (l >> 4) + t) * 16 + (l & 15)] = acc[t];
+  barrier_lds();
+  SP_TRACE(2);
+  if (w == 0) {
+    // lane -> row l / 4, columns 4 (l % 4) .. + 3 of the slice; the waves'
+    // partials summed in wave order, then split into bf16 hi + lo and
+    // stored as GEMM2's MFMA operand rows (see P in SplitArgs): with
+    // M <= 8, rows 0-7 of plane 0 hold hi and rows 8-15 lo of T rows 0-7;
+    // otherwise plane 0 holds hi and plane 1 lo of T rows 0-15.  Rows of T
+    // >= M are exactly zero (so are their X rows), which clears whatever a
+    // call with a larger M left there.
+    const bool packed = a.M <= 8;
+    const int row = l >> 2, c = (l & 3) * 4;
+    const int trow = packed ? (row & 7) : row;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < kSpWaves; ++q) s += red[q][trow * 16 + c + i];
+      v[i] = s;
+    }
+    uint32_t hi[2], lo[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint32_t h0 = f32_to_bf16_rne(v[2 * p]), h1 = f32_to_bf16_rne(v[2 * p + 1]);
+      hi[p] = h0 | (h1 << 16);
+      lo[p] = pack_bf16x2(v[2 * p] - __uint_as_float(h0 << 16), v[2 * p + 1] - __uint_as_float(h1 << 16));
+    }
+    const bool take_lo = packed && row >= 8;
+    const int planes = packed ? 1 : 2;
+    const int64_t plane = (int64_t)16 * a.ldp;       // bf16 per plane
+    const int64_t rep = plane * planes;              // bf16 per replica
+    const rsrc_t rP = make_rsrc(a.P, rep * a.nrep * 2);
+    const uint32_t off = (uint32_t)((row * a.ldp + 16 * j + c) * 2);
+    for (int q = 0; q < a.nrep; ++q) {
+      const uint32_t qo = off + (uint32_t)(q * rep * 2);
+      buf_store8_coherent(rP, qo, take_lo ? lo[0] : hi[0], take_lo ? lo[1] : hi[1]);
+      if (!packed) buf_store8_coherent(rP, qo + (uint32_t)(plane * 2), lo[0], lo[1]);
+    }
+    wait_vmem_all();  // the slice is visible before its flags
+    if (l < a.nrep)
+      buf_store_u32_coherent(make_rsrc(a.flags, (int64_t)a.nrep * a.ldf * 4), (uint32_t)(l * a.ldf + j) * 4u, epoch);
+  }
+  SP_TRACE(3);
+}
+
+// Wave 0 spins until the 32-bit words [first, first + count) of `r` all
+// equal `want` (and, when `count_too`, ctrl[1] equals GB), with
+// device-coherent loads.  Gives up after kSpSpinLimit rounds and raises the
+// timeout flag.
+__device__ __forceinline__ void spin_until(const SplitArgs& a, rsrc_t r, int first, int count, uint32_t want,
+                                           bool count_too, int lane) {
+  const rsrc_t rC = make_rsrc(a.ctrl, 8);
+  uint32_t spins = 0;
+  while (true) {
+    bool ok = true;
+    for (int i = lane; i < count; i += 64) {
+      const uint32_t off = (uint32_t)(first + i) * 4u;
+      ok = ok && (buf_load_u32_coherent(r, off) == want);
+    }
+    if (count_too && lane == 0) ok = ok && (buf_load_u32_coherent(rC, 4u) == (uint32_t)a.GB);
+    if (__all(ok)) break;
+    if (++spins > kSpSpinLimit) {
+      if (lane == 0) st_agent_u32(a.ctrl + 2, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Y producer b: column groups b * gpw .. + gpw - 1, the waves of a group
+// splitting the rank's k-steps; NB = B blocks held per wave.  `tlds`
+// receives T's operand planes (whole kilobytes).
+template <int NB>
+__device__ __forceinline__ void y_producer(const SplitArgs& a, int b, uint32_t gen, uint32_t epoch, float (*red)[256],
+                                           char* tlds, uint64_t* tr) {
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int wpg = kSpWaves / a.gpw;  // waves per column group
+  const int gi = w / wpg, sub = w - gi * wpg;
+  const int64_t g = (int64_t)b * a.gpw + gi;
+  const int nk = a.nkB;
+  const int per = (nk + wpg - 1) / wpg;
+  const int s0 = min(nk, sub * per), s1 = min(nk, s0 + per);
+  const bool gok = g < a.GN;
+  const rsrc_t rB = make_rsrc(a.Bsw, (int64_t)a.GN * nk * 1024);
+  const uint32_t gbase = (uint32_t)(g * nk * 1024);
+
+  // count this producer in (no return value: nothing waits for it).  The
+  // increment takes its operand from an empty asm statement that reads the
+  // generation, so it cannot be issued before the generation load returned.
+  if (tid == 0) {
+    uint32_t one = 1u;
+    asm volatile("" : "+v"(one) : "s"(gen));
+    (void)add_agent_u32(a.ctrl + 1, one);
+  }
+
+  // the whole B slab of this wave, requested at once
+  u32x4_t bv[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int s = s0 + i;
+    bv[i] = buf_load16(rB, (gok && s < s1) ? gbase + (uint32_t)(s * 1024 + l * 16) : kSpOut);
+  }
+  SP_TRACE(4);
+
+  // T hand-off: this producer reads replica b % nrep of T and of the T
+  // flags (every replica holds all of T), so that the producers' reads of
+  // the same few kilobytes spread over nrep copies in different memory
+  // channels.  Y producer 0 also waits for the count of Y producers: with
+  // every T flag and every Y producer in, every workgroup of the launch has
+  // read the generation, and it stores the next one.
+  const int q = b % a.nrep;
+  const bool packed = a.M <= 8;
+  const int64_t plane = (int64_t)16 * a.ldp;
+  const int64_t pbytes = plane * (packed ? 1 : 2) * 2;
+  const rsrc_t rP = make_rsrc(a.P + (int64_t)q * plane * (packed ? 1 : 2), pbytes);
+  const rsrc_t rF = make_rsrc(a.flags + (int64_t)q * a.ldf, (int64_t)a.GA * 4);
+  const int nchunk = (int)((pbytes + 1023) / 1024);
+  if (w == 0) spin_until(a, rF, 0, a.GA, epoch, b == 0, l);
+  if (b == 0 && tid == 0) {
+    st_agent_u32(a.ctrl + 1, 0u);
+    st_agent_u32(a.ctrl, epoch);
+  }
+  barrier_lds();
+  SP_TRACE(5);
+  // T's operand planes into LDS: device-coherent direct loads, one kilobyte
+  // per wave instruction, each workgroup starting at a different kilobyte
+  const int c0 = (b * 5) % nchunk;
+  for (int c = w; c < nchunk; c += kSpWaves) {
+    const int cc = c0 + c < nchunk ? c0 + c : c0 + c - nchunk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(tlds + cc * 1024), 16, cc * 1024 + l * 16, 0, 0, kCoherent);
+  }
+  wait_vmem_all();
+  barrier_lds();
+  SP_TRACE(11);
+
+  // GEMM2: lane l, step s reads its operand (row l % 16, columns
+  // 32 s + 8 (l / 16) .. + 7) straight from the planes.  With M <= 8 one
+  // MFMA per step (output rows m and m + 8 add up to Y row m), otherwise
+  // hi then lo.  Steps past this wave's range meet zero B blocks.
+  const uint16_t* prow = reinterpret_cast<const uint16_t*>(tlds) + (l & 15) * a.ldp + 8 * (l >> 4);
+  f32x4_t acc = zero4();
+  if (packed) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int s = min(s0 + i, nk - 1);
+      acc = mfma_16x16x32(*reinterpret_cast<const u32x4_t*>(prow + 32 * s), bv[i], acc);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int s = min(s0 + i, nk - 1);
+      acc = mfma_16x16x32(*reinterpret_cast<const u32x4_t*>(prow + 32 * s), bv[i], acc);
+      acc = mfma_16x16x32(*reinterpret_cast<const u32x4_t*>(prow + plane + 32 * s), bv[i], acc);
+    }
+  }
+  SP_TRACE(7);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) red[w][(4 * (l >> 4) + t) * 16 + (l & 15)] = acc[t];
+  barrier_lds();
+  SP_TRACE(8);
+  for (int idx = tid; idx < a.gpw * 256; idx += kSpThreads) {
+    const int gq = idx >> 8, e = idx & 255;
+    const int row = e >> 4, col = e & 15;
+    float sum = 0.f;
+    for (int q2 = 0; q2 < wpg; ++q2) sum += red[gq * wpg + q2][e];
+    if (packed) {
+      float sum_lo = 0.f;
+      if (row < 8)
+        for (int q2 = 0; q2 < wpg; ++q2) sum_lo += red[gq * wpg + q2][e + 128];
+      sum += sum_lo;
+    }
+    const int64_t n = 16 * ((int64_t)b * a.gpw + gq) + col;
+    if (row < a.M && n < a.N) a.Y[(int64_t)row * a.N + n] = (uint16_t)f32_to_bf16_rne(sum);
+  }
+  SP_TRACE(9);
+}
+
+}  // namespace
+
+template <int NB, bool XAL>
+__global__ __launch_bounds__(kSpThreads) void lr_decode_split_kernel(const SplitArgs a) {
+  __shared__ float red[kSpWaves][256];
+  extern __shared__ __align__(16) char sp_tlds[];  // Y producers: T's operand planes
+  uint64_t tr[16] = {};
+  SP_TRACE(15);
+  const uint32_t gen = __builtin_amdgcn_readfirstlane(ld_agent_u32(a.ctrl));
+  const uint32_t epoch = gen + 1u == 0u ? 1u : gen + 1u;
+  SP_TRACE(0);
+  const int wg = blockIdx.x;
+  if (wg < a.GA)
+    t_producer<XAL>(a, wg, epoch, red, tr);
+  else
+    y_producer<NB>(a, wg - a.GA, gen, epoch, red, sp_tlds, tr);
+#ifdef LR_DECODE_TRACE
+  if (a.trace && threadIdx.x == 0)
+    for (int i = 0; i < 16; ++i) a.trace[blockIdx.x * 16 + i] = tr[i];
+#else
+  (void)tr;
+#endif
+}
+
+int split_blocks_per_wave(const SplitArgs& a) {
+  const int wpg = kSpWaves / a.gpw;
+  return (a.nkB + wpg - 1) / wpg;
+}
+
+template <int NB, bool XAL>
+hipError_t launch_split_variant(const SplitArgs& a, size_t lds, hipStream_t stream) {
+  static bool attr_set = false;  // T takes more than the default 64 KB of dynamic LDS
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)lr_decode_split_kernel<NB, XAL>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSplitMaxTBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((lr_decode_split_kernel<NB, XAL>), dim3((unsigned)(a.GA + a.GB)), dim3(kSpThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_split(const SplitArgs& a, hipStream_t stream) {
+  if (a.M < 1 || a.M > 16 || a.GA < 1 || a.GB < 1 || !(a.gpw == 1 || a.gpw == 2 || a.gpw == 4 || a.gpw == 8))
+    return hipErrorInvalidValue;
+  if ((int64_t)a.GB * a.gpw < a.GN || a.ldp < 32 * a.nkB || a.ldp % 8 != 0 || 16 * a.GA > a.ldp || a.nrep < 1 ||
+      a.nrep > 64 || a.ldf < a.GA)
+    return hipErrorInvalidValue;
+  const size_t lds = (size_t)((16 * a.ldp * 2 * (a.M <= 8 ? 1 : 2) + 1023) / 1024) * 1024;
+  if (lds > (size_t)kSplitMaxTBytes) return hipErrorInvalidValue;
+  const int nb = split_blocks_per_wave(a);
+  const bool xal = (a.K & 7) == 0;
+  if (nb <= 4) return xal ? launch_split_variant<4, true>(a, lds, stream) : launch_split_variant<4, false>(a, lds, stream);
+  if (nb <= 8) return xal ? launch_split_variant<8, true>(a, lds, stream) : launch_split_variant<8, false>(a, lds, stream);
+  if (nb <= kSplitMaxBlocks)
+    return xal ? launch_split_variant<kSplitMaxBlocks, true>(a, lds, stream)
+               : launch_split_variant<kSplitMaxBlocks, false>(a, lds, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lrk

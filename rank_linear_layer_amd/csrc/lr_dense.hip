@@ -33,21 +33,6 @@ constexpr int kDnThreads = 512;  // 8 waves
 constexpr int kDnWaves = kDnThreads / 64;
 constexpr int kDnChunk = 16;     // k-steps whose operands are in flight at once per wave
 
-// Elements [d, d + 8) of the 16-element window (lo, hi), d in 0..7 per lane.
-__device__ __forceinline__ u32x4_t realign_lane(const u32x4_t& lo, const u32x4_t& hi, int d) {
-  const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  const int q = d >> 1;
-  const uint32_t sh = (uint32_t)(d & 1) * 16u;
-  u32x4_t o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t a = q == 0 ? w[i] : q == 1 ? w[i + 1] : q == 2 ? w[i + 2] : w[i + 3];
-    const uint32_t b = q == 0 ? w[i + 1] : q == 1 ? w[i + 2] : q == 2 ? w[i + 3] : w[i + 4];
-    o[i] = __builtin_amdgcn_alignbit(b, a, sh);
-  }
-  return o;
-}
-
 }  // namespace
 
 __global__ __launch_bounds__(256) void lr_dense_swizzle_kernel(const uint16_t* W, uint16_t* Wsw, int64_t K, int64_t N,

@@ -91,6 +91,22 @@ __device__ __forceinline__ u32x4_t realign(const u32x4_t& lo, const u32x4_t& hi,
   return o;
 }
 
+// Elements [d, d + 8) of the 16-element window (lo, hi), d in 0..7 per lane
+// (not wave-uniform: each lane selects its own shift).
+__device__ __forceinline__ u32x4_t realign_lane(const u32x4_t& lo, const u32x4_t& hi, int d) {
+  const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  const int q = d >> 1;
+  const uint32_t sh = (uint32_t)(d & 1) * 16u;
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = q == 0 ? w[i] : q == 1 ? w[i + 1] : q == 2 ? w[i + 2] : w[i + 3];
+    const uint32_t b = q == 0 ? w[i + 1] : q == 1 ? w[i + 2] : q == 2 ? w[i + 3] : w[i + 4];
+    o[i] = __builtin_amdgcn_alignbit(b, a, sh);
+  }
+  return o;
+}
+
 // Zero the elements of an 8-element segment whose column col0 + e >= ncols.
 __device__ __forceinline__ u32x4_t mask_cols(const u32x4_t& v, int64_t col0, int64_t ncols) {
   if (col0 + 8 <= ncols) return v;

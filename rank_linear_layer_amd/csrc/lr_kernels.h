@@ -76,6 +76,33 @@ bool xcd_round_robin(int grid);
 // Workgroups of the decode kernel that one compute unit holds at once (0 on error).
 int decode_blocks_per_cu();
 
+// Role-split decode kernel (lr_decode_split.hip): workgroups [0, GA) each
+// produce 16 rank columns of T over all of K, workgroups [GA, GA + GB) each
+// produce gpw 16-column groups of Y over the whole rank.  Asw and Bsw are A
+// (K x r) and B (r x N) in the dense path's decode layout (see DenseArgs).
+constexpr int kSplitMaxBlocks = 16;  // B blocks a wave of a Y producer holds
+constexpr int64_t kSplitMaxTBytes = 144 * 1024;  // LDS for T's operand planes (whole KB) in a Y producer
+struct SplitArgs {
+  const uint16_t* X;    // [M x K] bf16
+  const uint16_t* Asw;  // ceil(r/16) groups x nkA blocks
+  const uint16_t* Bsw;  // ceil(N/16) groups x nkB blocks
+  uint16_t* Y;          // [M x N] bf16
+  uint16_t* P;          // nrep replicas of T as GEMM2 operand planes, each 16 x ldp bf16: with M <= 8
+                        // one plane (rows 0-7 bf16 hi of T, rows 8-15 bf16 lo), else two (hi, lo of
+                        // 16 rows); columns >= 16 GA stay zero
+  uint32_t* flags;      // nrep replicas of [GA] epoch stamps of published T slices (replica stride ldf)
+  uint32_t* ctrl;       // [0] generation, [1] Y producers past the T wait, [2] spin-timeout flag
+  uint64_t* trace;      // per-workgroup phase timestamps (builds with LR_DECODE_TRACE only)
+  int nrep, ldf;        // replicas of T and of the flags; flag words per replica (multiple of 32)
+  int M, K, r, N;
+  int nkA, nkB;         // ceil(K/32), ceil(r/32)
+  int ldp;              // 32 nkB + 8 (plane rows staggered across LDS banks)
+  int GA, GN, GB, gpw;  // T producers = ceil(r/16); column groups = ceil(N/16); Y producers; groups each
+};
+hipError_t launch_decode_split(const SplitArgs& args, hipStream_t stream);
+// B blocks per wave of a Y producer for this plan (<= kSplitMaxBlocks to launch).
+int split_blocks_per_wave(const SplitArgs& args);
+
 // ----------------------------------------------------------------- dense ---
 // Dense fallback (W = A . B precomputed).  Wsw is W in the decode layout:
 // ceil(N/16) column groups x ceil(K/32) k-steps of 1 KB blocks, each block

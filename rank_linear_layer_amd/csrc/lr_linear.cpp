@@ -83,6 +83,13 @@ struct lr_linear {
   bool dense;
   uint16_t* W;
   uint16_t* Wsw;
+  // role-split decode (dp.kind 2): A and B in the operand block layout,
+  // T [dec_max_M x 32 ceil(r/32)] fp32 and the T slice flags
+  uint16_t* Asw;
+  uint16_t* Bsw;
+  uint16_t* Tsp;
+  uint32_t* sflags;
+  int nrep, ldf;       // replicas of T and of its flags; flag words per replica
 };
 
 namespace {
@@ -162,8 +169,48 @@ lr_status run_dense_decode(const lr_linear* h, uint16_t* Y, const void* X, int64
   return LR_OK;
 }
 
+static_assert(lrk::kSplitMaxBlocks == 16 && lrk::kSplitMaxTBytes == 144 * 1024,
+              "the split plan (decode_split_partition defaults) matches the kernel's limits");
+lr_status run_split_decode(const lr_linear* h, uint16_t* Y, const void* X, int64_t M, hipStream_t stream) {
+  lrk::SplitArgs a;
+  a.X = (const uint16_t*)X;
+  a.Asw = h->Asw;
+  a.Bsw = h->Bsw;
+  a.Y = Y;
+  a.P = h->Tsp;
+  a.flags = h->sflags;
+  a.ctrl = h->ctrl;
+  a.nrep = h->nrep;
+  a.ldf = h->ldf;
+  a.trace = nullptr;
+#ifdef LR_DECODE_TRACE
+  a.trace = g_trace;
+#endif
+  a.M = (int)M;
+  a.K = (int)h->K;
+  a.r = (int)h->r;
+  a.N = (int)h->N;
+  a.nkA = (int)lrv::ceil_div(h->K, 32);
+  a.nkB = (int)lrv::ceil_div(h->r, 32);
+  a.ldp = 32 * a.nkB + 8;
+  a.GA = h->dp.ga;
+  a.GN = h->dp.gn;
+  a.GB = h->dp.gb;
+  a.gpw = h->dp.gpw;
+  const hipError_t e = lrk::launch_decode_split(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "split decode launch");
+  return LR_OK;
+}
+
 lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                      hipStream_t stream) {
+  if (hs[0]->dp.kind == 2) {
+    for (int i = 0; i < n; ++i) {
+      const lr_status st = run_split_decode(hs[i], Ys[i], X, M, stream);
+      if (st != LR_OK) return st;
+    }
+    return LR_OK;
+  }
   lrk::DecArgs a;
   memset(&a, 0, sizeof a);
   a.X = (const uint16_t*)X;
@@ -418,11 +465,17 @@ lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, cons
     }
   }
   for (int b = 0; b < nd;) {
+    if (dh[b]->dp.kind == 2) {  // one launch per projection: it fills the machine by itself
+      const lr_status st = run_split_decode(dh[b], dy[b], X, M, stream);
+      if (st != LR_OK) return st;
+      ++b;
+      continue;
+    }
     const int per_cu = dh[b]->dp.kind == 1 ? 1 : lrk::decode_blocks_per_cu();
     const int64_t cap = (int64_t)num_cus(dh[b]->device) * per_cu;
     int64_t wgs = (int64_t)dh[b]->dp.Jw * dh[b]->dp.S;
     int e = b + 1;
-    while (e < nd && dh[e]->dp.kind == dh[b]->dp.kind && wgs + (int64_t)dh[e]->dp.Jw * dh[e]->dp.S <= cap) {
+    while (e < nd && dh[e]->dp.kind == dh[b]->dp.kind && dh[e]->dp.kind != 2 && wgs + (int64_t)dh[e]->dp.Jw * dh[e]->dp.S <= cap) {
       wgs += (int64_t)dh[e]->dp.Jw * dh[e]->dp.S;
       ++e;
     }
@@ -488,6 +541,7 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
 
   size_t off = 0;
   size_t o_ctrl = 0, o_tcnt = 0, o_tflag = 0, o_ycnt = 0, o_tpart = 0, o_tfin = 0, o_ypart = 0, o_tbuf = 0;
+  size_t o_sflags = 0, o_tsp = 0, o_asw = 0, o_bsw = 0;
   if (h->has_decode) h->dec_max_M = (int)(max_M < LR_DECODE_MAX_M ? max_M : LR_DECODE_MAX_M);
   if (h->has_decode && !h->dense) {
     const int occ = lrk::decode_blocks_per_cu();
@@ -496,7 +550,27 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
       return fail(LR_ERR_HIP, "decode kernel cannot be resident on this device");
     }
     h->dp = lrv::decode_partition(K, r, N, num_cus(dev),
-                                  !(flags & LR_FLAG_DECODE_STREAMING) && lrk::decode_res_available());
+                                  !(flags & LR_FLAG_DECODE_STREAMING) && lrk::decode_res_available(),
+                                  !(flags & (LR_FLAG_DECODE_STREAMING | LR_FLAG_DECODE_RESIDENT)), h->dec_max_M);
+  }
+  if (h->has_decode && !h->dense && h->dp.kind == 2) {
+    // role-split kernel: control words, replicated T slice flags and T
+    // (the Y producers' reads of T spread over the replicas), and both
+    // factors in the operand block layout
+    h->nrep = h->dp.gb < 16 ? h->dp.gb : 16;
+    h->ldf = (int)lrv::round_up(h->dp.ga, 32);
+    o_ctrl = off;
+    off = align_up(off + 64);
+    o_sflags = off;
+    off = align_up(off + (size_t)h->nrep * h->ldf * 4);
+    o_tsp = off;
+    off = align_up(off + (size_t)h->nrep * (h->dec_max_M > 8 ? 2 : 1) * 16 * (32 * lrv::ceil_div(r, 32) + 8) * 2);
+    o_asw = off;
+    off = align_up(off + (size_t)h->dp.ga * lrv::ceil_div(K, 32) * 1024);
+    o_bsw = off;
+    off = align_up(off + (size_t)h->dp.gn * lrv::ceil_div(r, 32) * 1024);
+    h->dws_bytes = (int64_t)off;
+  } else if (h->has_decode && !h->dense) {
     const int64_t G = (int64_t)h->dp.Jw * h->dp.S;
     o_ctrl = off;
     off = align_up(off + 64);
@@ -565,7 +639,22 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     }
   }
   char* base = (char*)h->ws;
-  if (h->has_decode && !h->dense) {
+  if (h->has_decode && !h->dense && h->dp.kind == 2) {
+    h->dws = base;
+    h->ctrl = (uint32_t*)(base + o_ctrl);
+    h->sflags = (uint32_t*)(base + o_sflags);
+    h->Tsp = (uint16_t*)(base + o_tsp);
+    h->Asw = (uint16_t*)(base + o_asw);
+    h->Bsw = (uint16_t*)(base + o_bsw);
+    e = lrk::launch_dense_swizzle(h->A, h->Asw, K, r, nullptr);
+    if (e == hipSuccess) e = lrk::launch_dense_swizzle(h->B, h->Bsw, r, N, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      (void)hipFree(h->ws);
+      delete h;
+      return hip_fail(e, "split decode: factor layout");
+    }
+  } else if (h->has_decode && !h->dense) {
     h->dws = base;  // the decode regions start the workspace
     h->ctrl = (uint32_t*)(base + o_ctrl);
     h->tcnt = (uint32_t*)(base + o_tcnt);
@@ -666,12 +755,20 @@ void lr_linear_destroy(lr_linear* h) {
 
 lr_status lr_linear_describe(const lr_linear* h, char* buf, int64_t len) {
   if (!h || !buf || len <= 0) return fail(LR_ERR_INVALID_ARG, "null handle or buffer");
+  char dec[160];
+  if (h->dp.kind == 2)
+    snprintf(dec, sizeof dec, "kind=split GA=%d GB=%d gpw=%d blocks_per_wave=%d grid=%d", h->dp.ga, h->dp.gb,
+             h->dp.gpw, h->dp.ntps, h->dp.ga + h->dp.gb);
+  else
+    snprintf(dec, sizeof dec, "kind=%s Jw=%d JS=%d S=%d ktps=%d ntps=%d grid=%d",
+             h->dp.kind == 1 ? "resident" : "streaming", h->dp.Jw, h->dp.js_w, h->dp.S, h->dp.ktps, h->dp.ntps,
+             h->dp.Jw * h->dp.S);
   snprintf(buf, (size_t)len,
-           "K=%lld r=%lld N=%lld r_pad=%lld max_M=%lld dense=%d decode=%d[kind=%s Jw=%d JS=%d S=%d ktps=%d ntps=%d grid=%d] "
+           "K=%lld r=%lld N=%lld r_pad=%lld max_M=%lld dense=%d decode=%d[%s] "
            "xcd_local=%d prefill=%d[last phase1 kind=%d nb=%d splits=%d, phase2 kind=%d nb=%d splits=%d] "
            "workspace=%zu",
            (long long)h->K, (long long)h->r, (long long)h->N, (long long)h->r_pad, (long long)h->max_M,
-           (int)h->dense, (int)h->has_decode, h->dp.kind == 1 ? "resident" : "streaming", h->dp.Jw, h->dp.js_w, h->dp.S, h->dp.ktps, h->dp.ntps, h->dp.Jw * h->dp.S, (int)h->xcd_local, (int)h->has_prefill,
+           (int)h->dense, (int)h->has_decode, dec, (int)h->xcd_local, (int)h->has_prefill,
            h->last_plan[0][0].load(), h->last_plan[0][1].load(), h->last_plan[0][2].load(), h->last_plan[1][0].load(),
            h->last_plan[1][1].load(), h->last_plan[1][2].load(), h->ws_bytes);
   return LR_OK;

@@ -48,7 +48,8 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
     return LR_ERR_UNSUPPORTED;
   }
   const uint32_t known = LR_FLAG_FORCE_DECODE | LR_FLAG_FORCE_PREFILL | LR_FLAG_DECODE_STREAMING |
-                         LR_FLAG_PREFILL_TWO_WAVE | LR_FLAG_PREFILL_ONE_WAVE | LR_FLAG_DENSE | LR_FLAG_FACTORED;
+                         LR_FLAG_PREFILL_TWO_WAVE | LR_FLAG_PREFILL_ONE_WAVE | LR_FLAG_DENSE | LR_FLAG_FACTORED |
+                         LR_FLAG_DECODE_SPLIT | LR_FLAG_DECODE_RESIDENT;
   if (flags & ~known) { snprintf(err, errlen, "unknown flag bits 0x%x", flags & ~known); return LR_ERR_UNSUPPORTED; }
   if ((flags & LR_FLAG_FORCE_DECODE) && (flags & LR_FLAG_FORCE_PREFILL)) {
     snprintf(err, errlen, "FORCE_DECODE and FORCE_PREFILL are exclusive");
@@ -57,6 +58,13 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
   if ((flags & LR_FLAG_PREFILL_TWO_WAVE) && (flags & LR_FLAG_PREFILL_ONE_WAVE)) {
     snprintf(err, errlen, "PREFILL_TWO_WAVE and PREFILL_ONE_WAVE are exclusive");
     return LR_ERR_INVALID_ARG;
+  }
+  {
+    const uint32_t dk = flags & (LR_FLAG_DECODE_STREAMING | LR_FLAG_DECODE_SPLIT | LR_FLAG_DECODE_RESIDENT);
+    if (dk & (dk - 1)) {
+      snprintf(err, errlen, "DECODE_STREAMING, DECODE_SPLIT and DECODE_RESIDENT are exclusive");
+      return LR_ERR_INVALID_ARG;
+    }
   }
   if ((flags & LR_FLAG_DENSE) && (flags & LR_FLAG_FACTORED)) {
     snprintf(err, errlen, "DENSE and FACTORED are exclusive");
@@ -166,6 +174,7 @@ inline lr_status check_packed(const Shape& g, const Shape& u, const void* X, con
 // smaller S), subject to Jw * S <= budget.
 struct DecPart {
   int kind, Jw, S, ktps, ntps, js_w, nt_w;
+  int ga, gn, gb, gpw;  // kind 2 only
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -200,7 +209,7 @@ inline bool decode_resident_partition(int64_t K, int64_t r, int64_t N, int budge
 
 inline DecPart decode_streaming_partition(int64_t K, int64_t r, int64_t N, int budget) {
   const int64_t js_w = 120, kt = 32, nt = 120;
-  DecPart p;
+  DecPart p{};
   p.kind = 0;
   p.js_w = (int)js_w;
   p.nt_w = (int)nt;
@@ -221,8 +230,46 @@ inline DecPart decode_streaming_partition(int64_t K, int64_t r, int64_t N, int b
   return p;
 }
 
-inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget, bool allow_resident = true) {
-  DecPart p;
+// kind 2 (role-split): GA = ceil(r/16) workgroups each produce 16 rank
+//   columns of T over all of K; GB workgroups each produce gpw 16-column
+//   groups of Y (gpw the smallest of 1, 2, 4, 8 that fits) over the whole
+//   rank, holding their B blocks in registers: at most max_blocks 1 KB
+//   blocks per wave, eight waves, so ceil(ceil(r/32) / (8 / gpw)) <=
+//   max_blocks.  GA + GB <= budget (one launch, every workgroup resident),
+//   the decode layout of B below 2 GiB (32-bit offsets), and T's GEMM2
+//   operand planes (one plane of 16 x (32 ceil(r/32) + 8) bf16 for
+//   max_M <= 8, two otherwise; whole kilobytes) within max_t_bytes of LDS.
+inline bool decode_split_partition(int64_t K, int64_t r, int64_t N, int budget, DecPart* out, int max_blocks = 16,
+                                   int64_t max_M = 16, int64_t max_t_bytes = 144 * 1024) {
+  const int64_t ga = ceil_div(r, 16), gn = ceil_div(N, 16), nkb = ceil_div(r, 32);
+  if (gn * nkb * 1024 >= ((int64_t)1 << 31) || ceil_div(K, 32) * 1024 >= ((int64_t)1 << 31)) return false;
+  if (ceil_div((max_M > 8 ? 2 : 1) * 16 * (32 * nkb + 8) * 2, 1024) * 1024 > max_t_bytes) return false;
+  for (int gpw = 1; gpw <= 8; gpw *= 2) {
+    const int64_t gb = ceil_div(gn, gpw);
+    const int64_t per = ceil_div(nkb, 8 / gpw);
+    if (ga + gb <= budget && per <= max_blocks) {
+      out->kind = 2;
+      out->Jw = (int)ga;  // reported as the producer counts
+      out->S = 1;
+      out->ktps = (int)ceil_div(K, 32);
+      out->ntps = (int)per;
+      out->js_w = 16;
+      out->nt_w = 16 * gpw;
+      out->ga = (int)ga;
+      out->gn = (int)gn;
+      out->gb = (int)gb;
+      out->gpw = gpw;
+      return true;
+    }
+  }
+  return false;
+}
+
+// `split`: take the role-split kind when it fits (else the others).
+inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget, bool allow_resident = true,
+                                bool split = false, int64_t max_M = 16) {
+  DecPart p{};
+  if (split && decode_split_partition(K, r, N, budget, &p, 16, max_M)) return p;
   if (allow_resident && decode_resident_partition(K, r, N, budget, &p)) return p;
   return decode_streaming_partition(K, r, N, budget);
 }

@@ -62,7 +62,7 @@ def test_create_rejects_bad_arguments_before_any_hip_call(lib):
     # misaligned factor
     assert lib.lr_linear_create(ctypes.byref(h), 8, 4, 8, ctypes.c_void_p(0x1002), fake, 4, 0) == lrl.LR_ERR_INVALID_ARG
     # unknown flags / contradictory flags / forced decode above 16 rows
-    assert lib.lr_linear_create(ctypes.byref(h), 8, 4, 8, fake, fake, 4, 0x80) == lrl.LR_ERR_UNSUPPORTED
+    assert lib.lr_linear_create(ctypes.byref(h), 8, 4, 8, fake, fake, 4, 0x200) == lrl.LR_ERR_UNSUPPORTED
     assert lib.lr_linear_create(ctypes.byref(h), 8, 4, 8, fake, fake, 4, 3) == lrl.LR_ERR_INVALID_ARG
     assert lib.lr_linear_create(ctypes.byref(h), 8, 4, 8, fake, fake, 17, 1) == lrl.LR_ERR_UNSUPPORTED
     # null out pointer

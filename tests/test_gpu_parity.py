@@ -49,7 +49,7 @@ def run_case(M, K, r, N, seed, flags=0, max_M=None, full=True, rows=None, cols=N
 
 # ------------------------------------------------------------ workloads ---
 
-DECODE_KERNELS = [0, lrl.LR_FLAG_DECODE_STREAMING]
+DECODE_KERNELS = [0, lrl.LR_FLAG_DECODE_STREAMING, lrl.LR_FLAG_DECODE_RESIDENT]
 
 
 @pytest.mark.parametrize("M", [1, 8, 16])
@@ -462,7 +462,8 @@ def test_canary_guards_and_poison(gpu, M, N, flags):
     assert_parity(allbits[G:G + M * N].reshape(M, N), oracle.lowrank_bf16(Xb, Ab, Bb), "canary")
 
 
-@pytest.mark.parametrize("M,flags", [(8, 0), (8, lrl.LR_FLAG_DECODE_STREAMING), (48, 0)])
+@pytest.mark.parametrize("M,flags", [(8, 0), (8, lrl.LR_FLAG_DECODE_STREAMING), (8, lrl.LR_FLAG_DECODE_RESIDENT),
+                                     (48, 0)])
 def test_deterministic_bitwise(M, flags):
     K, r, N = 1024, 333, 1500
     Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 1234)
@@ -490,17 +491,61 @@ def test_repeated_calls_new_inputs_and_streams(gpu):
         assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, Ab, Bb), "call %d M=%d" % (i, M))
 
 
-def test_zero_rank_padding_gpu(gpu):
+# role-split decode kernel: shapes whose plan fits it (K of any residue)
+SPLIT_GRID = [(1, 8, 1, 1), (16, 33, 5, 7), (5, 100, 17, 121), (3, 257, 241, 3999), (8, 4096, 1637, 4096),
+              (16, 4100, 1000, 4096), (2, 2000, 300, 250), (7, 4096, 2048, 2048), (1, 4096, 1100, 3999)]
+
+
+@pytest.mark.parametrize("M,K,r,N", SPLIT_GRID)
+def test_split_decode_shapes(M, K, r, N):
+    p, lin, _, _ = run_case(M, K, r, N, 7300 + r + N + M, flags=lrl.LR_FLAG_DECODE_SPLIT)
+    assert "kind=split" in lin.describe(), lin.describe()
+
+
+def test_split_decode_repeated_calls(gpu):
+    # the generation word advances once per launch: many calls on one
+    # handle, M changing, on two streams, each against the oracle
+    torch = gpu
+    K, r, N = 1000, 333, 1500
+    _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 556)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=16, flags=lrl.LR_FLAG_DECODE_SPLIT | lrl.LR_FLAG_FACTORED)
+    assert "kind=split" in lin.describe()
+    side = torch.cuda.Stream()
+    for i, M in enumerate([1, 16, 7, 16, 3, 1, 9, 16]):
+        Xb = datagen.normal_bf16((M, K), 1.0, 700 + i)
+        X = to_dev(Xb)
+        if i % 2:
+            with torch.cuda.stream(side):
+                Y = lin(X)
+            side.synchronize()
+        else:
+            Y = lin(X)
+        assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, Ab, Bb), "split call %d M=%d" % (i, M))
+    # many launches back to back, then one checked
+    Xb = datagen.normal_bf16((4, K), 1.0, 799)
+    X = to_dev(Xb)
+    for _ in range(200):
+        Y = lin(X)
+    torch.cuda.synchronize()
+    assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, Ab, Bb), "split after 200 launches")
+
+
+@pytest.mark.parametrize("flags,width", [(lrl.LR_FLAG_DECODE_STREAMING, 120), (0, 32)])
+def test_zero_rank_padding_gpu(gpu, flags, width):
+    # zero columns of A and rows of B leave the result bitwise unchanged
+    # while the kernel's partition of the rank does not change (120-column
+    # slices for the streaming kernel, 32-deep k-steps for the role-split
+    # one); otherwise the result still meets the oracle
     torch = gpu
     M, K, r, N = 8, 512, 107, 512
     Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 808)
     X = to_dev(Xb)
-    base = to_bits(lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M)(X))
+    base = to_bits(lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=flags)(X))
     for p in (1, 13, 21, 200):
         Ap = np.concatenate([Ab, np.zeros((K, p), np.uint16)], axis=1)
         Bp = np.concatenate([Bb, np.zeros((p, N), np.uint16)], axis=0)
-        yp = to_bits(lrl.LowRankLinear(to_dev(Ap), to_dev(Bp), max_M=M)(X))
-        if (r + p + 119) // 120 == (r + 119) // 120:
+        yp = to_bits(lrl.LowRankLinear(to_dev(Ap), to_dev(Bp), max_M=M, flags=flags)(X))
+        if (r + p + width - 1) // width == (r + width - 1) // width:
             assert np.array_equal(yp, base), "padding by %d changed the result" % p
         else:
             assert_parity(yp, oracle.lowrank_bf16(Xb, Ab, Bb), "padded by %d" % p)
@@ -541,7 +586,8 @@ def test_error_paths_on_device(gpu):
 # replay follows eager work on the same handles and new contents of the
 # captured input, and must equal the eager result for those contents.
 
-@pytest.mark.parametrize("M,flags", [(1, 0), (5, lrl.LR_FLAG_DECODE_STREAMING), (64, 0)])
+@pytest.mark.parametrize("M,flags", [(1, 0), (5, lrl.LR_FLAG_DECODE_STREAMING), (3, lrl.LR_FLAG_DECODE_RESIDENT),
+                                     (12, lrl.LR_FLAG_DECODE_SPLIT), (64, 0)])
 def test_layer_graph_replay(gpu, M, flags):
     torch = gpu
     banner("graph replay M=%d flags=%d" % (M, flags))

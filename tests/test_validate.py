@@ -51,6 +51,17 @@ void t_partition(long long K, long long r, long long N, int budget, int allow_re
   out[0] = p.Jw; out[1] = p.S; out[2] = p.ktps; out[3] = p.ntps;
   out[4] = p.kind; out[5] = p.js_w; out[6] = p.nt_w;
 }
+int t_split_partition(long long K, long long r, long long N, int budget, int* out) {
+  lrv::DecPart p{};
+  const bool ok = lrv::decode_split_partition(K, r, N, budget, &p);
+  out[0] = p.ga; out[1] = p.gn; out[2] = p.gb; out[3] = p.gpw; out[4] = p.ntps; out[5] = p.kind;
+  return ok ? 1 : 0;
+}
+void t_partition2(long long K, long long r, long long N, int budget, int allow_res, int split, int* out) {
+  lrv::DecPart p = lrv::decode_partition(K, r, N, budget, allow_res != 0, split != 0);
+  out[0] = p.Jw; out[1] = p.S; out[2] = p.ktps; out[3] = p.ntps;
+  out[4] = p.kind; out[5] = p.js_w; out[6] = p.nt_w;
+}
 void t_prefill_plan(long long rows, long long c0, long long c1, int nout, long long kd, int cus, int kinds,
                     int q_aligned, int* out) {
   const int64_t cols[2] = {c0, c1};
@@ -129,7 +140,12 @@ def test_create_validation(shim):
     assert shim.t_check_create(4096, 1637, 4096, 0, 0x2000000, 16, 0) == INVALID
     assert shim.t_check_create(4096, 0, 4096, 0x100000, 0x2000000, 16, 0) == INVALID
     assert shim.t_check_create(4096, 1637, 4096, 0x100008, 0x2000000, 16, 0) == INVALID  # 8B aligned only
-    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 128) == UNSUPPORTED  # unknown flag
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 512) == UNSUPPORTED  # unknown flag
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 256) == OK  # DECODE_RESIDENT
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 384) == INVALID  # SPLIT | RESIDENT
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 260) == INVALID  # STREAMING | RESIDENT
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 128) == OK  # DECODE_SPLIT
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 132) == INVALID  # with STREAMING
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 32) == OK  # DENSE
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 64) == OK  # FACTORED
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 96) == INVALID  # both
@@ -241,6 +257,52 @@ def test_decode_partition_balances_q_proj(shim):
     per_wg = ktps * 32 * 120 + ntps * 120 * 120
     ideal = (128 * 32 * 120 + 35 * 120 * 120) / S
     assert per_wg <= 1.25 * ideal
+
+
+def _split(shim, K, r, N, budget=256):
+    out = (ctypes.c_int * 6)()
+    ok = shim.t_split_partition(K, r, N, budget, out)
+    return ok, tuple(out)
+
+
+@pytest.mark.parametrize("K,r,N", [(4096, 1637, 4096), (4096, 1000, 4096), (4096, 1100, 3999), (4096, 817, 1024),
+                                   (33, 5, 7), (100, 17, 121), (257, 241, 3999), (8, 1, 1), (4096, 1, 4096),
+                                   (4096, 2048, 2048)])
+def test_split_partition_covers_and_fits(shim, K, r, N):
+    ok, (ga, gn, gb, gpw, per, kind) = _split(shim, K, r, N)
+    assert ok and kind == 2
+    assert ga == -(-r // 16) and gn == -(-N // 16)
+    assert gpw in (1, 2, 4, 8) and gb == -(-gn // gpw)   # every column group has a producer
+    assert ga + gb <= 256                                # one launch, every workgroup resident
+    nkb = -(-r // 32)
+    assert per == -(-nkb // (8 // gpw)) and per <= 16    # B blocks held per wave
+    assert (8 // gpw) * per >= nkb                       # the waves of a group cover the rank
+    # the smallest gpw that fits
+    if gpw > 1:
+        g2 = gpw // 2
+        assert ga + -(-gn // g2) > 256 or -(-nkb // (8 // g2)) > 16
+
+
+def test_split_partition_q_proj_and_limits(shim):
+    ok, (ga, gn, gb, gpw, per, _) = _split(shim, 4096, 1637, 4096)
+    assert ok and (ga, gn, gb, gpw, per) == (103, 256, 128, 2, 13)
+    # MLP projections: too many producers, or too many B blocks per wave
+    assert not _split(shim, 4096, 2867, 14336)[0]
+    assert not _split(shim, 14336, 2867, 4096)[0]
+    # a rank that needs more than 16 blocks per wave even at gpw = 1
+    assert not _split(shim, 4096, 4200, 512)[0]
+    # a small machine
+    assert not _split(shim, 4096, 1637, 4096, budget=64)[0]
+
+
+def test_split_flag_selects_split_partition(shim):
+    out = (ctypes.c_int * 7)()
+    shim.t_partition2(4096, 1637, 4096, 256, 1, 1, out)
+    assert out[4] == 2
+    shim.t_partition2(4096, 2867, 14336, 256, 1, 1, out)   # does not fit: the other kinds
+    assert out[4] in (0, 1)
+    shim.t_partition2(4096, 1637, 4096, 256, 1, 0, out)
+    assert out[4] == 1
 
 
 TWO_WAVE, ONE_WAVE = 1, 2
