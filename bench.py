@@ -35,7 +35,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "low-rank linear: decode TB/s and prefill TFLOP/s vs roofline, across rank r"
 _CSRC = "rank_linear_layer_amd/csrc/"
-DECODE_SOURCES = [_CSRC + f for f in ("lr_decode.hip", "lr_decode_res.hip", "lr_device.h", "lr_kernels.h")]
+DECODE_SOURCES = [_CSRC + f for f in ("lr_decode.hip", "lr_decode_res.hip", "lr_decode_split.hip", "lr_device.h",
+                                       "lr_kernels.h")]
 PREFILL_SOURCES = [_CSRC + f for f in ("lr_prefill.hip", "lr_prefill_w4.hip", "lr_device.h", "lr_kernels.h",
                                        "lr_validate.h", "lr_linear.cpp")]
 PREFILL_KERNELS = {0: "lr_prefill_gemm_kernel", 1: "lr_prefill_w4_kernel"}
@@ -129,15 +130,36 @@ def bench_decode(torch, lrl, configs, datagen, metrics, steps, warmup):
     tbs = per / (ms * 1e-3) / 1e12
     # warm-cache figure (same copy every step) for context
     ms_warm = time_steps(torch, lambda i: lins[0](X, out=Y), max(50, steps // 4), 10, stream)
+    # the same rotation replayed from a captured graph, for context
+    us_graph = replay_us(torch, step, ncopies, steps, warmup)
     return dict(M=M, K=K, r=r, N=N, ms=ms, tbs=tbs, bytes=per, ncopies=ncopies,
-                warm_tbs=per / (ms_warm * 1e-3) / 1e12, plan=lins[0].describe())
+                warm_tbs=per / (ms_warm * 1e-3) / 1e12, graph_us=us_graph, plan=lins[0].describe())
+
+
+def replay_us(torch, fn, n, steps, warmup):
+    """Microseconds per call of fn(0..n-1) replayed from one captured HIP
+    graph (no host launch work between the kernels)."""
+    for i in range(n):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    reps = max(1, steps // n)
+    ms = time_steps(torch, lambda i: g.replay(), reps, max(1, warmup // n), torch.cuda.current_stream())
+    del g
+    return ms * 1e3 / n
 
 
 def bench_dense_decode(torch, lrl, configs, steps, warmup):
     """Dense fallback decode (W = A.B formed at create): the k/v layer shape,
     where the library takes it by itself, and the q_proj shape with
     LR_FLAG_DENSE.  Bytes per launch are what the kernel reads and writes,
-    2 (MK + KN + MN); W copies rotate over >= 1 GiB."""
+    2 (MK + KN + MN); W copies rotate over >= 1 GiB.  A single launch is
+    shorter than the host's work per call, so the figure is taken from a
+    captured graph of one launch per copy (the eager figure is kept for
+    context)."""
     g = torch.Generator(device="cuda")
     g.manual_seed(configs.seed_base(configs.LAYER_INDEX, 1))
     out = {}
@@ -150,14 +172,16 @@ def bench_dense_decode(torch, lrl, configs, steps, warmup):
         ncop = max(2, int(np.ceil((1 << 30) / (2 * K * N))))
         lins = [lrl.LowRankLinear(A, B, max_M=M, flags=flags) for _ in range(ncop)]
         assert "dense=1" in lins[0].describe()
-        ms = time_steps(torch, lambda i: lins[i % ncop](X, out=Y), steps, warmup, torch.cuda.current_stream())
+        call = lambda i: lins[i % ncop](X, out=Y)  # noqa: E731
+        eager = time_steps(torch, call, steps, warmup, torch.cuda.current_stream()) * 1e3
+        us = replay_us(torch, call, ncop, steps, warmup)
         byts = 2 * (M * K + K * N + M * N)
-        out[name] = {"M": M, "K": K, "r": r, "N": N, "us_per_launch": round(ms * 1e3, 3),
-                     "hbm_bytes_per_launch": byts, "tbs": round(byts / (ms * 1e-3) / 1e12, 4),
-                     "roofline_frac_hbm": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        out[name] = {"M": M, "K": K, "r": r, "N": N, "us_per_launch": round(us, 3), "us_per_launch_eager": round(eager, 3),
+                     "hbm_bytes_per_launch": byts, "tbs": round(byts / (us * 1e-6) / 1e12, 4),
+                     "roofline_frac_hbm": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": "lr_dense_decode_kernel", "w_copies": ncop}
-        log("dense decode %s: %.2f us/launch, %.3f TB/s of W bytes (%d copies)" % (name, ms * 1e3,
-                                                                                  out[name]["tbs"], ncop))
+        log("dense decode %s: %.2f us/launch from a graph (%.2f eager), %.3f TB/s of W bytes (%d copies)"
+            % (name, us, eager, out[name]["tbs"], ncop))
         del lins
         torch.cuda.empty_cache()
     return out
@@ -395,7 +419,8 @@ def main():
 
     torch.cuda.synchronize()
     d = bench_decode(torch, lrl, configs, datagen, metrics, args.steps, args.warmup)
-    log("decode: %.3f us/step, %.3f TB/s (warm-cache %.3f TB/s)" % (d["ms"] * 1e3, d["tbs"], d["warm_tbs"]))
+    log("decode: %.3f us/step, %.3f TB/s (warm-cache %.3f TB/s; from a captured graph %.3f us/step)"
+        % (d["ms"] * 1e3, d["tbs"], d["warm_tbs"], d["graph_us"]))
     kname = decode_kernel_name(d["plan"])
     # one step is one launch of the decode kernel, launched back to back:
     # the event-timed average step is the kernel's average launch duration
@@ -422,6 +447,7 @@ def main():
                      "kernel": kname, "algorithmic_bytes_per_launch": d["bytes"],
                      "us_per_launch": round(d["ms"] * 1e3, 3)},
         "warm_cache_tbs": round(d["warm_tbs"], 4),
+        "graph_replay_us_per_step": round(d["graph_us"], 3),
     }
     if not args.no_prefill:
         p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 50), 3)
