@@ -29,11 +29,14 @@
  * Ownership
  * ---------
  * A and B are BORROWED by the handle: the caller keeps them alive and
- * unchanged until lr_linear_destroy.  They are never copied, repacked or
- * padded in device memory.  X and Y are borrowed for the duration of the
- * enqueued work.  The handle OWNS a device workspace (allocated at create,
- * sized for max_M) that holds split-K partial sums and, for M > 16, the
- * bf16 intermediate T; lr_linear_destroy frees it.  Because the workspace
+ * unchanged until lr_linear_destroy.  X and Y are borrowed for the duration
+ * of the enqueued work.  The handle OWNS a device workspace (allocated at
+ * create, sized for max_M) that holds split-K partial sums, for M > 16 the
+ * bf16 intermediate T, and the copies that some kernels read instead of A
+ * and B: the dense fallback's W, and for the role-split decode kernel A
+ * and B in its operand block layout (both made at create, so decode does
+ * not see later changes to A and B; prefill reads A and B themselves);
+ * lr_linear_destroy frees it.  Because the workspace
  * is shared by every call on a handle, a handle must not be used by two
  * streams at the same time.
  *
@@ -101,8 +104,13 @@ typedef struct lr_linear lr_linear;
  *   max_M  : largest M that lr_linear_run will be called with (>= 0).
  *   flags  : LR_FLAG_* bits.
  * Chooses the kernels' partitioning for this shape and allocates the
- * workspace on the current HIP device.  Launches no kernel, except for the
- * dense fallback: when LR_FLAG_DENSE is set, or (without LR_FLAG_FACTORED)
+ * workspace on the current HIP device.  Decode (M <= 16) takes the
+ * role-split kernel where its plan fits (T produced by ceil(r/16)
+ * workgroups, Y by the rest, all resident at once; B's blocks for one
+ * workgroup in registers), unless LR_FLAG_DECODE_RESIDENT or
+ * LR_FLAG_DECODE_STREAMING is set; create then copies A and B into its
+ * operand layout on the null stream and waits.  Otherwise create launches
+ * no kernel, except for the dense fallback: when LR_FLAG_DENSE is set, or (without LR_FLAG_FACTORED)
  * when the factors hold at least 95% of the bytes of the K x N matrix they
  * replace, i.e. 100 r (K + N) >= 95 K N ("LowRankArena: What Happens When
  * You Force SVD Compression Papers to Play by the Same Rules", Q3: a dense
@@ -123,8 +131,9 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N,
 /*
  * lr_linear_run -- Y[M x N] = (X[M x K] . A) . B on `stream`.
  *   M in [0, max_M]; M == 0 returns LR_OK and launches nothing.
- * M <= 16: one fused launch (split-K GEMM1, on-chip T hand-off, GEMM2,
- * deterministic reduction; T never round-trips through HBM).
+ * M <= 16: one fused launch (GEMM1, T handed between workgroups inside the
+ * launch, GEMM2, deterministic reductions; T is never written as a tensor
+ * for a second kernel).
  * M > 16: MFMA GEMM1 into a bf16 T workspace, then MFMA GEMM2.
  * Graph capture: a run only enqueues kernels, and its launch arguments do
  * not change from call to call (the decode kernels stamp their exchanges
