@@ -53,6 +53,10 @@ constexpr uint32_t kSpOut = 0x7FFFFF00u;  // past every buffer range: loads read
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+__device__ __forceinline__ void buf_store_u16(rsrc_t r, uint32_t byte_off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, r, (int)byte_off, 0, 0);
+}
+
 __device__ __forceinline__ void buf_store8_coherent(rsrc_t r, uint32_t byte_off, uint32_t v0, uint32_t v1) {
   typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
   const u32x2_t v = {v0, v1};
@@ -165,11 +169,11 @@ __device__ __forceinline__ void t_producer(const SplitArgs& a, int j, uint32_t e
 }
 
 // Wave 0 spins until the 32-bit words [first, first + count) of `r` all
-// equal `want` (and, when `count_too`, ctrl[1] equals GB), with
+// equal `want` (and, when `count_too`, ctrl[1] equals `count_want`), with
 // device-coherent loads.  Gives up after kSpSpinLimit rounds and raises the
 // timeout flag.
 __device__ __forceinline__ void spin_until(const SplitArgs& a, rsrc_t r, int first, int count, uint32_t want,
-                                           bool count_too, int lane) {
+                                           bool count_too, uint32_t count_want, int lane) {
   const rsrc_t rC = make_rsrc(a.ctrl, 8);
   uint32_t spins = 0;
   while (true) {
@@ -178,7 +182,7 @@ __device__ __forceinline__ void spin_until(const SplitArgs& a, rsrc_t r, int fir
       const uint32_t off = (uint32_t)(first + i) * 4u;
       ok = ok && (buf_load_u32_coherent(r, off) == want);
     }
-    if (count_too && lane == 0) ok = ok && (buf_load_u32_coherent(rC, 4u) == (uint32_t)a.GB);
+    if (count_too && lane == 0) ok = ok && (buf_load_u32_coherent(rC, 4u) == count_want);
     if (__all(ok)) break;
     if (++spins > kSpSpinLimit) {
       if (lane == 0) st_agent_u32(a.ctrl + 2, 1u);
@@ -238,7 +242,7 @@ __device__ __forceinline__ void y_producer(const SplitArgs& a, int b, uint32_t g
   const rsrc_t rP = make_rsrc(a.P + (int64_t)q * plane * (packed ? 1 : 2), pbytes);
   const rsrc_t rF = make_rsrc(a.flags + (int64_t)q * a.ldf, (int64_t)a.GA * 4);
   const int nchunk = (int)((pbytes + 1023) / 1024);
-  if (w == 0) spin_until(a, rF, 0, a.GA, epoch, b == 0, l);
+  if (w == 0) spin_until(a, rF, 0, a.GA, epoch, b == 0, (uint32_t)a.GB, l);
   if (b == 0 && tid == 0) {
     st_agent_u32(a.ctrl + 1, 0u);
     st_agent_u32(a.ctrl, epoch);
@@ -298,6 +302,127 @@ __device__ __forceinline__ void y_producer(const SplitArgs& a, int b, uint32_t g
   SP_TRACE(9);
 }
 
+// Count this workgroup in (ctrl[1]; no return value, so nothing waits for
+// it).  The increment takes its operand from an empty asm statement that
+// reads the generation, so it cannot be issued before that load returned.
+__device__ __forceinline__ void count_in(const SplitArgs& a, uint32_t gen) {
+  if (threadIdx.x == 0) {
+    uint32_t one = 1u;
+    asm volatile("" : "+v"(one) : "s"(gen));
+    (void)add_agent_u32(a.ctrl + 1, one);
+  }
+}
+
+// The B blocks of column group g for this wave's k-steps [s0, s1) (zeros
+// when !ok or past s1).
+template <int NB>
+__device__ __forceinline__ void load_group(u32x4_t (&buf)[NB], rsrc_t rB, int64_t g, int nk, int s0, int s1, bool ok,
+                                           int l) {
+  const uint32_t base = (uint32_t)(g * nk * 1024) + (uint32_t)(l * 16);
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    buf[i] = buf_load16(rB, (ok && s0 + i < s1) ? base + (uint32_t)((s0 + i) * 1024) : kSpOut);
+}
+
+// Y work of the streaming variant: column groups [g0, g1), each over the
+// whole rank, the eight waves splitting its k-steps.  A wave loads its T
+// operands once and keeps them in registers for every group; B blocks
+// stream through two register buffers, both filled before T is awaited and
+// each refilled as soon as its MFMAs are issued; each group's eight
+// partials are summed in LDS (two buffers, one barrier per group) and
+// stored as bf16.  `writer`: this
+// workgroup waits for every workgroup's count as well and stores the next
+// generation.
+template <int NB, bool TWO>
+__device__ __forceinline__ void y_stream(const SplitArgs& a, int wg, int g0, int g1, uint32_t epoch, bool writer,
+                                         float (*red)[kSpWaves][256], uint64_t* tr) {
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int nk = a.nkB;
+  const int per = (nk + kSpWaves - 1) / kSpWaves;
+  const int s0 = min(nk, w * per), s1 = min(nk, s0 + per);
+  const rsrc_t rB = make_rsrc(a.Bsw, (int64_t)a.GN * nk * 1024);
+  u32x4_t b0[NB], b1[NB];
+  load_group<NB>(b0, rB, g0, nk, s0, s1, g0 < g1, l);
+  load_group<NB>(b1, rB, g0 + 1, nk, s0, s1, g0 + 1 < g1, l);
+  SP_TRACE(4);
+
+  // every T slice published (device-coherent flags of replica wg % nrep)
+  const int q = wg % a.nrep;
+  constexpr bool packed = !TWO;  // TWO: M > 8, hi and lo in two planes
+  const int64_t plane = (int64_t)16 * a.ldp;
+  if (w == 0) spin_until(a, make_rsrc(a.flags + (int64_t)q * a.ldf, (int64_t)a.GA * 4), 0, a.GA, epoch, writer,
+                         (uint32_t)a.G, l);
+  if (writer && tid == 0) {
+    st_agent_u32(a.ctrl + 1, 0u);
+    st_agent_u32(a.ctrl, epoch);
+  }
+  barrier_lds();
+  SP_TRACE(5);
+  // this wave's T operands: lane l, step s -> plane row l % 16, columns
+  // 32 s + 8 (l / 16) .. + 7.  Rows that hold only zeros for this M are not
+  // fetched (out-of-range offsets read as zero).
+  const int m = l & 15;
+  const bool row_used = packed ? (m & 7) < a.M : m < a.M;
+  const rsrc_t rP = make_rsrc(a.P + (int64_t)q * plane * (packed ? 1 : 2), plane * (packed ? 1 : 2) * 2);
+  const uint32_t pbase = (uint32_t)((m * a.ldp + 8 * (l >> 4)) * 2);
+  u32x4_t t0[NB], t1[TWO ? NB : 1];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const bool ok = row_used && s0 + i < s1;
+    const uint32_t off = pbase + (uint32_t)((s0 + i) * 64);
+    t0[i] = __builtin_bit_cast(u32x4_t, buf_load16_coherent(rP, ok ? off : kSpOut));
+    if constexpr (TWO) t1[i] = __builtin_bit_cast(u32x4_t, buf_load16_coherent(rP, ok ? off + (uint32_t)(plane * 2) : kSpOut));
+  }
+  SP_TRACE(11);
+
+  const rsrc_t rY = make_rsrc(a.Y, (int64_t)a.M * a.N * 2);
+  int buf = 0;
+  auto mma = [&](const u32x4_t(&bv)[NB]) {
+    f32x4_t acc = zero4();
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      acc = mfma_16x16x32(t0[i], bv[i], acc);
+      if constexpr (TWO) acc = mfma_16x16x32(t1[i], bv[i], acc);
+    }
+    return acc;
+  };
+  // sum group g's partials and store them (stores past M, N or g1 are dropped)
+  auto finish = [&](const f32x4_t& acc, int g) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) red[buf][w][(4 * (l >> 4) + t) * 16 + (l & 15)] = acc[t];
+    barrier_lds();
+    if (tid < 256) {
+      const int row = tid >> 4, col = tid & 15;
+      float sum = 0.f;
+#pragma unroll
+      for (int v = 0; v < kSpWaves; ++v) sum += red[buf][v][tid];
+      if (packed && row < 8) {
+        float lo = 0.f;
+#pragma unroll
+        for (int v = 0; v < kSpWaves; ++v) lo += red[buf][v][tid + 128];
+        sum += lo;
+      }
+      const int64_t n = 16 * (int64_t)g + col;
+      const bool ok = g < g1 && row < a.M && n < a.N;
+      buf_store_u16(rY, ok ? (uint32_t)((row * (int64_t)a.N + n) * 2) : kSpOut, f32_to_bf16_rne(sum));
+    }
+    buf ^= 1;
+  };
+  // two groups in flight: a buffer is refilled as soon as its MFMAs are
+  // issued, before the group's partials are summed
+  for (int g = g0; g < g1; g += 2) {
+    const f32x4_t acc0 = mma(b0);
+    load_group<NB>(b0, rB, g + 2, nk, s0, s1, g + 2 < g1, l);
+    finish(acc0, g);
+    const f32x4_t acc1 = mma(b1);
+    load_group<NB>(b1, rB, g + 3, nk, s0, s1, g + 3 < g1, l);
+    finish(acc1, g + 1);
+  }
+  SP_TRACE(9);
+}
+
 }  // namespace
 
 template <int NB, bool XAL>
@@ -327,6 +452,45 @@ int split_blocks_per_wave(const SplitArgs& a) {
   return (a.nkB + wpg - 1) / wpg;
 }
 
+// Streaming variant: every workgroup computes Y for its column groups; the
+// first GA also produce T first (and take fewer groups).
+template <int NB, bool XAL, bool TWO>
+__global__ __launch_bounds__(kSpThreads) void lr_decode_splits_kernel(const SplitArgs a) {
+  __shared__ float red[2][kSpWaves][256];
+  uint64_t tr[16] = {};
+  SP_TRACE(15);
+  const uint32_t gen = __builtin_amdgcn_readfirstlane(ld_agent_u32(a.ctrl));
+  const uint32_t epoch = gen + 1u == 0u ? 1u : gen + 1u;
+  SP_TRACE(0);
+  count_in(a, gen);
+  const int wg = blockIdx.x;
+  int g0, g1;
+  if (wg < a.GA) {
+    t_producer<XAL>(a, wg, epoch, red[0], tr);
+    g0 = wg * a.nt;
+    g1 = g0 + a.nt;
+  } else {
+    const int y = wg - a.GA, gy = a.G - a.GA;
+    const int rest = a.GN - a.GA * a.nt;
+    g0 = a.GA * a.nt + (int)((int64_t)y * rest / gy);
+    g1 = a.GA * a.nt + (int)((int64_t)(y + 1) * rest / gy);
+  }
+  g1 = min(g1, a.GN);
+  y_stream<NB, TWO>(a, wg, g0, g1, epoch, wg == a.G - 1, red, tr);
+#ifdef LR_DECODE_TRACE
+  if (a.trace && threadIdx.x == 0)
+    for (int i = 0; i < 16; ++i) a.trace[blockIdx.x * 16 + i] = tr[i];
+#else
+  (void)tr;
+#endif
+}
+
+template <int NB, bool XAL, bool TWO>
+hipError_t launch_splits_variant(const SplitArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((lr_decode_splits_kernel<NB, XAL, TWO>), dim3((unsigned)a.G), dim3(kSpThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int NB, bool XAL>
 hipError_t launch_split_variant(const SplitArgs& a, size_t lds, hipStream_t stream) {
   static bool attr_set = false;  // T takes more than the default 64 KB of dynamic LDS
@@ -341,6 +505,26 @@ hipError_t launch_split_variant(const SplitArgs& a, size_t lds, hipStream_t stre
 }
 
 hipError_t launch_decode_split(const SplitArgs& a, hipStream_t stream) {
+  if (a.stream_y) {
+    // streaming variant: G workgroups, the first GA also T producers with nt
+    // groups each; every wave of a workgroup holds at most kSplitMaxBlocks
+    // B blocks of a group (twice) and as many T operands (twice for M > 8)
+    const int per = (a.nkB + kSpWaves - 1) / kSpWaves;
+    if (a.M < 1 || a.M > 16 || a.GA < 1 || a.G < a.GA || a.G < 1 || a.nt < 0 || (a.G > a.GA && (int64_t)a.GA * a.nt > a.GN) ||
+        (a.G == a.GA && (int64_t)a.GA * a.nt < a.GN) || a.ldp < 32 * a.nkB || a.ldp % 8 != 0 || 16 * a.GA > a.ldp ||
+        a.nrep < 1 || a.nrep > 64 || a.ldf < a.GA || per > kSplitMaxBlocks || (a.M > 8 && per > 8))
+      return hipErrorInvalidValue;
+    const bool xal = (a.K & 7) == 0;
+    if (a.M > 8) {
+      if (per <= 4) return xal ? launch_splits_variant<4, true, true>(a, stream) : launch_splits_variant<4, false, true>(a, stream);
+      return xal ? launch_splits_variant<8, true, true>(a, stream) : launch_splits_variant<8, false, true>(a, stream);
+    }
+    if (per <= 4) return xal ? launch_splits_variant<4, true, false>(a, stream) : launch_splits_variant<4, false, false>(a, stream);
+    if (per <= 8) return xal ? launch_splits_variant<8, true, false>(a, stream) : launch_splits_variant<8, false, false>(a, stream);
+    if (per <= 12)
+      return xal ? launch_splits_variant<12, true, false>(a, stream) : launch_splits_variant<12, false, false>(a, stream);
+    return xal ? launch_splits_variant<16, true, false>(a, stream) : launch_splits_variant<16, false, false>(a, stream);
+  }
   if (a.M < 1 || a.M > 16 || a.GA < 1 || a.GB < 1 || !(a.gpw == 1 || a.gpw == 2 || a.gpw == 4 || a.gpw == 8))
     return hipErrorInvalidValue;
   if ((int64_t)a.GB * a.gpw < a.GN || a.ldp < 32 * a.nkB || a.ldp % 8 != 0 || 16 * a.GA > a.ldp || a.nrep < 1 ||

@@ -98,6 +98,10 @@ struct SplitArgs {
   int nkA, nkB;         // ceil(K/32), ceil(r/32)
   int ldp;              // 32 nkB + 8 (plane rows staggered across LDS banks)
   int GA, GN, GB, gpw;  // T producers = ceil(r/16); column groups = ceil(N/16); Y producers; groups each
+  // streaming variant (stream_y = 1): G workgroups, all computing Y; the
+  // first GA produce T first and take nt column groups each, the other
+  // G - GA share the rest.  Every wave keeps its T operands in registers.
+  int stream_y, G, nt;
 };
 hipError_t launch_decode_split(const SplitArgs& args, hipStream_t stream);
 // B blocks per wave of a Y producer for this plan (<= kSplitMaxBlocks to launch).

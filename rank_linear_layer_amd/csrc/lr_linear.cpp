@@ -197,6 +197,9 @@ lr_status run_split_decode(const lr_linear* h, uint16_t* Y, const void* X, int64
   a.GN = h->dp.gn;
   a.GB = h->dp.gb;
   a.gpw = h->dp.gpw;
+  a.stream_y = h->dp.kind == 3 ? 1 : 0;
+  a.G = h->dp.g;
+  a.nt = h->dp.nt;
   const hipError_t e = lrk::launch_decode_split(a, stream);
   if (e != hipSuccess) return hip_fail(e, "split decode launch");
   return LR_OK;
@@ -204,7 +207,7 @@ lr_status run_split_decode(const lr_linear* h, uint16_t* Y, const void* X, int64
 
 lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                      hipStream_t stream) {
-  if (hs[0]->dp.kind == 2) {
+  if (hs[0]->dp.kind == 2 || hs[0]->dp.kind == 3) {
     for (int i = 0; i < n; ++i) {
       const lr_status st = run_split_decode(hs[i], Ys[i], X, M, stream);
       if (st != LR_OK) return st;
@@ -465,7 +468,7 @@ lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, cons
     }
   }
   for (int b = 0; b < nd;) {
-    if (dh[b]->dp.kind == 2) {  // one launch per projection: it fills the machine by itself
+    if (dh[b]->dp.kind == 2 || dh[b]->dp.kind == 3) {  // one launch per projection: it fills the machine
       const lr_status st = run_split_decode(dh[b], dy[b], X, M, stream);
       if (st != LR_OK) return st;
       ++b;
@@ -475,7 +478,7 @@ lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, cons
     const int64_t cap = (int64_t)num_cus(dh[b]->device) * per_cu;
     int64_t wgs = (int64_t)dh[b]->dp.Jw * dh[b]->dp.S;
     int e = b + 1;
-    while (e < nd && dh[e]->dp.kind == dh[b]->dp.kind && dh[e]->dp.kind != 2 && wgs + (int64_t)dh[e]->dp.Jw * dh[e]->dp.S <= cap) {
+    while (e < nd && dh[e]->dp.kind == dh[b]->dp.kind && dh[e]->dp.kind < 2 && wgs + (int64_t)dh[e]->dp.Jw * dh[e]->dp.S <= cap) {
       wgs += (int64_t)dh[e]->dp.Jw * dh[e]->dp.S;
       ++e;
     }
@@ -553,11 +556,12 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
                                   !(flags & LR_FLAG_DECODE_STREAMING) && lrk::decode_res_available(),
                                   !(flags & (LR_FLAG_DECODE_STREAMING | LR_FLAG_DECODE_RESIDENT)), h->dec_max_M);
   }
-  if (h->has_decode && !h->dense && h->dp.kind == 2) {
-    // role-split kernel: control words, replicated T slice flags and T
+  if (h->has_decode && !h->dense && (h->dp.kind == 2 || h->dp.kind == 3)) {
+    // role-split kernels: control words, replicated T slice flags and T
     // (the Y producers' reads of T spread over the replicas), and both
     // factors in the operand block layout
-    h->nrep = h->dp.gb < 16 ? h->dp.gb : 16;
+    const int readers = h->dp.kind == 3 ? h->dp.g : h->dp.gb;
+    h->nrep = readers < 16 ? readers : 16;
     h->ldf = (int)lrv::round_up(h->dp.ga, 32);
     o_ctrl = off;
     off = align_up(off + 64);
@@ -639,7 +643,7 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     }
   }
   char* base = (char*)h->ws;
-  if (h->has_decode && !h->dense && h->dp.kind == 2) {
+  if (h->has_decode && !h->dense && (h->dp.kind == 2 || h->dp.kind == 3)) {
     h->dws = base;
     h->ctrl = (uint32_t*)(base + o_ctrl);
     h->sflags = (uint32_t*)(base + o_sflags);
@@ -759,6 +763,9 @@ lr_status lr_linear_describe(const lr_linear* h, char* buf, int64_t len) {
   if (h->dp.kind == 2)
     snprintf(dec, sizeof dec, "kind=split GA=%d GB=%d gpw=%d blocks_per_wave=%d grid=%d", h->dp.ga, h->dp.gb,
              h->dp.gpw, h->dp.ntps, h->dp.ga + h->dp.gb);
+  else if (h->dp.kind == 3)
+    snprintf(dec, sizeof dec, "kind=split_stream GA=%d GY=%d nt=%d blocks_per_wave=%d grid=%d", h->dp.ga, h->dp.gb,
+             h->dp.nt, h->dp.ntps, h->dp.g);
   else
     snprintf(dec, sizeof dec, "kind=%s Jw=%d JS=%d S=%d ktps=%d ntps=%d grid=%d",
              h->dp.kind == 1 ? "resident" : "streaming", h->dp.Jw, h->dp.js_w, h->dp.S, h->dp.ktps, h->dp.ntps,

@@ -174,7 +174,8 @@ inline lr_status check_packed(const Shape& g, const Shape& u, const void* X, con
 // smaller S), subject to Jw * S <= budget.
 struct DecPart {
   int kind, Jw, S, ktps, ntps, js_w, nt_w;
-  int ga, gn, gb, gpw;  // kind 2 only
+  int ga, gn, gb, gpw;  // kinds 2 and 3
+  int g, nt;            // kind 3: workgroups, column groups per T producer
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -265,11 +266,59 @@ inline bool decode_split_partition(int64_t K, int64_t r, int64_t N, int budget, 
   return false;
 }
 
-// `split`: take the role-split kind when it fits (else the others).
+// kind 3 (role-split, streaming Y): for shapes whose B does not fit the
+//   Y producers' registers (the MLP projections).  G = min(budget,
+//   GA + GN) workgroups all compute Y; the first GA (GA = ceil(r/16) <= G)
+//   first produce T and so take fewer column groups: bytes per workgroup
+//   are balanced with A's slab plus X (ceil(K/32) KB + max_M K 2 bytes) per
+//   T producer against ceil(r/32) KB of B per column group; a T producer's
+//   slab above the average share rules the kind out.  Every wave
+//   holds at most max_blocks of a group's B blocks (twice) and as many T
+//   operands (twice for max_M > 8, allowed up to 8 blocks per wave).
+inline bool decode_split_stream_partition(int64_t K, int64_t r, int64_t N, int budget, DecPart* out,
+                                          int max_blocks = 16, int64_t max_M = 16) {
+  const int64_t ga = ceil_div(r, 16), gn = ceil_div(N, 16), nkb = ceil_div(r, 32), nka = ceil_div(K, 32);
+  const int64_t per = ceil_div(nkb, 8);
+  if (per > max_blocks || (max_M > 8 && per > 8)) return false;
+  if (gn * nkb * 1024 >= ((int64_t)1 << 31) || nka * 1024 >= ((int64_t)1 << 31)) return false;
+  if (ga > budget) return false;
+  const int64_t g = budget < ga + gn ? budget : ga + gn;
+  const int64_t gy = g - ga;
+  const double ca = (double)nka + (double)(max_M * K * 2) / 1024.0, cb = (double)nkb;
+  int64_t nt;
+  if (gy == 0) {
+    nt = ceil_div(gn, ga);
+  } else {
+    const double target = ((double)ga * ca + (double)gn * cb) / (double)g;
+    // a T producer's slab heavier than the average workgroup's share would
+    // make the T side the bound (the down projection: K = 14336): the
+    // slice-split kernels spread A over every workgroup instead
+    if (ca > target) return false;
+    nt = (int64_t)((target - ca) / cb);
+    if (ga * nt > gn) nt = gn / ga;
+  }
+  out->kind = 3;
+  out->Jw = (int)ga;
+  out->S = 1;
+  out->ktps = (int)nka;
+  out->ntps = (int)per;
+  out->js_w = 16;
+  out->nt_w = 16;
+  out->ga = (int)ga;
+  out->gn = (int)gn;
+  out->gb = (int)gy;
+  out->gpw = 0;
+  out->g = (int)g;
+  out->nt = (int)nt;
+  return true;
+}
+
+// `split`: take a role-split kind when one fits (else the others).
 inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget, bool allow_resident = true,
                                 bool split = false, int64_t max_M = 16) {
   DecPart p{};
   if (split && decode_split_partition(K, r, N, budget, &p, 16, max_M)) return p;
+  if (split && decode_split_stream_partition(K, r, N, budget, &p, 16, max_M)) return p;
   if (allow_resident && decode_resident_partition(K, r, N, budget, &p)) return p;
   return decode_streaming_partition(K, r, N, budget);
 }

@@ -502,6 +502,45 @@ def test_split_decode_shapes(M, K, r, N):
     assert "kind=split" in lin.describe(), lin.describe()
 
 
+# streaming-Y role-split kernel: B too large for the Y producers' registers
+SPLIT_STREAM_GRID = [(1, 4096, 2867, 14336, 1), (8, 4096, 2867, 14336, 8), (4, 2048, 2867, 9000, 4),
+                     (3, 1001, 2500, 9001, 3), (12, 2048, 2000, 12000, 12), (9, 2048, 2000, 12000, 16),
+                     (1, 512, 4096, 64, 1), (2, 300, 1500, 20000, 2)]
+
+
+@pytest.mark.parametrize("M,K,r,N,max_M", SPLIT_STREAM_GRID)
+def test_split_stream_decode_shapes(M, K, r, N, max_M):
+    p, lin, _, _ = run_case(M, K, r, N, 7700 + r + N + M, max_M=max_M)
+    assert "kind=split_stream" in lin.describe(), lin.describe()
+
+
+def test_split_stream_repeated_calls(gpu):
+    # one handle, M changing within max_M = 8, several streams, then many
+    # launches back to back
+    torch = gpu
+    K, r, N = 1500, 2100, 9000
+    _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 557)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=8, flags=lrl.LR_FLAG_FACTORED)
+    assert "kind=split_stream" in lin.describe(), lin.describe()
+    side = torch.cuda.Stream()
+    for i, M in enumerate([1, 8, 5, 8, 2, 1]):
+        Xb = datagen.normal_bf16((M, K), 1.0, 720 + i)
+        X = to_dev(Xb)
+        if i % 2:
+            with torch.cuda.stream(side):
+                Y = lin(X)
+            side.synchronize()
+        else:
+            Y = lin(X)
+        assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, Ab, Bb), "split_stream call %d M=%d" % (i, M))
+    Xb = datagen.normal_bf16((3, K), 1.0, 798)
+    X = to_dev(Xb)
+    for _ in range(100):
+        Y = lin(X)
+    torch.cuda.synchronize()
+    assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, Ab, Bb), "split_stream after 100 launches")
+
+
 def test_split_decode_repeated_calls(gpu):
     # the generation word advances once per launch: many calls on one
     # handle, M changing, on two streams, each against the oracle

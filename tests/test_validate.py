@@ -57,8 +57,15 @@ int t_split_partition(long long K, long long r, long long N, int budget, int* ou
   out[0] = p.ga; out[1] = p.gn; out[2] = p.gb; out[3] = p.gpw; out[4] = p.ntps; out[5] = p.kind;
   return ok ? 1 : 0;
 }
-void t_partition2(long long K, long long r, long long N, int budget, int allow_res, int split, int* out) {
-  lrv::DecPart p = lrv::decode_partition(K, r, N, budget, allow_res != 0, split != 0);
+int t_split_stream_partition(long long K, long long r, long long N, int budget, long long max_M, int* out) {
+  lrv::DecPart p{};
+  const bool ok = lrv::decode_split_stream_partition(K, r, N, budget, &p, 16, max_M);
+  out[0] = p.ga; out[1] = p.gn; out[2] = p.gb; out[3] = p.g; out[4] = p.nt; out[5] = p.ntps; out[6] = p.kind;
+  return ok ? 1 : 0;
+}
+void t_partition2(long long K, long long r, long long N, int budget, int allow_res, int split, long long max_M,
+                  int* out) {
+  lrv::DecPart p = lrv::decode_partition(K, r, N, budget, allow_res != 0, split != 0, max_M);
   out[0] = p.Jw; out[1] = p.S; out[2] = p.ktps; out[3] = p.ntps;
   out[4] = p.kind; out[5] = p.js_w; out[6] = p.nt_w;
 }
@@ -297,12 +304,63 @@ def test_split_partition_q_proj_and_limits(shim):
 
 def test_split_flag_selects_split_partition(shim):
     out = (ctypes.c_int * 7)()
-    shim.t_partition2(4096, 1637, 4096, 256, 1, 1, out)
+    shim.t_partition2(4096, 1637, 4096, 256, 1, 1, ctypes.c_longlong(16), out)
     assert out[4] == 2
-    shim.t_partition2(4096, 2867, 14336, 256, 1, 1, out)   # does not fit: the other kinds
+    shim.t_partition2(4096, 4200, 14336, 256, 1, 1, ctypes.c_longlong(16), out)   # fits neither split kind: the other kinds
     assert out[4] in (0, 1)
-    shim.t_partition2(4096, 1637, 4096, 256, 1, 0, out)
+    shim.t_partition2(4096, 1637, 4096, 256, 1, 0, ctypes.c_longlong(16), out)
     assert out[4] == 1
+
+
+def _split_stream(shim, K, r, N, budget=256, max_M=1):
+    out = (ctypes.c_int * 7)()
+    ok = shim.t_split_stream_partition(K, r, N, budget, max_M, out)
+    return ok, tuple(out)
+
+
+@pytest.mark.parametrize("K,r,N,max_M", [(4096, 2867, 14336, 1), (4096, 2867, 14336, 8), (2048, 2867, 14336, 1),
+                                         (1001, 2500, 9001, 3), (2048, 2000, 12000, 12), (512, 4096, 64, 1),
+                                         (2048, 1637, 4096, 1), (64, 16, 16, 1)])
+def test_split_stream_partition_covers_and_balances(shim, K, r, N, max_M):
+    ok, (ga, gn, gy, g, nt, per, kind) = _split_stream(shim, K, r, N, max_M=max_M)
+    assert ok and kind == 3
+    assert ga == -(-r // 16) and gn == -(-N // 16) and g == min(256, ga + gn) and gy == g - ga
+    nkb = -(-r // 32)
+    assert per == -(-nkb // 8) and per <= 16 and (max_M <= 8 or per <= 8)
+    if gy == 0:
+        assert ga * nt >= gn                 # T producers take every group
+    else:
+        assert 0 <= ga * nt <= gn            # the rest go to the Y-only workgroups
+        # bytes per workgroup balanced to within one group (or T producers
+        # take none because their A slab alone exceeds the average)
+        ca = -(-K // 32) + max_M * K * 2 / 1024.0
+        rest = gn - ga * nt
+        y_max = -(-rest // gy) * nkb
+        t_bytes = ca + nt * nkb
+        assert ca <= (ga * ca + gn * nkb) / g    # T producers not above the average
+        assert nt == 0 or t_bytes <= y_max + 2 * nkb + ca
+
+
+def test_split_stream_partition_layer_shapes(shim):
+    # gate/up at M = 1: 180 T producers with 3 column groups each, 76 more
+    # workgroups share the other 356
+    ok, (ga, gn, gy, g, nt, per, _) = _split_stream(shim, 4096, 2867, 14336)
+    assert ok and (ga, gn, gy, g, nt, per) == (180, 896, 76, 256, 3, 12)
+    # down: the A slab (448 KB) exceeds the average share: not this kind
+    assert not _split_stream(shim, 14336, 2867, 4096)[0]
+    # M up to 16 needs at most 8 blocks per wave
+    assert not _split_stream(shim, 4096, 2867, 14336, max_M=16)[0]
+    # a rank above 4096 does not fit; more T producers than CUs neither
+    assert not _split_stream(shim, 4096, 4200, 512)[0]
+    assert not _split_stream(shim, 4096, 4100, 4096, budget=200)[0]
+
+
+def test_decode_partition_prefers_register_split_then_streaming_split(shim):
+    out = (ctypes.c_int * 7)()
+    shim.t_partition2(4096, 1637, 4096, 256, 1, 1, ctypes.c_longlong(16), out)
+    assert out[4] == 2
+    shim.t_partition2(4096, 2867, 14336, 256, 1, 1, ctypes.c_longlong(1), out)   # B too large for registers: streaming split
+    assert out[4] == 3
 
 
 TWO_WAVE, ONE_WAVE = 1, 2
