@@ -320,7 +320,7 @@ def _split_stream(shim, K, r, N, budget=256, max_M=1):
 
 @pytest.mark.parametrize("K,r,N,max_M", [(4096, 2867, 14336, 1), (4096, 2867, 14336, 8), (2048, 2867, 14336, 1),
                                          (1001, 2500, 9001, 3), (2048, 2000, 12000, 12), (512, 4096, 64, 1),
-                                         (2048, 1637, 4096, 1), (64, 16, 16, 1)])
+                                         (2048, 1637, 4096, 1), (1024, 700, 30000, 2)])
 def test_split_stream_partition_covers_and_balances(shim, K, r, N, max_M):
     ok, (ga, gn, gy, g, nt, per, kind) = _split_stream(shim, K, r, N, max_M=max_M)
     assert ok and kind == 3
