@@ -544,12 +544,10 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
 }
 
 hipError_t launch_decode_res(const DecArgs& args, int grid, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lr_decode_res_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kResLdsBytes);
+  static std::atomic<uint64_t> attr_done{0};
+  {
+    const hipError_t e = ensure_dynamic_lds((const void*)lr_decode_res_kernel, kResLdsBytes, attr_done);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   hipLaunchKernelGGL(lr_decode_res_kernel, dim3(grid), dim3(kResThreads), kResLdsBytes, stream, args);
   return hipGetLastError();

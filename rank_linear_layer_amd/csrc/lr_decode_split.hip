@@ -49,6 +49,9 @@ constexpr int kSpThreads = 512;  // 8 waves
 constexpr int kSpWaves = kSpThreads / 64;
 constexpr int kSpChunk = 16;     // A blocks in flight per wave at once
 constexpr uint32_t kSpSpinLimit = 1u << 22;
+#ifndef LR_SPLIT_SLEEP
+#define LR_SPLIT_SLEEP 1  // s_sleep units (64 clocks) between flag polls
+#endif
 constexpr uint32_t kSpOut = 0x7FFFFF00u;  // past every buffer range: loads read 0, stores are dropped
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -188,7 +191,7 @@ __device__ __forceinline__ void spin_until(const SplitArgs& a, rsrc_t r, int fir
       if (lane == 0) st_agent_u32(a.ctrl + 2, 1u);
       break;
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(LR_SPLIT_SLEEP);
   }
 }
 
@@ -493,12 +496,10 @@ hipError_t launch_splits_variant(const SplitArgs& a, hipStream_t stream) {
 
 template <int NB, bool XAL>
 hipError_t launch_split_variant(const SplitArgs& a, size_t lds, hipStream_t stream) {
-  static bool attr_set = false;  // T takes more than the default 64 KB of dynamic LDS
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)lr_decode_split_kernel<NB, XAL>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSplitMaxTBytes);
+  static std::atomic<uint64_t> attr_done{0};
+  {
+    const hipError_t e = ensure_dynamic_lds((const void*)lr_decode_split_kernel<NB, XAL>, (int)kSplitMaxTBytes, attr_done);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   hipLaunchKernelGGL((lr_decode_split_kernel<NB, XAL>), dim3((unsigned)(a.GA + a.GB)), dim3(kSpThreads), lds, stream, a);
   return hipGetLastError();

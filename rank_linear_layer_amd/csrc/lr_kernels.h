@@ -4,7 +4,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace lrk {
+
+// Raise a kernel's dynamic-LDS limit to `bytes` once per device (the limit
+// is a property of the kernel on the current device; `done` holds one bit
+// per device id below 64, set after a successful call, so concurrent first
+// calls at worst set it twice).
+inline hipError_t ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // ---------------------------------------------------------------- decode ---
 // Tile geometry of the fused decode kernel (M <= 16).

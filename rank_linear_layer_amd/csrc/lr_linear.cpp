@@ -46,6 +46,12 @@ __attribute__((visibility("hidden"))) lr_status lr_internal_fail(lr_status st, c
 namespace {
 
 constexpr size_t kAlign = 256;
+// Replicas of the role-split kernels' T planes and flags: the Y producers'
+// reads of the same few kilobytes spread over this many copies.
+#ifndef LR_SPLIT_NREP
+#define LR_SPLIT_NREP 8
+#endif
+constexpr int kSplitReplicas = LR_SPLIT_NREP;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 }  // namespace
@@ -561,7 +567,7 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     // (the Y producers' reads of T spread over the replicas), and both
     // factors in the operand block layout
     const int readers = h->dp.kind == 3 ? h->dp.g : h->dp.gb;
-    h->nrep = readers < 16 ? readers : 16;
+    h->nrep = readers < kSplitReplicas ? readers : kSplitReplicas;
     h->ldf = (int)lrv::round_up(h->dp.ga, 32);
     o_ctrl = off;
     off = align_up(off + 64);

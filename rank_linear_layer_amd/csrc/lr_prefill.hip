@@ -465,12 +465,10 @@ __global__ __launch_bounds__(256) void lr_prefill_reduce_kernel(const float* par
 
 template <int NB, bool PAL>
 hipError_t launch_one(const PreArgs& args, int grid, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lr_prefill_gemm_kernel<NB, PAL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPreLdsBytes);
+  static std::atomic<uint64_t> attr_done{0};
+  {
+    const hipError_t e = ensure_dynamic_lds((const void*)lr_prefill_gemm_kernel<NB, PAL>, kPreLdsBytes, attr_done);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   hipLaunchKernelGGL((lr_prefill_gemm_kernel<NB, PAL>), dim3(grid), dim3(kThreads), kPreLdsBytes, stream, args);
   return hipGetLastError();

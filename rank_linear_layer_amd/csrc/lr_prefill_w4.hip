@@ -547,12 +547,10 @@ __global__ __launch_bounds__(kThreads, 1) void lr_prefill_w4_kernel(const PreArg
 
 template <int QMOD>
 hipError_t launch_w4(const PreArgs& args, int grid, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lr_prefill_w4_kernel<QMOD>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  static std::atomic<uint64_t> attr_done{0};
+  {
+    const hipError_t e = ensure_dynamic_lds((const void*)lr_prefill_w4_kernel<QMOD>, kLdsBytes, attr_done);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   hipLaunchKernelGGL((lr_prefill_w4_kernel<QMOD>), dim3(grid), dim3(kThreads), kLdsBytes, stream, args);
   return hipGetLastError();
