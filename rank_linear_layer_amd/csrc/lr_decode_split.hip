@@ -81,6 +81,37 @@ __device__ __forceinline__ uint64_t sp_trace_now() {
   } while (0)
 #endif
 
+// Wave-level: T slice j (lane -> row `row` of the 16 operand rows, columns
+// c .. c + 3 of the slice, values v) split into bf16 hi + lo and stored as
+// GEMM2's MFMA operand rows in every replica (see P in SplitArgs), then
+// every replica's flag of slice j set to `epoch` once the stores are
+// acknowledged.
+__device__ __forceinline__ void publish_planes(const SplitArgs& a, int j, const float (&v)[4], int row, int c,
+                                               uint32_t epoch, int l) {
+  const bool packed = a.M <= 8;
+  uint32_t hi[2], lo[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t h0 = f32_to_bf16_rne(v[2 * p]), h1 = f32_to_bf16_rne(v[2 * p + 1]);
+    hi[p] = h0 | (h1 << 16);
+    lo[p] = pack_bf16x2(v[2 * p] - __uint_as_float(h0 << 16), v[2 * p + 1] - __uint_as_float(h1 << 16));
+  }
+  const bool take_lo = packed && row >= 8;
+  const int planes = packed ? 1 : 2;
+  const int64_t plane = (int64_t)16 * a.ldp;  // bf16 per plane
+  const int64_t rep = plane * planes;         // bf16 per replica
+  const rsrc_t rP = make_rsrc(a.P, rep * a.nrep * 2);
+  const uint32_t off = (uint32_t)((row * a.ldp + 16 * j + c) * 2);
+  for (int q = 0; q < a.nrep; ++q) {
+    const uint32_t qo = off + (uint32_t)(q * rep * 2);
+    buf_store8_coherent(rP, qo, take_lo ? lo[0] : hi[0], take_lo ? lo[1] : hi[1]);
+    if (!packed) buf_store8_coherent(rP, qo + (uint32_t)(plane * 2), lo[0], lo[1]);
+  }
+  wait_vmem_all();  // the slice is visible before its flags
+  if (l < a.nrep)
+    buf_store_u32_coherent(make_rsrc(a.flags, (int64_t)a.nrep * a.ldf * 4), (uint32_t)(l * a.ldf + j) * 4u, epoch);
+}
+
 // T producer: rank columns [16 j, 16 j + 16) over all of K, eight waves
 // splitting the k-steps, then the slice published and flagged.
 template <bool XAL>
@@ -146,27 +177,7 @@ __device__ __forceinline__ void t_producer(const SplitArgs& a, int j, uint32_t e
       for (int q = 0; q < kSpWaves; ++q) s += red[q][trow * 16 + c + i];
       v[i] = s;
     }
-    uint32_t hi[2], lo[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint32_t h0 = f32_to_bf16_rne(v[2 * p]), h1 = f32_to_bf16_rne(v[2 * p + 1]);
-      hi[p] = h0 | (h1 << 16);
-      lo[p] = pack_bf16x2(v[2 * p] - __uint_as_float(h0 << 16), v[2 * p + 1] - __uint_as_float(h1 << 16));
-    }
-    const bool take_lo = packed && row >= 8;
-    const int planes = packed ? 1 : 2;
-    const int64_t plane = (int64_t)16 * a.ldp;       // bf16 per plane
-    const int64_t rep = plane * planes;              // bf16 per replica
-    const rsrc_t rP = make_rsrc(a.P, rep * a.nrep * 2);
-    const uint32_t off = (uint32_t)((row * a.ldp + 16 * j + c) * 2);
-    for (int q = 0; q < a.nrep; ++q) {
-      const uint32_t qo = off + (uint32_t)(q * rep * 2);
-      buf_store8_coherent(rP, qo, take_lo ? lo[0] : hi[0], take_lo ? lo[1] : hi[1]);
-      if (!packed) buf_store8_coherent(rP, qo + (uint32_t)(plane * 2), lo[0], lo[1]);
-    }
-    wait_vmem_all();  // the slice is visible before its flags
-    if (l < a.nrep)
-      buf_store_u32_coherent(make_rsrc(a.flags, (int64_t)a.nrep * a.ldf * 4), (uint32_t)(l * a.ldf + j) * 4u, epoch);
+    publish_planes(a, j, v, row, c, epoch, l);
   }
   SP_TRACE(3);
 }
@@ -330,15 +341,33 @@ __device__ __forceinline__ void load_group(u32x4_t (&buf)[NB], rsrc_t rB, int64_
 // Y work of the streaming variant: column groups [g0, g1), each over the
 // whole rank, the eight waves splitting its k-steps.  A wave loads its T
 // operands once and keeps them in registers for every group; B blocks
-// stream through two register buffers, both filled before T is awaited and
-// each refilled as soon as its MFMAs are issued; each group's eight
+// stream through two register buffers, both filled (y_prefetch) before T
+// is awaited and each refilled as soon as its MFMAs are issued; each group's eight
 // partials are summed in LDS (two buffers, one barrier per group) and
 // stored as bf16.  `writer`: this
 // workgroup waits for every workgroup's count as well and stores the next
 // generation.
+// The first two column groups' B blocks of this wave, requested ahead of
+// the rest of the Y work (y_stream refills the same buffers).
+template <int NB>
+struct YBufs {
+  u32x4_t b0[NB], b1[NB];
+};
+template <int NB>
+__device__ __forceinline__ void y_prefetch(const SplitArgs& a, int g0, int g1, YBufs<NB>& yb) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  const int nk = a.nkB;
+  const int per = (nk + kSpWaves - 1) / kSpWaves;
+  const int s0 = min(nk, w * per), s1 = min(nk, s0 + per);
+  const rsrc_t rB = make_rsrc(a.Bsw, (int64_t)a.GN * nk * 1024);
+  load_group<NB>(yb.b0, rB, g0, nk, s0, s1, g0 < g1, l);
+  load_group<NB>(yb.b1, rB, g0 + 1, nk, s0, s1, g0 + 1 < g1, l);
+}
+
 template <int NB, bool TWO>
 __device__ __forceinline__ void y_stream(const SplitArgs& a, int wg, int g0, int g1, uint32_t epoch, bool writer,
-                                         float (*red)[kSpWaves][256], uint64_t* tr) {
+                                         float (*red)[kSpWaves][256], uint64_t* tr, YBufs<NB>& yb) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
@@ -346,9 +375,8 @@ __device__ __forceinline__ void y_stream(const SplitArgs& a, int wg, int g0, int
   const int per = (nk + kSpWaves - 1) / kSpWaves;
   const int s0 = min(nk, w * per), s1 = min(nk, s0 + per);
   const rsrc_t rB = make_rsrc(a.Bsw, (int64_t)a.GN * nk * 1024);
-  u32x4_t b0[NB], b1[NB];
-  load_group<NB>(b0, rB, g0, nk, s0, s1, g0 < g1, l);
-  load_group<NB>(b1, rB, g0 + 1, nk, s0, s1, g0 + 1 < g1, l);
+  u32x4_t(&b0)[NB] = yb.b0;
+  u32x4_t(&b1)[NB] = yb.b1;
   SP_TRACE(4);
 
   // every T slice published (device-coherent flags of replica wg % nrep)
@@ -426,6 +454,139 @@ __device__ __forceinline__ void y_stream(const SplitArgs& a, int wg, int g0, int
   SP_TRACE(9);
 }
 
+// First contributor (workgroup) of the flat block range that holds block b:
+// the largest w with floor(w TB / G) <= b.
+__device__ __forceinline__ int flat_owner(int64_t b, int64_t TB, int G) {
+  return (int)(((b + 1) * G + TB - 1) / TB) - 1;
+}
+
+// T work of the flat variant: workgroup wg takes the A blocks
+// [wg TB / G, (wg + 1) TB / G) of the operand block layout, which is in
+// slice-major order (TB = GA ceil(K/32) blocks), so its range covers parts
+// of at most two rank slices (GA <= G).  The eight waves split the range;
+// a block of the first slice accumulates into acc0, of the second into
+// acc1 (two predicated MFMAs per block, no branch).  Per slice segment:
+// the slice's first contributor (lowest id) owns it: it waits for the
+// other contributors' fp32 partials, adds them to its own in contributor
+// order and publishes the operand planes; every other contributor
+// publishes its partial (device-coherent, with an epoch flag) and never
+// waits.  Wave 0 handles the first segment, wave 1 the second.
+template <bool XAL>
+__device__ __forceinline__ void t_flat(const SplitArgs& a, int wg, uint32_t epoch, float (*red)[kSpWaves][256],
+                                       uint64_t* tr) {
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int nk = a.nkA;
+  const int64_t TB = (int64_t)a.GA * nk;
+  const int64_t b_lo = (int64_t)wg * TB / a.G, b_hi = (int64_t)(wg + 1) * TB / a.G;
+  if (b_lo >= b_hi) return;  // no A work (more workgroups than blocks)
+  const int j0 = (int)(b_lo / nk);
+  const int64_t split_at = (int64_t)(j0 + 1) * nk;  // first block of the second slice
+  const int64_t pw = (b_hi - b_lo + kSpWaves - 1) / kSpWaves;
+  const int64_t w_lo = min64(b_hi, b_lo + w * pw), w_hi = min64(b_hi, w_lo + pw);
+  const rsrc_t rA = make_rsrc(a.Asw, TB * 1024);
+  const rsrc_t rX = make_rsrc(a.X, (int64_t)a.M * a.K * 2);
+  const int m = l & 15;
+  const int64_t xrow = (int64_t)m * a.K;
+  const int d = (int)(xrow & 7);
+  f32x4_t acc0 = zero4(), acc1 = zero4();
+  for (int64_t c0 = w_lo; c0 < w_hi; c0 += kSpChunk) {
+    u32x4_t wv[kSpChunk], xl[kSpChunk], xh[kSpChunk];
+#pragma unroll
+    for (int i = 0; i < kSpChunk; ++i) {
+      const int64_t b = c0 + i;
+      wv[i] = buf_load16(rA, b < w_hi ? (uint32_t)(b * 1024 + l * 16) : kSpOut);
+      const int64_t s = b - (b >= split_at ? split_at : split_at - nk);  // k-step within its slice
+      const int64_t e = xrow + 32 * s + 8 * (l >> 4);
+      if (XAL) {
+        xl[i] = buf_load16(rX, (uint32_t)(e * 2));
+      } else {
+        xl[i] = buf_load16(rX, (uint32_t)((e >> 3) * 16));
+        xh[i] = buf_load16(rX, (uint32_t)((e >> 3) * 16 + 16));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kSpChunk; ++i) {
+      const int64_t b = c0 + i;
+      const int64_t s = b - (b >= split_at ? split_at : split_at - nk);
+      const u32x4_t x0 = mask_cols(XAL ? xl[i] : realign_lane(xl[i], xh[i], d), 32 * s + 8 * (l >> 4), a.K);
+      const u32x4_t x = m < a.M ? x0 : zerou4();
+      const bool second = b >= split_at;
+      acc0 = mfma_16x16x32(second ? zerou4() : x, wv[i], acc0);
+      acc1 = mfma_16x16x32(second ? x : zerou4(), wv[i], acc1);
+    }
+  }
+  SP_TRACE(1);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    red[0][w][(4 * (l >> 4) + t) * 16 + (l & 15)] = acc0[t];
+    red[1][w][(4 * (l >> 4) + t) * 16 + (l & 15)] = acc1[t];
+  }
+  barrier_lds();
+  SP_TRACE(2);
+  const int nseg = b_hi > split_at ? 2 : 1;
+  if (w < nseg) {
+    const int seg = w;
+    const int j = j0 + seg;
+    const int64_t s_beg = (int64_t)j * nk;                 // the slice's blocks
+    const int64_t s_end = s_beg + nk;
+    const int first = flat_owner(s_beg, TB, a.G), last = flat_owner(s_end - 1, TB, a.G);
+    const bool packed = a.M <= 8;
+    const int row = l >> 2, c = (l & 3) * 4;
+    const int trow = packed ? (row & 7) : row;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < kSpWaves; ++q) sum += red[seg][q][trow * 16 + c + i];
+      v[i] = sum;
+    }
+    // partials: [GA][maxc] tiles of 16 x 16 fp32 (rows as T rows), flags [GA][maxc]
+    const rsrc_t rPart = make_rsrc(a.part, (int64_t)a.GA * a.maxc * 1024);
+    const rsrc_t rPF = make_rsrc(a.pflags, (int64_t)a.GA * a.maxc * 4);
+    const int ci = wg - first;
+    if (ci > 0) {
+      // not the owner: publish the partial (T rows 0..15, this lane's row
+      // `row` and columns c..c+3) and its flag
+      f32x4_t pv;
+      for (int i = 0; i < 4; ++i) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < kSpWaves; ++q) sum += red[seg][q][row * 16 + c + i];
+        pv[i] = sum;
+      }
+      buf_store16_coherent(rPart, (uint32_t)(((int64_t)j * a.maxc + ci) * 1024 + (row * 16 + c) * 4), pv);
+      wait_vmem_all();
+      if (l == 0) buf_store_u32_coherent(rPF, (uint32_t)(j * a.maxc + ci) * 4u, epoch);
+    } else {
+      // the owner: add the other contributors' partials in order
+      const int n = last - first + 1;
+      if (n > 1) {
+        uint32_t spins = 0;
+        while (true) {
+          bool ok = true;
+          for (int q = 1 + l; q < n; q += 64) ok = ok && (buf_load_u32_coherent(rPF, (uint32_t)(j * a.maxc + q) * 4u) == epoch);
+          if (__all(ok)) break;
+          if (++spins > kSpSpinLimit) {
+            if (l == 0) st_agent_u32(a.ctrl + 2, 1u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(LR_SPLIT_SLEEP);
+        }
+        for (int q = 1; q < n; ++q) {
+          const f32x4_t pv = buf_load16_coherent(rPart, (uint32_t)(((int64_t)j * a.maxc + q) * 1024 + (trow * 16 + c) * 4));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] += pv[i];
+        }
+      }
+      publish_planes(a, j, v, row, c, epoch, l);
+    }
+  }
+  SP_TRACE(3);
+}
+
 }  // namespace
 
 template <int NB, bool XAL>
@@ -469,7 +630,6 @@ __global__ __launch_bounds__(kSpThreads) void lr_decode_splits_kernel(const Spli
   const int wg = blockIdx.x;
   int g0, g1;
   if (wg < a.GA) {
-    t_producer<XAL>(a, wg, epoch, red[0], tr);
     g0 = wg * a.nt;
     g1 = g0 + a.nt;
   } else {
@@ -479,7 +639,10 @@ __global__ __launch_bounds__(kSpThreads) void lr_decode_splits_kernel(const Spli
     g1 = a.GA * a.nt + (int)((int64_t)(y + 1) * rest / gy);
   }
   g1 = min(g1, a.GN);
-  y_stream<NB, TWO>(a, wg, g0, g1, epoch, wg == a.G - 1, red, tr);
+  YBufs<NB> yb;
+  if (wg < a.GA) t_producer<XAL>(a, wg, epoch, red[0], tr);
+  y_prefetch<NB>(a, g0, g1, yb);
+  y_stream<NB, TWO>(a, wg, g0, g1, epoch, wg == a.G - 1, red, tr, yb);
 #ifdef LR_DECODE_TRACE
   if (a.trace && threadIdx.x == 0)
     for (int i = 0; i < 16; ++i) a.trace[blockIdx.x * 16 + i] = tr[i];
@@ -491,6 +654,40 @@ __global__ __launch_bounds__(kSpThreads) void lr_decode_splits_kernel(const Spli
 template <int NB, bool XAL, bool TWO>
 hipError_t launch_splits_variant(const SplitArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((lr_decode_splits_kernel<NB, XAL, TWO>), dim3((unsigned)a.G), dim3(kSpThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Flat variant: every workgroup takes an equal share of A (in slice-major
+// block order) and then an equal share of Y's column groups.
+template <int NB, bool XAL, bool TWO>
+__global__ __launch_bounds__(kSpThreads) void lr_decode_splitf_kernel(const SplitArgs a) {
+  __shared__ float red[2][kSpWaves][256];
+  uint64_t tr[16] = {};
+  SP_TRACE(15);
+  const uint32_t gen = __builtin_amdgcn_readfirstlane(ld_agent_u32(a.ctrl));
+  const uint32_t epoch = gen + 1u == 0u ? 1u : gen + 1u;
+  SP_TRACE(0);
+  count_in(a, gen);
+  const int wg = blockIdx.x;
+  const int g0 = (int)((int64_t)wg * a.GN / a.G), g1 = (int)((int64_t)(wg + 1) * a.GN / a.G);
+  // B is requested only once this workgroup's share of A is in and its T
+  // work published: requested earlier, it slows the A stream that every
+  // slice waits for
+  t_flat<XAL>(a, wg, epoch, red, tr);
+  YBufs<NB> yb;
+  y_prefetch<NB>(a, g0, g1, yb);
+  y_stream<NB, TWO>(a, wg, g0, g1, epoch, wg == a.G - 1, red, tr, yb);
+#ifdef LR_DECODE_TRACE
+  if (a.trace && threadIdx.x == 0)
+    for (int i = 0; i < 16; ++i) a.trace[blockIdx.x * 16 + i] = tr[i];
+#else
+  (void)tr;
+#endif
+}
+
+template <int NB, bool XAL, bool TWO>
+hipError_t launch_splitf_variant(const SplitArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((lr_decode_splitf_kernel<NB, XAL, TWO>), dim3((unsigned)a.G), dim3(kSpThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -506,6 +703,30 @@ hipError_t launch_split_variant(const SplitArgs& a, size_t lds, hipStream_t stre
 }
 
 hipError_t launch_decode_split(const SplitArgs& a, hipStream_t stream) {
+  if (a.stream_y == 2) {
+    // flat variant: GA <= G (a workgroup's share of A spans at most two
+    // slices), partial tiles for maxc contributors per slice
+    const int per = (a.nkB + kSpWaves - 1) / kSpWaves;
+    const int64_t TB = (int64_t)a.GA * a.nkA;
+    if (a.M < 1 || a.M > 16 || a.GA < 1 || a.G < a.GA || TB * 1024 >= ((int64_t)1 << 31) || a.ldp < 32 * a.nkB ||
+        a.ldp % 8 != 0 || 16 * a.GA > a.ldp || a.nrep < 1 || a.nrep > 64 || a.ldf < a.GA || per > kSplitMaxBlocks ||
+        (a.M > 8 && per > 8) || a.maxc < 1 || !a.part || !a.pflags)
+      return hipErrorInvalidValue;
+    // every slice's contributors fit the partial table: a slice of nkA
+    // blocks meets at most ceil(nkA / R) + 1 ranges of length >= R
+    const int64_t R = TB / a.G > 0 ? TB / a.G : 1;
+    if ((a.nkA + R - 1) / R + 1 > a.maxc) return hipErrorInvalidValue;
+    const bool xal = (a.K & 7) == 0;
+    if (a.M > 8) {
+      if (per <= 4) return xal ? launch_splitf_variant<4, true, true>(a, stream) : launch_splitf_variant<4, false, true>(a, stream);
+      return xal ? launch_splitf_variant<8, true, true>(a, stream) : launch_splitf_variant<8, false, true>(a, stream);
+    }
+    if (per <= 4) return xal ? launch_splitf_variant<4, true, false>(a, stream) : launch_splitf_variant<4, false, false>(a, stream);
+    if (per <= 8) return xal ? launch_splitf_variant<8, true, false>(a, stream) : launch_splitf_variant<8, false, false>(a, stream);
+    if (per <= 12)
+      return xal ? launch_splitf_variant<12, true, false>(a, stream) : launch_splitf_variant<12, false, false>(a, stream);
+    return xal ? launch_splitf_variant<16, true, false>(a, stream) : launch_splitf_variant<16, false, false>(a, stream);
+  }
   if (a.stream_y) {
     // streaming variant: G workgroups, the first GA also T producers with nt
     // groups each; every wave of a workgroup holds at most kSplitMaxBlocks

@@ -119,6 +119,12 @@ struct SplitArgs {
   // first GA produce T first and take nt column groups each, the other
   // G - GA share the rest.  Every wave keeps its T operands in registers.
   int stream_y, G, nt;
+  // flat variant (stream_y = 2): every workgroup takes TB / G of A's blocks
+  // in slice-major order (TB = GA nkA) and GN / G column groups of Y; the
+  // first contributor of a slice adds the others' partials
+  float* part;          // [GA][maxc] tiles of 16 x 16 fp32
+  uint32_t* pflags;     // [GA][maxc] epoch stamps of the partial tiles
+  int maxc;             // contributors per slice the table holds (>= ceil(nkA / max(1, TB / G)) + 1)
 };
 hipError_t launch_decode_split(const SplitArgs& args, hipStream_t stream);
 // B blocks per wave of a Y producer for this plan (<= kSplitMaxBlocks to launch).

@@ -96,6 +96,8 @@ struct lr_linear {
   uint16_t* Tsp;
   uint32_t* sflags;
   int nrep, ldf;       // replicas of T and of its flags; flag words per replica
+  float* fpart;        // flat variant: partial tiles [GA][maxc] of 16 x 16 fp32
+  uint32_t* pflags;    // flat variant: their flags
 };
 
 namespace {
@@ -203,9 +205,12 @@ lr_status run_split_decode(const lr_linear* h, uint16_t* Y, const void* X, int64
   a.GN = h->dp.gn;
   a.GB = h->dp.gb;
   a.gpw = h->dp.gpw;
-  a.stream_y = h->dp.kind == 3 ? 1 : 0;
+  a.stream_y = h->dp.kind == 4 ? 2 : h->dp.kind == 3 ? 1 : 0;
   a.G = h->dp.g;
   a.nt = h->dp.nt;
+  a.part = h->fpart;
+  a.pflags = h->pflags;
+  a.maxc = h->dp.maxc;
   const hipError_t e = lrk::launch_decode_split(a, stream);
   if (e != hipSuccess) return hip_fail(e, "split decode launch");
   return LR_OK;
@@ -213,7 +218,7 @@ lr_status run_split_decode(const lr_linear* h, uint16_t* Y, const void* X, int64
 
 lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                      hipStream_t stream) {
-  if (hs[0]->dp.kind == 2 || hs[0]->dp.kind == 3) {
+  if (hs[0]->dp.kind >= 2) {
     for (int i = 0; i < n; ++i) {
       const lr_status st = run_split_decode(hs[i], Ys[i], X, M, stream);
       if (st != LR_OK) return st;
@@ -474,7 +479,7 @@ lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, cons
     }
   }
   for (int b = 0; b < nd;) {
-    if (dh[b]->dp.kind == 2 || dh[b]->dp.kind == 3) {  // one launch per projection: it fills the machine
+    if (dh[b]->dp.kind >= 2) {  // one launch per projection: it fills the machine
       const lr_status st = run_split_decode(dh[b], dy[b], X, M, stream);
       if (st != LR_OK) return st;
       ++b;
@@ -550,7 +555,7 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
 
   size_t off = 0;
   size_t o_ctrl = 0, o_tcnt = 0, o_tflag = 0, o_ycnt = 0, o_tpart = 0, o_tfin = 0, o_ypart = 0, o_tbuf = 0;
-  size_t o_sflags = 0, o_tsp = 0, o_asw = 0, o_bsw = 0;
+  size_t o_sflags = 0, o_tsp = 0, o_asw = 0, o_bsw = 0, o_fpart = 0, o_pflags = 0;
   if (h->has_decode) h->dec_max_M = (int)(max_M < LR_DECODE_MAX_M ? max_M : LR_DECODE_MAX_M);
   if (h->has_decode && !h->dense) {
     const int occ = lrk::decode_blocks_per_cu();
@@ -562,11 +567,11 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
                                   !(flags & LR_FLAG_DECODE_STREAMING) && lrk::decode_res_available(),
                                   !(flags & (LR_FLAG_DECODE_STREAMING | LR_FLAG_DECODE_RESIDENT)), h->dec_max_M);
   }
-  if (h->has_decode && !h->dense && (h->dp.kind == 2 || h->dp.kind == 3)) {
+  if (h->has_decode && !h->dense && (h->dp.kind >= 2)) {
     // role-split kernels: control words, replicated T slice flags and T
     // (the Y producers' reads of T spread over the replicas), and both
     // factors in the operand block layout
-    const int readers = h->dp.kind == 3 ? h->dp.g : h->dp.gb;
+    const int readers = h->dp.kind >= 3 ? h->dp.g : h->dp.gb;
     h->nrep = readers < kSplitReplicas ? readers : kSplitReplicas;
     h->ldf = (int)lrv::round_up(h->dp.ga, 32);
     o_ctrl = off;
@@ -575,6 +580,12 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     off = align_up(off + (size_t)h->nrep * h->ldf * 4);
     o_tsp = off;
     off = align_up(off + (size_t)h->nrep * (h->dec_max_M > 8 ? 2 : 1) * 16 * (32 * lrv::ceil_div(r, 32) + 8) * 2);
+    if (h->dp.kind == 4) {
+      o_fpart = off;
+      off = align_up(off + (size_t)h->dp.ga * h->dp.maxc * 1024);
+      o_pflags = off;
+      off = align_up(off + (size_t)h->dp.ga * h->dp.maxc * 4);
+    }
     o_asw = off;
     off = align_up(off + (size_t)h->dp.ga * lrv::ceil_div(K, 32) * 1024);
     o_bsw = off;
@@ -649,11 +660,13 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     }
   }
   char* base = (char*)h->ws;
-  if (h->has_decode && !h->dense && (h->dp.kind == 2 || h->dp.kind == 3)) {
+  if (h->has_decode && !h->dense && (h->dp.kind >= 2)) {
     h->dws = base;
     h->ctrl = (uint32_t*)(base + o_ctrl);
     h->sflags = (uint32_t*)(base + o_sflags);
     h->Tsp = (uint16_t*)(base + o_tsp);
+    h->fpart = h->dp.kind == 4 ? (float*)(base + o_fpart) : nullptr;
+    h->pflags = h->dp.kind == 4 ? (uint32_t*)(base + o_pflags) : nullptr;
     h->Asw = (uint16_t*)(base + o_asw);
     h->Bsw = (uint16_t*)(base + o_bsw);
     e = lrk::launch_dense_swizzle(h->A, h->Asw, K, r, nullptr);
@@ -772,6 +785,9 @@ lr_status lr_linear_describe(const lr_linear* h, char* buf, int64_t len) {
   else if (h->dp.kind == 3)
     snprintf(dec, sizeof dec, "kind=split_stream GA=%d GY=%d nt=%d blocks_per_wave=%d grid=%d", h->dp.ga, h->dp.gb,
              h->dp.nt, h->dp.ntps, h->dp.g);
+  else if (h->dp.kind == 4)
+    snprintf(dec, sizeof dec, "kind=split_flat GA=%d maxc=%d blocks_per_wave=%d grid=%d", h->dp.ga, h->dp.maxc,
+             h->dp.ntps, h->dp.g);
   else
     snprintf(dec, sizeof dec, "kind=%s Jw=%d JS=%d S=%d ktps=%d ntps=%d grid=%d",
              h->dp.kind == 1 ? "resident" : "streaming", h->dp.Jw, h->dp.js_w, h->dp.S, h->dp.ktps, h->dp.ntps,

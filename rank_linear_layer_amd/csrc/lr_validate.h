@@ -175,7 +175,8 @@ inline lr_status check_packed(const Shape& g, const Shape& u, const void* X, con
 struct DecPart {
   int kind, Jw, S, ktps, ntps, js_w, nt_w;
   int ga, gn, gb, gpw;  // kinds 2 and 3
-  int g, nt;            // kind 3: workgroups, column groups per T producer
+  int g, nt;            // kinds 3 and 4: workgroups; kind 3: column groups per T producer
+  int maxc;             // kind 4: contributors per rank slice
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -313,12 +314,46 @@ inline bool decode_split_stream_partition(int64_t K, int64_t r, int64_t N, int b
   return true;
 }
 
+// kind 4 (role-split, flat): for A-heavy shapes that neither split kind
+//   takes (the down projection).  G = budget workgroups each take an equal
+//   share of A's operand blocks in slice-major order (GA <= G, so a share
+//   spans at most two slices) and an equal share of Y's column groups; a
+//   slice's first contributor adds the others' partials (at most
+//   ceil(nkA / max(1, floor(TB / G))) + 1 contributors, TB = GA ceil(K/32)).
+//   Y work as in kind 3.
+inline bool decode_split_flat_partition(int64_t K, int64_t r, int64_t N, int budget, DecPart* out,
+                                        int max_blocks = 16, int64_t max_M = 16) {
+  const int64_t ga = ceil_div(r, 16), gn = ceil_div(N, 16), nkb = ceil_div(r, 32), nka = ceil_div(K, 32);
+  const int64_t per = ceil_div(nkb, 8);
+  if (per > max_blocks || (max_M > 8 && per > 8)) return false;
+  const int64_t tb = ga * nka;
+  if (gn * nkb * 1024 >= ((int64_t)1 << 31) || tb * 1024 >= ((int64_t)1 << 31)) return false;
+  if (ga > budget || budget < 1) return false;
+  const int64_t rlen = tb / budget > 0 ? tb / budget : 1;
+  out->kind = 4;
+  out->Jw = (int)ga;
+  out->S = 1;
+  out->ktps = (int)nka;
+  out->ntps = (int)per;
+  out->js_w = 16;
+  out->nt_w = 16;
+  out->ga = (int)ga;
+  out->gn = (int)gn;
+  out->gb = budget - (int)ga;
+  out->gpw = 0;
+  out->g = budget;
+  out->nt = 0;
+  out->maxc = (int)(ceil_div(nka, rlen) + 1);
+  return true;
+}
+
 // `split`: take a role-split kind when one fits (else the others).
 inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget, bool allow_resident = true,
                                 bool split = false, int64_t max_M = 16) {
   DecPart p{};
   if (split && decode_split_partition(K, r, N, budget, &p, 16, max_M)) return p;
   if (split && decode_split_stream_partition(K, r, N, budget, &p, 16, max_M)) return p;
+  if (split && decode_split_flat_partition(K, r, N, budget, &p, 16, max_M)) return p;
   if (allow_resident && decode_resident_partition(K, r, N, budget, &p)) return p;
   return decode_streaming_partition(K, r, N, budget);
 }

@@ -541,6 +541,42 @@ def test_split_stream_repeated_calls(gpu):
     assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, Ab, Bb), "split_stream after 100 launches")
 
 
+# flat role-split kernel: A-heavy shapes (every workgroup takes a share of A)
+SPLIT_FLAT_GRID = [(1, 14336, 2867, 4096, 1), (4, 14336, 2867, 4096, 4), (2, 12001, 2000, 6000, 2),
+                   (12, 12000, 1800, 9000, 12), (7, 12000, 1800, 9000, 8)]
+
+
+@pytest.mark.parametrize("M,K,r,N,max_M", SPLIT_FLAT_GRID)
+def test_split_flat_decode_shapes(M, K, r, N, max_M):
+    p, lin, _, _ = run_case(M, K, r, N, 7900 + r + N + M, max_M=max_M)
+    assert "kind=split_flat" in lin.describe(), lin.describe()
+
+
+def test_split_flat_repeated_calls(gpu):
+    torch = gpu
+    K, r, N = 12001, 2000, 6000
+    _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 558)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=8, flags=lrl.LR_FLAG_FACTORED)
+    assert "kind=split_flat" in lin.describe(), lin.describe()
+    side = torch.cuda.Stream()
+    for i, M in enumerate([1, 8, 3, 8, 1]):
+        Xb = datagen.normal_bf16((M, K), 1.0, 740 + i)
+        X = to_dev(Xb)
+        if i % 2:
+            with torch.cuda.stream(side):
+                Y = lin(X)
+            side.synchronize()
+        else:
+            Y = lin(X)
+        assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, Ab, Bb), "split_flat call %d M=%d" % (i, M))
+    Xb = datagen.normal_bf16((2, K), 1.0, 797)
+    X = to_dev(Xb)
+    for _ in range(100):
+        Y = lin(X)
+    torch.cuda.synchronize()
+    assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, Ab, Bb), "split_flat after 100 launches")
+
+
 def test_split_decode_repeated_calls(gpu):
     # the generation word advances once per launch: many calls on one
     # handle, M changing, on two streams, each against the oracle

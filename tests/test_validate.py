@@ -63,6 +63,12 @@ int t_split_stream_partition(long long K, long long r, long long N, int budget, 
   out[0] = p.ga; out[1] = p.gn; out[2] = p.gb; out[3] = p.g; out[4] = p.nt; out[5] = p.ntps; out[6] = p.kind;
   return ok ? 1 : 0;
 }
+int t_split_flat_partition(long long K, long long r, long long N, int budget, long long max_M, int* out) {
+  lrv::DecPart p{};
+  const bool ok = lrv::decode_split_flat_partition(K, r, N, budget, &p, 16, max_M);
+  out[0] = p.ga; out[1] = p.gn; out[2] = p.g; out[3] = p.maxc; out[4] = p.ntps; out[5] = p.kind;
+  return ok ? 1 : 0;
+}
 void t_partition2(long long K, long long r, long long N, int budget, int allow_res, int split, long long max_M,
                   int* out) {
   lrv::DecPart p = lrv::decode_partition(K, r, N, budget, allow_res != 0, split != 0, max_M);
@@ -355,12 +361,43 @@ def test_split_stream_partition_layer_shapes(shim):
     assert not _split_stream(shim, 4096, 4100, 4096, budget=200)[0]
 
 
+def _split_flat(shim, K, r, N, budget=256, max_M=1):
+    out = (ctypes.c_int * 6)()
+    ok = shim.t_split_flat_partition(K, r, N, budget, max_M, out)
+    return ok, tuple(out)
+
+
+@pytest.mark.parametrize("K,r,N,budget", [(14336, 2867, 4096, 256), (12001, 2000, 6000, 256), (12000, 1800, 9000, 256),
+                                          (4096, 1637, 4096, 256), (100, 300, 50, 256), (14336, 2867, 4096, 200)])
+def test_split_flat_partition_contributors_fit(shim, K, r, N, budget):
+    ok, (ga, gn, g, maxc, per, kind) = _split_flat(shim, K, r, N, budget=budget)
+    assert ok and kind == 4 and g == budget
+    nka = -(-K // 32)
+    tb = ga * nka
+    # every workgroup's share of the slice-major blocks spans at most two
+    # slices, and every slice has at most maxc contributors
+    lo = [w * tb // g for w in range(g + 1)]
+    for w in range(g):
+        if lo[w] < lo[w + 1]:
+            assert (lo[w + 1] - 1) // nka - lo[w] // nka <= 1
+    for j in range(ga):
+        contrib = [w for w in range(g) if lo[w] < lo[w + 1] and lo[w] < (j + 1) * nka and lo[w + 1] > j * nka]
+        assert 1 <= len(contrib) <= maxc
+        # the owner (first contributor) is the one flat_owner finds for the slice's first block
+        b = j * nka
+        assert contrib[0] == ((b + 1) * g + tb - 1) // tb - 1
+
+
 def test_decode_partition_prefers_register_split_then_streaming_split(shim):
     out = (ctypes.c_int * 7)()
     shim.t_partition2(4096, 1637, 4096, 256, 1, 1, ctypes.c_longlong(16), out)
     assert out[4] == 2
     shim.t_partition2(4096, 2867, 14336, 256, 1, 1, ctypes.c_longlong(1), out)   # B too large for registers: streaming split
     assert out[4] == 3
+    shim.t_partition2(14336, 2867, 4096, 256, 1, 1, ctypes.c_longlong(1), out)   # A-heavy (down): flat split
+    assert out[4] == 4
+    shim.t_partition2(14336, 2867, 4096, 256, 1, 0, ctypes.c_longlong(1), out)   # resident/streaming only
+    assert out[4] in (0, 1)
 
 
 TWO_WAVE, ONE_WAVE = 1, 2
