@@ -480,7 +480,6 @@ __device__ __forceinline__ void t_flat(const SplitArgs& a, int wg, uint32_t epoc
   const int nk = a.nkA;
   const int64_t TB = (int64_t)a.GA * nk;
   const int64_t b_lo = (int64_t)wg * TB / a.G, b_hi = (int64_t)(wg + 1) * TB / a.G;
-  if (b_lo >= b_hi) return;  // no A work (more workgroups than blocks)
   const int j0 = (int)(b_lo / nk);
   const int64_t split_at = (int64_t)(j0 + 1) * nk;  // first block of the second slice
   const int64_t pw = (b_hi - b_lo + kSpWaves - 1) / kSpWaves;
@@ -708,13 +707,14 @@ hipError_t launch_decode_split(const SplitArgs& a, hipStream_t stream) {
     // slices), partial tiles for maxc contributors per slice
     const int per = (a.nkB + kSpWaves - 1) / kSpWaves;
     const int64_t TB = (int64_t)a.GA * a.nkA;
-    if (a.M < 1 || a.M > 16 || a.GA < 1 || a.G < a.GA || TB * 1024 >= ((int64_t)1 << 31) || a.ldp < 32 * a.nkB ||
+    if (a.M < 1 || a.M > 16 || a.GA < 1 || a.G < a.GA || TB < a.G || TB * 1024 >= ((int64_t)1 << 31) || a.ldp < 32 * a.nkB ||
         a.ldp % 8 != 0 || 16 * a.GA > a.ldp || a.nrep < 1 || a.nrep > 64 || a.ldf < a.GA || per > kSplitMaxBlocks ||
         (a.M > 8 && per > 8) || a.maxc < 1 || !a.part || !a.pflags)
       return hipErrorInvalidValue;
     // every slice's contributors fit the partial table: a slice of nkA
-    // blocks meets at most ceil(nkA / R) + 1 ranges of length >= R
-    const int64_t R = TB / a.G > 0 ? TB / a.G : 1;
+    // blocks meets at most ceil(nkA / R) + 1 ranges of length >= R (>= 1:
+    // TB >= G, so no workgroup's share is empty)
+    const int64_t R = TB / a.G;
     if ((a.nkA + R - 1) / R + 1 > a.maxc) return hipErrorInvalidValue;
     const bool xal = (a.K & 7) == 0;
     if (a.M > 8) {

@@ -319,7 +319,8 @@ inline bool decode_split_stream_partition(int64_t K, int64_t r, int64_t N, int b
 //   share of A's operand blocks in slice-major order (GA <= G, so a share
 //   spans at most two slices) and an equal share of Y's column groups; a
 //   slice's first contributor adds the others' partials (at most
-//   ceil(nkA / max(1, floor(TB / G))) + 1 contributors, TB = GA ceil(K/32)).
+//   ceil(nkA / floor(TB / G)) + 1 contributors, TB = GA ceil(K/32) >= G so
+//   that no share is empty).
 //   Y work as in kind 3.
 inline bool decode_split_flat_partition(int64_t K, int64_t r, int64_t N, int budget, DecPart* out,
                                         int max_blocks = 16, int64_t max_M = 16) {
@@ -328,8 +329,10 @@ inline bool decode_split_flat_partition(int64_t K, int64_t r, int64_t N, int bud
   if (per > max_blocks || (max_M > 8 && per > 8)) return false;
   const int64_t tb = ga * nka;
   if (gn * nkb * 1024 >= ((int64_t)1 << 31) || tb * 1024 >= ((int64_t)1 << 31)) return false;
-  if (ga > budget || budget < 1) return false;
-  const int64_t rlen = tb / budget > 0 ? tb / budget : 1;
+  // every workgroup needs a non-empty share: an owner waits for each
+  // workgroup id between it and the slice's last contributor
+  if (ga > budget || budget < 1 || tb < budget) return false;
+  const int64_t rlen = tb / budget;
   out->kind = 4;
   out->Jw = (int)ga;
   out->S = 1;

@@ -368,7 +368,7 @@ def _split_flat(shim, K, r, N, budget=256, max_M=1):
 
 
 @pytest.mark.parametrize("K,r,N,budget", [(14336, 2867, 4096, 256), (12001, 2000, 6000, 256), (12000, 1800, 9000, 256),
-                                          (4096, 1637, 4096, 256), (100, 300, 50, 256), (14336, 2867, 4096, 200)])
+                                          (4096, 1637, 4096, 256), (300, 700, 50, 256), (14336, 2867, 4096, 200)])
 def test_split_flat_partition_contributors_fit(shim, K, r, N, budget):
     ok, (ga, gn, g, maxc, per, kind) = _split_flat(shim, K, r, N, budget=budget)
     assert ok and kind == 4 and g == budget
@@ -377,15 +377,22 @@ def test_split_flat_partition_contributors_fit(shim, K, r, N, budget):
     # every workgroup's share of the slice-major blocks spans at most two
     # slices, and every slice has at most maxc contributors
     lo = [w * tb // g for w in range(g + 1)]
+    assert tb >= g                           # no workgroup's share is empty
     for w in range(g):
-        if lo[w] < lo[w + 1]:
-            assert (lo[w + 1] - 1) // nka - lo[w] // nka <= 1
+        assert lo[w] < lo[w + 1]
+        assert (lo[w + 1] - 1) // nka - lo[w] // nka <= 1
     for j in range(ga):
         contrib = [w for w in range(g) if lo[w] < lo[w + 1] and lo[w] < (j + 1) * nka and lo[w + 1] > j * nka]
         assert 1 <= len(contrib) <= maxc
         # the owner (first contributor) is the one flat_owner finds for the slice's first block
         b = j * nka
         assert contrib[0] == ((b + 1) * g + tb - 1) // tb - 1
+
+
+def test_split_flat_partition_rejects_empty_shares(shim):
+    # fewer A blocks than workgroups: some shares would be empty
+    assert not _split_flat(shim, 100, 300, 50)[0]          # 19 slices x 4 blocks = 76 < 256
+    assert _split_flat(shim, 100, 300, 50, budget=64)[0]   # 76 >= 64
 
 
 def test_decode_partition_prefers_register_split_then_streaming_split(shim):
