@@ -341,8 +341,9 @@ __device__ __forceinline__ void load_group(u32x4_t (&buf)[NB], rsrc_t rB, int64_
 // Y work of the streaming variant: column groups [g0, g1), each over the
 // whole rank, the eight waves splitting its k-steps.  A wave loads its T
 // operands once and keeps them in registers for every group; B blocks
-// stream through two register buffers, both filled (y_prefetch) before T
-// is awaited and each refilled as soon as its MFMAs are issued; each group's eight
+// stream through two register buffers, both filled (y_prefetch, with a
+// third group in LDS) before T is awaited and each refilled as soon as its
+// MFMAs are issued; each group's eight
 // partials are summed in LDS (two buffers, one barrier per group) and
 // stored as bf16.  `writer`: this
 // workgroup waits for every workgroup's count as well and stores the next
@@ -353,8 +354,10 @@ template <int NB>
 struct YBufs {
   u32x4_t b0[NB], b1[NB];
 };
+// A third group (g0 + 2) goes straight into this wave's LDS region `glds`
+// (NB kilobytes per wave).
 template <int NB>
-__device__ __forceinline__ void y_prefetch(const SplitArgs& a, int g0, int g1, YBufs<NB>& yb) {
+__device__ __forceinline__ void y_prefetch(const SplitArgs& a, int g0, int g1, YBufs<NB>& yb, char* glds) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   const int nk = a.nkB;
@@ -363,11 +366,18 @@ __device__ __forceinline__ void y_prefetch(const SplitArgs& a, int g0, int g1, Y
   const rsrc_t rB = make_rsrc(a.Bsw, (int64_t)a.GN * nk * 1024);
   load_group<NB>(yb.b0, rB, g0, nk, s0, s1, g0 < g1, l);
   load_group<NB>(yb.b1, rB, g0 + 1, nk, s0, s1, g0 + 1 < g1, l);
+  const bool ok = g0 + 2 < g1;
+  const uint32_t base = (uint32_t)((int64_t)(g0 + 2) * nk * 1024) + (uint32_t)(l * 16);
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(glds + (w * NB + i) * 1024), 16,
+                                             (ok && s0 + i < s1) ? (int)(base + (uint32_t)((s0 + i) * 1024)) : (int)kSpOut,
+                                             0, 0, 0);
 }
 
 template <int NB, bool TWO>
 __device__ __forceinline__ void y_stream(const SplitArgs& a, int wg, int g0, int g1, uint32_t epoch, bool writer,
-                                         float (*red)[kSpWaves][256], uint64_t* tr, YBufs<NB>& yb) {
+                                         float (*red)[kSpWaves][256], uint64_t* tr, YBufs<NB>& yb, const char* glds) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
@@ -441,15 +451,28 @@ __device__ __forceinline__ void y_stream(const SplitArgs& a, int wg, int g0, int
     }
     buf ^= 1;
   };
+  // the group staged in LDS first (its loads were the last prefetched, so
+  // waiting for everything in flight costs nothing more), then the rest
+  // through the registers: groups g0, g0 + 1, g0 + 3, g0 + 4, ...
+  const bool in_lds = g0 + 2 < g1;
+  if (in_lds) {
+    wait_vmem_all();
+    u32x4_t bl[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) bl[i] = *reinterpret_cast<const u32x4_t*>(glds + (w * NB + i) * 1024 + l * 16);
+    finish(mma(bl), g0 + 2);
+  }
+  const int nreg = g1 - g0 - (in_lds ? 1 : 0);
+  auto gmap = [&](int k) { return g0 + k + (in_lds && k >= 2 ? 1 : 0); };
   // two groups in flight: a buffer is refilled as soon as its MFMAs are
   // issued, before the group's partials are summed
-  for (int g = g0; g < g1; g += 2) {
+  for (int k = 0; k < nreg; k += 2) {
     const f32x4_t acc0 = mma(b0);
-    load_group<NB>(b0, rB, g + 2, nk, s0, s1, g + 2 < g1, l);
-    finish(acc0, g);
+    load_group<NB>(b0, rB, gmap(k + 2), nk, s0, s1, k + 2 < nreg, l);
+    finish(acc0, gmap(k));
     const f32x4_t acc1 = mma(b1);
-    load_group<NB>(b1, rB, g + 3, nk, s0, s1, g + 3 < g1, l);
-    finish(acc1, g + 1);
+    load_group<NB>(b1, rB, gmap(k + 3), nk, s0, s1, k + 3 < nreg, l);
+    finish(acc1, k + 1 < nreg ? gmap(k + 1) : g1);
   }
   SP_TRACE(9);
 }
@@ -620,6 +643,7 @@ int split_blocks_per_wave(const SplitArgs& a) {
 template <int NB, bool XAL, bool TWO>
 __global__ __launch_bounds__(kSpThreads) void lr_decode_splits_kernel(const SplitArgs a) {
   __shared__ float red[2][kSpWaves][256];
+  extern __shared__ __align__(16) char sp_glds[];  // one column group's B blocks, NB KB per wave
   uint64_t tr[16] = {};
   SP_TRACE(15);
   const uint32_t gen = __builtin_amdgcn_readfirstlane(ld_agent_u32(a.ctrl));
@@ -640,8 +664,8 @@ __global__ __launch_bounds__(kSpThreads) void lr_decode_splits_kernel(const Spli
   g1 = min(g1, a.GN);
   YBufs<NB> yb;
   if (wg < a.GA) t_producer<XAL>(a, wg, epoch, red[0], tr);
-  y_prefetch<NB>(a, g0, g1, yb);
-  y_stream<NB, TWO>(a, wg, g0, g1, epoch, wg == a.G - 1, red, tr, yb);
+  y_prefetch<NB>(a, g0, g1, yb, sp_glds);
+  y_stream<NB, TWO>(a, wg, g0, g1, epoch, wg == a.G - 1, red, tr, yb, sp_glds);
 #ifdef LR_DECODE_TRACE
   if (a.trace && threadIdx.x == 0)
     for (int i = 0; i < 16; ++i) a.trace[blockIdx.x * 16 + i] = tr[i];
@@ -652,7 +676,11 @@ __global__ __launch_bounds__(kSpThreads) void lr_decode_splits_kernel(const Spli
 
 template <int NB, bool XAL, bool TWO>
 hipError_t launch_splits_variant(const SplitArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((lr_decode_splits_kernel<NB, XAL, TWO>), dim3((unsigned)a.G), dim3(kSpThreads), 0, stream, a);
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t e = ensure_dynamic_lds((const void*)lr_decode_splits_kernel<NB, XAL, TWO>, kSpWaves * NB * 1024, attr_done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((lr_decode_splits_kernel<NB, XAL, TWO>), dim3((unsigned)a.G), dim3(kSpThreads),
+                     (size_t)kSpWaves * NB * 1024, stream, a);
   return hipGetLastError();
 }
 
@@ -661,6 +689,7 @@ hipError_t launch_splits_variant(const SplitArgs& a, hipStream_t stream) {
 template <int NB, bool XAL, bool TWO>
 __global__ __launch_bounds__(kSpThreads) void lr_decode_splitf_kernel(const SplitArgs a) {
   __shared__ float red[2][kSpWaves][256];
+  extern __shared__ __align__(16) char sp_glds[];  // one column group's B blocks, NB KB per wave
   uint64_t tr[16] = {};
   SP_TRACE(15);
   const uint32_t gen = __builtin_amdgcn_readfirstlane(ld_agent_u32(a.ctrl));
@@ -674,8 +703,8 @@ __global__ __launch_bounds__(kSpThreads) void lr_decode_splitf_kernel(const Spli
   // slice waits for
   t_flat<XAL>(a, wg, epoch, red, tr);
   YBufs<NB> yb;
-  y_prefetch<NB>(a, g0, g1, yb);
-  y_stream<NB, TWO>(a, wg, g0, g1, epoch, wg == a.G - 1, red, tr, yb);
+  y_prefetch<NB>(a, g0, g1, yb, sp_glds);
+  y_stream<NB, TWO>(a, wg, g0, g1, epoch, wg == a.G - 1, red, tr, yb, sp_glds);
 #ifdef LR_DECODE_TRACE
   if (a.trace && threadIdx.x == 0)
     for (int i = 0; i < 16; ++i) a.trace[blockIdx.x * 16 + i] = tr[i];
@@ -686,7 +715,11 @@ __global__ __launch_bounds__(kSpThreads) void lr_decode_splitf_kernel(const Spli
 
 template <int NB, bool XAL, bool TWO>
 hipError_t launch_splitf_variant(const SplitArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((lr_decode_splitf_kernel<NB, XAL, TWO>), dim3((unsigned)a.G), dim3(kSpThreads), 0, stream, a);
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t e = ensure_dynamic_lds((const void*)lr_decode_splitf_kernel<NB, XAL, TWO>, kSpWaves * NB * 1024, attr_done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((lr_decode_splitf_kernel<NB, XAL, TWO>), dim3((unsigned)a.G), dim3(kSpThreads),
+                     (size_t)kSpWaves * NB * 1024, stream, a);
   return hipGetLastError();
 }
 
