@@ -180,12 +180,16 @@ lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const vo
  *   Ys : host array of n device pointers, bf16 [M x N_i] row-major; no
  *        output may overlap X, another output or any handle's factors.
  *   M  : rows, in [0, min max_M]; M == 0 returns LR_OK and launches nothing.
- * Projections that take the decode kernel at this M share decode launches
- * (as many as fit on the device at once); the others share one launch per
+ * Projections that take the dense fallback's decode at this M share one
+ * launch; factorized projections that take a decode kernel share decode
+ * launches where their kernel allows it (the role-split kernels fill the
+ * device and run one launch each); the others share one launch per
  * prefill GEMM, in which every output's tiles are dealt over the CUs
  * together (one launch per weight leading dimension mod 8 where the
  * one-wave kernel is cheaper that way).  Results equal n lr_linear_run
- * calls up to the order of fp32 additions.
+ * calls up to the order of fp32 additions (bitwise for the dense and
+ * role-split decodes, whose per-output work does not depend on the
+ * group).
  * Errors: INVALID_ARG (null array, handle or pointer, n outside
  * [1, LR_GROUP_MAX], repeated handle, unequal K, M out of range,
  * misaligned base, overlapping output), HIP (launch failure).

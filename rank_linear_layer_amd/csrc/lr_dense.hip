@@ -17,8 +17,9 @@
 //    zero.
 //
 //  * lr_dense_decode_kernel (M <= 16, HBM-bound): one workgroup per column
-//    group reads that group's K x 16 slab of Wsw as whole 1 KB blocks (each
-//    wave instruction is one contiguous kilobyte) and multiplies it by X.
+//    group (of every output sharing X in the launch) reads that group's
+//    K x 16 slab of Wsw as whole 1 KB blocks (each wave instruction is one
+//    contiguous kilobyte) and multiplies it by X.
 //    The eight waves split K; their 16 x 16 partials are summed in LDS in
 //    wave order and written as bf16.  No workgroup exchanges anything with
 //    another, so the kernel is one HBM stream plus one LDS reduction.
@@ -65,13 +66,24 @@ __global__ __launch_bounds__(kDnThreads) void lr_dense_decode_kernel(const Dense
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
-  const int64_t g = blockIdx.x;  // column group
+  // (output, column group) of this workgroup: outputs' groups in order
+  int64_t g = blockIdx.x;
+  int oi = 0;
+#pragma unroll
+  for (int i = 0; i < kDenseMaxOut - 1; ++i) {
+    const int64_t ng = (a.o[oi].N + 15) / 16;
+    if (oi + 1 < a.nout && g >= ng) {
+      g -= ng;
+      ++oi;
+    }
+  }
+  const DenseOut& o = a.o[oi];
   const int64_t nk = a.nk;
   // this wave's k-steps [s0, s1)
   const int64_t per = (nk + kDnWaves - 1) / kDnWaves;
   const int64_t s0 = min64(nk, (int64_t)w * per), s1 = min64(nk, s0 + per);
 
-  const rsrc_t rW = make_rsrc(a.Wsw + g * nk * 512, nk * 1024);
+  const rsrc_t rW = make_rsrc(o.Wsw + g * nk * 512, nk * 1024);
   const rsrc_t rX = make_rsrc(a.X, (int64_t)a.M * a.K * 2);
   // A operand of lane l: row m = l % 16 of X (rows >= M read as zero),
   // columns 32 s + 8 (l / 16) .. + 7.  With K a multiple of 8 that is one
@@ -115,7 +127,7 @@ __global__ __launch_bounds__(kDnThreads) void lr_dense_decode_kernel(const Dense
 #pragma unroll
     for (int i = 0; i < kDnWaves; ++i) s += red[i][tid];
     const int64_t n = 16 * g + col;
-    if (row < a.M && n < a.N) a.Y[(int64_t)row * a.N + n] = (uint16_t)f32_to_bf16_rne(s);
+    if (row < a.M && n < o.N) o.Y[(int64_t)row * o.N + n] = (uint16_t)f32_to_bf16_rne(s);
   }
 }
 
@@ -131,9 +143,15 @@ hipError_t launch_dense_swizzle(const uint16_t* W, uint16_t* Wsw, int64_t K, int
 }
 
 hipError_t launch_dense_decode(const DenseArgs& args, hipStream_t stream) {
-  const int64_t ng = (args.N + 15) / 16;
-  if (ng <= 0 || args.M <= 0) return hipSuccess;
-  if (args.M > 16 || args.nk != (args.K + 31) / 32 || ng > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (args.M <= 0) return hipSuccess;
+  if (args.nout < 1 || args.nout > kDenseMaxOut || args.M > 16 || args.nk != (args.K + 31) / 32)
+    return hipErrorInvalidValue;
+  int64_t ng = 0;
+  for (int i = 0; i < args.nout; ++i) {
+    if (args.o[i].N < 1) return hipErrorInvalidValue;
+    ng += (args.o[i].N + 15) / 16;
+  }
+  if (ng > 0x7FFFFFFF) return hipErrorInvalidValue;
   if ((args.K & 7) == 0)
     hipLaunchKernelGGL(lr_dense_decode_kernel<true>, dim3((unsigned)ng), dim3(kDnThreads), 0, stream, args);
   else

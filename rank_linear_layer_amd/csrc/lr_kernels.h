@@ -134,16 +134,24 @@ int split_blocks_per_wave(const SplitArgs& args);
 // Dense fallback (W = A . B precomputed).  Wsw is W in the decode layout:
 // ceil(N/16) column groups x ceil(K/32) k-steps of 1 KB blocks, each block
 // the 16x16x32 MFMA B operand of that group and step (zero past K and N).
+constexpr int kDenseMaxOut = 4;  // projections sharing X in one dense decode launch
+struct DenseOut {
+  const uint16_t* Wsw;  // decode layout of this projection's W
+  uint16_t* Y;          // [M x N] bf16
+  int64_t N;
+};
 struct DenseArgs {
   const uint16_t* X;    // [M x K] bf16
-  const uint16_t* Wsw;  // decode layout of W
-  uint16_t* Y;          // [M x N] bf16
-  int64_t M, K, N;
+  int64_t M, K;
   int64_t nk;           // ceil(K / 32)
+  int nout;             // 1 .. kDenseMaxOut outputs; workgroups are dealt output by output
+  int pad_;
+  DenseOut o[kDenseMaxOut];
 };
 // Wsw from W (row-major [K x N]); Wsw holds ceil(N/16)*ceil(K/32)*512 bf16.
 hipError_t launch_dense_swizzle(const uint16_t* W, uint16_t* Wsw, int64_t K, int64_t N, hipStream_t stream);
-// Y = X . W for M <= 16: one workgroup per 16-column group, no exchange.
+// Y_i = X . W_i for M <= 16: one workgroup per 16-column group of every
+// output, no exchange.
 hipError_t launch_dense_decode(const DenseArgs& args, hipStream_t stream);
 
 // --------------------------------------------------------------- prefill ---

@@ -163,15 +163,22 @@ int num_cus(int device) {
 uint64_t* g_trace = nullptr;
 #endif
 
-lr_status run_dense_decode(const lr_linear* h, uint16_t* Y, const void* X, int64_t M, hipStream_t stream) {
+// Dense-fallback decode of n <= kDenseMaxOut projections sharing X (equal
+// K) in one launch.
+lr_status run_dense_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
+                           hipStream_t stream) {
   lrk::DenseArgs a;
+  memset(&a, 0, sizeof a);
   a.X = (const uint16_t*)X;
-  a.Wsw = h->Wsw;
-  a.Y = Y;
   a.M = M;
-  a.K = h->K;
-  a.N = h->N;
-  a.nk = lrv::ceil_div(h->K, 32);
+  a.K = hs[0]->K;
+  a.nk = lrv::ceil_div(hs[0]->K, 32);
+  a.nout = n;
+  for (int i = 0; i < n; ++i) {
+    a.o[i].Wsw = hs[i]->Wsw;
+    a.o[i].Y = Ys[i];
+    a.o[i].N = hs[i]->N;
+  }
   const hipError_t e = lrk::launch_dense_decode(a, stream);
   if (e != hipSuccess) return hip_fail(e, "dense decode launch");
   return LR_OK;
@@ -458,18 +465,22 @@ lr_status form_dense(lr_linear* h, uint16_t* W) {
   return LR_OK;
 }
 
-static_assert(lrk::kDecMaxProj >= lrv::kMaxGroup && lrk::kPreMaxOut >= lrv::kMaxGroup, "group size");
+static_assert(lrk::kDecMaxProj >= lrv::kMaxGroup && lrk::kPreMaxOut >= lrv::kMaxGroup &&
+                  lrk::kDenseMaxOut >= lrv::kMaxGroup,
+              "group size");
 lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                     hipStream_t stream) {
   const lr_linear* dh[lrk::kDecMaxProj];
   uint16_t* dy[lrk::kDecMaxProj];
   const lr_linear* ph[lrk::kPreMaxOut];
   uint16_t* py[lrk::kPreMaxOut];
-  int nd = 0, np = 0;
+  const lr_linear* xh[lrk::kDenseMaxOut];  // dense-fallback decode: one launch for all of them
+  uint16_t* xy[lrk::kDenseMaxOut];
+  int nd = 0, np = 0, nx = 0;
   for (int i = 0; i < n; ++i) {
     if (use_decode(hs[i], M) && hs[i]->dense) {
-      const lr_status st = run_dense_decode(hs[i], Ys[i], X, M, stream);
-      if (st != LR_OK) return st;
+      xh[nx] = hs[i];
+      xy[nx++] = Ys[i];
     } else if (use_decode(hs[i], M)) {
       dh[nd] = hs[i];
       dy[nd++] = Ys[i];
@@ -477,6 +488,10 @@ lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, cons
       ph[np] = hs[i];
       py[np++] = Ys[i];
     }
+  }
+  if (nx > 0) {
+    const lr_status st = run_dense_decode(xh, xy, nx, X, M, stream);
+    if (st != LR_OK) return st;
   }
   for (int b = 0; b < nd;) {
     if (dh[b]->dp.kind >= 2) {  // one launch per projection: it fills the machine
@@ -727,7 +742,7 @@ lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, v
   if (st != LR_OK || M == 0) return st;
   uint16_t* Ys[1] = {(uint16_t*)Y};
   const lr_linear* hs[1] = {h};
-  if (use_decode(h, M) && h->dense) return run_dense_decode(h, Ys[0], X, M, (hipStream_t)stream);
+  if (use_decode(h, M) && h->dense) return run_dense_decode(hs, Ys, 1, X, M, (hipStream_t)stream);
   if (use_decode(h, M)) return run_decode(hs, Ys, 1, X, M, (hipStream_t)stream);
   return run_prefill(hs, Ys, 1, X, M, (hipStream_t)stream);
 }

@@ -440,6 +440,22 @@ def test_group_mixed_dense_and_factored():
             assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, A, B), "mixed group %s M=%d" % (nm, M))
 
 
+@pytest.mark.parametrize("M,K", [(1, 1001), (7, 512), (16, 2048)])
+def test_group_dense_projections_one_launch(M, K):
+    # several dense-fallback projections sharing X run as one launch; each
+    # output equals its own call bitwise and meets the oracle
+    shapes = [(K, 40, 1000), (K, 8, 33), (K, 64, 4097), (K, 16, 17)]
+    fac = [datagen.factorized_inputs(1, k, r, n, 8100 + i)[1:] for i, (k, r, n) in enumerate(shapes)]
+    Xb = datagen.normal_bf16((M, K), 1.0, 8199)
+    X = to_dev(Xb)
+    lins = [lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M, flags=lrl.LR_FLAG_DENSE) for A, B in fac]
+    Ys = lrl.group_run(lins, X)
+    for i, (lin, Y, (A, B)) in enumerate(zip(lins, Ys, fac)):
+        yb = to_bits(Y)
+        assert np.array_equal(yb, to_bits(lin(X))), "grouped dense output %d differs from its own call" % i
+        assert_parity(yb, oracle.lowrank_bf16(Xb, A, B), "grouped dense %d M=%d K=%d" % (i, M, K))
+
+
 # ----------------------------------------------------- invariants/edges ---
 
 @pytest.mark.parametrize("M,N,flags", [(3, 3999, 0), (33, 3999, 0), (5, 241, lrl.LR_FLAG_FORCE_PREFILL),
