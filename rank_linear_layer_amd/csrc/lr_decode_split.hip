@@ -1,26 +1,38 @@
-// Role-split fused decode kernel (M <= 16): Y = (X . A) . B in one launch,
+// Role-split fused decode kernels (M <= 16): Y = (X . A) . B in one launch,
 // with the compute units divided between the two products instead of every
 // workgroup taking a share of both.
 //
 // Decode reads each weight byte once and is bound by HBM ("LowRankArena
 // ...", "Why theoretical FLOPs saved does not equal faster inference").  A
 // single launch pays its start-up and its end once, but the second product
-// needs all of T = X . A: in the kernels that give every workgroup a rank
-// slice of both factors, the T hand-off sits between the A stream and the
-// B stream's use, and the partial Y sums of the rank slices need a second
-// hand-off.  Here:
+// needs all of T = X . A: in kernels that give every workgroup a rank slice
+// of both factors, the T hand-off sits between the A stream and the B
+// stream's use, and the partial Y sums of the rank slices need a second
+// hand-off.  Here no partial Y ever leaves a workgroup:
 //
-//  * workgroups [0, GA) produce T: producer j owns rank columns
-//    [16 j, 16 j + 16) and computes T[:, those] = X . A[:, those] over all
-//    of K, so a T slice is final where it is computed.  It is published
-//    device-coherent (fp32) with an epoch flag;
-//  * workgroups [GA, GA + GB) produce Y: each owns gpw 16-column groups of N
-//    and computes Y[:, those] = T . B[:, those] over the whole rank, so no
-//    partial Y ever leaves a workgroup.  A Y producer requests its whole B
-//    slab into registers at entry, while the T producers stream A, so both
-//    factors are in flight from the start; it then waits for the GA flags,
-//    reads T and finishes with MFMAs on operands it already holds (T as
-//    bf16 hi + lo: two MFMAs per step, about fp32 accuracy).
+//  * T producers: producer j owns rank columns [16 j, 16 j + 16) and
+//    computes T[:, those] = X . A[:, those] over all of K, so a T slice is
+//    final where it is computed.  It is published as GEMM2's MFMA operand
+//    rows, bf16 hi + lo (about fp32 accuracy; for M <= 8 hi and lo share
+//    one operand, rows 0-7 and 8-15), into nrep replicas with epoch flags,
+//    so that many readers of the same few kilobytes spread over memory
+//    channels;
+//  * Y producers: each owns 16-column groups of N and computes
+//    Y[:, those] = T . B[:, those] over the whole rank.
+//
+// Three variants:
+//  * lr_decode_split_kernel: GA T producers and GB Y producers; a Y
+//    producer requests its whole B slab into registers at entry, while the
+//    T producers stream A, then waits for the flags, stages one replica of
+//    the operand planes in LDS and finishes with one MFMA per step;
+//  * lr_decode_splits_kernel (B too large for registers): every workgroup
+//    computes Y for a balanced share of the column groups, the first GA
+//    after producing their T slice; B streams through registers (and one
+//    group through LDS) while each wave keeps its T operands in registers;
+//  * lr_decode_splitf_kernel (A-heavy shapes): every workgroup takes an
+//    equal share of A's blocks in slice-major order, a slice's first
+//    contributor adds the others' fp32 partial tiles and publishes the
+//    planes; then Y as in the streaming variant.
 //
 // Both factors are kept in the MFMA operand block layout of the dense path
 // (copied at create): 16 columns x 32 rows per 1 KB block, lane l holding
@@ -29,15 +41,18 @@
 // no row alignment reaches the kernel: a misaligned rank or width costs
 // only its zero padding.
 //
-// T producers have lower workgroup ids and never wait, so the launch
-// completes even when not every workgroup is resident at once.  The epoch
-// of a launch is the generation word ctrl[0] plus one, read by every
-// workgroup at entry.  Each Y producer counts itself in ctrl[1] once it has
-// read the generation; Y producer 0 waits for that count as well as for the
-// T flags (each stored after its producer read the generation), then
-// clears the count and stores the epoch as the next generation.  No
-// argument changes between launches and nothing is cleared from the host,
-// so a captured graph can replay it.
+// The epoch of a launch is the generation word ctrl[0] plus one, read by
+// every workgroup at entry.  Workgroups count themselves in ctrl[1] once
+// they have read the generation; one workgroup (Y producer 0, or the last
+// workgroup of the streaming variants) waits for that count and for every
+// T flag (each stored after its producer read the generation), then clears
+// the count and stores the epoch as the next generation.  No argument
+// changes between launches and nothing is cleared from the host, so a
+// captured graph can replay a launch.  In the first variant T producers
+// have the lowest ids and never wait, so it completes even when not every
+// workgroup is resident at once; the other two assume all G workgroups
+// are (one per CU), and every spin gives up after kSpSpinLimit rounds,
+// raising ctrl[2].
 #include "lr_device.h"
 #include "lr_kernels.h"
 
@@ -338,24 +353,14 @@ __device__ __forceinline__ void load_group(u32x4_t (&buf)[NB], rsrc_t rB, int64_
     buf[i] = buf_load16(rB, (ok && s0 + i < s1) ? base + (uint32_t)((s0 + i) * 1024) : kSpOut);
 }
 
-// Y work of the streaming variant: column groups [g0, g1), each over the
-// whole rank, the eight waves splitting its k-steps.  A wave loads its T
-// operands once and keeps them in registers for every group; B blocks
-// stream through two register buffers, both filled (y_prefetch, with a
-// third group in LDS) before T is awaited and each refilled as soon as its
-// MFMAs are issued; each group's eight
-// partials are summed in LDS (two buffers, one barrier per group) and
-// stored as bf16.  `writer`: this
-// workgroup waits for every workgroup's count as well and stores the next
-// generation.
 // The first two column groups' B blocks of this wave, requested ahead of
-// the rest of the Y work (y_stream refills the same buffers).
+// the rest of the Y work (y_stream refills the same buffers); a third
+// group (g0 + 2) goes straight into this wave's LDS region `glds` (NB
+// kilobytes per wave).
 template <int NB>
 struct YBufs {
   u32x4_t b0[NB], b1[NB];
 };
-// A third group (g0 + 2) goes straight into this wave's LDS region `glds`
-// (NB kilobytes per wave).
 template <int NB>
 __device__ __forceinline__ void y_prefetch(const SplitArgs& a, int g0, int g1, YBufs<NB>& yb, char* glds) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -375,6 +380,14 @@ __device__ __forceinline__ void y_prefetch(const SplitArgs& a, int g0, int g1, Y
                                              0, 0, 0);
 }
 
+// Y work of the streaming variants: column groups [g0, g1), each over the
+// whole rank, the eight waves splitting its k-steps.  A wave loads its T
+// operands once and keeps them in registers for every group.  The group
+// staged in LDS is multiplied first, then the others stream through the
+// two register buffers, each refilled as soon as its MFMAs are issued;
+// each group's eight partials are summed in LDS (two buffers, one barrier
+// per group) and stored as bf16.  `writer`: this workgroup also waits for
+// every workgroup's count and stores the next generation.
 template <int NB, bool TWO>
 __device__ __forceinline__ void y_stream(const SplitArgs& a, int wg, int g0, int g1, uint32_t epoch, bool writer,
                                          float (*red)[kSpWaves][256], uint64_t* tr, YBufs<NB>& yb, const char* glds) {
