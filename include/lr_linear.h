@@ -104,11 +104,12 @@ typedef struct lr_linear lr_linear;
  *   max_M  : largest M that lr_linear_run will be called with (>= 0).
  *   flags  : LR_FLAG_* bits.
  * Chooses the kernels' partitioning for this shape and allocates the
- * workspace on the current HIP device.  Decode (M <= 16) takes the
- * role-split kernel where its plan fits (T produced by ceil(r/16)
- * workgroups, Y by the rest, all resident at once; B's blocks for one
- * workgroup in registers), unless LR_FLAG_DECODE_RESIDENT or
- * LR_FLAG_DECODE_STREAMING is set; create then copies A and B into its
+ * workspace on the current HIP device.  Decode (M <= 16) takes a
+ * role-split kernel where a plan fits (T produced in 16-column rank slices
+ * and handed to the workgroups that produce Y, which never exchange
+ * partial Y; variants for B held in registers, B streamed, and A spread
+ * over every workgroup), unless LR_FLAG_DECODE_RESIDENT or
+ * LR_FLAG_DECODE_STREAMING is set; create then copies A and B into their
  * operand layout on the null stream and waits.  Otherwise create launches
  * no kernel, except for the dense fallback: when LR_FLAG_DENSE is set, or (without LR_FLAG_FACTORED)
  * when the factors hold at least 95% of the bytes of the K x N matrix they
