@@ -735,6 +735,49 @@ def test_layer_graph_replay(gpu, M, flags):
     del g
 
 
+@pytest.mark.parametrize("M,K,r,N,kind", [(1, 4096, 2867, 14336, "split_stream"), (3, 14336, 2867, 4096, "split_flat"),
+                                          (8, 4096, 1637, 4096, "split")])
+def test_split_variants_graph_replay(gpu, M, K, r, N, kind):
+    # each role-split variant captured with two launches on one handle (so
+    # the generation word advances twice per replay), replayed with eager
+    # launches of the same handle in between; every replay bitwise equal to
+    # the eager result, the last one against the oracle
+    torch = gpu
+    banner("graph replay %s M=%d K=%d r=%d N=%d" % (kind, M, K, r, N))
+    _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 8300 + r)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=lrl.LR_FLAG_FACTORED)
+    assert "kind=%s " % kind in lin.describe(), lin.describe()
+    X1 = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    X2 = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    Y1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    Y2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def load(seed):
+        X1.copy_(torch.from_numpy(datagen.normal_bf16((M, K), 1.0, seed).view(np.int16)).view(torch.bfloat16))
+        X2.copy_(torch.from_numpy(datagen.normal_bf16((M, K), 1.0, seed + 1).view(np.int16)).view(torch.bfloat16))
+
+    def step():
+        lin(X1, out=Y1)
+        lin(X2, out=Y2)
+
+    load(5)
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep, seed in enumerate([5, 17, 29]):
+        load(seed)
+        step()
+        torch.cuda.synchronize()
+        ref = (to_bits(Y1).copy(), to_bits(Y2).copy())
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(Y1), ref[0]) and np.array_equal(to_bits(Y2), ref[1]), "replay %d" % rep
+    assert_parity(to_bits(Y2), oracle.lowrank_bf16(datagen.normal_bf16((M, K), 1.0, 30), Ab, Bb), "graph %s" % kind)
+    del g
+
+
 def test_handle_released_during_capture(gpu):
     # a handle freed while a graph is being captured (a garbage-collected
     # handle of earlier work) must not invalidate that capture
