@@ -509,7 +509,8 @@ def test_repeated_calls_new_inputs_and_streams(gpu):
 
 # role-split decode kernel: shapes whose plan fits it (K of any residue)
 SPLIT_GRID = [(1, 8, 1, 1), (16, 33, 5, 7), (5, 100, 17, 121), (3, 257, 241, 3999), (8, 4096, 1637, 4096),
-              (16, 4100, 1000, 4096), (2, 2000, 300, 250), (7, 4096, 2048, 2048), (1, 4096, 1100, 3999)]
+              (16, 4100, 1000, 4096), (2, 2000, 300, 250), (7, 4096, 2048, 2048), (1, 4096, 1100, 3999),
+              (16, 1, 1, 1), (3, 7, 33, 16), (9, 3, 2, 5000)]
 
 
 @pytest.mark.parametrize("M,K,r,N", SPLIT_GRID)
@@ -521,7 +522,7 @@ def test_split_decode_shapes(M, K, r, N):
 # streaming-Y role-split kernel: B too large for the Y producers' registers
 SPLIT_STREAM_GRID = [(1, 4096, 2867, 14336, 1), (8, 4096, 2867, 14336, 8), (4, 2048, 2867, 9000, 4),
                      (3, 1001, 2500, 9001, 3), (12, 2048, 2000, 12000, 12), (9, 2048, 2000, 12000, 16),
-                     (1, 512, 4096, 64, 1), (2, 300, 1500, 20000, 2)]
+                     (1, 512, 4096, 64, 1), (2, 300, 1500, 20000, 2), (1, 2, 4096, 8, 1)]
 
 
 @pytest.mark.parametrize("M,K,r,N,max_M", SPLIT_STREAM_GRID)
