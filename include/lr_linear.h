@@ -4,12 +4,12 @@
  * The operation
  * -------------
  * A linear layer Y = X.W whose weight has been replaced by two factors,
- * W ~ A.B, with the rank r as the inner dimension of two smaller GEMMs
- * ("Why Smaller Is Slower? Dimensional Misalignment in Compressed LLMs",
- * section 1 and Figure 1).  The factor pair keeps the layer's input/output
- * interface: y = Wx becomes y = A(Bx) in the column-vector orientation of
- * "LowRankArena: What Happens When You Force SVD Compression Papers to Play
- * by the Same Rules" (Prerequisites, Figure A).  Here, row-major:
+ * W ~ A.B, so that one large product becomes two thin ones that meet at the
+ * rank r ("Why Smaller Is Slower? Dimensional Misalignment in Compressed
+ * LLMs", section 1 and Figure 1).  The factor pair keeps the layer's
+ * input/output interface: in the column-vector orientation of "LowRankArena:
+ * What Happens When You Force SVD Compression Papers to Play by the Same
+ * Rules" (Prerequisites, Figure A) y = Wx becomes y = A(Bx).  Here, row-major:
  *
  *     X[M x K] . A[K x r] = T[M x r],     T . B[r x N] = Y[M x N]
  *
@@ -28,17 +28,23 @@
  *
  * Ownership
  * ---------
- * A and B are BORROWED by the handle: the caller keeps them alive and
- * unchanged until lr_linear_destroy.  X and Y are borrowed for the duration
- * of the enqueued work.  The handle OWNS a device workspace (allocated at
- * create, sized for max_M) that holds split-K partial sums, for M > 16 the
- * bf16 intermediate T, and the copies that some kernels read instead of A
- * and B: the dense fallback's W, and for the role-split decode kernel A
- * and B in its operand block layout (both made at create, so decode does
- * not see later changes to A and B; prefill reads A and B themselves);
- * lr_linear_destroy frees it.  Because the workspace
- * is shared by every call on a handle, a handle must not be used by two
- * streams at the same time.
+ * A and B are BORROWED by the handle: the caller keeps them alive until
+ * lr_linear_destroy, and every call reads them where they are (decode and
+ * prefill alike), so an update of A or B in place between calls is seen by
+ * the next call.  X and Y are borrowed for the duration of the enqueued
+ * work.  The handle OWNS a device workspace (allocated at create, sized for
+ * max_M) that holds the exchange tables of the decode kernels, split-K
+ * partial sums, and for M > 16 the bf16 intermediate T; and a 64-byte
+ * pinned host word in which a decode kernel reports a wait that gave up
+ * (see Errors).  Two opt-in modes also keep a derived copy of the factors
+ * in the workspace, made at create and not refreshed afterwards: the dense
+ * fallback's W = A.B (LR_FLAG_DENSE, or automatic, see lr_linear_create),
+ * and LR_FLAG_DECODE_SPLIT, whose decode kernel reads A and B from a copy
+ * in its 1 KB operand block layout (2 (ceil(r/16) ceil(K/32) +
+ * ceil(N/16) ceil(r/32)) x 512 bytes, about the size of A and B).
+ * lr_linear_destroy frees all of it.  Because the workspace is shared by
+ * every call on a handle, a handle must not be used by two streams at the
+ * same time.
  *
  * Semantics
  * ---------
@@ -52,7 +58,15 @@
  * ------
  * Functions return an lr_status and never abort, print or throw across the
  * ABI.  lr_last_error() returns a thread-local detail string for the most
- * recent failure on the calling thread.
+ * recent failure on the calling thread.  The decode kernels divide one
+ * launch among one workgroup per compute unit that wait on one another's
+ * partial results, which needs every workgroup of the launch resident at
+ * once; create checks that the kernel's occupancy allows it, but another
+ * kernel running concurrently on the same GPU can hold compute units.  A
+ * wait then gives up after a bounded number of polls (seconds) instead of
+ * hanging, the launch ends normally with an invalid output, and the handle's
+ * next lr_linear_run / lr_group_run / lr_mlp_packed_run, or
+ * lr_linear_status, returns LR_ERR_HIP (once).
  */
 #ifndef LR_LINEAR_H
 #define LR_LINEAR_H
@@ -88,10 +102,15 @@ typedef struct lr_linear lr_linear;
                                         same leading dimension mod 8 for both factors of a pair */
 #define LR_FLAG_DENSE    32u  /* dense fallback: form W = A.B (bf16) at create and run Y = X.W */
 #define LR_FLAG_FACTORED 64u  /* never take the dense fallback */
-#define LR_FLAG_DECODE_SPLIT 128u  /* decode with the role-split kernel where its plan fits (the
-                                      default already; kept for callers that name it) */
-#define LR_FLAG_DECODE_RESIDENT 256u  /* never the role-split kernel: the LDS-resident kernel where
-                                         it applies, else the register-streaming one */
+#define LR_FLAG_DECODE_SPLIT 128u  /* decode with the role-split kernel where its plan fits; it
+                                      reads a copy of A and B in its operand block layout, made at
+                                      create (see Ownership) */
+#define LR_FLAG_DECODE_RESIDENT 256u  /* decode with the LDS-resident kernel where it applies, else
+                                         the register-streaming one */
+#define LR_FLAG_TEST_STALL (1u << 30) /* for testing the error path only: in every decode launch one
+                                         workgroup never publishes its partial result and waits give
+                                         up after 2048 polls, so each decode call's output is invalid
+                                         and the next call reports LR_ERR_HIP */
 
 /* Largest M that the fused decode kernel takes (more rows use prefill). */
 #define LR_DECODE_MAX_M 16
@@ -104,24 +123,29 @@ typedef struct lr_linear lr_linear;
  *   max_M  : largest M that lr_linear_run will be called with (>= 0).
  *   flags  : LR_FLAG_* bits.
  * Chooses the kernels' partitioning for this shape and allocates the
- * workspace on the current HIP device.  Decode (M <= 16) takes a
- * role-split kernel where a plan fits (T produced in 16-column rank slices
- * and handed to the workgroups that produce Y, which never exchange
- * partial Y; variants for B held in registers, B streamed, and A spread
- * over every workgroup), unless LR_FLAG_DECODE_RESIDENT or
- * LR_FLAG_DECODE_STREAMING is set; create then copies A and B into their
- * operand layout on the null stream and waits.  Otherwise create launches
- * no kernel, except for the dense fallback: when LR_FLAG_DENSE is set, or (without LR_FLAG_FACTORED)
- * when the factors hold at least 95% of the bytes of the K x N matrix they
- * replace, i.e. 100 r (K + N) >= 95 K N ("LowRankArena: What Happens When
- * You Force SVD Compression Papers to Play by the Same Rules", Q3: a dense
- * GEMM where the retained rank saves no memory bandwidth), create forms
- * W = A.B in bf16 (fp32 accumulation) with the prefill GEMM on the null
- * stream, plus W in the decode kernel's operand layout, and waits for them.
- * Runs then compute Y = X.W: decode with one workgroup per 16 columns and
- * no exchange between workgroups, prefill with one GEMM.  W is a snapshot:
- * A and B are not read again.  The workspace then holds W (K x N bf16) when
- * max_M > 16 and its decode layout when decode applies.
+ * workspace on the current HIP device.  Decode (M <= 16) takes the
+ * XCD-sliced kernel: one workgroup per compute unit, each streaming an equal
+ * share of A and of B straight from the caller's row-major factors; XCD x
+ * computes T for rank rows [x r / 8, (x + 1) r / 8) (its workgroups split K
+ * and the range, then add their partials through the XCD's L2) and the
+ * partial Y of those rows, and the eight partials of Y are added across
+ * XCDs.  LR_FLAG_DECODE_RESIDENT, _STREAMING and _SPLIT select the older
+ * decode kernels instead (the split one copies A and B at create, see
+ * Ownership); shapes the XCD-sliced plan cannot take (a sub-range above 128
+ * columns, a column slab above 1024, a device whose CU count is not a
+ * multiple of 8) take the LDS-resident or streaming kernel.  Create launches
+ * no kernel, except for LR_FLAG_DECODE_SPLIT and for the dense fallback:
+ * when LR_FLAG_DENSE is set, or (without LR_FLAG_FACTORED) when the factors
+ * hold at least 95% of the bytes of the K x N matrix they replace, i.e.
+ * 100 r (K + N) >= 95 K N ("LowRankArena: What Happens When You Force SVD
+ * Compression Papers to Play by the Same Rules", Q3: a dense GEMM where the
+ * retained rank saves no memory bandwidth), create forms W = A.B in bf16
+ * (fp32 accumulation) with the prefill GEMM on the null stream, plus W in
+ * the dense decode kernel's operand layout, and waits for them.  Runs then
+ * compute Y = X.W: decode with one workgroup per 16 columns and no exchange
+ * between workgroups, prefill with one GEMM.  W is a snapshot: A and B are
+ * not read again.  The workspace then holds W (K x N bf16) when max_M > 16
+ * and its decode layout when decode applies.
  * Errors: INVALID_ARG (null/size/alignment, exclusive flags together),
  * UNSUPPORTED (no gfx950 device, unknown flags, FORCE_DECODE with
  * max_M > 16, DENSE with a W above 2 GiB), OUT_OF_MEMORY, HIP.
@@ -145,7 +169,9 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N,
  * capturing (the first call sets kernel attributes), and do not replay a
  * graph while another call on the same handle is in flight.
  * Errors: INVALID_ARG (null handle/pointers, M out of range, misaligned
- * base, Y overlapping X/A/B), HIP (launch failure).
+ * base, Y overlapping X/A/B), HIP (launch failure; or a wait of an earlier
+ * decode launch on this handle gave up, see Errors above: nothing is
+ * launched and the report is cleared).
  */
 lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, void* stream);
 
@@ -197,6 +223,15 @@ lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const vo
  */
 lr_status lr_group_run(const lr_linear* const* hs, int n, const void* X, void* const* Ys,
                        int64_t M, void* stream);
+
+/*
+ * lr_linear_status -- LR_ERR_HIP (once, with a detail in lr_last_error) if a
+ * decode launch of this handle gave up waiting for another of its
+ * workgroups since the last report (see Errors), else LR_OK.  Reads a pinned
+ * host word and enqueues nothing; synchronize the stream first to include
+ * the launches still in flight.  INVALID_ARG for a NULL handle.
+ */
+lr_status lr_linear_status(const lr_linear* h);
 
 /* lr_linear_destroy -- free the workspace and the handle.  NULL is a no-op.
  * The caller must ensure no enqueued work still uses the handle. */

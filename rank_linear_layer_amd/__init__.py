@@ -36,6 +36,7 @@ LR_FLAG_DENSE = 32
 LR_FLAG_FACTORED = 64
 LR_FLAG_DECODE_SPLIT = 128
 LR_FLAG_DECODE_RESIDENT = 256
+LR_FLAG_TEST_STALL = 1 << 30
 LR_DECODE_MAX_M = 16
 LR_GROUP_MAX = 4
 
@@ -49,6 +50,7 @@ EXPORTED_SYMBOLS = (
     "lr_last_error",
     "lr_linear_describe",
     "lr_linear_workspace_bytes",
+    "lr_linear_status",
     "lr_gac_select",
 )
 
@@ -96,6 +98,8 @@ def load_library(path: str | None = None):
         lib.lr_linear_describe.restype = ctypes.c_int
         lib.lr_linear_workspace_bytes.argtypes = [vp]
         lib.lr_linear_workspace_bytes.restype = i64
+        lib.lr_linear_status.argtypes = [vp]
+        lib.lr_linear_status.restype = ctypes.c_int
         P = ctypes.POINTER
         lib.lr_gac_select.argtypes = [ctypes.c_int, P(ctypes.c_double), P(i64), P(ctypes.c_double),
                                       P(ctypes.c_int), P(i64), i64, i64, P(i64), P(ctypes.c_double)]
@@ -170,6 +174,12 @@ class LowRankLinear:
 
     def workspace_bytes(self) -> int:
         return int(self._lib.lr_linear_workspace_bytes(self._h))
+
+    def status(self) -> int:
+        """lr_linear_status: LR_ERR_HIP (reported once) if a decode launch of
+        this handle gave up waiting for another of its workgroups, else
+        LR_OK.  Synchronize the stream first to include launches in flight."""
+        return int(self._lib.lr_linear_status(self._h))
 
     def __call__(self, X, out=None, stream=None):
         import torch

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "liblr_linear.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["lr_linear.cpp", "lr_decode.hip", "lr_decode_res.hip", "lr_prefill.hip", "lr_prefill_w4.hip", "lr_dense.hip",
-           "lr_decode_split.hip",
+           "lr_decode_split.hip", "lr_decode_xcd.hip",
            "lr_gac.cpp"]
 ARCH = "gfx950"
 

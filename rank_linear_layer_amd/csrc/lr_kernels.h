@@ -130,6 +130,50 @@ hipError_t launch_decode_split(const SplitArgs& args, hipStream_t stream);
 // B blocks per wave of a Y producer for this plan (<= kSplitMaxBlocks to launch).
 int split_blocks_per_wave(const SplitArgs& args);
 
+// XCD-sliced decode kernel (lr_decode_xcd.hip): one workgroup per compute
+// unit; XCD x owns rank rows [x r / 8, (x + 1) r / 8) of each projection,
+// and projection p's workgroups are local indices [p0, p0 + pn) of every
+// XCD (workgroup g runs on XCD g % 8, local index g / 8).  A and B are read
+// in place.  Exchange tables hold fp32 columns of 4 mq rows (mq =
+// ceil(M / 4)), column-major.
+constexpr int kXcdMaxProj = 4;          // projections sharing X in one launch
+constexpr int kXcdMaxLds = 160 * 1024;  // dynamic LDS limit of the kernel
+constexpr int kXcdTilesA = 16;          // 16-column GEMM1 tiles per rank sub-range (256 columns)
+constexpr int kXcdTilesB = 16;          // 16-column GEMM2 tiles per column chunk (256 columns)
+struct XcdProj {
+  const uint16_t* A;  // [K x r] bf16 row-major
+  const uint16_t* B;  // [r x N]
+  uint16_t* Y;        // [M x N]
+  uint32_t* ctrl;     // [0] generation, [1] workgroups finished, [2] a wait timed out
+  uint32_t* err;      // device address of the host-visible timeout word (may be null)
+  uint32_t* flags;    // [3][8 pn] epoch stamps: partial T stored, T columns reduced, partial Y stored
+  float* tpart;       // [8 (pa / rs)][ldtp][4 mq] partial T of each (XCD, K-slab) over the XCD's rank range
+  float* tfin;        // [8][ldtp][4 mq] T of each XCD's rank range
+  float* ypart;       // [8 (pn - pa)][ws][4 mq] partial Y of each B workgroup's column slab
+  int r, N;
+  int p0, pn;         // local workgroup indices [p0, p0 + pn) of this projection on every XCD
+  int pa, rs;         // the first pa of them stream A: (pa / rs) K-slabs x rs rank sub-ranges;
+                      // the other pn - pa stream B, one column slab each
+  int nc;             // column chunks of a B slab (1, 2, 4 or 8; wave w takes chunk w % nc)
+  int cpr_a, cpr_b;   // 16-byte chunks per LDS row of an A piece / of a B chunk (even)
+  int da, db;         // k-steps in flight per wave of an A / a B workgroup
+  int ldtp, ws;       // rank range (>= ceil(r/8)) and slab (>= ceil(N/(pn - pa))) lengths of the tables
+  int withhold;       // test hook: this workgroup never stamps its partial-T flag (-1: none)
+};
+struct XcdArgs {
+  const uint16_t* X;  // [M x K] bf16
+  int M, K;
+  int nproj, grid;    // grid = 8 x (sum of pn)
+  int xcd_local;      // 1: the T exchange runs through each XCD's L2 (workgroup placement verified)
+  uint32_t spin_limit;
+  uint64_t* trace;    // phase timestamps (builds with LR_DECODE_TRACE only)
+  XcdProj p[kXcdMaxProj];
+};
+hipError_t launch_decode_xcd(const XcdArgs& args, int lds_bytes, hipStream_t stream);
+// Workgroups of the XCD-sliced kernel a compute unit holds at once with
+// lds_bytes of dynamic LDS (0 on error).
+int decode_xcd_blocks_per_cu(int lds_bytes);
+
 // ----------------------------------------------------------------- dense ---
 // Dense fallback (W = A . B precomputed).  Wsw is W in the decode layout:
 // ceil(N/16) column groups x ceil(K/32) k-steps of 1 KB blocks, each block

@@ -98,6 +98,22 @@ struct lr_linear {
   int nrep, ldf;       // replicas of T and of its flags; flag words per replica
   float* fpart;        // flat variant: partial tiles [GA][maxc] of 16 x 16 fp32
   uint32_t* pflags;    // flat variant: their flags
+  // XCD-sliced decode (dp.kind 5, the default): plans for xcd_P, xcd_P / 2
+  // and xcd_P / 4 workgroups per XCD (alone in a launch, or one of two, or
+  // of three or four projections sharing X), and their exchange tables
+  int xcd_P;
+  bool xcd_ok[3];
+  lrv::XcdPlan xp[3];
+  uint32_t* xflags;  // [3][8 xcd_P] epoch stamps
+  float* xtpart;
+  float* xtfin;
+  float* xypart;
+  uint32_t spin_limit;  // polls before a cross-workgroup wait gives up
+  int withhold;         // LR_FLAG_TEST_STALL: workgroup that never publishes its partial T (-1: none)
+  // pinned host word that a decode kernel raises when one of its waits gave
+  // up; the next call on the handle (or lr_linear_status) reports it
+  uint32_t* err_host;
+  uint32_t* err_dev;
 };
 
 namespace {
@@ -138,6 +154,13 @@ lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
   return p;
 }
 
+// Frees what a partly built handle holds (create's error paths).
+void discard(lr_linear* h) {
+  if (h->err_host) (void)hipHostFree(h->err_host);
+  if (h->ws) (void)hipFree(h->ws);
+  delete h;
+}
+
 // Whether workgroups are dealt to XCDs round-robin (checked once per device).
 bool xcd_map_ok(int device) {
   static std::mutex mu;
@@ -161,6 +184,7 @@ int num_cus(int device) {
 
 #ifdef LR_DECODE_TRACE
 uint64_t* g_trace = nullptr;
+bool g_xcd_coherent = false;  // trace builds: run the XCD-local exchange device-coherent
 #endif
 
 // Dense-fallback decode of n <= kDenseMaxOut projections sharing X (equal
@@ -223,8 +247,109 @@ lr_status run_split_decode(const lr_linear* h, uint16_t* Y, const void* X, int64
   return LR_OK;
 }
 
+// A decode kernel of an earlier call gave up waiting for another workgroup
+// (not every workgroup was resident, e.g. another kernel held compute
+// units): that call's output is invalid.  Reported once, then cleared.
+lr_status take_stall(const lr_linear* h) {
+  if (!h->err_host) return LR_OK;
+  if (__atomic_load_n(h->err_host, __ATOMIC_ACQUIRE) == 0) return LR_OK;
+  __atomic_store_n(h->err_host, 0u, __ATOMIC_RELEASE);
+  return fail(LR_ERR_HIP,
+              "an earlier decode call on this handle gave up waiting for another workgroup (the launch's "
+              "workgroups were not all resident at once); its output is invalid");
+}
+
+// Plan index for pn = xcd_P >> v.
+int xcd_share(int n, int rank_by_bytes) {
+  if (n == 1) return 0;
+  if (n == 2) return 1;
+  if (n == 3) return rank_by_bytes == 0 ? 1 : 2;
+  return 2;
+}
+
+// XCD-sliced decode of n <= kXcdMaxProj kind-5 handles sharing X in one
+// launch: projection i takes xcd_P >> v_i workgroups per XCD (all of them
+// alone; half each for two; half for the largest of three and a quarter for
+// the others; a quarter each for four).  Returns LR_ERR_UNSUPPORTED (with no
+// launch) when some handle has no plan for its share.
+lr_status run_xcd_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
+                         hipStream_t stream) {
+  int rank[lrk::kXcdMaxProj] = {0, 0, 0, 0};
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) {
+      const int64_t bi = hs[i]->r * (hs[i]->K + hs[i]->N), bj = hs[j]->r * (hs[j]->K + hs[j]->N);
+      if (bj > bi || (bj == bi && j < i)) ++rank[i];
+    }
+  lrk::XcdArgs a;
+  memset(&a, 0, sizeof a);
+  a.X = (const uint16_t*)X;
+  a.M = (int)M;
+  a.K = (int)hs[0]->K;
+  a.nproj = n;
+  a.xcd_local = 1;
+  a.spin_limit = hs[0]->spin_limit;
+#ifdef LR_DECODE_TRACE
+  a.trace = g_trace;
+#endif
+  int p0 = 0;
+#ifdef LR_DECODE_TRACE
+  const bool force_coherent = g_xcd_coherent;
+#else
+  const bool force_coherent = false;
+#endif
+  int64_t lds = 0;
+  for (int i = 0; i < n; ++i) {
+    const lr_linear* h = hs[i];
+    const int v = xcd_share(n, rank[i]);
+    if (h->dp.kind != 5 || !h->xcd_ok[v] || h->xcd_P != hs[0]->xcd_P) return LR_ERR_UNSUPPORTED;
+    const lrv::XcdPlan& pl = h->xp[v];
+    lrk::XcdProj& P = a.p[i];
+    P.A = h->A;
+    P.B = h->B;
+    P.Y = Ys[i];
+    P.ctrl = h->ctrl;
+    P.err = h->err_dev;
+    P.flags = h->xflags;
+    P.tpart = h->xtpart;
+    P.tfin = h->xtfin;
+    P.ypart = h->xypart;
+    P.r = (int)h->r;
+    P.N = (int)h->N;
+    P.p0 = p0;
+    P.pn = pl.pn;
+    P.pa = pl.pa;
+    P.rs = pl.rs;
+    P.nc = pl.nc;
+    P.cpr_a = pl.cpr_a;
+    P.cpr_b = pl.cpr_b;
+    P.da = pl.da;
+    P.db = pl.db;
+    P.ldtp = pl.ldtp;
+    P.ws = pl.ws;
+    P.withhold = h->withhold;
+    p0 += pl.pn;
+    lds = lds > pl.lds ? lds : pl.lds;
+    a.xcd_local = a.xcd_local && h->xcd_local;
+    a.spin_limit = a.spin_limit < h->spin_limit ? a.spin_limit : h->spin_limit;
+  }
+  if (p0 != hs[0]->xcd_P) return LR_ERR_UNSUPPORTED;
+  if (force_coherent) a.xcd_local = 0;
+  a.grid = 8 * p0;
+  const hipError_t e = lrk::launch_decode_xcd(a, (int)lds, stream);
+  if (e != hipSuccess) return hip_fail(e, "xcd decode launch");
+  return LR_OK;
+}
+
 lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
                      hipStream_t stream) {
+  if (hs[0]->dp.kind == 5) {
+    for (int i = 0; i < n; ++i) {
+      const lr_status st = run_xcd_decode(hs + i, Ys + i, 1, X, M, stream);
+      if (st == LR_ERR_UNSUPPORTED) return fail(st, "no XCD-sliced decode plan for this handle");
+      if (st != LR_OK) return st;
+    }
+    return LR_OK;
+  }
   if (hs[0]->dp.kind >= 2) {
     for (int i = 0; i < n; ++i) {
       const lr_status st = run_split_decode(hs[i], Ys[i], X, M, stream);
@@ -493,6 +618,33 @@ lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, cons
     const lr_status st = run_dense_decode(xh, xy, nx, X, M, stream);
     if (st != LR_OK) return st;
   }
+  {
+    // XCD-sliced handles share one launch where every one has a plan for its
+    // share of the workgroups; otherwise each runs alone
+    const lr_linear* xh5[lrk::kXcdMaxProj];
+    uint16_t* xy5[lrk::kXcdMaxProj];
+    int n5 = 0, rest = 0;
+    for (int i = 0; i < nd; ++i) {
+      if (dh[i]->dp.kind == 5) {
+        xh5[n5] = dh[i];
+        xy5[n5++] = dy[i];
+      } else {
+        dh[rest] = dh[i];
+        dy[rest++] = dy[i];
+      }
+    }
+    nd = rest;
+    if (n5 > 0) {
+      lr_status st = run_xcd_decode(xh5, xy5, n5, X, M, stream);
+      for (int i = 0; st == LR_ERR_UNSUPPORTED && i < n5; ++i) {
+        // every kind-5 handle has a plan for running alone
+        st = run_xcd_decode(xh5 + i, xy5 + i, 1, X, M, stream);
+        if (st == LR_ERR_UNSUPPORTED) return fail(st, "no XCD-sliced decode plan for a handle");
+        if (st == LR_OK && i + 1 < n5) st = LR_ERR_UNSUPPORTED;
+      }
+      if (st != LR_OK) return st;
+    }
+  }
   for (int b = 0; b < nd;) {
     if (dh[b]->dp.kind >= 2) {  // one launch per projection: it fills the machine
       const lr_status st = run_split_decode(dh[b], dy[b], X, M, stream);
@@ -572,7 +724,26 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
   size_t o_ctrl = 0, o_tcnt = 0, o_tflag = 0, o_ycnt = 0, o_tpart = 0, o_tfin = 0, o_ypart = 0, o_tbuf = 0;
   size_t o_sflags = 0, o_tsp = 0, o_asw = 0, o_bsw = 0, o_fpart = 0, o_pflags = 0;
   if (h->has_decode) h->dec_max_M = (int)(max_M < LR_DECODE_MAX_M ? max_M : LR_DECODE_MAX_M);
-  if (h->has_decode && !h->dense) {
+  h->withhold = (flags & LR_FLAG_TEST_STALL) ? 0 : -1;
+  h->spin_limit = (flags & LR_FLAG_TEST_STALL) ? 2048u : (1u << 22);
+  const uint32_t decode_kind_flags = LR_FLAG_DECODE_STREAMING | LR_FLAG_DECODE_RESIDENT | LR_FLAG_DECODE_SPLIT;
+  if (h->has_decode && !h->dense && !(flags & decode_kind_flags)) {
+    // the XCD-sliced kernel: one workgroup per compute unit, all resident at
+    // once (its workgroups wait on one another), so the occupancy of its
+    // largest plan must allow at least one per compute unit
+    const int cus = num_cus(dev);
+    if (cus >= 8 && cus % 8 == 0) {
+      h->xcd_P = cus / 8;
+      int64_t lds = 0;
+      for (int v = 0; v < 3; ++v) {
+        const int pn = h->xcd_P >> v;
+        h->xcd_ok[v] = pn >= 1 && (pn << v) == h->xcd_P && lrv::xcd_plan(K, r, N, pn, h->dec_max_M, &h->xp[v]);
+        if (h->xcd_ok[v]) lds = lds > h->xp[v].lds ? lds : h->xp[v].lds;
+      }
+      if (h->xcd_ok[0] && lrk::decode_xcd_blocks_per_cu((int)lds) >= 1) h->dp.kind = 5;
+    }
+  }
+  if (h->has_decode && !h->dense && h->dp.kind != 5) {
     const int occ = lrk::decode_blocks_per_cu();
     if (occ < 1) {
       delete h;
@@ -580,9 +751,35 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     }
     h->dp = lrv::decode_partition(K, r, N, num_cus(dev),
                                   !(flags & LR_FLAG_DECODE_STREAMING) && lrk::decode_res_available(),
-                                  !(flags & (LR_FLAG_DECODE_STREAMING | LR_FLAG_DECODE_RESIDENT)), h->dec_max_M);
+                                  (flags & LR_FLAG_DECODE_SPLIT) != 0, h->dec_max_M);
   }
-  if (h->has_decode && !h->dense && (h->dp.kind >= 2)) {
+  size_t o_xtf = 0, o_xyf = 0, o_xtp = 0, o_xyp = 0;
+  if (h->has_decode && !h->dense && h->dp.kind == 5) {
+    // XCD-sliced kernel: control words, one T and one Y flag per workgroup,
+    // and the partial T and partial Y tables of the largest plan
+    int64_t tp = 0, tf = 0, yp = 0;
+    for (int v = 0; v < 3; ++v)
+      if (h->xcd_ok[v]) {
+        tp = tp > h->xp[v].tpart_bytes ? tp : h->xp[v].tpart_bytes;
+        tf = tf > h->xp[v].tfin_bytes ? tf : h->xp[v].tfin_bytes;
+        yp = yp > h->xp[v].ypart_bytes ? yp : h->xp[v].ypart_bytes;
+      }
+    o_ctrl = off;
+    off = align_up(off + 64);
+    o_xtf = off;
+    off = align_up(off + (size_t)3 * 8 * h->xcd_P * 4);
+    o_xtp = off;
+    off = align_up(off + (size_t)tp);
+    o_xyf = off;  // T of each XCD's range
+    off = align_up(off + (size_t)tf);
+    o_xyp = off;
+    off = align_up(off + (size_t)yp);
+    if (off >= ((size_t)1 << 31)) {
+      delete h;
+      return fail(LR_ERR_UNSUPPORTED, "decode workspace of %zu bytes exceeds 2 GiB", off);
+    }
+    h->dws_bytes = (int64_t)off;
+  } else if (h->has_decode && !h->dense && (h->dp.kind >= 2)) {
     // role-split kernels: control words, replicated T slice flags and T
     // (the Y producers' reads of T spread over the replicas), and both
     // factors in the operand block layout
@@ -675,7 +872,28 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     }
   }
   char* base = (char*)h->ws;
-  if (h->has_decode && !h->dense && (h->dp.kind >= 2)) {
+  if (h->has_decode && !h->dense) {
+    // pinned host word for the decode kernels' timeout report
+    e = hipHostMalloc((void**)&h->err_host, 64, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e == hipSuccess) {
+      *h->err_host = 0u;
+      e = hipHostGetDevicePointer((void**)&h->err_dev, h->err_host, 0);
+    }
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      discard(h);
+      return hip_fail(e, "pinned status word");
+    }
+  }
+  if (h->has_decode && !h->dense && h->dp.kind == 5) {
+    h->dws = base;
+    h->ctrl = (uint32_t*)(base + o_ctrl);
+    h->xflags = (uint32_t*)(base + o_xtf);
+    h->xtpart = (float*)(base + o_xtp);
+    h->xtfin = (float*)(base + o_xyf);
+    h->xypart = (float*)(base + o_xyp);
+    h->xcd_local = xcd_map_ok(dev);
+  } else if (h->has_decode && !h->dense && (h->dp.kind >= 2)) {
     h->dws = base;
     h->ctrl = (uint32_t*)(base + o_ctrl);
     h->sflags = (uint32_t*)(base + o_sflags);
@@ -688,8 +906,7 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     if (e == hipSuccess) e = lrk::launch_dense_swizzle(h->B, h->Bsw, r, N, nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
-      (void)hipFree(h->ws);
-      delete h;
+      discard(h);
       return hip_fail(e, "split decode: factor layout");
     }
   } else if (h->has_decode && !h->dense) {
@@ -717,8 +934,7 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
       e = hipMalloc(&tmp, (size_t)K * N * 2);
       if (e != hipSuccess) {
         (void)hipGetLastError();
-        (void)hipFree(h->ws);
-        delete h;
+        discard(h);
         return fail(LR_ERR_OUT_OF_MEMORY, "dense fallback: hipMalloc(%lld) for W", (long long)(K * N * 2));
       }
     }
@@ -726,8 +942,7 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     st = form_dense(h, h->W ? h->W : (uint16_t*)tmp);
     if (tmp) (void)hipFree(tmp);
     if (st != LR_OK) {
-      (void)hipFree(h->ws);
-      delete h;
+      discard(h);
       return st;
     }
   }
@@ -739,6 +954,8 @@ lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, v
   if (!h) return fail(LR_ERR_INVALID_ARG, "handle is null");
   lrv::Shape s{h->K, h->r, h->N, h->max_M, h->A, h->B};
   lr_status st = lrv::check_run(s, X, Y, M, g_err, sizeof g_err);
+  if (st != LR_OK) return st;
+  st = take_stall(h);
   if (st != LR_OK || M == 0) return st;
   uint16_t* Ys[1] = {(uint16_t*)Y};
   const lr_linear* hs[1] = {h};
@@ -762,7 +979,12 @@ lr_status lr_group_run(const lr_linear* const* hs, int n, const void* X, void* c
     yv[i] = Ys[i];
     ys[i] = (uint16_t*)Ys[i];
   }
-  const lr_status st = lrv::check_group(s, n, X, yv, M, g_err, sizeof g_err);
+  lr_status st = lrv::check_group(s, n, X, yv, M, g_err, sizeof g_err);
+  if (st != LR_OK) return st;
+  for (int i = 0; i < n; ++i) {
+    const lr_status si = take_stall(hs[i]);
+    if (si != LR_OK) st = si;
+  }
   if (st != LR_OK || M == 0) return st;
   return run_group(hs, ys, n, X, M, (hipStream_t)stream);
 }
@@ -788,13 +1010,23 @@ void lr_linear_destroy(lr_linear* h) {
     (void)hipFree(h->ws);
     if (swapped) (void)hipThreadExchangeStreamCaptureMode(&mode);
   }
+  if (h->err_host) (void)hipHostFree(h->err_host);
   delete h;
+}
+
+lr_status lr_linear_status(const lr_linear* h) {
+  if (!h) return fail(LR_ERR_INVALID_ARG, "handle is null");
+  return take_stall(h);
 }
 
 lr_status lr_linear_describe(const lr_linear* h, char* buf, int64_t len) {
   if (!h || !buf || len <= 0) return fail(LR_ERR_INVALID_ARG, "null handle or buffer");
-  char dec[160];
-  if (h->dp.kind == 2)
+  char dec[200];
+  if (h->dp.kind == 5)
+    snprintf(dec, sizeof dec, "kind=xcd P=%d pa=%d rs=%d nc=%d cpr_a=%d cpr_b=%d da=%d db=%d lds=%lld grid=%d",
+             h->xcd_P, h->xp[0].pa, h->xp[0].rs, h->xp[0].nc, h->xp[0].cpr_a, h->xp[0].cpr_b, h->xp[0].da,
+             h->xp[0].db, (long long)h->xp[0].lds, 8 * h->xcd_P);
+  else if (h->dp.kind == 2)
     snprintf(dec, sizeof dec, "kind=split GA=%d GB=%d gpw=%d blocks_per_wave=%d grid=%d", h->dp.ga, h->dp.gb,
              h->dp.gpw, h->dp.ntps, h->dp.ga + h->dp.gb);
   else if (h->dp.kind == 3)
@@ -823,6 +1055,7 @@ int64_t lr_linear_workspace_bytes(const lr_linear* h) { return h ? (int64_t)h->w
 #ifdef LR_DECODE_TRACE
 // Trace builds only: device buffer of grid * 8 uint64 phase timestamps.
 void lr_debug_set_trace(void* device_buf) { g_trace = (uint64_t*)device_buf; }
+void lr_debug_set_xcd_coherent(int on) { g_xcd_coherent = on != 0; }
 #endif
 
 }  // extern "C"

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <algorithm>
+
 #include "../../include/lr_linear.h"
 
 namespace lrv {
@@ -49,7 +51,7 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
   }
   const uint32_t known = LR_FLAG_FORCE_DECODE | LR_FLAG_FORCE_PREFILL | LR_FLAG_DECODE_STREAMING |
                          LR_FLAG_PREFILL_TWO_WAVE | LR_FLAG_PREFILL_ONE_WAVE | LR_FLAG_DENSE | LR_FLAG_FACTORED |
-                         LR_FLAG_DECODE_SPLIT | LR_FLAG_DECODE_RESIDENT;
+                         LR_FLAG_DECODE_SPLIT | LR_FLAG_DECODE_RESIDENT | LR_FLAG_TEST_STALL;
   if (flags & ~known) { snprintf(err, errlen, "unknown flag bits 0x%x", flags & ~known); return LR_ERR_UNSUPPORTED; }
   if ((flags & LR_FLAG_FORCE_DECODE) && (flags & LR_FLAG_FORCE_PREFILL)) {
     snprintf(err, errlen, "FORCE_DECODE and FORCE_PREFILL are exclusive");
@@ -362,6 +364,85 @@ inline DecPart decode_partition(int64_t K, int64_t r, int64_t N, int budget, boo
 }
 
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// XCD-sliced decode (the default decode kernel, lr_decode_xcd.hip).  With
+// P workgroups per XCD (one per compute unit), a projection given pn of
+// them per XCD: XCD x owns rank rows [x r / 8, (x + 1) r / 8).  The first pa
+// of its pn workgroups stream A: (pa / rs) K-slabs x rs rank sub-ranges,
+// each computing a partial T; the other pb = pn - pa stream B, one column
+// slab of N each, for GEMM2 over the XCD's rank range.  A compute unit that
+// streams one factor never holds the exchange of the other behind its own
+// requests.  pa follows the bytes each side streams (A and X against B).
+// Wide row pieces stream best (a compute unit moves whole 128-byte lines
+// much faster than pieces of a few dozen bytes): rs is the smallest power of
+// two that keeps a sub-range within kXcdMaxTilesA 16-column MFMA tiles, and
+// a slab is cut into nc (1, 2, 4 or 8) column chunks of at most
+// kXcdMaxTilesB tiles.  The k-steps in flight per wave (da, db) are as many
+// as the LDS holds and each wave's vector-memory counter (6 bits) counts.
+constexpr int kXcdMaxTilesA = 16;
+constexpr int kXcdMaxTilesB = 16;
+constexpr int64_t kXcdLdsBytes = 160 * 1024;
+constexpr int kXcdMaxInFlight = 62;         // vector-memory operations a wave keeps in flight
+struct XcdPlan {
+  int pn, pa, rs, nc;
+  int cpr_a, cpr_b;  // 16-byte chunks per LDS row of an A piece / a B chunk
+  int da, db;        // k-steps in flight per wave of an A / a B workgroup
+  int ldtp, ws;      // rank-range and slab lengths of the exchange tables
+  int64_t lds;       // dynamic LDS bytes (the larger of the two roles)
+  int64_t tpart_bytes, tfin_bytes, ypart_bytes;
+};
+inline bool xcd_plan(int64_t K, int64_t r, int64_t N, int pn, int64_t max_M, XcdPlan* out) {
+  if (pn < 2 || K < 1 || r < 1 || N < 1 || max_M < 1 || max_M > kDecodeMaxM) return false;
+  const int64_t rw = ceil_div(r, 8);          // widest XCD rank range
+  const int64_t nks = ceil_div(K, 32);
+  int rs = 1;
+  while (ceil_div(rw, rs) > 16 * kXcdMaxTilesA && rs < pn) rs *= 2;
+  if (ceil_div(rw, rs) > 16 * kXcdMaxTilesA) return false;
+  // A workgroups in proportion to the bytes streamed, a multiple of rs,
+  // leaving at least one B workgroup
+  const double abytes = (double)K * (double)r + (double)max_M * (double)K * 8.0;
+  const double bbytes = (double)r * (double)N;
+  int pa = (int)((double)pn * abytes / (abytes + bbytes) / rs + 0.5) * rs;
+  if (pa < rs) pa = rs;
+  while (pa > pn - 1 && pa > rs) pa -= rs;
+  if (pa > pn - 1) return false;
+  XcdPlan p{};
+  p.pn = pn;
+  p.pa = pa;
+  p.rs = rs;
+  const int64_t ks = pa / rs;
+  p.cpr_a = (int)(2 * ceil_div(ceil_div(rw, rs), 16));
+  p.ws = (int)ceil_div(N, pn - pa);
+  p.nc = 1;
+  while (ceil_div(p.ws, p.nc) > 16 * kXcdMaxTilesB && p.nc < 8) p.nc *= 2;
+  if (ceil_div(p.ws, p.nc) > 16 * kXcdMaxTilesB) return false;
+  p.cpr_b = (int)(2 * ceil_div(ceil_div(p.ws, p.nc), 16));
+  const int64_t nks2 = ceil_div(rw, 32);
+  const int64_t ldt = 32 * nks2 + 8;
+  const int64_t tbytes = (max_M > 8 ? 32 : 16) * ldt * 2;
+  // LDS tiles have rows of cpr + 1 chunks (an odd pitch spreads rows over
+  // the banks), loaded by whole 64-lane instructions
+  const int64_t ia = ceil_div(32 * (p.cpr_a + 1), 64), ib = ceil_div(32 * (p.cpr_b + 1), 64);
+  const int64_t slot_a = 1024 * ia + 1024, slot_b = 1024 * ib;
+  const int64_t ka = std::max<int64_t>(1, ceil_div(ceil_div(nks, ks), 8));   // k-steps of the busiest A wave
+  const int64_t kb = std::max<int64_t>(1, ceil_div(nks2, 8 / p.nc));        // and of the busiest B wave
+  const int64_t da_max = std::min<int64_t>(ka, kXcdMaxInFlight / (ia + 1));
+  const int64_t db_max = std::min<int64_t>(kb, kXcdMaxInFlight / ib);
+  if (da_max < 1 || db_max < 1 || 8 * slot_a > kXcdLdsBytes || 8 * slot_b + tbytes > kXcdLdsBytes) return false;
+  int64_t da = 1, db = 1;
+  while (da < da_max && 8 * (da + 1) * slot_a <= kXcdLdsBytes) ++da;
+  while (db < db_max && 8 * (db + 1) * slot_b + tbytes <= kXcdLdsBytes) ++db;
+  p.da = (int)da;
+  p.db = (int)db;
+  p.ldtp = (int)rw;
+  p.lds = std::max<int64_t>(8 * da * slot_a, 8 * db * slot_b + tbytes);
+  const int64_t colb = 16 * ceil_div(max_M, 4);
+  p.tpart_bytes = 8 * ks * p.ldtp * colb;
+  p.tfin_bytes = 8 * (int64_t)p.ldtp * colb;
+  p.ypart_bytes = 8 * (int64_t)(pn - pa) * p.ws * colb;
+  *out = p;
+  return true;
+}
 
 // Prefill launch plan: tile width 32 * nb columns (nb in [6, 7]) and a
 // k-split.  Cost unit: one 32-deep k-step of one workgroup with one MFMA

@@ -527,7 +527,7 @@ SPLIT_STREAM_GRID = [(1, 4096, 2867, 14336, 1), (8, 4096, 2867, 14336, 8), (4, 2
 
 @pytest.mark.parametrize("M,K,r,N,max_M", SPLIT_STREAM_GRID)
 def test_split_stream_decode_shapes(M, K, r, N, max_M):
-    p, lin, _, _ = run_case(M, K, r, N, 7700 + r + N + M, max_M=max_M)
+    p, lin, _, _ = run_case(M, K, r, N, 7700 + r + N + M, max_M=max_M, flags=lrl.LR_FLAG_DECODE_SPLIT)
     assert "kind=split_stream" in lin.describe(), lin.describe()
 
 
@@ -537,7 +537,7 @@ def test_split_stream_repeated_calls(gpu):
     torch = gpu
     K, r, N = 1500, 2100, 9000
     _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 557)
-    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=8, flags=lrl.LR_FLAG_FACTORED)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=8, flags=lrl.LR_FLAG_FACTORED | lrl.LR_FLAG_DECODE_SPLIT)
     assert "kind=split_stream" in lin.describe(), lin.describe()
     side = torch.cuda.Stream()
     for i, M in enumerate([1, 8, 5, 8, 2, 1]):
@@ -565,7 +565,7 @@ SPLIT_FLAT_GRID = [(1, 14336, 2867, 4096, 1), (4, 14336, 2867, 4096, 4), (2, 120
 
 @pytest.mark.parametrize("M,K,r,N,max_M", SPLIT_FLAT_GRID)
 def test_split_flat_decode_shapes(M, K, r, N, max_M):
-    p, lin, _, _ = run_case(M, K, r, N, 7900 + r + N + M, max_M=max_M)
+    p, lin, _, _ = run_case(M, K, r, N, 7900 + r + N + M, max_M=max_M, flags=lrl.LR_FLAG_DECODE_SPLIT)
     assert "kind=split_flat" in lin.describe(), lin.describe()
 
 
@@ -573,7 +573,7 @@ def test_split_flat_repeated_calls(gpu):
     torch = gpu
     K, r, N = 12001, 2000, 6000
     _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 558)
-    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=8, flags=lrl.LR_FLAG_FACTORED)
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=8, flags=lrl.LR_FLAG_FACTORED | lrl.LR_FLAG_DECODE_SPLIT)
     assert "kind=split_flat" in lin.describe(), lin.describe()
     side = torch.cuda.Stream()
     for i, M in enumerate([1, 8, 3, 8, 1]):
@@ -737,7 +737,8 @@ def test_layer_graph_replay(gpu, M, flags):
 
 
 @pytest.mark.parametrize("M,K,r,N,kind", [(1, 4096, 2867, 14336, "split_stream"), (3, 14336, 2867, 4096, "split_flat"),
-                                          (8, 4096, 1637, 4096, "split")])
+                                          (8, 4096, 1637, 4096, "split"), (8, 4096, 1637, 4096, "xcd"),
+                                          (1, 4096, 2867, 14336, "xcd"), (12, 14336, 2867, 4096, "xcd")])
 def test_split_variants_graph_replay(gpu, M, K, r, N, kind):
     # each role-split variant captured with two launches on one handle (so
     # the generation word advances twice per replay), replayed with eager
@@ -746,7 +747,8 @@ def test_split_variants_graph_replay(gpu, M, K, r, N, kind):
     torch = gpu
     banner("graph replay %s M=%d K=%d r=%d N=%d" % (kind, M, K, r, N))
     _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 8300 + r)
-    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=lrl.LR_FLAG_FACTORED)
+    extra = 0 if kind == "xcd" else lrl.LR_FLAG_DECODE_SPLIT
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=lrl.LR_FLAG_FACTORED | extra)
     assert "kind=%s " % kind in lin.describe(), lin.describe()
     X1 = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
     X2 = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
