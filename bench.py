@@ -35,8 +35,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "low-rank linear: decode TB/s and prefill TFLOP/s vs roofline, across rank r"
 _CSRC = "rank_linear_layer_amd/csrc/"
-DECODE_SOURCES = [_CSRC + f for f in ("lr_decode.hip", "lr_decode_res.hip", "lr_decode_split.hip", "lr_device.h",
-                                       "lr_kernels.h")]
+DECODE_SOURCES = [_CSRC + f for f in ("lr_decode.hip", "lr_decode_res.hip", "lr_decode_split.hip", "lr_decode_xcd.hip",
+                                       "lr_device.h", "lr_kernels.h")]
 PREFILL_SOURCES = [_CSRC + f for f in ("lr_prefill.hip", "lr_prefill_w4.hip", "lr_device.h", "lr_kernels.h",
                                        "lr_validate.h", "lr_linear.cpp")]
 PREFILL_KERNELS = {0: "lr_prefill_gemm_kernel", 1: "lr_prefill_w4_kernel"}
@@ -87,9 +87,12 @@ def time_steps(torch, fn, steps, warmup, stream):
 
 
 def decode_kernel_name(plan):
-    if "kind=split" in plan:
-        return "lr_decode_split_kernel"
-    return "lr_decode_res_kernel" if "kind=resident" in plan else "lr_decode_fused_kernel"
+    for kind, name in (("kind=split_stream", "lr_decode_splits_kernel"), ("kind=split_flat", "lr_decode_splitf_kernel"),
+                       ("kind=split", "lr_decode_split_kernel"), ("kind=xcd", "lr_decode_xcd_kernel"),
+                       ("kind=resident", "lr_decode_res_kernel")):
+        if kind in plan:
+            return name
+    return "lr_decode_fused_kernel"
 
 
 def traffic_from_profile(name, sources=None, key="hbm_bytes_per_launch"):
@@ -108,7 +111,9 @@ def traffic_from_profile(name, sources=None, key="hbm_bytes_per_launch"):
     return d.get(key)
 
 
-def bench_decode(torch, lrl, configs, datagen, metrics, steps, warmup):
+def bench_decode(torch, lrl, configs, datagen, metrics, steps, warmup, flags=0, context=True):
+    """q_proj decode through the kernel that `flags` selects (0: the
+    library's default, which reads A and B in place)."""
     c = configs.QPROJ_DECODE
     M, K, r, N = c["M"], c["K"], c["r"], c["N"]
     Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, configs.seed_base(c["index"]))
@@ -119,21 +124,27 @@ def bench_decode(torch, lrl, configs, datagen, metrics, steps, warmup):
     Bs = [B0] + [B0.clone() for _ in range(ncopies - 1)]
     X = dev_bf16(torch, Xb)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    lins = [lrl.LowRankLinear(a, b, max_M=M) for a, b in zip(As, Bs)]
+    lins = [lrl.LowRankLinear(a, b, max_M=M, flags=flags) for a, b in zip(As, Bs)]
     stream = torch.cuda.current_stream()
-    log("decode plan: %s; %d weight copies (%.0f MB)" % (lins[0].describe(), ncopies, ncopies * 2 * (K * r + r * N) / 1e6))
+    log("decode plan (flags %d): %s; %d weight copies (%.0f MB)"
+        % (flags, lins[0].describe(), ncopies, ncopies * 2 * (K * r + r * N) / 1e6))
 
     def step(i):
         lins[i % ncopies](X, out=Y)
 
     ms = time_steps(torch, step, steps, warmup, stream)
     tbs = per / (ms * 1e-3) / 1e12
-    # warm-cache figure (same copy every step) for context
-    ms_warm = time_steps(torch, lambda i: lins[0](X, out=Y), max(50, steps // 4), 10, stream)
-    # the same rotation replayed from a captured graph, for context
-    us_graph = replay_us(torch, step, ncopies, steps, warmup)
-    return dict(M=M, K=K, r=r, N=N, ms=ms, tbs=tbs, bytes=per, ncopies=ncopies,
-                warm_tbs=per / (ms_warm * 1e-3) / 1e12, graph_us=us_graph, plan=lins[0].describe())
+    out = dict(M=M, K=K, r=r, N=N, ms=ms, tbs=tbs, bytes=per, ncopies=ncopies, plan=lins[0].describe(),
+               workspace_bytes=lins[0].workspace_bytes())
+    if context:
+        # warm-cache figure (same copy every step), and the same rotation
+        # replayed from a captured graph
+        ms_warm = time_steps(torch, lambda i: lins[0](X, out=Y), max(50, steps // 4), 10, stream)
+        out["warm_tbs"] = per / (ms_warm * 1e-3) / 1e12
+        out["graph_us"] = replay_us(torch, step, ncopies, steps, warmup)
+    del lins
+    torch.cuda.empty_cache()
+    return out
 
 
 def replay_us(torch, fn, n, steps, warmup):
@@ -195,12 +206,19 @@ def bench_prefill(torch, lrl, configs, metrics, steps, warmup):
     X = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     A = (torch.randn((K, r), generator=g, device="cuda", dtype=torch.float32) / np.sqrt(K)).to(torch.bfloat16)
     B = (torch.randn((r, N), generator=g, device="cuda", dtype=torch.float32) / np.sqrt(r)).to(torch.bfloat16)
-    lin = lrl.LowRankLinear(A, B, max_M=M)
-    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    # four copies of the whole working set (X, A, B, Y: about 280 MB each,
+    # above the 256 MB last-level cache) rotate, so every step starts cold
+    ncop = 4
+    Xs = [X] + [X.clone() for _ in range(ncop - 1)]
+    lins = [lrl.LowRankLinear(A.clone() if i else A, B.clone() if i else B, max_M=M) for i in range(ncop)]
+    Ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(ncop)]
     stream = torch.cuda.current_stream()
-    ms = time_steps(torch, lambda i: lin(X, out=Y), steps, warmup, stream)
+    ms = time_steps(torch, lambda i: lins[i % ncop](Xs[i % ncop], out=Ys[i % ncop]), steps, warmup, stream)
     fl = metrics.lowrank_flops(M, K, r, N)
-    return dict(M=M, K=K, r=r, N=N, ms=ms, tflops=fl / (ms * 1e-3) / 1e12, flops=fl, plan=lin.describe())
+    plan = lins[0].describe()
+    del lins, Xs, Ys
+    torch.cuda.empty_cache()
+    return dict(M=M, K=K, r=r, N=N, ms=ms, tflops=fl / (ms * 1e-3) / 1e12, flops=fl, plan=plan, copies=ncop)
 
 
 def bench_layer(torch, lrl, configs, metrics, M, steps, warmup, grouped=True, graph=False):
@@ -293,7 +311,7 @@ def calib_copy(torch):
     log("calibration copy: 3 x %d bytes read and written" % nbytes)
 
 
-def run_sweep(torch, lrl, configs, metrics, steps, stride=1):
+def run_sweep(torch, lrl, configs, metrics, steps, stride=1, ranks=None):
     """Throughput against rank at K = 4096 for both widths N and both M of
     the alignment sweep (the no-cliff check).  Every point is printed as a
     JSON line on stderr; the summary per (N, M) series goes into the result:
@@ -302,7 +320,7 @@ def run_sweep(torch, lrl, configs, metrics, steps, stride=1):
     rows = []
     K = configs.SWEEP_K
     for N in configs.SWEEP_N:
-        for r in configs.SWEEP_R[::stride]:
+        for r in (ranks if ranks is not None else configs.SWEEP_R[::stride]):
             g = torch.Generator(device="cuda")
             g.manual_seed(configs.sweep_seed(N, r))
             wb = 2 * (K * r + r * N)
@@ -335,9 +353,14 @@ def run_sweep(torch, lrl, configs, metrics, steps, stride=1):
                 nb = np.concatenate([v[max(0, i - 8):i], v[i + 1:i + 9]])
                 if len(nb) and x[key] < 0.9 * np.median(nb):
                     cliffs.append(x["r"])
+            peak = HBM_PEAK_GBS / 1e3 if M <= 16 else BF16_PEAK_TFLOPS
             summary["N%d_M%d" % (N, M)] = {"unit": "TB/s" if M <= 16 else "TFLOP/s", "points": len(ser),
+                                           "ranks": [x["r"] for x in ser],
+                                           "residues_mod8": sorted({x["r"] % 8 for x in ser}),
                                            "min": float(v.min()), "median": float(np.median(v)),
-                                           "max": float(v.max()), "cliff_ranks": cliffs}
+                                           "max": float(v.max()), "min_frac": round(float(v.min()) / peak, 4),
+                                           "max_over_min": round(float(v.max() / v.min()), 4),
+                                           "cliff_ranks": cliffs}
     return summary, rows
 
 
@@ -392,7 +415,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
-    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="the full rank sweep (every r of the sweep range)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the default strided rank sweep")
+    ap.add_argument("--no-alternatives", action="store_true", help="skip the opt-in decode kernels")
     ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--sweep-stride", type=int, default=1)
     ap.add_argument("--gac", action="store_true", help="with --sweep: GAC rank re-selection on the measured table")
@@ -419,6 +444,21 @@ def main():
 
     torch.cuda.synchronize()
     d = bench_decode(torch, lrl, configs, datagen, metrics, args.steps, args.warmup)
+    alts = {}
+    if not args.no_alternatives:
+        # the opt-in decode kernels on the same workload, for context: the
+        # role-split kernel reads a copy of A and B in its operand block
+        # layout (extra workspace bytes), the XCD-sliced one reads them in place
+        for name, fl in (("split_copy", lrl.LR_FLAG_DECODE_SPLIT), ("xcd", lrl.LR_FLAG_DECODE_XCD),
+                         ("streaming", lrl.LR_FLAG_DECODE_STREAMING)):
+            a_ = bench_decode(torch, lrl, configs, datagen, metrics, max(200, args.steps // 2), 50, flags=fl,
+                              context=False)
+            alts[name] = {"flag": fl, "kernel": decode_kernel_name(a_["plan"]), "us_per_launch": round(a_["ms"] * 1e3, 3),
+                          "value": round(a_["tbs"], 4), "roofline_frac_hbm": round(a_["tbs"] * 1e3 / HBM_PEAK_GBS, 4),
+                          "workspace_bytes": a_["workspace_bytes"],
+                          "reads_factors_in_place": fl != lrl.LR_FLAG_DECODE_SPLIT}
+            log("decode %s: %.3f us/step, %.3f TB/s, workspace %d bytes"
+                % (name, a_["ms"] * 1e3, a_["tbs"], a_["workspace_bytes"]))
     log("decode: %.3f us/step, %.3f TB/s (warm-cache %.3f TB/s; from a captured graph %.3f us/step)"
         % (d["ms"] * 1e3, d["tbs"], d["warm_tbs"], d["graph_us"]))
     kname = decode_kernel_name(d["plan"])
@@ -440,7 +480,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) bf16 factors; %d rotating weight copies, "
                 "cold last-level cache)" % d["ncopies"],
         "config": {"workload": "Llama-3-8B-shaped q_proj decode, misaligned rank", "M": d["M"], "K": d["K"],
-                   "r": d["r"], "N": d["N"], "path": kname, "weight_copies": d["ncopies"]},
+                   "r": d["r"], "N": d["N"], "path": kname, "weight_copies": d["ncopies"],
+                   "factors_read_in_place": True, "workspace_bytes": d["workspace_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile("%s_qproj_decode_pmc.json" % kname),
@@ -448,13 +489,15 @@ def main():
                      "us_per_launch": round(d["ms"] * 1e3, 3)},
         "warm_cache_tbs": round(d["warm_tbs"], 4),
         "graph_replay_us_per_step": round(d["graph_us"], 3),
+        "decode_alternatives": alts or None,
     }
     if not args.no_prefill:
         p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 50), 3)
         log("prefill: %.3f ms/step, %.1f TFLOP/s" % (p["ms"], p["tflops"]))
         kn = prefill_kernels(p["plan"])
         result["prefill"] = {
-            "workload": "MLP up-projection prefill M=4096 K=4096 r=2867 N=14336",
+            "workload": "MLP up-projection prefill M=4096 K=4096 r=2867 N=14336 (%d rotating copies of X, A, B, Y)"
+                        % p["copies"],
             "ms_per_step": round(p["ms"], 5), "value": round(p["tflops"], 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(p["tflops"], 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(p["tflops"] / BF16_PEAK_TFLOPS, 4),
@@ -496,6 +539,12 @@ def main():
                                        "down 14336->4096 r2867", **lay}
     if args.sweep:
         result["sweep"], sweep_rows = run_sweep(torch, lrl, configs, metrics, args.sweep_steps, args.sweep_stride)
+    elif not args.no_sweep:
+        # strided: 16 ranks, stride 3, so every residue of r mod 8 appears twice
+        result["sweep"], sweep_rows = run_sweep(torch, lrl, configs, metrics, args.sweep_steps,
+                                                ranks=configs.SWEEP_R_DEFAULT)
+    if args.sweep or not args.no_sweep:
+        log("sweep: %s" % json.dumps(result["sweep"]))
         if args.gac:
             result["gac"] = gac_from_sweep(sweep_rows, configs)
             log("gac: %s" % json.dumps(result["gac"]))

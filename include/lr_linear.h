@@ -58,15 +58,16 @@
  * ------
  * Functions return an lr_status and never abort, print or throw across the
  * ABI.  lr_last_error() returns a thread-local detail string for the most
- * recent failure on the calling thread.  The decode kernels divide one
- * launch among one workgroup per compute unit that wait on one another's
- * partial results, which needs every workgroup of the launch resident at
- * once; create checks that the kernel's occupancy allows it, but another
- * kernel running concurrently on the same GPU can hold compute units.  A
- * wait then gives up after a bounded number of polls (seconds) instead of
- * hanging, the launch ends normally with an invalid output, and the handle's
- * next lr_linear_run / lr_group_run / lr_mlp_packed_run, or
- * lr_linear_status, returns LR_ERR_HIP (once).
+ * recent failure on the calling thread.  The workgroups of a decode launch
+ * wait on one another's partial results, which needs every workgroup of the
+ * launch resident at once.  Create checks every launch the handle can make
+ * against its kernel's occupancy (UNSUPPORTED if one cannot fit), and every
+ * launch is checked again before it is enqueued.  Another kernel running
+ * concurrently on the same GPU can still hold compute units: a wait then
+ * gives up after a bounded number of polls (seconds) instead of hanging,
+ * the launch ends normally with an invalid output, and the handle's next
+ * lr_linear_run / lr_group_run / lr_mlp_packed_run, or lr_linear_status,
+ * returns LR_ERR_HIP (once).
  */
 #ifndef LR_LINEAR_H
 #define LR_LINEAR_H
@@ -106,9 +107,13 @@ typedef struct lr_linear lr_linear;
                                       reads a copy of A and B in its operand block layout, made at
                                       create (see Ownership) */
 #define LR_FLAG_DECODE_RESIDENT 256u  /* decode with the LDS-resident kernel where it applies, else
-                                         the register-streaming one */
-#define LR_FLAG_TEST_STALL (1u << 30) /* for testing the error path only: in every decode launch one
-                                         workgroup never publishes its partial result and waits give
+                                         the register-streaming one (the default's choice too) */
+#define LR_FLAG_DECODE_XCD 512u  /* decode with the XCD-sliced kernel where its plan fits: it reads
+                                    A and B in place, one workgroup per compute unit, each XCD
+                                    owning an eighth of the rank; gate/up or q/k/v handles that all
+                                    carry this flag share one launch in lr_group_run */
+#define LR_FLAG_TEST_STALL (1u << 30) /* for testing the error path only: the T hand-off wait of every
+                                         decode launch expects a value that is never stored and gives
                                          up after 2048 polls, so each decode call's output is invalid
                                          and the next call reports LR_ERR_HIP */
 
@@ -123,18 +128,17 @@ typedef struct lr_linear lr_linear;
  *   max_M  : largest M that lr_linear_run will be called with (>= 0).
  *   flags  : LR_FLAG_* bits.
  * Chooses the kernels' partitioning for this shape and allocates the
- * workspace on the current HIP device.  Decode (M <= 16) takes the
- * XCD-sliced kernel: one workgroup per compute unit, each streaming an equal
- * share of A and of B straight from the caller's row-major factors; XCD x
- * computes T for rank rows [x r / 8, (x + 1) r / 8) (its workgroups split K
- * and the range, then add their partials through the XCD's L2) and the
- * partial Y of those rows, and the eight partials of Y are added across
- * XCDs.  LR_FLAG_DECODE_RESIDENT, _STREAMING and _SPLIT select the older
- * decode kernels instead (the split one copies A and B at create, see
- * Ownership); shapes the XCD-sliced plan cannot take (a sub-range above 128
- * columns, a column slab above 1024, a device whose CU count is not a
- * multiple of 8) take the LDS-resident or streaming kernel.  Create launches
- * no kernel, except for LR_FLAG_DECODE_SPLIT and for the dense fallback:
+ * workspace on the current HIP device.  By default decode (M <= 16) reads
+ * the caller's row-major A and B in place and pads the rank on chip: the
+ * LDS-resident kernel where its slabs fit in LDS (rank slices of 128
+ * columns; T partials added inside an XCD, Y partials across XCDs), else
+ * the register-streaming kernel (rank slices of 120 columns).  No copy of
+ * the factors is made.  LR_FLAG_DECODE_STREAMING, _RESIDENT, _XCD and
+ * _SPLIT select a kernel explicitly; _SPLIT is the only one that reads a
+ * copy (see Ownership), and is the fastest where the extra bytes are
+ * acceptable.  A flag whose plan does not fit the shape falls back to the
+ * default.  Create launches no kernel, except for LR_FLAG_DECODE_SPLIT and
+ * for the dense fallback:
  * when LR_FLAG_DENSE is set, or (without LR_FLAG_FACTORED) when the factors
  * hold at least 95% of the bytes of the K x N matrix they replace, i.e.
  * 100 r (K + N) >= 95 K N ("LowRankArena: What Happens When You Force SVD
@@ -148,7 +152,8 @@ typedef struct lr_linear lr_linear;
  * and its decode layout when decode applies.
  * Errors: INVALID_ARG (null/size/alignment, exclusive flags together),
  * UNSUPPORTED (no gfx950 device, unknown flags, FORCE_DECODE with
- * max_M > 16, DENSE with a W above 2 GiB), OUT_OF_MEMORY, HIP.
+ * max_M > 16, DENSE with a W above 2 GiB, a decode launch whose workgroups
+ * cannot all be resident at once), OUT_OF_MEMORY, HIP.
  */
 lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N,
                            const void* A, const void* B, int64_t max_M, uint32_t flags);
@@ -180,8 +185,10 @@ lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, v
  * ("FlashSVD v1.5: Making Low-Rank Transformers Inference Actually Fast",
  * abstract: packed MLP execution).  Computes
  *     Y_gate = (X.A_gate).B_gate   and   Y_up = (X.A_up).B_up
- * in the same launch(es), reading each tile of X once for both GEMM1s.
- * Same as lr_group_run with n = 2 and handles {gate, up}.
+ * as lr_group_run with n = 2 and handles {gate, up}: at M > 16 the tiles of
+ * both GEMM1s are dealt over the CUs in one prefill launch (each workgroup
+ * loads the X tile of its own output tile); at decode the two run in one
+ * launch where the kernel allows it (see lr_group_run).
  * gate and up must be distinct handles with equal K; their r and N may
  * differ.  M must not exceed either handle's max_M.  Y_gate and Y_up must
  * not overlap each other or any input.
@@ -209,11 +216,12 @@ lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const vo
  *   M  : rows, in [0, min max_M]; M == 0 returns LR_OK and launches nothing.
  * Projections that take the dense fallback's decode at this M share one
  * launch; factorized projections that take a decode kernel share decode
- * launches where their kernel allows it (the role-split kernels fill the
- * device and run one launch each); the others share one launch per
- * prefill GEMM, in which every output's tiles are dealt over the CUs
- * together (one launch per weight leading dimension mod 8 where the
- * one-wave kernel is cheaper that way).  Results equal n lr_linear_run
+ * launches where their kernel allows it: the resident and streaming
+ * kernels while the workgroups of all fit the device at once, the
+ * XCD-sliced kernel always (each projection takes a share of every XCD's
+ * compute units), the role-split kernels never (each fills the device).
+ * The others share one launch per prefill GEMM, in which every output's
+ * tiles are dealt over the CUs together.  Results equal n lr_linear_run
  * calls up to the order of fp32 additions (bitwise for the dense and
  * role-split decodes, whose per-output work does not depend on the
  * group).

@@ -36,6 +36,7 @@ LR_FLAG_DENSE = 32
 LR_FLAG_FACTORED = 64
 LR_FLAG_DECODE_SPLIT = 128
 LR_FLAG_DECODE_RESIDENT = 256
+LR_FLAG_DECODE_XCD = 512
 LR_FLAG_TEST_STALL = 1 << 30
 LR_DECODE_MAX_M = 16
 LR_GROUP_MAX = 4

@@ -53,6 +53,9 @@ SWEEP_K = 4096
 SWEEP_N = (4096, 3999)
 SWEEP_R = tuple(range(1000, 1101))
 SWEEP_M = (1, 512)
+# the strided subset a default benchmark run measures: stride 3, so every
+# residue of r mod 8 appears twice
+SWEEP_R_DEFAULT = tuple(range(1024, 1072, 3))
 
 
 def seed_base(workload_index: int, projection_index: int = 0) -> int:

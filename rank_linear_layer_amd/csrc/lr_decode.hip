@@ -30,8 +30,6 @@
 
 namespace lrk {
 
-constexpr uint32_t kSpinLimit = 1u << 22;
-
 // Optional phase timestamps (constant-rate device clock), compiled in only
 // with -DLR_DECODE_TRACE; used to see where a launch spends its time.  They
 // are held in scalar registers and stored when the kernel ends, so that no
@@ -281,10 +279,10 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
     if (w == 0) {
       uint32_t spins = 0;
       while (true) {
-        const bool ok = ld_agent_u32(P.tflag + js) == epoch;
+        const bool ok = ld_agent_u32(P.tflag + js) == (epoch ^ P.stall_xor);
         if (ok) break;
-        if (++spins > kSpinLimit) {
-          if (l == 0) st_agent_u32(P.ctrl + 2, 1u);
+        if (++spins > P.spin_limit) {
+          if (l == 0) raise_stall(P.ctrl, P.err);
           break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -403,6 +401,9 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
 }
 
 hipError_t launch_decode(const DecArgs& args, int grid, hipStream_t stream) {
+  static std::atomic<uint64_t> occ{0};
+  const hipError_t e = check_coresident((const void*)lr_decode_fused_kernel, kDecThreads, 0, grid, occ);
+  if (e != hipSuccess || args.check_only) return e;
   hipLaunchKernelGGL(lr_decode_fused_kernel, dim3(grid), dim3(kDecThreads), 0, stream, args);
   return hipGetLastError();
 }

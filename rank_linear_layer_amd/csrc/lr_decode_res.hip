@@ -48,7 +48,6 @@ namespace lrk {
 
 namespace {
 
-constexpr uint32_t kResSpinLimit = 1u << 22;
 // Byte offset past the end of every buffer range used here: the load
 // returns zeros (and writes them to LDS) without any branch.
 constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
@@ -399,11 +398,11 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
       for (int i = l; i < P.S; i += 64) {
         const uint32_t f = P.xcd_local ? buf_load_u32_l2(rW, tflag_grp + (uint32_t)i * 4u)
                                        : buf_load_u32_coherent(rW, tflag_grp + (uint32_t)i * 4u);
-        ok = ok && (f == epoch);
+        ok = ok && (f == (epoch ^ P.stall_xor));
       }
       if (__all(ok)) break;
-      if (++spins > kResSpinLimit) {
-        if (l == 0) st_agent_u32(P.ctrl + 2, 1u);
+      if (++spins > P.spin_limit) {
+        if (l == 0) raise_stall(P.ctrl, P.err);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -503,8 +502,8 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
         bool ok = true;
         for (int i = l; i < P.Jw; i += 64) ok = ok && (buf_load_u32_coherent(rW, yflag_grp + (uint32_t)i * 4u) == epoch);
         if (__all(ok)) break;
-        if (++spins > kResSpinLimit) {
-          if (l == 0) st_agent_u32(P.ctrl + 2, 1u);
+        if (++spins > P.spin_limit) {
+          if (l == 0) raise_stall(P.ctrl, P.err);
           break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -545,10 +544,10 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
 
 hipError_t launch_decode_res(const DecArgs& args, int grid, hipStream_t stream) {
   static std::atomic<uint64_t> attr_done{0};
-  {
-    const hipError_t e = ensure_dynamic_lds((const void*)lr_decode_res_kernel, kResLdsBytes, attr_done);
-    if (e != hipSuccess) return e;
-  }
+  static std::atomic<uint64_t> occ{0};
+  hipError_t e = ensure_dynamic_lds((const void*)lr_decode_res_kernel, kResLdsBytes, attr_done);
+  if (e == hipSuccess) e = check_coresident((const void*)lr_decode_res_kernel, kResThreads, kResLdsBytes, grid, occ);
+  if (e != hipSuccess || args.check_only) return e;
   hipLaunchKernelGGL(lr_decode_res_kernel, dim3(grid), dim3(kResThreads), kResLdsBytes, stream, args);
   return hipGetLastError();
 }

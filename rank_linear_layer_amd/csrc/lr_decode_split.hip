@@ -51,8 +51,9 @@
 // captured graph can replay a launch.  In the first variant T producers
 // have the lowest ids and never wait, so it completes even when not every
 // workgroup is resident at once; the other two assume all G workgroups
-// are (one per CU), and every spin gives up after kSpSpinLimit rounds,
-// raising ctrl[2].
+// are (one per CU; the launcher refuses a grid that does not fit), and
+// every spin gives up after spin_limit rounds, raising ctrl[2] and the
+// handle's pinned host word.
 #include "lr_device.h"
 #include "lr_kernels.h"
 
@@ -63,7 +64,6 @@ namespace {
 constexpr int kSpThreads = 512;  // 8 waves
 constexpr int kSpWaves = kSpThreads / 64;
 constexpr int kSpChunk = 16;     // A blocks in flight per wave at once
-constexpr uint32_t kSpSpinLimit = 1u << 22;
 #ifndef LR_SPLIT_SLEEP
 #define LR_SPLIT_SLEEP 1  // s_sleep units (64 clocks) between flag polls
 #endif
@@ -199,8 +199,9 @@ __device__ __forceinline__ void t_producer(const SplitArgs& a, int j, uint32_t e
 
 // Wave 0 spins until the 32-bit words [first, first + count) of `r` all
 // equal `want` (and, when `count_too`, ctrl[1] equals `count_want`), with
-// device-coherent loads.  Gives up after kSpSpinLimit rounds and raises the
-// timeout flag.
+// device-coherent loads.  Gives up after spin_limit rounds and raises the
+// timeout flags.  The flag words are compared with want ^ stall_xor (see
+// SplitArgs).
 __device__ __forceinline__ void spin_until(const SplitArgs& a, rsrc_t r, int first, int count, uint32_t want,
                                            bool count_too, uint32_t count_want, int lane) {
   const rsrc_t rC = make_rsrc(a.ctrl, 8);
@@ -209,12 +210,12 @@ __device__ __forceinline__ void spin_until(const SplitArgs& a, rsrc_t r, int fir
     bool ok = true;
     for (int i = lane; i < count; i += 64) {
       const uint32_t off = (uint32_t)(first + i) * 4u;
-      ok = ok && (buf_load_u32_coherent(r, off) == want);
+      ok = ok && (buf_load_u32_coherent(r, off) == (want ^ a.stall_xor));
     }
     if (count_too && lane == 0) ok = ok && (buf_load_u32_coherent(rC, 4u) == count_want);
     if (__all(ok)) break;
-    if (++spins > kSpSpinLimit) {
-      if (lane == 0) st_agent_u32(a.ctrl + 2, 1u);
+    if (++spins > a.spin_limit) {
+      if (lane == 0) raise_stall(a.ctrl, a.err);
       break;
     }
     __builtin_amdgcn_s_sleep(LR_SPLIT_SLEEP);
@@ -604,8 +605,8 @@ __device__ __forceinline__ void t_flat(const SplitArgs& a, int wg, uint32_t epoc
           bool ok = true;
           for (int q = 1 + l; q < n; q += 64) ok = ok && (buf_load_u32_coherent(rPF, (uint32_t)(j * a.maxc + q) * 4u) == epoch);
           if (__all(ok)) break;
-          if (++spins > kSpSpinLimit) {
-            if (l == 0) st_agent_u32(a.ctrl + 2, 1u);
+          if (++spins > a.spin_limit) {
+            if (l == 0) raise_stall(a.ctrl, a.err);
             break;
           }
           __builtin_amdgcn_s_sleep(LR_SPLIT_SLEEP);
@@ -690,8 +691,11 @@ __global__ __launch_bounds__(kSpThreads) void lr_decode_splits_kernel(const Spli
 template <int NB, bool XAL, bool TWO>
 hipError_t launch_splits_variant(const SplitArgs& a, hipStream_t stream) {
   static std::atomic<uint64_t> attr_done{0};
-  const hipError_t e = ensure_dynamic_lds((const void*)lr_decode_splits_kernel<NB, XAL, TWO>, kSpWaves * NB * 1024, attr_done);
-  if (e != hipSuccess) return e;
+  static std::atomic<uint64_t> occ{0};
+  hipError_t e = ensure_dynamic_lds((const void*)lr_decode_splits_kernel<NB, XAL, TWO>, kSpWaves * NB * 1024, attr_done);
+  if (e == hipSuccess)
+    e = check_coresident((const void*)lr_decode_splits_kernel<NB, XAL, TWO>, kSpThreads, (size_t)kSpWaves * NB * 1024, a.G, occ);
+  if (e != hipSuccess || a.check_only) return e;
   hipLaunchKernelGGL((lr_decode_splits_kernel<NB, XAL, TWO>), dim3((unsigned)a.G), dim3(kSpThreads),
                      (size_t)kSpWaves * NB * 1024, stream, a);
   return hipGetLastError();
@@ -729,8 +733,11 @@ __global__ __launch_bounds__(kSpThreads) void lr_decode_splitf_kernel(const Spli
 template <int NB, bool XAL, bool TWO>
 hipError_t launch_splitf_variant(const SplitArgs& a, hipStream_t stream) {
   static std::atomic<uint64_t> attr_done{0};
-  const hipError_t e = ensure_dynamic_lds((const void*)lr_decode_splitf_kernel<NB, XAL, TWO>, kSpWaves * NB * 1024, attr_done);
-  if (e != hipSuccess) return e;
+  static std::atomic<uint64_t> occ{0};
+  hipError_t e = ensure_dynamic_lds((const void*)lr_decode_splitf_kernel<NB, XAL, TWO>, kSpWaves * NB * 1024, attr_done);
+  if (e == hipSuccess)
+    e = check_coresident((const void*)lr_decode_splitf_kernel<NB, XAL, TWO>, kSpThreads, (size_t)kSpWaves * NB * 1024, a.G, occ);
+  if (e != hipSuccess || a.check_only) return e;
   hipLaunchKernelGGL((lr_decode_splitf_kernel<NB, XAL, TWO>), dim3((unsigned)a.G), dim3(kSpThreads),
                      (size_t)kSpWaves * NB * 1024, stream, a);
   return hipGetLastError();
@@ -739,10 +746,11 @@ hipError_t launch_splitf_variant(const SplitArgs& a, hipStream_t stream) {
 template <int NB, bool XAL>
 hipError_t launch_split_variant(const SplitArgs& a, size_t lds, hipStream_t stream) {
   static std::atomic<uint64_t> attr_done{0};
-  {
-    const hipError_t e = ensure_dynamic_lds((const void*)lr_decode_split_kernel<NB, XAL>, (int)kSplitMaxTBytes, attr_done);
-    if (e != hipSuccess) return e;
-  }
+  static std::atomic<uint64_t> occ{0};
+  hipError_t e = ensure_dynamic_lds((const void*)lr_decode_split_kernel<NB, XAL>, (int)kSplitMaxTBytes, attr_done);
+  if (e == hipSuccess)
+    e = check_coresident((const void*)lr_decode_split_kernel<NB, XAL>, kSpThreads, lds, (int64_t)a.GA + a.GB, occ);
+  if (e != hipSuccess || a.check_only) return e;
   hipLaunchKernelGGL((lr_decode_split_kernel<NB, XAL>), dim3((unsigned)(a.GA + a.GB)), dim3(kSpThreads), lds, stream, a);
   return hipGetLastError();
 }

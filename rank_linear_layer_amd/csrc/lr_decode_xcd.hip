@@ -41,8 +41,8 @@
 // itself out in ctrl[1] when done; the last one resets the count and stores
 // the epoch as the next generation, so no host-side clearing is needed and a
 // captured graph can replay the launch.  The launch assumes all of its
-// workgroups are resident at once (one per compute unit; the host checks the
-// occupancy at create), and each wait gives up after spin_limit polls,
+// workgroups are resident at once (one per compute unit; the launcher refuses
+// a grid that does not fit), and each wait gives up after spin_limit polls,
 // raising ctrl[2] and the host-visible error word instead of hanging.
 #include "lr_device.h"
 #include "lr_kernels.h"
@@ -249,15 +249,12 @@ __device__ __forceinline__ XcdProj opaque_proj(const XcdProj& s) {
   P.db = opq(s.db);
   P.ldtp = opq(s.ldtp);
   P.ws = opq(s.ws);
-  P.withhold = opq(s.withhold);
+  P.stall_xor = (uint32_t)opq((int)s.stall_xor);
   return P;
 }
 
 // Raise the timeout flags of projection p (device word and host word).
-__device__ __forceinline__ void raise_timeout(const XcdProj& P) {
-  st_agent_u32(P.ctrl + 2, 1u);
-  if (P.err) __hip_atomic_store(P.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
+__device__ __forceinline__ void raise_timeout(const XcdProj& P) { raise_stall(P.ctrl, P.err); }
 
 // One wave spins until the `count` words of `r` at word offsets
 // first + stride * i (i < count <= 64) all equal `want`.  Gives up after
@@ -472,12 +469,12 @@ __global__ __launch_bounds__(kXThreads) void lr_decode_xcd_kernel(const XcdArgs 
     wait_vmem_all();  // the partial is visible before its flag
     XT(10);
     barrier_all();
-    if (w == 0 && l == 0 && wg != P.withhold) xstore_u32(loc, rFL, (uint32_t)(fl1 + x * P.pa + ia) * 4u, epoch);
+    if (w == 0 && l == 0) xstore_u32(loc, rFL, (uint32_t)(fl1 + x * P.pa + ia) * 4u, epoch);
     XT(3);
     // every partial of the XCD's A workgroups is in: this one sums columns
     // [ia RW / pa, (ia + 1) RW / pa) of the range over the ks slabs in slab
     // order (lane = column, rows in quads) and publishes them
-    if (w == 0) spin_flags(P, rFL, fl1 + x * P.pa, 1, P.pa, epoch, loc, spin_limit, l);
+    if (w == 0) spin_flags(P, rFL, fl1 + x * P.pa, 1, P.pa, epoch ^ P.stall_xor, loc, spin_limit, l);
     barrier_all();
     XT(4);
     {
@@ -724,8 +721,10 @@ hipError_t launch_decode_xcd(const XcdArgs& a, int lds_bytes, hipStream_t stream
     total += P.pn;
   }
   if (total * 8 != a.grid) return hipErrorInvalidValue;
-  const hipError_t e = ensure_dynamic_lds((const void*)lr_decode_xcd_kernel, kXcdMaxLds, attr_done);
-  if (e != hipSuccess) return e;
+  static std::atomic<uint64_t> occ{0};
+  hipError_t e = ensure_dynamic_lds((const void*)lr_decode_xcd_kernel, kXcdMaxLds, attr_done);
+  if (e == hipSuccess) e = check_coresident((const void*)lr_decode_xcd_kernel, kXThreads, (size_t)lds_bytes, a.grid, occ);
+  if (e != hipSuccess || a.check_only) return e;
   hipLaunchKernelGGL(lr_decode_xcd_kernel, dim3((unsigned)a.grid), dim3(kXThreads), (size_t)lds_bytes, stream, a);
   return hipGetLastError();
 }

@@ -277,6 +277,13 @@ __device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
 __device__ __forceinline__ uint32_t add_agent_u32(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A cross-workgroup wait gave up: raise the device timeout word ctrl[2] and,
+// when the handle has one, the pinned host word `err` (system scope, so the
+// host sees it without a device synchronisation).
+__device__ __forceinline__ void raise_stall(uint32_t* ctrl, uint32_t* err) {
+  st_agent_u32(ctrl + 2, 1u);
+  if (err) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // accesses (lgkmcnt = 0) and meets the other waves, without waiting for
 // global loads or stores still in flight.  (__syncthreads() also drains the

@@ -23,6 +23,42 @@ inline hipError_t ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<
   return e;
 }
 
+// Kernels whose workgroups wait on one another complete only when every
+// workgroup of the grid is resident at once.  True when `grid` workgroups of
+// `kernel` (`threads` each, `lds` bytes of dynamic LDS) fit the current
+// device together: the occupancy calculator's workgroups per compute unit
+// times the compute units.  The last answer is cached per kernel instance
+// in `cache` (device, LDS bytes, capacity), so a launch pays for the query
+// only when one of them changes.
+inline hipError_t check_coresident(const void* kernel, int threads, size_t lds, int64_t grid,
+                                   std::atomic<uint64_t>& cache) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t key = ((uint64_t)(dev & 0xFF) << 56) | ((uint64_t)(lds & 0xFFFFFF) << 32);
+  uint64_t c = cache.load(std::memory_order_acquire);
+  if ((c & 0x80000000u) == 0 || (c & ~(uint64_t)0xFFFFFFFFu) != key) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t cap = (int64_t)per_cu * cus;
+    c = key | 0x80000000u | (uint64_t)(cap < 0x7FFFFFFF ? cap : 0x7FFFFFFF);
+    cache.store(c, std::memory_order_release);
+  }
+  return grid <= (int64_t)(c & 0x7FFFFFFFu) ? hipSuccess : hipErrorCooperativeLaunchTooLarge;
+}
+
+// Bounded waits.  Every cross-workgroup wait of the decode kernels gives up
+// after `spin_limit` polls; it then raises the handle's device word ctrl[2]
+// and stores 1 to `err`, a word of pinned host memory that the host library
+// reads before the handle's next call.  `stall_xor` is XORed into the flag
+// value the T hand-off waits for: zero in normal use; a test sets its top
+// bit, so that this wait can never succeed and must give up while every
+// workgroup still runs to its end.
+constexpr uint32_t kStallXor = 0x80000000u;
+
 // ---------------------------------------------------------------- decode ---
 // Tile geometry of the fused decode kernel (M <= 16).
 constexpr int kDecThreads = 256;  // 4 waves
@@ -56,12 +92,15 @@ struct DecProj {
   int js_w;       // rank columns per slice
   int xcd_local;  // workgroups are dealt to XCDs round-robin (verified) and wg_begin % 8 == 0:
                   // resident kernel: rank-slice groups share an XCD; streaming: adjacent slices do
+  uint32_t* err;  // pinned host word set to 1 when a wait gives up (null: none)
+  uint32_t spin_limit, stall_xor;
 };
 
 struct DecArgs {
   const uint16_t* X;
   uint64_t* trace;  // per-workgroup phase timestamps (builds with LR_DECODE_TRACE only)
-  int M, K, nproj, pad_;
+  int M, K, nproj;
+  int check_only;   // the launcher validates and checks residency, and launches nothing
   DecProj p[kDecMaxProj];
 };
 constexpr int kDecTracePoints = 16;
@@ -125,6 +164,9 @@ struct SplitArgs {
   float* part;          // [GA][maxc] tiles of 16 x 16 fp32
   uint32_t* pflags;     // [GA][maxc] epoch stamps of the partial tiles
   int maxc;             // contributors per slice the table holds (>= ceil(nkA / max(1, TB / G)) + 1)
+  uint32_t* err;        // pinned host word set to 1 when a wait gives up (null: none)
+  uint32_t spin_limit, stall_xor;
+  int check_only;       // the launcher validates and checks residency, and launches nothing
 };
 hipError_t launch_decode_split(const SplitArgs& args, hipStream_t stream);
 // B blocks per wave of a Y producer for this plan (<= kSplitMaxBlocks to launch).
@@ -158,7 +200,7 @@ struct XcdProj {
   int cpr_a, cpr_b;   // 16-byte chunks per LDS row of an A piece / of a B chunk (even)
   int da, db;         // k-steps in flight per wave of an A / a B workgroup
   int ldtp, ws;       // rank range (>= ceil(r/8)) and slab (>= ceil(N/(pn - pa))) lengths of the tables
-  int withhold;       // test hook: this workgroup never stamps its partial-T flag (-1: none)
+  uint32_t stall_xor; // XORed into the value the partial-T wait expects (a test sets kStallXor)
 };
 struct XcdArgs {
   const uint16_t* X;  // [M x K] bf16
@@ -167,6 +209,7 @@ struct XcdArgs {
   int xcd_local;      // 1: the T exchange runs through each XCD's L2 (workgroup placement verified)
   uint32_t spin_limit;
   uint64_t* trace;    // phase timestamps (builds with LR_DECODE_TRACE only)
+  int check_only;     // the launcher validates and checks residency, and launches nothing
   XcdProj p[kXcdMaxProj];
 };
 hipError_t launch_decode_xcd(const XcdArgs& args, int lds_bytes, hipStream_t stream);

@@ -109,7 +109,7 @@ struct lr_linear {
   float* xtfin;
   float* xypart;
   uint32_t spin_limit;  // polls before a cross-workgroup wait gives up
-  int withhold;         // LR_FLAG_TEST_STALL: workgroup that never publishes its partial T (-1: none)
+  uint32_t stall_xor;   // LR_FLAG_TEST_STALL: kStallXor (the T hand-off wait cannot succeed), else 0
   // pinned host word that a decode kernel raises when one of its waits gave
   // up; the next call on the handle (or lr_linear_status) reports it
   uint32_t* err_host;
@@ -151,6 +151,9 @@ lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
   p.ktps = h->dp.ktps;
   p.ntps = h->dp.ntps;
   p.wg_begin = wg_begin;
+  p.err = h->err_dev;
+  p.spin_limit = h->spin_limit;
+  p.stall_xor = h->stall_xor;
   return p;
 }
 
@@ -210,8 +213,13 @@ lr_status run_dense_decode(const lr_linear* const* hs, uint16_t* const* Ys, int 
 
 static_assert(lrk::kSplitMaxBlocks == 16 && lrk::kSplitMaxTBytes == 144 * 1024,
               "the split plan (decode_split_partition defaults) matches the kernel's limits");
-lr_status run_split_decode(const lr_linear* h, uint16_t* Y, const void* X, int64_t M, hipStream_t stream) {
+lr_status run_split_decode(const lr_linear* h, uint16_t* Y, const void* X, int64_t M, hipStream_t stream,
+                           bool check_only = false) {
   lrk::SplitArgs a;
+  a.err = h->err_dev;
+  a.spin_limit = h->spin_limit;
+  a.stall_xor = h->stall_xor;
+  a.check_only = check_only ? 1 : 0;
   a.X = (const uint16_t*)X;
   a.Asw = h->Asw;
   a.Bsw = h->Bsw;
@@ -243,6 +251,9 @@ lr_status run_split_decode(const lr_linear* h, uint16_t* Y, const void* X, int64
   a.pflags = h->pflags;
   a.maxc = h->dp.maxc;
   const hipError_t e = lrk::launch_decode_split(a, stream);
+  if (e == hipErrorCooperativeLaunchTooLarge)
+    return fail(LR_ERR_UNSUPPORTED, "split decode: %d workgroups cannot all be resident at once on this device",
+                a.stream_y ? a.G : a.GA + a.GB);
   if (e != hipSuccess) return hip_fail(e, "split decode launch");
   return LR_OK;
 }
@@ -273,7 +284,7 @@ int xcd_share(int n, int rank_by_bytes) {
 // the others; a quarter each for four).  Returns LR_ERR_UNSUPPORTED (with no
 // launch) when some handle has no plan for its share.
 lr_status run_xcd_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool check_only = false) {
   int rank[lrk::kXcdMaxProj] = {0, 0, 0, 0};
   for (int i = 0; i < n; ++i)
     for (int j = 0; j < n; ++j) {
@@ -286,6 +297,7 @@ lr_status run_xcd_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n,
   a.M = (int)M;
   a.K = (int)hs[0]->K;
   a.nproj = n;
+  a.check_only = check_only ? 1 : 0;
   a.xcd_local = 1;
   a.spin_limit = hs[0]->spin_limit;
 #ifdef LR_DECODE_TRACE
@@ -326,7 +338,7 @@ lr_status run_xcd_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n,
     P.db = pl.db;
     P.ldtp = pl.ldtp;
     P.ws = pl.ws;
-    P.withhold = h->withhold;
+    P.stall_xor = h->stall_xor;
     p0 += pl.pn;
     lds = lds > pl.lds ? lds : pl.lds;
     a.xcd_local = a.xcd_local && h->xcd_local;
@@ -336,15 +348,17 @@ lr_status run_xcd_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n,
   if (force_coherent) a.xcd_local = 0;
   a.grid = 8 * p0;
   const hipError_t e = lrk::launch_decode_xcd(a, (int)lds, stream);
+  if (e == hipErrorCooperativeLaunchTooLarge)
+    return fail(LR_ERR_UNSUPPORTED, "xcd decode: %d workgroups cannot all be resident at once on this device", a.grid);
   if (e != hipSuccess) return hip_fail(e, "xcd decode launch");
   return LR_OK;
 }
 
 lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
-                     hipStream_t stream) {
+                     hipStream_t stream, bool check_only = false) {
   if (hs[0]->dp.kind == 5) {
     for (int i = 0; i < n; ++i) {
-      const lr_status st = run_xcd_decode(hs + i, Ys + i, 1, X, M, stream);
+      const lr_status st = run_xcd_decode(hs + i, Ys + i, 1, X, M, stream, check_only);
       if (st == LR_ERR_UNSUPPORTED) return fail(st, "no XCD-sliced decode plan for this handle");
       if (st != LR_OK) return st;
     }
@@ -352,7 +366,7 @@ lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, con
   }
   if (hs[0]->dp.kind >= 2) {
     for (int i = 0; i < n; ++i) {
-      const lr_status st = run_split_decode(hs[i], Ys[i], X, M, stream);
+      const lr_status st = run_split_decode(hs[i], Ys[i], X, M, stream, check_only);
       if (st != LR_OK) return st;
     }
     return LR_OK;
@@ -360,6 +374,7 @@ lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, con
   lrk::DecArgs a;
   memset(&a, 0, sizeof a);
   a.X = (const uint16_t*)X;
+  a.check_only = check_only ? 1 : 0;
 #ifdef LR_DECODE_TRACE
   a.trace = g_trace;
 #endif
@@ -372,6 +387,8 @@ lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, con
     wg += hs[i]->dp.Jw * hs[i]->dp.S;
   }
   hipError_t e = hs[0]->dp.kind == 1 ? lrk::launch_decode_res(a, wg, stream) : lrk::launch_decode(a, wg, stream);
+  if (e == hipErrorCooperativeLaunchTooLarge)
+    return fail(LR_ERR_UNSUPPORTED, "decode: %d workgroups cannot all be resident at once on this device", wg);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return LR_OK;
 }
@@ -724,10 +741,9 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
   size_t o_ctrl = 0, o_tcnt = 0, o_tflag = 0, o_ycnt = 0, o_tpart = 0, o_tfin = 0, o_ypart = 0, o_tbuf = 0;
   size_t o_sflags = 0, o_tsp = 0, o_asw = 0, o_bsw = 0, o_fpart = 0, o_pflags = 0;
   if (h->has_decode) h->dec_max_M = (int)(max_M < LR_DECODE_MAX_M ? max_M : LR_DECODE_MAX_M);
-  h->withhold = (flags & LR_FLAG_TEST_STALL) ? 0 : -1;
+  h->stall_xor = (flags & LR_FLAG_TEST_STALL) ? lrk::kStallXor : 0u;
   h->spin_limit = (flags & LR_FLAG_TEST_STALL) ? 2048u : (1u << 22);
-  const uint32_t decode_kind_flags = LR_FLAG_DECODE_STREAMING | LR_FLAG_DECODE_RESIDENT | LR_FLAG_DECODE_SPLIT;
-  if (h->has_decode && !h->dense && !(flags & decode_kind_flags)) {
+  if (h->has_decode && !h->dense && (flags & LR_FLAG_DECODE_XCD)) {
     // the XCD-sliced kernel: one workgroup per compute unit, all resident at
     // once (its workgroups wait on one another), so the occupancy of its
     // largest plan must allow at least one per compute unit
@@ -920,6 +936,24 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     h->off_ypart = (uint32_t)o_ypart;
     h->off_tflag = (uint32_t)o_tflag;
   }
+  if (h->has_decode && !h->dense) {
+    // The decode kernels' workgroups wait on one another, so a launch
+    // completes only if all of them are resident at once: every launch this
+    // handle makes alone is checked against the occupancy of its kernel
+    // (M = 1 and the largest M select different variants), with nothing
+    // launched.  The pointers below are never dereferenced.
+    static uint16_t probe;
+    const lr_linear* self = h;
+    uint16_t* yprobe = &probe;
+    const int64_t ms[2] = {1, h->dec_max_M};
+    for (int64_t m : ms) {
+      const lr_status cst = run_decode(&self, &yprobe, 1, &probe, m, nullptr, true);
+      if (cst != LR_OK) {
+        discard(h);
+        return cst;
+      }
+    }
+  }
   if (h->has_prefill) {
     h->Tbuf = h->dense ? nullptr : (uint16_t*)(base + o_tbuf);
     h->part = h->part_bytes > 0 ? (float*)(base + o_part) : nullptr;
@@ -999,18 +1033,18 @@ lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const vo
 
 void lr_linear_destroy(lr_linear* h) {
   if (!h) return;
-  if (h->ws) {
+  if (h->ws || h->err_host) {
     // A handle may be released (e.g. by a garbage collector) while another
-    // stream captures a graph.  hipFree is not allowed under a global-mode
-    // capture and would invalidate it; in relaxed mode this thread's free
-    // leaves other captures alone.  (The caller must not free a handle that
-    // a graph being captured or replayed still uses.)
+    // stream captures a graph.  hipFree and hipHostFree are not allowed
+    // under a global-mode capture and would invalidate it; in relaxed mode
+    // this thread's frees leave other captures alone.  (The caller must not
+    // free a handle that a graph being captured or replayed still uses.)
     hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
     const bool swapped = hipThreadExchangeStreamCaptureMode(&mode) == hipSuccess;
-    (void)hipFree(h->ws);
+    if (h->ws) (void)hipFree(h->ws);
+    if (h->err_host) (void)hipHostFree(h->err_host);
     if (swapped) (void)hipThreadExchangeStreamCaptureMode(&mode);
   }
-  if (h->err_host) (void)hipHostFree(h->err_host);
   delete h;
 }
 

@@ -51,7 +51,7 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
   }
   const uint32_t known = LR_FLAG_FORCE_DECODE | LR_FLAG_FORCE_PREFILL | LR_FLAG_DECODE_STREAMING |
                          LR_FLAG_PREFILL_TWO_WAVE | LR_FLAG_PREFILL_ONE_WAVE | LR_FLAG_DENSE | LR_FLAG_FACTORED |
-                         LR_FLAG_DECODE_SPLIT | LR_FLAG_DECODE_RESIDENT | LR_FLAG_TEST_STALL;
+                         LR_FLAG_DECODE_SPLIT | LR_FLAG_DECODE_RESIDENT | LR_FLAG_DECODE_XCD | LR_FLAG_TEST_STALL;
   if (flags & ~known) { snprintf(err, errlen, "unknown flag bits 0x%x", flags & ~known); return LR_ERR_UNSUPPORTED; }
   if ((flags & LR_FLAG_FORCE_DECODE) && (flags & LR_FLAG_FORCE_PREFILL)) {
     snprintf(err, errlen, "FORCE_DECODE and FORCE_PREFILL are exclusive");
@@ -62,9 +62,10 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
     return LR_ERR_INVALID_ARG;
   }
   {
-    const uint32_t dk = flags & (LR_FLAG_DECODE_STREAMING | LR_FLAG_DECODE_SPLIT | LR_FLAG_DECODE_RESIDENT);
+    const uint32_t dk =
+        flags & (LR_FLAG_DECODE_STREAMING | LR_FLAG_DECODE_SPLIT | LR_FLAG_DECODE_RESIDENT | LR_FLAG_DECODE_XCD);
     if (dk & (dk - 1)) {
-      snprintf(err, errlen, "DECODE_STREAMING, DECODE_SPLIT and DECODE_RESIDENT are exclusive");
+      snprintf(err, errlen, "DECODE_STREAMING, DECODE_SPLIT, DECODE_RESIDENT and DECODE_XCD are exclusive");
       return LR_ERR_INVALID_ARG;
     }
   }

@@ -49,7 +49,7 @@ def run_case(M, K, r, N, seed, flags=0, max_M=None, full=True, rows=None, cols=N
 
 # ------------------------------------------------------------ workloads ---
 
-DECODE_KERNELS = [0, lrl.LR_FLAG_DECODE_STREAMING, lrl.LR_FLAG_DECODE_RESIDENT]
+DECODE_KERNELS = [0, lrl.LR_FLAG_DECODE_STREAMING, lrl.LR_FLAG_DECODE_RESIDENT, lrl.LR_FLAG_DECODE_XCD]
 
 
 @pytest.mark.parametrize("M", [1, 8, 16])
@@ -747,7 +747,7 @@ def test_split_variants_graph_replay(gpu, M, K, r, N, kind):
     torch = gpu
     banner("graph replay %s M=%d K=%d r=%d N=%d" % (kind, M, K, r, N))
     _, Ab, Bb = datagen.factorized_inputs(1, K, r, N, 8300 + r)
-    extra = 0 if kind == "xcd" else lrl.LR_FLAG_DECODE_SPLIT
+    extra = lrl.LR_FLAG_DECODE_XCD if kind == "xcd" else lrl.LR_FLAG_DECODE_SPLIT
     lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=lrl.LR_FLAG_FACTORED | extra)
     assert "kind=%s " % kind in lin.describe(), lin.describe()
     X1 = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
@@ -802,3 +802,41 @@ def test_handle_released_during_capture(gpu):
     g.replay()
     torch.cuda.synchronize()
     assert_parity(to_bits(Y), oracle.lowrank_bf16(Xb, A, B), "after a release during capture")
+
+
+@pytest.mark.parametrize("flag,kinds", [(0, ("resident", "streaming")), (lrl.LR_FLAG_DECODE_STREAMING, ("streaming",)),
+                                        (lrl.LR_FLAG_DECODE_SPLIT, ("split", "split_stream", "split_flat")),
+                                        (lrl.LR_FLAG_DECODE_XCD, ("xcd",))])
+def test_stalled_wait_is_reported(gpu, flag, kinds):
+    # LR_FLAG_TEST_STALL makes the T hand-off wait of every decode launch
+    # expect a value nobody stores, with a short spin limit: each launch's
+    # waits give up, every workgroup still runs to its end, and the handle
+    # reports LR_ERR_HIP once, on the next call or through lr_linear_status.
+    # A second handle on the same factors, used before and after, is
+    # unaffected and stays correct.
+    torch = gpu
+    M, K, r, N = 4, 1024, 300, 1000
+    banner("stall report flags=%d" % flag)
+    Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 8800 + flag % 97)
+    A, B, X = to_dev(Ab), to_dev(Bb), to_dev(Xb)
+    ref = oracle.lowrank_bf16(Xb, Ab, Bb)
+    good = lrl.LowRankLinear(A, B, max_M=M, flags=lrl.LR_FLAG_FACTORED | flag)
+    bad = lrl.LowRankLinear(A, B, max_M=M, flags=lrl.LR_FLAG_FACTORED | flag | lrl.LR_FLAG_TEST_STALL)
+    kind = bad.describe().split("kind=")[1].split()[0]
+    assert kind in kinds, bad.describe()
+    assert_parity(to_bits(good(X)), ref, "before the stall")
+    assert bad.status() == lrl.LR_OK
+    bad(X)                      # enqueued; its waits give up on the device
+    torch.cuda.synchronize()    # and the launch ends
+    assert bad.status() == lrl.LR_ERR_HIP
+    assert "gave up waiting" in lrl.load_library().lr_last_error().decode()
+    assert bad.status() == lrl.LR_OK   # reported once
+    bad(X)
+    torch.cuda.synchronize()
+    with pytest.raises(lrl.LRError) as ei:
+        bad(X)                  # the report comes back from the next call, which launches nothing
+    assert ei.value.status == lrl.LR_ERR_HIP
+    assert bad.status() == lrl.LR_OK
+    for _ in range(2):
+        assert_parity(to_bits(good(X)), ref, "after the stall")
+    assert good.status() == lrl.LR_OK

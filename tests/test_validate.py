@@ -81,6 +81,14 @@ void t_prefill_plan(long long rows, long long c0, long long c1, int nout, long l
   lrv::PrePlan p = lrv::prefill_plan(rows, cols, nout, kd, cus, 32, kinds, q_aligned != 0);
   out[0] = p.nb; out[1] = p.splits; out[2] = p.split_steps; out[3] = p.kind;
 }
+int t_xcd_plan(long long K, long long r, long long N, int pn, long long max_M, long long* out) {
+  lrv::XcdPlan p{};
+  const bool ok = lrv::xcd_plan(K, r, N, pn, max_M, &p);
+  const long long v[14] = {p.pn, p.pa, p.rs, p.nc, p.cpr_a, p.cpr_b, p.da, p.db, p.ldtp, p.ws,
+                           (long long)p.lds, (long long)p.tpart_bytes, (long long)p.tfin_bytes, (long long)p.ypart_bytes};
+  for (int i = 0; i < 14; ++i) out[i] = v[i];
+  return ok ? 1 : 0;
+}
 long long t_partial_bytes(long long max_M, long long K, long long r_pad, long long N, int cus) {
   return lrv::prefill_partial_bytes(max_M, K, r_pad, N, cus);
 }
@@ -107,6 +115,7 @@ def shim(tmp_path_factory):
     lib.t_partition.argtypes = [ll, ll, ll, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.t_prefill_plan.argtypes = [ll, ll, ll, ctypes.c_int, ll, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.POINTER(ctypes.c_int)]
+    lib.t_xcd_plan.argtypes = [ll, ll, ll, ctypes.c_int, ll, ctypes.POINTER(ll)]
     lib.t_partial_bytes.argtypes = [ll, ll, ll, ll, ctypes.c_int]
     lib.t_partial_bytes.restype = ll
     return lib
@@ -153,7 +162,10 @@ def test_create_validation(shim):
     assert shim.t_check_create(4096, 1637, 4096, 0, 0x2000000, 16, 0) == INVALID
     assert shim.t_check_create(4096, 0, 4096, 0x100000, 0x2000000, 16, 0) == INVALID
     assert shim.t_check_create(4096, 1637, 4096, 0x100008, 0x2000000, 16, 0) == INVALID  # 8B aligned only
-    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 512) == UNSUPPORTED  # unknown flag
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 1024) == UNSUPPORTED  # unknown flag
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 512) == OK  # DECODE_XCD
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 512 | 128) == INVALID  # XCD | SPLIT
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 512 | 4) == INVALID  # XCD | STREAMING
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 256) == OK  # DECODE_RESIDENT
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 384) == INVALID  # SPLIT | RESIDENT
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 260) == INVALID  # STREAMING | RESIDENT
@@ -474,3 +486,51 @@ def test_prefill_partial_bytes_cover_every_plan(shim):
                         nb, splits, steps, kind = _plan(shim, M, cols, kd, kinds=kinds, q_aligned=qa)
                         if splits > 1:
                             assert splits * M * (-(-cols[0] // 4) * 4) * 4 <= have, (max_M, M, cols, kd, splits)
+
+
+def _xcd(shim, K, r, N, pn, max_M):
+    out = (ctypes.c_longlong * 14)()
+    ok = shim.t_xcd_plan(K, r, N, pn, max_M, out)
+    keys = ["pn", "pa", "rs", "nc", "cpr_a", "cpr_b", "da", "db", "ldtp", "ws", "lds", "tpart", "tfin", "ypart"]
+    return bool(ok), dict(zip(keys, out))
+
+
+def _inst(cpr):
+    # 64-lane DMA instructions per 32-row k-step tile with rows of cpr + 1 chunks
+    return (32 * (cpr + 1) + 63) // 64
+
+
+@pytest.mark.parametrize("K,r,N", [(4096, 1637, 4096), (4096, 2867, 14336), (14336, 2867, 4096), (1024, 300, 1000),
+                                   (4096, 1024, 4096), (4096, 1063, 3999), (2048, 7, 33), (333, 2049, 77)])
+@pytest.mark.parametrize("pn", [8, 16, 32])
+@pytest.mark.parametrize("max_M", [1, 8, 16])
+def test_xcd_plan_covers_and_fits(shim, K, r, N, pn, max_M):
+    ok, p = _xcd(shim, K, r, N, pn, max_M)
+    if not ok:
+        return
+    rw = -(-r // 8)
+    assert 1 <= p["pa"] < pn and p["pa"] % p["rs"] == 0 and p["rs"] & (p["rs"] - 1) == 0
+    sub = -(-rw // p["rs"])                      # rank columns of one A workgroup's sub-range
+    assert 8 * p["cpr_a"] >= sub and p["cpr_a"] % 2 == 0 and p["cpr_a"] <= 32
+    assert p["ws"] * (pn - p["pa"]) >= N         # the B slabs cover N
+    assert p["nc"] in (1, 2, 4, 8) and 8 * p["cpr_b"] * p["nc"] >= p["ws"] and p["cpr_b"] <= 32
+    assert p["ldtp"] >= rw and p["lds"] <= 160 * 1024
+    assert p["da"] >= 1 and p["da"] * (_inst(p["cpr_a"]) + 1) <= 62
+    assert p["db"] >= 1 and p["db"] * _inst(p["cpr_b"]) <= 62
+    colb = 16 * -(-max_M // 4)
+    assert p["tfin"] == 8 * p["ldtp"] * colb
+    assert p["ypart"] == 8 * (pn - p["pa"]) * p["ws"] * colb
+
+
+def test_xcd_plan_layer_shapes(shim):
+    # every projection of the layer has a plan for the whole device and for
+    # half of it (two projections sharing a launch)
+    for K, r, N in [(4096, 1637, 4096), (4096, 2867, 14336), (14336, 2867, 4096)]:
+        for pn in (32, 16):
+            ok, p = _xcd(shim, K, r, N, pn, 8)
+            assert ok, (K, r, N, pn)
+    ok, p = _xcd(shim, 4096, 1637, 4096, 32, 8)
+    assert (p["pa"], p["rs"], p["nc"]) == (16, 1, 1)
+    # too few workgroups for the up-projection's B slab
+    assert not _xcd(shim, 4096, 2867, 14336, 8, 1)[0]
+    assert not _xcd(shim, 4096, 1637, 4096, 1, 1)[0]
