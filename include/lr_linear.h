@@ -233,6 +233,35 @@ lr_status lr_group_run(const lr_linear* const* hs, int n, const void* X, void* c
                        int64_t M, void* stream);
 
 /*
+ * lr_decode_noalloc -- Y[M x N] = (X[M x K] . A[K x r]) . B[r x N] for
+ * M <= 16, with no handle and without allocating anything: for callers that
+ * cannot call hipMalloc (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It runs the decode kernel that
+ * lr_linear_create + lr_linear_run choose by default for max_M = M
+ * (LDS-resident or register-streaming, reading A and B in place), with that
+ * kernel's exchange tables in a fixed 32 MiB device array inside the
+ * library instead of a handle's workspace.
+ *   X, A, B, Y : device pointers, bf16 row-major, as for lr_linear_run
+ *                (16-byte aligned bases; Y must not overlap the inputs).
+ *   M          : rows, in [0, 16]; 0 returns LR_OK and launches nothing.
+ *   status     : optional device pointer (4-byte aligned) to a word the
+ *                caller owns and clears: a wait of the launch that gives up
+ *                (see Errors) stores 1 there.  NULL: not reported.
+ *   stream     : hipStream_t as void* (NULL = default stream).
+ * Each call enqueues a small clearing kernel and the decode kernel; it
+ * calls no hipMalloc, hipFree or other allocating routine.  Every call on a
+ * GPU uses that GPU's one array, which keeps the last call's contents:
+ * calls that overlap in time on one GPU (different streams, or threads)
+ * race and give wrong results; calls in stream order are safe.  The array
+ * is the device's for the life of the process.
+ * Errors: INVALID_ARG (null pointer, sizes, misaligned base, overlap,
+ * M > 16), UNSUPPORTED (a shape whose tables exceed the 32 MiB array, or
+ * whose launch cannot be resident at once), HIP (launch failure).
+ */
+lr_status lr_decode_noalloc(const void* X, const void* A, const void* B, void* Y, int64_t M,
+                            int64_t K, int64_t r, int64_t N, uint32_t* status, void* stream);
+
+/*
  * lr_linear_status -- LR_ERR_HIP (once, with a detail in lr_last_error) if a
  * decode launch of this handle gave up waiting for another of its
  * workgroups since the last report (see Errors), else LR_OK.  Reads a pinned

@@ -52,6 +52,7 @@ EXPORTED_SYMBOLS = (
     "lr_linear_describe",
     "lr_linear_workspace_bytes",
     "lr_linear_status",
+    "lr_decode_noalloc",
     "lr_gac_select",
 )
 
@@ -101,6 +102,8 @@ def load_library(path: str | None = None):
         lib.lr_linear_workspace_bytes.restype = i64
         lib.lr_linear_status.argtypes = [vp]
         lib.lr_linear_status.restype = ctypes.c_int
+        lib.lr_decode_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp]
+        lib.lr_decode_noalloc.restype = ctypes.c_int
         P = ctypes.POINTER
         lib.lr_gac_select.argtypes = [ctypes.c_int, P(ctypes.c_double), P(i64), P(ctypes.c_double),
                                       P(ctypes.c_int), P(i64), i64, i64, P(i64), P(ctypes.c_double)]
@@ -256,6 +259,29 @@ def group_run(projs, X, outs=None, stream=None):
     st = load_library().lr_group_run(hs, n, ctypes.c_void_p(X.data_ptr()), ys, X.shape[0], _stream_ptr(stream))
     _check(st, "lr_group_run")
     return outs
+
+
+def decode_noalloc(X, A, B, out, status=None, stream=None):
+    """Y = (X.A).B for M <= 16 through lr_decode_noalloc: no handle and no
+    allocation inside the library (the caller passes every buffer).
+    `status`: optional int32 GPU tensor of one element that a wait which
+    gave up sets to 1."""
+    for t, name in ((X, "X"), (A, "A"), (B, "B"), (out, "out")):
+        _require_bf16_cuda(t, name)
+    M, K = X.shape
+    if A.shape[0] != K or B.shape[0] != A.shape[1] or tuple(out.shape) != (M, B.shape[1]):
+        raise ValueError("shapes X %s, A %s, B %s, out %s do not chain" % (tuple(X.shape), tuple(A.shape),
+                                                                            tuple(B.shape), tuple(out.shape)))
+    st_ptr = None
+    if status is not None:
+        if not status.is_cuda or status.element_size() != 4 or status.numel() < 1:
+            raise ValueError("status must be a GPU tensor of 32-bit words")
+        st_ptr = ctypes.c_void_p(status.data_ptr())
+    st = load_library().lr_decode_noalloc(ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(A.data_ptr()),
+                                          ctypes.c_void_p(B.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                          M, K, A.shape[1], B.shape[1], st_ptr, _stream_ptr(stream))
+    _check(st, "lr_decode_noalloc")
+    return out
 
 
 def status_name(status: int) -> str:

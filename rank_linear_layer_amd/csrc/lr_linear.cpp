@@ -98,7 +98,7 @@ struct lr_linear {
   int nrep, ldf;       // replicas of T and of its flags; flag words per replica
   float* fpart;        // flat variant: partial tiles [GA][maxc] of 16 x 16 fp32
   uint32_t* pflags;    // flat variant: their flags
-  // XCD-sliced decode (dp.kind 5, the default): plans for xcd_P, xcd_P / 2
+  // XCD-sliced decode (dp.kind 5, LR_FLAG_DECODE_XCD): plans for xcd_P, xcd_P / 2
   // and xcd_P / 4 workgroups per XCD (alone in a launch, or one of two, or
   // of three or four projections sharing X), and their exchange tables
   int xcd_P;
@@ -177,6 +177,36 @@ bool xcd_map_ok(int device) {
   if (device < 0 || device >= 64) return false;
   if (cached[device] < 0) cached[device] = lrk::xcd_round_robin(1024) ? 1 : 0;
   return cached[device] == 1;
+}
+
+// Byte offsets of the in-place decode kernels' regions (LDS-resident and
+// register-streaming, dp.kind 1 and 0) in a workspace whose decode part
+// starts at `off`.  The control words (ctrl, counters, flags) come first and
+// end where the fp32 tables begin (`tpart`).
+struct InplaceLayout {
+  size_t ctrl, tcnt, tflag, yflag, ycnt, tpart, tfin, ypart, end;
+};
+InplaceLayout inplace_layout(const lrv::DecPart& dp, int max_M, size_t off) {
+  const int64_t G = (int64_t)dp.Jw * dp.S;
+  InplaceLayout L;
+  L.ctrl = off;
+  off = align_up(off + 64);
+  L.tcnt = off;
+  off = align_up(off + (size_t)dp.Jw * 4);
+  L.tflag = off;
+  off = align_up(off + (size_t)G * 4);  // one flag per workgroup (resident kernel) or per slice
+  L.yflag = off;
+  off = align_up(off + (size_t)G * 4);
+  L.ycnt = off;
+  off = align_up(off + (size_t)dp.S * 4);
+  L.tpart = off;
+  off = align_up(off + (size_t)G * max_M * (dp.kind == 1 ? 128 : dp.js_w) * 4);
+  L.tfin = off;
+  off = align_up(off + (size_t)dp.Jw * max_M * dp.js_w * 4);
+  L.ypart = off;
+  off = align_up(off + (size_t)G * dp.ntps * max_M * dp.nt_w * 4);
+  L.end = off;
+  return L;
 }
 
 int num_cus(int device) {
@@ -685,6 +715,38 @@ lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, cons
   return LR_OK;
 }
 
+// ------------------------------------------------- allocation-free decode ---
+// lr_decode_noalloc keeps the in-place decode kernels' exchange tables in
+// this file-scope device array instead of a handle's workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  Host code
+// never uses the array's name as an address: its device address is taken
+// once per device with hipGetSymbolAddress and cached in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on `dev` (nullptr and an error on failure).
+lr_status scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(LR_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LR_OK;
+}
+
+// Zeroes n 32-bit words (a kernel rather than hipMemsetAsync, so that the
+// clear is an ordinary kernel node when the caller captures a graph).
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -820,23 +882,16 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     off = align_up(off + (size_t)h->dp.gn * lrv::ceil_div(r, 32) * 1024);
     h->dws_bytes = (int64_t)off;
   } else if (h->has_decode && !h->dense) {
-    const int64_t G = (int64_t)h->dp.Jw * h->dp.S;
-    o_ctrl = off;
-    off = align_up(off + 64);
-    o_tcnt = off;
-    off = align_up(off + (size_t)h->dp.Jw * 4);
-    o_tflag = off;
-    off = align_up(off + (size_t)G * 4);  // one flag per workgroup (resident kernel) or per slice
-    h->off_yflag = (uint32_t)off;
-    off = align_up(off + (size_t)G * 4);
-    o_ycnt = off;
-    off = align_up(off + (size_t)h->dp.S * 4);
-    o_tpart = off;
-    off = align_up(off + (size_t)G * h->dec_max_M * (h->dp.kind == 1 ? 128 : h->dp.js_w) * 4);
-    o_tfin = off;
-    off = align_up(off + (size_t)h->dp.Jw * h->dec_max_M * h->dp.js_w * 4);
-    o_ypart = off;
-    off = align_up(off + (size_t)G * h->dp.ntps * h->dec_max_M * h->dp.nt_w * 4);
+    const InplaceLayout L = inplace_layout(h->dp, h->dec_max_M, off);
+    o_ctrl = L.ctrl;
+    o_tcnt = L.tcnt;
+    o_tflag = L.tflag;
+    h->off_yflag = (uint32_t)L.yflag;
+    o_ycnt = L.ycnt;
+    o_tpart = L.tpart;
+    o_tfin = L.tfin;
+    o_ypart = L.ypart;
+    off = L.end;
     // resident kernel: its T exchange runs through one XCD's L2, so every
     // rank-slice group must sit on one XCD (Jw a multiple of 8); streaming
     // kernel: only a traffic-saving placement of adjacent rank slices
@@ -996,6 +1051,69 @@ lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, v
   if (use_decode(h, M) && h->dense) return run_dense_decode(hs, Ys, 1, X, M, (hipStream_t)stream);
   if (use_decode(h, M)) return run_decode(hs, Ys, 1, X, M, (hipStream_t)stream);
   return run_prefill(hs, Ys, 1, X, M, (hipStream_t)stream);
+}
+
+lr_status lr_decode_noalloc(const void* X, const void* A, const void* B, void* Y, int64_t M, int64_t K, int64_t r,
+                            int64_t N, uint32_t* status, void* stream) {
+  lr_status st = lrv::check_create(K, r, N, A, B, M, LR_FLAG_FACTORED, g_err, sizeof g_err);
+  if (st != LR_OK) return st;
+  if (M > LR_DECODE_MAX_M) return fail(LR_ERR_INVALID_ARG, "M=%lld: this entry point takes M <= %d", (long long)M, LR_DECODE_MAX_M);
+  lrv::Shape s{K, r, N, M, A, B};
+  st = lrv::check_run(s, X, Y, M, g_err, sizeof g_err);
+  if (st != LR_OK || M == 0) return st;
+  if (status && reinterpret_cast<uintptr_t>(status) % 4 != 0) return fail(LR_ERR_INVALID_ARG, "status must be 4-byte aligned");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  // the plan lr_linear_create makes by default for max_M = M, on a handle
+  // that lives on this stack frame and points into the scratch array
+  lr_linear h{};
+  h.K = K;
+  h.r = r;
+  h.N = N;
+  h.max_M = M;
+  h.flags = LR_FLAG_FORCE_DECODE | LR_FLAG_FACTORED;
+  h.device = dev;
+  h.A = (const uint16_t*)A;
+  h.B = (const uint16_t*)B;
+  h.has_decode = true;
+  h.dec_max_M = (int)M;
+  h.dp = lrv::decode_partition(K, r, N, num_cus(dev), lrk::decode_res_available(), false, M);
+  if (h.dp.kind != 0 && h.dp.kind != 1) return fail(LR_ERR_UNSUPPORTED, "no in-place decode plan for this shape");
+  const InplaceLayout L = inplace_layout(h.dp, (int)M, 0);
+  if (L.end > kNoAllocScratchBytes)
+    return fail(LR_ERR_UNSUPPORTED, "this shape needs %zu bytes of decode scratch; the allocation-free entry point has %zu",
+                L.end, kNoAllocScratchBytes);
+  void* base = nullptr;
+  st = scratch_address(dev, &base);
+  if (st != LR_OK) return st;
+  char* b = (char*)base;
+  h.dws = b;
+  h.dws_bytes = (int64_t)L.end;
+  h.ctrl = (uint32_t*)(b + L.ctrl);
+  h.tcnt = (uint32_t*)(b + L.tcnt);
+  h.tflag = (uint32_t*)(b + L.tflag);
+  h.ycnt = (uint32_t*)(b + L.ycnt);
+  h.off_tpart = (uint32_t)L.tpart;
+  h.off_tfin = (uint32_t)L.tfin;
+  h.off_ypart = (uint32_t)L.ypart;
+  h.off_tflag = (uint32_t)L.tflag;
+  h.off_yflag = (uint32_t)L.yflag;
+  h.xcd_local = false;  // the placement check would allocate: exchange device-coherent
+  h.spin_limit = 1u << 22;
+  h.stall_xor = 0u;
+  h.err_dev = status;
+  // The array keeps the last call's contents, which may be another shape's
+  // tables: the control words (generation, counters, flags) start at zero
+  // every call, so no stale flag can match this call's epoch.
+  const int words = (int)(L.tpart / 4);
+  hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)((words + 255) / 256 < 64 ? (words + 255) / 256 : 64)), dim3(256), 0,
+                     (hipStream_t)stream, h.ctrl, words);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
+  const lr_linear* hs[1] = {&h};
+  uint16_t* Ys[1] = {(uint16_t*)Y};
+  return run_decode(hs, Ys, 1, X, M, (hipStream_t)stream);
 }
 
 lr_status lr_group_run(const lr_linear* const* hs, int n, const void* X, void* const* Ys, int64_t M, void* stream) {

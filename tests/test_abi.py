@@ -97,3 +97,16 @@ def test_python_binding_rejects_cpu_tensors():
         lrl.LowRankLinear(A, B, max_M=4)
     with pytest.raises(TypeError):
         lrl.LowRankLinear(A.float(), B, max_M=4)
+
+
+def test_noalloc_entry_point_validates_before_any_hip_call(lib):
+    fake = ctypes.c_void_p(0x1000)
+    y = ctypes.c_void_p(0x100000)
+    # M above the decode range, null input, zero-sized shape, misaligned factor
+    assert lib.lr_decode_noalloc(fake, fake, fake, y, 17, 8, 4, 8, None, None) == lrl.LR_ERR_INVALID_ARG
+    assert b"M <= 16" in lib.lr_last_error()
+    assert lib.lr_decode_noalloc(None, fake, fake, y, 1, 8, 4, 8, None, None) == lrl.LR_ERR_INVALID_ARG
+    assert lib.lr_decode_noalloc(fake, fake, fake, y, 1, 0, 4, 8, None, None) == lrl.LR_ERR_INVALID_ARG
+    assert lib.lr_decode_noalloc(fake, ctypes.c_void_p(0x1002), fake, y, 1, 8, 4, 8, None, None) == lrl.LR_ERR_INVALID_ARG
+    # M = 0 is a no-op that touches nothing
+    assert lib.lr_decode_noalloc(fake, fake, fake, y, 0, 8, 4, 8, None, None) == lrl.LR_OK
