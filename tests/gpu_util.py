@@ -34,3 +34,14 @@ def assert_parity(y_bits: np.ndarray, y_ref: np.ndarray, what: str):
 
 def banner(msg: str):
     print("[gpu-test] " + msg, flush=True)
+
+
+def tile_cover(n: int, block: int, seed: int, extra=()) -> np.ndarray:
+    """Sorted distinct indices of range(n): one at a seeded offset inside
+    every `block`-sized block (so every output tile of width >= block holds
+    at least one), the first and the last index, and `extra`."""
+    rng = np.random.default_rng(seed)
+    starts = np.arange(0, n, block)
+    picks = starts + rng.integers(0, np.minimum(block, n - starts))
+    ex = np.array([e for e in extra if 0 <= e < n], dtype=np.int64)
+    return np.unique(np.concatenate([picks, [0, n - 1], ex]).astype(np.int64))

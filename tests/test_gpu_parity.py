@@ -13,7 +13,7 @@ import pytest
 import oracle
 import rank_linear_layer_amd as lrl
 from rank_linear_layer_amd import configs, datagen
-from tests.gpu_util import assert_parity, banner, to_bits, to_dev
+from tests.gpu_util import assert_parity, banner, tile_cover, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -96,11 +96,19 @@ def test_qproj_decode_full(dflag):
     banner("q_proj decode parity %s plan %s" % (p, lin.describe()))
 
 
+# Prefill tiles are 256 rows by 192, 224 or 256 columns (phase 2) and the
+# k-split / tile walk differs per plan, so the sampled checks take one row in
+# every 256-row block and one column in every 128-column block (every output
+# tile holds at least one sampled element), plus tile edges and the ragged end.
+def _cover(M, N, seed):
+    rows = tile_cover(M, 256, seed, extra=(1, 255, 256, M - 2))
+    cols = tile_cover(N, 128, seed + 1, extra=(1, 191, 192, 223, 224, 255, 256, N - 2))
+    return rows, cols
+
+
 def test_mlp_up_prefill_sampled():
     c = configs.MLP_UP_PREFILL
-    rows = np.array([0, 1, 127, 128, 2047, 4094, 4095])
-    cols = np.unique(np.concatenate([np.arange(0, 20), np.arange(230, 250), np.arange(7000, 7010),
-                                     np.arange(14300, 14336)]))
+    rows, cols = _cover(c["M"], c["N"], 600)
     p, lin, _, _ = run_case(c["M"], c["K"], c["r"], c["N"], configs.seed_base(c["index"]), full=False,
                             rows=rows, cols=cols)
     banner("mlp_up prefill sampled parity %s plan %s" % (p, lin.describe()))
@@ -113,15 +121,13 @@ def test_layer_projections_decode_m1(name):
     run_case(1, proj.K, proj.r, proj.N, configs.seed_base(configs.LAYER_INDEX, idx))
 
 
-@pytest.mark.parametrize("name", ["q", "k", "down"])
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "gate", "up", "down"])
 def test_layer_projections_prefill_m2048_sampled(name):
-    # at M = 2048 these projections have fewer output tiles than compute
-    # units, so the prefill plan splits k (fp32 partials + reduction kernel)
+    # every projection of the bench's layer line at M = 2048 (q, k, o, down
+    # have fewer output tiles than compute units, so their plans split k)
     proj = {p.name: p for p in configs.LAYER_PROJS}[name]
     idx = [p.name for p in configs.LAYER_PROJS].index(name)
-    rows = np.array([0, 1, 255, 256, 1023, 2046, 2047])
-    cols = np.unique(np.concatenate([np.arange(0, 9), np.arange(190, 260), np.array([proj.N // 2]),
-                                     np.arange(proj.N - 9, proj.N)]))
+    rows, cols = _cover(2048, proj.N, 700 + idx)
     p, lin, _, _ = run_case(2048, proj.K, proj.r, proj.N, configs.seed_base(configs.LAYER_INDEX, idx), full=False,
                             rows=rows, cols=cols)
     banner("layer %s M=2048 sampled parity %s plan %s" % (name, p, lin.describe()))
@@ -131,8 +137,7 @@ def test_layer_projections_prefill_m2048_sampled(name):
 def test_alignment_sweep_points(N, r):
     seed = configs.sweep_seed(N, r)
     run_case(1, configs.SWEEP_K, r, N, seed)
-    rows = np.array([0, 255, 511])
-    cols = np.array([0, 1, 2, 119, 120, 121, 2000, N - 2, N - 1])
+    rows, cols = _cover(512, N, seed)
     run_case(512, configs.SWEEP_K, r, N, seed, full=False, rows=rows, cols=cols)
 
 
@@ -282,11 +287,8 @@ def test_group_qkv_m2048_sampled():
     Xb, fac = _layer_group(["q", "k", "v"], M)
     lins = [lrl.LowRankLinear(to_dev(A), to_dev(B), max_M=M) for A, B in fac]
     Ys = lrl.group_run(lins, to_dev(Xb))
-    rows = np.array([0, 1, 255, 256, 777, 1023, 1024, 2046, 2047])
-    for nm, Y, (A, B), lin in zip("qkv", Ys, fac, lins):
-        N = B.shape[1]
-        cols = np.unique(np.concatenate([np.arange(0, 9), np.arange(250, 260), np.array([N // 2]),
-                                         np.arange(N - 9, N)]))
+    for i, (nm, Y, (A, B), lin) in enumerate(zip("qkv", Ys, fac, lins)):
+        rows, cols = _cover(M, B.shape[1], 800 + i)
         y = to_bits(Y)
         p = assert_parity(y[np.ix_(rows, cols)], oracle.lowrank_bf16_sampled(Xb, A, B, rows, cols),
                           "group %s M=2048 sampled" % nm)
@@ -378,6 +380,47 @@ def test_mlp_packed_matches_oracle_and_separate_runs(M):  # noqa: C901
     assert_parity(yu, datagen.bf16_bits_to_f32(to_bits(up(X))).astype(np.float64), "packed vs separate up")
     Yg2, Yu2 = lrl.mlp_packed(gate, up, X)
     assert np.array_equal(yg, to_bits(Yg2)) and np.array_equal(yu, to_bits(Yu2))
+
+
+def _gate_up(M):
+    Xb, fac = _layer_group(["gate", "up"], M)
+    (Agb, Bgb), (Aub, Bub) = fac
+    return Xb, Agb, Bgb, Aub, Bub
+
+
+def test_mlp_packed_gate_up_m2048_sampled():
+    # the bench layer line's packed gate/up at M = 2048 (K 4096, r 2867,
+    # N 14336 each), every output tile sampled, against the oracle and
+    # against single calls of each handle
+    M = 2048
+    banner("packed gate/up M=%d" % M)
+    Xb, Agb, Bgb, Aub, Bub = _gate_up(M)
+    gate = lrl.LowRankLinear(to_dev(Agb), to_dev(Bgb), max_M=M)
+    up = lrl.LowRankLinear(to_dev(Aub), to_dev(Bub), max_M=M)
+    X = to_dev(Xb)
+    Yg, Yu = lrl.mlp_packed(gate, up, X)
+    for i, (nm, Y, A, B, lin) in enumerate((("gate", Yg, Agb, Bgb, gate), ("up", Yu, Aub, Bub, up))):
+        rows, cols = _cover(M, B.shape[1], 900 + i)
+        y = to_bits(Y)
+        p = assert_parity(y[np.ix_(rows, cols)], oracle.lowrank_bf16_sampled(Xb, A, B, rows, cols), "packed " + nm)
+        assert np.all(np.isfinite(datagen.bf16_bits_to_f32(y)))
+        ys = to_bits(lin(X))
+        assert_parity(y, datagen.bf16_bits_to_f32(ys).astype(np.float64), "packed vs single " + nm)
+        banner("packed %s M=2048 sampled parity %s plan %s" % (nm, p, lin.describe()))
+
+
+@pytest.mark.parametrize("flags", [0, lrl.LR_FLAG_DECODE_XCD, lrl.LR_FLAG_DECODE_SPLIT])
+@pytest.mark.parametrize("M", [1, 8])
+def test_mlp_packed_gate_up_layer_decode(flags, M):
+    # the bench layer line's packed gate/up at decode, full output against
+    # the oracle, for the default kernel and the two opt-in ones
+    banner("packed gate/up decode M=%d flags=%d" % (M, flags))
+    Xb, Agb, Bgb, Aub, Bub = _gate_up(M)
+    gate = lrl.LowRankLinear(to_dev(Agb), to_dev(Bgb), max_M=M, flags=flags | lrl.LR_FLAG_FACTORED)
+    up = lrl.LowRankLinear(to_dev(Aub), to_dev(Bub), max_M=M, flags=flags | lrl.LR_FLAG_FACTORED)
+    Yg, Yu = lrl.mlp_packed(gate, up, to_dev(Xb))
+    assert_parity(to_bits(Yg), oracle.lowrank_bf16(Xb, Agb, Bgb), "packed decode gate")
+    assert_parity(to_bits(Yu), oracle.lowrank_bf16(Xb, Aub, Bub), "packed decode up")
 
 
 # ----------------------------------------------------------- dense fallback ---
