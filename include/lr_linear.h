@@ -99,8 +99,8 @@ typedef struct lr_linear lr_linear;
 #define LR_FLAG_PREFILL_TWO_WAVE 8u  /* prefill only with the two-waves-per-SIMD kernel (tiles of
                                         256 x 192 or 224) instead of the cost model's choice */
 #define LR_FLAG_PREFILL_ONE_WAVE 16u /* prefill with the one-wave-per-SIMD kernel (256 x 256 tiles)
-                                        wherever it applies: X, or T, rows 16-byte aligned, and the
-                                        same leading dimension mod 8 for both factors of a pair */
+                                        wherever it applies: rows of its left operand (X, or T)
+                                        16-byte aligned, i.e. K a multiple of 8 for phase 1 */
 #define LR_FLAG_DENSE    32u  /* dense fallback: form W = A.B (bf16) at create and run Y = X.W */
 #define LR_FLAG_FACTORED 64u  /* never take the dense fallback */
 #define LR_FLAG_DECODE_SPLIT 128u  /* decode with the role-split kernel where its plan fits; it

@@ -202,17 +202,6 @@ __device__ __forceinline__ uint32_t xload_u32(bool local, rsrc_t r, uint32_t off
   return local ? load_u32<kSkipL1>(r, off) : load_u32<kCoherent>(r, off);
 }
 
-// Element e of a bf16 matrix through the scalar cache (wave-uniform e): the
-// dword holding it is read whole (it cannot cross a page, so even the 2
-// bytes past an odd-length matrix are safe to touch).  Scalar loads are
-// counted apart from the vector-memory counter, which the factor streams use.
-__device__ __forceinline__ uint32_t scalar_elem(const uint16_t* base, int64_t e) {
-  const uint64_t byte = (uint64_t)e * 2;
-  typedef __attribute__((address_space(4))) const uint32_t* cptr;
-  const uint32_t d = *(cptr)((const char*)base + (byte & ~(uint64_t)3));
-  return (byte & 2) ? (d >> 16) : (d & 0xFFFFu);
-}
-
 __device__ __forceinline__ int opq(int v) {
   asm volatile("" : "+s"(v));
   return v;

@@ -149,6 +149,21 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int64_t rounded = (bytes + 3) & ~(int64_t)3;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)rounded, kRsrcFlags);
 }
+// Element e of a bf16 matrix through the scalar cache (wave-uniform e): the
+// dword holding it is read whole (it cannot cross a page, so even the 2
+// bytes past an odd-length matrix are safe to touch).  Scalar loads are
+// counted apart from the vector-memory counter.  Used to patch a matrix's
+// last element where an unaligned 16-byte buffer load loses it: the range
+// check zeroes every dword that reaches past the range end, and a load that
+// starts 2 bytes past a dword boundary puts the last element of a matrix
+// ending on a dword boundary into such a dword.
+__device__ __forceinline__ uint32_t scalar_elem(const uint16_t* base, int64_t e) {
+  const uint64_t byte = (uint64_t)e * 2;
+  typedef __attribute__((address_space(4))) const uint32_t* cptr;
+  const uint32_t d = *(cptr)((const char*)base + (byte & ~(uint64_t)3));
+  return (byte & 2) ? (d >> 16) : (d & 0xFFFFu);
+}
+
 __device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }

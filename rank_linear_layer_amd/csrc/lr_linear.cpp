@@ -423,10 +423,8 @@ lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, con
   return LR_OK;
 }
 
-// One prefill phase: C_i = P_i . Q_i for the n outputs, then the k-split
-// reduction if the plan splits k.
 // The one-wave-per-SIMD kernel loads P straight into LDS (16-byte aligned
-// rows only) and is specialised on the weight leading dimension mod 8.
+// rows only); its weight loads take any row alignment.
 bool w4_operands(const lrk::PreOut& o) {
   return o.ldp % 8 == 0 && reinterpret_cast<uintptr_t>(o.P) % 16 == 0;
 }
@@ -446,11 +444,10 @@ lrv::PrePlan plan_launch(const lr_linear* const* hs, const lrk::PreArgs& a, int 
   const int cus = num_cus(hs[0]->device);
   int64_t cols[lrk::kPreMaxOut] = {};
   for (int i = 0; i < n; ++i) cols[i] = a.o[i].out_cols;
-  const bool q_aligned = a.o[0].ldq % 8 == 0;
-  lrv::PrePlan pl = lrv::prefill_plan(a.rows, cols, n, kd, cus, 32, kinds, q_aligned);
+  lrv::PrePlan pl = lrv::prefill_plan(a.rows, cols, n, kd, cus, 32, kinds);
   for (int i = 0; i < n && pl.splits > 1; ++i) {
     const int64_t need = (int64_t)pl.splits * a.rows * lrv::round_up(cols[i], 4) * 4;
-    if (need > hs[i]->part_bytes) pl = lrv::prefill_plan(a.rows, cols, n, kd, cus, 1, kinds, q_aligned);
+    if (need > hs[i]->part_bytes) pl = lrv::prefill_plan(a.rows, cols, n, kd, cus, 1, kinds);
   }
   return pl;
 }
@@ -458,54 +455,15 @@ lrv::PrePlan plan_launch(const lr_linear* const* hs, const lrk::PreArgs& a, int 
 lr_status launch_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, const lrv::PrePlan& pl, int phase,
                        hipStream_t stream, const char* what);
 
-// One prefill phase: C_i = P_i . Q_i for the n outputs, then the k-split
-// reduction if the plan splits k.  Outputs whose weights differ in leading
-// dimension mod 8 cannot share a one-wave launch; they run as one two-wave
-// launch or as one launch per residue class, whichever the cost model
-// prefers.
+// One prefill phase: C_i = P_i . Q_i for the n outputs in one launch (the
+// cost model's kernel and k-split for all of them together), then the
+// k-split reduction if the plan splits k.
 lr_status prefill_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, int64_t kd, int phase,
                         hipStream_t stream, const char* what) {
-  bool w4 = true, same_mod = true;
-  for (int i = 0; i < n; ++i) {
-    w4 = w4 && w4_operands(a.o[i]);
-    same_mod = same_mod && a.o[i].ldq % 8 == a.o[0].ldq % 8;
-  }
-  const int kinds_all = allowed_kinds(hs[0], w4);
-  const lrv::PrePlan joint = plan_launch(hs, a, n, kd, same_mod ? kinds_all : lrv::kPlanTwoWave);
-  if (same_mod || !(kinds_all & lrv::kPlanOneWave) || (hs[0]->flags & LR_FLAG_PREFILL_TWO_WAVE))
-    return launch_phase(hs, a, n, joint, phase, stream, what);
-  // residue classes of the weight leading dimension, in first-seen order
-  lrk::PreArgs sub[lrk::kPreMaxOut];
-  const lr_linear* sub_hs[lrk::kPreMaxOut][lrk::kPreMaxOut];
-  int64_t sub_kd[lrk::kPreMaxOut] = {};
-  int64_t mods[lrk::kPreMaxOut];
-  int ng = 0;
-  for (int i = 0; i < n; ++i) {
-    int g = 0;
-    while (g < ng && mods[g] != a.o[i].ldq % 8) ++g;
-    if (g == ng) {
-      mods[ng] = a.o[i].ldq % 8;
-      sub[ng] = a;
-      sub[ng].nout = 0;
-      ++ng;
-    }
-    sub_hs[g][sub[g].nout] = hs[i];
-    sub[g].o[sub[g].nout++] = a.o[i];
-    sub_kd[g] = sub_kd[g] > a.o[i].kd ? sub_kd[g] : a.o[i].kd;
-  }
-  lrv::PrePlan plans[lrk::kPreMaxOut];
-  double split_cost = 0;
-  for (int g = 0; g < ng; ++g) {
-    plans[g] = plan_launch(sub_hs[g], sub[g], sub[g].nout, sub_kd[g], kinds_all);
-    split_cost += plans[g].cost;
-  }
-  if (!(hs[0]->flags & LR_FLAG_PREFILL_ONE_WAVE) && joint.cost <= split_cost)
-    return launch_phase(hs, a, n, joint, phase, stream, what);
-  for (int g = 0; g < ng; ++g) {
-    const lr_status st = launch_phase(sub_hs[g], sub[g], sub[g].nout, plans[g], phase, stream, what);
-    if (st != LR_OK) return st;
-  }
-  return LR_OK;
+  bool w4 = true;
+  for (int i = 0; i < n; ++i) w4 = w4 && w4_operands(a.o[i]);
+  const lrv::PrePlan pl = plan_launch(hs, a, n, kd, allowed_kinds(hs[0], w4));
+  return launch_phase(hs, a, n, pl, phase, stream, what);
 }
 
 lr_status launch_phase(const lr_linear* const* hs, lrk::PreArgs& a, int n, const lrv::PrePlan& pl, int phase,
@@ -620,7 +578,7 @@ lr_status form_dense(lr_linear* h, uint16_t* W) {
   const bool w4 = w4_operands(o);
   const int kinds = lrv::kPlanTwoWave | (w4 ? lrv::kPlanOneWave : 0);
   const int64_t cols = h->N;
-  const lrv::PrePlan pl = lrv::prefill_plan(h->K, &cols, 1, h->r, num_cus(h->device), 1, kinds, h->N % 8 == 0);
+  const lrv::PrePlan pl = lrv::prefill_plan(h->K, &cols, 1, h->r, num_cus(h->device), 1, kinds);
   a.nb = pl.nb;
   a.splits = 1;
   a.split_steps = pl.split_steps;

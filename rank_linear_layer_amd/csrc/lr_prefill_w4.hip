@@ -11,16 +11,22 @@
 //    8 R + (c ^ ((R / 2) mod 8))) that keeps the MFMA operand reads free of
 //    bank conflicts.
 //  * The weight operand (A or B, output index contiguous) is read with
-//    aligned 16-byte loads into registers: lanes 0-31 take 32 consecutive
-//    chunks of one row, lanes 32-63 the same chunks 8 rows further.  A row
-//    that starts d elements past a 16-byte boundary (odd rank or width) is
-//    realigned in registers with the neighbouring lane's chunk (DPP wave
-//    shift) and a byte funnel shift; d depends only on the row modulo 8 and
-//    on the leading dimension modulo 8, which is a template argument.  Each
-//    lane then transposes its 8 rows x 8 columns block with v_perm_b32 and
-//    writes 8 operand vectors (8 k of one column) into the Qt slot, whose
-//    16-column groups are XOR-permuted so that both these writes and the
-//    MFMA reads are conflict free.
+//    16-byte loads into registers: lanes 0-31 take 32 consecutive chunks of
+//    one row, lanes 32-63 the same chunks 8 rows further.  Each load starts
+//    exactly at its 8 elements, wherever the row begins: gfx950's buffer
+//    loads return the 16 bytes at any 2-byte aligned offset (checked on
+//    MI355X, at the same streaming bandwidth as aligned loads), so an odd
+//    rank or width takes the same instructions as an aligned one and no
+//    code depends on the leading dimension modulo 8.  One exception, at the
+//    matrix's end: the buffer range check zeroes a dword that reaches past
+//    the range, so when the matrix ends on a dword boundary the lane whose
+//    load starts 2 bytes past one and covers the last element reads it as
+//    zero; that element is patched from a scalar load, in the stages whose
+//    rows can reach it only.  Each lane then
+//    transposes its 8 rows x 8 columns block with v_perm_b32 and writes 8
+//    operand vectors (8 k of one column) into the Qt slot, whose 16-column
+//    groups are XOR-permuted so that both these writes and the MFMA reads
+//    are conflict free.
 //  * Four waves, one per SIMD, each own a 128 x 128 quarter of the 256 x 256
 //    tile: 16 v_mfma_f32_32x32x16_bf16 accumulators (256 AGPRs), the largest
 //    wave tile the register file holds, which minimises LDS operand traffic
@@ -104,17 +110,6 @@ __device__ __forceinline__ void wait_vm() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Misalignment (elements) of weight row i of an 8-row group when the leading
-// dimension is QMOD modulo 8 (the group's first row and the tile's first
-// column are multiples of 8).
-__host__ __device__ constexpr int row_shift(int qmod, int i) { return (i * qmod) & 7; }
-template <int QMOD>
-__host__ __device__ constexpr int extra_loads() {
-  int n = 0;
-  for (int i = 0; i < 8; ++i) n += row_shift(QMOD, i) != 0;
-  return n;
-}
-
 // 16-column groups of Qt are permuted: column n sits at entry pos(n).
 __device__ __forceinline__ int qt_pos(int n) { return (n & ~15) | ((n & 15) ^ ((n >> 4) & 15)); }
 
@@ -162,33 +157,9 @@ __device__ __forceinline__ Tile map_tile(const PreArgs& a, int bid) {
   return T;
 }
 
-// Chunk j of a weight row and the following chunk (the next lane's, or `x`
-// for the last lane of each half), shifted down by d elements (d is a
-// constant after unrolling).
-__device__ __forceinline__ u32x4_t realign(const u32x4_t& lo, const u32x4_t& x, bool last, int d) {
-  if (d == 0) return lo;
-  const int q = d >> 1;
-  uint32_t cat[8];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    cat[t] = lo[t];
-    if (t <= q) {
-      const uint32_t nx = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo[t], 0x130, 0xf, 0xf, false);  // wave_shl:1
-      cat[4 + t] = last ? x[t] : nx;
-    } else {
-      cat[4 + t] = 0u;
-    }
-  }
-  u32x4_t o;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) o[t] = (d & 1) ? __builtin_amdgcn_alignbyte(cat[t + q + 1], cat[t + q], 2) : cat[t + q];
-  return o;
-}
-
-template <int QMOD, bool MASK>
+template <bool MASK>
 __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks, char* smem) {
-  constexpr int NX = extra_loads<QMOD>();
-  constexpr int NQ = 8 + NX;  // register loads per stage
+  constexpr int NQ = 8;  // register loads per stage
   const PreOut& O = a.o[T.bi];
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
@@ -225,57 +196,30 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
     for (int i = 0; i < 8; ++i) p_issue_one(smem + (st % kPSlots) * kPSlot, st, i);
   };
 
-  // ---- weight rows: lane (L, gL) loads chunk L of rows row0 + i (i < 8),
-  // row0 = k0 + 16w + 8gL; row0 * ldq + nb is a multiple of 8, so row i's
-  // first chunk is that of row 0 plus floor(i * ldq / 8)
+  // ---- weight rows: lane (L, gL) loads the 8 elements at columns
+  // nb + 8L .. + 7 of rows row0 + i (i < 8), row0 = k0 + 16w + 8gL, from
+  // wherever they start (any 2-byte offset)
   const int64_t row0 = k0 + 16 * w + 8 * gL;
   const uint32_t q_base = (uint32_t)(2 * (row0 * O.ldq + T.nb) + 16 * L);
   const uint32_t q_stride = (uint32_t)(128 * O.ldq);  // 64 rows
+  const uint32_t q_row = (uint32_t)(2 * O.ldq);        // 1 row
+  // the matrix's last element, where a load can lose it (see the top)
+  const int64_t q_elems = O.qrows * O.ldq;
+  const bool q_tail = (q_elems & 1) == 0;
+  const uint32_t q_end = (uint32_t)(2 * q_elems);
+  const uint32_t q_last = q_tail ? scalar_elem(O.Q, q_elems - 1) : 0u;
   // Two register sets for the weight rows alternate between stages (rows of
-  // stage s + 1 are realigned from one while the rows of stage s + 2 arrive
-  // in the other), so no loaded register is ever copied or reused while its
-  // load is in flight.  The chunk after a misaligned row is fetched with only
-  // the dwords the funnel shift reads.
+  // stage s + 1 are transposed from one while the rows of stage s + 2 arrive
+  // in the other), so no loaded register is ever reused while its load is
+  // in flight.
   struct QRegs {
-    u32x4_t v[8], x[8];
+    u32x4_t v[8];
   };
   QRegs qa, qb;
-  auto q_row_off = [&](int i, int st, bool& ok) {
-    ok = row0 + 64 * (int64_t)st + i < O.qrows;
-    return q_base + q_stride * (uint32_t)st + 16u * (uint32_t)((i * O.ldq) >> 3);
-  };
-  auto q_issue_row_main = [&](QRegs& q, int i, int st) {
-    bool ok;
-    const uint32_t off = q_row_off(i, st, ok);
-    q.v[i] = buf_load16(rQ, ok ? off : kOutOfRange);
-  };
-  auto q_issue_row_extra = [&](QRegs& q, int i, int st) {
-    const int d = row_shift(QMOD, i);
-    if (d == 0) return;
-    bool ok;
-    const uint32_t xo = q_row_off(i, st, ok) + 16u;
-    const uint32_t xoff = ok && L == 31 ? xo : kOutOfRange;
-    const int n = (d >> 1) + 1;  // dwords of the next chunk the shift reads
-    u32x4_t x = zerou4();
-    if (n == 1) {
-      x[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rQ, (int)xoff, 0, 0);
-    } else if (n == 2) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b64(rQ, (int)xoff, 0, 0);
-      x[0] = t[0];
-      x[1] = t[1];
-    } else if (n == 3) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b96(rQ, (int)xoff, 0, 0);
-      x[0] = t[0];
-      x[1] = t[1];
-      x[2] = t[2];
-    } else {
-      x = buf_load16(rQ, xoff);
-    }
-    q.x[i] = x;
-  };
   auto q_issue_row = [&](QRegs& q, int i, int st) {
-    q_issue_row_main(q, i, st);
-    q_issue_row_extra(q, i, st);
+    const bool ok = row0 + 64 * (int64_t)st + i < O.qrows;
+    const uint32_t off = q_base + q_stride * (uint32_t)st + q_row * (uint32_t)i;
+    q.v[i] = buf_load16(rQ, ok ? off : kOutOfRange);
   };
   auto q_issue = [&](QRegs& q, int st) {
 #pragma unroll
@@ -286,7 +230,20 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
   const int m7 = (L >> 1) & 7;
   const int qt_w0 = qt_c * 4096 + 16 * (16 * (L >> 1) + ((8 * (L & 1)) ^ (((L >> 1) & 15) & 8)));
   u32x4_t r[8];
-  auto q_realign_row = [&](const QRegs& q, int i) { r[i] = realign(q.v[i], q.x[i], L == 31, row_shift(QMOD, i)); };
+  auto q_take_row = [&](const QRegs& q, int i, int st) {
+    r[i] = q.v[i];
+    // wave-uniform: can a chunk of this wave's rows of stage st reach the
+    // last element?  (the furthest element is column nb + 255 of row rmax)
+    const int64_t rmax = k0 + 64 * (int64_t)st + 16 * w + 15;
+    if (q_tail && rmax * O.ldq + T.nb + 255 >= q_elems - 1) {
+      const uint32_t o = q_base + q_stride * (uint32_t)st + q_row * (uint32_t)i;
+      const bool lost = (o & 2u) && o < q_end && o + 16u > q_end;
+      const int j = (int)((q_end - 2u - o) >> 2);  // dword of the chunk holding the last element
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (lost && t == j) r[i][t] = q_last;
+    }
+  };
   // column e of the lane's block: 8 k of column 8L + e, into Qt slot `qt`
   auto q_store_col = [&](int e, char* qt) {
     const int t = e >> 1;
@@ -300,7 +257,7 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
   auto q_store = [&](const QRegs& q, int st) {
     char* qt = smem + kQtBase + (st & 1) * kQtSlot;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q_realign_row(q, i);
+    for (int i = 0; i < 8; ++i) q_take_row(q, i, st);
 #pragma unroll
     for (int e = 0; e < 8; ++e) q_store_col(e, qt);
   };
@@ -367,7 +324,7 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
   //   M0: the weight rows of stage s + 2 are requested into the register set
   //       stage s - 1 emptied;
   //   M1: the rows of stage s + 1 (requested during stage s - 1) are
-  //       realigned and transposed into Qt of s + 1;
+  //       transposed into Qt of s + 1;
   //   M2: the last reads of this stage's P slot and Qt;
   //   then P of s + 1 is awaited and the stage's one barrier met;
   //   M3: the first operands of stage s + 1 are read and P of stage s + 3 is
@@ -385,10 +342,7 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
       mf1(A0, B0, i);
       fence();
       if (i < 8) rd1(ps, qs, 1, A1, B1, i);
-      if ((i & 1) == 0)
-        q_issue_row_main(qout, i >> 1, s + 2);
-      else
-        q_issue_row_extra(qout, i >> 1, s + 2);
+      if ((i & 1) == 0) q_issue_row(qout, i >> 1, s + 2);
       fence();
     }
     W4_TRACE(1);
@@ -398,7 +352,7 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
       fence();
       if (i < 8) rd1(ps, qs, 2, A0, B0, i);
       if (i < 8)
-        q_realign_row(qin, i);
+        q_take_row(qin, i, s + 1);
       else
         q_store_col(i - 8, qt_next);
       fence();
@@ -533,27 +487,15 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
   W4_TRACE_TILE(3);
 }
 
-template <int QMOD>
 __global__ __launch_bounds__(kThreads, 1) void lr_prefill_w4_kernel(const PreArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tiles = a.row_tiles * total_col_tiles(a);
   const int ks = (int)blockIdx.x / tiles;
   const Tile T = map_tile(a, (int)blockIdx.x - ks * tiles);
   if (a.o[T.bi].ldq - T.nb < kBN)
-    w4_tile<QMOD, true>(a, T, ks, smem);
+    w4_tile<true>(a, T, ks, smem);
   else
-    w4_tile<QMOD, false>(a, T, ks, smem);
-}
-
-template <int QMOD>
-hipError_t launch_w4(const PreArgs& args, int grid, hipStream_t stream) {
-  static std::atomic<uint64_t> attr_done{0};
-  {
-    const hipError_t e = ensure_dynamic_lds((const void*)lr_prefill_w4_kernel<QMOD>, kLdsBytes, attr_done);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((lr_prefill_w4_kernel<QMOD>), dim3(grid), dim3(kThreads), kLdsBytes, stream, args);
-  return hipGetLastError();
+    w4_tile<false>(a, T, ks, smem);
 }
 
 }  // namespace
@@ -563,19 +505,11 @@ hipError_t launch_prefill_w4(const PreArgs& args, hipStream_t stream) {
   const int grid = ct * args.row_tiles * args.splits;
   if (grid <= 0) return hipSuccess;
   if (args.nb != 8 || args.split_steps % 2 != 0) return hipErrorInvalidValue;
-  const int qmod = (int)(args.o[0].ldq & 7);
-  for (int i = 1; i < args.nout; ++i)
-    if ((int)(args.o[i].ldq & 7) != qmod) return hipErrorInvalidValue;
-  switch (qmod) {
-    case 0: return launch_w4<0>(args, grid, stream);
-    case 1: return launch_w4<1>(args, grid, stream);
-    case 2: return launch_w4<2>(args, grid, stream);
-    case 3: return launch_w4<3>(args, grid, stream);
-    case 4: return launch_w4<4>(args, grid, stream);
-    case 5: return launch_w4<5>(args, grid, stream);
-    case 6: return launch_w4<6>(args, grid, stream);
-    default: return launch_w4<7>(args, grid, stream);
-  }
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t e = ensure_dynamic_lds((const void*)lr_prefill_w4_kernel, kLdsBytes, attr_done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lr_prefill_w4_kernel, dim3(grid), dim3(kThreads), kLdsBytes, stream, args);
+  return hipGetLastError();
 }
 
 }  // namespace lrk

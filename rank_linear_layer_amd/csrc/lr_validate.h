@@ -459,20 +459,23 @@ struct PrePlan {
   double cost;  // the model's cost of the plan
 };
 // Kernel, tile width and k-split for one prefill phase, from a cost model in
-// units of about 0.14 us (one 32-deep k-step of the two-wave kernel at nb = 7
-// is 8.55): rounds of the 256-CU machine times (k-steps per split x the
-// kernel's per-step cost + its per-tile cost: start-up, epilogue), plus the
-// partial write/read and reduction launch when k is split.  Measured on
-// MI355X: two-wave kernel nb = 6 7.9 and nb = 7 8.55 per step, 40 per tile
-// (80 with fp32 partials); one-wave kernel 5.9 per step when the weight
-// leading dimension is a multiple of 8 and 8.45 otherwise (rows realigned in
-// registers), 85 per tile (200 with fp32 partials), k-splits on 64-deep
-// stages.  `kinds`: bit 0 allows the two-wave kernel, bit 1 the one-wave
-// kernel (which needs a 16-byte aligned P).
+// units of about 0.14 us: rounds of the 256-CU machine times (k-steps per
+// split x the kernel's per-step cost + its per-tile cost: start-up,
+// epilogue), plus the partial write/read and reduction launch when k is
+// split.  Per 32-deep k-step of one tile, measured on MI355X at steady clocks
+// (MLP up-projection, M = 4096: 120 us for phase 1 with the two-wave kernel
+// at nb = 6, 1 round of 128 steps; 388 us for phase 2 at nb = 7 and 393 us
+// with the one-wave kernel, 4 rounds of 90 steps): two-wave nb = 6 6.75 and
+// nb = 7 7.7, 40 per tile (80 with fp32 partials); one-wave 7.8, 85 per tile
+// (200 with fp32 partials), k-splits on 64-deep stages.  No cost depends on the
+// weight's leading dimension (r or N) modulo 8: both kernels read misaligned
+// rows with the same instructions as aligned ones.  `kinds`: bit 0 allows
+// the two-wave kernel, bit 1 the one-wave kernel (which needs a 16-byte
+// aligned P: X with K mod 8 = 0, or T).
 constexpr int kPlanTwoWave = 1;
 constexpr int kPlanOneWave = 2;
 inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int64_t kd, int num_cus,
-                            int max_splits = 32, int kinds_allowed = kPlanTwoWave, bool q_aligned = false) {
+                            int max_splits = 32, int kinds_allowed = kPlanTwoWave) {
   const int64_t row_tiles = ceil_div(rows, 256);
   const int64_t nks = ceil_div(kd, 32);
   const int cus = num_cus > 0 ? num_cus : 1;
@@ -483,7 +486,7 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
   const struct {
     int nb, kind;
     double per_step, per_tile, per_tile_split;
-  } kinds[3] = {{8, 1, q_aligned ? 5.9 : 8.45, 85.0, 200.0}, {7, 0, 8.55, 40.0, 80.0}, {6, 0, 7.9, 40.0, 80.0}};
+  } kinds[3] = {{8, 1, 7.8, 85.0, 200.0}, {7, 0, 7.7, 40.0, 80.0}, {6, 0, 6.75, 40.0, 80.0}};
   for (const auto& kn : kinds) {
     if (!(kinds_allowed & (kn.kind == 1 ? kPlanOneWave : kPlanTwoWave))) continue;
     const int gran = kn.kind == 1 ? 2 : 1;
@@ -521,15 +524,13 @@ inline int64_t prefill_partial_bytes(int64_t max_M, int64_t K, int64_t r_pad, in
     const int64_t lo = m - 255 < hi ? m - 255 : hi;
     const int64_t c1 = r_pad, c2 = N;
     for (int kinds = 1; kinds <= 3; ++kinds) {
-      for (int qa = 0; qa < 2; ++qa) {
-        const int64_t cd = dense ? c2 : c1;
-        const PrePlan p1 = prefill_plan(lo, &cd, 1, K, num_cus, 32, kinds, qa != 0);
-        const PrePlan p2 = prefill_plan(lo, &c2, 1, dense ? K : r_pad, num_cus, 32, kinds, qa != 0);
-        const int64_t n1 = p1.splits > 1 ? p1.splits * hi * round_up(cd, 4) * 4 : 0;
-        const int64_t n2 = p2.splits > 1 ? p2.splits * hi * round_up(c2, 4) * 4 : 0;
-        need = need > n1 ? need : n1;
-        need = need > n2 ? need : n2;
-      }
+      const int64_t cd = dense ? c2 : c1;
+      const PrePlan p1 = prefill_plan(lo, &cd, 1, K, num_cus, 32, kinds);
+      const PrePlan p2 = prefill_plan(lo, &c2, 1, dense ? K : r_pad, num_cus, 32, kinds);
+      const int64_t n1 = p1.splits > 1 ? p1.splits * hi * round_up(cd, 4) * 4 : 0;
+      const int64_t n2 = p2.splits > 1 ? p2.splits * hi * round_up(c2, 4) * 4 : 0;
+      need = need > n1 ? need : n1;
+      need = need > n2 ? need : n2;
     }
     if (hi == max_M) break;
   }

@@ -382,6 +382,28 @@ def test_mlp_packed_matches_oracle_and_separate_runs(M):  # noqa: C901
     assert np.array_equal(yg, to_bits(Yg2)) and np.array_equal(yu, to_bits(Yu2))
 
 
+# The last element of A and of B, made large: a kernel that loses it (an
+# unaligned load that reaches past a matrix ending on a dword boundary reads
+# it as zero) misses the bar by far.  Shapes with K*r and r*N even and odd.
+LAST_SHAPES = [(300, 512, 259, 514), (64, 256, 258, 1001), (40, 1024, 97, 66), (33, 96, 255, 257)]
+
+
+@pytest.mark.parametrize("flags", [lrl.LR_FLAG_PREFILL_ONE_WAVE, lrl.LR_FLAG_PREFILL_TWO_WAVE, 0] + DECODE_KERNELS[1:])
+@pytest.mark.parametrize("M,K,r,N", LAST_SHAPES)
+def test_last_elements_count(M, K, r, N, flags):
+    if flags in DECODE_KERNELS:
+        M = min(M, 8)
+    banner("last elements M=%d K=%d r=%d N=%d flags=%d" % (M, K, r, N, flags))
+    Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 9500 + r)
+    Ab, Bb = Ab.copy(), Bb.copy()
+    Ab[-1, -1] = 0x4100  # bf16 8.0
+    Bb[-1, -1] = 0x4100
+    Xb = Xb.copy()
+    Xb[:, -1] = 0x3F80   # bf16 1.0: the last row of A reaches every output row
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=flags | lrl.LR_FLAG_FACTORED)
+    assert_parity(to_bits(lin(to_dev(Xb))), oracle.lowrank_bf16(Xb, Ab, Bb), "last elements flags=%d" % flags)
+
+
 def _gate_up(M):
     Xb, fac = _layer_group(["gate", "up"], M)
     (Agb, Bgb), (Aub, Bub) = fac

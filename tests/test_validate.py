@@ -76,9 +76,9 @@ void t_partition2(long long K, long long r, long long N, int budget, int allow_r
   out[4] = p.kind; out[5] = p.js_w; out[6] = p.nt_w;
 }
 void t_prefill_plan(long long rows, long long c0, long long c1, int nout, long long kd, int cus, int kinds,
-                    int q_aligned, int* out) {
+                    int* out) {
   const int64_t cols[2] = {c0, c1};
-  lrv::PrePlan p = lrv::prefill_plan(rows, cols, nout, kd, cus, 32, kinds, q_aligned != 0);
+  lrv::PrePlan p = lrv::prefill_plan(rows, cols, nout, kd, cus, 32, kinds);
   out[0] = p.nb; out[1] = p.splits; out[2] = p.split_steps; out[3] = p.kind;
 }
 int t_xcd_plan(long long K, long long r, long long N, int pn, long long max_M, long long* out) {
@@ -113,8 +113,7 @@ def shim(tmp_path_factory):
     lib.t_check_group.argtypes = [ctypes.c_int, P(ll), P(ll), P(ll), P(ull), P(ull), ull, P(ull), ll]
     lib.t_choose_dense.argtypes = [ll, ll, ll, ctypes.c_uint]
     lib.t_partition.argtypes = [ll, ll, ll, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
-    lib.t_prefill_plan.argtypes = [ll, ll, ll, ctypes.c_int, ll, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                   ctypes.POINTER(ctypes.c_int)]
+    lib.t_prefill_plan.argtypes = [ll, ll, ll, ctypes.c_int, ll, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.t_xcd_plan.argtypes = [ll, ll, ll, ctypes.c_int, ll, ctypes.POINTER(ll)]
     lib.t_partial_bytes.argtypes = [ll, ll, ll, ll, ctypes.c_int]
     lib.t_partial_bytes.restype = ll
@@ -422,10 +421,10 @@ def test_decode_partition_prefers_register_split_then_streaming_split(shim):
 TWO_WAVE, ONE_WAVE = 1, 2
 
 
-def _plan(shim, rows, cols, kd, cus=256, kinds=TWO_WAVE, q_aligned=False):
+def _plan(shim, rows, cols, kd, cus=256, kinds=TWO_WAVE):
     out = (ctypes.c_int * 4)()
     c = list(cols) + [0]
-    shim.t_prefill_plan(rows, c[0], c[1], len(cols), kd, cus, kinds, int(q_aligned), out)
+    shim.t_prefill_plan(rows, c[0], c[1], len(cols), kd, cus, kinds, out)
     return tuple(out)
 
 
@@ -439,10 +438,9 @@ PLAN_SHAPES = [
 
 
 @pytest.mark.parametrize("kinds", [TWO_WAVE, ONE_WAVE, TWO_WAVE | ONE_WAVE])
-@pytest.mark.parametrize("q_aligned", [False, True])
 @pytest.mark.parametrize("rows,cols,kd", PLAN_SHAPES)
-def test_prefill_plan_covers_k_and_fits(shim, rows, cols, kd, kinds, q_aligned):
-    nb, splits, steps, kind = _plan(shim, rows, cols, kd, kinds=kinds, q_aligned=q_aligned)
+def test_prefill_plan_covers_k_and_fits(shim, rows, cols, kd, kinds):
+    nb, splits, steps, kind = _plan(shim, rows, cols, kd, kinds=kinds)
     nks = -(-kd // 32)
     assert kind in (0, 1) and (kinds >> kind) & 1
     if kind == 0:
@@ -457,13 +455,26 @@ def test_prefill_plan_covers_k_and_fits(shim, rows, cols, kd, kinds, q_aligned):
 
 def test_prefill_plan_picks_by_cost(shim):
     both = TWO_WAVE | ONE_WAVE
-    # MLP up phase 2 (B rows aligned, 14336 wide): the one-wave kernel
-    assert _plan(shim, 4096, (14336,), 2880, kinds=both, q_aligned=True)[3] == 1
-    # MLP up phase 1 (A rows 2867 wide, misaligned): the two-wave kernel
-    assert _plan(shim, 4096, (2880,), 4096, kinds=both, q_aligned=False)[3] == 0
+    # MLP up, both phases (whatever r mod 8 is): the two-wave kernel, 192
+    # columns wide for phase 1 (240 tiles: one round), 224 for phase 2 (1024
+    # tiles: four full rounds, where the one-wave kernel's 896 leave the
+    # last round half empty)
+    assert _plan(shim, 4096, (14336,), 2880, kinds=both)[::3] == (7, 0)
+    assert _plan(shim, 4096, (2880,), 4096, kinds=both)[::3] == (6, 0)
     # only one kind allowed: that kind
-    assert _plan(shim, 4096, (14336,), 2880, kinds=TWO_WAVE, q_aligned=True)[3] == 0
-    assert _plan(shim, 4096, (2880,), 4096, kinds=ONE_WAVE, q_aligned=False)[3] == 1
+    assert _plan(shim, 4096, (14336,), 2880, kinds=TWO_WAVE)[3] == 0
+    assert _plan(shim, 4096, (2880,), 4096, kinds=ONE_WAVE)[3] == 1
+
+
+def test_prefill_plan_does_not_depend_on_alignment(shim):
+    # the plan sees only the padded rank, the output width and the depth:
+    # every r in 2864..2872 (all residues mod 8) and widths 3993..4000 get
+    # the plan of their aligned neighbour
+    both = TWO_WAVE | ONE_WAVE
+    p1 = {_plan(shim, 4096, (-(-r // 32) * 32,), 4096, kinds=both) for r in range(2849, 2881)}
+    assert len(p1) == 1
+    p2 = {_plan(shim, 4096, (n,), 2880, kinds=both)[:2] for n in range(3969, 4001)}
+    assert len(p2) == 1
 
 
 def test_prefill_plan_fills_the_machine_for_small_m(shim):
@@ -482,10 +493,9 @@ def test_prefill_partial_bytes_cover_every_plan(shim):
         for M in list(range(17, max_M + 1, 97)) + [max_M]:
             for cols, kd in (((r_pad,), K), ((N,), r_pad)):
                 for kinds in (TWO_WAVE, ONE_WAVE, TWO_WAVE | ONE_WAVE):
-                    for qa in (False, True):
-                        nb, splits, steps, kind = _plan(shim, M, cols, kd, kinds=kinds, q_aligned=qa)
-                        if splits > 1:
-                            assert splits * M * (-(-cols[0] // 4) * 4) * 4 <= have, (max_M, M, cols, kd, splits)
+                    nb, splits, steps, kind = _plan(shim, M, cols, kd, kinds=kinds)
+                    if splits > 1:
+                        assert splits * M * (-(-cols[0] // 4) * 4) * 4 <= have, (max_M, M, cols, kd, splits)
 
 
 def _xcd(shim, K, r, N, pn, max_M):
