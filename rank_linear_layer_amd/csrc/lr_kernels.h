@@ -222,23 +222,29 @@ int decode_xcd_blocks_per_cu(int lds_bytes);
 // ceil(N/16) column groups x ceil(K/32) k-steps of 1 KB blocks, each block
 // the 16x16x32 MFMA B operand of that group and step (zero past K and N).
 constexpr int kDenseMaxOut = 4;  // projections sharing X in one dense decode launch
+constexpr int kDenseMaxSplits = 16;  // K slices of one column group (workgroups that share it)
 struct DenseOut {
   const uint16_t* Wsw;  // decode layout of this projection's W
   uint16_t* Y;          // [M x N] bf16
   int64_t N;
+  float* part;          // [splits][ceil(N/16)][256] fp32 partial tiles (splits > 1)
+  uint32_t* cnt;        // [ceil(N/16)] arrivals per column group, zero between launches
 };
 struct DenseArgs {
   const uint16_t* X;    // [M x K] bf16
   int64_t M, K;
   int64_t nk;           // ceil(K / 32)
+  int64_t ng;           // column groups of all outputs
   int nout;             // 1 .. kDenseMaxOut outputs; workgroups are dealt output by output
+  int splits;           // 1 .. kDenseMaxSplits K slices per column group
   int pad_;
   DenseOut o[kDenseMaxOut];
 };
 // Wsw from W (row-major [K x N]); Wsw holds ceil(N/16)*ceil(K/32)*512 bf16.
 hipError_t launch_dense_swizzle(const uint16_t* W, uint16_t* Wsw, int64_t K, int64_t N, hipStream_t stream);
-// Y_i = X . W_i for M <= 16: one workgroup per 16-column group of every
-// output, no exchange.
+// Y_i = X . W_i for M <= 16: `splits` workgroups per 16-column group of
+// every output, each over a slice of K; the last of a group's workgroups to
+// finish adds the fp32 partials in slice order (nothing waits).
 hipError_t launch_dense_decode(const DenseArgs& args, hipStream_t stream);
 
 // --------------------------------------------------------------- prefill ---

@@ -89,6 +89,8 @@ struct lr_linear {
   bool dense;
   uint16_t* W;
   uint16_t* Wsw;
+  float* dpart;     // dense decode: [kDenseMaxSplits][ceil(N/16)][256] fp32 partials
+  uint32_t* dcnt;   // dense decode: [ceil(N/16)] arrival counters
   // role-split decode (dp.kind 2): A and B in the operand block layout,
   // T [dec_max_M x 32 ceil(r/32)] fp32 and the T slice flags
   uint16_t* Asw;
@@ -235,7 +237,16 @@ lr_status run_dense_decode(const lr_linear* const* hs, uint16_t* const* Ys, int 
     a.o[i].Wsw = hs[i]->Wsw;
     a.o[i].Y = Ys[i];
     a.o[i].N = hs[i]->N;
+    a.o[i].part = hs[i]->dpart;
+    a.o[i].cnt = hs[i]->dcnt;
+    a.ng += lrv::ceil_div(hs[i]->N, 16);
   }
+  // K slices per column group, measured on MI355X: slicing pays only for
+  // deep, narrow outputs (K = 14336, 64 groups: four slices 10.8 us against
+  // 14.3), so the slices bring the launch to about one workgroup per compute
+  // unit and keep at least 64 k-steps each
+  const int64_t want = lrv::ceil_div((int64_t)num_cus(hs[0]->device), a.ng);
+  a.splits = (int)std::max<int64_t>(1, std::min<int64_t>({want, (int64_t)lrk::kDenseMaxSplits, a.nk / 64}));
   const hipError_t e = lrk::launch_dense_decode(a, stream);
   if (e != hipSuccess) return hip_fail(e, "dense decode launch");
   return LR_OK;
@@ -880,9 +891,14 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     o_w = off;
     off = align_up(off + (size_t)K * N * 2);
   }
+  size_t o_dpart = 0, o_dcnt = 0;
   if (h->dense && h->has_decode) {
     o_wsw = off;
     off = align_up(off + (size_t)lrv::ceil_div(N, 16) * lrv::ceil_div(K, 32) * 1024);
+    o_dpart = off;
+    off = align_up(off + (size_t)lrk::kDenseMaxSplits * lrv::ceil_div(N, 16) * 1024);
+    o_dcnt = off;
+    off = align_up(off + (size_t)lrv::ceil_div(N, 16) * 4);
   }
   h->ws_bytes = off;
   if (off > 0) {
@@ -985,7 +1001,11 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
         return fail(LR_ERR_OUT_OF_MEMORY, "dense fallback: hipMalloc(%lld) for W", (long long)(K * N * 2));
       }
     }
-    if (h->has_decode) h->Wsw = (uint16_t*)(base + o_wsw);
+    if (h->has_decode) {
+      h->Wsw = (uint16_t*)(base + o_wsw);
+      h->dpart = (float*)(base + o_dpart);
+      h->dcnt = (uint32_t*)(base + o_dcnt);
+    }
     st = form_dense(h, h->W ? h->W : (uint16_t*)tmp);
     if (tmp) (void)hipFree(tmp);
     if (st != LR_OK) {

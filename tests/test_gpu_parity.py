@@ -455,7 +455,11 @@ DENSE_CASES = [(1, 4096, 817, 1024, 0), (8, 4096, 817, 1024, 0), (16, 4096, 817,
                (8, 4096, 1637, 4096, lrl.LR_FLAG_DENSE), (5, 1001, 700, 300, lrl.LR_FLAG_DENSE),
                (16, 4096, 1063, 3999, lrl.LR_FLAG_DENSE), (1, 8, 3, 1, 0), (3, 33, 40, 17, 0),
                (300, 1024, 645, 1000, lrl.LR_FLAG_DENSE), (40, 520, 400, 300, lrl.LR_FLAG_DENSE),
-               (513, 1001, 900, 700, 0), (4, 64, 5, 48, lrl.LR_FLAG_DENSE | lrl.LR_FLAG_FORCE_PREFILL)]
+               (513, 1001, 900, 700, 0), (4, 64, 5, 48, lrl.LR_FLAG_DENSE | lrl.LR_FLAG_FORCE_PREFILL),
+               # deep and narrow: decode cuts K into slices whose fp32 partials the last
+               # workgroup of each column group adds
+               (1, 14336, 2867, 1024, lrl.LR_FLAG_DENSE), (16, 14336, 900, 1000, lrl.LR_FLAG_DENSE),
+               (7, 8200, 1000, 40, lrl.LR_FLAG_DENSE)]
 
 
 def _expect_dense(K, r, N, flags):
@@ -544,9 +548,11 @@ def test_canary_guards_and_poison(gpu, M, N, flags):
 
 
 @pytest.mark.parametrize("M,flags", [(8, 0), (8, lrl.LR_FLAG_DECODE_STREAMING), (8, lrl.LR_FLAG_DECODE_RESIDENT),
-                                     (48, 0)])
-def test_deterministic_bitwise(M, flags):
-    K, r, N = 1024, 333, 1500
+                                     (8, lrl.LR_FLAG_DECODE_XCD), (8, lrl.LR_FLAG_DECODE_SPLIT),
+                                     (8, lrl.LR_FLAG_DENSE), (48, 0)])
+@pytest.mark.parametrize("K", [1024, 14336])
+def test_deterministic_bitwise(M, flags, K):
+    r, N = 333, 1500
     Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 1234)
     lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=flags)
     X = to_dev(Xb)
