@@ -36,7 +36,7 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096
 METRIC = "low-rank linear: decode TB/s and prefill TFLOP/s vs roofline, across rank r"
 _CSRC = "rank_linear_layer_amd/csrc/"
 DECODE_SOURCES = [_CSRC + f for f in ("lr_decode.hip", "lr_decode_res.hip", "lr_decode_split.hip", "lr_decode_xcd.hip",
-                                       "lr_device.h", "lr_kernels.h")]
+                                       "lr_device.h", "lr_kernels.h", "lr_ldsops.h")]
 PREFILL_SOURCES = [_CSRC + f for f in ("lr_prefill.hip", "lr_prefill_w4.hip", "lr_device.h", "lr_kernels.h",
                                        "lr_validate.h", "lr_linear.cpp")]
 PREFILL_KERNELS = {0: "lr_prefill_gemm_kernel", 1: "lr_prefill_w4_kernel"}
@@ -418,6 +418,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="the full rank sweep (every r of the sweep range)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the default strided rank sweep")
     ap.add_argument("--no-alternatives", action="store_true", help="skip the opt-in decode kernels")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill leg (for profiling it): prints its JSON object")
     ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--sweep-stride", type=int, default=1)
     ap.add_argument("--gac", action="store_true", help="with --sweep: GAC rank re-selection on the measured table")
@@ -441,6 +443,13 @@ def main():
 
     if args.calib_copy:
         calib_copy(torch)
+
+    if args.prefill_only:
+        p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 50), 3)
+        log("prefill: %.3f ms/step, %.1f TFLOP/s, plan %s" % (p["ms"], p["tflops"], p["plan"]))
+        print(json.dumps({"prefill_ms_per_step": round(p["ms"], 5), "tflops": round(p["tflops"], 2),
+                          "flops_per_step": p["flops"], "plan": p["plan"]}), flush=True)
+        return
 
     torch.cuda.synchronize()
     d = bench_decode(torch, lrl, configs, datagen, metrics, args.steps, args.warmup)
