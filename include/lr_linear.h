@@ -29,19 +29,22 @@
  * Ownership
  * ---------
  * A and B are BORROWED by the handle: the caller keeps them alive until
- * lr_linear_destroy, and every call reads them where they are (decode and
- * prefill alike), so an update of A or B in place between calls is seen by
- * the next call.  X and Y are borrowed for the duration of the enqueued
+ * lr_linear_destroy.  By default every call reads them where they are
+ * (decode and prefill alike), so an update of A or B in place between calls
+ * is seen by the next call.  X and Y are borrowed for the duration of the enqueued
  * work.  The handle OWNS a device workspace (allocated at create, sized for
  * max_M) that holds the exchange tables of the decode kernels, split-K
  * partial sums, and for M > 16 the bf16 intermediate T; and a 64-byte
  * pinned host word in which a decode kernel reports a wait that gave up
- * (see Errors).  Two opt-in modes also keep a derived copy of the factors
- * in the workspace, made at create and not refreshed afterwards: the dense
- * fallback's W = A.B (LR_FLAG_DENSE, or automatic, see lr_linear_create),
- * and LR_FLAG_DECODE_SPLIT, whose decode kernel reads A and B from a copy
- * in its 1 KB operand block layout (2 (ceil(r/16) ceil(K/32) +
- * ceil(N/16) ceil(r/32)) x 512 bytes, about the size of A and B).
+ * (see Errors).  Two modes instead keep a derived copy of the factors in
+ * the workspace, made at create and not refreshed afterwards, which every
+ * call of the handle reads (an in-place update of A or B is then not seen):
+ * the dense fallback's W = A.B (LR_FLAG_DENSE, or automatic, see
+ * lr_linear_create; decode and prefill both read W), and the decode-only
+ * LR_FLAG_DECODE_SPLIT, whose kernel reads A and B from a copy in its 1 KB
+ * operand block layout: 2 (ceil(r/16) ceil(K/32) + ceil(N/16) ceil(r/32))
+ * x 512 bytes, about the size of A and B (27.1 MB for K = N = 4096,
+ * r = 1637).
  * lr_linear_destroy frees all of it.  Because the workspace is shared by
  * every call on a handle, a handle must not be used by two streams at the
  * same time.
@@ -105,7 +108,9 @@ typedef struct lr_linear lr_linear;
 #define LR_FLAG_FACTORED 64u  /* never take the dense fallback */
 #define LR_FLAG_DECODE_SPLIT 128u  /* decode with the role-split kernel where its plan fits; it
                                       reads a copy of A and B in its operand block layout, made at
-                                      create (see Ownership) */
+                                      create (see Ownership).  Decode-only: max_M <= 16 and not
+                                      with FORCE_PREFILL, so every call on the handle reads the
+                                      same copy */
 #define LR_FLAG_DECODE_RESIDENT 256u  /* decode with the LDS-resident kernel where it applies, else
                                          the register-streaming one (the default's choice too) */
 #define LR_FLAG_DECODE_XCD 512u  /* decode with the XCD-sliced kernel where its plan fits: it reads

@@ -69,6 +69,13 @@ inline lr_status check_create(int64_t K, int64_t r, int64_t N, const void* A, co
       return LR_ERR_INVALID_ARG;
     }
   }
+  if ((flags & LR_FLAG_DECODE_SPLIT) && (max_M > kDecodeMaxM || (flags & LR_FLAG_FORCE_PREFILL))) {
+    // its decode reads a copy of A and B made at create; a handle that also
+    // ran prefill would read the live factors there and the copy here
+    snprintf(err, errlen, "DECODE_SPLIT handles are decode-only: max_M must be <= %d and FORCE_PREFILL unset",
+             (int)kDecodeMaxM);
+    return LR_ERR_INVALID_ARG;
+  }
   if ((flags & LR_FLAG_DENSE) && (flags & LR_FLAG_FACTORED)) {
     snprintf(err, errlen, "DENSE and FACTORED are exclusive");
     return LR_ERR_INVALID_ARG;

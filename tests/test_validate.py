@@ -169,6 +169,9 @@ def test_create_validation(shim):
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 384) == INVALID  # SPLIT | RESIDENT
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 260) == INVALID  # STREAMING | RESIDENT
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 128) == OK  # DECODE_SPLIT
+    # DECODE_SPLIT handles are decode-only (their copy of A and B is what decode reads)
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 17, 128) == INVALID
+    assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 8, 128 | 2) == INVALID
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 132) == INVALID  # with STREAMING
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 32) == OK  # DENSE
     assert shim.t_check_create(4096, 1637, 4096, 0x100000, 0x2000000, 16, 64) == OK  # FACTORED
