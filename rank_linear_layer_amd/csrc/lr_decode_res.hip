@@ -38,9 +38,12 @@
 // changes from one launch to the next, so a captured graph can replay the
 // launch.
 //
-// The misalignment of the rows (ld mod 8) selects one of eight compile-time
-// shift patterns for a whole GEMM loop (one uniform switch per phase); the
-// eight variants are the same code with different constants.
+// Every row run is loaded from its exact first element (16-byte direct
+// loads at any 2-byte offset), so a misaligned rank or width takes the same
+// instructions as an aligned one: no code depends on the leading dimension
+// modulo 8.  The buffer range check zeroes a dword that reaches past the
+// matrix, so the workgroup whose slab holds the last element of A or of B
+// writes it into LDS from a scalar load.
 #include "lr_device.h"
 #include "lr_kernels.h"
 
@@ -62,10 +65,9 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, void* lds_base_wave, uint32
 }
 
 // Direct loads of `rows` runs of `cpr` 16-byte chunks into LDS slots
-// [0, rows * cpr) of `lds` (run q at slot q * cpr).  Run q starts at the
-// aligned chunk that holds element e_first + q * ld; of each run only the
-// chunks that hold its `ncols` elements are fetched, and runs q >= valid
-// rows read as zero.  This wave issues load instructions first, first +
+// [0, rows * cpr) of `lds` (run q at slot q * cpr).  Run q starts exactly at
+// element e_first + q * ld; of each run only the chunks that hold its
+// `ncols` elements are fetched, and runs q >= valid rows read as zero.  This wave issues load instructions first, first +
 // step, ... (64 slots each).  The slot -> (run, chunk) map advances by a
 // constant per instruction, so no division is done per load; element
 // offsets fit 32 bits (matrices are below 2 GiB).
@@ -79,9 +81,9 @@ __device__ __forceinline__ void dma_runs(rsrc_t r, char* lds, uint32_t e_first, 
   uint32_t e0 = e_first + (uint32_t)row * ld;
   const uint32_t dld = (uint32_t)drow * ld;
   for (int i = first; i < ninst; i += step) {
-    const int need = (int)(((e0 & 7u) + (uint32_t)max(ncols, 0) + 7u) >> 3);
+    const int need = (max(ncols, 0) + 7) >> 3;
     const bool ok = row < valid && cc < need;
-    lds_load16(r, lds + i * 1024, ok ? ((e0 >> 3) + (uint32_t)cc) * 16u : kOutOfRange);
+    lds_load16(r, lds + i * 1024, ok ? (e0 + 8u * (uint32_t)cc) * 2u : kOutOfRange);
     row += drow;
     cc += dcc;
     e0 += dld;
@@ -98,30 +100,17 @@ __device__ __forceinline__ void lds_write16(char* p, const u32x4_t& v) { *reinte
 
 // 8 rows held as chunk runs in LDS (row q at rows + q * pitch) -> 8 MFMA
 // B-operands, in two steps so that the LDS reads of the next tile can be in
-// flight while this one is transposed.  lane16 reads chunks c_off + lane16
-// and c_off + lane16 + 1 of each run; LD8 = (leading dimension mod 8) fixes
-// every row's shift.  No masking here: rows past the matrix are zero in
-// LDS, and output columns past the slice or the matrix are dropped by the
-// callers.
+// flight while this one is transposed.  lane16 reads chunk c_off + lane16 of
+// each run.  No masking here: rows past the matrix are zero in LDS, and
+// output columns past the slice or the matrix are dropped by the callers.
 struct TileRaw {
-  u32x4_t lo[8], hi[8];
+  u32x4_t lo[8];
 };
-template <int LD8>
 __device__ __forceinline__ void tile_read(const char* rows, int pitch, int c_off, int lane16, TileRaw& t) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const char* p = rows + q * pitch + (c_off + lane16) * 16;
-    t.lo[q] = lds_read16(p);
-    if (((q * LD8) & 7) != 0) t.hi[q] = lds_read16(p + 16);
-  }
+  for (int q = 0; q < 8; ++q) t.lo[q] = lds_read16(rows + q * pitch + (c_off + lane16) * 16);
 }
-template <int LD8>
-__device__ __forceinline__ void tile_ops(const TileRaw& t, u32x4_t op[8]) {
-  u32x4_t seg[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) seg[q] = ((q * LD8) & 7) != 0 ? realign(t.lo[q], t.hi[q], (q * LD8) & 7) : t.lo[q];
-  transpose8x8(seg, op);
-}
+__device__ __forceinline__ void tile_ops(const TileRaw& t, u32x4_t op[8]) { transpose8x8(t.lo, op); }
 
 struct ResCtx {
   const char* sA;
@@ -138,7 +127,6 @@ struct ResCtx {
 // zeros.  (Straight-line MFMA code keeps the accumulators in place; a
 // conditional block around the MFMAs made the compiler shuffle them right
 // behind each MFMA.)
-template <int LD8>
 __device__ __forceinline__ void gemm1_wave(const ResCtx& c, f32x4_t acc[8]) {
   const int pitch = kResCA * 16;
   TileRaw rt[2];
@@ -146,14 +134,14 @@ __device__ __forceinline__ void gemm1_wave(const ResCtx& c, f32x4_t acc[8]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = c.w + 4 * h;
-    tile_read<LD8>(c.sA + (size_t)(t * kResKT + 8 * c.g) * pitch, pitch, 0, c.np, rt[h]);
+    tile_read(c.sA + (size_t)(t * kResKT + 8 * c.g) * pitch, pitch, 0, c.np, rt[h]);
     xt[h] = lds_read16(c.sX + c.np * (kResXK * 2) + (t * kResKT + 8 * c.g) * 2);
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = c.w + 4 * h;
     u32x4_t op[8];
-    tile_ops<LD8>(rt[h], op);
+    tile_ops(rt[h], op);
     // X columns >= K (and tiles past kt_cnt) contribute zero
     const int64_t k0 = c.kbase + (int64_t)t * kResKT + 8 * c.g;
     const u32x4_t x = (t < c.kt_cnt && k0 < c.K) ? xt[h] : zerou4();
@@ -165,17 +153,16 @@ __device__ __forceinline__ void gemm1_wave(const ResCtx& c, f32x4_t acc[8]) {
 // GEMM2 partials of this workgroup's two 128-column n-tiles for this wave's
 // 32 rank rows (the second is computed even when the workgroup has one
 // n-tile and is then never stored).
-template <int LD8>
 __device__ __forceinline__ void gemm2_wave(const ResCtx& c, const u32x4_t& thi, const u32x4_t& tlo, f32x4_t y0[8],
                                            f32x4_t y1[8]) {
   const char* rows = c.sB + (size_t)(32 * c.w + 8 * c.g) * (c.CB * 16);
   TileRaw b[2];
-  tile_read<LD8>(rows, c.CB * 16, 0, c.np, b[0]);
-  tile_read<LD8>(rows, c.CB * 16, 16, c.np, b[1]);
+  tile_read(rows, c.CB * 16, 0, c.np, b[0]);
+  tile_read(rows, c.CB * 16, 16, c.np, b[1]);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     u32x4_t op[8];
-    tile_ops<LD8>(b[h], op);
+    tile_ops(b[h], op);
     f32x4_t* y = h == 0 ? y0 : y1;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -215,18 +202,6 @@ __device__ __forceinline__ uint64_t res_trace_now() {
   } while (0)
 #define RES_TRACE_FLUSH() do { } while (0)
 #endif
-
-#define LR_LD8_SWITCH(v, CALL) \
-  switch ((v) & 7) {           \
-    case 0: CALL(0); break;    \
-    case 1: CALL(1); break;    \
-    case 2: CALL(2); break;    \
-    case 3: CALL(3); break;    \
-    case 4: CALL(4); break;    \
-    case 5: CALL(5); break;    \
-    case 6: CALL(6); break;    \
-    default: CALL(7); break;   \
-  }
 
 __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArgs a) {
   RES_TRACE_ENTRY();
@@ -310,6 +285,13 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   }
   wait_vmem_all();
   barrier_lds();  // X and A are in LDS
+  // A's last element (K - 1, r - 1), if this workgroup's slab holds it (see the top)
+  if (jend == r && kt_cnt > 0 && kbase + (int64_t)kt_cnt * kResKT >= K) {
+    if (tid == 0)
+      *reinterpret_cast<uint16_t*>(sA + (size_t)(K - 1 - kbase) * kResCA * 16 + (r - 1 - j0) * 2) =
+          (uint16_t)scalar_elem(P.A, (int64_t)K * r - 1);
+    barrier_lds();
+  }
   const uint32_t gen = __builtin_amdgcn_readfirstlane(gen_v);
   const uint32_t epoch = gen + 1u == 0u ? 1u : gen + 1u;  // 0 is the value of a fresh flag
   RES_TRACE(1);
@@ -334,9 +316,7 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   f32x4_t acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = zero4();
-#define LR_G1(D) gemm1_wave<D>(ctx, acc)
-  LR_LD8_SWITCH(r, LR_G1)
-#undef LR_G1
+  gemm1_wave(ctx, acc);
   RES_TRACE(2);
   barrier_lds();  // every wave is done reading A: the A region is free
 #pragma unroll
@@ -441,6 +421,13 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   RES_TRACE(9);
   wait_vmem_all();  // B (loaded by waves 2-3) is in LDS
   barrier_lds();
+  // B's last element (r - 1, N - 1), if this workgroup's slab holds it
+  if (jend == r && nt_cnt > 0 && nb0 + (int64_t)nt_cnt * kResNT >= N) {
+    if (tid == 0)
+      *reinterpret_cast<uint16_t*>(sB + (size_t)(r - 1 - j0) * CB * 16 + (N - 1 - nb0) * 2) =
+          (uint16_t)scalar_elem(P.B, (int64_t)r * N - 1);
+    barrier_lds();
+  }
   RES_TRACE(5);
 
   // bf16 hi/lo split of this wave's 32 rank rows: lane (i = np, g) holds
@@ -465,9 +452,7 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
     y0[e] = zero4();
     y1[e] = zero4();
   }
-#define LR_G2(D) gemm2_wave<D>(ctx, thi, tlo, y0, y1)
-  LR_LD8_SWITCH(N, LR_G2)
-#undef LR_G2
+  gemm2_wave(ctx, thi, tlo, y0, y1);
   RES_TRACE(10);
   for (int ntl = 0; ntl < nt_cnt; ++ntl) {
     barrier_lds();  // previous tile's red reads (and the Ts reads) are done
