@@ -198,9 +198,11 @@ def bench_dense_decode(torch, lrl, configs, steps, warmup):
     return out
 
 
-def bench_prefill(torch, lrl, configs, metrics, steps, warmup):
+def bench_prefill(torch, lrl, configs, metrics, steps, warmup, r=None):
+    """MLP up-projection prefill (the rank `r` overrides the workload's)."""
     c = configs.MLP_UP_PREFILL
-    M, K, r, N = c["M"], c["K"], c["r"], c["N"]
+    M, K, N = c["M"], c["K"], c["N"]
+    r = r or c["r"]
     g = torch.Generator(device="cuda")
     g.manual_seed(configs.seed_base(c["index"]))
     X = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
@@ -420,6 +422,9 @@ def main():
     ap.add_argument("--no-alternatives", action="store_true", help="skip the opt-in decode kernels")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill leg (for profiling it): prints its JSON object")
+    ap.add_argument("--prefill-ranks", default=None,
+                    help="with --prefill-only: a rank range lo-hi; the prefill step is timed at every r in it, "
+                         "after a few seconds of warm-up, in two passes (ascending, then descending)")
     ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--sweep-stride", type=int, default=1)
     ap.add_argument("--gac", action="store_true", help="with --sweep: GAC rank re-selection on the measured table")
@@ -444,6 +449,24 @@ def main():
     if args.calib_copy:
         calib_copy(torch)
 
+    if args.prefill_only and args.prefill_ranks:
+        lo, hi = (int(v) for v in args.prefill_ranks.split("-"))
+        ranks = list(range(lo, hi + 1))
+        t_end = time.time() + 4.0  # steady clocks before the first timed rank
+        while time.time() < t_end:
+            bench_prefill(torch, lrl, configs, metrics, 5, 1, r=ranks[0])
+        per = {r: [] for r in ranks}
+        for order in (ranks, ranks[::-1]):
+            for r in order:
+                p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 50), 3, r=r)
+                per[r].append(p["ms"])
+                print(json.dumps({"prefill_r": r, "ms": round(p["ms"], 5), "plan": p["plan"].split("prefill=")[1][:80]}),
+                      file=sys.stderr, flush=True)
+        ms = {r: float(np.mean(v)) for r, v in per.items()}
+        print(json.dumps({"workload": "MLP up-projection prefill M=4096 K=4096 N=14336 across r",
+                          "ms_per_step": {str(r): round(v, 5) for r, v in ms.items()},
+                          "max_over_min": round(max(ms.values()) / min(ms.values()), 4)}), flush=True)
+        return
     if args.prefill_only:
         p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 50), 3)
         log("prefill: %.3f ms/step, %.1f TFLOP/s, plan %s" % (p["ms"], p["tflops"], p["plan"]))
