@@ -255,7 +255,9 @@ constexpr int kPreKT = 32;        // k per LDS stage (one MFMA k-step)
 // columns per workgroup tile = 32 * nb, nb in [kPreMinNB, kPreMaxNB]
 constexpr int kPreMinNB = 6;
 constexpr int kPreMaxNB = 7;
-constexpr int kPreLdsBytes = 4 * (16 + 15) * 1024 + 2 * 16 * 1024;  // 4 raw slots + 2 gathered tiles
+constexpr int kPreSlotBytes = (16 + 15) * 1024;  // one k-step: P (16 KB) + Q of the widest tile (15 KB)
+constexpr int kPreSlots = 5;                      // ring of k-steps in LDS
+constexpr int kPreLdsBytes = kPreSlots * kPreSlotBytes + 1024;  // + a spare 1 KB for loads that fill nothing
 
 // C[rows x out_cols] = P[rows x kd] . Q[kd x ldq] for one or two column
 // blocks in one launch.  P is k-contiguous (X or T); Q is row-major with

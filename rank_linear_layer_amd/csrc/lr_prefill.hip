@@ -9,10 +9,10 @@
 //   phase 2  Y[M x N]     = T . B      (reduction over r_pad; B rows >= r
 //                                       read as 0, never fetched)
 // The rank is padded to the 32-wide MFMA K-step on chip only; A and B keep
-// their public shapes.  Any r mod 8 and N mod 8 runs through the same code
-// (the page on dimensional misalignment, "Why Smaller Is Slower? ...",
-// section 3.3, traces part of the slowdown of odd ranks to misaligned
-// rows; here a misaligned row costs nothing extra on the compute path).
+// their public shapes.  Any r mod 8, N mod 8 and K mod 8 runs through the
+// same instructions (the page on dimensional misalignment, "Why Smaller Is
+// Slower? ...", section 3.3, traces part of the slowdown of odd ranks to
+// misaligned rows): every row is loaded from its exact first element.
 //
 // Workgroup: 8 waves (two per SIMD), tile 256 rows x 32*NB columns, 32-deep
 // k-steps.  Wave (wm, wn) = (w % 4, w / 4) owns rows [64 wm, +64) and NB
@@ -20,22 +20,30 @@
 // two waves of a SIMD interleave: while one waits on LDS or a barrier the
 // other keeps the matrix core busy.
 //
-// Every global read is a direct-to-LDS buffer load (no registers), issued
-// three k-steps ahead into a ring of three raw slots:
-//   P slot  256 rows x 32 k, already in MFMA operand order
-//           (16-row block b, chunk c, row L at b*1024 + c*256 + L*16: one
-//           operand read is 256 contiguous bytes per 16 lanes)
-//   Q slot  32 rows x 33 raw 16-byte chunks of A or B, each row starting at
-//           the aligned chunk that holds the tile's first column
+// Every global read is a direct-to-LDS 16-byte buffer load (no registers)
+// that starts at the exact element it needs: gfx950's buffer loads return
+// the 16 bytes at any 2-byte aligned offset.  Loads run four k-steps ahead
+// into a ring of five slots, each holding
+//   P  256 rows x 32 k of X or T in MFMA operand order (16-row block b,
+//      chunk c, row L at b*1024 + c*256 + L*16: one operand read is 1 KB
+//      contiguous per wave)
+//   Q  32 rows x 32*NB columns of A or B, row-major with a pitch of
+//      64 NB + 32 bytes, k-row 8 kq + 4 h + q stored at slot row
+//      16 h + 4 kq + q.
 // The MFMA B operand wants 8 consecutive k of one output column per lane,
-// while A and B store the output index contiguously.  One k-step ahead of
-// the MFMAs the waves gather the Q slot into Qt (same layout as the P slot,
-// 16 output columns per block) with 2-byte LDS reads: element (k, n) sits at
-// byte 2 (d_k + n) of raw row k, d_k = the row's misalignment, so an odd
-// leading dimension needs no shifting in registers at all.
+// while A and B store the output index contiguously: the transposing LDS
+// read (ds_read_b64_tr_b16) delivers it from Q directly.  Its 16-lane
+// groups read 4 slot rows each; with the row order above a half-wave reads
+// 8 consecutive slot rows, whose pitch (an odd multiple of 32 bytes) puts
+// them in 8 different 32-byte bank groups.
 //
-// An aligned P (X with K mod 8 = 0, and always T) is loaded straight into its
-// slot; a misaligned X goes through registers one step ahead (2-byte loads).
+// The buffer range check zeroes a dword that reaches past the range end, so
+// an unaligned load loses a matrix's last element when the matrix ends on a
+// dword boundary; and a P row chunk that straddles the reduction length
+// holds the next row's first elements.  The one k-step of a tile where
+// either happens patches its slot after the loads land (a scalar load for
+// the last element, zeros past the reduction length) behind one more
+// barrier.
 //
 // Grid: tiles are dealt so that each XCD (workgroup id mod 8) gets one
 // contiguous run of the tile order, and the order walks groups of four row
@@ -43,6 +51,7 @@
 // and Q panels in that XCD's L2.
 #include "lr_device.h"
 #include "lr_kernels.h"
+#include "lr_ldsops.h"
 
 namespace lrk {
 
@@ -51,38 +60,71 @@ namespace {
 constexpr int kThreads = kPreThreads;  // 512
 constexpr int kBM = kPreBM;            // 256
 constexpr int kBK = kPreKT;            // 32
-constexpr int kSlotP = 16 * 1024;      // P slot: 16 blocks of 16 rows x 4 chunks
-constexpr int kSlotQ = 15 * 1024;      // Q slot: 32 raw rows of up to 29 chunks (nb <= 7)
-constexpr int kSlot = kSlotP + kSlotQ;
-constexpr int kSlots = 4;              // ring depth: loads run three k-steps ahead
-constexpr int kQt = 16 * 1024;         // gathered Q: 16 column blocks (the gather covers 256 columns)
-constexpr int kQtBase = kSlots * kSlot;
+constexpr int kSlotP = 16 * 1024;      // P: 16 blocks of 16 rows x 4 chunks
+constexpr int kSlot = kPreSlotBytes;   // P + Q of the widest tile
+constexpr int kSlots = kPreSlots;      // ring depth: loads run kSlots - 1 k-steps ahead
+constexpr int kAhead = kSlots - 1;
 constexpr int kGroupRows = 4;          // row tiles per group in the tile order
 constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
-static_assert(kQtBase + 2 * kQt <= kPreLdsBytes, "LDS layout");
+static_assert(kSlots * kSlot + 1024 <= kPreLdsBytes, "LDS layout: the ring and a spare 1 KB");
+static_assert(kAhead == 4, "wait_stages covers three stages in flight");
 
 // Geometry that depends on the tile width 32 * NB.
 template <int NB>
 struct Geo {
-  static constexpr int kQChunks = 4 * NB + 1;  // raw chunks per Q row: 32 NB columns + one for misalignment
-  static constexpr int kQRowBytes = kQChunks * 16;
-  static constexpr int kQInst = (32 * kQChunks + 63) / 64;  // direct loads per Q slot
-  static constexpr int kEpiPitch = kQRowBytes;               // epilogue staging row pitch
-  static_assert(kQInst * 1024 <= kSlotQ, "Q slot");
+  static constexpr int kQPitch = 64 * NB + 32;              // bytes per Q slot row (an odd multiple of 32)
+  static constexpr int kQInst = 2 * NB + 1;                 // 1 KB direct loads per Q slot (32 rows)
+  static constexpr int kQChunks = 4 * NB;                   // 16-byte chunks of data per Q row
+  static constexpr int kEpiPitch = (4 * NB + 1) * 16;       // epilogue staging row pitch
+  static_assert(32 * kQPitch == 1024 * kQInst, "Q slot is a whole number of loads");
+  static_assert(kSlotP + 1024 * kQInst <= kSlot, "Q slot");
   static_assert(kQInst <= 16, "two direct loads per wave cover the Q slot");
-  // the gather reads columns up to 255 (+ 7 of misalignment) of the last raw row
-  static_assert(31 * kQRowBytes + 2 * (255 + 7) + 2 <= kSlotQ, "gather stays inside the Q slot");
   static_assert(kBM * kEpiPitch <= kPreLdsBytes, "epilogue staging");
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ u32x4_t lds_read16(const char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void lds_write16(char* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
-__device__ __forceinline__ uint32_t lds_read_u16(const char* p) { return *reinterpret_cast<const uint16_t*>(p); }
-__device__ __forceinline__ void dma16(rsrc_t r, char* lds_wave_base, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 16, (int)off, 0, 0, 0);
+// Transposing LDS reads of the NB B operands of a wave: within a 16-lane
+// group, lane 4 q + c reads 8 bytes (row q, columns 4 c .. 4 c + 3 of a
+// 4 x 16 bf16 tile) and receives the 4 values of column (lane mod 16).
+// Operand j takes the 32-byte column group j of slot rows l / 4 (k-rows
+// 8 kq + q) and 16 + l / 4 (k-rows 8 kq + 4 + q) from base address `a`.
+// One asm block issues every read and then waits for them: left to itself
+// the compiler cannot tell these reads from the direct-to-LDS loads still
+// in flight into other slots and would wait for every one of those.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+#define LR_TR(dst, off) "ds_read_b64_tr_b16 %" #dst ", %[a] offset:" #off "\n\t"
+template <int NB>
+__device__ __forceinline__ void tr_operands(uint32_t a, u32x4_t (&b)[NB]);
+template <>
+__device__ __forceinline__ void tr_operands<7>(uint32_t a, u32x4_t (&b)[7]) {
+  u32x2_t lo[7], hi[7];  // hi: 16 rows further, 16 * 480 = 7680 bytes
+  asm volatile(LR_TR(0, 0) LR_TR(1, 7680) LR_TR(2, 32) LR_TR(3, 7712) LR_TR(4, 64) LR_TR(5, 7744) LR_TR(6, 96)
+                   LR_TR(7, 7776) LR_TR(8, 128) LR_TR(9, 7808) LR_TR(10, 160) LR_TR(11, 7840) LR_TR(12, 192)
+                       LR_TR(13, 7872) "s_waitcnt lgkmcnt(0)"
+               : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]),
+                 "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]), "=&v"(lo[6]), "=&v"(hi[6])
+               : [a] "v"(a)
+               : "memory");
+#pragma unroll
+  for (int j = 0; j < 7; ++j) b[j] = u32x4_t{lo[j][0], lo[j][1], hi[j][0], hi[j][1]};
 }
+template <>
+__device__ __forceinline__ void tr_operands<6>(uint32_t a, u32x4_t (&b)[6]) {
+  u32x2_t lo[6], hi[6];  // hi: 16 rows further, 16 * 416 = 6656 bytes
+  asm volatile(LR_TR(0, 0) LR_TR(1, 6656) LR_TR(2, 32) LR_TR(3, 6688) LR_TR(4, 64) LR_TR(5, 6720) LR_TR(6, 96)
+                   LR_TR(7, 6752) LR_TR(8, 128) LR_TR(9, 6784) LR_TR(10, 160) LR_TR(11, 6816) "s_waitcnt lgkmcnt(0)"
+               : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]),
+                 "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5])
+               : [a] "v"(a)
+               : "memory");
+#pragma unroll
+  for (int j = 0; j < 6; ++j) b[j] = u32x4_t{lo[j][0], lo[j][1], hi[j][0], hi[j][1]};
+}
+#undef LR_TR
+// Slot row of k-row kr (0..31) of a Q slot.
+__host__ __device__ __forceinline__ int q_slot_row(int kr) { return 16 * ((kr >> 2) & 1) + 4 * (kr >> 3) + (kr & 3); }
 
 // Column tiles of all the outputs of a launch (outputs follow one another
 // in the tile order).
@@ -131,7 +173,9 @@ __device__ __forceinline__ Tile map_tile(const PreArgs& a, int bn, int bid) {
 
 struct Ctx {
   rsrc_t rP, rQ;
-  int64_t ldp, kd, ldq, qrows, mb, nb;
+  const uint16_t* P;
+  const uint16_t* Q;
+  int64_t rows, ldp, kd, ldq, qrows, mb, nb;
   int qcols;  // columns of Q inside this tile (<= BN; past them the rows hold other data)
   int w, l;
 };
@@ -139,11 +183,11 @@ struct Ctx {
 // -------------------------------------------------------------- loads ---
 // Every direct load's byte offset is computed once per workgroup and then
 // advanced by a uniform stride per k-step: P moves 32 columns (64 bytes) and
-// Q moves 32 rows (64 * ldq bytes) per step, which keeps each row's
-// misalignment, so the chunk selection of a lane never changes.
+// Q moves 32 rows (64 * ldq bytes) per step.
 
-// P slot, aligned P: wave w loads 16-row blocks w and w + 8.  Lane l of a
-// block fills chunk l / 16 of row l % 16; chunks at or past kd read zero.
+// P slot: wave w loads 16-row blocks w and w + 8.  Lane l of a block fills
+// chunk l / 16 of row l % 16 from its exact first element; chunks that start
+// at or past kd read zero, rows past the matrix fall outside the range.
 struct PDma {
   uint32_t off0[2];  // byte offset at k-step 0 of this split
   int kcol;          // lane's first column at k-step 0
@@ -162,131 +206,125 @@ __device__ __forceinline__ void p_dma(const Ctx& c, const PDma& d, char* slotP, 
   for (int h = 0; h < 2; ++h) dma16(c.rP, slotP + (c.w + 8 * h) * 1024, ok ? d.off0[h] + 64u * t : kOutOfRange);
 }
 
-// P slot, misaligned P: the same two chunks per lane through registers.
-struct PRegs {
-  u32x4_t v[2];
-};
-__device__ __forceinline__ void p_regs_load(const Ctx& c, PRegs& p, int64_t kb) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int b = c.w + 8 * h;
-    p.v[h] = load_kvec(c.rP, c.mb + 16 * b + (c.l & 15), c.ldp, kb + 8 * (c.l >> 4), c.kd, false);
-  }
-}
-__device__ __forceinline__ void p_regs_store(const Ctx& c, const PRegs& p, char* slotP) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) lds_write16(slotP + (c.w + 8 * h) * 1024 + c.l * 16, p.v[h]);
-}
-
-// Q slot: 32 raw rows x (4 NB + 1) chunks in Geo::kQInst loads of 64
-// chunks; wave w issues loads w and w + 8 (when they exist).  Only the
-// chunks that hold the tile's qcols columns of a row are fetched.
+// Q slot: Geo::kQInst loads of 1 KB; wave w issues loads w and w + 8 (when
+// they exist).  Lane l of load u lands at slot byte 1024 u + 16 l, i.e. slot
+// row R, chunk ch; it fetches chunk ch of k-row kr(R) from its exact first
+// element.  Chunks in the row padding, past the tile's qcols columns or past
+// the matrix's rows read zero.
 struct QDma {
   uint32_t off0[2];  // byte offset at k-step 0 of this split
-  int krow[2];       // lane's raw row at k-step 0 (k index)
-  bool ok[2];        // lane fills a real chunk of a real row of the slot
+  int krow[2];       // lane's k-row at k-step 0
+  bool ok[2];        // lane fills a real chunk of the slot
 };
 template <int NB>
 __device__ __forceinline__ void q_dma_init(const Ctx& c, int64_t k0, QDma& d) {
-  constexpr int QC = Geo<NB>::kQChunks;
+  constexpr int kPitch = Geo<NB>::kQPitch;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int i = c.w + 8 * h;
-    const int s = 64 * i + c.l;
-    const int row = s / QC, ch = s - row * QC;
-    const int64_t e0 = (k0 + row) * c.ldq + c.nb;
-    const int need = (int)(((e0 & 7) + c.qcols + 7) >> 3);
-    d.ok[h] = i < Geo<NB>::kQInst && row < kBK && ch < need;
-    d.off0[h] = d.ok[h] ? (uint32_t)(((e0 >> 3) + ch) * 16) : 0u;
-    d.krow[h] = (int)(k0 + row);
+    const int u = c.w + 8 * h;
+    const int pos = 1024 * u + 16 * c.l;
+    const int R = pos / kPitch, ch = (pos - R * kPitch) >> 4;
+    const int kr = 8 * ((R >> 2) & 3) + 4 * (R >> 4) + (R & 3);
+    d.ok[h] = u < Geo<NB>::kQInst && ch < Geo<NB>::kQChunks && 8 * ch < c.qcols;
+    d.krow[h] = (int)(k0 + kr);
+    d.off0[h] = d.ok[h] ? (uint32_t)(((k0 + kr) * c.ldq + c.nb + 8 * ch) * 2) : 0u;
   }
 }
 template <int NB>
-__device__ __forceinline__ void q_dma(const Ctx& c, const QDma& d, char* slotQ, int t) {
+__device__ __forceinline__ void q_dma(const Ctx& c, const QDma& d, char* slotQ, char* dummy, int t) {
   const uint32_t stride = (uint32_t)(64 * c.ldq);  // 32 rows of bf16
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    if (c.w + 8 * h < Geo<NB>::kQInst) {  // uniform
-      const bool ok = d.ok[h] && (int64_t)d.krow[h] + 32 * t < c.qrows;
-      dma16(c.rQ, slotQ + (c.w + 8 * h) * 1024, ok ? d.off0[h] + stride * (uint32_t)t : kOutOfRange);
-    }
+    // waves without a second load of the slot issue one that reads nothing
+    // into a spare 1 KB of LDS, so that every wave counts kDmaPerStage loads
+    const bool real = c.w + 8 * h < Geo<NB>::kQInst;  // uniform
+    const bool ok = real && d.ok[h] && (int64_t)d.krow[h] + 32 * t < c.qrows;
+    dma16(c.rQ, real ? slotQ + (c.w + 8 * h) * 1024 : dummy, ok ? d.off0[h] + stride * (uint32_t)t : kOutOfRange);
   }
 }
-// Direct loads one stage costs wave w (P: 2, Q: its share of kQInst).
-template <int NB, bool PAL>
-__device__ __forceinline__ int dma_per_stage(int w) {
-  return (PAL ? 2 : 0) + (w < Geo<NB>::kQInst ? (Geo<NB>::kQInst - 1 - w) / 8 + 1 : 0);
-}
-// s_waitcnt vmcnt(n), n in [0, 4] (gfx9 encoding: expcnt and lgkmcnt left at max).
-__device__ __forceinline__ void wait_vmem_upto(int n) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+// Direct loads per wave and k-step: two of P, two of Q.
+constexpr int kDmaPerStage = 4;
+// Wait until at most n stages of this wave's loads are in flight (n <= 3).
+__device__ __forceinline__ void wait_stages(int n) {
   switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 0: wait_vm_dyn(0); break;
+    case 1: wait_vm_dyn(kDmaPerStage); break;
+    case 2: wait_vm_dyn(2 * kDmaPerStage); break;
+    default: wait_vm_dyn(3 * kDmaPerStage); break;
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// --------------------------------------------------------------- gather ---
-// Qt block cb, chunk g, lane L holds the 8 k of k-group g for output column
-// 16 cb + L.  Item = (g, n) for all 256 columns of the slot (columns past
-// the tile width land in Qt blocks that no MFMA reads), two per thread, so
-// the gather is straight-line code that the compiler can interleave with the
-// MFMAs of the current step.  Consecutive lanes take consecutive columns:
-// each 2-byte read instruction touches one contiguous run of a raw row.
-// Columns at or past qcols are written as zero.
+// The k-step of a tile whose slot needs patching after its loads land:
+//  * Q with an odd leading dimension: the matrix's last element (row
+//    qrows - 1, column ldq - 1), in the tile holding that column;
+//  * P with kd mod 8 != 0: the chunks that straddle kd hold the next row's
+//    first elements (cleared), and the matrix's last element (set).
 template <int NB>
-__device__ __forceinline__ void gather(const Ctx& c, const char* slotQ, char* qt) {
-  constexpr int kQRowBytes = Geo<NB>::kQRowBytes;
-  // misalignment of raw row 8g + q: ((kb + 8g + q) * ldq + nb) mod 8 = (q * ldq) mod 8
-  // (kb and nb are multiples of 8)
-  int dq[8];
+__device__ __forceinline__ void patch_slot(const Ctx& c, char* slotP, char* slotQ, int64_t kstep0, bool fix_q,
+                                           bool fix_p) {
+  if (fix_q && c.w == 0 && c.l == 0) {
+    const int kr = (int)(c.qrows - 1 - kstep0);
+    const int n = (int)(c.ldq - 1 - c.nb);
+    *reinterpret_cast<uint16_t*>(slotQ + q_slot_row(kr) * Geo<NB>::kQPitch + 2 * n) =
+        (uint16_t)scalar_elem(c.Q, c.qrows * c.ldq - 1);
+  }
+  if (fix_p) {
+    const int64_t kk = kstep0 + 8 * (c.l >> 4);
+    if (kk < c.kd && kk + 8 > c.kd) {
+      const int valid = (int)(c.kd - kk);  // 1 .. 7 elements of this chunk lie below kd
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dq[q] = (int)((q * c.ldq) & 7);
-  const int tid = 64 * c.w + c.l;
+      for (int h = 0; h < 2; ++h) {
+        const int64_t row = c.mb + 16 * (c.w + 8 * h) + (c.l & 15);
+        char* p = slotP + (c.w + 8 * h) * 1024 + 16 * c.l;
+        u32x4_t v = lds_read16(p);
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int item = tid + kThreads * it;
-    const int g = item >> 8, n = item & 255;
-    const char* rows = slotQ + (8 * g) * kQRowBytes + 2 * n;
-    uint32_t e[8];
+        for (int i = 0; i < 4; ++i) {
+          // dword i holds elements 2 i and 2 i + 1
+          const uint32_t keep = 2 * i + 1 < valid ? 0xFFFFFFFFu : (2 * i < valid ? 0x0000FFFFu : 0u);
+          v[i] &= keep;
+        }
+        if (row == c.rows - 1 && c.ldp == c.kd) {
+          const int e = valid - 1;
+          const uint32_t x = scalar_elem(c.P, c.rows * c.ldp - 1) << (16 * (e & 1));
+          const uint32_t m = 0xFFFFu << (16 * (e & 1));
 #pragma unroll
-    for (int q = 0; q < 8; ++q) e[q] = lds_read_u16(rows + q * kQRowBytes + 2 * dq[q]);
-    u32x4_t v;
-    v[0] = e[0] | (e[1] << 16);
-    v[1] = e[2] | (e[3] << 16);
-    v[2] = e[4] | (e[5] << 16);
-    v[3] = e[6] | (e[7] << 16);
-    if (n >= c.qcols) v = zerou4();
-    lds_write16(qt + (n >> 4) * 1024 + g * 256 + (n & 15) * 16, v);
+          for (int i = 0; i < 4; ++i)
+            if (i == (e >> 1)) v[i] = (v[i] & ~m) | x;
+        }
+        lds_write16(p, v);
+      }
+    }
   }
 }
 
 // -------------------------------------------------------------- compute ---
 template <int NB>
-__device__ __forceinline__ void compute(const char* slotP, const char* qt, int wm, int wn, int lane_off,
+__device__ __forceinline__ void compute(const char* slotP, const char* slotQ, int wm, int wn, int l,
                                         f32x4_t (&acc)[4][NB]) {
   u32x4_t a[4], b[NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = lds_read16(slotP + (4 * wm + i) * 1024 + lane_off);
-#pragma unroll
-  for (int j = 0; j < NB; ++j) b[j] = lds_read16(qt + (NB * wn + j) * 1024 + lane_off);
+  for (int i = 0; i < 4; ++i) a[i] = lds_read16(slotP + (4 * wm + i) * 1024 + 16 * l);
+  // lane l = 16 kq + 4 q + c reads slot rows l / 4 and 16 + l / 4, bytes
+  // 8 c of each 32-byte column group
+  static_assert(16 * Geo<NB>::kQPitch == (NB == 7 ? 7680 : 6656), "offsets of tr_operands");
+  const char* qb = slotQ + (l >> 2) * Geo<NB>::kQPitch + 8 * (l & 3) + 32 * NB * wn;
+  tr_operands<NB>((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)qb, b);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = mfma_16x16x32(a[i], b[j], acc[i][j]);
 }
 
-template <int NB, bool PAL>
+template <int NB>
 __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int ks, char* smem) {
   constexpr int BN = 32 * NB;
   const PreOut& O = a.o[T.bi];
   Ctx c;
   c.rP = make_rsrc(O.P, a.rows * O.ldp * 2);
   c.rQ = make_rsrc(O.Q, O.qrows * O.ldq * 2);
+  c.P = O.P;
+  c.Q = O.Q;
+  c.rows = a.rows;
   c.ldp = O.ldp;
   c.kd = O.kd;
   c.ldq = O.ldq;
@@ -297,7 +335,6 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   c.w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform: scalar branches
   c.l = threadIdx.x & 63;
   const int wm = c.w & 3, wn = c.w >> 2;
-  const int lane_off = (c.l >> 4) * 256 + (c.l & 15) * 16;
 
   f32x4_t acc[4][NB];
 #pragma unroll
@@ -310,63 +347,47 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   const int s0 = ks * a.split_steps;
   const int nks = max(0, min(nks_all - s0, a.split_steps));
   const int64_t k0 = (int64_t)s0 * kBK;
-  auto slot = [&](int s) { return smem + (s & (kSlots - 1)) * kSlot; };
-  auto qtb = [&](int s) { return smem + kQtBase + (s & 1) * kQt; };
+  auto slot = [&](int s) { return smem + (s % kSlots) * kSlot; };
   PDma pd;
   QDma qd;
-  if (PAL) p_dma_init(c, k0, pd);
+  p_dma_init(c, k0, pd);
   q_dma_init<NB>(c, k0, qd);
   auto stage_dma = [&](int s) {
-    if (PAL) p_dma(c, pd, slot(s), s);
-    q_dma<NB>(c, qd, slot(s) + kSlotP, s);
+    p_dma(c, pd, slot(s), s);
+    q_dma<NB>(c, qd, slot(s) + kSlotP, smem + kSlots * kSlot, s);
   };
-  const int dma_w = dma_per_stage<NB, PAL>(c.w);
+  // the k-steps (relative to this split) that need a patch, else -1
+  const bool q_last_tile = (c.ldq & 1) && T.nb + c.qcols == c.ldq;
+  const int q_fix = q_last_tile && c.qrows - 1 >= k0 ? (int)((c.qrows - 1 - k0) / kBK) : -1;
+  const int p_fix = (c.kd & 7) && c.kd - 1 >= k0 ? (int)((c.kd - 1 - k0) / kBK) : -1;
 
-  // prologue: stages 0 and 1 landed, stage 0 gathered, stages 2 and 3 in flight
-  PRegs pr;
-  if (nks > 0) {
-    if (!PAL) p_regs_load(c, pr, k0);
-    stage_dma(0);
-  }
-  if (nks > 1) stage_dma(1);
-  wait_vmem_all();
-  if (!PAL && nks > 0) p_regs_store(c, pr, slot(0));
-  barrier_lds();
-  if (nks > 0) gather<NB>(c, slot(0) + kSlotP, qtb(0));
-  if (!PAL && nks > 1) p_regs_load(c, pr, k0 + kBK);
-  if (nks > 2) stage_dma(2);
-  if (nks > 3) stage_dma(3);
-  if (!PAL && nks > 1) {
-    wait_vmem_all();
-    p_regs_store(c, pr, slot(1));
-  }
-  barrier_lds();
-
+  for (int t = 0; t < kAhead && t < nks; ++t) stage_dma(t);
   for (int s = 0; s < nks; ++s) {
-    // misaligned P: stage s + 2 travels through registers during this step
-    if (!PAL && s + 2 < nks) p_regs_load(c, pr, k0 + (int64_t)(s + 2) * kBK);
-    compute<NB>(slot(s), qtb(s), wm, wn, lane_off, acc);
-    // next stage's operand (past the last stage this reads a consumed slot
-    // and fills a Qt buffer nothing reads again)
-    gather<NB>(c, slot(s + 1) + kSlotP, qtb(s + 1));
-    // stage s + 2 has landed; stage s + 3 (issued one step later) may still
-    // be in flight.  The misaligned P path drains everything.
-    if (PAL && s + 3 < nks)
-      wait_vmem_upto(dma_w);
-    else
-      wait_vmem_all();
-    if (!PAL && s + 2 < nks) p_regs_store(c, pr, slot(s + 2));
+    // this wave's loads of stage s have landed (later stages may be in flight)
+    wait_stages(min(kAhead - 1, nks - 1 - s));
     barrier_lds();
-    // slot s is free: every wave is past compute(s) and gathered s earlier
-    if (s + 4 < nks) stage_dma(s + 4);
+    if (s == q_fix || s == p_fix) {  // uniform
+      patch_slot<NB>(c, slot(s), slot(s) + kSlotP, k0 + (int64_t)s * kBK, s == q_fix, s == p_fix);
+      barrier_lds();
+    }
+    // slot (s - 1) mod kSlots is free: every wave is past compute(s - 1)
+    if (s + kAhead < nks) stage_dma(s + kAhead);
+    compute<NB>(slot(s), slot(s) + kSlotP, wm, wn, c.l, acc);
   }
 
   // ------------------------------------------------------------ epilogue --
+  // Columns at or past qcols are 0 (a chunk that straddles qcols brought in
+  // the next row's first elements).
+  const int L = c.l & 15, G = c.l >> 4;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    if (16 * (NB * wn + j) + L >= c.qcols)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = zero4();
   if (a.splits > 1) {
     // fp32 partial of this k-split: [ks][rows][ldpart], summed in split order
     // and rounded by lr_prefill_reduce_kernel.  Lane (L, G) of tile (i, j)
     // holds rows 64 wm + 16 i + 4 G + t, column 16 (NB wn + j) + L.
-    const int L = c.l & 15, G = c.l >> 4;
     float* part = O.part + (int64_t)ks * a.rows * O.ldpart;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -385,7 +406,8 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   // misalignment d = (row * ldc + nb) mod 8, so that LDS chunk k of a row is
   // global 16-byte chunk k of that row's segment.  Lane (L, G) of tile
   // (i, j) holds rows 64 wm + 16 i + 4 G + t, column 16 (NB wn + j) + L.
-  const int L = c.l & 15, G = c.l >> 4;
+  // Every wave is past its last compute: the ring memory is free.
+  barrier_lds();
   const int64_t ldc = O.ldc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -402,7 +424,7 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
 
   const rsrc_t rC = make_rsrc(O.C, a.rows * ldc * 2);
   const int ncols = (int)min64((int64_t)BN, O.out_cols - T.nb);
-  constexpr int kQChunks = Geo<NB>::kQChunks;
+  constexpr int kQChunks = Geo<NB>::kQChunks + 1;
   constexpr int nitems = kBM * kQChunks;
   for (int item = threadIdx.x; item < nitems; item += kThreads) {
     const int m = item / kQChunks, k = item - m * kQChunks;
@@ -427,7 +449,7 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   }
 }
 
-template <int NB, bool PAL>
+template <int NB>
 __global__ __launch_bounds__(kThreads, 1) void lr_prefill_gemm_kernel(const PreArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // workgroup -> (tile, k-split): consecutive ids are different tiles of one
@@ -435,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void lr_prefill_gemm_kernel(const PreA
   const int tiles = a.row_tiles * total_col_tiles(a);
   const int ks = (int)blockIdx.x / tiles;
   const Tile T = map_tile(a, 32 * NB, (int)blockIdx.x - ks * tiles);
-  gemm_tile<NB, PAL>(a, T, ks, smem);
+  gemm_tile<NB>(a, T, ks, smem);
 }
 
 // Y (or T) = bf16(sum over k-splits of the fp32 partials, in split order).
@@ -463,14 +485,14 @@ __global__ __launch_bounds__(256) void lr_prefill_reduce_kernel(const float* par
   }
 }
 
-template <int NB, bool PAL>
+template <int NB>
 hipError_t launch_one(const PreArgs& args, int grid, hipStream_t stream) {
   static std::atomic<uint64_t> attr_done{0};
   {
-    const hipError_t e = ensure_dynamic_lds((const void*)lr_prefill_gemm_kernel<NB, PAL>, kPreLdsBytes, attr_done);
+    const hipError_t e = ensure_dynamic_lds((const void*)lr_prefill_gemm_kernel<NB>, kPreLdsBytes, attr_done);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((lr_prefill_gemm_kernel<NB, PAL>), dim3(grid), dim3(kThreads), kPreLdsBytes, stream, args);
+  hipLaunchKernelGGL((lr_prefill_gemm_kernel<NB>), dim3(grid), dim3(kThreads), kPreLdsBytes, stream, args);
   return hipGetLastError();
 }
 
@@ -480,11 +502,9 @@ hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream) {
   const int ct = total_col_tiles(args);
   const int grid = ct * args.row_tiles * args.splits;
   if (grid <= 0) return hipSuccess;
-  bool pal = true;
-  for (int i = 0; i < args.nout; ++i) pal = pal && (args.o[i].ldp & 7) == 0;
   switch (args.nb) {
-    case 6: return pal ? launch_one<6, true>(args, grid, stream) : launch_one<6, false>(args, grid, stream);
-    case 7: return pal ? launch_one<7, true>(args, grid, stream) : launch_one<7, false>(args, grid, stream);
+    case 6: return launch_one<6>(args, grid, stream);
+    case 7: return launch_one<7>(args, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -185,6 +185,35 @@ def test_prefill_k_split_plans(M, K, r, N):
     banner("k-split case M=%d K=%d r=%d N=%d parity %s plan %s" % (M, K, r, N, p, lin.describe()))
 
 
+# A NaN stays where it belongs.  X rows and B rows are loaded from their
+# exact first element, so the chunk that ends a row also brings in the next
+# row's first elements: for X (K mod 8 != 0) the kernel clears them before
+# the MFMAs, and for B (N mod 8 != 0) they only reach output columns past N,
+# which are never stored.  NaN rows of X must give NaN rows of Y and nothing
+# else; a NaN in B's column 0 must give a NaN column 0 and nothing else.
+@pytest.mark.parametrize("flags", [0, lrl.LR_FLAG_PREFILL_TWO_WAVE])
+@pytest.mark.parametrize("K", [100, 1001])
+def test_nan_stays_in_its_row_and_column(gpu, flags, K):
+    M, r, N = 300, 77, 203
+    Xb, Ab, Bb = datagen.factorized_inputs(M, K, r, N, 5300 + K)
+    Xb, Bb = Xb.copy(), Bb.copy()
+    bad_rows = [1, 17, 255, 256, 299]
+    Xb[bad_rows, 0] = 0x7FC0  # bf16 quiet NaN
+    Bb[[5, 40], 0] = 0x7FC0
+    banner("nan case M=%d K=%d r=%d N=%d flags=%d" % (M, K, r, N, flags))
+    lin = lrl.LowRankLinear(to_dev(Ab), to_dev(Bb), max_M=M, flags=flags | lrl.LR_FLAG_FACTORED)
+    yb = to_bits(lin(to_dev(Xb)))
+    y = datagen.bf16_bits_to_f32(yb)
+    good = np.setdiff1d(np.arange(M), bad_rows)
+    assert np.all(np.isnan(y[bad_rows])), "NaN rows of X must give NaN rows of Y"
+    assert np.all(np.isnan(y[:, 0])), "a NaN in B's column 0 must reach Y's column 0"
+    assert np.all(np.isfinite(y[np.ix_(good, np.arange(1, N))])), "NaN leaked into other rows or columns"
+    Bc = Bb.copy()
+    Bc[[5, 40], 0] = 0
+    ref = oracle.lowrank_bf16(Xb[good], Ab, Bc)
+    assert_parity(yb[np.ix_(good, np.arange(1, N))], ref[:, 1:], "finite part")
+
+
 @pytest.mark.parametrize("M", [300])
 def test_mlp_packed_prefill_k_split(M):
     # packed gate/up at a small M: the shared plan splits k for both outputs
@@ -201,9 +230,8 @@ def test_mlp_packed_prefill_k_split(M):
 
 # ------------------------------------------------- prefill kernel kinds ---
 # Each prefill kernel forced on its own: the two-wave kernel (256 x 192 or
-# 224 tiles, 2-byte LDS gather) and the one-wave kernel (256 x 256 tiles,
-# weight rows realigned in registers, specialised on the weight leading
-# dimension mod 8).  Phase 1 reads A (leading dimension r) and phase 2 reads
+# 224 tiles, weight rows read with the transposing LDS read) and the
+# one-wave kernel (256 x 256 tiles, weight rows transposed in registers).  Phase 1 reads A (leading dimension r) and phase 2 reads
 # B (leading dimension N), so the first eight shapes cover every r mod 8 and
 # N mod 8; the rest add ragged M, partial column tiles, rank padding,
 # k-splits and a misaligned X (K mod 8 != 0: phase 1 falls back to the
