@@ -17,8 +17,8 @@
 // Workgroup: 8 waves (two per SIMD), tile 256 rows x 32*NB columns, 32-deep
 // k-steps.  Wave (wm, wn) = (w % 4, w / 4) owns rows [64 wm, +64) and NB
 // MFMA column blocks of 16: 4 x NB tiles of v_mfma_f32_16x16x32_bf16.  The
-// two waves of a SIMD interleave: while one waits on LDS or a barrier the
-// other keeps the matrix core busy.
+// two waves of a SIMD alternate between barriers: one issues its MFMAs
+// while the other reads its next operands from LDS.
 //
 // Every global read is a direct-to-LDS 16-byte buffer load (no registers)
 // that starts at the exact element it needs: gfx950's buffer loads return
@@ -298,21 +298,38 @@ __device__ __forceinline__ void patch_slot(const Ctx& c, char* slotP, char* slot
 }
 
 // -------------------------------------------------------------- compute ---
+// Barrier that no instruction crosses: the MFMAs carry no memory dependence,
+// so without the scheduling fences the compiler would move them past the
+// barriers that separate the two wave groups' turns.
+__device__ __forceinline__ void turn_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  barrier_lds();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The operands of one k-step, in registers until the MFMAs consume them.
 template <int NB>
-__device__ __forceinline__ void compute(const char* slotP, const char* slotQ, int wm, int wn, int l,
-                                        f32x4_t (&acc)[4][NB]) {
+struct Ops {
   u32x4_t a[4], b[NB];
+};
+template <int NB>
+__device__ __forceinline__ void read_operands(const char* slotP, const char* slotQ, int wm, int wn, int l,
+                                              Ops<NB>& o) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = lds_read16(slotP + (4 * wm + i) * 1024 + 16 * l);
+  for (int i = 0; i < 4; ++i) o.a[i] = lds_read16(slotP + (4 * wm + i) * 1024 + 16 * l);
   // lane l = 16 kq + 4 q + c reads slot rows l / 4 and 16 + l / 4, bytes
-  // 8 c of each 32-byte column group
+  // 8 c of each 32-byte column group (the asm block also waits for the P
+  // reads above)
   static_assert(16 * Geo<NB>::kQPitch == (NB == 7 ? 7680 : 6656), "offsets of tr_operands");
   const char* qb = slotQ + (l >> 2) * Geo<NB>::kQPitch + 8 * (l & 3) + 32 * NB * wn;
-  tr_operands<NB>((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)qb, b);
+  tr_operands<NB>((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)qb, o.b);
+}
+template <int NB>
+__device__ __forceinline__ void mma(const Ops<NB>& o, f32x4_t (&acc)[4][NB]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = mfma_16x16x32(a[i], b[j], acc[i][j]);
+    for (int j = 0; j < NB; ++j) acc[i][j] = mfma_16x16x32(o.a[i], o.b[j], acc[i][j]);
 }
 
 template <int NB>
@@ -361,18 +378,56 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   const int q_fix = q_last_tile && c.qrows - 1 >= k0 ? (int)((c.qrows - 1 - k0) / kBK) : -1;
   const int p_fix = (c.kd & 7) && c.kd - 1 >= k0 ? (int)((c.kd - 1 - k0) / kBK) : -1;
 
+  // The two waves of a SIMD take turns (waves 0-3 and 4-7, one of each per
+  // SIMD): between two barriers one group issues its MFMAs while the other
+  // reads its next operands from LDS and issues the next loads, so the
+  // matrix cores stay busy while the LDS reads of the other group are in
+  // flight.  Group 0 reads stage t, then multiplies it; group 1 multiplies
+  // stage t - 1 while group 0 reads t, and reads t while group 0
+  // multiplies.  Both groups meet the same barriers:
+  //   wait for stage t; barrier; [patch; barrier]; X; barrier; Y
+  //   group 0: X = read t + loads of t + 4, Y = MFMAs of t
+  //   group 1: X = MFMAs of t - 1,          Y = read t + loads of t + 4
+  // Stage t's slot was last read by group 1 before the first barrier of
+  // iteration t + 1, so both groups refill it (with stage t + 5) after that.
+  const int grp = c.w >> 2;
+  Ops<NB> ops;
   for (int t = 0; t < kAhead && t < nks; ++t) stage_dma(t);
-  for (int s = 0; s < nks; ++s) {
-    // this wave's loads of stage s have landed (later stages may be in flight)
+  // wait for stage s, publish it, patch it where needed
+  auto arrive = [&](int s) {
     wait_stages(min(kAhead - 1, nks - 1 - s));
-    barrier_lds();
+    turn_barrier();
     if (s == q_fix || s == p_fix) {  // uniform
       patch_slot<NB>(c, slot(s), slot(s) + kSlotP, k0 + (int64_t)s * kBK, s == q_fix, s == p_fix);
-      barrier_lds();
+      turn_barrier();
     }
-    // slot (s - 1) mod kSlots is free: every wave is past compute(s - 1)
+  };
+  auto fetch = [&](int s) {
+    read_operands<NB>(slot(s), slot(s) + kSlotP, wm, wn, c.l, ops);
     if (s + kAhead < nks) stage_dma(s + kAhead);
-    compute<NB>(slot(s), slot(s) + kSlotP, wm, wn, c.l, acc);
+  };
+  if (grp == 0) {
+    for (int s = 0; s < nks; ++s) {
+      arrive(s);
+      fetch(s);
+      turn_barrier();
+      mma<NB>(ops, acc);
+    }
+    turn_barrier();
+  } else if (nks > 0) {
+    arrive(0);
+    turn_barrier();
+    fetch(0);
+    for (int s = 1; s < nks; ++s) {
+      arrive(s);
+      mma<NB>(ops, acc);
+      turn_barrier();
+      fetch(s);
+    }
+    turn_barrier();
+    mma<NB>(ops, acc);
+  } else {
+    turn_barrier();
   }
 
   // ------------------------------------------------------------ epilogue --
@@ -406,7 +461,7 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   // misalignment d = (row * ldc + nb) mod 8, so that LDS chunk k of a row is
   // global 16-byte chunk k of that row's segment.  Lane (L, G) of tile
   // (i, j) holds rows 64 wm + 16 i + 4 G + t, column 16 (NB wn + j) + L.
-  // Every wave is past its last compute: the ring memory is free.
+  // Every wave is past its last LDS read: the ring memory is free.
   barrier_lds();
   const int64_t ldc = O.ldc;
 #pragma unroll
