@@ -253,7 +253,7 @@ constexpr int kPreThreads = 512;  // 8 waves (two per SIMD)
 constexpr int kPreBM = 256;       // rows per workgroup tile
 constexpr int kPreKT = 32;        // k per LDS stage (one MFMA k-step)
 // columns per workgroup tile = 32 * nb, nb in [kPreMinNB, kPreMaxNB]
-constexpr int kPreMinNB = 6;
+constexpr int kPreMinNB = 2;
 constexpr int kPreMaxNB = 7;
 constexpr int kPreSlotBytes = (16 + 15) * 1024;  // one k-step: P (16 KB) + Q of the widest tile (15 KB)
 constexpr int kPreSlots = 5;                      // ring of k-steps in LDS

@@ -94,34 +94,47 @@ __device__ __forceinline__ void lds_write16(char* p, const u32x4_t& v) { *reinte
 // the compiler cannot tell these reads from the direct-to-LDS loads still
 // in flight into other slots and would wait for every one of those.
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-#define LR_TR(dst, off) "ds_read_b64_tr_b16 %" #dst ", %[a] offset:" #off "\n\t"
-template <int NB>
-__device__ __forceinline__ void tr_operands(uint32_t a, u32x4_t (&b)[NB]);
-template <>
-__device__ __forceinline__ void tr_operands<7>(uint32_t a, u32x4_t (&b)[7]) {
-  u32x2_t lo[7], hi[7];  // hi: 16 rows further, 16 * 480 = 7680 bytes
-  asm volatile(LR_TR(0, 0) LR_TR(1, 7680) LR_TR(2, 32) LR_TR(3, 7712) LR_TR(4, 64) LR_TR(5, 7744) LR_TR(6, 96)
-                   LR_TR(7, 7776) LR_TR(8, 128) LR_TR(9, 7808) LR_TR(10, 160) LR_TR(11, 7840) LR_TR(12, 192)
-                       LR_TR(13, 7872) "s_waitcnt lgkmcnt(0)"
-               : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]),
-                 "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]), "=&v"(lo[6]), "=&v"(hi[6])
-               : [a] "v"(a)
-               : "memory");
+// column group j: slot rows l / 4 at byte 32 j, and 16 rows further (offset
+// hi = 16 x the slot pitch, an assembler expression)
+#define LR_TR(j) \
+  "ds_read_b64_tr_b16 %[lo" #j "], %[a] offset:" #j "*32\n\t" \
+  "ds_read_b64_tr_b16 %[hi" #j "], %[a] offset:%[h]+" #j "*32\n\t"
+#define LR_TR_OUT(j) [lo##j] "=&v"(lo[j]), [hi##j] "=&v"(hi[j])
+template <int NB, int HI>
+__device__ __forceinline__ void tr_operands(uint32_t a, u32x4_t (&b)[NB]) {
+  u32x2_t lo[NB], hi[NB];
+  if constexpr (NB == 2) {
+    asm volatile(LR_TR(0) LR_TR(1) "s_waitcnt lgkmcnt(0)"
+                 : LR_TR_OUT(0), LR_TR_OUT(1)
+                 : [a] "v"(a), [h] "n"(HI)
+                 : "memory");
+  } else if constexpr (NB == 3) {
+    asm volatile(LR_TR(0) LR_TR(1) LR_TR(2) "s_waitcnt lgkmcnt(0)"
+                 : LR_TR_OUT(0), LR_TR_OUT(1), LR_TR_OUT(2)
+                 : [a] "v"(a), [h] "n"(HI)
+                 : "memory");
+  } else if constexpr (NB == 4) {
+    asm volatile(LR_TR(0) LR_TR(1) LR_TR(2) LR_TR(3) "s_waitcnt lgkmcnt(0)"
+                 : LR_TR_OUT(0), LR_TR_OUT(1), LR_TR_OUT(2), LR_TR_OUT(3)
+                 : [a] "v"(a), [h] "n"(HI)
+                 : "memory");
+  } else if constexpr (NB == 6) {
+    asm volatile(LR_TR(0) LR_TR(1) LR_TR(2) LR_TR(3) LR_TR(4) LR_TR(5) "s_waitcnt lgkmcnt(0)"
+                 : LR_TR_OUT(0), LR_TR_OUT(1), LR_TR_OUT(2), LR_TR_OUT(3), LR_TR_OUT(4), LR_TR_OUT(5)
+                 : [a] "v"(a), [h] "n"(HI)
+                 : "memory");
+  } else {
+    static_assert(NB == 7, "tile widths 64, 96, 128, 192 and 224");
+    asm volatile(LR_TR(0) LR_TR(1) LR_TR(2) LR_TR(3) LR_TR(4) LR_TR(5) LR_TR(6) "s_waitcnt lgkmcnt(0)"
+                 : LR_TR_OUT(0), LR_TR_OUT(1), LR_TR_OUT(2), LR_TR_OUT(3), LR_TR_OUT(4), LR_TR_OUT(5),
+                   LR_TR_OUT(6)
+                 : [a] "v"(a), [h] "n"(HI)
+                 : "memory");
+  }
 #pragma unroll
-  for (int j = 0; j < 7; ++j) b[j] = u32x4_t{lo[j][0], lo[j][1], hi[j][0], hi[j][1]};
+  for (int j = 0; j < NB; ++j) b[j] = u32x4_t{lo[j][0], lo[j][1], hi[j][0], hi[j][1]};
 }
-template <>
-__device__ __forceinline__ void tr_operands<6>(uint32_t a, u32x4_t (&b)[6]) {
-  u32x2_t lo[6], hi[6];  // hi: 16 rows further, 16 * 416 = 6656 bytes
-  asm volatile(LR_TR(0, 0) LR_TR(1, 6656) LR_TR(2, 32) LR_TR(3, 6688) LR_TR(4, 64) LR_TR(5, 6720) LR_TR(6, 96)
-                   LR_TR(7, 6752) LR_TR(8, 128) LR_TR(9, 6784) LR_TR(10, 160) LR_TR(11, 6816) "s_waitcnt lgkmcnt(0)"
-               : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]),
-                 "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5])
-               : [a] "v"(a)
-               : "memory");
-#pragma unroll
-  for (int j = 0; j < 6; ++j) b[j] = u32x4_t{lo[j][0], lo[j][1], hi[j][0], hi[j][1]};
-}
+#undef LR_TR_OUT
 #undef LR_TR
 // Slot row of k-row kr (0..31) of a Q slot.
 __host__ __device__ __forceinline__ int q_slot_row(int kr) { return 16 * ((kr >> 2) & 1) + 4 * (kr >> 3) + (kr & 3); }
@@ -320,9 +333,8 @@ __device__ __forceinline__ void read_operands(const char* slotP, const char* slo
   // lane l = 16 kq + 4 q + c reads slot rows l / 4 and 16 + l / 4, bytes
   // 8 c of each 32-byte column group (the asm block also waits for the P
   // reads above)
-  static_assert(16 * Geo<NB>::kQPitch == (NB == 7 ? 7680 : 6656), "offsets of tr_operands");
   const char* qb = slotQ + (l >> 2) * Geo<NB>::kQPitch + 8 * (l & 3) + 32 * NB * wn;
-  tr_operands<NB>((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)qb, o.b);
+  tr_operands<NB, 16 * Geo<NB>::kQPitch>((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)qb, o.b);
 }
 template <int NB>
 __device__ __forceinline__ void mma(const Ops<NB>& o, f32x4_t (&acc)[4][NB]) {
@@ -558,6 +570,9 @@ hipError_t launch_prefill_gemm(const PreArgs& args, hipStream_t stream) {
   const int grid = ct * args.row_tiles * args.splits;
   if (grid <= 0) return hipSuccess;
   switch (args.nb) {
+    case 2: return launch_one<2>(args, grid, stream);
+    case 3: return launch_one<3>(args, grid, stream);
+    case 4: return launch_one<4>(args, grid, stream);
     case 6: return launch_one<6>(args, grid, stream);
     case 7: return launch_one<7>(args, grid, stream);
     default: return hipErrorInvalidValue;

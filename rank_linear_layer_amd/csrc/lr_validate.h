@@ -452,14 +452,12 @@ inline bool xcd_plan(int64_t K, int64_t r, int64_t N, int pn, int64_t max_M, Xcd
   return true;
 }
 
-// Prefill launch plan: tile width 32 * nb columns (nb in [6, 7]) and a
-// k-split.  Cost unit: one 32-deep k-step of one workgroup with one MFMA
-// column block per wave (a step costs about nb + 2 units: nb column blocks
-// plus a fixed share for loads and the barrier; one unit is about 0.14 us).
-// A launch takes as many rounds as it has workgroups per compute unit.  A
-// k-split (splits > 1) adds a reduction kernel: one launch (about 14 units)
-// plus writing and reading the fp32 partials (about 700 KB per unit).  The
-// cheapest plan wins (fewer splits, then the wider tile, on a tie).
+// Prefill launch plan: tile width 32 * nb columns and a k-split.  Cost
+// unit: about 0.14 us.  A launch takes as many rounds as it has workgroups
+// per compute unit.  A k-split (splits > 1) adds a reduction kernel: one
+// launch (about 14 units) plus writing and reading the fp32 partials (about
+// 700 KB per unit).  The cheapest plan wins (fewer splits, then the wider
+// tile, on a tie).
 struct PrePlan {
   int nb, splits, split_steps;
   int kind;     // 0: two waves per SIMD, tile 256 x 32 nb; 1: one wave per SIMD, tile 256 x 256
@@ -469,16 +467,19 @@ struct PrePlan {
 // units of about 0.14 us: rounds of the 256-CU machine times (k-steps per
 // split x the kernel's per-step cost + its per-tile cost: start-up,
 // epilogue), plus the partial write/read and reduction launch when k is
-// split.  Per 32-deep k-step of one tile, measured on MI355X at steady clocks
-// (MLP up-projection, M = 4096: 120 us for phase 1 with the two-wave kernel
-// at nb = 6, 1 round of 128 steps; 388 us for phase 2 at nb = 7 and 393 us
-// with the one-wave kernel, 4 rounds of 90 steps): two-wave nb = 6 6.75 and
-// nb = 7 7.7, 40 per tile (80 with fp32 partials); one-wave 7.8, 85 per tile
-// (200 with fp32 partials), k-splits on 64-deep stages.  No cost depends on the
-// weight's leading dimension (r or N) modulo 8: both kernels read misaligned
-// rows with the same instructions as aligned ones.  `kinds`: bit 0 allows
-// the two-wave kernel, bit 1 the one-wave kernel (which needs a 16-byte
-// aligned P: X with K mod 8 = 0, or T).
+// split.  Per 32-deep k-step of one tile, measured on MI355X from kernel
+// traces (MLP up-projection M = 4096: phase 1 at nb = 6, one round of 128
+// steps, 122 us; phase 2 at nb = 7, four rounds of 90 steps, 347-371 us;
+// the one-wave kernel 157 and 433 us; X . W at K = N = 4096 with nb = 4,
+// two rounds of 128 steps, 195 us, and one-wave, one round, 144 us; nb = 2
+// and 3 from the same phases with only that width allowed): two-wave nb = 2
+// 4.2, 3 4.7, 4 5.4, 6 6.7, 7 7.35, 40 per tile (80 with fp32 partials);
+// one-wave 8.3, 85 per tile (200 with fp32 partials), k-splits on 64-deep
+// stages.  No cost depends on the weight's leading dimension (r or N) modulo
+// 8: both kernels read misaligned rows with the same instructions as
+// aligned ones.  `kinds`: bit 0 allows the two-wave kernel, bit 1 the
+// one-wave kernel (which needs a 16-byte aligned P: X with K mod 8 = 0, or
+// T).
 constexpr int kPlanTwoWave = 1;
 constexpr int kPlanOneWave = 2;
 inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int64_t kd, int num_cus,
@@ -493,7 +494,8 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
   const struct {
     int nb, kind;
     double per_step, per_tile, per_tile_split;
-  } kinds[3] = {{8, 1, 7.8, 85.0, 200.0}, {7, 0, 7.7, 40.0, 80.0}, {6, 0, 6.75, 40.0, 80.0}};
+  } kinds[6] = {{8, 1, 8.3, 85.0, 200.0}, {7, 0, 7.35, 40.0, 80.0}, {6, 0, 6.7, 40.0, 80.0},
+                {4, 0, 5.4, 40.0, 80.0},    {3, 0, 4.7, 40.0, 80.0},  {2, 0, 4.2, 40.0, 80.0}};
   for (const auto& kn : kinds) {
     if (!(kinds_allowed & (kn.kind == 1 ? kPlanOneWave : kPlanTwoWave))) continue;
     const int gran = kn.kind == 1 ? 2 : 1;
