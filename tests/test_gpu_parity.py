@@ -229,10 +229,11 @@ def test_mlp_packed_prefill_k_split(M):
 
 
 # ------------------------------------------------- prefill kernel kinds ---
-# Each prefill kernel forced on its own: the two-wave kernel (256 x 192 or
-# 224 tiles, weight rows read with the transposing LDS read) and the
-# one-wave kernel (256 x 256 tiles, weight rows transposed in registers).  Phase 1 reads A (leading dimension r) and phase 2 reads
-# B (leading dimension N), so the first eight shapes cover every r mod 8 and
+# Each prefill kernel forced on its own: the two-wave kernel (256 x 32 nb
+# tiles, weight rows read with the transposing LDS read) and the one-wave
+# kernel (256 x 256 tiles, weight rows transposed in registers).  Phase 1
+# reads A (leading dimension r) and phase 2 reads B (leading dimension N),
+# so the first eight shapes cover every r mod 8 and
 # N mod 8; the rest add ragged M, partial column tiles, rank padding,
 # k-splits and a misaligned X (K mod 8 != 0: phase 1 falls back to the
 # two-wave kernel).
