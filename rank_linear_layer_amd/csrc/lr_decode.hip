@@ -184,16 +184,18 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   const int64_t jrow0 = (int64_t)j0 + 32 * w;
   const int64_t jrow_end = min64(r, (int64_t)j0 + kDecJS);
 
-  RawTile t0, t1, b0, b1;
-  u32x4_t x0 = zerou4(), x1 = zerou4();
-  int kt = kt_beg + w;
-  if (kt < kt_end) {
-    load_tile_raw(t0, rA, (int64_t)kt * kDecKT, r, j0, np, g);
-    x0 = load_kvec(rX, np, K, (int64_t)kt * kDecKT + 8 * g, K, xal);
-  }
-  if (kt + kDecWaves < kt_end) {
-    load_tile_raw(t1, rA, (int64_t)(kt + kDecWaves) * kDecKT, r, j0, np, g);
-    x1 = load_kvec(rX, np, K, (int64_t)(kt + kDecWaves) * kDecKT + 8 * g, K, xal);
+  // This wave's k-tiles are kt0, kt0 + 4, ...; a ring of kDecABuf of them is
+  // in flight from the start (with the X segments they meet), and each is
+  // requested again right after its use, with no branch around a load.
+  constexpr int kDecABuf = 4;
+  RawTile ta[kDecABuf], b0, b1;
+  u32x4_t xa[kDecABuf];
+  const int kt0 = kt_beg + w;
+#pragma unroll
+  for (int i = 0; i < kDecABuf; ++i) {
+    const int k = kt0 + kDecWaves * i;
+    load_tile_raw_if(ta[i], rA, (int64_t)k * kDecKT, r, j0, np, g, k < kt_end);
+    xa[i] = load_kvec(rX, np, K, (int64_t)k * kDecKT + 8 * g, K, xal);
   }
   if (nt_beg < nt_end) load_tile_raw(b0, rB, jrow0, N, (int64_t)nt_beg * kDecNT, np, g);
   if (nt_beg + 1 < nt_end) load_tile_raw(b1, rB, jrow0, N, (int64_t)(nt_beg + 1) * kDecNT, np, g);
@@ -202,31 +204,20 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   f32x4_t acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = zero4();
-  while (kt < kt_end) {
-    {
-      u32x4_t op[8];
-      tile_operands(t0, op, (int64_t)kt * kDecKT, g, K, r, j0, np, r);
-      const u32x4_t xm = kvec_mask(x0, (int64_t)kt * kDecKT + 8 * g, K);
+  for (int base = kt0; base < kt_end; base += kDecWaves * kDecABuf) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = mfma_16x16x32(xm, op[e], acc[e]);
-    }
-    kt += kDecWaves;
-    if (kt + kDecWaves < kt_end) {
-      load_tile_raw(t0, rA, (int64_t)(kt + kDecWaves) * kDecKT, r, j0, np, g);
-      x0 = load_kvec(rX, np, K, (int64_t)(kt + kDecWaves) * kDecKT + 8 * g, K, xal);
-    }
-    if (kt >= kt_end) break;
-    {
-      u32x4_t op[8];
-      tile_operands(t1, op, (int64_t)kt * kDecKT, g, K, r, j0, np, r);
-      const u32x4_t xm = kvec_mask(x1, (int64_t)kt * kDecKT + 8 * g, K);
+    for (int i = 0; i < kDecABuf; ++i) {
+      const int k = base + kDecWaves * i;
+      if (k < kt_end) {
+        u32x4_t op[8];
+        tile_operands(ta[i], op, (int64_t)k * kDecKT, g, K, r, j0, np, r);
+        const u32x4_t xm = kvec_mask(xa[i], (int64_t)k * kDecKT + 8 * g, K);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = mfma_16x16x32(xm, op[e], acc[e]);
-    }
-    kt += kDecWaves;
-    if (kt + kDecWaves < kt_end) {
-      load_tile_raw(t1, rA, (int64_t)(kt + kDecWaves) * kDecKT, r, j0, np, g);
-      x1 = load_kvec(rX, np, K, (int64_t)(kt + kDecWaves) * kDecKT + 8 * g, K, xal);
+        for (int e = 0; e < 8; ++e) acc[e] = mfma_16x16x32(xm, op[e], acc[e]);
+      }
+      const int kn = k + kDecWaves * kDecABuf;
+      load_tile_raw_if(ta[i], rA, (int64_t)kn * kDecKT, r, j0, np, g, kn < kt_end);
+      xa[i] = load_kvec(rX, np, K, (int64_t)kn * kDecKT + 8 * g, K, xal);
     }
   }
 
