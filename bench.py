@@ -20,6 +20,7 @@ bounded sample as a baseline.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -73,16 +74,26 @@ def dev_bf16(torch, bits):
 
 
 def time_steps(torch, fn, steps, warmup, stream):
+    """Event-timed average step.  Python's cyclic garbage collector is run
+    before the timed region and held off during it: a collection that
+    starts inside the launch loop stalls the host for about a millisecond,
+    the GPU runs dry, and a short step reads up to 1.7x slower (seen as a
+    one-point dip at a fixed place of the rank sweep)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(steps):
-        fn(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
+    try:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
     return e0.elapsed_time(e1) / steps  # ms per step
 
 
