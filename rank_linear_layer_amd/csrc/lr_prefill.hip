@@ -405,9 +405,10 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   const int grp = c.w >> 2;
   Ops<NB> ops;
   for (int t = 0; t < kAhead && t < nks; ++t) stage_dma(t);
-  // wait for stage s, publish it, patch it where needed
-  auto arrive = [&](int s) {
-    wait_stages(min(kAhead - 1, nks - 1 - s));
+  // wait for stage s, publish it, patch it where needed; `steady`: three
+  // later stages are in flight (a constant wait, no branch on the count)
+  auto arrive = [&](int s, bool steady) {
+    wait_stages(steady ? kAhead - 1 : min(kAhead - 1, nks - 1 - s));
     turn_barrier();
     if (s == q_fix || s == p_fix) {  // uniform
       patch_slot<NB>(c, slot(s), slot(s) + kSlotP, k0 + (int64_t)s * kBK, s == q_fix, s == p_fix);
@@ -418,20 +419,35 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
     read_operands<NB>(slot(s), slot(s) + kSlotP, wm, wn, c.l, ops);
     if (s + kAhead < nks) stage_dma(s + kAhead);
   };
+  const int steady_end = nks - (kAhead - 1);  // k-steps with three later stages in flight
   if (grp == 0) {
-    for (int s = 0; s < nks; ++s) {
-      arrive(s);
+    int s = 0;
+    for (; s < steady_end; ++s) {
+      arrive(s, true);
+      fetch(s);
+      turn_barrier();
+      mma<NB>(ops, acc);
+    }
+    for (; s < nks; ++s) {
+      arrive(s, false);
       fetch(s);
       turn_barrier();
       mma<NB>(ops, acc);
     }
     turn_barrier();
   } else if (nks > 0) {
-    arrive(0);
+    arrive(0, steady_end > 0);
     turn_barrier();
     fetch(0);
-    for (int s = 1; s < nks; ++s) {
-      arrive(s);
+    int s = 1;
+    for (; s < steady_end; ++s) {
+      arrive(s, true);
+      mma<NB>(ops, acc);
+      turn_barrier();
+      fetch(s);
+    }
+    for (; s < nks; ++s) {
+      arrive(s, false);
       mma<NB>(ops, acc);
       turn_barrier();
       fetch(s);
