@@ -325,14 +325,18 @@ template <int NB>
 struct Ops {
   u32x4_t a[4], b[NB];
 };
+// The P operands (plain LDS reads: the compiler waits for them before the
+// MFMAs that use them) and the B operands (one asm block that also waits for
+// the P reads issued before it).
 template <int NB>
-__device__ __forceinline__ void read_operands(const char* slotP, const char* slotQ, int wm, int wn, int l,
-                                              Ops<NB>& o) {
+__device__ __forceinline__ void read_p(const char* slotP, int wm, int l, Ops<NB>& o) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o.a[i] = lds_read16(slotP + (4 * wm + i) * 1024 + 16 * l);
+}
+template <int NB>
+__device__ __forceinline__ void read_q(const char* slotQ, int wn, int l, Ops<NB>& o) {
   // lane l = 16 kq + 4 q + c reads slot rows l / 4 and 16 + l / 4, bytes
-  // 8 c of each 32-byte column group (the asm block also waits for the P
-  // reads above)
+  // 8 c of each 32-byte column group
   const char* qb = slotQ + (l >> 2) * Geo<NB>::kQPitch + 8 * (l & 3) + 32 * NB * wn;
   tr_operands<NB, 16 * Geo<NB>::kQPitch>((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)qb, o.b);
 }
@@ -415,9 +419,12 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
       turn_barrier();
     }
   };
+  // the P reads go out first, the next loads are issued while they are in
+  // flight, and the B reads (which wait for everything) come last
   auto fetch = [&](int s) {
-    read_operands<NB>(slot(s), slot(s) + kSlotP, wm, wn, c.l, ops);
+    read_p<NB>(slot(s), wm, c.l, ops);
     if (s + kAhead < nks) stage_dma(s + kAhead);
+    read_q<NB>(slot(s) + kSlotP, wn, c.l, ops);
   };
   const int steady_end = nks - (kAhead - 1);  // k-steps with three later stages in flight
   if (grp == 0) {
