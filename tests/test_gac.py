@@ -122,6 +122,32 @@ def test_candidate_filter_of_the_sweep():
     assert c == [d for d in range(96, 129, 8)]
 
 
+def test_page_candidate_set_end_to_end():
+    # The page's candidate set for d* = 107.3 (section 4.2: C = {96, 104,
+    # 112, 128}) for two weights of equal cost c, budget = both weights at
+    # d* (214.6 c, so d1 + d2 <= 214) and scores 2 and 1.  By hand: the
+    # pairs that fit are those with d1 + d2 <= 214; the objective
+    # sum_i s_i c (d_i - 107.3) is largest for (112, 96): 2 (4.7) - 11.3 =
+    # -1.9 per c, against (104, 104): -9.9, (96, 112): -17.9, (104, 96):
+    # -23.2.  Exhaustive search and the library agree with that.
+    gac = _gac()
+    C = [96, 104, 112, 128]
+    c = 4096
+    scores, costs, dstar = [2.0, 1.0], [c, c], [107.3, 107.3]
+    budget = int(c * 214.6)
+    best, optimal = ref.best_selection(scores, costs, dstar, [C, C], budget, c)
+    assert optimal == [[112, 96]]
+    assert float(best) == pytest.approx(c * (2 * 4.7 - 11.3), rel=1e-12)
+    dims, obj = gac.select(scores, costs, dstar, [C, C], budget, c)
+    assert dims == [112, 96] and obj == pytest.approx(float(best), rel=1e-12)
+    # with equal scores the objective is c (d1 + d2 - 214.6): every pair
+    # summing to 208 ties, and the library returns one of them
+    best2, optimal2 = ref.best_selection([1.0, 1.0], costs, dstar, [C, C], budget, c)
+    assert sorted(optimal2) == [[96, 112], [104, 104], [112, 96]]
+    dims2, _ = gac.select([1.0, 1.0], costs, dstar, [C, C], budget, c)
+    assert dims2 in optimal2
+
+
 def test_layer_scale_instance_beats_rounding_down():
     # 32 layers x 7 projections of the Llama-3-8B-shaped layer at 15%
     # compression: the program's choice fits the budget and keeps at least
