@@ -24,9 +24,9 @@
 // that starts at the exact element it needs: gfx950's buffer loads return
 // the 16 bytes at any 2-byte aligned offset.  Loads run four k-steps ahead
 // into a ring of five slots, each holding
-//   P  256 rows x 32 k of X or T in MFMA operand order (16-row block b,
-//      chunk c, row L at b*1024 + c*256 + L*16: one operand read is 1 KB
-//      contiguous per wave)
+//   P  256 rows x 32 k of X or T in 16-row blocks of 1 KB; chunk c of row
+//      L at 16 (4 L + (c ^ (L / 4 mod 4))): a lane quad loads one row's 64
+//      bytes, and the MFMA operand reads are free of bank conflicts
 //   Q  32 rows x 32*NB columns of A or B, row-major with a pitch of
 //      64 NB + 32 bytes, k-row 8 kq + 4 h + q stored at slot row
 //      16 h + 4 kq + q.
@@ -205,13 +205,21 @@ struct PDma {
   uint32_t off0[2];  // byte offset at k-step 0 of this split
   int kcol;          // lane's first column at k-step 0
 };
+// Position (16-byte unit) of chunk c of row L in a 16-row P block: the four
+// lanes of a quad load one row's 64 bytes (whole row segments per request),
+// and the XOR by L / 4 keeps the MFMA operand reads (16 lanes, one chunk of
+// 16 rows) free of bank conflicts.
+__device__ __forceinline__ int p_pos(int L, int c) { return 4 * L + (c ^ ((L >> 2) & 3)); }
+// Row and chunk that lane l of a P load fills (the inverse of p_pos).
+__device__ __forceinline__ int p_row(int l) { return l >> 2; }
+__device__ __forceinline__ int p_chunk(int l) { return (l & 3) ^ ((l >> 4) & 3); }
 __device__ __forceinline__ void p_dma_init(const Ctx& c, int64_t k0, PDma& d) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int64_t row = c.mb + 16 * (c.w + 8 * h) + (c.l & 15);
-    d.off0[h] = (uint32_t)((row * c.ldp + k0 + 8 * (c.l >> 4)) * 2);
+    const int64_t row = c.mb + 16 * (c.w + 8 * h) + p_row(c.l);
+    d.off0[h] = (uint32_t)((row * c.ldp + k0 + 8 * p_chunk(c.l)) * 2);
   }
-  d.kcol = (int)(k0 + 8 * (c.l >> 4));
+  d.kcol = (int)(k0 + 8 * p_chunk(c.l));
 }
 __device__ __forceinline__ void p_dma(const Ctx& c, const PDma& d, char* slotP, int t) {
   const bool ok = (int64_t)d.kcol + 32 * t < c.kd;
@@ -282,12 +290,12 @@ __device__ __forceinline__ void patch_slot(const Ctx& c, char* slotP, char* slot
         (uint16_t)scalar_elem(c.Q, c.qrows * c.ldq - 1);
   }
   if (fix_p) {
-    const int64_t kk = kstep0 + 8 * (c.l >> 4);
+    const int64_t kk = kstep0 + 8 * p_chunk(c.l);
     if (kk < c.kd && kk + 8 > c.kd) {
       const int valid = (int)(c.kd - kk);  // 1 .. 7 elements of this chunk lie below kd
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int64_t row = c.mb + 16 * (c.w + 8 * h) + (c.l & 15);
+        const int64_t row = c.mb + 16 * (c.w + 8 * h) + p_row(c.l);
         char* p = slotP + (c.w + 8 * h) * 1024 + 16 * c.l;
         u32x4_t v = lds_read16(p);
 #pragma unroll
@@ -330,8 +338,9 @@ struct Ops {
 // the P reads issued before it).
 template <int NB>
 __device__ __forceinline__ void read_p(const char* slotP, int wm, int l, Ops<NB>& o) {
+  const int off = 16 * p_pos(l & 15, l >> 4);  // row l % 16, chunk l / 16
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o.a[i] = lds_read16(slotP + (4 * wm + i) * 1024 + 16 * l);
+  for (int i = 0; i < 4; ++i) o.a[i] = lds_read16(slotP + (4 * wm + i) * 1024 + off);
 }
 template <int NB>
 __device__ __forceinline__ void read_q(const char* slotQ, int wn, int l, Ops<NB>& o) {
