@@ -469,13 +469,13 @@ struct PrePlan {
 // epilogue), plus the partial write/read and reduction launch when k is
 // split.  Per 32-deep k-step of one tile, measured on MI355X from kernel
 // traces (MLP up-projection M = 4096: phase 1 at nb = 6, one round of 128
-// steps, 122 us; phase 2 at nb = 7, four rounds of 90 steps, 347-371 us;
-// the one-wave kernel 157 and 433 us; X . W at K = N = 4096 with nb = 4,
-// two rounds of 128 steps, 195 us, and one-wave, one round, 144 us; nb = 2
-// and 3 from the same phases with only that width allowed): two-wave nb = 2
-// 4.2, 3 4.7, 4 5.4, 6 6.7, 7 7.35, 40 per tile (80 with fp32 partials);
-// one-wave 8.3, 85 per tile (200 with fp32 partials), k-splits on 64-deep
-// stages.  No cost depends on the weight's leading dimension (r or N) modulo
+// steps, 106 us; phase 2 at nb = 7, four rounds of 90 steps, 325 us; the
+// one-wave kernel 156 and 432 us; X . W at K = N = 4096 with nb = 4, two
+// rounds of 128 steps, 165 us, and one-wave, one round, 151 us; nb = 2 and
+// 3 scaled from the same phases with only that width allowed): two-wave
+// nb = 2 3.6, 3 4.0, 4 4.6, 6 6.0, 7 6.4, 40 per tile (80 with fp32
+// partials); one-wave 8.3, 85 per tile (200 with fp32 partials), k-splits on
+// 64-deep stages.  No cost depends on the weight's leading dimension (r or N) modulo
 // 8: both kernels read misaligned rows with the same instructions as
 // aligned ones.  `kinds`: bit 0 allows the two-wave kernel, bit 1 the
 // one-wave kernel (which needs a 16-byte aligned P: X with K mod 8 = 0, or
@@ -494,8 +494,8 @@ inline PrePlan prefill_plan(int64_t rows, const int64_t* out_cols, int nout, int
   const struct {
     int nb, kind;
     double per_step, per_tile, per_tile_split;
-  } kinds[6] = {{8, 1, 8.3, 85.0, 200.0}, {7, 0, 7.35, 40.0, 80.0}, {6, 0, 6.7, 40.0, 80.0},
-                {4, 0, 5.4, 40.0, 80.0},    {3, 0, 4.7, 40.0, 80.0},  {2, 0, 4.2, 40.0, 80.0}};
+  } kinds[6] = {{8, 1, 8.3, 85.0, 200.0}, {7, 0, 6.4, 40.0, 80.0}, {6, 0, 6.0, 40.0, 80.0},
+                {4, 0, 4.6, 40.0, 80.0},    {3, 0, 4.0, 40.0, 80.0},  {2, 0, 3.6, 40.0, 80.0}};
   for (const auto& kn : kinds) {
     if (!(kinds_allowed & (kn.kind == 1 ? kPlanOneWave : kPlanTwoWave))) continue;
     const int gran = kn.kind == 1 ? 2 : 1;
