@@ -84,58 +84,34 @@ struct Geo {
 
 
 __device__ __forceinline__ u32x4_t lds_read16(const char* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-__device__ __forceinline__ void lds_write16(char* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
-// Transposing LDS reads of the NB B operands of a wave: within a 16-lane
-// group, lane 4 q + c reads 8 bytes (row q, columns 4 c .. 4 c + 3 of a
-// 4 x 16 bf16 tile) and receives the 4 values of column (lane mod 16).
-// Operand j takes the 32-byte column group j of slot rows l / 4 (k-rows
-// 8 kq + q) and 16 + l / 4 (k-rows 8 kq + 4 + q) from base address `a`.
-// One asm block issues every read and then waits for them: left to itself
-// the compiler cannot tell these reads from the direct-to-LDS loads still
-// in flight into other slots and would wait for every one of those.
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-// column group j: slot rows l / 4 at byte 32 j, and 16 rows further (offset
-// hi = 16 x the slot pitch, an assembler expression)
-#define LR_TR(j) \
-  "ds_read_b64_tr_b16 %[lo" #j "], %[a] offset:" #j "*32\n\t" \
-  "ds_read_b64_tr_b16 %[hi" #j "], %[a] offset:%[h]+" #j "*32\n\t"
-#define LR_TR_OUT(j) [lo##j] "=&v"(lo[j]), [hi##j] "=&v"(hi[j])
-template <int NB, int HI>
-__device__ __forceinline__ void tr_operands(uint32_t a, u32x4_t (&b)[NB]) {
-  u32x2_t lo[NB], hi[NB];
-  if constexpr (NB == 2) {
-    asm volatile(LR_TR(0) LR_TR(1) "s_waitcnt lgkmcnt(0)"
-                 : LR_TR_OUT(0), LR_TR_OUT(1)
-                 : [a] "v"(a), [h] "n"(HI)
-                 : "memory");
-  } else if constexpr (NB == 3) {
-    asm volatile(LR_TR(0) LR_TR(1) LR_TR(2) "s_waitcnt lgkmcnt(0)"
-                 : LR_TR_OUT(0), LR_TR_OUT(1), LR_TR_OUT(2)
-                 : [a] "v"(a), [h] "n"(HI)
-                 : "memory");
-  } else if constexpr (NB == 4) {
-    asm volatile(LR_TR(0) LR_TR(1) LR_TR(2) LR_TR(3) "s_waitcnt lgkmcnt(0)"
-                 : LR_TR_OUT(0), LR_TR_OUT(1), LR_TR_OUT(2), LR_TR_OUT(3)
-                 : [a] "v"(a), [h] "n"(HI)
-                 : "memory");
-  } else if constexpr (NB == 6) {
-    asm volatile(LR_TR(0) LR_TR(1) LR_TR(2) LR_TR(3) LR_TR(4) LR_TR(5) "s_waitcnt lgkmcnt(0)"
-                 : LR_TR_OUT(0), LR_TR_OUT(1), LR_TR_OUT(2), LR_TR_OUT(3), LR_TR_OUT(4), LR_TR_OUT(5)
-                 : [a] "v"(a), [h] "n"(HI)
-                 : "memory");
-  } else {
-    static_assert(NB == 7, "tile widths 64, 96, 128, 192 and 224");
-    asm volatile(LR_TR(0) LR_TR(1) LR_TR(2) LR_TR(3) LR_TR(4) LR_TR(5) LR_TR(6) "s_waitcnt lgkmcnt(0)"
-                 : LR_TR_OUT(0), LR_TR_OUT(1), LR_TR_OUT(2), LR_TR_OUT(3), LR_TR_OUT(4), LR_TR_OUT(5),
-                   LR_TR_OUT(6)
-                 : [a] "v"(a), [h] "n"(HI)
-                 : "memory");
-  }
-#pragma unroll
-  for (int j = 0; j < NB; ++j) b[j] = u32x4_t{lo[j][0], lo[j][1], hi[j][0], hi[j][1]};
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
-#undef LR_TR_OUT
-#undef LR_TR
+// Raw buffer resource (base, no stride, `bytes` rounded up to whole dwords).
+__device__ __forceinline__ i32x4_t rsrc4(const void* base, int64_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return i32x4_t{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)(uint32_t)((bytes + 3) & ~(int64_t)3),
+                 kRsrcFlags};
+}
+// 16 bytes per lane from byte offset `off` of the buffer into LDS at
+// lds_base + 16 * lane.  Issued from asm: the compiler then does not count
+// it among the stores to LDS that an LDS read has to wait for (the loop
+// waits for its loads with explicit counts).  No register receives data.
+__device__ __forceinline__ void dma16a(const i32x4_t& r, uint32_t lds_base, uint32_t off) {
+  // one wait state between the write of M0 and the load that reads it
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ void lds_write16(char* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+// Transposing LDS read (ds_read_b64_tr_b16): within a 16-lane group, lane
+// 4 q + c reads 8 bytes (row q, columns 4 c .. 4 c + 3 of a 4 x 16 bf16
+// tile) and receives the 4 values of column (lane mod 16).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+__device__ __forceinline__ u32x2_t lds_read_tr(const lds_s16x4_t* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_t*>(p)));
+}
 // Slot row of k-row kr (0..31) of a Q slot.
 __host__ __device__ __forceinline__ int q_slot_row(int kr) { return 16 * ((kr >> 2) & 1) + 4 * (kr >> 3) + (kr & 3); }
 
@@ -185,7 +161,7 @@ __device__ __forceinline__ Tile map_tile(const PreArgs& a, int bn, int bid) {
 }
 
 struct Ctx {
-  rsrc_t rP, rQ;
+  i32x4_t rP, rQ;
   const uint16_t* P;
   const uint16_t* Q;
   int64_t rows, ldp, kd, ldq, qrows, mb, nb;
@@ -224,7 +200,7 @@ __device__ __forceinline__ void p_dma_init(const Ctx& c, int64_t k0, PDma& d) {
 __device__ __forceinline__ void p_dma(const Ctx& c, const PDma& d, char* slotP, int t) {
   const bool ok = (int64_t)d.kcol + 32 * t < c.kd;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) dma16(c.rP, slotP + (c.w + 8 * h) * 1024, ok ? d.off0[h] + 64u * t : kOutOfRange);
+  for (int h = 0; h < 2; ++h) dma16a(c.rP, lds_addr(slotP + (c.w + 8 * h) * 1024), ok ? d.off0[h] + 64u * t : kOutOfRange);
 }
 
 // Q slot: Geo::kQInst loads of 1 KB; wave w issues loads w and w + 8 (when
@@ -260,7 +236,7 @@ __device__ __forceinline__ void q_dma(const Ctx& c, const QDma& d, char* slotQ, 
     // into a spare 1 KB of LDS, so that every wave counts kDmaPerStage loads
     const bool real = c.w + 8 * h < Geo<NB>::kQInst;  // uniform
     const bool ok = real && d.ok[h] && (int64_t)d.krow[h] + 32 * t < c.qrows;
-    dma16(c.rQ, real ? slotQ + (c.w + 8 * h) * 1024 : dummy, ok ? d.off0[h] + stride * (uint32_t)t : kOutOfRange);
+    dma16a(c.rQ, lds_addr(real ? slotQ + (c.w + 8 * h) * 1024 : dummy), ok ? d.off0[h] + stride * (uint32_t)t : kOutOfRange);
   }
 }
 // Direct loads per wave and k-step: two of P, two of Q.
@@ -327,15 +303,24 @@ __device__ __forceinline__ void turn_barrier() {
   barrier_lds();
   __builtin_amdgcn_sched_barrier(0);
 }
+// The barrier between a group's operand reads and its MFMAs: it does not
+// wait for those reads (the MFMAs wait for the operands they use), only for
+// the other group to finish its MFMAs' issue.
+__device__ __forceinline__ void handoff_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // The operands of one k-step, in registers until the MFMAs consume them.
 template <int NB>
 struct Ops {
   u32x4_t a[4], b[NB];
 };
-// The P operands (plain LDS reads: the compiler waits for them before the
-// MFMAs that use them) and the B operands (one asm block that also waits for
-// the P reads issued before it).
+// The operand reads of one k-step: the compiler waits for each before the
+// first MFMA that uses it.  (The direct loads are issued from asm, so the
+// compiler does not make these reads wait for the loads still in flight
+// into other slots.)
 template <int NB>
 __device__ __forceinline__ void read_p(const char* slotP, int wm, int l, Ops<NB>& o) {
   const int off = 16 * p_pos(l & 15, l >> 4);  // row l % 16, chunk l / 16
@@ -346,8 +331,14 @@ template <int NB>
 __device__ __forceinline__ void read_q(const char* slotQ, int wn, int l, Ops<NB>& o) {
   // lane l = 16 kq + 4 q + c reads slot rows l / 4 and 16 + l / 4, bytes
   // 8 c of each 32-byte column group
-  const char* qb = slotQ + (l >> 2) * Geo<NB>::kQPitch + 8 * (l & 3) + 32 * NB * wn;
-  tr_operands<NB, 16 * Geo<NB>::kQPitch>((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)qb, o.b);
+  const uint32_t a = lds_addr(slotQ) + (uint32_t)((l >> 2) * Geo<NB>::kQPitch + 8 * (l & 3) + 32 * NB * wn);
+  const lds_s16x4_t* q = (const lds_s16x4_t*)(uintptr_t)a;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    // 8-byte elements: column group j at byte 32 j, the second half 16 slot rows further
+    const u32x2_t lo = lds_read_tr(q + 4 * j), hi = lds_read_tr(q + 2 * Geo<NB>::kQPitch + 4 * j);
+    o.b[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  }
 }
 template <int NB>
 __device__ __forceinline__ void mma(const Ops<NB>& o, f32x4_t (&acc)[4][NB]) {
@@ -362,8 +353,8 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   constexpr int BN = 32 * NB;
   const PreOut& O = a.o[T.bi];
   Ctx c;
-  c.rP = make_rsrc(O.P, a.rows * O.ldp * 2);
-  c.rQ = make_rsrc(O.Q, O.qrows * O.ldq * 2);
+  c.rP = rsrc4(O.P, a.rows * O.ldp * 2);
+  c.rQ = rsrc4(O.Q, O.qrows * O.ldq * 2);
   c.P = O.P;
   c.Q = O.Q;
   c.rows = a.rows;
@@ -405,9 +396,11 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
 
   // The two waves of a SIMD take turns (waves 0-3 and 4-7, one of each per
   // SIMD): between two barriers one group issues its MFMAs while the other
-  // reads its next operands from LDS and issues the next loads, so the
-  // matrix cores stay busy while the LDS reads of the other group are in
-  // flight.  Group 0 reads stage t, then multiplies it; group 1 multiplies
+  // issues its next operand reads and the next loads, so the matrix cores
+  // stay busy while the LDS reads of the other group are in flight.  The
+  // barrier between a group's reads and its MFMAs (the hand-off) does not
+  // wait for the reads; the barrier that opens a k-step does, and every slot
+  // is refilled only after one of those.  Group 0 reads stage t, then multiplies it; group 1 multiplies
   // stage t - 1 while group 0 reads t, and reads t while group 0
   // multiplies.  Both groups meet the same barriers:
   //   wait for stage t; barrier; [patch; barrier]; X; barrier; Y
@@ -429,7 +422,7 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
     }
   };
   // the P reads go out first, the next loads are issued while they are in
-  // flight, and the B reads (which wait for everything) come last
+  // flight, and the B reads come last; nothing here waits for them
   auto fetch = [&](int s) {
     read_p<NB>(slot(s), wm, c.l, ops);
     if (s + kAhead < nks) stage_dma(s + kAhead);
@@ -441,31 +434,31 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
     for (; s < steady_end; ++s) {
       arrive(s, true);
       fetch(s);
-      turn_barrier();
+      handoff_barrier();
       mma<NB>(ops, acc);
     }
     for (; s < nks; ++s) {
       arrive(s, false);
       fetch(s);
-      turn_barrier();
+      handoff_barrier();
       mma<NB>(ops, acc);
     }
     turn_barrier();
   } else if (nks > 0) {
     arrive(0, steady_end > 0);
-    turn_barrier();
+    handoff_barrier();
     fetch(0);
     int s = 1;
     for (; s < steady_end; ++s) {
       arrive(s, true);
       mma<NB>(ops, acc);
-      turn_barrier();
+      handoff_barrier();
       fetch(s);
     }
     for (; s < nks; ++s) {
       arrive(s, false);
       mma<NB>(ops, acc);
-      turn_barrier();
+      handoff_barrier();
       fetch(s);
     }
     turn_barrier();
