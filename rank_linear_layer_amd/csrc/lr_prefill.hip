@@ -131,15 +131,21 @@ struct Tile {
   int64_t nb;  // first column
 };
 
-// Workgroup id -> tile.  XCD x (= id mod 8) receives the contiguous run
-// [x*q + min(x, rem), ...) of the tile order; the order is row-tile groups of
-// kGroupRows, walked column tile by column tile across both outputs.
-__device__ __forceinline__ Tile map_tile(const PreArgs& a, int bn, int bid) {
+// Workgroup id -> (tile, k-split).  The units of a launch are ordered
+// split by split, and within a split row-tile groups of kGroupRows walked
+// column tile by column tile across all the outputs.  XCD x (= id mod 8)
+// receives the contiguous run [x*q + min(x, rem), ...) of that order, so
+// the workgroups resident on one XCD share P and Q panels, and with a
+// k-split each XCD reads the k-range of one or two splits only.
+__device__ __forceinline__ Tile map_unit(const PreArgs& a, int bn, int bid, int& ks) {
   const int ct_total = total_col_tiles(a);
-  const int total = a.row_tiles * ct_total;
+  const int tiles = a.row_tiles * ct_total;
+  const int total = tiles * a.splits;
   const int q = total >> 3, rem = total & 7;
   const int x = bid & 7, j = bid >> 3;
-  const int t = x * q + min(x, rem) + j;
+  const int u = x * q + min(x, rem) + j;
+  ks = u / tiles;
+  const int t = u - ks * tiles;
   const int per_group = kGroupRows * ct_total;
   const int grp = t / per_group;
   const int first = grp * kGroupRows;
@@ -544,11 +550,8 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
 template <int NB>
 __global__ __launch_bounds__(kThreads, 1) void lr_prefill_gemm_kernel(const PreArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // workgroup -> (tile, k-split): consecutive ids are different tiles of one
-  // split, so the XCD dealing of tiles is the same for every split
-  const int tiles = a.row_tiles * total_col_tiles(a);
-  const int ks = (int)blockIdx.x / tiles;
-  const Tile T = map_tile(a, 32 * NB, (int)blockIdx.x - ks * tiles);
+  int ks;
+  const Tile T = map_unit(a, 32 * NB, (int)blockIdx.x, ks);
   gemm_tile<NB>(a, T, ks, smem);
 }
 

@@ -128,15 +128,20 @@ struct Tile {
   int64_t mb, nb;
 };
 
-// Tiles are dealt so that each XCD (workgroup id mod 8) gets one contiguous
-// run of the tile order, which walks groups of four row tiles column by
-// column: the workgroups on one XCD share P and weight panels in its L2.
-__device__ __forceinline__ Tile map_tile(const PreArgs& a, int bid) {
+// Workgroup id -> (tile, k-split).  Units are ordered split by split, and
+// within a split the tile order walks groups of four row tiles column by
+// column.  Each XCD (workgroup id mod 8) gets one contiguous run of that
+// order: the workgroups on one XCD share P and weight panels in its L2, and
+// with a k-split each XCD reads the k-range of one or two splits only.
+__device__ __forceinline__ Tile map_unit(const PreArgs& a, int bid, int& ks) {
   const int ct_total = total_col_tiles(a);
-  const int total = a.row_tiles * ct_total;
+  const int tiles = a.row_tiles * ct_total;
+  const int total = tiles * a.splits;
   const int q = total >> 3, rem = total & 7;
   const int x = bid & 7, j = bid >> 3;
-  const int t = x * q + min(x, rem) + j;
+  const int u = x * q + min(x, rem) + j;
+  ks = u / tiles;
+  const int t = u - ks * tiles;
   const int per_group = kGroupRows * ct_total;
   const int grp = t / per_group;
   const int first = grp * kGroupRows;
@@ -489,9 +494,8 @@ __device__ __forceinline__ void w4_tile(const PreArgs& a, const Tile& T, int ks,
 
 __global__ __launch_bounds__(kThreads, 1) void lr_prefill_w4_kernel(const PreArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int tiles = a.row_tiles * total_col_tiles(a);
-  const int ks = (int)blockIdx.x / tiles;
-  const Tile T = map_tile(a, (int)blockIdx.x - ks * tiles);
+  int ks;
+  const Tile T = map_unit(a, (int)blockIdx.x, ks);
   if (a.o[T.bi].ldq - T.nb < kBN)
     w4_tile<true>(a, T, ks, smem);
   else
