@@ -73,15 +73,27 @@ def dev_bf16(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def time_steps(torch, fn, steps, warmup, stream):
+def time_steps(torch, fn, steps, warmup, stream, warm_seconds=0.0):
     """Event-timed average step.  Python's cyclic garbage collector is run
     before the timed region and held off during it: a collection that
     starts inside the launch loop stalls the host for about a millisecond,
     the GPU runs dry, and a short step reads up to 1.7x slower (seen as a
-    one-point dip at a fixed place of the rank sweep)."""
+    one-point dip at a fixed place of the rank sweep).  `warm_seconds` keeps
+    running warm-up steps until that much time has passed: the compute-bound
+    prefill steps otherwise start timing before the GPU clock has risen from
+    the lighter load before them (the first launches of a run are up to 25%
+    slower)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    if warm_seconds > 0:
+        t_end = time.time() + warm_seconds
+        i = warmup
+        while time.time() < t_end:
+            for _ in range(8):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
     gc.collect()
     gc.disable()
     try:
@@ -209,7 +221,7 @@ def bench_dense_decode(torch, lrl, configs, steps, warmup):
     return out
 
 
-def bench_prefill(torch, lrl, configs, metrics, steps, warmup, r=None):
+def bench_prefill(torch, lrl, configs, metrics, steps, warmup, r=None, warm_seconds=0.0):
     """MLP up-projection prefill (the rank `r` overrides the workload's)."""
     c = configs.MLP_UP_PREFILL
     M, K, N = c["M"], c["K"], c["N"]
@@ -226,7 +238,8 @@ def bench_prefill(torch, lrl, configs, metrics, steps, warmup, r=None):
     lins = [lrl.LowRankLinear(A.clone() if i else A, B.clone() if i else B, max_M=M) for i in range(ncop)]
     Ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(ncop)]
     stream = torch.cuda.current_stream()
-    ms = time_steps(torch, lambda i: lins[i % ncop](Xs[i % ncop], out=Ys[i % ncop]), steps, warmup, stream)
+    ms = time_steps(torch, lambda i: lins[i % ncop](Xs[i % ncop], out=Ys[i % ncop]), steps, warmup, stream,
+                    warm_seconds=warm_seconds)
     fl = metrics.lowrank_flops(M, K, r, N)
     plan = lins[0].describe()
     del lins, Xs, Ys
@@ -234,7 +247,7 @@ def bench_prefill(torch, lrl, configs, metrics, steps, warmup, r=None):
     return dict(M=M, K=K, r=r, N=N, ms=ms, tflops=fl / (ms * 1e-3) / 1e12, flops=fl, plan=plan, copies=ncop)
 
 
-def bench_layer(torch, lrl, configs, metrics, M, steps, warmup, grouped=True, graph=False):
+def bench_layer(torch, lrl, configs, metrics, M, steps, warmup, grouped=True, graph=False, warm_seconds=0.0):
     """One decoder layer of factorized projections (q, k, v, o, packed
     gate/up, down) at M rows: the layer's span per step.  q, k and v share X
     in one group call (or three separate calls with grouped=False).  Weights
@@ -279,10 +292,11 @@ def bench_layer(torch, lrl, configs, metrics, M, steps, warmup, grouped=True, gr
             for i in range(ncop):
                 step(i)
         reps = max(1, steps // ncop)
-        ms = time_steps(torch, lambda i: g.replay(), reps, max(1, warmup // ncop), torch.cuda.current_stream()) / ncop
+        ms = time_steps(torch, lambda i: g.replay(), reps, max(1, warmup // ncop), torch.cuda.current_stream(),
+                        warm_seconds=warm_seconds) / ncop
         del g
     else:
-        ms = time_steps(torch, step, steps, warmup, torch.cuda.current_stream())
+        ms = time_steps(torch, step, steps, warmup, torch.cuda.current_stream(), warm_seconds=warm_seconds)
     byts = sum(metrics.decode_bytes(M, p.K, p.r, p.N) for p in configs.LAYER_PROJS)
     fl = sum(metrics.lowrank_flops(M, p.K, p.r, p.N) for p in configs.LAYER_PROJS)
     dense = [nm for nm, lin in sets[0].items() if "dense=1" in lin.describe()]
@@ -479,7 +493,7 @@ def main():
                           "max_over_min": round(max(ms.values()) / min(ms.values()), 4)}), flush=True)
         return
     if args.prefill_only:
-        p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 50), 3)
+        p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 20), 3, warm_seconds=2.0)
         log("prefill: %.3f ms/step, %.1f TFLOP/s, plan %s" % (p["ms"], p["tflops"], p["plan"]))
         print(json.dumps({"prefill_ms_per_step": round(p["ms"], 5), "tflops": round(p["tflops"], 2),
                           "flops_per_step": p["flops"], "plan": p["plan"]}), flush=True)
@@ -535,7 +549,7 @@ def main():
         "decode_alternatives": alts or None,
     }
     if not args.no_prefill:
-        p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 50), 3)
+        p = bench_prefill(torch, lrl, configs, metrics, max(10, args.steps // 20), 3, warm_seconds=2.0)
         log("prefill: %.3f ms/step, %.1f TFLOP/s" % (p["ms"], p["tflops"]))
         kn = prefill_kernels(p["plan"])
         result["prefill"] = {
@@ -553,10 +567,10 @@ def main():
         result["dense_decode"] = bench_dense_decode(torch, lrl, configs, min(args.steps, 400), 20)
         lay = {}
         for M in configs.LAYER_M:
-            steps_, warm_ = (200, 20) if M <= 16 else (10, 2)
-            d_ = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_)
-            sep = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_, grouped=False)
-            gr = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_, graph=True)
+            steps_, warm_, ws_ = (200, 20, 0.0) if M <= 16 else (20, 2, 1.0)
+            d_ = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_, warm_seconds=ws_)
+            sep = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_, grouped=False, warm_seconds=ws_)
+            gr = bench_layer(torch, lrl, configs, metrics, M, steps_, warm_, graph=True, warm_seconds=ws_)
             log("layer M=%d: %.1f us/layer, %.3f TB/s, %.1f TFLOP/s (%d library calls, %d weight copies); "
                 "q, k, v as separate calls: %.1f us/layer; replayed as a HIP graph: %.1f us/layer"
                 % (M, d_["ms"] * 1e3, d_["tbs"], d_["tflops"], d_["calls"], d_["copies"], sep["ms"] * 1e3,
