@@ -79,6 +79,11 @@ struct Geo {
   static_assert(32 * kQPitch == 1024 * kQInst, "Q slot is a whole number of loads");
   static_assert(kSlotP + 1024 * kQInst <= kSlot, "Q slot");
   static_assert(kQInst <= 16, "two direct loads per wave cover the Q slot");
+  // Direct loads per wave and k-step: two of P and one or two of Q (a wave
+  // without a Q load of its own issues one that reads nothing, so that every
+  // wave counts the same loads).  Tiles up to 96 wide need at most 7 Q loads
+  // per slot: one per wave.
+  static constexpr int kDma = kQInst <= 8 ? 3 : 4;
   static_assert(kBM * kEpiPitch <= kPreLdsBytes, "epilogue staging");
 };
 
@@ -237,23 +242,23 @@ template <int NB>
 __device__ __forceinline__ void q_dma(const Ctx& c, const QDma& d, char* slotQ, char* dummy, int t) {
   const uint32_t stride = (uint32_t)(64 * c.ldq);  // 32 rows of bf16
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    // waves without a second load of the slot issue one that reads nothing
-    // into a spare 1 KB of LDS, so that every wave counts kDmaPerStage loads
+  for (int h = 0; h < Geo<NB>::kDma - 2; ++h) {
+    // waves without a load of the slot issue one that reads nothing into a
+    // spare 1 KB of LDS, so that every wave counts Geo<NB>::kDma loads
     const bool real = c.w + 8 * h < Geo<NB>::kQInst;  // uniform
     const bool ok = real && d.ok[h] && (int64_t)d.krow[h] + 32 * t < c.qrows;
     dma16a(c.rQ, lds_addr(real ? slotQ + (c.w + 8 * h) * 1024 : dummy), ok ? d.off0[h] + stride * (uint32_t)t : kOutOfRange);
   }
 }
-// Direct loads per wave and k-step: two of P, two of Q.
-constexpr int kDmaPerStage = 4;
 // Wait until at most n stages of this wave's loads are in flight (n <= 3).
+template <int NB>
 __device__ __forceinline__ void wait_stages(int n) {
+  constexpr int d = Geo<NB>::kDma;
   switch (n) {
     case 0: wait_vm_dyn(0); break;
-    case 1: wait_vm_dyn(kDmaPerStage); break;
-    case 2: wait_vm_dyn(2 * kDmaPerStage); break;
-    default: wait_vm_dyn(3 * kDmaPerStage); break;
+    case 1: wait_vm_dyn(d); break;
+    case 2: wait_vm_dyn(2 * d); break;
+    default: wait_vm_dyn(3 * d); break;
   }
 }
 
@@ -420,7 +425,7 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   // wait for stage s, publish it, patch it where needed; `steady`: three
   // later stages are in flight (a constant wait, no branch on the count)
   auto arrive = [&](int s, bool steady) {
-    wait_stages(steady ? kAhead - 1 : min(kAhead - 1, nks - 1 - s));
+    wait_stages<NB>(steady ? kAhead - 1 : min(kAhead - 1, nks - 1 - s));
     turn_barrier();
     if (s == q_fix || s == p_fix) {  // uniform
       patch_slot<NB>(c, slot(s), slot(s) + kSlotP, k0 + (int64_t)s * kBK, s == q_fix, s == p_fix);
