@@ -49,6 +49,8 @@
 // contiguous run of the tile order, and the order walks groups of four row
 // tiles column by column: the workgroups resident on one XCD share their P
 // and Q panels in that XCD's L2.
+#include <type_traits>
+
 #include "lr_device.h"
 #include "lr_kernels.h"
 #include "lr_ldsops.h"
@@ -79,11 +81,7 @@ struct Geo {
   static_assert(32 * kQPitch == 1024 * kQInst, "Q slot is a whole number of loads");
   static_assert(kSlotP + 1024 * kQInst <= kSlot, "Q slot");
   static_assert(kQInst <= 16, "two direct loads per wave cover the Q slot");
-  // Direct loads per wave and k-step: two of P and one or two of Q (a wave
-  // without a Q load of its own issues one that reads nothing, so that every
-  // wave counts the same loads).  Tiles up to 96 wide need at most 7 Q loads
-  // per slot: one per wave.
-  static constexpr int kDma = kQInst <= 8 ? 3 : 4;
+
   static_assert(kBM * kEpiPitch <= kPreLdsBytes, "epilogue staging");
 };
 
@@ -238,22 +236,25 @@ __device__ __forceinline__ void q_dma_init(const Ctx& c, int64_t k0, QDma& d) {
     d.off0[h] = d.ok[h] ? (uint32_t)(((k0 + kr) * c.ldq + c.nb + 8 * ch) * 2) : 0u;
   }
 }
-template <int NB>
+// Direct loads per wave and k-step: two of P and D - 2 of Q.  A wave whose
+// second Q load exists (w + 8 < kQInst) has D = 4, every other wave D = 3;
+// a wave without a first Q load of its own issues one that reads nothing
+// into a spare 1 KB of LDS, so that the count per wave is fixed.
+template <int NB, int D>
 __device__ __forceinline__ void q_dma(const Ctx& c, const QDma& d, char* slotQ, char* dummy, int t) {
   const uint32_t stride = (uint32_t)(64 * c.ldq);  // 32 rows of bf16
 #pragma unroll
-  for (int h = 0; h < Geo<NB>::kDma - 2; ++h) {
-    // waves without a load of the slot issue one that reads nothing into a
-    // spare 1 KB of LDS, so that every wave counts Geo<NB>::kDma loads
+  for (int h = 0; h < D - 2; ++h) {
     const bool real = c.w + 8 * h < Geo<NB>::kQInst;  // uniform
     const bool ok = real && d.ok[h] && (int64_t)d.krow[h] + 32 * t < c.qrows;
     dma16a(c.rQ, lds_addr(real ? slotQ + (c.w + 8 * h) * 1024 : dummy), ok ? d.off0[h] + stride * (uint32_t)t : kOutOfRange);
   }
 }
-// Wait until at most n stages of this wave's loads are in flight (n <= 3).
-template <int NB>
+// Wait until at most n stages of this wave's loads (D per stage) are in
+// flight (n <= 3).
+template <int D>
 __device__ __forceinline__ void wait_stages(int n) {
-  constexpr int d = Geo<NB>::kDma;
+  constexpr int d = D;
   switch (n) {
     case 0: wait_vm_dyn(0); break;
     case 1: wait_vm_dyn(d); break;
@@ -396,10 +397,6 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   QDma qd;
   p_dma_init(c, k0, pd);
   q_dma_init<NB>(c, k0, qd);
-  auto stage_dma = [&](int s) {
-    p_dma(c, pd, slot(s), s);
-    q_dma<NB>(c, qd, slot(s) + kSlotP, smem + kSlots * kSlot, s);
-  };
   // the k-steps (relative to this split) that need a patch, else -1
   const bool q_last_tile = (c.ldq & 1) && T.nb + c.qcols == c.ldq;
   const int q_fix = q_last_tile && c.qrows - 1 >= k0 ? (int)((c.qrows - 1 - k0) / kBK) : -1;
@@ -411,71 +408,88 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   // stay busy while the LDS reads of the other group are in flight.  The
   // barrier between a group's reads and its MFMAs (the hand-off) does not
   // wait for the reads; the barrier that opens a k-step does, and every slot
-  // is refilled only after one of those.  Group 0 reads stage t, then multiplies it; group 1 multiplies
-  // stage t - 1 while group 0 reads t, and reads t while group 0
-  // multiplies.  Both groups meet the same barriers:
+  // is refilled only after one of those.  Group 0 reads stage t, then
+  // multiplies it; group 1 multiplies stage t - 1 while group 0 reads t, and
+  // reads t while group 0 multiplies.  Both groups meet the same barriers:
   //   wait for stage t; barrier; [patch; barrier]; X; barrier; Y
   //   group 0: X = read t + loads of t + 4, Y = MFMAs of t
   //   group 1: X = MFMAs of t - 1,          Y = read t + loads of t + 4
   // Stage t's slot was last read by group 1 before the first barrier of
   // iteration t + 1, so both groups refill it (with stage t + 5) after that.
+  // The loop is instantiated for the wave's load count D (3 or 4), so that
+  // every wait count is a constant.
   const int grp = c.w >> 2;
-  Ops<NB> ops;
-  for (int t = 0; t < kAhead && t < nks; ++t) stage_dma(t);
-  // wait for stage s, publish it, patch it where needed; `steady`: three
-  // later stages are in flight (a constant wait, no branch on the count)
-  auto arrive = [&](int s, bool steady) {
-    wait_stages<NB>(steady ? kAhead - 1 : min(kAhead - 1, nks - 1 - s));
-    turn_barrier();
-    if (s == q_fix || s == p_fix) {  // uniform
-      patch_slot<NB>(c, slot(s), slot(s) + kSlotP, k0 + (int64_t)s * kBK, s == q_fix, s == p_fix);
+  auto run = [&](auto dtag) {
+    constexpr int D = decltype(dtag)::value;
+    auto stage_dma = [&](int s) {
+      p_dma(c, pd, slot(s), s);
+      q_dma<NB, D>(c, qd, slot(s) + kSlotP, smem + kSlots * kSlot, s);
+    };
+    Ops<NB> ops;
+    for (int t = 0; t < kAhead && t < nks; ++t) stage_dma(t);
+    // wait for stage s, publish it, patch it where needed; `steady`: three
+    // later stages are in flight (a constant wait, no branch on the count)
+    auto arrive = [&](int s, bool steady) {
+      wait_stages<D>(steady ? kAhead - 1 : min(kAhead - 1, nks - 1 - s));
+      turn_barrier();
+      if (s == q_fix || s == p_fix) {  // uniform
+        patch_slot<NB>(c, slot(s), slot(s) + kSlotP, k0 + (int64_t)s * kBK, s == q_fix, s == p_fix);
+        turn_barrier();
+      }
+    };
+    // the P reads go out first, the next loads are issued while they are in
+    // flight, and the B reads come last; nothing here waits for them
+    auto fetch = [&](int s) {
+      read_p<NB>(slot(s), wm, c.l, ops);
+      if (s + kAhead < nks) stage_dma(s + kAhead);
+      read_q<NB>(slot(s) + kSlotP, wn, c.l, ops);
+    };
+    const int steady_end = nks - (kAhead - 1);  // k-steps with three later stages in flight
+    if (grp == 0) {
+      int s = 0;
+      for (; s < steady_end; ++s) {
+        arrive(s, true);
+        fetch(s);
+        handoff_barrier();
+        mma<NB>(ops, acc);
+      }
+      for (; s < nks; ++s) {
+        arrive(s, false);
+        fetch(s);
+        handoff_barrier();
+        mma<NB>(ops, acc);
+      }
+      turn_barrier();
+    } else if (nks > 0) {
+      arrive(0, steady_end > 0);
+      handoff_barrier();
+      fetch(0);
+      int s = 1;
+      for (; s < steady_end; ++s) {
+        arrive(s, true);
+        mma<NB>(ops, acc);
+        handoff_barrier();
+        fetch(s);
+      }
+      for (; s < nks; ++s) {
+        arrive(s, false);
+        mma<NB>(ops, acc);
+        handoff_barrier();
+        fetch(s);
+      }
+      turn_barrier();
+      mma<NB>(ops, acc);
+    } else {
       turn_barrier();
     }
   };
-  // the P reads go out first, the next loads are issued while they are in
-  // flight, and the B reads come last; nothing here waits for them
-  auto fetch = [&](int s) {
-    read_p<NB>(slot(s), wm, c.l, ops);
-    if (s + kAhead < nks) stage_dma(s + kAhead);
-    read_q<NB>(slot(s) + kSlotP, wn, c.l, ops);
-  };
-  const int steady_end = nks - (kAhead - 1);  // k-steps with three later stages in flight
-  if (grp == 0) {
-    int s = 0;
-    for (; s < steady_end; ++s) {
-      arrive(s, true);
-      fetch(s);
-      handoff_barrier();
-      mma<NB>(ops, acc);
-    }
-    for (; s < nks; ++s) {
-      arrive(s, false);
-      fetch(s);
-      handoff_barrier();
-      mma<NB>(ops, acc);
-    }
-    turn_barrier();
-  } else if (nks > 0) {
-    arrive(0, steady_end > 0);
-    handoff_barrier();
-    fetch(0);
-    int s = 1;
-    for (; s < steady_end; ++s) {
-      arrive(s, true);
-      mma<NB>(ops, acc);
-      handoff_barrier();
-      fetch(s);
-    }
-    for (; s < nks; ++s) {
-      arrive(s, false);
-      mma<NB>(ops, acc);
-      handoff_barrier();
-      fetch(s);
-    }
-    turn_barrier();
-    mma<NB>(ops, acc);
+  if constexpr (Geo<NB>::kQInst > 8) {
+    if (c.w + 8 < Geo<NB>::kQInst)  // uniform
+      run(std::integral_constant<int, 4>{});
+    else
+      run(std::integral_constant<int, 3>{});
   } else {
-    turn_barrier();
+    run(std::integral_constant<int, 3>{});
   }
 
   // ------------------------------------------------------------ epilogue --
