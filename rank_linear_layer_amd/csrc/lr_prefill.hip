@@ -236,10 +236,9 @@ __device__ __forceinline__ void q_dma_init(const Ctx& c, int64_t k0, QDma& d) {
     d.off0[h] = d.ok[h] ? (uint32_t)(((k0 + kr) * c.ldq + c.nb + 8 * ch) * 2) : 0u;
   }
 }
-// Direct loads per wave and k-step: two of P and D - 2 of Q.  A wave whose
-// second Q load exists (w + 8 < kQInst) has D = 4, every other wave D = 3;
-// a wave without a first Q load of its own issues one that reads nothing
-// into a spare 1 KB of LDS, so that the count per wave is fixed.
+// Direct loads per wave and k-step: two of P and D - 2 of Q, one for each Q
+// load wave w has (loads w and w + 8 of the slot, where they exist).  The
+// spare 1 KB of LDS stays as a target for loads that fill nothing.
 template <int NB, int D>
 __device__ __forceinline__ void q_dma(const Ctx& c, const QDma& d, char* slotQ, char* dummy, int t) {
   const uint32_t stride = (uint32_t)(64 * c.ldq);  // 32 rows of bf16
@@ -416,8 +415,8 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
   //   group 1: X = MFMAs of t - 1,          Y = read t + loads of t + 4
   // Stage t's slot was last read by group 1 before the first barrier of
   // iteration t + 1, so both groups refill it (with stage t + 5) after that.
-  // The loop is instantiated for the wave's load count D (3 or 4), so that
-  // every wait count is a constant.
+  // The loop is instantiated for the wave's load count D (2, 3 or 4), so
+  // that every wait count is a constant.
   const int grp = c.w >> 2;
   auto run = [&](auto dtag) {
     constexpr int D = decltype(dtag)::value;
@@ -489,7 +488,10 @@ __device__ __forceinline__ void gemm_tile(const PreArgs& a, const Tile& T, int k
     else
       run(std::integral_constant<int, 3>{});
   } else {
-    run(std::integral_constant<int, 3>{});
+    if (c.w < Geo<NB>::kQInst)  // uniform
+      run(std::integral_constant<int, 3>{});
+    else
+      run(std::integral_constant<int, 2>{});
   }
 
   // ------------------------------------------------------------ epilogue --
