@@ -25,14 +25,16 @@
 //          order s = 0..S-1 (bitwise identical in every member).  Without a
 //          verified XCD map the same exchange runs device-coherent.
 //   GEMM2  Y_js[:, Ns] = T_js . B[js, Ns]               (T as bf16 hi + lo)
-//   Y reduce-scatter across XCDs: partials published device-coherent with
-//          epoch flags; member js of n-slice s sums its 1/Jw share of the
-//          n-slice over the Jw partials in order and writes bf16 Y.
+//   Y reduce-scatter across XCDs: partials stored device-coherent, every
+//          value beside a copy of the launch's epoch in the same 16-byte
+//          word; member js of n-slice s polls its 1/Jw share of the
+//          n-slice until the Jw partials carry the epoch, sums them in
+//          order and writes bf16 Y.
 // No atomics and no floating-point reordering: results are bitwise
 // reproducible.  The epoch of a launch is the handle's generation word
 // (ctrl[0]) plus one, read by every workgroup at entry; workgroup 0 stores
-// it back at its end.  Workgroup 0 finishes only after the Y flags of all
-// rank slices of its n-slice, each of which followed the T flags of every
+// it back at its end.  Workgroup 0 finishes only after the Y partials of
+// all rank slices of its n-slice, each of which followed the T flags of every
 // K slice of that rank slice, so by then every workgroup of the launch has
 // read the word.  No counter is reset between calls and no argument
 // changes from one launch to the next, so a captured graph can replay the
@@ -443,9 +445,14 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
   }
 
   // ---------------------------------------------------------- GEMM2 ------
-  // Y partial layout per (s, js): [nt][M][128] fp32 = ntps*M*32 float4
+  // Y partial layout per (s, js): [nt][M][128] fp32 = ntps*M*32 float4, each
+  // stored as two tagged 16-byte words {y0, epoch, y1, epoch}: a reader that
+  // finds this launch's epoch in both tags of a word has both values (one
+  // 16-byte store is never seen in part), so no flag and no wait for the
+  // stores to complete are needed.
   const int vmax = ntps * M * 32;
-  const uint32_t ypart_wg = P.off_ypart + (uint32_t)(s * P.Jw + js) * (uint32_t)vmax * 16u;
+  const uint32_t ypart_wg = P.off_ypart + (uint32_t)(s * P.Jw + js) * (uint32_t)vmax * 32u;
+  const float tagf = __uint_as_float(epoch);
   f32x4_t y0[8], y1[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -469,58 +476,63 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
         const int o = m * 128 + c + i;
         v[i] = ((red[o] + red[16 * 128 + o]) + red[32 * 128 + o]) + red[48 * 128 + o];
       }
-      buf_store16_coherent(rW, ypart_wg + (uint32_t)(ntl * M * 32 + vi) * 16u, v);
+      const uint32_t off = ypart_wg + (uint32_t)(ntl * M * 32 + vi) * 32u;
+      buf_store16_coherent(rW, off, f32x4_t{v[0], tagf, v[1], tagf});
+      buf_store16_coherent(rW, off + 16u, f32x4_t{v[2], tagf, v[3], tagf});
     }
   }
   RES_TRACE(6);
 
   // -------------------------------- Y reduce-scatter over the Jw slices --
   if (nt_cnt > 0) {
-    wait_vmem_all();
     RES_TRACE(11);
-    barrier_lds();
-    const uint32_t yflag_grp = P.off_yflag + (uint32_t)(s * P.Jw) * 4u;
-    if (tid == 0) buf_store_u32_coherent(rW, yflag_grp + (uint32_t)js * 4u, epoch);
-    if (w == 0) {
-      uint32_t spins = 0;
-      while (true) {
-        bool ok = true;
-        for (int i = l; i < P.Jw; i += 64) ok = ok && (buf_load_u32_coherent(rW, yflag_grp + (uint32_t)i * 4u) == epoch);
-        if (__all(ok)) break;
-        if (++spins > P.spin_limit) {
-          if (l == 0) raise_stall(P.ctrl, P.err);
-          break;
+    // my share of the n-slice: value pairs [q_lo, q_hi) of nt_cnt*M*64 (pair
+    // q is the tagged word at byte 16 q of a partial); each thread polls the
+    // Jw partials of a pair until every tag holds this launch's epoch and
+    // sums them in order.
+    const int qtot = nt_cnt * M * 64;
+    const int share = (qtot + P.Jw - 1) / P.Jw;
+    const int q_lo = js * share;
+    const int q_hi = min(qtot, q_lo + share);
+    const uint32_t grp_y = P.off_ypart + (uint32_t)(s * P.Jw) * (uint32_t)vmax * 32u;
+    for (int q = q_lo + tid; q < q_hi; q += kResThreads) {
+      float s0 = 0.f, s1 = 0.f;
+      for (int p0 = 0; p0 < P.Jw; p0 += 16) {
+        const int np0 = min(16, P.Jw - p0);
+        f32x4_t t[16];
+        uint32_t spins = 0;
+        while (true) {
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            t[u] = buf_load16_coherent(rW, grp_y + ((uint32_t)(p0 + min(u, np0 - 1)) * (uint32_t)vmax * 2u + (uint32_t)q) * 16u);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          bool ok = true;
+#pragma unroll
+          for (int u = 0; u < 16; ++u) ok = ok && __float_as_uint(t[u][1]) == epoch && __float_as_uint(t[u][3]) == epoch;
+          if (ok) break;
+          if (++spins > P.spin_limit) {
+            raise_stall(P.ctrl, P.err);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    barrier_lds();
-    RES_TRACE(7);
-    // my share of the n-slice: float4 indices [v_lo, v_hi) of nt_cnt*M*32
-    const int vtot = nt_cnt * M * 32;
-    const int share = (vtot + P.Jw - 1) / P.Jw;
-    const int v_lo = js * share;
-    const int v_hi = min(vtot, v_lo + share);
-    const uint32_t grp_y = P.off_ypart + (uint32_t)(s * P.Jw) * (uint32_t)vmax * 16u;
-    for (int vi = v_lo + tid; vi < v_hi; vi += kResThreads) {
-      f32x4_t sum = zero4();
-      for (int p0 = 0; p0 < P.Jw; p0 += 32) {
-        f32x4_t t[32];
 #pragma unroll
-        for (int u = 0; u < 32; ++u)
-          t[u] = buf_load16_coherent(rW, grp_y + ((uint32_t)min(p0 + u, P.Jw - 1) * (uint32_t)vmax + (uint32_t)vi) * 16u);
-#pragma unroll
-        for (int u = 0; u < 32; ++u)
-          if (p0 + u < P.Jw) sum += t[u];
+        for (int u = 0; u < 16; ++u)
+          if (u < np0) {
+            s0 += t[u][0];
+            s1 += t[u][2];
+          }
       }
+      const int vi = q >> 1;
       const int ntl = vi / (M * 32);
       const int rem = vi - ntl * M * 32;
-      const int m = rem >> 5, c = (rem & 31) * 4;
+      const int m = rem >> 5, c = (rem & 31) * 4 + 2 * (q & 1);
       const int64_t n0 = nb0 + (int64_t)ntl * kResNT + c;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (n0 + i < N) P.Y[(int64_t)m * N + n0 + i] = (uint16_t)f32_to_bf16_rne(sum[i]);
+      if (n0 < N) P.Y[(int64_t)m * N + n0] = (uint16_t)f32_to_bf16_rne(s0);
+      if (n0 + 1 < N) P.Y[(int64_t)m * N + n0 + 1] = (uint16_t)f32_to_bf16_rne(s1);
     }
+    RES_TRACE(7);
   }
   RES_TRACE(8);
   if (local == 0 && tid == 0) st_agent_u32(P.ctrl, epoch);  // the next launch's generation

@@ -75,7 +75,8 @@ constexpr int kDecMaxProj = 4;    // projections sharing X in one launch
 // Workspace regions are byte offsets from `ws` (one buffer resource):
 //   off_tpart  [Jw*S][M][kDecJS] fp32   GEMM1 partials
 //   off_tfin   [Jw][M][kDecJS]   fp32   reduced T slices
-//   off_ypart  [S][Jw][ntps][M][kDecNT] fp32 GEMM2 partials
+//   off_ypart  [S][Jw][ntps][M][kDecNT] fp32 GEMM2 partials (resident kernel:
+//              each value beside a 32-bit epoch tag, twice the bytes)
 struct DecProj {
   const uint16_t* A;
   const uint16_t* B;

@@ -206,7 +206,8 @@ InplaceLayout inplace_layout(const lrv::DecPart& dp, int max_M, size_t off) {
   L.tfin = off;
   off = align_up(off + (size_t)dp.Jw * max_M * dp.js_w * 4);
   L.ypart = off;
-  off = align_up(off + (size_t)G * dp.ntps * max_M * dp.nt_w * 4);
+  // the resident kernel stores each Y partial value beside an epoch tag
+  off = align_up(off + (size_t)G * dp.ntps * max_M * dp.nt_w * 4 * (dp.kind == 1 ? 2 : 1));
   L.end = off;
   return L;
 }
@@ -1083,10 +1084,11 @@ lr_status lr_decode_noalloc(const void* X, const void* A, const void* B, void* Y
   h.err_dev = status;
   // The array keeps the last call's contents, which may be another shape's
   // tables: the control words (generation, counters, flags) start at zero
-  // every call, so no stale flag can match this call's epoch.
-  const int words = (int)(L.tpart / 4);
-  hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)((words + 255) / 256 < 64 ? (words + 255) / 256 : 64)), dim3(256), 0,
-                     (hipStream_t)stream, h.ctrl, words);
+  // every call, so no stale flag can match this call's epoch; the resident
+  // kernel's epoch-tagged Y partials are cleared with them.
+  const int words = (int)((h.dp.kind == 1 ? L.end : L.tpart) / 4);
+  const int clear_blocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
+  hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)clear_blocks), dim3(256), 0, (hipStream_t)stream, h.ctrl, words);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
   const lr_linear* hs[1] = {&h};
