@@ -244,7 +244,7 @@ lr_status lr_group_run(const lr_linear* const* hs, int n, const void* X, void* c
  * harnesses that forbid allocation).  It runs the decode kernel that
  * lr_linear_create + lr_linear_run choose by default for max_M = M
  * (LDS-resident or register-streaming, reading A and B in place), with that
- * kernel's exchange tables in a fixed 32 MiB device array inside the
+ * kernel's exchange tables in a fixed 64 MiB device array inside the
  * library instead of a handle's workspace.
  *   X, A, B, Y : device pointers, bf16 row-major, as for lr_linear_run
  *                (16-byte aligned bases; Y must not overlap the inputs).
@@ -260,7 +260,7 @@ lr_status lr_group_run(const lr_linear* const* hs, int n, const void* X, void* c
  * race and give wrong results; calls in stream order are safe.  The array
  * is the device's for the life of the process.
  * Errors: INVALID_ARG (null pointer, sizes, misaligned base, overlap,
- * M > 16), UNSUPPORTED (a shape whose tables exceed the 32 MiB array, or
+ * M > 16), UNSUPPORTED (a shape whose tables exceed the 64 MiB array, or
  * whose launch cannot be resident at once), HIP (launch failure).
  */
 lr_status lr_decode_noalloc(const void* X, const void* A, const void* B, void* Y, int64_t M,

@@ -14,17 +14,17 @@
 //      so all of its HBM traffic is in flight from the start;
 //   2. GEMM1 partial T_s[:, js] = X[:, Ks] . A[Ks, js] (MFMA); the four waves
 //      take alternate 32-row k-tiles and are summed in LDS;
-//   3. T hand-off: the partial is published with device-coherent stores; the
-//      last of the S workgroups of slice js to arrive sums the S partials in
-//      fixed order and publishes T_js with an epoch-stamped flag, which the
-//      others poll;
+//   3. T hand-off: the partial is published as epoch-tagged exchange words
+//      (lr_device.h); every one of the S workgroups of slice js polls the S
+//      partials and sums them in fixed order (one hop, no last arriver);
 //   4. GEMM2 partial Y_js[:, Ns] = T_js . B[js, Ns] with T split into bf16
-//      hi + lo halves (two MFMAs keep ~16 mantissa bits of T);
-//   5. the last of the Jw workgroups to publish a partial for n-slice s sums
-//      the Jw partials in fixed order and writes bf16 Y.
-// No floating-point atomics: results are bitwise reproducible.  Counters
-// reset themselves and a device-side generation number stamps each launch,
-// so no memset is needed between calls.
+//      hi + lo halves (two MFMAs keep ~16 mantissa bits of T), published as
+//      exchange words;
+//   5. the Jw workgroups of n-slice s each poll their 1/Jw share of it in the
+//      Jw partials, sum it in fixed order and write bf16 Y.
+// No atomics: results are bitwise reproducible.  A device-side generation
+// number stamps each launch (workgroup 0 advances it at its end), so no
+// memset is needed between calls and a captured graph can replay them.
 #include "lr_device.h"
 #include "lr_kernels.h"
 
@@ -102,37 +102,11 @@ __device__ __forceinline__ void tile_operands(const RawTile& t, u32x4_t op[8], i
   transpose8x8(seg, op);
 }
 
-// out[v] = sum over p < npart (in order) of the float4 at
-// base + p * pstride + (tid + 256 v) * 16, for vector indices < nvec.
-template <int V>
-__device__ __forceinline__ void sum_partials(rsrc_t ws, uint32_t base, uint32_t pstride, int npart, int nvec,
-                                             int tid, f32x4_t out[V]) {
-#pragma unroll
-  for (int v = 0; v < V; ++v) out[v] = zero4();
-  for (int p0 = 0; p0 < npart; p0 += 8) {
-    f32x4_t t[8][V];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int vi = tid + kDecThreads * v;
-        const bool ok = (p0 + u < npart) && (vi < nvec);
-        const uint32_t off = ok ? base + (uint32_t)(p0 + u) * pstride + (uint32_t)vi * 16u : base;
-        const f32x4_t x = buf_load16_coherent(ws, off);
-        t[u][v] = ok ? x : zero4();
-      }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int v = 0; v < V; ++v) out[v] += t[u][v];
-  }
-}
-
 __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecArgs a) {
   DEC_TRACE_ENTRY();
   __shared__ float red[kDecWaves][16][kDecJS + 8];
   __shared__ float Ts[16][kDecJS + 8];
-  __shared__ uint32_t sh_epoch, sh_old;
+  __shared__ uint32_t sh_epoch;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
@@ -169,7 +143,10 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
 
   DEC_TRACE(0);
   DEC_TRACE_ENTRY_STORE();
-  if (tid == 0) sh_epoch = ld_agent_u32(P.ctrl) + 1u;
+  if (tid == 0) {
+    const uint32_t gen = ld_agent_u32(P.ctrl);
+    sh_epoch = gen + 1u == 0u ? 1u : gen + 1u;  // 0 is the value of fresh memory
+  }
 
   // ------------------------------------------------ issue all loads -----
   const int j0 = js * kDecJS;
@@ -221,71 +198,40 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
     }
   }
 
-  // WG reduction of the four waves' partial T; publish it (float4 rows of
-  // kDecJS floats, M rows).
+  // WG reduction of the four waves' partial T, published as exchange words
+  // (lr_device.h): row m of the slice is words [kHP m, kHP m + kHP).
 #pragma unroll
   for (int e = 0; e < 8; ++e)
 #pragma unroll
     for (int t = 0; t < 4; ++t) red[w][4 * g + t][8 * np + e] = acc[e][t];
   barrier_lds();
   DEC_TRACE(1);
-  constexpr int kV4 = kDecJS / 4;  // float4 per row of a slice
-  const int nvecT = M * kV4;
-  const uint32_t slice_bytes = (uint32_t)(M * kDecJS * 4);
-  for (int vi = tid; vi < nvecT; vi += kDecThreads) {
-    const int m = vi / kV4, c = (vi - m * kV4) * 4;
-    f32x4_t v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = ((red[0][m][c + i] + red[1][m][c + i]) + red[2][m][c + i]) + red[3][m][c + i];
-    buf_store16_coherent(rW, P.off_tpart + (uint32_t)(js * P.S + s) * slice_bytes + (uint32_t)vi * 16u, v);
-  }
-  wait_vmem_all();
-  barrier_lds();
-  DEC_TRACE(2);
+  constexpr int kHP = kDecJS / 2;  // exchange words per row of a slice
+  const int nqT = M * kHP;
+  const uint32_t blkT = (uint32_t)(M * kHP * 16);
+  const uint32_t tgrp = P.off_tpart + (uint32_t)(js * P.S) * blkT;
   const uint32_t epoch = sh_epoch;
-  if (tid == 0) sh_old = add_agent_u32(P.tcnt + js, 1u);
-  barrier_lds();
+  const float tagf = __uint_as_float(epoch);
+  for (int q = tid; q < nqT; q += kDecThreads) {
+    const int m = q / kHP, c = 2 * (q - m * kHP);
+    const float v0 = ((red[0][m][c] + red[1][m][c]) + red[2][m][c]) + red[3][m][c];
+    const float v1 = ((red[0][m][c + 1] + red[1][m][c + 1]) + red[2][m][c + 1]) + red[3][m][c + 1];
+    xstore_coherent(rW, tgrp + (uint32_t)s * blkT + (uint32_t)q * 16u, v0, v1, tagf);
+  }
+  DEC_TRACE(2);
   DEC_TRACE(3);
 
   // ----------------------------------------------------- T hand-off ------
-  if (sh_old == (uint32_t)(P.S - 1)) {
-    // Last arriver: reduce the S partials of slice js in order, publish T_js.
-    if (tid == 0) st_agent_u32(P.tcnt + js, 0u);
-    f32x4_t sum[1];
-    for (int vbase = 0; vbase < nvecT; vbase += kDecThreads) {
-      sum_partials<1>(rW, P.off_tpart + (uint32_t)(js * P.S) * slice_bytes + (uint32_t)vbase * 16u, slice_bytes,
-                      P.S, nvecT - vbase, tid, sum);
-      const int vi = vbase + tid;
-      if (vi < nvecT) {
-        buf_store16_coherent(rW, P.off_tfin + (uint32_t)js * slice_bytes + (uint32_t)vi * 16u, sum[0]);
-        const int m = vi / kV4, c = (vi - m * kV4) * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Ts[m][c + i] = sum[0][i];
-      }
-    }
-    wait_vmem_all();
-    barrier_lds();
-    if (tid == 0) st_agent_u32(P.tflag + js, epoch);
-  } else {
-    if (w == 0) {
-      uint32_t spins = 0;
-      while (true) {
-        const bool ok = ld_agent_u32(P.tflag + js) == (epoch ^ P.stall_xor);
-        if (ok) break;
-        if (++spins > P.spin_limit) {
-          if (l == 0) raise_stall(P.ctrl, P.err);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    barrier_lds();
-    for (int vi = tid; vi < nvecT; vi += kDecThreads) {
-      const f32x4_t v = buf_load16_coherent(rW, P.off_tfin + (uint32_t)js * slice_bytes + (uint32_t)vi * 16u);
-      const int m = vi / kV4, c = (vi - m * kV4) * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Ts[m][c + i] = v[i];
-    }
+  // Every member of slice js polls the S partials and sums them in order
+  // s = 0..S-1 (bitwise the same T_js in every member); one hop, no counter
+  // and no last arriver.  The stall test flag changes the epoch this wait
+  // looks for.
+  for (int q = tid; q < nqT; q += kDecThreads) {
+    float s0, s1;
+    xpoll_sum(rW, tgrp, blkT, P.S, (uint32_t)q * 16u, epoch ^ P.stall_xor, P.spin_limit, P.ctrl, P.err, s0, s1);
+    const int m = q / kHP, c = 2 * (q - m * kHP);
+    Ts[m][c] = s0;
+    Ts[m][c + 1] = s1;
   }
   // rows >= M and columns >= kDecJS of Ts are zero (read as operands)
   for (int idx = tid; idx < 16 * (kDecJS + 8); idx += kDecThreads) {
@@ -308,7 +254,9 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   }
 
   // ---------------------------------------------------------- GEMM2 ------
-  const uint32_t ypart_wg = P.off_ypart + (uint32_t)((s * P.Jw + js) * P.ntps) * (uint32_t)(M * kDecNT * 4);
+  // Y partial of n-tile nt: [M][kDecNT] values as exchange words
+  const uint32_t ytile_b = (uint32_t)(M * kDecNT * 8);
+  const uint32_t ypart_wg = P.off_ypart + (uint32_t)((s * P.Jw + js) * P.ntps) * ytile_b;
   // One n-tile: its partial is stored only when `ok` (a tile past the end of
   // the slice is computed on zeros and its stores are dropped).
   auto gemm2_tile = [&](const RawTile& bt, int nt, bool ok) {
@@ -330,13 +278,14 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
 #pragma unroll
       for (int t = 0; t < 4; ++t) red[w][4 * g + t][8 * np + e] = y[e][t];
     barrier_lds();
-    const uint32_t yp = ypart_wg + (uint32_t)(nt - nt_beg) * (uint32_t)(M * kDecNT * 4);
+    const uint32_t yp = ypart_wg + (uint32_t)(nt - nt_beg) * ytile_b;
     for (int vi = tid; vi < M * (kDecNT / 4); vi += kDecThreads) {
       const int m = vi / (kDecNT / 4), c = (vi - m * (kDecNT / 4)) * 4;
       f32x4_t v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = ((red[0][m][c + i] + red[1][m][c + i]) + red[2][m][c + i]) + red[3][m][c + i];
-      buf_store16_coherent(rW, off_if(yp + (uint32_t)vi * 16u, ok), v);
+      xstore_coherent(rW, off_if(yp + (uint32_t)vi * 32u, ok), v[0], v[1], tagf);
+      xstore_coherent(rW, off_if(yp + (uint32_t)vi * 32u + 16u, ok), v[2], v[3], tagf);
     }
     barrier_lds();
   };
@@ -349,44 +298,36 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
     load_tile_raw_if(b1, rB, jrow0, N, (int64_t)(nt + 3) * kDecNT, np, g, nt + 3 < nt_end);
   }
 
-  // ------------------------------------------- final deterministic sum ---
+  // ---------------------------------- Y reduce-scatter over the Jw slices --
+  // Member js of n-slice s polls its 1/Jw share of the n-slice's exchange
+  // words in the Jw partials (word q at byte 16 q of a partial), sums them
+  // in order js' = 0..Jw-1 and writes bf16 Y.
   DEC_TRACE(5);
-  wait_vmem_all();
-  barrier_lds();
-  if (tid == 0) sh_old = add_agent_u32(P.ycnt + s, 1u);
-  barrier_lds();
-  DEC_TRACE(6);
-  if (sh_old == (uint32_t)(P.Jw - 1)) {
-    if (tid == 0) st_agent_u32(P.ycnt + s, 0u);
-    const uint32_t stride_js = (uint32_t)P.ntps * (uint32_t)(M * kDecNT * 4);
+  const int nty = nt_end - nt_beg;
+  if (nty > 0) {
+    const uint32_t stride_js = (uint32_t)P.ntps * ytile_b;
     const uint32_t ys = P.off_ypart + (uint32_t)(s * P.Jw) * stride_js;
-    const int nvecY = (nt_end - nt_beg) * M * (kDecNT / 4);
-    f32x4_t sum[2];
-    for (int vbase = 0; vbase < nvecY; vbase += 2 * kDecThreads) {
-      sum_partials<2>(rW, ys + (uint32_t)vbase * 16u, stride_js, P.Jw, nvecY - vbase, tid, sum);
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const int vi = vbase + tid + kDecThreads * v;
-        if (vi >= nvecY) continue;
-        const int ntl = vi / (M * (kDecNT / 4));
-        const int rem = vi - ntl * M * (kDecNT / 4);
-        const int m = rem / (kDecNT / 4), c = (rem - m * (kDecNT / 4)) * 4;
-        const int64_t n0 = (int64_t)(nt_beg + ntl) * kDecNT + c;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (n0 + i < N) P.Y[(int64_t)m * N + n0 + i] = (uint16_t)f32_to_bf16_rne(sum[v][i]);
-      }
-    }
-    wait_vmem_all();
-    barrier_lds();
-    if (tid == 0) {
-      const uint32_t old2 = add_agent_u32(P.ctrl + 1, 1u);
-      if (old2 == (uint32_t)(P.S - 1)) {
-        st_agent_u32(P.ctrl + 1, 0u);
-        st_agent_u32(P.ctrl, epoch);
-      }
+    const int qtot = nty * M * (kDecNT / 2);
+    const int share = (qtot + P.Jw - 1) / P.Jw;
+    const int q_lo = js * share, q_hi = min(qtot, q_lo + share);
+    for (int q = q_lo + tid; q < q_hi; q += kDecThreads) {
+      float s0, s1;
+      xpoll_sum(rW, ys, stride_js, P.Jw, (uint32_t)q * 16u, epoch, P.spin_limit, P.ctrl, P.err, s0, s1);
+      const int vi = q >> 1;  // float4 of [nty][M][kDecNT / 4]
+      const int ntl = vi / (M * (kDecNT / 4));
+      const int rem = vi - ntl * M * (kDecNT / 4);
+      const int m = rem / (kDecNT / 4), c = (rem - m * (kDecNT / 4)) * 4 + 2 * (q & 1);
+      const int64_t n0 = (int64_t)(nt_beg + ntl) * kDecNT + c;
+      if (n0 < N) P.Y[(int64_t)m * N + n0] = (uint16_t)f32_to_bf16_rne(s0);
+      if (n0 + 1 < N) P.Y[(int64_t)m * N + n0 + 1] = (uint16_t)f32_to_bf16_rne(s1);
     }
   }
+  DEC_TRACE(6);
+  // The next launch's generation.  Workgroup 0 is (js, s) = (0, 0); its
+  // thread 0 polled word 0 of n-slice 0 from every rank slice, each of which
+  // followed the T partials of all its K slices, so every workgroup of the
+  // launch has read the word by now.
+  if (local == 0 && tid == 0) st_agent_u32(P.ctrl, epoch);
   DEC_TRACE(7);
   DEC_TRACE_FLUSH();
 }

@@ -446,10 +446,8 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
 
   // ---------------------------------------------------------- GEMM2 ------
   // Y partial layout per (s, js): [nt][M][128] fp32 = ntps*M*32 float4, each
-  // stored as two tagged 16-byte words {y0, epoch, y1, epoch}: a reader that
-  // finds this launch's epoch in both tags of a word has both values (one
-  // 16-byte store is never seen in part), so no flag and no wait for the
-  // stores to complete are needed.
+  // stored as two epoch-tagged exchange words (lr_device.h), polled by the
+  // reduce-scatter below: no flag and no wait for the stores to complete.
   const int vmax = ntps * M * 32;
   const uint32_t ypart_wg = P.off_ypart + (uint32_t)(s * P.Jw + js) * (uint32_t)vmax * 32u;
   const float tagf = __uint_as_float(epoch);
@@ -477,8 +475,8 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
         v[i] = ((red[o] + red[16 * 128 + o]) + red[32 * 128 + o]) + red[48 * 128 + o];
       }
       const uint32_t off = ypart_wg + (uint32_t)(ntl * M * 32 + vi) * 32u;
-      buf_store16_coherent(rW, off, f32x4_t{v[0], tagf, v[1], tagf});
-      buf_store16_coherent(rW, off + 16u, f32x4_t{v[2], tagf, v[3], tagf});
+      xstore_coherent(rW, off, v[0], v[1], tagf);
+      xstore_coherent(rW, off + 16u, v[2], v[3], tagf);
     }
   }
   RES_TRACE(6);
@@ -496,34 +494,8 @@ __global__ __launch_bounds__(kResThreads) void lr_decode_res_kernel(const DecArg
     const int q_hi = min(qtot, q_lo + share);
     const uint32_t grp_y = P.off_ypart + (uint32_t)(s * P.Jw) * (uint32_t)vmax * 32u;
     for (int q = q_lo + tid; q < q_hi; q += kResThreads) {
-      float s0 = 0.f, s1 = 0.f;
-      for (int p0 = 0; p0 < P.Jw; p0 += 16) {
-        const int np0 = min(16, P.Jw - p0);
-        f32x4_t t[16];
-        uint32_t spins = 0;
-        while (true) {
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-#pragma unroll
-          for (int u = 0; u < 16; ++u)
-            t[u] = buf_load16_coherent(rW, grp_y + ((uint32_t)(p0 + min(u, np0 - 1)) * (uint32_t)vmax * 2u + (uint32_t)q) * 16u);
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-          bool ok = true;
-#pragma unroll
-          for (int u = 0; u < 16; ++u) ok = ok && __float_as_uint(t[u][1]) == epoch && __float_as_uint(t[u][3]) == epoch;
-          if (ok) break;
-          if (++spins > P.spin_limit) {
-            raise_stall(P.ctrl, P.err);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (u < np0) {
-            s0 += t[u][0];
-            s1 += t[u][2];
-          }
-      }
+      float s0, s1;
+      xpoll_sum(rW, grp_y, (uint32_t)vmax * 32u, P.Jw, (uint32_t)q * 16u, epoch, P.spin_limit, P.ctrl, P.err, s0, s1);
       const int vi = q >> 1;
       const int ntl = vi / (M * 32);
       const int rem = vi - ntl * M * 32;

@@ -299,6 +299,56 @@ __device__ __forceinline__ void raise_stall(uint32_t* ctrl, uint32_t* err) {
   st_agent_u32(ctrl + 2, 1u);
   if (err) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
+// Epoch-tagged exchange words between workgroups: {v0, tag, v1, tag}, two
+// values of a partial result, each beside a copy of the launch's epoch,
+// written as one 16-byte device-coherent store.  A reader that finds the
+// epoch it waits for in both tags of a word has both values (each value
+// shares an aligned 8-byte half of the store with its tag, and a store is
+// never seen split inside such a half), so an exchange needs neither a flag
+// nor a wait for the stores to complete: the reader polls the data itself.
+__device__ __forceinline__ void xstore_coherent(rsrc_t r, uint32_t off, float v0, float v1, float tag) {
+  buf_store16_coherent(r, off, f32x4_t{v0, tag, v1, tag});
+}
+__device__ __forceinline__ bool xtagged(const f32x4_t& t, uint32_t want) {
+  return __float_as_uint(t[1]) == want && __float_as_uint(t[3]) == want;
+}
+// Polls the exchange word at byte voff of n partials (stride bytes apart
+// from base), 16 partials in flight at a time, until all carry `want`, and
+// returns the two sums over the partials in order 0 .. n - 1.  A wait that
+// reaches spin_limit polls raises the stall words and sums what it read.
+__device__ __forceinline__ void xpoll_sum(rsrc_t r, uint32_t base, uint32_t stride, int n, uint32_t voff,
+                                          uint32_t want, uint32_t spin_limit, uint32_t* ctrl, uint32_t* err, float& s0,
+                                          float& s1) {
+  s0 = 0.f;
+  s1 = 0.f;
+  for (int p0 = 0; p0 < n; p0 += 16) {
+    const int np0 = min(16, n - p0);
+    f32x4_t t[16];
+    uint32_t spins = 0;
+    while (true) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // a fresh read every poll
+#pragma unroll
+      for (int u = 0; u < 16; ++u) t[u] = buf_load16_coherent(r, base + (uint32_t)(p0 + min(u, np0 - 1)) * stride + voff);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      bool ok = true;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) ok = ok && xtagged(t[u], want);
+      if (ok) break;
+      if (++spins > spin_limit) {
+        raise_stall(ctrl, err);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (u < np0) {
+        s0 += t[u][0];
+        s1 += t[u][2];
+      }
+  }
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // accesses (lgkmcnt = 0) and meets the other waves, without waiting for
 // global loads or stores still in flight.  (__syncthreads() also drains the

@@ -201,13 +201,14 @@ InplaceLayout inplace_layout(const lrv::DecPart& dp, int max_M, size_t off) {
   off = align_up(off + (size_t)G * 4);
   L.ycnt = off;
   off = align_up(off + (size_t)dp.S * 4);
+  // T partials of the streaming kernel and Y partials of both are stored as
+  // epoch-tagged exchange words: each value beside a tag, twice the bytes
   L.tpart = off;
-  off = align_up(off + (size_t)G * max_M * (dp.kind == 1 ? 128 : dp.js_w) * 4);
+  off = align_up(off + (size_t)G * max_M * (dp.kind == 1 ? 128 * 4 : dp.js_w * 8));
   L.tfin = off;
   off = align_up(off + (size_t)dp.Jw * max_M * dp.js_w * 4);
   L.ypart = off;
-  // the resident kernel stores each Y partial value beside an epoch tag
-  off = align_up(off + (size_t)G * dp.ntps * max_M * dp.nt_w * 4 * (dp.kind == 1 ? 2 : 1));
+  off = align_up(off + (size_t)G * dp.ntps * max_M * dp.nt_w * 8);
   L.end = off;
   return L;
 }
@@ -691,7 +692,7 @@ lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, cons
 // the library runs on holds its own copy until the process ends.  Host code
 // never uses the array's name as an address: its device address is taken
 // once per device with hipGetSymbolAddress and cached in g_scratch_ptr.
-constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
@@ -711,10 +712,10 @@ lr_status scratch_address(int dev, void** out) {
   return LR_OK;
 }
 
-// Zeroes n 32-bit words (a kernel rather than hipMemsetAsync, so that the
+// Zeroes n 16-byte words (a kernel rather than hipMemsetAsync, so that the
 // clear is an ordinary kernel node when the caller captures a graph).
-__global__ void clear_words_kernel(uint32_t* p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+__global__ void clear_words_kernel(uint4* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 }  // namespace
@@ -1084,11 +1085,12 @@ lr_status lr_decode_noalloc(const void* X, const void* A, const void* B, void* Y
   h.err_dev = status;
   // The array keeps the last call's contents, which may be another shape's
   // tables: the control words (generation, counters, flags) start at zero
-  // every call, so no stale flag can match this call's epoch; the resident
-  // kernel's epoch-tagged Y partials are cleared with them.
-  const int words = (int)((h.dp.kind == 1 ? L.end : L.tpart) / 4);
-  const int clear_blocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
-  hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)clear_blocks), dim3(256), 0, (hipStream_t)stream, h.ctrl, words);
+  // every call, and so do the epoch-tagged exchange words, so no stale flag
+  // or tag can match this call's epoch.
+  const int vecs = (int)(L.end / 16);  // the layout's regions are 256-byte aligned
+  const int clear_blocks = (vecs + 255) / 256 < 1024 ? (vecs + 255) / 256 : 1024;
+  hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)clear_blocks), dim3(256), 0, (hipStream_t)stream,
+                     reinterpret_cast<uint4*>(b), vecs);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
   const lr_linear* hs[1] = {&h};
