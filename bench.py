@@ -75,28 +75,31 @@ def dev_bf16(torch, bits):
 
 def time_steps(torch, fn, steps, warmup, stream, warm_seconds=0.0):
     """Event-timed average step.  Python's cyclic garbage collector is run
-    before the timed region and held off during it: a collection that
-    starts inside the launch loop stalls the host for about a millisecond,
-    the GPU runs dry, and a short step reads up to 1.7x slower (seen as a
-    one-point dip at a fixed place of the rank sweep).  `warm_seconds` keeps
-    running warm-up steps until that much time has passed: the compute-bound
-    prefill steps otherwise start timing before the GPU clock has risen from
-    the lighter load before them (the first launches of a run are up to 25%
-    slower)."""
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    if warm_seconds > 0:
-        t_end = time.time() + warm_seconds
-        i = warmup
-        while time.time() < t_end:
-            for _ in range(8):
-                fn(i)
-                i += 1
-            torch.cuda.synchronize()
+    once before the warm-up and held off until the timed region ends: a
+    collection that starts inside the launch loop stalls the host for about
+    a millisecond, the GPU runs dry, and a short step reads up to 1.7x
+    slower (seen as a one-point dip at a fixed place of the rank sweep).
+    The collection itself takes tens of milliseconds, so it must not sit
+    between the warm-up and the timed region either: after that long an
+    idle gap the first compute-bound prefill steps run through a clock
+    transient (up to 1.3x slower for a few milliseconds).  `warm_seconds`
+    keeps running warm-up steps until that much time has passed: the
+    compute-bound prefill steps otherwise start timing before the GPU clock
+    has settled from the lighter load before them."""
     gc.collect()
     gc.disable()
     try:
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        if warm_seconds > 0:
+            t_end = time.time() + warm_seconds
+            i = warmup
+            while time.time() < t_end:
+                for _ in range(8):
+                    fn(i)
+                    i += 1
+                torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)

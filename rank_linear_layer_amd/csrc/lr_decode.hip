@@ -165,7 +165,10 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   // in flight from the start (with the X segments they meet), and each is
   // requested again right after its use, with no branch around a load.
   constexpr int kDecABuf = 4;
-  RawTile ta[kDecABuf], b0, b1;
+  // B tiles in flight per wave (3 or 4 measured slower: the extra requests
+  // compete with A's stream)
+  constexpr int kDecBBuf = 2;
+  RawTile ta[kDecABuf], tb[kDecBBuf];
   u32x4_t xa[kDecABuf];
   const int kt0 = kt_beg + w;
 #pragma unroll
@@ -174,8 +177,9 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
     load_tile_raw_if(ta[i], rA, (int64_t)k * kDecKT, r, j0, np, g, k < kt_end);
     xa[i] = load_kvec(rX, np, K, (int64_t)k * kDecKT + 8 * g, K, xal);
   }
-  if (nt_beg < nt_end) load_tile_raw(b0, rB, jrow0, N, (int64_t)nt_beg * kDecNT, np, g);
-  if (nt_beg + 1 < nt_end) load_tile_raw(b1, rB, jrow0, N, (int64_t)(nt_beg + 1) * kDecNT, np, g);
+#pragma unroll
+  for (int i = 0; i < kDecBBuf; ++i)
+    load_tile_raw_if(tb[i], rB, jrow0, N, (int64_t)(nt_beg + i) * kDecNT, np, g, nt_beg + i < nt_end);
 
   // ---------------------------------------------------------- GEMM1 ------
   f32x4_t acc[8];
@@ -289,13 +293,15 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
     }
     barrier_lds();
   };
-  // Tiles in pairs with no branch around a load or store: the next tile of
-  // each buffer is requested (or replaced by zeros) right after its use.
-  for (int nt = nt_beg; nt < nt_end; nt += 2) {
-    gemm2_tile(b0, nt, true);
-    load_tile_raw_if(b0, rB, jrow0, N, (int64_t)(nt + 2) * kDecNT, np, g, nt + 2 < nt_end);
-    gemm2_tile(b1, nt + 1, nt + 1 < nt_end);
-    load_tile_raw_if(b1, rB, jrow0, N, (int64_t)(nt + 3) * kDecNT, np, g, nt + 3 < nt_end);
+  // Tiles in groups of kDecBBuf with no branch around a load or store: the
+  // next tile of each buffer is requested (or replaced by zeros) right after
+  // its use.
+  for (int nt = nt_beg; nt < nt_end; nt += kDecBBuf) {
+#pragma unroll
+    for (int i = 0; i < kDecBBuf; ++i) {
+      gemm2_tile(tb[i], nt + i, nt + i < nt_end);
+      load_tile_raw_if(tb[i], rB, jrow0, N, (int64_t)(nt + i + kDecBBuf) * kDecNT, np, g, nt + i + kDecBBuf < nt_end);
+    }
   }
 
   // ---------------------------------- Y reduce-scatter over the Jw slices --
