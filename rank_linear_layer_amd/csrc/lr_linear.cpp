@@ -76,6 +76,12 @@ struct lr_linear {
   uint32_t* tflag;
   uint32_t* ycnt;
   uint32_t off_tpart, off_tfin, off_ypart, off_tflag, off_yflag;
+  // register-streaming kernel: a second plan on half the compute units, so
+  // that two such projections sharing X (gate and up) fit one launch; its
+  // tables share the decode region (same control words)
+  bool has_half;
+  lrv::DecPart dph;
+  uint32_t hoff_tpart, hoff_ypart;
   bool xcd_local;
   // prefill workspace: T [max_M x r_pad] bf16, and fp32 k-split partials
   bool has_prefill;
@@ -127,7 +133,7 @@ bool use_decode(const lr_linear* h, int64_t M) {
 }
 
 // Fill the kernel-side descriptor of one projection in a decode launch.
-lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
+lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin, bool half = false) {
   lrk::DecProj p;
   p.A = h->A;
   p.B = h->B;
@@ -148,10 +154,15 @@ lrk::DecProj dec_proj(const lr_linear* h, uint16_t* Y, int wg_begin) {
   p.xcd_local = (h->xcd_local && wg_begin % 8 == 0) ? 1 : 0;
   p.r = (int)h->r;
   p.N = (int)h->N;
-  p.Jw = h->dp.Jw;
-  p.S = h->dp.S;
-  p.ktps = h->dp.ktps;
-  p.ntps = h->dp.ntps;
+  const lrv::DecPart& dp = half ? h->dph : h->dp;
+  p.Jw = dp.Jw;
+  p.S = dp.S;
+  p.ktps = dp.ktps;
+  p.ntps = dp.ntps;
+  if (half) {
+    p.off_tpart = h->hoff_tpart;
+    p.off_ypart = h->hoff_ypart;
+  }
   p.wg_begin = wg_begin;
   p.err = h->err_dev;
   p.spin_limit = h->spin_limit;
@@ -398,7 +409,7 @@ lr_status run_xcd_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n,
 }
 
 lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, const void* X, int64_t M,
-                     hipStream_t stream, bool check_only = false) {
+                     hipStream_t stream, bool check_only = false, bool half = false) {
   if (hs[0]->dp.kind == 5) {
     for (int i = 0; i < n; ++i) {
       const lr_status st = run_xcd_decode(hs + i, Ys + i, 1, X, M, stream, check_only);
@@ -426,8 +437,9 @@ lr_status run_decode(const lr_linear* const* hs, uint16_t* const* Ys, int n, con
   a.nproj = n;
   int wg = 0;
   for (int i = 0; i < n; ++i) {
-    a.p[i] = dec_proj(hs[i], Ys[i], wg);
-    wg += hs[i]->dp.Jw * hs[i]->dp.S;
+    a.p[i] = dec_proj(hs[i], Ys[i], wg, half);
+    const lrv::DecPart& dp = half ? hs[i]->dph : hs[i]->dp;
+    wg += dp.Jw * dp.S;
   }
   hipError_t e = hs[0]->dp.kind == 1 ? lrk::launch_decode_res(a, wg, stream) : lrk::launch_decode(a, wg, stream);
   if (e == hipErrorCooperativeLaunchTooLarge)
@@ -673,6 +685,20 @@ lr_status run_group(const lr_linear* const* hs, uint16_t* const* Ys, int n, cons
     const int per_cu = dh[b]->dp.kind == 1 ? 1 : lrk::decode_blocks_per_cu();
     const int64_t cap = (int64_t)num_cus(dh[b]->device) * per_cu;
     int64_t wgs = (int64_t)dh[b]->dp.Jw * dh[b]->dp.S;
+    // two register-streaming projections that do not fit one launch with
+    // their own plans share one on their half-machine plans
+    if (b + 1 < nd && dh[b]->dp.kind == 0 && dh[b + 1]->dp.kind == 0 && dh[b]->has_half && dh[b + 1]->has_half &&
+        wgs + (int64_t)dh[b + 1]->dp.Jw * dh[b + 1]->dp.S > cap &&
+        (int64_t)dh[b]->dph.Jw * dh[b]->dph.S + (int64_t)dh[b + 1]->dph.Jw * dh[b + 1]->dph.S <= cap) {
+      const lr_status st = run_decode(dh + b, dy + b, 2, X, M, stream, false, true);
+      if (st == LR_OK) {
+        b += 2;
+        continue;
+      }
+      // refused before launching (the pair cannot be resident at once): run
+      // them apart
+      if (st != LR_ERR_UNSUPPORTED) return st;
+    }
     int e = b + 1;
     while (e < nd && dh[e]->dp.kind == dh[b]->dp.kind && dh[e]->dp.kind < 2 && wgs + (int64_t)dh[e]->dp.Jw * dh[e]->dp.S <= cap) {
       wgs += (int64_t)dh[e]->dp.Jw * dh[e]->dp.S;
@@ -863,6 +889,17 @@ lr_status lr_linear_create(lr_linear** out, int64_t K, int64_t r, int64_t N, con
     o_tfin = L.tfin;
     o_ypart = L.ypart;
     off = L.end;
+    h->has_half = false;
+    if (h->dp.kind == 0) {
+      // the half-machine plan's tables, laid out from the same start (same
+      // control words; the epoch tags keep the two plans' words apart)
+      h->dph = lrv::decode_streaming_partition(K, r, N, num_cus(dev) / 2);
+      const InplaceLayout Lh = inplace_layout(h->dph, h->dec_max_M, L.ctrl);
+      h->has_half = (int64_t)h->dph.Jw * h->dph.S <= num_cus(dev) / 2;
+      h->hoff_tpart = (uint32_t)Lh.tpart;
+      h->hoff_ypart = (uint32_t)Lh.ypart;
+      if (h->has_half && Lh.end > off) off = Lh.end;
+    }
     // resident kernel: its T exchange runs through one XCD's L2, so every
     // rank-slice group must sit on one XCD (Jw a multiple of 8); streaming
     // kernel: only a traffic-saving placement of adjacent rank slices
