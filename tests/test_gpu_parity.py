@@ -474,6 +474,53 @@ def test_mlp_packed_gate_up_layer_decode(flags, M):
     assert_parity(to_bits(Yu), oracle.lowrank_bf16(Xb, Aub, Bub), "packed decode up")
 
 
+def test_packed_half_plans_alternate_with_single_runs(gpu):
+    # gate and up (register-streaming decode) do not fit one launch on their
+    # own plans, so the packed call runs both on their half-machine plans in
+    # the same decode tables; single calls use the full plans.  Alternating
+    # the two, eager and from a captured graph, every output must equal the
+    # first (stale epoch-tagged words of the other plan must never match).
+    torch = gpu
+    M = 1
+    banner("packed half plans alternating with single runs, M=%d" % M)
+    Xb, Agb, Bgb, Aub, Bub = _gate_up(M)
+    X = to_dev(Xb)
+    gate = lrl.LowRankLinear(to_dev(Agb), to_dev(Bgb), max_M=M)
+    up = lrl.LowRankLinear(to_dev(Aub), to_dev(Bub), max_M=M)
+    assert "kind=streaming" in gate.describe()
+    ref_g, ref_u = oracle.lowrank_bf16(Xb, Agb, Bgb), oracle.lowrank_bf16(Xb, Aub, Bub)
+    Yg, Yu = lrl.mlp_packed(gate, up, X)
+    first_g, first_u = to_bits(Yg), to_bits(Yu)
+    assert_parity(first_g, ref_g, "packed gate")
+    assert_parity(first_u, ref_u, "packed up")
+    for it in range(3):
+        yg1, yu1 = to_bits(gate(X)), to_bits(up(X))
+        assert_parity(yg1, ref_g, "single gate, round %d" % it)
+        assert_parity(yu1, ref_u, "single up, round %d" % it)
+        Yg, Yu = lrl.mlp_packed(gate, up, X)
+        assert np.array_equal(to_bits(Yg), first_g) and np.array_equal(to_bits(Yu), first_u), "round %d" % it
+    # graph replays of the packed call, with single eager calls between them
+    Og = torch.empty_like(Yg)
+    Ou = torch.empty_like(Yu)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lrl.mlp_packed(gate, up, X, Og, Ou)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lrl.mlp_packed(gate, up, X, Og, Ou)
+    for it in range(3):
+        Og.zero_()
+        Ou.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(Og), first_g) and np.array_equal(to_bits(Ou), first_u), "replay %d" % it
+        assert_parity(to_bits(gate(X)), ref_g, "single gate after replay %d" % it)
+    assert gate.status() == 0 and up.status() == 0
+
+
 # ----------------------------------------------------------- dense fallback ---
 # W = A.B formed at create; decode reads its MFMA-operand layout with no
 # exchange between workgroups, prefill runs X.W through the prefill GEMM.
