@@ -105,6 +105,7 @@ __device__ __forceinline__ void tile_operands(const RawTile& t, u32x4_t op[8], i
 __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecArgs a) {
   DEC_TRACE_ENTRY();
   __shared__ float red[kDecWaves][16][kDecJS + 8];
+  __shared__ float red2[kDecWaves][16][kDecJS + 8];  // the second n-tile of a GEMM2 pair
   __shared__ float Ts[16][kDecJS + 8];
   __shared__ uint32_t sh_epoch;
 
@@ -261,48 +262,64 @@ __global__ __launch_bounds__(kDecThreads) void lr_decode_fused_kernel(const DecA
   // Y partial of n-tile nt: [M][kDecNT] values as exchange words
   const uint32_t ytile_b = (uint32_t)(M * kDecNT * 8);
   const uint32_t ypart_wg = P.off_ypart + (uint32_t)((s * P.Jw + js) * P.ntps) * ytile_b;
-  // One n-tile: its partial is stored only when `ok` (a tile past the end of
-  // the slice is computed on zeros and its stores are dropped).
-  auto gemm2_tile = [&](const RawTile& bt, int nt, bool ok) {
-    const int64_t nb = (int64_t)nt * kDecNT;
-    f32x4_t y[8];
+  // A pair of n-tiles nt, nt + 1: both products, one LDS reduction over the
+  // four waves' rank rows (two barriers per pair), and the partials' stores;
+  // tile nt + 1's are dropped when `ok1` is false (past the slice: computed
+  // on zeros).
+  auto gemm2_pair = [&](int nt, bool ok1) {
+    f32x4_t y0[8], y1[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = zero4();
+    for (int e = 0; e < 8; ++e) {
+      y0[e] = zero4();
+      y1[e] = zero4();
+    }
     {
       u32x4_t op[8];
-      tile_operands(bt, op, jrow0, g, jrow_end, N, nb, np, N);
+      tile_operands(tb[0], op, jrow0, g, jrow_end, N, (int64_t)nt * kDecNT, np, N);
+      // the buffer is free once its operands are formed: request its next tile
+      load_tile_raw_if(tb[0], rB, jrow0, N, (int64_t)(nt + 2) * kDecNT, np, g, nt + 2 < nt_end);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        y[e] = mfma_16x16x32(thi, op[e], y[e]);
-        y[e] = mfma_16x16x32(tlo, op[e], y[e]);
+        y0[e] = mfma_16x16x32(thi, op[e], y0[e]);
+        y0[e] = mfma_16x16x32(tlo, op[e], y0[e]);
+      }
+    }
+    {
+      u32x4_t op[8];
+      tile_operands(tb[1], op, jrow0, g, jrow_end, N, (int64_t)(nt + 1) * kDecNT, np, N);
+      load_tile_raw_if(tb[1], rB, jrow0, N, (int64_t)(nt + 3) * kDecNT, np, g, nt + 3 < nt_end);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y1[e] = mfma_16x16x32(thi, op[e], y1[e]);
+        y1[e] = mfma_16x16x32(tlo, op[e], y1[e]);
       }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) red[w][4 * g + t][8 * np + e] = y[e][t];
+      for (int t = 0; t < 4; ++t) {
+        red[w][4 * g + t][8 * np + e] = y0[e][t];
+        red2[w][4 * g + t][8 * np + e] = y1[e][t];
+      }
     barrier_lds();
-    const uint32_t yp = ypart_wg + (uint32_t)(nt - nt_beg) * ytile_b;
-    for (int vi = tid; vi < M * (kDecNT / 4); vi += kDecThreads) {
+    const int nv = M * (kDecNT / 4);
+    for (int v2 = tid; v2 < 2 * nv; v2 += kDecThreads) {
+      const int h = v2 >= nv ? 1 : 0, vi = v2 - h * nv;
+      float(*rr)[16][kDecJS + 8] = h ? red2 : red;
       const int m = vi / (kDecNT / 4), c = (vi - m * (kDecNT / 4)) * 4;
       f32x4_t v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = ((red[0][m][c + i] + red[1][m][c + i]) + red[2][m][c + i]) + red[3][m][c + i];
+      for (int i = 0; i < 4; ++i) v[i] = ((rr[0][m][c + i] + rr[1][m][c + i]) + rr[2][m][c + i]) + rr[3][m][c + i];
+      const uint32_t yp = ypart_wg + (uint32_t)(nt + h - nt_beg) * ytile_b;
+      const bool ok = h == 0 || ok1;
       xstore_coherent(rW, off_if(yp + (uint32_t)vi * 32u, ok), v[0], v[1], tagf);
       xstore_coherent(rW, off_if(yp + (uint32_t)vi * 32u + 16u, ok), v[2], v[3], tagf);
     }
     barrier_lds();
   };
-  // Tiles in groups of kDecBBuf with no branch around a load or store: the
-  // next tile of each buffer is requested (or replaced by zeros) right after
-  // its use.
-  for (int nt = nt_beg; nt < nt_end; nt += kDecBBuf) {
-#pragma unroll
-    for (int i = 0; i < kDecBBuf; ++i) {
-      gemm2_tile(tb[i], nt + i, nt + i < nt_end);
-      load_tile_raw_if(tb[i], rB, jrow0, N, (int64_t)(nt + i + kDecBBuf) * kDecNT, np, g, nt + i + kDecBBuf < nt_end);
-    }
-  }
+  // Pairs of tiles with no branch around a load or store: the next tile of
+  // each buffer is requested (or replaced by zeros) right after its use.
+  for (int nt = nt_beg; nt < nt_end; nt += 2) gemm2_pair(nt, nt + 1 < nt_end);
 
   // ---------------------------------- Y reduce-scatter over the Jw slices --
   // Member js of n-slice s polls its 1/Jw share of the n-slice's exchange
