@@ -193,7 +193,8 @@ lr_status lr_linear_run(const lr_linear* h, const void* X, void* Y, int64_t M, v
  * as lr_group_run with n = 2 and handles {gate, up}: at M > 16 the tiles of
  * both GEMM1s are dealt over the CUs in one prefill launch (each workgroup
  * loads the X tile of its own output tile); at decode the two run in one
- * launch where the kernel allows it (see lr_group_run).
+ * launch where the kernel allows it (see lr_group_run), the layer's gate
+ * and up (register-streaming kernel) on each handle's half-machine plan.
  * gate and up must be distinct handles with equal K; their r and N may
  * differ.  M must not exceed either handle's max_M.  Y_gate and Y_up must
  * not overlap each other or any input.
@@ -222,7 +223,9 @@ lr_status lr_mlp_packed_run(const lr_linear* gate, const lr_linear* up, const vo
  * Projections that take the dense fallback's decode at this M share one
  * launch; factorized projections that take a decode kernel share decode
  * launches where their kernel allows it: the resident and streaming
- * kernels while the workgroups of all fit the device at once, the
+ * kernels while the workgroups of all fit the device at once (two
+ * streaming projections that do not, such as a layer's gate and up, on
+ * the second plan each handle holds for half the compute units), the
  * XCD-sliced kernel always (each projection takes a share of every XCD's
  * compute units), the role-split kernels never (each fills the device).
  * The others share one launch per prefill GEMM, in which every output's
